@@ -21,8 +21,10 @@ def main():
     out_d, _, fin_d = oracle.gdn_decode(dec.q, dec.k, dec.v, dec.a, dec.b, dec.A_log, dec.dt_bias,
                                         dec.slot, pool1, dec.scale)
     pool2 = oracle.apply_final_states(pool1, fin_d)
+    touched = np.asarray(ext.slot)
     np.savez_compressed(os.path.join(HERE, "config0_oracle.npz"), extend_out=out_e,
-                        decode_out=out_d, pool_after_extend=pool1, pool_after_decode=pool2)
+                        decode_out=out_d, slots=touched, state_after_extend=pool1[touched],
+                        state_after_decode=pool2[touched])
 
 
 if __name__ == "__main__":
