@@ -1,1 +1,342 @@
-"""MI355X-native GDN (Gated DeltaNet) layer: HIP kernels behind a C-ABI library."""
+"""MI355X-native GDN (Gated DeltaNet) linear-attention layer.
+
+Thin Python binding over libgdn.so (include/gdn.h): every step of the layer runs
+in the library's HIP kernels; this module only checks tensors, allocates outputs
+the caller did not supply and passes pointers, strides and torch's current HIP
+stream.  There is no fallback: without the built library every call raises.
+
+Entry points (same names as the C ABI):
+  gate / ssd_gate      a, b -> (log g, beta)               -> gdn_gate
+  extend               packed varlen extend over a pool   -> gdn_extend
+  decode               one token per sequence, in place   -> gdn_decode
+  validate_slots       opt-in device check of slots       -> gdn_validate_slots
+and the two call shapes of the pages:
+  forward_gdn(layer, forward_batch, mixed_qkv, a, b)  (pymllm HybridAttnBackend.forward_gdn)
+  ssd_combined_fwd(x, dt, A, B, C, ...)               (flashinfer.mamba.ssd_combined_fwd subset)
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import math
+
+import torch
+
+from . import _lib
+from ._lib import GDN_BF16, GDN_F32, GDN_MODE_GDN, GDN_MODE_SSD, GDNError
+
+__all__ = ["load", "gate", "ssd_gate", "extend", "decode", "validate_slots", "forward_gdn",
+           "ssd_combined_fwd", "GDNError", "split_mixed_qkv"]
+
+
+def load():
+    """Load libgdn.so (raises RuntimeError when it is missing)."""
+    return _lib.load()
+
+
+# ------------------------------------------------------------------ helpers
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ct.c_void_p:
+    return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on_gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _rows(t: torch.Tensor, name: str, heads: int, dim: int) -> int:
+    """Token stride of a [T, heads, dim] view whose heads are contiguous."""
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != dim:
+        raise ValueError(f"{name} must be [T, {heads}, {dim}], got {tuple(t.shape)}")
+    if t.stride(2) != 1 or (heads > 1 and t.stride(1) != dim):
+        raise ValueError(f"{name} must have contiguous heads (strides {t.stride()})")
+    return t.stride(0)
+
+
+def _mat_rows(t: torch.Tensor, name: str, T: int, H: int) -> int:
+    if t.dim() != 2 or t.shape[0] != T or t.shape[1] != H or (H > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be [{T}, {H}] with unit column stride, got "
+                         f"{tuple(t.shape)} / {t.stride()}")
+    return t.stride(0) if T > 1 else H
+
+
+def _i32(t: torch.Tensor, name: str, n: int) -> torch.Tensor:
+    if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous int32 vector of length {n}")
+    return t
+
+
+def split_mixed_qkv(mixed_qkv: torch.Tensor, H_qk: int, H_v: int, d_k: int, d_v: int):
+    """Views q [T,H_qk,d_k], k [T,H_qk,d_k], v [T,H_v,d_v] of a [T, 2 H_qk d_k + H_v d_v]
+    projection laid out q | k | v with heads contiguous inside each block."""
+    T, width = mixed_qkv.shape
+    nq = H_qk * d_k
+    if width != 2 * nq + H_v * d_v or mixed_qkv.stride(1) != 1:
+        raise ValueError(f"mixed_qkv width {width} != 2*{H_qk}*{d_k} + {H_v}*{d_v}")
+    q = mixed_qkv[:, :nq].unflatten(1, (H_qk, d_k))
+    k = mixed_qkv[:, nq:2 * nq].unflatten(1, (H_qk, d_k))
+    v = mixed_qkv[:, 2 * nq:].unflatten(1, (H_v, d_v))
+    return q, k, v
+
+
+# ------------------------------------------------------------------ gdn_gate
+def gate(a: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor | None = None,
+         *, log_g: torch.Tensor | None = None, beta: torch.Tensor | None = None):
+    """GDN gate: log_g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); fp32 [T, H]."""
+    lib = _lib.load()
+    T, H = a.shape
+    dev = _on_gpu(a, b, A_log, dt_bias, log_g, beta)
+    if b.dtype != a.dtype:
+        raise ValueError("a and b must share a dtype")
+    for t, nm in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (H,) or not t.is_contiguous()):
+            raise ValueError(f"{nm} must be contiguous fp32 [{H}]")
+    log_g = torch.empty((T, H), dtype=torch.float32, device=dev) if log_g is None else log_g
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev) if beta is None else beta
+    for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.shape != (T, H) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous fp32 [{T}, {H}]")
+    args = _lib.GateArgs(mode=GDN_MODE_GDN, in_dtype=_dtype_code(a), T=T, H=H, a=_ptr(a),
+                         a_stride=_mat_rows(a, "a", T, H), b=_ptr(b),
+                         b_stride=_mat_rows(b, "b", T, H), A=_ptr(A_log), dt_bias=_ptr(dt_bias),
+                         dt_softplus=1, dt_min=0.0, dt_max=math.inf, log_g=_ptr(log_g),
+                         beta=_ptr(beta))
+    _lib.check("gdn_gate", lib.gdn_gate(ct.byref(args), _stream(dev)))
+    return log_g, beta
+
+
+def ssd_gate(dt: torch.Tensor, A: torch.Tensor, dt_bias: torch.Tensor | None = None,
+             dt_softplus: bool = False, dt_limit=(0.0, math.inf), *,
+             log_g: torch.Tensor | None = None, beta: torch.Tensor | None = None):
+    """Delta-off gate: dt' = clamp(softplus?(dt + dt_bias), dt_limit); log_g = dt' A; beta = dt'."""
+    lib = _lib.load()
+    T, H = dt.shape
+    dev = _on_gpu(dt, A, dt_bias, log_g, beta)
+    for t, nm in ((A, "A"), (dt_bias, "dt_bias")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (H,) or not t.is_contiguous()):
+            raise ValueError(f"{nm} must be contiguous fp32 [{H}]")
+    log_g = torch.empty((T, H), dtype=torch.float32, device=dev) if log_g is None else log_g
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev) if beta is None else beta
+    args = _lib.GateArgs(mode=GDN_MODE_SSD, in_dtype=_dtype_code(dt), T=T, H=H, a=_ptr(dt),
+                         a_stride=_mat_rows(dt, "dt", T, H), b=None, b_stride=0, A=_ptr(A),
+                         dt_bias=_ptr(dt_bias), dt_softplus=int(bool(dt_softplus)),
+                         dt_min=float(dt_limit[0]), dt_max=float(dt_limit[1]),
+                         log_g=_ptr(log_g), beta=_ptr(beta))
+    _lib.check("gdn_gate", lib.gdn_gate(ct.byref(args), _stream(dev)))
+    return log_g, beta
+
+
+# ------------------------------------------------------------------ gdn_extend
+def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
+           out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0):
+    """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
+    cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
+    (updated in place).  Returns out [T, H_v, d_v]."""
+    lib = _lib.load()
+    T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    dev = _on_gpu(q, k, v, log_g, beta, cu_seqlens, slot, pool, has_init, out, D, z)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    ssd = mode == "ssd"
+    if mode not in ("gdn", "ssd"):
+        raise ValueError(f"mode must be 'gdn' or 'ssd', got {mode!r}")
+    if pool.dtype != torch.float32 or pool.dim() != 4 or pool.shape[1:] != (H_v, d_v, d_k) \
+            or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous fp32 [num_slots, {H_v}, {d_v}, {d_k}]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, H_v, d_v), dtype=out_dtype, device=dev)
+    if scale is None:
+        scale = 1.0 if ssd else d_k ** -0.5
+    _i32(cu_seqlens, "cu_seqlens", N + 1)
+    _i32(slot, "slot", N)
+    if has_init is not None:
+        _i32(has_init, "has_init", N)
+    for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.shape != (T, H_v) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous fp32 [{T}, {H_v}]")
+    if D is not None and (D.dtype != q.dtype or not D.is_contiguous()
+                          or D.shape not in ((H_v,), (H_v, d_v))):
+        raise ValueError(f"D must be contiguous [{H_v}] or [{H_v}, {d_v}] in the input dtype")
+    if z is not None and z.dtype != q.dtype:
+        raise ValueError("z must share the input dtype")
+    args = _lib.ExtendArgs(
+        mode=GDN_MODE_SSD if ssd else GDN_MODE_GDN, in_dtype=_dtype_code(q),
+        out_dtype=_dtype_code(out), N=N, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, chunk=chunk,
+        max_seqlen=int(max_seqlen), q=_ptr(q), q_stride=_rows(q, "q", H_qk, d_k), k=_ptr(k),
+        k_stride=_rows(k, "k", H_qk, d_k), v=_ptr(v), v_stride=_rows(v, "v", H_v, d_v),
+        log_g=_ptr(log_g), beta=_ptr(beta), cu_seqlens=_ptr(cu_seqlens), slot=_ptr(slot),
+        has_init=_ptr(has_init), pool=_ptr(pool), num_slots=pool.shape[0], out=_ptr(out),
+        out_stride=_rows(out, "out", H_v, d_v), scale=float(scale),
+        D_per_dim=int(D is not None and D.dim() == 2), D=_ptr(D), z=_ptr(z),
+        z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0)
+    _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------------ gdn_decode
+def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=None):
+    """One token per sequence; pool slots are read and written in place."""
+    lib = _lib.load()
+    B, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    dev = _on_gpu(q, k, v, log_g, beta, slot, pool, out)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if pool.dtype != torch.float32 or pool.dim() != 4 or pool.shape[1:] != (H_v, d_v, d_k) \
+            or not pool.is_contiguous():
+        raise ValueError(f"pool must be contiguous fp32 [num_slots, {H_v}, {d_v}, {d_k}]")
+    _i32(slot, "slot", B)
+    for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.shape != (B, H_v) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous fp32 [{B}, {H_v}]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H_v, d_v), dtype=out_dtype, device=dev)
+    scale = d_k ** -0.5 if scale is None else scale
+    args = _lib.DecodeArgs(
+        in_dtype=_dtype_code(q), out_dtype=_dtype_code(out), B=B, H_qk=H_qk, H_v=H_v, d_k=d_k,
+        d_v=d_v, q=_ptr(q), q_stride=_rows(q, "q", H_qk, d_k), k=_ptr(k),
+        k_stride=_rows(k, "k", H_qk, d_k), v=_ptr(v), v_stride=_rows(v, "v", H_v, d_v),
+        log_g=_ptr(log_g), beta=_ptr(beta), slot=_ptr(slot), pool=_ptr(pool),
+        num_slots=pool.shape[0], out=_ptr(out), out_stride=_rows(out, "out", H_v, d_v),
+        scale=float(scale))
+    _lib.check("gdn_decode", lib.gdn_decode(ct.byref(args), _stream(dev)))
+    return out
+
+
+def validate_slots(slot: torch.Tensor, num_slots: int) -> int:
+    """0 = ok, bit 1 = out of range, bit 2 = duplicate (synchronises to read the flag)."""
+    lib = _lib.load()
+    dev = _on_gpu(slot)
+    _i32(slot, "slot", slot.shape[0])
+    flag = torch.empty(1, dtype=torch.int32, device=dev)
+    _lib.check("gdn_validate_slots", lib.gdn_validate_slots(_ptr(slot), slot.shape[0], num_slots,
+                                                            _ptr(flag), _stream(dev)))
+    return int(flag.item())
+
+
+# ------------------------------------------------------------------ forward_gdn adapter
+_DECODE_MODES = {"decode", "idle"}
+_EXTEND_MODES = {"extend", "mixed", "draft_extend", "draft_extend_v2", "target_verify",
+                 "split_prefill", "dllm_extend"}
+
+
+def _mode_kind(forward_mode) -> str:
+    """'decode' or 'extend' for the legal forward modes, else ValueError.
+
+    The legal set follows the SGLang GDN test-matrix article (framerc.cn), section
+    on unsupported production combinations: decode-or-idle, or the extend family
+    (EXTEND, MIXED, DRAFT_EXTEND, DRAFT_EXTEND_V2, TARGET_VERIFY, SPLIT_PREFILL,
+    DLLM_EXTEND).  Objects with is_decode_or_idle() / is_extend() predicates are
+    accepted as well as plain names."""
+    if hasattr(forward_mode, "is_decode_or_idle") and forward_mode.is_decode_or_idle():
+        return "decode"
+    if hasattr(forward_mode, "is_extend"):
+        try:
+            ext = forward_mode.is_extend(include_draft_extend_v2=True)
+        except TypeError:
+            ext = forward_mode.is_extend()
+        if ext:
+            return "extend"
+    name = getattr(forward_mode, "name", forward_mode)
+    if isinstance(name, str):
+        key = name.lower()
+        if key in _DECODE_MODES:
+            return "decode"
+        if key in _EXTEND_MODES:
+            return "extend"
+    raise ValueError(f"Invalid forward mode: {forward_mode=}")
+
+
+def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, b: torch.Tensor):
+    """GDN layer call of a hybrid model (pymllm HybridAttnBackend.forward_gdn).
+
+    layer: num_k_heads, num_v_heads, head_k_dim, head_v_dim, A_log [H_v] fp32,
+           dt_bias [H_v] fp32, optional scale (default head_k_dim ** -0.5), layer_id.
+    forward_batch: forward_mode; state_slots int32 [N]; state_pool indexable by
+           layer_id -> fp32 [num_slots, H_v, d_v, d_k]; for extend modes also
+           cu_seqlens int32 [N+1], optional has_initial_state int32 [N] and max_seqlen.
+    mixed_qkv: [T, 2 H_qk d_k + H_v d_v], already convolved; a, b: [T, H_v].
+    Returns out [T, H_v * d_v] in mixed_qkv's dtype."""
+    kind = _mode_kind(forward_batch.forward_mode)
+    H_qk, H_v = layer.num_k_heads, layer.num_v_heads
+    d_k, d_v = layer.head_k_dim, layer.head_v_dim
+    scale = getattr(layer, "scale", None)
+    scale = d_k ** -0.5 if scale is None else scale
+    pool = forward_batch.state_pool[layer.layer_id]
+    q, k, v = split_mixed_qkv(mixed_qkv, H_qk, H_v, d_k, d_v)
+    T = mixed_qkv.shape[0]
+    if T == 0:
+        return mixed_qkv.new_empty((0, H_v * d_v))
+    log_g, beta = gate(a, b, layer.A_log, layer.dt_bias)
+    if kind == "decode":
+        o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale)
+    else:
+        o = extend(q, k, v, log_g, beta, forward_batch.cu_seqlens, forward_batch.state_slots, pool,
+                   has_init=getattr(forward_batch, "has_initial_state", None), scale=scale,
+                   max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0))
+    return o.view(T, H_v * d_v)
+
+
+# ------------------------------------------------------------------ ssd_combined_fwd subset
+def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
+                     dt_limit=(0.0, math.inf), initial_states=None, seq_idx=None,
+                     chunk_indices=None, chunk_offsets=None, seq_chunk_cumsum=None,
+                     update_seq_chunk_cumsum=False, checkpoint_token_indices=None,
+                     checkpoint_state_slots=None, checkpoint_states=None, out=None,
+                     return_final_states=True):
+    """Batched-mode subset of flashinfer.mamba.ssd_combined_fwd on the delta-off kernels.
+
+    x [batch, L, H, P] bf16; dt [batch, L, H]; A [H] fp32; B, C [batch, L, G, N];
+    D [H] or [H, P]; z like x; initial_states [batch, H, P, N].  States are fp32.
+    Returns (out [batch, L, H, P], final_states fp32 [batch, H, P, N] or None).
+    The packed-varlen metadata, checkpoint capture and the caller-owned 5-D `out`
+    storage are not supported and raise NotImplementedError."""
+    if any(t is not None for t in (seq_idx, chunk_indices, chunk_offsets, seq_chunk_cumsum,
+                                   checkpoint_token_indices, checkpoint_state_slots,
+                                   checkpoint_states, out)) or update_seq_chunk_cumsum:
+        raise NotImplementedError("varlen metadata, checkpoints and caller-owned out are not supported")
+    batch, L, H, P = x.shape
+    G, Nst = B.shape[2], B.shape[3]
+    dev = _on_gpu(x, dt, A, B, C, D, z, dt_bias, initial_states)
+    if H % G:
+        raise ValueError("nheads must be a multiple of ngroups")
+    T = batch * L
+    for t, nm in ((x, "x"), (dt, "dt"), (B, "B"), (C, "C"), (z, "z")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    log_g, dtp = ssd_gate(dt.view(T, H), A, dt_bias, dt_softplus, dt_limit)
+    if initial_states is not None:
+        pool = initial_states.to(torch.float32).contiguous().clone()
+    else:
+        pool = torch.empty((batch, H, P, Nst), dtype=torch.float32, device=dev)
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+    slot = torch.arange(batch, dtype=torch.int32, device=dev)
+    has_init = torch.full((batch,), int(initial_states is not None), dtype=torch.int32, device=dev)
+    o = extend(C.view(T, G, Nst), B.view(T, G, Nst), x.view(T, H, P), log_g, dtp, cu, slot, pool,
+               has_init=has_init, mode="ssd", D=D, z=None if z is None else z.view(T, H, P),
+               max_seqlen=L)
+    return o.view(batch, L, H, P), (pool if return_final_states else None)

@@ -1,0 +1,86 @@
+"""Build libgdn.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m hybrid_model_linear_amd.build          # compile + link
+
+Every kernel source is compiled with the packed-fp32 target feature disabled
+(plain scalar fp32 VALU code only), -O3, for gfx950.  The library is linked
+against the HIP runtime that the running PyTorch uses when PyTorch ships its own
+copy, so that torch's streams and device pointers belong to the same runtime.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libgdn.so")
+SOURCES = ["gate.hip", "recurrent.hip", "chunk.hip", "validate.hip", "gdn_abi.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libgdn.so)")
+
+
+def hip_runtime_dir() -> str | None:
+    """Directory of the libamdhip64.so that torch loads, if torch bundles one."""
+    try:
+        import importlib.util
+        spec = importlib.util.find_spec("torch")
+        if spec is None or spec.origin is None:
+            return None
+        d = os.path.join(os.path.dirname(spec.origin), "lib")
+        return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
+    except Exception:
+        return None
+
+
+def compile_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+            "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + compile_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{msg}")
+    if msg.strip() and verbose:
+        print(msg)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    rt = hip_runtime_dir()
+    if rt:
+        link += ["-L", rt, "-Wl,-rpath," + rt, "-lamdhip64"]
+    if verbose:
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,197 @@
+// C-ABI entry points of libgdn.so: host-side validation, then one launch per call.
+// Declarations and the contract (ownership, layouts, errors) are in include/gdn.h.
+#include "../../include/gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return e == hipSuccess ? GDN_OK : GDN_E_HIP;
+}
+
+bool dtype_ok(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// Checks shared by gdn_extend and gdn_decode; fills everything but the
+// per-call index fields.
+int check_seq_common(int32_t in_dtype, int32_t out_dtype, int32_t H_qk, int32_t H_v, int32_t d_k,
+                     int32_t d_v, int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                     int64_t out_stride, int64_t num_slots, float scale) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDN_E_DTYPE;
+  if (H_qk <= 0 || H_v <= 0 || H_v % H_qk != 0) return GDN_E_SHAPE;
+  if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_E_UNSUPPORTED;
+  if (q_stride < (int64_t)H_qk * d_k || k_stride < (int64_t)H_qk * d_k) return GDN_E_SHAPE;
+  if (v_stride < (int64_t)H_v * d_v || out_stride < (int64_t)H_v * d_v) return GDN_E_SHAPE;
+  if (num_slots <= 0) return GDN_E_SHAPE;
+  if (!std::isfinite(scale)) return GDN_E_SHAPE;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+int gdn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_E_NULL: return "required pointer is NULL";
+    case GDN_E_SHAPE: return "inconsistent sizes or strides";
+    case GDN_E_DTYPE: return "unsupported dtype";
+    case GDN_E_UNSUPPORTED: return "unsupported configuration";
+    case GDN_E_INDEX: return "index argument out of range";
+    case GDN_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gdn_gate(const gdn_gate_args* a, void* stream) {
+  if (!a) return GDN_E_NULL;
+  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
+  if (!dtype_ok(a->in_dtype)) return GDN_E_DTYPE;
+  if (a->T < 0 || a->H <= 0) return GDN_E_SHAPE;
+  if (a->T == 0) return GDN_OK;
+  if (!a->a || !a->A || !a->log_g || !a->beta) return GDN_E_NULL;
+  if (a->a_stride < a->H) return GDN_E_SHAPE;
+  if (a->mode == GDN_MODE_GDN) {
+    if (!a->b) return GDN_E_NULL;
+    if (a->b_stride < a->H) return GDN_E_SHAPE;
+  } else {
+    if (a->b) return GDN_E_SHAPE;            // SSD mode has no b input
+    if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
+      return GDN_E_SHAPE;
+  }
+  gdn::GateLaunch p{};
+  p.T = a->T;
+  p.H = a->H;
+  p.bf16 = a->in_dtype == GDN_BF16;
+  p.ssd = a->mode == GDN_MODE_SSD;
+  p.a = a->a;
+  p.a_stride = a->a_stride;
+  p.b = a->b;
+  p.b_stride = a->b_stride;
+  p.A = a->A;
+  p.dt_bias = a->dt_bias;
+  p.dt_softplus = a->dt_softplus;
+  p.dt_min = a->dt_min;
+  p.dt_max = a->dt_max;
+  p.log_g = a->log_g;
+  p.beta = a->beta;
+  return hip_status(gdn::launch_gate(p, (hipStream_t)stream));
+}
+
+int gdn_extend(const gdn_extend_args* a, void* stream) {
+  if (!a) return GDN_E_NULL;
+  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
+  int st = check_seq_common(a->in_dtype, a->out_dtype, a->H_qk, a->H_v, a->d_k, a->d_v,
+                            a->q_stride, a->k_stride, a->v_stride, a->out_stride, a->num_slots,
+                            a->scale);
+  if (st != GDN_OK) return st;
+  if (a->N < 0 || a->T < 0 || a->max_seqlen < 0) return GDN_E_SHAPE;
+  if (a->chunk != 0 && a->chunk != 64) return GDN_E_UNSUPPORTED;
+  if (a->mode == GDN_MODE_GDN && (a->D || a->z)) return GDN_E_SHAPE;   // SSD-only inputs
+  if (a->z && a->z_stride < (int64_t)a->H_v * a->d_v) return GDN_E_SHAPE;
+  if (a->N == 0) return GDN_OK;
+  if (!a->cu_seqlens || !a->slot || !a->pool) return GDN_E_NULL;
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->out))
+    return GDN_E_NULL;
+  if (a->T > INT32_MAX) return GDN_E_SHAPE;      // cu_seqlens is int32
+
+  gdn::SeqLaunch p{};
+  p.ssd = a->mode == GDN_MODE_SSD;
+  p.in_bf16 = a->in_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.N = a->N;
+  p.T = a->T;
+  p.H_qk = a->H_qk;
+  p.H_v = a->H_v;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.q = a->q;
+  p.q_stride = a->q_stride;
+  p.k = a->k;
+  p.k_stride = a->k_stride;
+  p.v = a->v;
+  p.v_stride = a->v_stride;
+  p.log_g = a->log_g;
+  p.beta = a->beta;
+  p.cu_seqlens = a->cu_seqlens;
+  p.slot = a->slot;
+  p.has_init = a->has_init;
+  p.pool = a->pool;
+  p.num_slots = a->num_slots;
+  p.out = a->out;
+  p.out_stride = a->out_stride;
+  p.scale = a->mode == GDN_MODE_SSD ? 1.0f : a->scale;
+  p.D = a->D;
+  p.D_per_dim = a->D_per_dim;
+  p.z = a->z;
+  p.z_stride = a->z_stride;
+  p.max_seqlen = a->max_seqlen;
+
+  const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
+  if (p.in_bf16 && !short_batch && gdn::chunked_supported(p))
+    return hip_status(gdn::launch_chunked(p, (hipStream_t)stream));
+  return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
+}
+
+int gdn_decode(const gdn_decode_args* a, void* stream) {
+  if (!a) return GDN_E_NULL;
+  int st = check_seq_common(a->in_dtype, a->out_dtype, a->H_qk, a->H_v, a->d_k, a->d_v,
+                            a->q_stride, a->k_stride, a->v_stride, a->out_stride, a->num_slots,
+                            a->scale);
+  if (st != GDN_OK) return st;
+  if (a->B < 0) return GDN_E_SHAPE;
+  if (a->B == 0) return GDN_OK;
+  if (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->slot || !a->pool || !a->out)
+    return GDN_E_NULL;
+  gdn::SeqLaunch p{};
+  p.ssd = 0;
+  p.in_bf16 = a->in_dtype == GDN_BF16;
+  p.out_bf16 = a->out_dtype == GDN_BF16;
+  p.N = a->B;
+  p.T = a->B;
+  p.H_qk = a->H_qk;
+  p.H_v = a->H_v;
+  p.d_k = a->d_k;
+  p.d_v = a->d_v;
+  p.q = a->q;
+  p.q_stride = a->q_stride;
+  p.k = a->k;
+  p.k_stride = a->k_stride;
+  p.v = a->v;
+  p.v_stride = a->v_stride;
+  p.log_g = a->log_g;
+  p.beta = a->beta;
+  p.cu_seqlens = nullptr;   // token b is sequence b
+  p.slot = a->slot;
+  p.has_init = nullptr;     // always resumes from the pool
+  p.pool = a->pool;
+  p.num_slots = a->num_slots;
+  p.out = a->out;
+  p.out_stride = a->out_stride;
+  p.scale = a->scale;
+  p.max_seqlen = 1;
+  return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
+}
+
+int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
+                       void* stream) {
+  if (!flag) return GDN_E_NULL;
+  if (n < 0 || num_slots <= 0) return GDN_E_SHAPE;
+  if (n > 0 && !slot) return GDN_E_NULL;
+  return hip_status(gdn::launch_validate_slots(slot, n, num_slots, flag, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launch descriptors between the C-ABI layer (gdn_abi.cpp) and the kernels.
+// Validation happens before these are filled; the kernels trust them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct GateLaunch {
+  int64_t T;
+  int H;
+  int bf16;                 // a/b stored as bf16 (else fp32)
+  int ssd;                  // delta-off mode
+  const void* a;
+  int64_t a_stride;
+  const void* b;
+  int64_t b_stride;
+  const float* A;           // GDN: A_log; SSD: A
+  const float* dt_bias;     // may be null
+  int dt_softplus;
+  float dt_min, dt_max;
+  float* log_g;
+  float* beta;
+};
+
+// One packed-varlen call: sequence n owns tokens [cu[n], cu[n+1]) (or token n
+// when cu is null), starts from pool[slot[n]] (zeros when has_init[n] == 0) and
+// writes its final state back to pool[slot[n]]; slot[n] < 0 skips it.
+struct SeqLaunch {
+  int ssd;                  // delta-off mode: no delta rule, no L2 norm, D and z epilogue
+  int in_bf16;              // q/k/v/z/D stored as bf16 (else fp32)
+  int out_bf16;             // out stored as bf16 (else fp32)
+  int N;
+  int64_t T;
+  int H_qk, H_v, d_k, d_v;
+  const void* q;
+  int64_t q_stride;         // elements between tokens; heads contiguous (stride d_k)
+  const void* k;
+  int64_t k_stride;
+  const void* v;
+  int64_t v_stride;         // heads contiguous (stride d_v)
+  const float* log_g;       // [T, H_v]
+  const float* beta;        // [T, H_v]
+  const int32_t* cu_seqlens;  // [N+1] or null (unit lengths)
+  const int32_t* slot;        // [N]
+  const int32_t* has_init;    // [N] or null (all 1)
+  float* pool;                // [num_slots, H_v, d_v, d_k]
+  int64_t num_slots;
+  void* out;                  // [T, H_v, d_v]
+  int64_t out_stride;
+  float scale;
+  const void* D;              // delta-off: [H_v] or [H_v, d_v], or null
+  int D_per_dim;
+  const void* z;              // delta-off: like v, or null
+  int64_t z_stride;
+  int max_seqlen;             // host hint, 0 = unknown
+};
+
+hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);
+hipError_t launch_recurrent(const SeqLaunch& p, hipStream_t stream);
+hipError_t launch_chunked(const SeqLaunch& p, hipStream_t stream);
+hipError_t launch_validate_slots(const int32_t* slot, int n, int64_t num_slots, int32_t* flag,
+                                 hipStream_t stream);
+bool chunked_supported(const SeqLaunch& p);
+
+}  // namespace gdn

@@ -33,21 +33,23 @@ __all__ = [
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16), round-to-nearest-even, NaN kept."""
+    """fp32 -> bf16 bit patterns (uint16), round-to-nearest-even (finite inputs)."""
+    return (bf16_round(x).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_round(x: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 value (RNE, ties to even); fp32 result.
+    Works in 32-bit integer arithmetic in place so that it scales to ~1e9 values."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(x)
-    if nan.any():
-        out[nan] = 0x7FC0
-    return out
-
-
-def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to the nearest bf16 value (RNE); result is fp32."""
-    bits = bf16_bits(x).astype(np.uint32) << 16
-    return bits.view(np.float32).reshape(np.shape(x))
+    res = np.array(x, copy=True) if out is None else out
+    if res is not x:
+        np.copyto(res, x)
+    u = res.view(np.uint32)
+    lsb = (u >> 16) & 1
+    lsb += 0x7FFF
+    u += lsb
+    u &= 0xFFFF0000
+    return res
 
 
 def _normal(rng, shape, sigma=1.0):
@@ -141,10 +143,13 @@ def make_gdn_case(name, *, seed, lens, has_init, H_qk, H_v, d_k, d_v, dtype="bf1
     cu = np.zeros(N + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     width = 2 * H_qk * d_k + H_v * d_v
-    qk = _normal(rng, (T, 2 * H_qk * d_k), qk_sigma)
-    vv = _normal(rng, (T, H_v * d_v), v_sigma)
-    mixed = _round_if(np.concatenate([qk, vv], axis=1), dtype)
-    assert mixed.shape == (T, width)
+    mixed = rng.standard_normal(size=(T, width), dtype=np.float32)   # q | k | v
+    if qk_sigma != 1.0:
+        mixed[:, :2 * H_qk * d_k] *= np.float32(qk_sigma)
+    if v_sigma != 1.0:
+        mixed[:, 2 * H_qk * d_k:] *= np.float32(v_sigma)
+    if dtype == "bf16":
+        bf16_round(mixed, out=mixed)
     a = _round_if(_normal(rng, (T, H_v), a_sigma), dtype)
     b = _round_if(_normal(rng, (T, H_v), b_sigma), dtype)
     if A_log is None:
@@ -276,3 +281,103 @@ def edge_case(name, lens, has_init=1, seed=7, H_qk=2, H_v=4, d_k=128, d_v=128,
     lengths 1/63/64/65/127/128/129 or the page-boundary tuples."""
     return make_gdn_case(name, seed=seed, lens=lens, has_init=has_init, H_qk=H_qk, H_v=H_v,
                          d_k=d_k, d_v=d_v, dtype=dtype, num_slots=num_slots, slot=slot)
+
+
+# ------------------------------------------------------------------ device-side generation
+# The full-size layer shapes are generated on the GPU with torch's seeded Philox
+# generator (same distributions, bf16 by round-to-nearest-even conversion): host
+# generation of ~1e9 values is too slow to sit in a test.  The oracle then reads
+# back only the rows it samples.
+def device_case(name, *, seed, lens, has_init, H_qk, H_v, d_k, d_v, num_slots, slot=None,
+                pool_sigma=0.1, scale=None, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    N = len(lens)
+    T = int(lens.sum())
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    width = 2 * H_qk * d_k + H_v * d_v
+    mixed = torch.empty((T, width), dtype=torch.bfloat16, device=device)
+    step = 4096
+    for r0 in range(0, T, step):                       # bounded fp32 temporaries
+        r1 = min(T, r0 + step)
+        mixed[r0:r1] = torch.randn((r1 - r0, width), generator=g, device=device).to(torch.bfloat16)
+    a = torch.randn((T, H_v), generator=g, device=device).to(torch.bfloat16)
+    b = torch.randn((T, H_v), generator=g, device=device).to(torch.bfloat16)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=H_v)).astype(np.float32)
+    dt_bias = _normal(rng, (H_v,), 0.5)
+    if slot is None:
+        slot = rng.permutation(num_slots)[:N].astype(np.int32)
+    has_init = np.broadcast_to(np.asarray(has_init, dtype=np.int32), (N,)).copy()
+    return GDNCase(name=name, dtype="bf16", H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v,
+                   scale=float(d_k) ** -0.5 if scale is None else float(scale), mixed_qkv=mixed,
+                   a=a, b=b, A_log=A_log, dt_bias=dt_bias, cu_seqlens=cu,
+                   slot=np.asarray(slot, np.int32), has_init=has_init, num_slots=int(num_slots),
+                   pool=None, pool_sigma=pool_sigma, pool_seed=int(rng.integers(0, 2**31 - 1)))
+
+
+def device_pool(case: GDNCase, device="cuda"):
+    """fp32 pool [num_slots, H_v, d_v, d_k] ~ N(0, pool_sigma), filled on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(case.pool_seed)
+    shape = (case.num_slots, case.H_v, case.d_v, case.d_k)
+    pool = torch.empty(shape, dtype=torch.float32, device=device)
+    for s0 in range(0, case.num_slots, 64):
+        s1 = min(case.num_slots, s0 + 64)
+        pool[s0:s1] = torch.randn((s1 - s0,) + shape[1:], generator=g, device=device) * case.pool_sigma
+    return pool
+
+
+def device_config1_decode(seed: int = 1001, device="cuda"):
+    rng = np.random.default_rng(seed + 7)
+    slot = rng.choice(1024, size=256, replace=False).astype(np.int32)
+    return device_case("decode-256", seed=seed, lens=np.ones(256, np.int64), has_init=1,
+                       H_qk=16, H_v=32, d_k=128, d_v=128, num_slots=1024, slot=slot,
+                       pool_sigma=0.05, device=device)
+
+
+def device_config2_prefill(seed: int = 1002, device="cuda"):
+    return device_case("prefill-8x4096", seed=seed, lens=[4096] * 8, has_init=0, H_qk=16,
+                       H_v=32, d_k=128, d_v=128, num_slots=16, device=device)
+
+
+def device_config3_ragged(seed: int = 1003, device="cuda"):
+    lens = ragged_lengths(seed)
+    rng = np.random.default_rng(seed + 11)
+    perm = rng.permutation(512).astype(np.int32)
+    return device_case("ragged-64", seed=seed, lens=lens, has_init=1, H_qk=16, H_v=32, d_k=128,
+                       d_v=128, num_slots=512, slot=perm[:64], device=device)
+
+
+def device_config3_verify(seed: int = 1003, device="cuda"):
+    rng = np.random.default_rng(seed + 11)
+    perm = rng.permutation(512).astype(np.int32)
+    return device_case("verify-32x4", seed=seed + 100, lens=[4] * 32, has_init=1, H_qk=16,
+                       H_v=32, d_k=128, d_v=128, num_slots=512, slot=perm[64:96], device=device)
+
+
+def device_config4_ssd(seed: int = 1004, batch=2, L=8192, H=80, P=64, G=1, Nst=128, device="cuda"):
+    """Mamba2-shaped delta-off inputs as torch tensors on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    rng = np.random.default_rng(seed)
+
+    def bf(shape):
+        return torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+
+    x = bf((batch, L, H, P))
+    dt = bf((batch, L, H))
+    B = bf((batch, L, G, Nst))
+    C = bf((batch, L, G, Nst))
+    D = bf((H,))
+    z = bf((batch, L, H, P))
+    A = torch.from_numpy((-rng.uniform(1.0, 16.0, size=H)).astype(np.float32)).to(device)
+    dt_bias = torch.from_numpy(_normal(rng, (H,), 0.5)).to(device)
+    return SSDCase(name=f"ssd-{batch}x{L}x{H}x{P}", x=x, dt=dt, A=A, B=B, C=C, D=D, z=z,
+                   dt_bias=dt_bias, dt_softplus=True, dt_limit=(0.0, float("inf")),
+                   initial_states=None)

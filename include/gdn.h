@@ -1,0 +1,195 @@
+/* gdn.h -- C ABI of libgdn.so, the MI355X (gfx950) GDN linear-attention layer.
+ *
+ * The layer is the Gated DeltaNet ("gated delta rule") linear attention that a
+ * hybrid full-attention + GDN model reaches through
+ * HybridAttnBackend.forward_gdn(layer, forward_batch, mixed_qkv, a, b)
+ * (pymllm.layers.attention.hybrid_backend API page, HybridAttnBackend.forward_gdn:
+ * "delegate GDN computation to the GDN backend").  The recurrence, per sequence and
+ * v-head, with q and k L2-normalised per head, is
+ *
+ *     S_t = g_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = scale S_t q_t
+ *     g_t = exp(-exp(A_log) softplus(a_t + dt_bias)),                beta_t = sigmoid(b_t)
+ *
+ * (Yang, Kautz & Hatamizadeh, Gated Delta Networks, ICLR 2025).  A delta-off mode
+ * computes the Mamba2 SSD scan of flashinfer.mamba.ssd_combined_fwd (parameter
+ * list of that page): S_t = exp(dt'_t A) S_{t-1} + dt'_t x_t B_t^T,
+ * y_t = S_t C_t + D x_t, out_t = y_t silu(z_t).
+ *
+ * Conventions shared by every call
+ *   - Every pointer in an args struct is DEVICE memory owned by the caller.  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream) and the call returns at once.
+ *   - Strides and sizes are in elements, not bytes.  Within a token, heads are
+ *     contiguous: element (t, head, i) of q is q[t * q_stride + head * d_k + i].
+ *   - Host-side validation runs first; on any error the call returns a nonzero
+ *     gdn_status, launches nothing and touches no buffer.  A failed launch returns
+ *     GDN_E_HIP; gdn_last_hip_error() then gives the hipError_t (per thread).
+ *   - Device-resident index data (cu_seqlens, slot, has_init) is trusted: checking
+ *     it would need a host synchronisation.  Out-of-range or duplicate slots are
+ *     undefined behaviour; gdn_validate_slots() is the opt-in device-side check.
+ *   - A negative slot disables its sequence: no output row and no pool slot is
+ *     touched (after the "negative entries disable" rule of the checkpoint
+ *     arguments on the flashinfer.mamba.ssd_combined_fwd page).
+ *   - Two calls that write the same pool slot must be ordered by the caller.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_E_NULL = 1,        /* a required pointer is NULL                        */
+  GDN_E_SHAPE = 2,       /* inconsistent sizes / strides                      */
+  GDN_E_DTYPE = 3,       /* unsupported dtype combination                     */
+  GDN_E_UNSUPPORTED = 4, /* valid request this build has no kernel for        */
+  GDN_E_INDEX = 5,       /* index argument out of range (host-checkable ones) */
+  GDN_E_HIP = 6          /* the HIP runtime reported an error at launch        */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+enum { GDN_MODE_GDN = 0, GDN_MODE_SSD = 1 };
+
+/* ---------------------------------------------------------------- gdn_gate
+ * a, b -> log g, beta for every (token, head).
+ *   GDN mode: log_g = -exp(A[h]) * softplus(a[t,h] + dt_bias[h]); beta = sigmoid(b[t,h]).
+ *             A holds A_log.  dt_softplus, dt_min, dt_max are ignored.
+ *   SSD mode: dt' = a[t,h] + dt_bias[h], softplus'd when dt_softplus != 0, then
+ *             clamped to [dt_min, dt_max] (inclusive, ssd_combined_fwd dt_limit);
+ *             log_g = dt' * A[h] (A < 0); beta = dt'.  b must be NULL.
+ * The decay is returned as log g (<= 0, fp32) because the chunked extend works with
+ * in-chunk cumulative sums of it; g = exp(log_g).
+ * Outputs log_g and beta are fp32 [T, H], row stride H (contiguous).  dt_bias may
+ * be NULL (zero bias).  T = 0 is a no-op. */
+typedef struct gdn_gate_args {
+  int32_t mode;          /* GDN_MODE_GDN | GDN_MODE_SSD                 */
+  int32_t in_dtype;      /* gdn_dtype of a and b                        */
+  int64_t T;             /* tokens                                      */
+  int32_t H;             /* heads (v-heads)                             */
+  int32_t _pad0;
+  const void* a;         /* [T, H], row stride a_stride (GDN: a; SSD: dt) */
+  int64_t a_stride;
+  const void* b;         /* [T, H], row stride b_stride (GDN only)      */
+  int64_t b_stride;
+  const float* A;        /* [H] fp32: GDN A_log, SSD A                  */
+  const float* dt_bias;  /* [H] fp32 or NULL                            */
+  int32_t dt_softplus;   /* SSD only                                    */
+  float dt_min, dt_max;  /* SSD only; use 0 and +inf for "no limit"     */
+  int32_t _pad1;
+  float* log_g;          /* out [T, H] fp32                             */
+  float* beta;           /* out [T, H] fp32                             */
+} gdn_gate_args;
+
+/* ---------------------------------------------------------------- gdn_extend
+ * Packed-varlen prefill / extend.  Sequence n owns tokens [cu_seqlens[n],
+ * cu_seqlens[n+1]) (cu_seqlens[0] = 0, non-decreasing, last = T).  It starts from
+ * pool[slot[n]] when has_init[n] != 0 (has_init NULL = all 1) and from zeros
+ * otherwise, and writes its final state to pool[slot[n]] -- also for a
+ * zero-length sequence, which writes its start state back.  slot[n] < 0 skips it.
+ *
+ *   q, k : [T, H_qk, d_k] (token stride q_stride / k_stride, heads contiguous)
+ *   v    : [T, H_v, d_v]  (token stride v_stride)
+ *   log_g, beta : [T, H_v] fp32 from gdn_gate
+ *   pool : fp32 [num_slots, H_v, d_v, d_k] -- one [d_v, d_k] matrix S per
+ *          (slot, v-head), d_k fastest; read and written in place
+ *   out  : [T, H_v, d_v] in out_dtype (token stride out_stride), RNE rounding
+ * v-head h reads qk-head h / (H_v / H_qk).  GDN mode L2-normalises q and k
+ * (q / sqrt(|q|^2 + 1e-6)) and uses `scale`; SSD mode does not normalise, ignores
+ * scale (1), and applies the D skip (D_per_dim ? D[h, i] : D[h]) and the silu(z)
+ * gate when D / z are non-NULL (D and z in in_dtype, z laid out like v).
+ * In SSD mode q = C, k = B (H_qk = ngroups, d_k = dstate), v = x (d_v = headdim),
+ * log_g / beta from gdn_gate in SSD mode.
+ *
+ * Supported: d_k, d_v in {64, 128}; H_v % H_qk == 0; in_dtype bf16 or fp32 with
+ * out_dtype bf16 or fp32.  chunk: 0 (default) or 64; bf16 inputs use the chunked
+ * MFMA kernel (chunk 64), fp32 inputs and short batches (max_seqlen in 1..8) the
+ * token-recurrent kernel.  max_seqlen is a host-side hint (an upper bound of the
+ * longest sequence, 0 = unknown); a wrong hint changes speed, never results. */
+typedef struct gdn_extend_args {
+  int32_t mode;          /* GDN_MODE_GDN | GDN_MODE_SSD          */
+  int32_t in_dtype;      /* q, k, v (and D, z)                   */
+  int32_t out_dtype;
+  int32_t N;             /* sequences                            */
+  int64_t T;             /* packed tokens                        */
+  int32_t H_qk, H_v, d_k, d_v;
+  int32_t chunk;         /* 0 = default                          */
+  int32_t max_seqlen;    /* hint, 0 = unknown                    */
+  const void* q;
+  int64_t q_stride;
+  const void* k;
+  int64_t k_stride;
+  const void* v;
+  int64_t v_stride;
+  const float* log_g;
+  const float* beta;
+  const int32_t* cu_seqlens; /* [N+1]                            */
+  const int32_t* slot;       /* [N]                              */
+  const int32_t* has_init;   /* [N] or NULL                      */
+  float* pool;
+  int64_t num_slots;
+  void* out;
+  int64_t out_stride;
+  float scale;
+  int32_t D_per_dim;
+  const void* D;         /* SSD only, or NULL                    */
+  const void* z;         /* SSD only, or NULL                    */
+  int64_t z_stride;
+} gdn_extend_args;
+
+/* ---------------------------------------------------------------- gdn_decode
+ * One token per sequence: token b belongs to sequence b, which always starts from
+ * pool[slot[b]] and writes it back in place (state read-modify-write).  slot[b] < 0
+ * marks a padding row: its output row and every pool slot stay untouched.
+ * Layouts as gdn_extend with T = B; log_g / beta are [B, H_v].  GDN mode only. */
+typedef struct gdn_decode_args {
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t B;
+  int32_t H_qk, H_v, d_k, d_v;
+  int32_t _pad0;
+  const void* q;
+  int64_t q_stride;
+  const void* k;
+  int64_t k_stride;
+  const void* v;
+  int64_t v_stride;
+  const float* log_g;
+  const float* beta;
+  const int32_t* slot;   /* [B] */
+  float* pool;
+  int64_t num_slots;
+  void* out;
+  int64_t out_stride;
+  float scale;
+  int32_t _pad1;
+} gdn_decode_args;
+
+/* `stream` is a hipStream_t passed as void* so this header needs no HIP include. */
+int gdn_gate(const gdn_gate_args* args, void* stream);
+int gdn_extend(const gdn_extend_args* args, void* stream);
+int gdn_decode(const gdn_decode_args* args, void* stream);
+
+/* Device-side check of slot[0..n): *flag (device int32) receives 0 when every
+ * non-negative slot is < num_slots and no non-negative slot repeats, 1 when one
+ * is out of range, 2 when one repeats (3 when both).  Negative slots are padding
+ * and may repeat.  Asynchronous like the others; O(n^2) comparisons. */
+int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
+                       void* stream);
+
+const char* gdn_status_str(int status);
+int gdn_last_hip_error(void);
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,224 @@
+"""Host-side tests of the C-ABI library and the Python binding (no GPU needed).
+
+The library is loaded and its error conventions are exercised with arguments
+that fail validation, so nothing is ever launched.  The forward_gdn adapter is
+tested with mocked library calls (spy technique of the SGLang GDN test-matrix
+article, section "Hybrid dispatch fan-out tests": sentinel identity, not exact
+argument shapes)."""
+import ctypes as ct
+import os
+import re
+import subprocess
+import tempfile
+from types import SimpleNamespace
+from unittest import mock
+
+import pytest
+import torch
+
+import hybrid_model_linear_amd as gdn
+from hybrid_model_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load()
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gdn_abi_version() == _lib.ABI_VERSION
+
+
+def test_struct_layouts_match_header():
+    """offsetof/sizeof from the C compiler == ctypes layout used by the binding."""
+    structs = {"gdn_gate_args": _lib.GateArgs, "gdn_extend_args": _lib.ExtendArgs,
+               "gdn_decode_args": _lib.DecodeArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void){']
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-o", exe, src], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ct.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def _ext(**kw):
+    base = dict(mode=0, in_dtype=1, out_dtype=1, N=1, T=4, H_qk=2, H_v=4, d_k=128, d_v=128,
+                chunk=0, max_seqlen=0, q_stride=2 * 2 * 128 + 4 * 128, k_stride=2 * 2 * 128 + 4 * 128,
+                v_stride=2 * 2 * 128 + 4 * 128, num_slots=8, out_stride=4 * 128, scale=0.088)
+    base.update(kw)
+    return _lib.ExtendArgs(**base)
+
+
+FAKE = ct.c_void_p(0x1000)   # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), _lib.GDN_E_NULL),                                   # q/k/v/... are NULL
+    (dict(H_v=3), _lib.GDN_E_SHAPE),                             # H_v % H_qk
+    (dict(d_k=96), _lib.GDN_E_UNSUPPORTED),
+    (dict(d_v=32), _lib.GDN_E_UNSUPPORTED),
+    (dict(in_dtype=7), _lib.GDN_E_DTYPE),
+    (dict(chunk=128), _lib.GDN_E_UNSUPPORTED),
+    (dict(mode=5), _lib.GDN_E_UNSUPPORTED),
+    (dict(q_stride=100), _lib.GDN_E_SHAPE),
+    (dict(out_stride=100), _lib.GDN_E_SHAPE),
+    (dict(num_slots=0), _lib.GDN_E_SHAPE),
+    (dict(scale=float("nan")), _lib.GDN_E_SHAPE),
+    (dict(D=FAKE), _lib.GDN_E_SHAPE),                            # SSD-only input in GDN mode
+    (dict(N=-1), _lib.GDN_E_SHAPE),
+])
+def test_extend_validation(kw, status):
+    lib = gdn.load()
+    assert lib.gdn_extend(ct.byref(_ext(**kw)), None) == status
+
+
+def test_extend_null_and_empty():
+    lib = gdn.load()
+    assert lib.gdn_extend(None, None) == _lib.GDN_E_NULL
+    assert lib.gdn_extend(ct.byref(_ext(N=0)), None) == _lib.GDN_OK      # nothing to do
+    a = _ext(cu_seqlens=FAKE, slot=FAKE, pool=FAKE)                      # q..out missing
+    assert lib.gdn_extend(ct.byref(a), None) == _lib.GDN_E_NULL
+
+
+def test_gate_and_decode_validation():
+    lib = gdn.load()
+    g = _lib.GateArgs(mode=0, in_dtype=1, T=0, H=4)
+    assert lib.gdn_gate(ct.byref(g), None) == _lib.GDN_OK              # T = 0 is a no-op
+    g = _lib.GateArgs(mode=0, in_dtype=1, T=3, H=4)
+    assert lib.gdn_gate(ct.byref(g), None) == _lib.GDN_E_NULL
+    g = _lib.GateArgs(mode=1, in_dtype=1, T=3, H=4, a=FAKE, a_stride=4, A=FAKE, log_g=FAKE,
+                      beta=FAKE, b=FAKE, b_stride=4)
+    assert lib.gdn_gate(ct.byref(g), None) == _lib.GDN_E_SHAPE         # b given in SSD mode
+    g = _lib.GateArgs(mode=1, in_dtype=1, T=3, H=4, a=FAKE, a_stride=4, A=FAKE, log_g=FAKE,
+                      beta=FAKE, dt_min=2.0, dt_max=1.0)
+    assert lib.gdn_gate(ct.byref(g), None) == _lib.GDN_E_SHAPE         # empty clamp range
+    g = _lib.GateArgs(mode=0, in_dtype=1, T=3, H=4, a=FAKE, a_stride=2, A=FAKE, log_g=FAKE,
+                      beta=FAKE, b=FAKE, b_stride=4)
+    assert lib.gdn_gate(ct.byref(g), None) == _lib.GDN_E_SHAPE         # row stride < H
+    d = _lib.DecodeArgs(in_dtype=1, out_dtype=1, B=2, H_qk=2, H_v=4, d_k=128, d_v=128,
+                        q_stride=1024, k_stride=1024, v_stride=1024, num_slots=4, out_stride=512,
+                        scale=0.1)
+    assert lib.gdn_decode(ct.byref(d), None) == _lib.GDN_E_NULL
+    d.B = 0
+    assert lib.gdn_decode(ct.byref(d), None) == _lib.GDN_OK
+    d.B, d.H_v = 2, 5
+    assert lib.gdn_decode(ct.byref(d), None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_validate_slots(None, 3, 4, None, None) == _lib.GDN_E_NULL
+    assert lib.gdn_validate_slots(None, 3, 4, FAKE, None) == _lib.GDN_E_NULL
+    assert lib.gdn_validate_slots(None, -1, 4, FAKE, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_status_str(_lib.GDN_E_HIP) == b"HIP runtime error"
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gdn.gate(q[:, :, 0], q[:, :, 1], torch.zeros(2), torch.zeros(2))
+
+
+# ------------------------------------------------------------------ forward_gdn dispatch
+class _Mode:
+    def __init__(self, name):
+        self.name = name
+
+    def is_decode_or_idle(self):
+        return self.name in ("DECODE", "IDLE")
+
+    def is_extend(self, include_draft_extend_v2=False):
+        fam = {"EXTEND", "MIXED", "DRAFT_EXTEND", "TARGET_VERIFY", "SPLIT_PREFILL", "DLLM_EXTEND"}
+        return self.name in fam or (include_draft_extend_v2 and self.name == "DRAFT_EXTEND_V2")
+
+    def __repr__(self):
+        return f"ForwardMode.{self.name}"
+
+
+@pytest.mark.parametrize("mode,kind", [("DECODE", "decode"), ("IDLE", "decode"),
+                                       ("EXTEND", "extend"), ("MIXED", "extend"),
+                                       ("DRAFT_EXTEND", "extend"), ("DRAFT_EXTEND_V2", "extend"),
+                                       ("TARGET_VERIFY", "extend"), ("SPLIT_PREFILL", "extend"),
+                                       ("DLLM_EXTEND", "extend"), ("decode", "decode"),
+                                       ("target_verify", "extend")])
+def test_mode_kind(mode, kind):
+    m = _Mode(mode) if mode.isupper() else mode
+    assert gdn._mode_kind(m) == kind
+
+
+@pytest.mark.parametrize("mode", [_Mode("DUMMY_FIRST"), "prefill_only", 3])
+def test_mode_kind_rejects(mode):
+    with pytest.raises(ValueError, match="Invalid forward mode"):
+        gdn._mode_kind(mode)
+
+
+def _layer():
+    return SimpleNamespace(num_k_heads=2, num_v_heads=4, head_k_dim=128, head_v_dim=128,
+                           A_log=object(), dt_bias=object(), scale=None, layer_id=3)
+
+
+@pytest.mark.parametrize("mode,expect", [("DECODE", "decode"), ("TARGET_VERIFY", "extend"),
+                                         ("EXTEND", "extend")])
+def test_forward_gdn_routes_by_mode(mode, expect):
+    T = 5
+    mixed = torch.zeros(T, 2 * 2 * 128 + 4 * 128)
+    a, b = torch.zeros(T, 4), torch.zeros(T, 4)
+    pool, slots, cu, hi = object(), object(), object(), object()
+    fb = SimpleNamespace(forward_mode=_Mode(mode), state_pool={3: pool}, state_slots=slots,
+                         cu_seqlens=cu, has_initial_state=hi, max_seqlen=7)
+    lg, bt = object(), object()
+    out = torch.zeros(T, 4, 128)
+    with mock.patch.object(gdn, "gate", return_value=(lg, bt)) as mg, \
+            mock.patch.object(gdn, "decode", return_value=out) as md, \
+            mock.patch.object(gdn, "extend", return_value=out) as me:
+        res = gdn.forward_gdn(_layer(), fb, mixed, a, b)
+    assert res.shape == (T, 512)
+    mg.assert_called_once()
+    assert mg.call_args.args[0] is a and mg.call_args.args[1] is b
+    called, other = (md, me) if expect == "decode" else (me, md)
+    called.assert_called_once()
+    other.assert_not_called()
+    sent = list(called.call_args.args) + list(called.call_args.kwargs.values())
+    assert any(x is pool for x in sent) and any(x is slots for x in sent)
+    assert any(x is lg for x in sent) and any(x is bt for x in sent)
+    if expect == "extend":
+        assert any(x is cu for x in sent) and any(x is hi for x in sent)
+        assert called.call_args.kwargs["max_seqlen"] == 7
+    # q, k, v are views of mixed_qkv, not copies
+    q, k, v = called.call_args.args[:3]
+    assert q.data_ptr() == mixed.data_ptr()
+    assert k.data_ptr() == mixed.data_ptr() + 2 * 128 * mixed.element_size()
+    assert v.data_ptr() == mixed.data_ptr() + 4 * 128 * mixed.element_size()
+
+
+def test_forward_gdn_invalid_mode_raises_before_any_call():
+    fb = SimpleNamespace(forward_mode=_Mode("DUMMY_FIRST"))
+    with mock.patch.object(gdn, "gate") as mg:
+        with pytest.raises(ValueError, match="Invalid forward mode"):
+            gdn.forward_gdn(_layer(), fb, torch.zeros(1, 1024), torch.zeros(1, 4), torch.zeros(1, 4))
+    mg.assert_not_called()
+
+
+def test_ssd_combined_rejects_unsupported_arguments():
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(NotImplementedError):
+        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, seq_idx=torch.zeros(1, 4))
+    with pytest.raises(NotImplementedError):
+        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, checkpoint_states=x)

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: slot / index handling bit-exact (untouched pool slots and skipped rows keep
+their bytes); outputs and final states within rel-L2 <= 2e-3 and max-abs <= 1e-2
+of the float64 oracle for bf16 inputs with fp32 state.  fp32 paths are held to a
+much tighter bound as a regression guard.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_model_linear_amd import synth
+from gpu_util import assert_close, host_rows, oracle_seq, rel_l2, run_extend, upload
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -12345.0
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ gate
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gate_parity(gdn_lib, dtype):
+    gdn = gdn_lib
+    _announce(f"gate {dtype}")
+    rng = np.random.default_rng(11)
+    T, H = 1000, 32
+    a = rng.standard_normal((T, H)).astype(np.float32) * 4
+    b = rng.standard_normal((T, H)).astype(np.float32) * 8
+    a[0, :4] = [-80.0, 80.0, 0.0, 30.0]
+    b[0, :4] = [-90.0, 90.0, 0.0, 1e-3]
+    if dtype == "bf16":
+        a, b = synth.bf16_round(a), synth.bf16_round(b)
+    A_log = np.log(rng.uniform(1, 16, H)).astype(np.float32)
+    bias = (rng.standard_normal(H) * 0.5).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ta = torch.from_numpy(a).to("cuda", tdt)
+    tb = torch.from_numpy(b).to("cuda", tdt)
+    lg, bt = gdn.gate(ta, tb, torch.from_numpy(A_log).cuda(), torch.from_numpy(bias).cuda())
+    rlg, rbt = oracle.gdn_gate(a, b, A_log, bias)
+    lg, bt = lg.cpu().numpy(), bt.cpu().numpy()
+    assert np.allclose(lg, rlg, rtol=2e-6, atol=1e-7), np.max(np.abs(lg - rlg) / (np.abs(rlg) + 1e-7))
+    assert np.allclose(bt, rbt, rtol=2e-6, atol=1e-7)
+    # ssd mode with a clamp
+    dt = synth.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    A = (-rng.uniform(1, 16, H)).astype(np.float32)
+    for sp, lim in ((True, (0.0, float("inf"))), (False, (0.05, 0.5)), (True, (0.2, 1.5))):
+        lg, dtp = gdn.ssd_gate(torch.from_numpy(dt).to("cuda", torch.bfloat16), torch.from_numpy(A).cuda(),
+                               torch.from_numpy(bias).cuda(), sp, lim)
+        rlg, rdt = oracle.ssd_gate(dt, A, bias, sp, lim)
+        assert np.allclose(dtp.cpu().numpy(), rdt, rtol=2e-6, atol=1e-7)
+        assert np.allclose(lg.cpu().numpy(), rlg, rtol=2e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ tiny fp32 (extend + decode)
+def test_config0_tiny_fp32_extend_then_decode(gdn_lib):
+    gdn = gdn_lib
+    _announce("config0 tiny fp32")
+    ext, dec = synth.config0_tiny()
+    d = upload(ext)
+    pool_before = d["pool"].clone()
+    out = run_extend(gdn, ext, d)
+    ref, written, fin = oracle.gdn_extend(ext.q, ext.k, ext.v, ext.a, ext.b, ext.A_log, ext.dt_bias,
+                                          ext.cu_seqlens, ext.slot, ext.has_init, ext.pool, ext.scale)
+    assert_close(out.cpu().numpy(), ref, "extend out", rel=1e-5, mx=1e-5)
+    pool1 = oracle.apply_final_states(ext.pool, fin)
+    got_pool = d["pool"].cpu().numpy()
+    assert_close(got_pool[ext.slot], pool1[ext.slot], "extend states", rel=1e-5, mx=1e-5)
+    untouched = np.setdiff1d(np.arange(ext.num_slots), ext.slot)
+    assert torch.equal(d["pool"][untouched], pool_before[untouched])
+    # one decode token per sequence from the extend's states
+    dd = upload(dec, pool=d["pool"])
+    q, k, v = gdn.split_mixed_qkv(dd["mixed"], 2, 2, 64, 64)
+    lg, bt = gdn.gate(dd["a"], dd["b"], dd["A_log"], dd["dt_bias"])
+    o = gdn.decode(q, k, v, lg, bt, dd["slot"], dd["pool"], scale=dec.scale)
+    ref2, _, fin2 = oracle.gdn_decode(dec.q, dec.k, dec.v, dec.a, dec.b, dec.A_log, dec.dt_bias,
+                                      dec.slot, pool1, dec.scale)
+    assert_close(o.cpu().numpy(), ref2, "decode out", rel=1e-5, mx=1e-5)
+    pool2 = oracle.apply_final_states(pool1, fin2)
+    assert_close(d["pool"].cpu().numpy()[dec.slot], pool2[dec.slot], "decode states", rel=1e-5, mx=1e-5)
+
+
+# ------------------------------------------------------------------ bf16 extend edge shapes
+EDGE = [
+    ("ragged-page", (15, 8, 1), (0, 1, 1)),
+    ("exact-page", (16,), (0,)),
+    ("chunk-boundary", (64, 65, 129), (0, 1, 1)),
+    ("lengths", (1, 63, 64, 65, 127, 128, 129), (1, 0, 1, 0, 1, 0, 1)),
+    ("batch1-long", (300,), (1,)),
+    ("with-empty", (5, 0, 70, 0, 1), (1, 1, 0, 0, 1)),
+]
+
+
+@pytest.mark.parametrize("name,lens,has_init", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_extend_edges(gdn_lib, name, lens, has_init, out_dtype):
+    gdn = gdn_lib
+    _announce(f"extend edge {name} out={out_dtype}")
+    case = synth.edge_case(name, lens, has_init=has_init, seed=sum(lens) + 3, num_slots=2 * len(lens) + 3)
+    d = upload(case)
+    pool_before = d["pool"].clone()
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.full((case.T, case.H_v, case.d_v), SENTINEL, dtype=odt, device="cuda")
+    run_extend(gdn, case, d, out=out)
+    torch.cuda.synchronize()
+    ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
+                                          case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
+                                          case.pool, case.scale)
+    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (2e-4, 2e-3)
+    if case.T:
+        assert_close(out.float().cpu().numpy(), ref, "out", *bar)
+    newpool = oracle.apply_final_states(case.pool, fin)
+    assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", 2e-3 if out_dtype == "bf16" else 2e-4, 1e-2)
+    untouched = np.setdiff1d(np.arange(case.num_slots), case.slot)
+    assert torch.equal(d["pool"][untouched], pool_before[untouched]), "untouched slots changed"
+
+
+def test_skipped_sequences_and_sentinels(gdn_lib):
+    gdn = gdn_lib
+    _announce("skipped sequences")
+    case = synth.edge_case("skip", (20, 70, 3, 66), has_init=(1, 1, 0, 1), seed=5, num_slots=9)
+    case.slot[:] = [4, -1, 7, -1]
+    d = upload(case)
+    pool_before = d["pool"].clone()
+    out = torch.full((case.T, case.H_v, case.d_v), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    run_extend(gdn, case, d, out=out)
+    ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
+                                          case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
+                                          case.pool, case.scale)
+    o = out.float().cpu().numpy()
+    assert (o[~written] == SENTINEL).all(), "rows of skipped sequences were written"
+    assert_close(o[written], ref[written], "out")
+    keep = np.setdiff1d(np.arange(9), [4, 7])
+    assert torch.equal(d["pool"][keep], pool_before[keep])
+    got = d["pool"].cpu().numpy()
+    assert_close(got[[4, 7]], np.stack([fin[4], fin[7]]), "states")
+
+
+def test_has_init_zero_ignores_pool_content(gdn_lib):
+    gdn = gdn_lib
+    _announce("has_init=0 ignores pool")
+    case = synth.edge_case("noinit", (40, 90), has_init=(0, 0), seed=9, num_slots=4)
+    d = upload(case)
+    d["pool"].fill_(float("nan"))
+    out = run_extend(gdn, case, d)
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init,
+                                    np.zeros_like(case.pool), case.scale)
+    assert_close(out.float().cpu().numpy(), ref, "out")
+    assert_close(d["pool"].cpu().numpy()[case.slot], np.stack([fin[s] for s in case.slot]), "states")
+
+
+@pytest.mark.parametrize("cut", [1, 37, 64, 100, 128])
+def test_split_resume(gdn_lib, cut):
+    """extend(A||B) == extend(A) then extend(B), and == extend(A) then decode per token."""
+    gdn = gdn_lib
+    _announce(f"split/resume cut={cut}")
+    L = 150
+    case = synth.edge_case("split", (L,), has_init=(1,), seed=21, num_slots=3)
+    full = upload(case)
+    out_full = run_extend(gdn, case, full, out_dtype=torch.float32)
+    # A then B
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    one = torch.ones(1, dtype=torch.int32, device="cuda")
+    oA = gdn.extend(q[:cut], k[:cut], v[:cut], lg[:cut].contiguous(), bt[:cut].contiguous(),
+                    torch.tensor([0, cut], dtype=torch.int32, device="cuda"), d["slot"], d["pool"],
+                    has_init=one, scale=case.scale, out_dtype=torch.float32)
+    oB = gdn.extend(q[cut:], k[cut:], v[cut:], lg[cut:].contiguous(), bt[cut:].contiguous(),
+                    torch.tensor([0, L - cut], dtype=torch.int32, device="cuda"), d["slot"], d["pool"],
+                    has_init=one, scale=case.scale, out_dtype=torch.float32)
+    got = torch.cat([oA, oB]).cpu().numpy()
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale)
+    assert_close(got, ref, "A|B out", 2e-4, 2e-3)
+    assert_close(d["pool"].cpu().numpy()[case.slot[0]], fin[case.slot[0]], "A|B state", 2e-4, 2e-3)
+    assert rel_l2(got, out_full.cpu().numpy()) < 2e-4
+    # A then per-token decode
+    d2 = upload(case)
+    gdn.extend(q[:cut], k[:cut], v[:cut], lg[:cut].contiguous(), bt[:cut].contiguous(),
+               torch.tensor([0, cut], dtype=torch.int32, device="cuda"), d2["slot"], d2["pool"],
+               has_init=one, scale=case.scale, out_dtype=torch.float32)
+    outs = []
+    for t in range(cut, min(L, cut + 12)):
+        outs.append(gdn.decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], lg[t:t + 1].contiguous(),
+                               bt[t:t + 1].contiguous(), d2["slot"], d2["pool"], scale=case.scale,
+                               out_dtype=torch.float32))
+    got2 = torch.cat(outs).cpu().numpy()
+    assert_close(got2, ref[cut:cut + len(outs)], "A|decode out", 2e-4, 2e-3)
+
+
+# ------------------------------------------------------------------ full-size configurations
+def test_config1_decode_full(gdn_lib):
+    gdn = gdn_lib
+    _announce("config1 decode 256 x [1024,32,128,128]")
+    case = synth.device_config1_decode()
+    pool = synth.device_pool(case)
+    d = upload(case, pool=pool)
+    before = pool.clone()
+    init = pool[torch.from_numpy(case.slot).long().cuda()].cpu().numpy()
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], 16, 32, 128, 128)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    out = gdn.decode(q, k, v, lg, bt, d["slot"], pool, scale=case.scale)
+    torch.cuda.synchronize()
+    mixed = host_rows(case.mixed_qkv, 0, 256)
+    nq = 16 * 128
+    ref, _, fin = oracle.gdn_decode(mixed[:, :nq].reshape(256, 16, 128), mixed[:, nq:2 * nq].reshape(256, 16, 128),
+                                    mixed[:, 2 * nq:].reshape(256, 32, 128), host_rows(case.a, 0, 256),
+                                    host_rows(case.b, 0, 256), case.A_log, case.dt_bias,
+                                    np.arange(256), {i: init[i] for i in range(256)}, case.scale)
+    assert_close(out.float().cpu().numpy(), ref, "decode out")
+    got = pool[torch.from_numpy(case.slot).long().cuda()].cpu().numpy()
+    assert_close(got, np.stack([fin[i] for i in range(256)]), "decode states")
+    mask = torch.ones(1024, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(case.slot).long().cuda()] = False
+    assert torch.equal(pool[mask], before[mask]), "untouched slots changed"
+
+
+@pytest.mark.slow
+def test_config2_prefill_sampled(gdn_lib):
+    gdn = gdn_lib
+    _announce("config2 prefill 8x4096 (sampled oracle)")
+    case = synth.device_config2_prefill()
+    pool = synth.device_pool(case)
+    d = upload(case, pool=pool)
+    out = run_extend(gdn, case, d)
+    torch.cuda.synchronize()
+    heads = [0, 1, 17, 31]
+    for n in (0, 5):
+        t0, t1 = int(case.cu_seqlens[n]), int(case.cu_seqlens[n + 1])
+        ref, fin = oracle_seq(case, n, heads, None)
+        assert_close(out[t0:t1, heads].float().cpu().numpy(), ref, f"seq {n} out")
+        assert_close(pool[int(case.slot[n])][heads].cpu().numpy(), fin, f"seq {n} state")
+
+
+@pytest.mark.slow
+def test_config3_ragged_sampled_and_verify(gdn_lib):
+    gdn = gdn_lib
+    _announce("config3 ragged 64 seqs (sampled oracle) + verify 32x4")
+    case = synth.device_config3_ragged()
+    pool = synth.device_pool(case)
+    d = upload(case, pool=pool)
+    lens = np.diff(case.cu_seqlens)
+    picks = [int(np.argmax(lens)), int(np.argmin(lens)), 7, 40]
+    inits = {n: pool[int(case.slot[n])].cpu().numpy() for n in picks}
+    before = pool.clone()
+    out = run_extend(gdn, case, d, max_seqlen=int(lens.max()))
+    torch.cuda.synchronize()
+    heads = [0, 13, 31]
+    for n in picks:
+        t0, t1 = int(case.cu_seqlens[n]), int(case.cu_seqlens[n + 1])
+        ref, fin = oracle_seq(case, n, heads, inits[n])
+        assert_close(out[t0:t1, heads].float().cpu().numpy(), ref, f"seq {n} (len {t1 - t0}) out")
+        assert_close(pool[int(case.slot[n])][heads].cpu().numpy(), fin, f"seq {n} state")
+    mask = torch.ones(512, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(case.slot).long().cuda()] = False
+    assert torch.equal(pool[mask], before[mask])
+    # verify-style batch on other slots of the same pool
+    ver = synth.device_config3_verify()
+    dv = upload(ver, pool=pool)
+    vinit = {n: pool[int(ver.slot[n])].cpu().numpy() for n in range(32)}
+    vout = run_extend(gdn, ver, dv, max_seqlen=4)
+    torch.cuda.synchronize()
+    for n in (0, 9, 31):
+        ref, fin = oracle_seq(ver, n, list(range(32)), vinit[n])
+        assert_close(vout[4 * n:4 * n + 4].float().cpu().numpy(), ref, f"verify seq {n} out")
+        assert_close(pool[int(ver.slot[n])].cpu().numpy(), fin, f"verify seq {n} state")
+
+
+# ------------------------------------------------------------------ delta-off (SSD)
+@pytest.mark.parametrize("shape", [(2, 150, 6, 64, 2, 128, False), (1, 64, 4, 64, 1, 128, True),
+                                   (3, 33, 8, 64, 4, 128, True)])
+def test_ssd_small(gdn_lib, shape):
+    gdn = gdn_lib
+    batch, L, H, P, G, Nst, init = shape
+    _announce(f"ssd small {shape}")
+    c = synth.config4_ssd(seed=L + H, batch=batch, L=L, H=H, P=P, G=G, Nst=Nst, initial=init)
+    tb = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
+    tf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.float32)
+    out, fin = gdn.ssd_combined_fwd(tb(c.x), tb(c.dt), tf(c.A), tb(c.B), tb(c.C), tb(c.D), tb(c.z),
+                                    tf(c.dt_bias), True, (0.0, float("inf")),
+                                    None if c.initial_states is None else tf(c.initial_states))
+    ref, rfin = oracle.ssd_combined(c.x, c.dt, c.A, c.B, c.C, c.D, c.z, c.dt_bias, True,
+                                    (0.0, float("inf")), c.initial_states, True)
+    assert_close(out.float().cpu().numpy(), ref, "ssd out")
+    assert_close(fin.cpu().numpy(), rfin, "ssd states")
+
+
+@pytest.mark.slow
+def test_config4_ssd_sampled(gdn_lib):
+    gdn = gdn_lib
+    _announce("config4 ssd [2,8192,80,64] (sampled oracle)")
+    c = synth.device_config4_ssd()
+    out, fin = gdn.ssd_combined_fwd(c.x, c.dt, c.A, c.B, c.C, c.D, c.z, c.dt_bias, True,
+                                    (0.0, float("inf")))
+    torch.cuda.synchronize()
+    heads = [0, 41, 79]
+    h = lambda t: t.float().cpu().numpy()
+    ref, rfin = oracle.ssd_combined(h(c.x), h(c.dt), h(c.A), h(c.B), h(c.C), h(c.D), h(c.z),
+                                    h(c.dt_bias), True, (0.0, float("inf")), None, True, heads=heads)
+    assert_close(h(out[:, :, heads]), ref, "ssd out")
+    assert_close(h(fin[:, heads]), rfin, "ssd states")
+
+
+# ------------------------------------------------------------------ adapter and helpers
+def test_forward_gdn_end_to_end(gdn_lib):
+    gdn = gdn_lib
+    _announce("forward_gdn extend + decode")
+    from types import SimpleNamespace
+    case = synth.edge_case("fwd", (30, 70), has_init=(1, 0), seed=33, num_slots=6)
+    d = upload(case)
+    layer = SimpleNamespace(num_k_heads=case.H_qk, num_v_heads=case.H_v, head_k_dim=case.d_k,
+                            head_v_dim=case.d_v, A_log=d["A_log"], dt_bias=d["dt_bias"],
+                            scale=case.scale, layer_id=0)
+    fb = SimpleNamespace(forward_mode="extend", state_pool=[d["pool"]], state_slots=d["slot"],
+                         cu_seqlens=d["cu"], has_initial_state=d["has_init"], max_seqlen=70)
+    out = gdn.forward_gdn(layer, fb, d["mixed"], d["a"], d["b"])
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale)
+    assert out.shape == (case.T, case.H_v * case.d_v)
+    assert_close(out.float().cpu().numpy().reshape(ref.shape), ref, "forward_gdn extend")
+
+
+def test_validate_slots(gdn_lib):
+    gdn = gdn_lib
+    _announce("validate_slots")
+    s = lambda v: torch.tensor(v, dtype=torch.int32, device="cuda")
+    assert gdn.validate_slots(s([3, 1, -1, -1, 0]), 4) == 0
+    assert gdn.validate_slots(s([3, 4]), 4) == 1
+    assert gdn.validate_slots(s([2, 1, 2]), 4) == 2
+    assert gdn.validate_slots(s([9, 9]), 4) == 3
+    assert gdn.validate_slots(s([]), 4) == 0
