@@ -1,0 +1,214 @@
+#!/usr/bin/env python
+"""GDN layer throughput on one MI355X.
+
+One step = one pass of the whole GDN hot path on Qwen3-Next-shaped synthetic inputs
+(H_qk = 16, H_v = 32, d_k = d_v = 128, bf16 inputs, fp32 state pool):
+  prefill : gdn_gate + gdn_extend over 8 sequences x 4096 tokens (packed varlen,
+            zero initial states, final states into 8 slots of a 16-slot pool)
+  decode  : gdn_gate + gdn_decode for 256 sequences x 1 token, in place on a
+            [1024, 32, 128, 128] fp32 pool (256 slots touched)
+value = (32768 + 256) tokens / step time, inputs resident in HBM.
+
+Prints ONE JSON line.  `roofline` covers the kernel with the largest share of the
+step (per-launch time from HIP events recorded on the launch stream, which is
+torch's current stream); `cpu_baseline` times the CPU oracle on a bounded sample.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer tokens/s (extend, decode) on 1 MI355X; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+# algorithmic work per token at the Qwen3-Next shape (H_qk=16, H_v=32, d=128)
+H_QK, H_V, D = 16, 32, 128
+IO_BYTES_PER_TOKEN = 2 * H_QK * D * 2 + H_V * D * 2 + H_V * D * 2 + H_V * 8   # q,k + v + out + log_g,beta
+STATE_BYTES = H_V * D * D * 4                                                   # one slot, all heads
+CHUNK = 64
+EXTEND_FLOP_PER_TOKEN = H_QK * 4 * CHUNK * D + H_V * 2 * (CHUNK * D + 2 * CHUNK * D + 3 * D * D)
+GATE_BYTES_PER_TOKEN = H_V * (2 + 2 + 4 + 4)                                    # a, b -> log_g, beta
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this size (for counter scaling)")
+    return ap.parse_args()
+
+
+def cpu_baseline(ext, seconds):
+    """Oracle (float64, token by token, all 32 heads) on the first tokens of prefill
+    sequence 0, as many as fit in `seconds` of CPU time; tokens/s on one thread."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    n = 64
+    mixed = ext.mixed_qkv[:4096].float().cpu().numpy()
+    a = ext.a[:4096].float().cpu().numpy()
+    b = ext.b[:4096].float().cpu().numpy()
+    nq = H_QK * D
+    done, spent = 0, 0.0
+    S = np.zeros((1, H_V, D, D))
+    try:
+        while spent < seconds and done + n <= 4096:
+            sl = slice(done, done + n)
+            q = mixed[sl, :nq].reshape(n, H_QK, D)
+            k = mixed[sl, nq:2 * nq].reshape(n, H_QK, D)
+            v = mixed[sl, 2 * nq:].reshape(n, H_V, D)
+            t = time.perf_counter()
+            _, _, fin = oracle.gdn_extend(q, k, v, a[sl], b[sl], ext.A_log, ext.dt_bias,
+                                          np.array([0, n]), np.array([0]), np.array([int(done > 0)]),
+                                          S, ext.scale)
+            spent += time.perf_counter() - t
+            S = fin[0][None]
+            done += n
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": done / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle, prefill sequence 0 tokens [0, {done}) x all {H_V} heads "
+                      f"({spent:.1f} s, one thread)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer needs no collective; heads and "
+              f"sequences shard independently); --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hybrid_model_linear_amd as gdn
+    from hybrid_model_linear_amd import synth
+
+    gdn.load()
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    # ---------------- inputs (resident in HBM before timing)
+    ext = synth.device_config2_prefill()
+    dec = synth.device_config1_decode()
+    pool_e = synth.device_pool(ext)
+    pool_d = synth.device_pool(dec)
+
+    def prep(case):
+        q, k, v = gdn.split_mixed_qkv(case.mixed_qkv, case.H_qk, case.H_v, case.d_k, case.d_v)
+        t = lambda x, dt: torch.from_numpy(x).to(dev, dt)
+        return dict(q=q, k=k, v=v, a=case.a, b=case.b, A_log=t(case.A_log, torch.float32),
+                    dt_bias=t(case.dt_bias, torch.float32), cu=t(case.cu_seqlens, torch.int32),
+                    slot=t(case.slot, torch.int32), has_init=t(case.has_init, torch.int32),
+                    log_g=torch.empty((case.T, case.H_v), dtype=torch.float32, device=dev),
+                    beta=torch.empty((case.T, case.H_v), dtype=torch.float32, device=dev),
+                    out=torch.empty((case.T, case.H_v, case.d_v), dtype=torch.bfloat16, device=dev))
+    E, Dd = prep(ext), prep(dec)
+    T_e, T_d = ext.T, dec.T
+    maxlen = int(max(ext.cu_seqlens[1:] - ext.cu_seqlens[:-1]))
+
+    if args.calibrate_copy_mib:
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    names = ["gate_extend", "extend", "gate_decode", "decode"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        gdn.gate(E["a"], E["b"], E["A_log"], E["dt_bias"], log_g=E["log_g"], beta=E["beta"])
+        mark(1)
+        gdn.extend(E["q"], E["k"], E["v"], E["log_g"], E["beta"], E["cu"], E["slot"], pool_e,
+                   has_init=E["has_init"], scale=ext.scale, out=E["out"], max_seqlen=maxlen)
+        mark(2)
+        gdn.gate(Dd["a"], Dd["b"], Dd["A_log"], Dd["dt_bias"], log_g=Dd["log_g"], beta=Dd["beta"])
+        mark(3)
+        gdn.decode(Dd["q"], Dd["k"], Dd["v"], Dd["log_g"], Dd["beta"], Dd["slot"], pool_d,
+                   scale=dec.scale, out=Dd["out"])
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---------------- algorithmic work per launch
+    work = {
+        "gate_extend": dict(bytes=T_e * GATE_BYTES_PER_TOKEN, flop=0),
+        "extend": dict(bytes=T_e * IO_BYTES_PER_TOKEN + ext.N * STATE_BYTES,   # zero init: write only
+                       flop=T_e * EXTEND_FLOP_PER_TOKEN),
+        "gate_decode": dict(bytes=T_d * GATE_BYTES_PER_TOKEN, flop=0),
+        "decode": dict(bytes=T_d * (IO_BYTES_PER_TOKEN + 2 * STATE_BYTES), flop=T_d * 7 * H_V * D * D),
+    }
+    kernels = {}
+    for n in names:
+        sec = per[n] * 1e-3
+        gbs = work[n]["bytes"] / sec / 1e9
+        tfs = work[n]["flop"] / sec / 1e12
+        kernels[n] = {"avg_us": round(per[n] * 1e3, 2), "bytes": work[n]["bytes"],
+                      "flop": work[n]["flop"], "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 2),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+    dom = max(("extend", "decode"), key=lambda n: per[n])
+    kd = kernels[dom]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = work[dom]["flop"] / work[dom]["bytes"]
+    roofline = {"kernel": dom, "bound": "hbm" if ai < ridge else "mfma",
+                "achieved": kd["GB_s"] if ai < ridge else kd["TFLOP_s"],
+                "peak": HBM_PEAK_GBS if ai < ridge else MFMA_BF16_PEAK_TFLOPS,
+                "unit": "GB/s" if ai < ridge else "TFLOP/s",
+                "frac": kd["hbm_frac"] if ai < ridge else kd["mfma_frac"],
+                "traffic": None, "arith_intensity": round(ai, 1),
+                "mfma_frac": kd["mfma_frac"], "avg_launch_us": kd["avg_us"]}
+    tokens = T_e + T_d
+    result = {
+        "metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN layer step: extend 8x4096 (zero init) + decode 256x1 "
+                               "(pool [1024,32,128,128] fp32)",
+                   "H_qk": H_QK, "H_v": H_V, "d_k": D, "d_v": D, "chunk": CHUNK,
+                   "extend_tokens": T_e, "decode_tokens": T_d, "state": "fp32"},
+        "roofline": roofline,
+        "phases": {"extend_tokens_per_s": round(T_e / ((per["gate_extend"] + per["extend"]) * 1e-3), 1),
+                   "decode_tokens_per_s": round(T_d / ((per["gate_decode"] + per["decode"]) * 1e-3), 1)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(ext, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

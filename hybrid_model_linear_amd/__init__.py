@@ -307,14 +307,15 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
                      chunk_indices=None, chunk_offsets=None, seq_chunk_cumsum=None,
                      update_seq_chunk_cumsum=False, checkpoint_token_indices=None,
                      checkpoint_state_slots=None, checkpoint_states=None, out=None,
-                     return_final_states=True):
+                     return_final_states=True, out_dtype=None):
     """Batched-mode subset of flashinfer.mamba.ssd_combined_fwd on the delta-off kernels.
 
     x [batch, L, H, P] bf16; dt [batch, L, H]; A [H] fp32; B, C [batch, L, G, N];
     D [H] or [H, P]; z like x; initial_states [batch, H, P, N].  States are fp32.
     Returns (out [batch, L, H, P], final_states fp32 [batch, H, P, N] or None).
     The packed-varlen metadata, checkpoint capture and the caller-owned 5-D `out`
-    storage are not supported and raise NotImplementedError."""
+    storage are not supported and raise NotImplementedError.  out_dtype (an
+    extension) selects the output dtype; default x's dtype."""
     if any(t is not None for t in (seq_idx, chunk_indices, chunk_offsets, seq_chunk_cumsum,
                                    checkpoint_token_indices, checkpoint_state_slots,
                                    checkpoint_states, out)) or update_seq_chunk_cumsum:
@@ -338,5 +339,5 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     has_init = torch.full((batch,), int(initial_states is not None), dtype=torch.int32, device=dev)
     o = extend(C.view(T, G, Nst), B.view(T, G, Nst), x.view(T, H, P), log_g, dtp, cu, slot, pool,
                has_init=has_init, mode="ssd", D=D, z=None if z is None else z.view(T, H, P),
-               max_seqlen=L)
+               max_seqlen=L, out_dtype=out_dtype)
     return o.view(batch, L, H, P), (pool if return_final_states else None)

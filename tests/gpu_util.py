@@ -23,8 +23,13 @@ def assert_close(got, ref, what, rel=REL_L2, mx=MAX_ABS):
     assert np.isfinite(got).all(), f"{what}: non-finite values"
     r = rel_l2(got, ref)
     m = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    print(f"  {what}: rel-L2 {r:.3e}  max-abs {m:.3e}", flush=True)
-    assert r <= rel and m <= mx, f"{what}: rel-L2 {r:.3e} (<= {rel}) max-abs {m:.3e} (<= {mx})"
+    # The max-abs bound is absolute for tensors of order one (GDN outputs and states)
+    # and relative to the peak magnitude for larger ones (delta-off outputs reach
+    # |y| ~ 1e2, where one bf16 ulp alone exceeds 1e-2).
+    peak = float(np.max(np.abs(ref))) if ref.size else 0.0
+    mx_eff = mx * max(1.0, peak)
+    print(f"  {what}: rel-L2 {r:.3e}  max-abs {m:.3e} (bound {mx_eff:.3e}, peak {peak:.3e})", flush=True)
+    assert r <= rel and m <= mx_eff, f"{what}: rel-L2 {r:.3e} (<= {rel}) max-abs {m:.3e} (<= {mx_eff:.3e})"
     return r, m
 
 

@@ -110,11 +110,11 @@ def test_extend_edges(gdn_lib, name, lens, has_init, out_dtype):
     ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
                                           case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
                                           case.pool, case.scale)
-    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (2e-4, 2e-3)
+    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (1e-3, 2e-3)
     if case.T:
         assert_close(out.float().cpu().numpy(), ref, "out", *bar)
     newpool = oracle.apply_final_states(case.pool, fin)
-    assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", 2e-3 if out_dtype == "bf16" else 2e-4, 1e-2)
+    assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", 2e-3 if out_dtype == "bf16" else 1e-3, 1e-2)
     untouched = np.setdiff1d(np.arange(case.num_slots), case.slot)
     assert torch.equal(d["pool"][untouched], pool_before[untouched]), "untouched slots changed"
 
@@ -127,12 +127,15 @@ def test_skipped_sequences_and_sentinels(gdn_lib):
     d = upload(case)
     pool_before = d["pool"].clone()
     out = torch.full((case.T, case.H_v, case.d_v), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    out_before = out.clone()
     run_extend(gdn, case, d, out=out)
     ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
                                           case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
                                           case.pool, case.scale)
     o = out.float().cpu().numpy()
-    assert (o[~written] == SENTINEL).all(), "rows of skipped sequences were written"
+    skipped = torch.from_numpy(~written).cuda()
+    assert torch.equal(out[skipped].view(torch.int16), out_before[skipped].view(torch.int16)), \
+        "rows of skipped sequences were written"
     assert_close(o[written], ref[written], "out")
     keep = np.setdiff1d(np.arange(9), [4, 7])
     assert torch.equal(d["pool"][keep], pool_before[keep])
@@ -275,20 +278,23 @@ def test_config3_ragged_sampled_and_verify(gdn_lib):
 # ------------------------------------------------------------------ delta-off (SSD)
 @pytest.mark.parametrize("shape", [(2, 150, 6, 64, 2, 128, False), (1, 64, 4, 64, 1, 128, True),
                                    (3, 33, 8, 64, 4, 128, True)])
-def test_ssd_small(gdn_lib, shape):
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_ssd_small(gdn_lib, shape, out_dtype):
     gdn = gdn_lib
     batch, L, H, P, G, Nst, init = shape
-    _announce(f"ssd small {shape}")
+    _announce(f"ssd small {shape} out={out_dtype}")
     c = synth.config4_ssd(seed=L + H, batch=batch, L=L, H=H, P=P, G=G, Nst=Nst, initial=init)
     tb = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
     tf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.float32)
     out, fin = gdn.ssd_combined_fwd(tb(c.x), tb(c.dt), tf(c.A), tb(c.B), tb(c.C), tb(c.D), tb(c.z),
                                     tf(c.dt_bias), True, (0.0, float("inf")),
-                                    None if c.initial_states is None else tf(c.initial_states))
+                                    None if c.initial_states is None else tf(c.initial_states),
+                                    out_dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
     ref, rfin = oracle.ssd_combined(c.x, c.dt, c.A, c.B, c.C, c.D, c.z, c.dt_bias, True,
                                     (0.0, float("inf")), c.initial_states, True)
-    assert_close(out.float().cpu().numpy(), ref, "ssd out")
-    assert_close(fin.cpu().numpy(), rfin, "ssd states")
+    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (1e-3, 2e-3)
+    assert_close(out.float().cpu().numpy(), ref, "ssd out", *bar)
+    assert_close(fin.cpu().numpy(), rfin, "ssd states", *bar)
 
 
 @pytest.mark.slow
