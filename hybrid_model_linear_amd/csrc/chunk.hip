@@ -39,7 +39,6 @@ constexpr int C = 64;            // chunk length
 constexpr int kQS = 8;           // row padding (bf16 elements) of row-major tiles
 constexpr int kTS = C + 8;       // row length of transposed tiles [d][token]
 constexpr int kPS = C + 8;       // row length of C x C bf16 tiles
-constexpr int kAS = C + 1;       // row length of C x C fp32 tiles
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -77,18 +76,25 @@ __device__ __forceinline__ void acc_split(const f32x16& a, int half, bf16x8& hi,
 // Row (token / d_k index) of accumulator element r held by lane half hh, tile origin 0.
 __device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 lds4(const u16* p) {
+  return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
+}
+
 template <int DK, int DV, bool kSSD>
 struct Smem {
-  u16 Q[C][DK + kQS];
-  u16 K[C][DK + kQS];
-  u16 KT[DK][kTS];
-  u16 VT[DV][kTS];
-  u16 Ph[C][kPS];
+  u16 Q[C][DK + kQS];          // raw q rows (bf16)
+  u16 K[C][DK + kQS];          // raw k rows
+  u16 KT[DK][kTS];             // k transposed [d_k][token]
+  u16 VT[DV][kTS];             // v transposed [d_v][token]
+  u16 Ph[C][kPS];              // P = hi + lo
   u16 Pl[C][kPS];
-  u16 Tm[kSSD ? 1 : C][kPS];
-  float A[kSSD ? 1 : C][kAS];
-  float T[kSSD ? 1 : C][kAS];
-  float Z[kSSD ? 1 : 3 * 256];
+  u16 AB[kSSD ? 1 : C][kPS];   // bf16(A), strictly lower
+  u16 Tb[kSSD ? 1 : C][kPS];   // bf16(T), unit lower, row-major
+  u16 TT[kSSD ? 1 : C][kPS];   // bf16(T) transposed (column access)
+  float Ad[kSSD ? 1 : 4][16][17];  // fp32 diagonal 16x16 blocks of A
   float G[C];
   float beta[C];
   float rk[C];
@@ -99,62 +105,93 @@ struct Smem {
 };
 
 // ------------------------------------------------------------------ phase A pieces
-template <int DK, int DV, bool kSSD, int NT>
-__device__ __forceinline__ void stage_chunk(Smem<DK, DV, kSSD>& sm, const SeqLaunch& p, int h, int j,
-                                            int t0, int n) {
+// Raw chunk data held in registers between its global load (issued one chunk
+// ahead, so that it is in flight during the previous chunk's phase B) and its
+// store into LDS.
+template <int DK, int DV, int NT>
+struct ChunkRegs {
+  static constexpr int QK_IT = (C / 2) * (DK / 8) / NT;
+  static constexpr int V_IT = (C / 2) * (DV / 8) / NT;
+  static_assert(QK_IT * NT == (C / 2) * (DK / 8) && V_IT * NT == (C / 2) * (DV / 8), "split");
+  uint4 q[QK_IT][2], k[QK_IT][2], v[V_IT][2];
+  float lg, bt;
+};
+
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, NT>& R, const SeqLaunch& p, int h, int j,
+                                           int t0, int n) {
   const int tid = threadIdx.x;
   const u16* qb = reinterpret_cast<const u16*>(p.q);
   const u16* kb = reinterpret_cast<const u16*>(p.k);
   const u16* vb = reinterpret_cast<const u16*>(p.v);
-  // q, k: token pairs x 8-column groups; k also transposed (two tokens per 32-bit write).
-  constexpr int KG = DK / 8;
-  for (int idx = tid; idx < (C / 2) * KG; idx += NT) {
-    const int pr = idx % (C / 2), cg = idx / (C / 2);
-    const int i0 = 2 * pr, i1 = 2 * pr + 1;
-    uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0, k0 = q0, k1 = q0;
-    if (i0 < n) {
-      q0 = *reinterpret_cast<const uint4*>(qb + (int64_t)(t0 + i0) * p.q_stride + (int64_t)j * DK + 8 * cg);
-      k0 = *reinterpret_cast<const uint4*>(kb + (int64_t)(t0 + i0) * p.k_stride + (int64_t)j * DK + 8 * cg);
-    }
-    if (i1 < n) {
-      q1 = *reinterpret_cast<const uint4*>(qb + (int64_t)(t0 + i1) * p.q_stride + (int64_t)j * DK + 8 * cg);
-      k1 = *reinterpret_cast<const uint4*>(kb + (int64_t)(t0 + i1) * p.k_stride + (int64_t)j * DK + 8 * cg);
-    }
-    *reinterpret_cast<uint4*>(&sm.Q[i0][8 * cg]) = q0;
-    *reinterpret_cast<uint4*>(&sm.Q[i1][8 * cg]) = q1;
-    *reinterpret_cast<uint4*>(&sm.K[i0][8 * cg]) = k0;
-    *reinterpret_cast<uint4*>(&sm.K[i1][8 * cg]) = k1;
-    const uint32_t a0[4] = {k0.x, k0.y, k0.z, k0.w}, a1[4] = {k1.x, k1.y, k1.z, k1.w};
+  const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+  for (int it = 0; it < R.QK_IT; ++it) {
+    const int idx = tid + it * NT;
+    const int pr = idx % (C / 2), cg = idx / (C / 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * pr + u;
+      const int64_t t = t0 + i;
+      R.q[it][u] = i < n ? *reinterpret_cast<const uint4*>(qb + t * p.q_stride + (int64_t)j * DK + 8 * cg) : z;
+      R.k[it][u] = i < n ? *reinterpret_cast<const uint4*>(kb + t * p.k_stride + (int64_t)j * DK + 8 * cg) : z;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < R.V_IT; ++it) {
+    const int idx = tid + it * NT;
+    const int pr = idx % (C / 2), cg = idx / (C / 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * pr + u;
+      R.v[it][u] = i < n ? *reinterpret_cast<const uint4*>(vb + (int64_t)(t0 + i) * p.v_stride + (int64_t)h * DV + 8 * cg) : z;
+    }
+  }
+  R.lg = 0.f;
+  R.bt = 0.f;
+  if (tid < n) {                     // padded tokens: log g = 0, beta = 0 (no effect)
+    const int64_t gi = (int64_t)(t0 + tid) * p.H_v + h;
+    R.lg = p.log_g[gi];
+    R.bt = p.beta[gi];
+  }
+}
+
+template <int DK, int DV, bool kSSD, int NT>
+__device__ __forceinline__ void store_chunk(Smem<DK, DV, kSSD>& sm, const ChunkRegs<DK, DV, NT>& R) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < R.QK_IT; ++it) {
+    const int idx = tid + it * NT;
+    const int pr = idx % (C / 2), cg = idx / (C / 2);
+    const int i0 = 2 * pr;
+    *reinterpret_cast<uint4*>(&sm.Q[i0][8 * cg]) = R.q[it][0];
+    *reinterpret_cast<uint4*>(&sm.Q[i0 + 1][8 * cg]) = R.q[it][1];
+    *reinterpret_cast<uint4*>(&sm.K[i0][8 * cg]) = R.k[it][0];
+    *reinterpret_cast<uint4*>(&sm.K[i0 + 1][8 * cg]) = R.k[it][1];
+    const uint32_t a0[4] = {R.k[it][0].x, R.k[it][0].y, R.k[it][0].z, R.k[it][0].w};
+    const uint32_t a1[4] = {R.k[it][1].x, R.k[it][1].y, R.k[it][1].z, R.k[it][1].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // two tokens per 32-bit write of the transposed tile
       *reinterpret_cast<uint32_t*>(&sm.KT[8 * cg + 2 * e][i0]) = (a0[e] & 0xffffu) | (a1[e] << 16);
       *reinterpret_cast<uint32_t*>(&sm.KT[8 * cg + 2 * e + 1][i0]) = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
     }
   }
-  constexpr int VG = DV / 8;
-  for (int idx = tid; idx < (C / 2) * VG; idx += NT) {
+#pragma unroll
+  for (int it = 0; it < R.V_IT; ++it) {
+    const int idx = tid + it * NT;
     const int pr = idx % (C / 2), cg = idx / (C / 2);
-    const int i0 = 2 * pr, i1 = 2 * pr + 1;
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (i0 < n) v0 = *reinterpret_cast<const uint4*>(vb + (int64_t)(t0 + i0) * p.v_stride + (int64_t)h * DV + 8 * cg);
-    if (i1 < n) v1 = *reinterpret_cast<const uint4*>(vb + (int64_t)(t0 + i1) * p.v_stride + (int64_t)h * DV + 8 * cg);
-    const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+    const int i0 = 2 * pr;
+    const uint32_t a0[4] = {R.v[it][0].x, R.v[it][0].y, R.v[it][0].z, R.v[it][0].w};
+    const uint32_t a1[4] = {R.v[it][1].x, R.v[it][1].y, R.v[it][1].z, R.v[it][1].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       *reinterpret_cast<uint32_t*>(&sm.VT[8 * cg + 2 * e][i0]) = (a0[e] & 0xffffu) | (a1[e] << 16);
       *reinterpret_cast<uint32_t*>(&sm.VT[8 * cg + 2 * e + 1][i0]) = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
     }
   }
-  // per-token gate values; padded tokens get log g = 0 and beta = 0 (no effect)
   if (tid < C) {
-    float lg = 0.f, bt = 0.f;
-    if (tid < n) {
-      const int64_t gi = (int64_t)(t0 + tid) * p.H_v + h;
-      lg = p.log_g[gi];
-      bt = p.beta[gi];
-    }
-    sm.G[tid] = lg;
-    sm.beta[tid] = bt;
+    sm.G[tid] = R.lg;
+    sm.beta[tid] = R.bt;
   }
 }
 
@@ -170,6 +207,7 @@ __device__ __forceinline__ void chunk_scalars(Smem<DK, DV, kSSD>& sm, float scal
     const int row = tid / TPR, part = tid % TPR;
     const u16* src = row < C ? &sm.Q[row][0] : &sm.K[row - C][0];
     float ss = 0.f;
+#pragma unroll
     for (int c8 = part; c8 < DK / 8; c8 += TPR) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * c8);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -213,85 +251,129 @@ __device__ __forceinline__ void chunk_scalars(Smem<DK, DV, kSSD>& sm, float scal
   gL = sm.G[C - 1];
 }
 
-// K K^T and Q K^T tiles (32x32, lower block triangle) -> A (fp32) and P (bf16 hi/lo).
+// Q K^T and K K^T tiles of the lower block triangle (32x32 tiles (0,0), (1,0), (1,1));
+// one wave per tile computes both products and shares the decay factors:
+//   P_im = scale r_q,i r_k,m Gam_im (Q K^T)_im  (m <= i)      -> Ph + Pl (bf16 split)
+//   A_im = beta_i r_k,i r_k,m Gam_im (K K^T)_im (m <  i)      -> AB (bf16), Ad (fp32 diag blocks)
 template <int DK, int DV, bool kSSD, int NW>
 __device__ __forceinline__ void build_A_P(Smem<DK, DV, kSSD>& sm, float scale) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int l32 = lane & 31, hh = lane >> 5;
-  constexpr int NTILES = kSSD ? 3 : 6;
-  for (int tix = w; tix < NTILES; tix += NW) {
-    const bool isKK = !kSSD && tix >= 3;
-    const int tt = tix % 3;
+  for (int tt = w; tt < 3; tt += NW) {
     const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
-    const u16* arow = isKK ? &sm.K[32 * ti + l32][0] : &sm.Q[32 * ti + l32][0];
-    const u16* brow = &sm.K[32 * tj + l32][0];
-    f32x16 acc = {};
+    const u16* qrow = &sm.Q[32 * ti + l32][8 * hh];
+    const u16* krow = &sm.K[32 * ti + l32][8 * hh];
+    const u16* brow = &sm.K[32 * tj + l32][8 * hh];
+    f32x16 qk = {}, kk = {};
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s)
-      acc = mfma32(lds_nat(arow + 16 * s + 8 * hh), lds_nat(brow + 16 * s + 8 * hh), acc);
+    for (int s = 0; s < DK / 16; ++s) {
+      const bf16x8 b = lds_nat(brow + 16 * s);
+      qk = mfma32(lds_nat(qrow + 16 * s), b, qk);
+      if constexpr (!kSSD) kk = mfma32(lds_nat(krow + 16 * s), b, kk);
+    }
     const int m = 32 * tj + l32;                 // key token (column)
     const float Gm = sm.G[m], rkm = sm.rk[m];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * ti + acc_row(r, hh);      // query / key token (row)
-      if (isKK) {
-        if (m < i) sm.A[i][m] = sm.beta[i] * sm.rk[i] * rkm * __expf(sm.G[i] - Gm) * acc[r];
-      } else {
-        float pv = 0.f;
-        if (m <= i) {
-          const float e = __expf(sm.G[i] - Gm);
-          pv = kSSD ? e * acc[r] : scale * sm.rq[i] * rkm * e * acc[r];
-        }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ib = 32 * ti + 8 * q4 + 4 * hh;
+      const float4 Gi = *reinterpret_cast<const float4*>(&sm.G[ib]);
+      const float4 rqi = *reinterpret_cast<const float4*>(&sm.rq[ib]);
+      const float4 rki = *reinterpret_cast<const float4*>(&sm.rk[ib]);
+      const float4 bi = *reinterpret_cast<const float4*>(&sm.beta[ib]);
+      const float Gv[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, rqv[4] = {rqi.x, rqi.y, rqi.z, rqi.w};
+      const float rkv[4] = {rki.x, rki.y, rki.z, rki.w}, bv[4] = {bi.x, bi.y, bi.z, bi.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e, i = ib + e;
+        const float gam = m <= i ? __expf(Gv[e] - Gm) : 0.f;    // masked before the exp
+        const float pv = kSSD ? gam * qk[r] : scale * rqv[e] * rkm * gam * qk[r];
         const __bf16 ph = (__bf16)pv;
         sm.Ph[i][m] = __builtin_bit_cast(u16, ph);
         sm.Pl[i][m] = f32_to_bf16(pv - (float)ph);
+        if constexpr (!kSSD) {
+          const float av = m < i ? bv[e] * rkv[e] * rkm * gam * kk[r] : 0.f;
+          sm.AB[i][m] = f32_to_bf16(av);
+          if ((i >> 4) == (m >> 4)) sm.Ad[i >> 4][i & 15][m & 15] = av;
+        }
       }
+    }
+  }
+  if constexpr (!kSSD) {
+    if (w == NW - 1) {
+      // zero the upper 16x16 blocks inside the two diagonal 32x32 tiles of T and T^T
+      const int blk = lane >> 4, row = lane & 15;
+      u16* dst = blk == 0 ? &sm.Tb[row][16] : blk == 1 ? &sm.Tb[32 + row][48]
+               : blk == 2 ? &sm.TT[16 + row][0] : &sm.TT[48 + row][32];
+      *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(0, 0, 0, 0);
     }
   }
 }
 
-// T = (I + A)^{-1} for strictly lower A (fp32, 16x16 blocks), stored as bf16(T - I).
-template <int DK, int DV, int NT>
+// T = (I + A)^{-1} for strictly lower A, in bf16 (unit diagonal), by 16 -> 32 -> 64
+// block doubling: diagonal 16x16 blocks by fp32 forward substitution, then
+// T_ab = -T_bb^{-1}... merged as T21 = -T22 (A21 T11) with MFMAs.  T - I only
+// enters the chunk as a correction term whose operand is bf16 already.
+template <int DK, int DV, int NW>
 __device__ __forceinline__ void invert_unit_lower(Smem<DK, DV, false>& sm) {
-  const int tid = threadIdx.x;
-  // diagonal blocks: thread (b, c) solves column c of block b by forward substitution
-  if (tid < 64) {
-    const int b = tid / 16, c = tid % 16;
-    float x[16];
+  static_assert(NW >= 2, "needs two waves");
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  // (1) diagonal blocks: wave w < 4 solves block w; lane c < 16 owns column c
+  for (int b = w; b < 4; b += NW) {
+    if (lane < 16) {
+      const int c = lane;
+      float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = (i == c) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) v -= sm.A[16 * b + i][16 * b + m] * x[m];
-      x[i] = v;
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sm.Ad[b][mm][i] * x[i];
+      }
+      uint32_t pk[8];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.Tb[16 * b + i][16 * b + c] = f32_to_bf16(x[i]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pk[i] = uint32_t(f32_to_bf16(x[2 * i])) | (uint32_t(f32_to_bf16(x[2 * i + 1])) << 16);
+      *reinterpret_cast<uint4*>(&sm.TT[16 * b + c][16 * b]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4*>(&sm.TT[16 * b + c][16 * b + 8]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.T[16 * b + i][16 * b + c] = x[i];
   }
   __syncthreads();
-  // off-diagonal blocks by distance d: T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb
-  for (int d = 1; d < 4; ++d) {
-    const int nblk = 4 - d;
-    for (int o = tid; o < nblk * 256; o += NT) {
-      const int blk = o / 256, e = o % 256, i = e / 16, c = e % 16;
-      const int b = blk, a = blk + d;
-      float z = 0.f;
-      for (int m = 16 * b; m < 16 * a; ++m) z += sm.A[16 * a + i][m] * sm.T[m][16 * b + c];
-      sm.Z[o] = z;
-    }
-    __syncthreads();
-    for (int o = tid; o < nblk * 256; o += NT) {
-      const int blk = o / 256, e = o % 256, i = e / 16, c = e % 16;
-      const int b = blk, a = blk + d;
-      float t = 0.f;
-      for (int m = 0; m <= i; ++m) t -= sm.T[16 * a + i][16 * a + m] * sm.Z[blk * 256 + m * 16 + c];
-      sm.T[16 * a + i][16 * b + c] = t;
-    }
-    __syncthreads();
+  // (2) 16 -> 32: inside diagonal 32x32 tile pp, T[16..31][0..15] = -D1^{-1} (A10 D0^{-1})
+  if (w < 2) {
+    const int pp = w, c = lane & 15, g = lane >> 4;
+    const int r0 = 32 * pp;
+    f32x4 y = {};
+    y = mfma16(lds4(&sm.AB[r0 + 16 + c][r0 + 4 * g]), lds4(&sm.TT[r0 + c][r0 + 4 * g]), y);
+    bf16x4 yb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+    f32x4 zz = {};
+    zz = mfma16(lds4(&sm.Tb[r0 + 16 + c][r0 + 16 + 4 * g]), yb, zz);
+    // zz: lane holds rows 4g .. 4g+3 of column c
+    uint32_t pk[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Tb[r0 + 16 + 4 * g + e][r0 + c] = f32_to_bf16(-zz[e]);
+    pk[0] = uint32_t(f32_to_bf16(-zz[0])) | (uint32_t(f32_to_bf16(-zz[1])) << 16);
+    pk[1] = uint32_t(f32_to_bf16(-zz[2])) | (uint32_t(f32_to_bf16(-zz[3])) << 16);
+    *reinterpret_cast<uint2*>(&sm.TT[r0 + c][r0 + 16 + 4 * g]) = make_uint2(pk[0], pk[1]);
   }
-  for (int o = tid; o < C * C; o += NT) {
-    const int i = o / C, m = o % C;
-    sm.Tm[i][m] = m < i ? f32_to_bf16(sm.T[i][m]) : (u16)0;
+  __syncthreads();
+  // (3) 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
+  if (w == 0) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    f32x16 y = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      y = mfma32(lds_nat(&sm.AB[32 + l32][16 * s + 8 * hh]), lds_nat(&sm.TT[l32][16 * s + 8 * hh]), y);
+    f32x16 zz = {};
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      zz = mfma32(lds_perm(&sm.Tb[32 + l32][32 + 16 * s + 4 * hh]), acc_to_op(y, s), zz);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.Tb[32 + acc_row(r, hh)][l32] = f32_to_bf16(-zz[r]);
   }
 }
 
@@ -330,23 +412,26 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
     }
   }
 
-  const OutT* dummy = nullptr;
-  (void)dummy;
   OutT* ob = reinterpret_cast<OutT*>(p.out);
+
+  ChunkRegs<DK, DV, NT> pre;
+  if (tbeg < tend) load_chunk<DK, DV, NT>(pre, p, h, j, tbeg, min(C, tend - tbeg));
 
   for (int t0 = tbeg; t0 < tend; t0 += C) {
     const int n = min(C, tend - t0);
     __syncthreads();                                       // previous chunk's readers done
-    stage_chunk<DK, DV, kSSD, NT>(sm, p, h, j, t0, n);
+    store_chunk<DK, DV, kSSD, NT>(sm, pre);
     __syncthreads();
     float gL;
     chunk_scalars<DK, DV, kSSD, NT>(sm, p.scale, n, gL);
     build_A_P<DK, DV, kSSD, NW>(sm, p.scale);
     __syncthreads();
     if constexpr (!kSSD) {
-      invert_unit_lower<DK, DV, NT>(sm);
+      invert_unit_lower<DK, DV, NW>(sm);
       __syncthreads();
     }
+    // next chunk's raw data: in flight while this chunk's phase B runs
+    if (t0 + C < tend) load_chunk<DK, DV, NT>(pre, p, h, j, t0 + C, min(C, tend - t0 - C));
 
     // ---------------- phase B: this wave's 32 d_v columns
     bf16x8 Sb[NKS];
@@ -389,13 +474,19 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
       }
     }
     if constexpr (!kSSD) {
-      // U = R + (T - I) bf16(R); (T - I) is strictly lower: tile 0 needs k-steps 0..1
+      // U = R + (T - I) bf16(R) = (R - bf16(R)) + T bf16(R); T is unit lower, so row
+      // tile 0 needs k-steps 0..1 only
       bf16x8 Rb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) Rb[s] = acc_to_op(U[s >> 1], s & 1);
 #pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) U[s >> 1][8 * (s & 1) + e] -= (float)Rb[s][e];
+      }
+#pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
-        const u16* trow = &sm.Tm[32 * ti + l32][4 * hh];
+        const u16* trow = &sm.Tb[32 * ti + l32][4 * hh];
 #pragma unroll
         for (int s = 0; s < 2 * (ti + 1); ++s) U[ti] = mfma32(lds_perm(trow + 16 * s), Rb[s], U[ti]);
       }
