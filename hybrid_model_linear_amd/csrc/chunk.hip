@@ -8,26 +8,38 @@
 //
 //   A  = strict_lower( beta_i r_k,i r_k,m Gam_im (K K^T)_im ),   T = (I + A)^{-1}
 //   X  = K S0^T,   R = diag(beta) V - diag(beta gamma r_k) X      (first-order innovations)
-//   U  = T R = R + (T - I) R                                       (delta-rule corrected values)
+//   U  = T R = (R - bf16(R)) + T bf16(R)                           (delta-rule corrected values)
 //   O  = diag(scale gamma r_q) Q S0^T + P U,  P = lower( scale r_q,i r_k,m Gam_im (Q K^T)_im )
 //   S1 = gamma_C S0 + U^T diag(exp(G_C - G_i) r_k,i) K
 //
 // Delta-off mode (Mamba2 SSD, flashinfer.mamba.ssd_combined_fwd): no norms, T = I,
 // U = diag(dt') X, scale 1, then O += D x and O *= silu(z).
 //
-// Precision layout: q, k, v enter the MFMAs as their exact bf16 values; norms,
-// beta and decays are fp32 row/column scalings applied after the products; S0 and
-// (T - I) R are single bf16 operands; P U and the state update use two-term
-// (hi + lo) bf16 splits of P, U and the scaled U.
+// Precision: q, k, v enter the MFMAs as their exact bf16 values; norms, beta and
+// decays are fp32 row/column scalings applied around the products; S0, T and the
+// correction operand bf16(R) are single bf16 operands; P U and the state update use
+// two-term (hi + lo) bf16 splits of P, U and the scaled U.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
-// order; the state never leaves registers.  Phase A (all waves, independent of
-// the state) stages Q, K, K^T, V^T in LDS and builds P and T - I; phase B gives
-// each wave 32 of the d_v columns: state rows are independent given the chunk's
-// keys, so the waves never exchange data there.  The state is held as S^T tiles in
-// MFMA accumulator layout and fed back as B operands without any data movement:
-// the reduction index of a 32x32x16 MFMA may be permuted freely as long as both
-// operands agree, so A operands are read from LDS in the accumulator's row order.
+// order; the state never leaves registers.  Each wave owns 32 of the d_v columns
+// (state rows are independent given the chunk's keys), held as S^T tiles in MFMA
+// accumulator layout and fed back as B operands directly: the reduction index of
+// a 32x32x16 MFMA may be permuted freely when both operands agree, so A operands
+// are read from LDS in the accumulator's row order.
+//
+// Data movement: q, k, v (and z) rows of chunk c+1 stream from HBM straight into
+// LDS (global_load_lds, 16 B per lane) while chunk c is computed; the two LDS
+// buffers are distinct objects and the chunk loop is unrolled by two, so no LDS
+// read has to wait on the transfer in flight.  Tiles are row-major and padded
+// by one 16-byte segment per row.  K^T and
+// V^T operands come from the row-major tiles through the LDS transpose read
+// (ds_read_b64_tr_b16): lane j of each 16-lane group receives column c0 + j of the
+// four rows addressed by the group's lanes 4e + j/4.
+//
+// Per chunk: the state-independent part (Q K^T, K K^T, P, A) runs on three waves,
+// then one wave builds T (diagonal 16x16 blocks by fp32 forward substitution,
+// 16 -> 32 -> 64 merges T21 = -T22 A21 T11 on MFMA) while all waves form
+// X = K S0^T, Y = Q S0^T and R; the T-dependent rest follows one barrier later.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -36,345 +48,133 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64;            // chunk length
-constexpr int kQS = 8;           // row padding (bf16 elements) of row-major tiles
-constexpr int kTS = C + 8;       // row length of transposed tiles [d][token]
-constexpr int kPS = C + 8;       // row length of C x C bf16 tiles
+constexpr int kPS = C + 8;       // row length (bf16) of the padded C x C tiles
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u16 lds_u16;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// 8 consecutive bf16 (16 B) from LDS: operand in natural k order.
-__device__ __forceinline__ bf16x8 lds_nat(const u16* p) {
-  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
-}
-// Operand in accumulator row order: k slots e = 0..3 at p[0..3], e = 4..7 at p[8..11]
-// (p already offset by 16 s + 4 hh).
-__device__ __forceinline__ bf16x8 lds_perm(const u16* p) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-// Accumulator half (elements 8 half .. 8 half + 7) as a bf16 operand.
-__device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)a[8 * half + e];
-  return r;
-}
-__device__ __forceinline__ void acc_split(const f32x16& a, int half, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = a[8 * half + e];
-    const __bf16 h = (__bf16)x;
-    hi[e] = h;
-    lo[e] = (__bf16)(x - (float)h);
-  }
-}
-// Row (token / d_k index) of accumulator element r held by lane half hh, tile origin 0.
-__device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
-
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x4 lds4(const u16* p) {
-  return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// LDS transpose read of 4 bf16 at p (8-byte aligned).
+__device__ __forceinline__ uint2 tr_read(const u16* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p)));
 }
 
-template <int DK, int DV, bool kSSD>
-struct Smem {
-  u16 Q[C][DK + kQS];          // raw q rows (bf16)
-  u16 K[C][DK + kQS];          // raw k rows
-  u16 KT[DK][kTS];             // k transposed [d_k][token]
-  u16 VT[DV][kTS];             // v transposed [d_v][token]
-  u16 Ph[C][kPS];              // P = hi + lo
-  u16 Pl[C][kPS];
-  u16 AB[kSSD ? 1 : C][kPS];   // bf16(A), strictly lower
-  u16 Tb[kSSD ? 1 : C][kPS];   // bf16(T), unit lower, row-major
-  u16 TT[kSSD ? 1 : C][kPS];   // bf16(T) transposed (column access)
-  float Ad[kSSD ? 1 : 4][16][17];  // fp32 diagonal 16x16 blocks of A
-  float G[C];
-  float beta[C];
-  float rk[C];
-  float rq[C];
-  float coefR[C];
-  float coefO[C];
-  float coefS[C];
-};
-
-// ------------------------------------------------------------------ phase A pieces
-// Raw chunk data held in registers between its global load (issued one chunk
-// ahead, so that it is in flight during the previous chunk's phase B) and its
-// store into LDS.
-template <int DK, int DV, int NT>
-struct ChunkRegs {
-  static constexpr int QK_IT = (C / 2) * (DK / 8) / NT;
-  static constexpr int V_IT = (C / 2) * (DV / 8) / NT;
-  static_assert(QK_IT * NT == (C / 2) * (DK / 8) && V_IT * NT == (C / 2) * (DV / 8), "split");
-  uint4 q[QK_IT][2], k[QK_IT][2], v[V_IT][2];
-  float lg, bt;
-};
-
-template <int DK, int DV, int NT>
-__device__ __forceinline__ void load_chunk(ChunkRegs<DK, DV, NT>& R, const SeqLaunch& p, int h, int j,
-                                           int t0, int n) {
-  const int tid = threadIdx.x;
-  const u16* qb = reinterpret_cast<const u16*>(p.q);
-  const u16* kb = reinterpret_cast<const u16*>(p.k);
-  const u16* vb = reinterpret_cast<const u16*>(p.v);
-  const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int it = 0; it < R.QK_IT; ++it) {
-    const int idx = tid + it * NT;
-    const int pr = idx % (C / 2), cg = idx / (C / 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * pr + u;
-      const int64_t t = t0 + i;
-      R.q[it][u] = i < n ? *reinterpret_cast<const uint4*>(qb + t * p.q_stride + (int64_t)j * DK + 8 * cg) : z;
-      R.k[it][u] = i < n ? *reinterpret_cast<const uint4*>(kb + t * p.k_stride + (int64_t)j * DK + 8 * cg) : z;
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < R.V_IT; ++it) {
-    const int idx = tid + it * NT;
-    const int pr = idx % (C / 2), cg = idx / (C / 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * pr + u;
-      R.v[it][u] = i < n ? *reinterpret_cast<const uint4*>(vb + (int64_t)(t0 + i) * p.v_stride + (int64_t)h * DV + 8 * cg) : z;
-    }
-  }
-  R.lg = 0.f;
-  R.bt = 0.f;
-  if (tid < n) {                     // padded tokens: log g = 0, beta = 0 (no effect)
-    const int64_t gi = (int64_t)(t0 + tid) * p.H_v + h;
-    R.lg = p.log_g[gi];
-    R.bt = p.beta[gi];
-  }
+// Row-major bf16 tiles of 64 rows x D columns are padded by one 16-byte segment per
+// row (D + 8 elements) so that MFMA operand reads of consecutive rows spread over
+// the LDS banks while every address stays an affine function of the lane.
+template <int D>
+__device__ __forceinline__ int pidx(int r, int c) { return r * (D + 8) + c; }
+// 4 consecutive bf16 (8 B), c % 4 == 0.
+template <int D>
+__device__ __forceinline__ uint2 ld4(const u16* t, int r, int c) {
+  return *reinterpret_cast<const uint2*>(t + pidx<D>(r, c));
 }
-
-template <int DK, int DV, bool kSSD, int NT>
-__device__ __forceinline__ void store_chunk(Smem<DK, DV, kSSD>& sm, const ChunkRegs<DK, DV, NT>& R) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < R.QK_IT; ++it) {
-    const int idx = tid + it * NT;
-    const int pr = idx % (C / 2), cg = idx / (C / 2);
-    const int i0 = 2 * pr;
-    *reinterpret_cast<uint4*>(&sm.Q[i0][8 * cg]) = R.q[it][0];
-    *reinterpret_cast<uint4*>(&sm.Q[i0 + 1][8 * cg]) = R.q[it][1];
-    *reinterpret_cast<uint4*>(&sm.K[i0][8 * cg]) = R.k[it][0];
-    *reinterpret_cast<uint4*>(&sm.K[i0 + 1][8 * cg]) = R.k[it][1];
-    const uint32_t a0[4] = {R.k[it][0].x, R.k[it][0].y, R.k[it][0].z, R.k[it][0].w};
-    const uint32_t a1[4] = {R.k[it][1].x, R.k[it][1].y, R.k[it][1].z, R.k[it][1].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {   // two tokens per 32-bit write of the transposed tile
-      *reinterpret_cast<uint32_t*>(&sm.KT[8 * cg + 2 * e][i0]) = (a0[e] & 0xffffu) | (a1[e] << 16);
-      *reinterpret_cast<uint32_t*>(&sm.KT[8 * cg + 2 * e + 1][i0]) = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < R.V_IT; ++it) {
-    const int idx = tid + it * NT;
-    const int pr = idx % (C / 2), cg = idx / (C / 2);
-    const int i0 = 2 * pr;
-    const uint32_t a0[4] = {R.v[it][0].x, R.v[it][0].y, R.v[it][0].z, R.v[it][0].w};
-    const uint32_t a1[4] = {R.v[it][1].x, R.v[it][1].y, R.v[it][1].z, R.v[it][1].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint32_t*>(&sm.VT[8 * cg + 2 * e][i0]) = (a0[e] & 0xffffu) | (a1[e] << 16);
-      *reinterpret_cast<uint32_t*>(&sm.VT[8 * cg + 2 * e + 1][i0]) = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-    }
-  }
-  if (tid < C) {
-    sm.G[tid] = R.lg;
-    sm.beta[tid] = R.bt;
-  }
+// 8 consecutive bf16 (16 B), c % 8 == 0.
+template <int D>
+__device__ __forceinline__ bf16x8 ld8(const u16* t, int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(t + pidx<D>(r, c)));
 }
-
-// Row norms (GDN), in-chunk cumulative decay and the per-token coefficients.
-template <int DK, int DV, bool kSSD, int NT>
-__device__ __forceinline__ void chunk_scalars(Smem<DK, DV, kSSD>& sm, float scale, int n,
-                                              float& gL) {
-  const int tid = threadIdx.x;
-  if constexpr (!kSSD) {
-    // 2 C rows (q and k), NT / (2C) threads per row.
-    constexpr int TPR = NT / (2 * C);
-    static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0, "threads per row");
-    const int row = tid / TPR, part = tid % TPR;
-    const u16* src = row < C ? &sm.Q[row][0] : &sm.K[row - C][0];
-    float ss = 0.f;
-#pragma unroll
-    for (int c8 = part; c8 < DK / 8; c8 += TPR) {
-      const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * c8);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(ws[e] << 16), hi = __uint_as_float(ws[e] & 0xffff0000u);
-        ss += lo * lo + hi * hi;
-      }
-    }
-    ss = group_sum<TPR>(ss);
-    if (part == 0) {
-      const int i = row % C;
-      const float r = i < n ? 1.0f / sqrtf(ss + 1e-6f) : 0.f;
-      if (row < C) sm.rq[i] = r; else sm.rk[i] = r;
-    }
-  } else {
-    if (tid < C) {
-      const float r = tid < n ? 1.f : 0.f;
-      sm.rq[tid] = r;
-      sm.rk[tid] = r;
-    }
-  }
-  __syncthreads();
-  // inclusive prefix sum of log g over the chunk (wave 0, lane = token)
-  if (tid < C) {
-    float Gi = sm.G[tid];
-#pragma unroll
-    for (int off = 1; off < C; off <<= 1) {
-      const float o = __shfl_up(Gi, off, kWave);
-      if (tid >= off) Gi += o;
-    }
-    const float GL = __shfl(Gi, C - 1, kWave);
-    const float gam = __expf(Gi);
-    const float bt = sm.beta[tid], rk = sm.rk[tid], rq = sm.rq[tid];
-    sm.G[tid] = Gi;
-    sm.coefR[tid] = bt * gam * rk;
-    sm.coefO[tid] = scale * gam * rq;
-    sm.coefS[tid] = __expf(GL - Gi) * rk;
-  }
-  __syncthreads();
-  gL = sm.G[C - 1];
+// Transpose read: lane j of a 16-lane group receives elements (rows[e], c0 + j),
+// e = 0..3, when lane i of the group passes (rows[i / 4], c0 + 4 (i % 4)).
+template <int D>
+__device__ __forceinline__ uint2 ldtr(const u16* t, int r, int c) {
+  return tr_read(t + pidx<D>(r, c));
 }
-
-// Q K^T and K K^T tiles of the lower block triangle (32x32 tiles (0,0), (1,0), (1,1));
-// one wave per tile computes both products and shares the decay factors:
-//   P_im = scale r_q,i r_k,m Gam_im (Q K^T)_im  (m <= i)      -> Ph + Pl (bf16 split)
-//   A_im = beta_i r_k,i r_k,m Gam_im (K K^T)_im (m <  i)      -> AB (bf16), Ad (fp32 diag blocks)
-template <int DK, int DV, bool kSSD, int NW>
-__device__ __forceinline__ void build_A_P(Smem<DK, DV, kSSD>& sm, float scale) {
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int l32 = lane & 31, hh = lane >> 5;
-  for (int tt = w; tt < 3; tt += NW) {
-    const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
-    const u16* qrow = &sm.Q[32 * ti + l32][8 * hh];
-    const u16* krow = &sm.K[32 * ti + l32][8 * hh];
-    const u16* brow = &sm.K[32 * tj + l32][8 * hh];
-    f32x16 qk = {}, kk = {};
+// Operand in accumulator row order from a padded [.][kPS] tile: k slots 0..3 at
+// p[0..3], 4..7 at p[8..11] (p offset by 16 s + 4 hh).
+__device__ __forceinline__ bf16x8 lds_perm(const u16* p) {
+  return join(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 8));
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
+  const int o = 8 * half;
+  return as_bf16x8(make_uint4(cvt2(a[o], a[o + 1]), cvt2(a[o + 2], a[o + 3]), cvt2(a[o + 4], a[o + 5]),
+                              cvt2(a[o + 6], a[o + 7])));
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void acc_split(const f32x16& a, int half, bf16x8& hi, bf16x8& lo) {
+  const int o = 8 * half;
+  uint32_t h[4], l[4];
 #pragma unroll
-    for (int s = 0; s < DK / 16; ++s) {
-      const bf16x8 b = lds_nat(brow + 16 * s);
-      qk = mfma32(lds_nat(qrow + 16 * s), b, qk);
-      if constexpr (!kSSD) kk = mfma32(lds_nat(krow + 16 * s), b, kk);
-    }
-    const int m = 32 * tj + l32;                 // key token (column)
-    const float Gm = sm.G[m], rkm = sm.rk[m];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int ib = 32 * ti + 8 * q4 + 4 * hh;
-      const float4 Gi = *reinterpret_cast<const float4*>(&sm.G[ib]);
-      const float4 rqi = *reinterpret_cast<const float4*>(&sm.rq[ib]);
-      const float4 rki = *reinterpret_cast<const float4*>(&sm.rk[ib]);
-      const float4 bi = *reinterpret_cast<const float4*>(&sm.beta[ib]);
-      const float Gv[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, rqv[4] = {rqi.x, rqi.y, rqi.z, rqi.w};
-      const float rkv[4] = {rki.x, rki.y, rki.z, rki.w}, bv[4] = {bi.x, bi.y, bi.z, bi.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q4 + e, i = ib + e;
-        const float gam = m <= i ? __expf(Gv[e] - Gm) : 0.f;    // masked before the exp
-        const float pv = kSSD ? gam * qk[r] : scale * rqv[e] * rkm * gam * qk[r];
-        const __bf16 ph = (__bf16)pv;
-        sm.Ph[i][m] = __builtin_bit_cast(u16, ph);
-        sm.Pl[i][m] = f32_to_bf16(pv - (float)ph);
-        if constexpr (!kSSD) {
-          const float av = m < i ? bv[e] * rkv[e] * rkm * gam * kk[r] : 0.f;
-          sm.AB[i][m] = f32_to_bf16(av);
-          if ((i >> 4) == (m >> 4)) sm.Ad[i >> 4][i & 15][m & 15] = av;
-        }
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = a[o + 2 * e], x1 = a[o + 2 * e + 1];
+    h[e] = cvt2(x0, x1);
+    l[e] = cvt2(x0 - __uint_as_float(h[e] << 16), x1 - __uint_as_float(h[e] & 0xffff0000u));
   }
-  if constexpr (!kSSD) {
-    if (w == NW - 1) {
-      // zero the upper 16x16 blocks inside the two diagonal 32x32 tiles of T and T^T
-      const int blk = lane >> 4, row = lane & 15;
-      u16* dst = blk == 0 ? &sm.Tb[row][16] : blk == 1 ? &sm.Tb[32 + row][48]
-               : blk == 2 ? &sm.TT[16 + row][0] : &sm.TT[48 + row][32];
-      *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(dst + 8) = make_uint4(0, 0, 0, 0);
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+// Row (token / d_k index) of accumulator element r held by lane half hh.
+__device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float f4get(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ------------------------------------------------------------------ chunk transfer
+// One padded 64-row tile of D bf16 columns, (D + 8) * 2 bytes per row, copied as
+// 1 KiB wave instructions (64 lanes x 16 B, lane l -> byte 16 l of the instruction's
+// block) spread over the NW waves; a lane that lands on a row's pad segment
+// re-reads that row's first segment.  Rows past the sequence end re-read row t0
+// (always valid): their values are finite and every coefficient that touches
+// them is zero.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(lds_u16* lds_tile, const u16* gbase, int64_t gstride, int t0,
+                                         int n) {
+  constexpr int RB = (D + 8) * 2;              // bytes per padded row
+  constexpr int NI = 64 * RB / 1024;           // wave instructions per tile
+  static_assert(NI * 1024 == 64 * RB, "tile is a whole number of 1 KiB blocks");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int it = 0; it < (NI + NW - 1) / NW; ++it) {
+    const int m = w + it * NW;
+    if (m < NI) {
+      const int b = m * 1024 + 16 * lane;
+      const int r = b / RB;
+      const int sg = (b % RB) / 16;
+      const int64_t t = t0 + (r < n ? r : 0);
+      const int seg = sg < D / 8 ? sg : 0;
+      __builtin_amdgcn_global_load_lds(gbase + t * gstride + 8 * seg, (lds_void*)(lds_tile + m * 512), 16, 0, 0);
     }
   }
 }
+// per-token fp32 gate values of one v-head ([T, H_v] layout), issued by wave 0
+__device__ __forceinline__ void dma_gate(lds_f32* lds_vec, const float* g, int H_v, int h, int t0, int n) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = t0 + (lane < n ? lane : 0);
+  __builtin_amdgcn_global_load_lds(g + t * H_v + h, (lds_void*)lds_vec, 4, 0, 0);
+}
 
-// T = (I + A)^{-1} for strictly lower A, in bf16 (unit diagonal), by 16 -> 32 -> 64
-// block doubling: diagonal 16x16 blocks by fp32 forward substitution, then
-// T_ab = -T_bb^{-1}... merged as T21 = -T22 (A21 T11) with MFMAs.  T - I only
-// enters the chunk as a correction term whose operand is bf16 already.
-template <int DK, int DV, int NW>
-__device__ __forceinline__ void invert_unit_lower(Smem<DK, DV, false>& sm) {
-  static_assert(NW >= 2, "needs two waves");
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  // (1) diagonal blocks: wave w < 4 solves block w; lane c < 16 owns column c
-  for (int b = w; b < 4; b += NW) {
-    if (lane < 16) {
-      const int c = lane;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sm.Ad[b][mm][i] * x[i];
-      }
-      uint32_t pk[8];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.Tb[16 * b + i][16 * b + c] = f32_to_bf16(x[i]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pk[i] = uint32_t(f32_to_bf16(x[2 * i])) | (uint32_t(f32_to_bf16(x[2 * i + 1])) << 16);
-      *reinterpret_cast<uint4*>(&sm.TT[16 * b + c][16 * b]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      *reinterpret_cast<uint4*>(&sm.TT[16 * b + c][16 * b + 8]) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    }
-  }
-  __syncthreads();
-  // (2) 16 -> 32: inside diagonal 32x32 tile pp, T[16..31][0..15] = -D1^{-1} (A10 D0^{-1})
-  if (w < 2) {
-    const int pp = w, c = lane & 15, g = lane >> 4;
-    const int r0 = 32 * pp;
-    f32x4 y = {};
-    y = mfma16(lds4(&sm.AB[r0 + 16 + c][r0 + 4 * g]), lds4(&sm.TT[r0 + c][r0 + 4 * g]), y);
-    bf16x4 yb;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
-    f32x4 zz = {};
-    zz = mfma16(lds4(&sm.Tb[r0 + 16 + c][r0 + 16 + 4 * g]), yb, zz);
-    // zz: lane holds rows 4g .. 4g+3 of column c
-    uint32_t pk[2];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Tb[r0 + 16 + 4 * g + e][r0 + c] = f32_to_bf16(-zz[e]);
-    pk[0] = uint32_t(f32_to_bf16(-zz[0])) | (uint32_t(f32_to_bf16(-zz[1])) << 16);
-    pk[1] = uint32_t(f32_to_bf16(-zz[2])) | (uint32_t(f32_to_bf16(-zz[3])) << 16);
-    *reinterpret_cast<uint2*>(&sm.TT[r0 + c][r0 + 16 + 4 * g]) = make_uint2(pk[0], pk[1]);
-  }
-  __syncthreads();
-  // (3) 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
-  if (w == 0) {
-    const int l32 = lane & 31, hh = lane >> 5;
-    f32x16 y = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      y = mfma32(lds_nat(&sm.AB[32 + l32][16 * s + 8 * hh]), lds_nat(&sm.TT[l32][16 * s + 8 * hh]), y);
-    f32x16 zz = {};
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      zz = mfma32(lds_perm(&sm.Tb[32 + l32][32 + 16 * s + 4 * hh]), acc_to_op(y, s), zz);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm.Tb[32 + acc_row(r, hh)][l32] = f32_to_bf16(-zz[r]);
-  }
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is a workgroup-scope
+// fence and would also wait for the global->LDS transfer in flight; here the
+// wave's own LDS accesses are drained (lgkmcnt(0)) and the compiler is kept from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
@@ -383,7 +183,21 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
   constexpr int NT = NW * kWave;
   constexpr int NKS = DK / 16;     // k-steps over d_k
   constexpr int NTK = DK / 32;     // S^T row tiles
-  __shared__ Smem<DK, DV, kSSD> sm;
+  static_assert(DK == 128 && (DV == 128 || DV == 64), "tile shapes");
+  static_assert(kSSD || NW == 4, "GDN mode uses four waves (d_v = 128)");
+
+  // double-buffered chunk data (distinct LDS objects: see the header comment)
+  __shared__ __attribute__((aligned(16))) u16 sQ0[C * (DK + 8)], sQ1[C * (DK + 8)];
+  __shared__ __attribute__((aligned(16))) u16 sK0[C * (DK + 8)], sK1[C * (DK + 8)];
+  __shared__ __attribute__((aligned(16))) u16 sV0[C * (DV + 8)], sV1[C * (DV + 8)];
+  __shared__ __attribute__((aligned(16))) u16 sZ0[kSSD ? C * (DV + 8) : 8], sZ1[kSSD ? C * (DV + 8) : 8];
+  __shared__ __attribute__((aligned(16))) float sGr0[C], sGr1[C], sBr0[C], sBr1[C];
+  // per-chunk working set
+  __shared__ __attribute__((aligned(16))) u16 sPh[C][kPS], sPl[C][kPS];
+  __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS], sTb[kSSD ? 1 : C][kPS];
+  __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16][20];
+  __shared__ __attribute__((aligned(16))) float sG[C], sBeta[C], sRk[C], sRq[C];
+  __shared__ __attribute__((aligned(16))) float sCR[C], sCO[C], sCS[C];   // per-token coefficients
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
@@ -393,105 +207,320 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
   const bool init = p.has_init ? (p.has_init[nseq] != 0) : true;
   const int j = h / (p.H_v / p.H_qk);
 
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, w = tid / kWave;
   const int l32 = lane & 31, hh = lane >> 5;
   const int col = 32 * w + l32;                            // this lane's d_v column
+  const int g16 = lane >> 4, j16 = lane & 15;              // transpose-read group / lane
+
+  const u16* qg = reinterpret_cast<const u16*>(p.q) + (int64_t)j * DK;
+  const u16* kg = reinterpret_cast<const u16*>(p.k) + (int64_t)j * DK;
+  const u16* vg = reinterpret_cast<const u16*>(p.v) + (int64_t)h * DV;
+  const u16* zg = reinterpret_cast<const u16*>(p.z) + (int64_t)h * DV;
+  OutT* ob = reinterpret_cast<OutT*>(p.out) + (int64_t)h * DV + col;
 
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
   f32x16 Sacc[NTK];
+  if (init) {
 #pragma unroll
-  for (int tk = 0; tk < NTK; ++tk) {
+    for (int tk = 0; tk < NTK; ++tk)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (init) v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 32 * tk + 8 * q4 + 4 * hh);
-      Sacc[tk][4 * q4 + 0] = v.x;
-      Sacc[tk][4 * q4 + 1] = v.y;
-      Sacc[tk][4 * q4 + 2] = v.z;
-      Sacc[tk][4 * q4 + 3] = v.w;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 32 * tk + 8 * q4 + 4 * hh);
+        Sacc[tk][4 * q4 + 0] = v.x;
+        Sacc[tk][4 * q4 + 1] = v.y;
+        Sacc[tk][4 * q4 + 2] = v.z;
+        Sacc[tk][4 * q4 + 3] = v.w;
+      }
+  } else {
+#pragma unroll
+    for (int tk = 0; tk < NTK; ++tk) Sacc[tk] = f32x16{};
   }
 
-  OutT* ob = reinterpret_cast<OutT*>(p.out);
+  // delta-off D skip coefficient of this lane's column (read once, outside the loop)
+  float Dc = 0.f;
+  if constexpr (kSSD) {
+    const u16* Db = reinterpret_cast<const u16*>(p.D);
+    if (Db) Dc = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
+  }
 
-  ChunkRegs<DK, DV, NT> pre;
-  if (tbeg < tend) load_chunk<DK, DV, NT>(pre, p, h, j, tbeg, min(C, tend - tbeg));
+  // bf16 outputs of the previous chunk, stored after the next transfer is issued
+  uint32_t opk[2][8];
+  int o_t0 = -1, o_n = 0;
 
-  for (int t0 = tbeg; t0 < tend; t0 += C) {
+  auto issue = [&](lds_u16* dQ, lds_u16* dK, lds_u16* dV, lds_u16* dZ, lds_f32* dG, lds_f32* dB, int t0) {
     const int n = min(C, tend - t0);
-    __syncthreads();                                       // previous chunk's readers done
-    store_chunk<DK, DV, kSSD, NT>(sm, pre);
-    __syncthreads();
-    float gL;
-    chunk_scalars<DK, DV, kSSD, NT>(sm, p.scale, n, gL);
-    build_A_P<DK, DV, kSSD, NW>(sm, p.scale);
-    __syncthreads();
-    if constexpr (!kSSD) {
-      invert_unit_lower<DK, DV, NW>(sm);
-      __syncthreads();
+    dma_tile<DK, NW>(dQ, qg, p.q_stride, t0, n);
+    dma_tile<DK, NW>(dK, kg, p.k_stride, t0, n);
+    dma_tile<DV, NW>(dV, vg, p.v_stride, t0, n);
+    if constexpr (kSSD) {
+      if (p.z) dma_tile<DV, NW>(dZ, zg, p.z_stride, t0, n);
     }
-    // next chunk's raw data: in flight while this chunk's phase B runs
-    if (t0 + C < tend) load_chunk<DK, DV, NT>(pre, p, h, j, t0 + C, min(C, tend - t0 - C));
+    if (w == 0) {
+      dma_gate(dG, p.log_g, p.H_v, h, t0, n);
+      dma_gate(dB, p.beta, p.H_v, h, t0, n);
+    }
+  };
 
-    // ---------------- phase B: this wave's 32 d_v columns
+  auto flush_out = [&]() {
+    if constexpr (sizeof(OutT) == 2) {
+      if (o_t0 < 0) return;
+      u16* o16 = reinterpret_cast<u16*>(ob);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 32 * ti + acc_row(r, hh);
+          const uint32_t wv = opk[ti][r >> 1];
+          if (i < o_n) o16[(int64_t)(o_t0 + i) * p.out_stride] = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
+        }
+      o_t0 = -1;
+    }
+  };
+
+  // One chunk on buffer set (Q, K, V, Z, Gr, Br); the following chunk's transfer
+  // goes to (nQ, nK, nV, nZ, nGr, nBr).
+  auto chunk = [&](const u16* Q, const u16* K, const u16* V, const u16* Z, const float* Gr,
+                   const float* Br, lds_u16* nQ, lds_u16* nK, lds_u16* nV, lds_u16* nZ, lds_f32* nGr,
+                   lds_f32* nBr, int t0) {
+    const int n = min(C, tend - t0);
+    wait_vm_all();
+    lds_sync();                                   // chunk data visible; previous chunk done
+
+    // ---- per-token scalars: norms (all threads), cumulative decay (wave 0)
+    if constexpr (!kSSD) {
+      constexpr int TPR = NT / (2 * C);                // threads per row (q and k rows)
+      const int row = tid / TPR, part = tid % TPR;
+      const int rr = row % C;
+      // (two explicit paths rather than a pointer select, so the compiler can tell
+      // these reads from the transfer in flight into the other buffer)
+      auto rowsq = [&](const u16* src) {
+        float a = 0.f;
+#pragma unroll
+        for (int c8 = part; c8 < DK / 8; c8 += TPR) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + pidx<DK>(rr, 8 * c8));
+          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a += bf_lo(ws[e]) * bf_lo(ws[e]) + bf_hi(ws[e]) * bf_hi(ws[e]);
+        }
+        return a;
+      };
+      float ss = row < C ? rowsq(Q) : rowsq(K);
+      ss = group_sum<TPR>(ss);
+      if (part == 0) {
+        const float r = rr < n ? 1.0f / sqrtf(ss + 1e-6f) : 0.f;
+        if (row < C) sRq[rr] = r; else sRk[rr] = r;
+      }
+    } else {
+      if (tid < C) {
+        sRq[tid] = tid < n ? 1.f : 0.f;
+        sRk[tid] = tid < n ? 1.f : 0.f;
+      }
+    }
+    if (w == 0) {
+      float Gi = lane < n ? Gr[lane] : 0.f;           // padded tokens: log g = 0, beta = 0
+      sBeta[lane] = lane < n ? Br[lane] : 0.f;
+#pragma unroll
+      for (int off = 1; off < C; off <<= 1) {
+        const float o = __shfl_up(Gi, off, kWave);
+        if (lane >= off) Gi += o;
+      }
+      sG[lane] = Gi;
+    }
+    lds_sync();
+    const float gL = sG[C - 1];
+    if (w == 0) {   // per-token coefficients of the state-dependent part (read after the next barrier)
+      const float Gi = sG[lane], bt = sBeta[lane], rk = sRk[lane], rq = sRq[lane];
+      const float gam = __expf(Gi);
+      sCR[lane] = bt * gam * rk;                 // R = beta V - CR X
+      sCO[lane] = p.scale * gam * rq;            // O = CO (Q S0^T) + P U
+      sCS[lane] = __expf(gL - Gi) * rk;          // S1 = gamma_C S0 + K^T diag(CS) U
+    }
+    // The next chunk's transfer is issued once the LDS reads that the compiler
+    // cannot attribute to one buffer are done (it would otherwise wait for the
+    // transfer before them); it then overlaps the rest of this chunk.
+    auto start_next = [&]() {
+      if (t0 + C < tend) issue(nQ, nK, nV, nZ, nGr, nBr, t0 + C);
+      flush_out();
+    };
+
+    // ---- Q K^T and K K^T on the lower block triangle -> P (hi + lo), A.  Computed as
+    // K Q^T and K K^T (= their transposes) so that each lane holds one query row i
+    // and four consecutive keys m per accumulator quad: 8-byte LDS writes.
+    for (int tt = w; tt < 3; tt += NW) {
+      const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;     // rows i in tile ti, keys m in tile tj
+      f32x16 qk = {}, kk = {};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
+        qk = mfma32(a, ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
+        if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
+      }
+      const int i = 32 * ti + l32;                                // this lane's row
+      const float Gi = sG[i];
+      const float rowP = p.scale * sRq[i];
+      const float rowA = sBeta[i] * sRk[i];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
+        const float4 Gm = ld_f4(&sG[mb]), rkm = ld_f4(&sRk[mb]);
+        float pv[4], av[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e, m = mb + e;
+          const float t = m <= i ? __expf(Gi - f4get(Gm, e)) * f4get(rkm, e) : 0.f;   // masked before the exp
+          pv[e] = rowP * t * qk[r];
+          av[e] = m < i ? rowA * t * kk[r] : 0.f;
+        }
+        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
+        const uint32_t l0 = cvt2(pv[0] - bf_lo(h0), pv[1] - bf_hi(h0));
+        const uint32_t l1 = cvt2(pv[2] - bf_lo(h1), pv[3] - bf_hi(h1));
+        *reinterpret_cast<uint2*>(&sPh[i][mb]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(&sPl[i][mb]) = make_uint2(l0, l1);
+        if constexpr (!kSSD) {
+          *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
+          if ((i >> 4) == (mb >> 4))
+            *reinterpret_cast<float4*>(&sAd[i >> 4][i & 15][mb & 15]) = make_float4(av[0], av[1], av[2], av[3]);
+        }
+      }
+    }
+    if constexpr (!kSSD) {
+      if (w == NW - 1) {      // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
+        const int blk = lane >> 5, row = lane & 15, half = (lane >> 4) & 1;
+        *reinterpret_cast<uint4*>(&sTb[32 * blk + row][16 + 32 * blk + 8 * half]) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    lds_sync();
+    if constexpr (kSSD) start_next();
+
+    // ---- T = (I + A)^{-1} on the last wave (a single wave: no barrier inside)
+    if constexpr (!kSSD) {
+      if (w == NW - 1) {
+        {   // diagonal 16x16 blocks: lane 16 b + c solves column c of block b in fp32
+          const int b = lane >> 4, c = lane & 15;
+          float x[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][mm][i] * x[i];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sTb[16 * b + i][16 * b + c] = f32_to_bf16(x[i]);
+        }
+        // 16 -> 32 inside both diagonal 32x32 tiles: T[16..31][0..15] = -D1 (A10 D0)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int r0 = 32 * pp;
+          // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
+          bf16x4 bD;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[r0 + 4 * g16 + e][r0 + j16]);
+          f32x4 y = {};
+          y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
+          bf16x4 yb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+          f32x4 zz = {};
+          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[r0 + 16 + j16][r0 + 16 + 4 * g16])), yb, zz);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sTb[r0 + 16 + 4 * g16 + e][r0 + j16] = f32_to_bf16(-zz[e]);
+        }
+        // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
+        {
+          f32x16 y = {};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
+            bf16x8 bT;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[16 * s + 8 * hh + e][l32]);
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sAB[32 + l32][16 * s + 8 * hh]));
+            y = mfma32(a, bT, y);
+          }
+          f32x16 zz = {};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) zz = mfma32(lds_perm(&sTb[32 + l32][32 + 16 * s + 4 * hh]), acc_to_op(y, s), zz);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sTb[32 + acc_row(r, hh)][l32] = f32_to_bf16(-zz[r]);
+        }
+      }
+    }
+
+    // ---- state-dependent part, this wave's 32 d_v columns
     bf16x8 Sb[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) Sb[s] = acc_to_op(Sacc[s >> 1], s & 1);
-
     f32x16 Y[2], U[2];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
       Y[ti] = f32x16{};
       U[ti] = f32x16{};
-      const u16* qrow = &sm.Q[32 * ti + l32][4 * hh];
-      const u16* krow = &sm.K[32 * ti + l32][4 * hh];
+      const int row = 32 * ti + l32;
+      bf16x8 aq = join(ld4<DK>(Q, row, 4 * hh), ld4<DK>(Q, row, 8 + 4 * hh));
+      bf16x8 ak = aq;
+      if constexpr (!kSSD) ak = join(ld4<DK>(K, row, 4 * hh), ld4<DK>(K, row, 8 + 4 * hh));
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        Y[ti] = mfma32(lds_perm(qrow + 16 * s), Sb[s], Y[ti]);
-        if constexpr (!kSSD) U[ti] = mfma32(lds_perm(krow + 16 * s), Sb[s], U[ti]);   // X = K S0^T
+        bf16x8 aq_n = aq, ak_n = ak;
+        if (s + 1 < NKS) {
+          aq_n = join(ld4<DK>(Q, row, 16 * (s + 1) + 4 * hh), ld4<DK>(Q, row, 16 * (s + 1) + 8 + 4 * hh));
+          if constexpr (!kSSD) ak_n = join(ld4<DK>(K, row, 16 * (s + 1) + 4 * hh), ld4<DK>(K, row, 16 * (s + 1) + 8 + 4 * hh));
+        }
+        Y[ti] = mfma32(aq, Sb[s], Y[ti]);
+        if constexpr (!kSSD) U[ti] = mfma32(ak, Sb[s], U[ti]);       // X = K S0^T
+        aq = aq_n;
+        ak = ak_n;
       }
     }
-    // R = beta V - coefR X  (GDN),  U = beta V (delta-off); kept in U
-    float vkeep[kSSD ? 2 : 1][kSSD ? 16 : 1];
+    // V in accumulator layout through transpose reads
+    float vv[2][16];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int i0 = 32 * ti + 8 * q4 + 4 * hh;
-        const uint2 vw = *reinterpret_cast<const uint2*>(&sm.VT[col][i0]);
-        const float vv[4] = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
-                             __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u)};
+        const int ra = 32 * ti + 8 * q4 + 4 * (g16 >> 1) + (j16 >> 2);
+        const int ca = 32 * w + 16 * (g16 & 1) + 4 * (j16 & 3);
+        const uint2 t = ldtr<DV>(V, ra, ca);
+        vv[ti][4 * q4 + 0] = bf_lo(t.x);
+        vv[ti][4 * q4 + 1] = bf_hi(t.x);
+        vv[ti][4 * q4 + 2] = bf_lo(t.y);
+        vv[ti][4 * q4 + 3] = bf_hi(t.y);
+      }
+    // R = beta V - beta gamma r_k X (GDN); U = beta V (delta-off)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int ib = 32 * ti + 8 * q4 + 4 * hh;
+        const float4 bi = ld_f4(&sBeta[ib]);
+        float4 cr = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (!kSSD) cr = ld_f4(&sCR[ib]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e, i = i0 + e;
-          if constexpr (kSSD) {
-            U[ti][r] = sm.beta[i] * vv[e];
-            vkeep[ti][r] = vv[e];
-          } else {
-            U[ti][r] = sm.beta[i] * vv[e] - sm.coefR[i] * U[ti][r];
-          }
+          const int r = 4 * q4 + e;
+          U[ti][r] = kSSD ? f4get(bi, e) * vv[ti][r] : f4get(bi, e) * vv[ti][r] - f4get(cr, e) * U[ti][r];
         }
       }
-    }
     if constexpr (!kSSD) {
-      // U = R + (T - I) bf16(R) = (R - bf16(R)) + T bf16(R); T is unit lower, so row
-      // tile 0 needs k-steps 0..1 only
+      lds_sync();                                   // T complete
+      start_next();
+      // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile 0 needs k-steps 0..1
       bf16x8 Rb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) Rb[s] = acc_to_op(U[s >> 1], s & 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) U[s >> 1][8 * (s & 1) + e] -= (float)Rb[s][e];
-      }
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
-        const u16* trow = &sm.Tb[32 * ti + l32][4 * hh];
+        const u16* trow = &sTb[32 * ti + l32][4 * hh];
 #pragma unroll
         for (int s = 0; s < 2 * (ti + 1); ++s) U[ti] = mfma32(lds_perm(trow + 16 * s), Rb[s], U[ti]);
       }
     }
-    // O = coefO Y + P U with two-term splits of P and U
+    // O = scale gamma r_q Y + P U (two-term splits of P and U)
     {
       bf16x8 Uh[4], Ul[4];
 #pragma unroll
@@ -499,73 +528,124 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Y[ti][r] *= sm.coefO[32 * ti + acc_row(r, hh)];
-        const u16* phrow = &sm.Ph[32 * ti + l32][4 * hh];
-        const u16* plrow = &sm.Pl[32 * ti + l32][4 * hh];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ib = 32 * ti + 8 * q4 + 4 * hh;
+          const float4 co = ld_f4(&sCO[ib]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Y[ti][4 * q4 + e] *= f4get(co, e);
+        }
+        const u16* phrow = &sPh[32 * ti + l32][4 * hh];
+        const u16* plrow = &sPl[32 * ti + l32][4 * hh];
+        bf16x8 ph = lds_perm(phrow), pl = lds_perm(plrow);
 #pragma unroll
         for (int s = 0; s < 2 * (ti + 1); ++s) {
-          const bf16x8 ph = lds_perm(phrow + 16 * s), pl = lds_perm(plrow + 16 * s);
+          bf16x8 ph_n = ph, pl_n = pl;
+          if (s + 1 < 2 * (ti + 1)) {
+            ph_n = lds_perm(phrow + 16 * (s + 1));
+            pl_n = lds_perm(plrow + 16 * (s + 1));
+          }
           Y[ti] = mfma32(ph, Uh[s], Y[ti]);
           Y[ti] = mfma32(pl, Uh[s], Y[ti]);
           Y[ti] = mfma32(ph, Ul[s], Y[ti]);
+          ph = ph_n;
+          pl = pl_n;
         }
       }
     }
-    // epilogue and store of this chunk's outputs
+    // epilogue (delta-off: D skip and silu(z) gate; x and z re-read from LDS)
+    if constexpr (kSSD) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
+      for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 32 * ti + acc_row(r, hh);
-        if (i < n) {
-          float o = Y[ti][r];
-          const int64_t tok = t0 + i;
-          if constexpr (kSSD) {
-            const u16* Db = reinterpret_cast<const u16*>(p.D);
-            if (Db) o += bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]) * vkeep[ti][r];
-            if (p.z) {
-              const float zz = bf16_to_f32(reinterpret_cast<const u16*>(p.z)[tok * p.z_stride + (int64_t)h * DV + col]);
-              o *= zz * sigmoid_f(zz);
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ra = 32 * ti + 8 * q4 + 4 * (g16 >> 1) + (j16 >> 2);
+          const int ca = 32 * w + 16 * (g16 & 1) + 4 * (j16 & 3);
+          const uint2 tx = ldtr<DV>(V, ra, ca);
+          const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
+          float zz[4] = {1.f, 1.f, 1.f, 1.f};
+          if (p.z) {
+            const uint2 tz = ldtr<DV>(Z, ra, ca);
+            const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
           }
-          Elem<OutT>::store(ob, tok * p.out_stride + (int64_t)h * DV + col, o);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            Y[ti][r] = (Y[ti][r] + Dc * xv[e]) * zz[e];
+          }
         }
-      }
     }
-    // state update: S^T = gamma_C S^T + K^T diag(coefS) U  (split hi + lo)
+    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored after the next transfer
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2)
+          opk[ti][r2] = cvt2(Y[ti][2 * r2], Y[ti][2 * r2 + 1]);
+      o_t0 = t0;
+      o_n = n;
+    } else {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 32 * ti + acc_row(r, hh);
+          if (i < n) Elem<OutT>::store(ob, (int64_t)(t0 + i) * p.out_stride, Y[ti][r]);
+        }
+    }
+    // state update: S^T = gamma_C S^T + K^T diag(exp(G_C - G) r_k) U  (split hi + lo)
     {
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ib = 32 * ti + 8 * q4 + 4 * hh;
+          const float4 cs = ld_f4(&sCS[ib]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) U[ti][4 * q4 + e] *= f4get(cs, e);
+        }
       bf16x8 Wh[4], Wl[4];
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) U[ti][r] *= sm.coefS[32 * ti + acc_row(r, hh)];
-      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc_split(U[s >> 1], s & 1, Wh[s], Wl[s]);
       const float gC = __expf(gL);
+      // A operand K^T: row d_k = 32 tk + l32, tokens 16 s + 4 hh + e and 16 s + 8 + 4 hh + e
+      const int rb = 4 * (g16 >> 1) + (j16 >> 2);
 #pragma unroll
       for (int tk = 0; tk < NTK; ++tk) {
         Sacc[tk] *= gC;
-        const u16* krow = &sm.KT[32 * tk + l32][4 * hh];
+        const int ca = 32 * tk + 16 * (g16 & 1) + 4 * (j16 & 3);
+        bf16x8 kt = join(ldtr<DK>(K, rb, ca), ldtr<DK>(K, rb + 8, ca));
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 kt = lds_perm(krow + 16 * s);
+          bf16x8 kt_n = kt;
+          if (s + 1 < 4) kt_n = join(ldtr<DK>(K, 16 * (s + 1) + rb, ca), ldtr<DK>(K, 16 * (s + 1) + 8 + rb, ca));
           Sacc[tk] = mfma32(kt, Wh[s], Sacc[tk]);
           Sacc[tk] = mfma32(kt, Wl[s], Sacc[tk]);
+          kt = kt_n;
         }
       }
     }
+  };
+
+  lds_u16 *lQ0 = (lds_u16*)sQ0, *lQ1 = (lds_u16*)sQ1, *lK0 = (lds_u16*)sK0, *lK1 = (lds_u16*)sK1;
+  lds_u16 *lV0 = (lds_u16*)sV0, *lV1 = (lds_u16*)sV1, *lZ0 = (lds_u16*)sZ0, *lZ1 = (lds_u16*)sZ1;
+  lds_f32 *lG0 = (lds_f32*)sGr0, *lG1 = (lds_f32*)sGr1, *lB0 = (lds_f32*)sBr0, *lB1 = (lds_f32*)sBr1;
+  if (tbeg < tend) issue(lQ0, lK0, lV0, lZ0, lG0, lB0, tbeg);
+  for (int t0 = tbeg; t0 < tend; t0 += 2 * C) {
+    chunk(sQ0, sK0, sV0, sZ0, sGr0, sBr0, lQ1, lK1, lV1, lZ1, lG1, lB1, t0);
+    if (t0 + C < tend)
+      chunk(sQ1, sK1, sV1, sZ1, sGr1, sBr1, lQ0, lK0, lV0, lZ0, lG0, lB0, t0 + C);
   }
+  flush_out();
 
 #pragma unroll
-  for (int tk = 0; tk < NTK; ++tk) {
+  for (int tk = 0; tk < NTK; ++tk)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 v = make_float4(Sacc[tk][4 * q4 + 0], Sacc[tk][4 * q4 + 1], Sacc[tk][4 * q4 + 2],
                                    Sacc[tk][4 * q4 + 3]);
       *reinterpret_cast<float4*>(state + (int64_t)col * DK + 32 * tk + 8 * q4 + 4 * hh) = v;
     }
-  }
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
@@ -575,25 +655,19 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int DK, int DV>
-hipError_t launch_dims(const SeqLaunch& p, hipStream_t stream) {
-  if (p.ssd) return p.out_bf16 ? launch_typed<DK, DV, true, u16>(p, stream)
-                               : launch_typed<DK, DV, true, float>(p, stream);
-  return p.out_bf16 ? launch_typed<DK, DV, false, u16>(p, stream)
-                    : launch_typed<DK, DV, false, float>(p, stream);
-}
-
 }  // namespace
 
 bool chunked_supported(const SeqLaunch& p) {
-  return p.in_bf16 && p.d_k == 128 && (p.d_v == 128 || p.d_v == 64) && p.N <= 65535;
+  if (!p.in_bf16 || p.d_k != 128 || p.N > 65535) return false;
+  return p.ssd ? p.d_v == 64 : p.d_v == 128;
 }
 
 hipError_t launch_chunked(const SeqLaunch& p, hipStream_t stream) {
   if (p.N == 0) return hipSuccess;
-  if (p.d_k == 128 && p.d_v == 128) return launch_dims<128, 128>(p, stream);
-  if (p.d_k == 128 && p.d_v == 64) return launch_dims<128, 64>(p, stream);
-  return hipErrorInvalidValue;
+  if (p.ssd) return p.out_bf16 ? launch_typed<128, 64, true, u16>(p, stream)
+                               : launch_typed<128, 64, true, float>(p, stream);
+  return p.out_bf16 ? launch_typed<128, 128, false, u16>(p, stream)
+                    : launch_typed<128, 128, false, float>(p, stream);
 }
 
 }  // namespace gdn
