@@ -120,10 +120,13 @@ def main():
     maxlen = int(max(ext.cu_seqlens[1:] - ext.cu_seqlens[:-1]))
 
     if args.calibrate_copy_mib:
-        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
+        # a plain streaming kernel of known traffic (reads and writes N bytes) whose
+        # FETCH_SIZE / WRITE_SIZE readings scale the counters of the GDN kernels
+        src = torch.ones((args.calibrate_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
+        del src, dst
 
     names = ["gate_extend", "extend", "gate_decode", "decode"]
 

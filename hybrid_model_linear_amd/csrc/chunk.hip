@@ -62,6 +62,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma1632(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -117,6 +120,23 @@ __device__ __forceinline__ void acc_split(const f32x16& a, int half, bf16x8& hi,
     const float x0 = a[o + 2 * e], x1 = a[o + 2 * e + 1];
     h[e] = cvt2(x0, x1);
     l[e] = cvt2(x0 - __uint_as_float(h[e] << 16), x1 - __uint_as_float(h[e] & 0xffff0000u));
+  }
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+// Two 16x16 accumulator tiles (rows 4 g + r of tile t0 and of tile t1) as one B
+// operand of a 16x16x32 MFMA whose 32 k slots are (g, e): e < 4 -> tile t0 row
+// 4 g + e, e >= 4 -> tile t1 row 4 g + e - 4.
+__device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
+  return as_bf16x8(make_uint4(cvt2(a[0], a[1]), cvt2(a[2], a[3]), cvt2(b[0], b[1]), cvt2(b[2], b[3])));
+}
+__device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = cvt2(x[2 * e], x[2 * e + 1]);
+    l[e] = cvt2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
   }
   hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
   lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
@@ -178,13 +198,13 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
-__global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p) {
-  constexpr int NW = DV / 32;
+__global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p) {
+  constexpr int NW = DV / 16;      // waves: 16 d_v columns each
   constexpr int NT = NW * kWave;
-  constexpr int NKS = DK / 16;     // k-steps over d_k
-  constexpr int NTK = DK / 32;     // S^T row tiles
+  constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
+  constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64), "tile shapes");
-  static_assert(kSSD || NW == 4, "GDN mode uses four waves (d_v = 128)");
+  static_assert(NW >= 4, "four or more waves");
 
   // double-buffered chunk data (distinct LDS objects: see the header comment)
   __shared__ __attribute__((aligned(16))) u16 sQ0[C * (DK + 8)], sQ1[C * (DK + 8)];
@@ -209,9 +229,9 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, w = tid / kWave;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int col = 32 * w + l32;                            // this lane's d_v column
-  const int g16 = lane >> 4, j16 = lane & 15;              // transpose-read group / lane
+  const int l32 = lane & 31, hh = lane >> 5;               // 32x32 MFMA lane split (phase A)
+  const int g16 = lane >> 4, j16 = lane & 15;              // 16x16 MFMA / transpose-read split
+  const int col = 16 * w + j16;                            // this lane's d_v column
 
   const u16* qg = reinterpret_cast<const u16*>(p.q) + (int64_t)j * DK;
   const u16* kg = reinterpret_cast<const u16*>(p.k) + (int64_t)j * DK;
@@ -219,22 +239,16 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
   const u16* zg = reinterpret_cast<const u16*>(p.z) + (int64_t)h * DV;
   OutT* ob = reinterpret_cast<OutT*>(p.out) + (int64_t)h * DV + col;
 
+  // S^T tiles in 16x16 accumulator layout: Sacc[tk][r] = S[col][16 tk + 4 g16 + r]
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
-  f32x16 Sacc[NTK];
-  if (init) {
+  f32x4 Sacc[NTK];
 #pragma unroll
-    for (int tk = 0; tk < NTK; ++tk)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 32 * tk + 8 * q4 + 4 * hh);
-        Sacc[tk][4 * q4 + 0] = v.x;
-        Sacc[tk][4 * q4 + 1] = v.y;
-        Sacc[tk][4 * q4 + 2] = v.z;
-        Sacc[tk][4 * q4 + 3] = v.w;
-      }
-  } else {
-#pragma unroll
-    for (int tk = 0; tk < NTK; ++tk) Sacc[tk] = f32x16{};
+  for (int tk = 0; tk < NTK; ++tk) {
+    Sacc[tk] = f32x4{};
+    if (init) {
+      const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16);
+      Sacc[tk] = f32x4{v.x, v.y, v.z, v.w};
+    }
   }
 
   // delta-off D skip coefficient of this lane's column (read once, outside the loop)
@@ -245,7 +259,7 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
   }
 
   // bf16 outputs of the previous chunk, stored after the next transfer is issued
-  uint32_t opk[2][8];
+  uint32_t opk[4][2];
   int o_t0 = -1, o_n = 0;
 
   auto issue = [&](lds_u16* dQ, lds_u16* dK, lds_u16* dV, lds_u16* dZ, lds_f32* dG, lds_f32* dB, int t0) {
@@ -267,11 +281,11 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
       if (o_t0 < 0) return;
       u16* o16 = reinterpret_cast<u16*>(ob);
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * ti + acc_row(r, hh);
-          const uint32_t wv = opk[ti][r >> 1];
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * rt + 4 * g16 + r;
+          const uint32_t wv = opk[rt][r >> 1];
           if (i < o_n) o16[(int64_t)(o_t0 + i) * p.out_stride] = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
         }
       o_t0 = -1;
@@ -284,6 +298,14 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
                    const float* Br, lds_u16* nQ, lds_u16* nK, lds_u16* nV, lds_u16* nZ, lds_f32* nGr,
                    lds_f32* nBr, int t0) {
     const int n = min(C, tend - t0);
+    // Lane-derived indices are recomputed in every chunk (an opaque copy of the lane
+    // id): hoisting the many per-lane LDS addresses out of the loop would keep them
+    // all live at once and spill them.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int l32 = lane_o & 31, hh = lane_o >> 5;
+    const int g16 = lane_o >> 4, j16 = lane_o & 15;
+    const int tid = w * kWave + lane_o;
     wait_vm_all();
     lds_sync();                                   // chunk data visible; previous chunk done
 
@@ -351,7 +373,7 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
       const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;     // rows i in tile ti, keys m in tile tj
       f32x16 qk = {}, kk = {};
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
+      for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
         const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
         qk = mfma32(a, ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
         if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
@@ -447,181 +469,149 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
       }
     }
 
-    // ---- state-dependent part, this wave's 32 d_v columns
-    bf16x8 Sb[NKS];
+    // ---- state-dependent part, this wave's 16 d_v columns (16x16x32 MFMAs)
+    bf16x8 Sb[NKS];            // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) Sb[s] = acc_to_op(Sacc[s >> 1], s & 1);
-    f32x16 Y[2], U[2];
+    for (int s2 = 0; s2 < NKS; ++s2) Sb[s2] = pair_to_op(Sacc[2 * s2], Sacc[2 * s2 + 1]);
+    f32x4 Y[4], U[4];          // row tiles of 16 tokens: rows 16 rt + 4 g16 + r
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      Y[ti] = f32x16{};
-      U[ti] = f32x16{};
-      const int row = 32 * ti + l32;
-      bf16x8 aq = join(ld4<DK>(Q, row, 4 * hh), ld4<DK>(Q, row, 8 + 4 * hh));
-      bf16x8 ak = aq;
-      if constexpr (!kSSD) ak = join(ld4<DK>(K, row, 4 * hh), ld4<DK>(K, row, 8 + 4 * hh));
+    for (int rt = 0; rt < 4; ++rt) {
+      Y[rt] = f32x4{};
+      U[rt] = f32x4{};
+      const int row = 16 * rt + j16;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        bf16x8 aq_n = aq, ak_n = ak;
-        if (s + 1 < NKS) {
-          aq_n = join(ld4<DK>(Q, row, 16 * (s + 1) + 4 * hh), ld4<DK>(Q, row, 16 * (s + 1) + 8 + 4 * hh));
-          if constexpr (!kSSD) ak_n = join(ld4<DK>(K, row, 16 * (s + 1) + 4 * hh), ld4<DK>(K, row, 16 * (s + 1) + 8 + 4 * hh));
+      for (int s2 = 0; s2 < NKS; ++s2) {
+        const bf16x8 aq = join(ld4<DK>(Q, row, 32 * s2 + 4 * g16), ld4<DK>(Q, row, 32 * s2 + 16 + 4 * g16));
+        Y[rt] = mfma1632(aq, Sb[s2], Y[rt]);
+        if constexpr (!kSSD) {
+          const bf16x8 ak = join(ld4<DK>(K, row, 32 * s2 + 4 * g16), ld4<DK>(K, row, 32 * s2 + 16 + 4 * g16));
+          U[rt] = mfma1632(ak, Sb[s2], U[rt]);                 // X = K S0^T
         }
-        Y[ti] = mfma32(aq, Sb[s], Y[ti]);
-        if constexpr (!kSSD) U[ti] = mfma32(ak, Sb[s], U[ti]);       // X = K S0^T
-        aq = aq_n;
-        ak = ak_n;
       }
     }
-    // V in accumulator layout through transpose reads
-    float vv[2][16];
+    // R = beta V - CR X (GDN); U = beta V (delta-off).  V through transpose reads.
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int rt = 0; rt < 4; ++rt) {
+      const int ib = 16 * rt + 4 * g16;
+      const uint2 t = ldtr<DV>(V, ib + (j16 >> 2), 16 * w + 4 * (j16 & 3));
+      const float vv[4] = {bf_lo(t.x), bf_hi(t.x), bf_lo(t.y), bf_hi(t.y)};
+      const float4 bi = ld_f4(&sBeta[ib]);
+      if constexpr (kSSD) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int ra = 32 * ti + 8 * q4 + 4 * (g16 >> 1) + (j16 >> 2);
-        const int ca = 32 * w + 16 * (g16 & 1) + 4 * (j16 & 3);
-        const uint2 t = ldtr<DV>(V, ra, ca);
-        vv[ti][4 * q4 + 0] = bf_lo(t.x);
-        vv[ti][4 * q4 + 1] = bf_hi(t.x);
-        vv[ti][4 * q4 + 2] = bf_lo(t.y);
-        vv[ti][4 * q4 + 3] = bf_hi(t.y);
+        for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e];
+      } else {
+        const float4 cr = ld_f4(&sCR[ib]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e] - f4get(cr, e) * U[rt][e];
       }
-    // R = beta V - beta gamma r_k X (GDN); U = beta V (delta-off)
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int ib = 32 * ti + 8 * q4 + 4 * hh;
-        const float4 bi = ld_f4(&sBeta[ib]);
-        float4 cr = make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (!kSSD) cr = ld_f4(&sCR[ib]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          U[ti][r] = kSSD ? f4get(bi, e) * vv[ti][r] : f4get(bi, e) * vv[ti][r] - f4get(cr, e) * U[ti][r];
-        }
-      }
+    }
     if constexpr (!kSSD) {
       lds_sync();                                   // T complete
       start_next();
-      // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile 0 needs k-steps 0..1
-      bf16x8 Rb[4];
+      // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
+      bf16x8 Rb[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Rb[s] = acc_to_op(U[s >> 1], s & 1);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        Rb[s2] = pair_to_op(U[2 * s2], U[2 * s2 + 1]);
+        const uint4 rw = __builtin_bit_cast(uint4, Rb[s2]);
+        U[2 * s2][0] -= bf_lo(rw.x);
+        U[2 * s2][1] -= bf_hi(rw.x);
+        U[2 * s2][2] -= bf_lo(rw.y);
+        U[2 * s2][3] -= bf_hi(rw.y);
+        U[2 * s2 + 1][0] -= bf_lo(rw.z);
+        U[2 * s2 + 1][1] -= bf_hi(rw.z);
+        U[2 * s2 + 1][2] -= bf_lo(rw.w);
+        U[2 * s2 + 1][3] -= bf_hi(rw.w);
+      }
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int rt = 0; rt < 4; ++rt) {
+        const u16* trow = &sTb[16 * rt + j16][4 * g16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) U[s >> 1][8 * (s & 1) + e] -= (float)Rb[s][e];
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
-        const u16* trow = &sTb[32 * ti + l32][4 * hh];
-#pragma unroll
-        for (int s = 0; s < 2 * (ti + 1); ++s) U[ti] = mfma32(lds_perm(trow + 16 * s), Rb[s], U[ti]);
+        for (int s2 = 0; s2 <= (rt >> 1); ++s2) U[rt] = mfma1632(join(*reinterpret_cast<const uint2*>(trow + 32 * s2),
+                                                                       *reinterpret_cast<const uint2*>(trow + 32 * s2 + 16)),
+                                                                  Rb[s2], U[rt]);
       }
     }
-    // O = scale gamma r_q Y + P U (two-term splits of P and U)
+    // O = CO (Q S0^T) + P U (two-term splits of P and U)
     {
-      bf16x8 Uh[4], Ul[4];
+      bf16x8 Uh[2], Ul[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc_split(U[s >> 1], s & 1, Uh[s], Ul[s]);
+      for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Uh[s2], Ul[s2]);
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti) {
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 co = ld_f4(&sCO[16 * rt + 4 * g16]);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ib = 32 * ti + 8 * q4 + 4 * hh;
-          const float4 co = ld_f4(&sCO[ib]);
+        for (int e = 0; e < 4; ++e) Y[rt][e] *= f4get(co, e);
+        const u16* phrow = &sPh[16 * rt + j16][4 * g16];
+        const u16* plrow = &sPl[16 * rt + j16][4 * g16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Y[ti][4 * q4 + e] *= f4get(co, e);
-        }
-        const u16* phrow = &sPh[32 * ti + l32][4 * hh];
-        const u16* plrow = &sPl[32 * ti + l32][4 * hh];
-        bf16x8 ph = lds_perm(phrow), pl = lds_perm(plrow);
-#pragma unroll
-        for (int s = 0; s < 2 * (ti + 1); ++s) {
-          bf16x8 ph_n = ph, pl_n = pl;
-          if (s + 1 < 2 * (ti + 1)) {
-            ph_n = lds_perm(phrow + 16 * (s + 1));
-            pl_n = lds_perm(plrow + 16 * (s + 1));
-          }
-          Y[ti] = mfma32(ph, Uh[s], Y[ti]);
-          Y[ti] = mfma32(pl, Uh[s], Y[ti]);
-          Y[ti] = mfma32(ph, Ul[s], Y[ti]);
-          ph = ph_n;
-          pl = pl_n;
+        for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+          const bf16x8 ph = join(*reinterpret_cast<const uint2*>(phrow + 32 * s2), *reinterpret_cast<const uint2*>(phrow + 32 * s2 + 16));
+          const bf16x8 pl = join(*reinterpret_cast<const uint2*>(plrow + 32 * s2), *reinterpret_cast<const uint2*>(plrow + 32 * s2 + 16));
+          Y[rt] = mfma1632(ph, Uh[s2], Y[rt]);
+          Y[rt] = mfma1632(pl, Uh[s2], Y[rt]);
+          Y[rt] = mfma1632(ph, Ul[s2], Y[rt]);
         }
       }
     }
     // epilogue (delta-off: D skip and silu(z) gate; x and z re-read from LDS)
     if constexpr (kSSD) {
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int rt = 0; rt < 4; ++rt) {
+        const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = 16 * w + 4 * (j16 & 3);
+        const uint2 tx = ldtr<DV>(V, ra, ca);
+        const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
+        float zz[4] = {1.f, 1.f, 1.f, 1.f};
+        if (p.z) {
+          const uint2 tz = ldtr<DV>(Z, ra, ca);
+          const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ra = 32 * ti + 8 * q4 + 4 * (g16 >> 1) + (j16 >> 2);
-          const int ca = 32 * w + 16 * (g16 & 1) + 4 * (j16 & 3);
-          const uint2 tx = ldtr<DV>(V, ra, ca);
-          const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
-          float zz[4] = {1.f, 1.f, 1.f, 1.f};
-          if (p.z) {
-            const uint2 tz = ldtr<DV>(Z, ra, ca);
-            const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
-            Y[ti][r] = (Y[ti][r] + Dc * xv[e]) * zz[e];
-          }
+          for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[rt][e] = (Y[rt][e] + Dc * xv[e]) * zz[e];
+      }
     }
     if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored after the next transfer
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2)
-          opk[ti][r2] = cvt2(Y[ti][2 * r2], Y[ti][2 * r2 + 1]);
+      for (int rt = 0; rt < 4; ++rt) {
+        opk[rt][0] = cvt2(Y[rt][0], Y[rt][1]);
+        opk[rt][1] = cvt2(Y[rt][2], Y[rt][3]);
+      }
       o_t0 = t0;
       o_n = n;
     } else {
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * ti + acc_row(r, hh);
-          if (i < n) Elem<OutT>::store(ob, (int64_t)(t0 + i) * p.out_stride, Y[ti][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * rt + 4 * g16 + r;
+          if (i < n) Elem<OutT>::store(ob, (int64_t)(t0 + i) * p.out_stride, Y[rt][r]);
         }
     }
-    // state update: S^T = gamma_C S^T + K^T diag(exp(G_C - G) r_k) U  (split hi + lo)
+    // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
     {
 #pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 cs = ld_f4(&sCS[16 * rt + 4 * g16]);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ib = 32 * ti + 8 * q4 + 4 * hh;
-          const float4 cs = ld_f4(&sCS[ib]);
+        for (int e = 0; e < 4; ++e) U[rt][e] *= f4get(cs, e);
+      }
+      bf16x8 Wh[2], Wl[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) U[ti][4 * q4 + e] *= f4get(cs, e);
-        }
-      bf16x8 Wh[4], Wl[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc_split(U[s >> 1], s & 1, Wh[s], Wl[s]);
+      for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Wh[s2], Wl[s2]);
       const float gC = __expf(gL);
-      // A operand K^T: row d_k = 32 tk + l32, tokens 16 s + 4 hh + e and 16 s + 8 + 4 hh + e
-      const int rb = 4 * (g16 >> 1) + (j16 >> 2);
+      // A operand K^T: row d_k = 16 tk + j16; k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
+      const int rb = 4 * g16 + (j16 >> 2);
 #pragma unroll
       for (int tk = 0; tk < NTK; ++tk) {
         Sacc[tk] *= gC;
-        const int ca = 32 * tk + 16 * (g16 & 1) + 4 * (j16 & 3);
-        bf16x8 kt = join(ldtr<DK>(K, rb, ca), ldtr<DK>(K, rb + 8, ca));
+        const int ca = 16 * tk + 4 * (j16 & 3);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 kt_n = kt;
-          if (s + 1 < 4) kt_n = join(ldtr<DK>(K, 16 * (s + 1) + rb, ca), ldtr<DK>(K, 16 * (s + 1) + 8 + rb, ca));
-          Sacc[tk] = mfma32(kt, Wh[s], Sacc[tk]);
-          Sacc[tk] = mfma32(kt, Wl[s], Sacc[tk]);
-          kt = kt_n;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, ca), ldtr<DK>(K, 32 * s2 + 16 + rb, ca));
+          Sacc[tk] = mfma1632(kt, Wh[s2], Sacc[tk]);
+          Sacc[tk] = mfma1632(kt, Wl[s2], Sacc[tk]);
         }
       }
     }
@@ -640,17 +630,13 @@ __global__ void __launch_bounds__((DV / 32) * kWave, 1) chunk_kernel(SeqLaunch p
 
 #pragma unroll
   for (int tk = 0; tk < NTK; ++tk)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v = make_float4(Sacc[tk][4 * q4 + 0], Sacc[tk][4 * q4 + 1], Sacc[tk][4 * q4 + 2],
-                                   Sacc[tk][4 * q4 + 3]);
-      *reinterpret_cast<float4*>(state + (int64_t)col * DK + 32 * tk + 8 * q4 + 4 * hh) = v;
-    }
+    *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
+        make_float4(Sacc[tk][0], Sacc[tk][1], Sacc[tk][2], Sacc[tk][3]);
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
 hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
-  dim3 grid(p.H_v, p.N), block((DV / 32) * kWave);
+  dim3 grid(p.H_v, p.N), block((DV / 16) * kWave);
   hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
