@@ -21,20 +21,19 @@
 // two-term (hi + lo) bf16 splits of P, U and the scaled U.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
-// order; the state never leaves registers.  Each wave owns 32 of the d_v columns
-// (state rows are independent given the chunk's keys), held as S^T tiles in MFMA
-// accumulator layout and fed back as B operands directly: the reduction index of
-// a 32x32x16 MFMA may be permuted freely when both operands agree, so A operands
-// are read from LDS in the accumulator's row order.
+// order; the state never leaves registers.  Each wave owns 16 of the d_v columns
+// (state rows are independent given the chunk's keys), held as S^T tiles in 16x16
+// MFMA accumulator layout and fed back as B operands directly: the reduction index
+// of an MFMA may be permuted freely when both operands agree, so A operands are
+// read from LDS in the accumulator's row order.
 //
-// Data movement: q, k, v (and z) rows of chunk c+1 stream from HBM straight into
-// LDS (global_load_lds, 16 B per lane) while chunk c is computed; the two LDS
-// buffers are distinct objects and the chunk loop is unrolled by two, so no LDS
-// read has to wait on the transfer in flight.  Tiles are row-major and padded
-// by one 16-byte segment per row.  K^T and
-// V^T operands come from the row-major tiles through the LDS transpose read
-// (ds_read_b64_tr_b16): lane j of each 16-lane group receives column c0 + j of the
-// four rows addressed by the group's lanes 4e + j/4.
+// Data movement: q, k, v (and z) rows and gate values of chunk c+1 are loaded into
+// registers at the start of chunk c and written to the other LDS buffer at its end,
+// so their HBM latency hides behind a whole chunk of compute.  Tiles are row-major
+// and padded by one 16-byte segment per row.  K^T and V^T operands come from the
+// row-major tiles through the LDS transpose read (ds_read_b64_tr_b16): lane j of
+// each 16-lane group receives column c0 + j of the four rows addressed by the
+// group's lanes 4e + j/4.
 //
 // Per chunk: the state-independent part (Q K^T, K K^T, P, A) runs on three waves,
 // then one wave builds T (diagonal 16x16 blocks by fp32 forward substitution,
@@ -48,11 +47,9 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64;            // chunk length
-constexpr int kPS = C + 8;       // row length (bf16) of the padded C x C tiles
+constexpr int kPS = C + 4;       // row length (bf16) of the padded C x C tiles: 34 dwords,
+                                 // so 16 consecutive rows hit distinct bank pairs
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) u16 lds_u16;
-typedef __attribute__((address_space(3))) float lds_f32;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -151,43 +148,47 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ------------------------------------------------------------------ chunk transfer
-// One padded 64-row tile of D bf16 columns, (D + 8) * 2 bytes per row, copied as
-// 1 KiB wave instructions (64 lanes x 16 B, lane l -> byte 16 l of the instruction's
-// block) spread over the NW waves; a lane that lands on a row's pad segment
-// re-reads that row's first segment.  Rows past the sequence end re-read row t0
-// (always valid): their values are finite and every coefficient that touches
-// them is zero.
-template <int D, int NW>
-__device__ __forceinline__ void dma_tile(lds_u16* lds_tile, const u16* gbase, int64_t gstride, int t0,
-                                         int n) {
-  constexpr int RB = (D + 8) * 2;              // bytes per padded row
-  constexpr int NI = 64 * RB / 1024;           // wave instructions per tile
-  static_assert(NI * 1024 == 64 * RB, "tile is a whole number of 1 KiB blocks");
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int it = 0; it < (NI + NW - 1) / NW; ++it) {
-    const int m = w + it * NW;
-    if (m < NI) {
-      const int b = m * 1024 + 16 * lane;
-      const int r = b / RB;
-      const int sg = (b % RB) / 16;
-      const int64_t t = t0 + (r < n ? r : 0);
-      const int seg = sg < D / 8 ? sg : 0;
-      __builtin_amdgcn_global_load_lds(gbase + t * gstride + 8 * seg, (lds_void*)(lds_tile + m * 512), 16, 0, 0);
+// The next chunk's q, k, v (and z) rows and gate values are loaded into registers
+// at the start of the current chunk and stored into the other LDS buffer at its
+// end, so the HBM latency overlaps a whole chunk of compute.  Consecutive threads
+// read consecutive 16-byte segments of a row (coalesced); rows past the sequence
+// end re-read row t0 (always valid): their values are finite and every
+// coefficient that touches them is zero.
+template <int D, int NT>
+struct TileRegs {
+  static constexpr int NSEG = D / 8;                  // 16-byte segments per row
+  static constexpr int N = 64 * NSEG / NT;            // segments per thread
+  static_assert(N * NT == 64 * NSEG && (N == 2 || N == 4), "segments split evenly");
+  uint4 s0, s1, s2, s3;                               // named registers, no array (kept out of scratch)
+  __device__ __forceinline__ static uint4 ld(const u16* gbase, int64_t gstride, int t0, int n, int i) {
+    const int sidx = threadIdx.x + i * NT, r = sidx / NSEG, c = sidx % NSEG;
+    const int64_t t = t0 + (r < n ? r : 0);
+    return *reinterpret_cast<const uint4*>(gbase + t * gstride + 8 * c);
+  }
+  __device__ __forceinline__ static void st(u16* tile, int i, uint4 v) {
+    const int sidx = threadIdx.x + i * NT, r = sidx / NSEG, c = sidx % NSEG;
+    *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
+  }
+  __device__ __forceinline__ void load(const u16* gbase, int64_t gstride, int t0, int n) {
+    s0 = ld(gbase, gstride, t0, n, 0);
+    s1 = ld(gbase, gstride, t0, n, 1);
+    if constexpr (N == 4) {
+      s2 = ld(gbase, gstride, t0, n, 2);
+      s3 = ld(gbase, gstride, t0, n, 3);
     }
   }
-}
-// per-token fp32 gate values of one v-head ([T, H_v] layout), issued by wave 0
-__device__ __forceinline__ void dma_gate(lds_f32* lds_vec, const float* g, int H_v, int h, int t0, int n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = t0 + (lane < n ? lane : 0);
-  __builtin_amdgcn_global_load_lds(g + t * H_v + h, (lds_void*)lds_vec, 4, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+  __device__ __forceinline__ void store(u16* tile) const {
+    st(tile, 0, s0);
+    st(tile, 1, s1);
+    if constexpr (N == 4) {
+      st(tile, 2, s2);
+      st(tile, 3, s3);
+    }
+  }
+};
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() is a workgroup-scope
-// fence and would also wait for the global->LDS transfer in flight; here the
+// fence and would also wait for the next chunk's global loads in flight; here the
 // wave's own LDS accesses are drained (lgkmcnt(0)) and the compiler is kept from
 // moving memory accesses across the barrier.
 __device__ __forceinline__ void lds_sync() {
@@ -206,7 +207,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
   static_assert(DK == 128 && (DV == 128 || DV == 64), "tile shapes");
   static_assert(NW >= 4, "four or more waves");
 
-  // double-buffered chunk data (distinct LDS objects: see the header comment)
+  // double-buffered chunk data
   __shared__ __attribute__((aligned(16))) u16 sQ0[C * (DK + 8)], sQ1[C * (DK + 8)];
   __shared__ __attribute__((aligned(16))) u16 sK0[C * (DK + 8)], sK1[C * (DK + 8)];
   __shared__ __attribute__((aligned(16))) u16 sV0[C * (DV + 8)], sV1[C * (DV + 8)];
@@ -258,21 +259,39 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     if (Db) Dc = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
   }
 
-  // bf16 outputs of the previous chunk, stored after the next transfer is issued
+  // bf16 outputs of the previous chunk, stored at the start of the next one
   uint32_t opk[4][2];
   int o_t0 = -1, o_n = 0;
 
-  auto issue = [&](lds_u16* dQ, lds_u16* dK, lds_u16* dV, lds_u16* dZ, lds_f32* dG, lds_f32* dB, int t0) {
+  // next chunk's raw data, in flight while the current chunk is computed
+  TileRegs<DK, NT> rq_, rk_;
+  TileRegs<DV, NT> rv_;
+  TileRegs<DV, NT> rz_;
+  float rg_ = 0.f, rb_ = 0.f;
+  auto prefetch = [&](int t0) {
     const int n = min(C, tend - t0);
-    dma_tile<DK, NW>(dQ, qg, p.q_stride, t0, n);
-    dma_tile<DK, NW>(dK, kg, p.k_stride, t0, n);
-    dma_tile<DV, NW>(dV, vg, p.v_stride, t0, n);
+    rq_.load(qg, p.q_stride, t0, n);
+    rk_.load(kg, p.k_stride, t0, n);
+    rv_.load(vg, p.v_stride, t0, n);
     if constexpr (kSSD) {
-      if (p.z) dma_tile<DV, NW>(dZ, zg, p.z_stride, t0, n);
+      if (p.z) rz_.load(zg, p.z_stride, t0, n);
     }
-    if (w == 0) {
-      dma_gate(dG, p.log_g, p.H_v, h, t0, n);
-      dma_gate(dB, p.beta, p.H_v, h, t0, n);
+    if (tid < C) {
+      const int64_t gi = (int64_t)(t0 + (tid < n ? tid : 0)) * p.H_v + h;
+      rg_ = p.log_g[gi];
+      rb_ = p.beta[gi];
+    }
+  };
+  auto land = [&](u16* dQ, u16* dK, u16* dV, u16* dZ, float* dG, float* dB) {
+    rq_.store(dQ);
+    rk_.store(dK);
+    rv_.store(dV);
+    if constexpr (kSSD) {
+      if (p.z) rz_.store(dZ);
+    }
+    if (tid < C) {
+      dG[tid] = rg_;
+      dB[tid] = rb_;
     }
   };
 
@@ -295,8 +314,8 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
   // One chunk on buffer set (Q, K, V, Z, Gr, Br); the following chunk's transfer
   // goes to (nQ, nK, nV, nZ, nGr, nBr).
   auto chunk = [&](const u16* Q, const u16* K, const u16* V, const u16* Z, const float* Gr,
-                   const float* Br, lds_u16* nQ, lds_u16* nK, lds_u16* nV, lds_u16* nZ, lds_f32* nGr,
-                   lds_f32* nBr, int t0) {
+                   const float* Br, u16* nQ, u16* nK, u16* nV, u16* nZ, float* nGr, float* nBr,
+                   int t0) {
     const int n = min(C, tend - t0);
     // Lane-derived indices are recomputed in every chunk (an opaque copy of the lane
     // id): hoisting the many per-lane LDS addresses out of the loop would keep them
@@ -306,16 +325,18 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     const int l32 = lane_o & 31, hh = lane_o >> 5;
     const int g16 = lane_o >> 4, j16 = lane_o & 15;
     const int tid = w * kWave + lane_o;
-    wait_vm_all();
     lds_sync();                                   // chunk data visible; previous chunk done
+    // previous outputs first: a later wait on their store data then leaves the
+    // loads of the next chunk in flight (the memory counter retires in order)
+    flush_out();
+    const bool more = t0 + C < tend;
+    if (more) prefetch(t0 + C);
 
     // ---- per-token scalars: norms (all threads), cumulative decay (wave 0)
     if constexpr (!kSSD) {
       constexpr int TPR = NT / (2 * C);                // threads per row (q and k rows)
       const int row = tid / TPR, part = tid % TPR;
       const int rr = row % C;
-      // (two explicit paths rather than a pointer select, so the compiler can tell
-      // these reads from the transfer in flight into the other buffer)
       auto rowsq = [&](const u16* src) {
         float a = 0.f;
 #pragma unroll
@@ -358,14 +379,6 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       sCO[lane] = p.scale * gam * rq;            // O = CO (Q S0^T) + P U
       sCS[lane] = __expf(gL - Gi) * rk;          // S1 = gamma_C S0 + K^T diag(CS) U
     }
-    // The next chunk's transfer is issued once the LDS reads that the compiler
-    // cannot attribute to one buffer are done (it would otherwise wait for the
-    // transfer before them); it then overlaps the rest of this chunk.
-    auto start_next = [&]() {
-      if (t0 + C < tend) issue(nQ, nK, nV, nZ, nGr, nBr, t0 + C);
-      flush_out();
-    };
-
     // ---- Q K^T and K K^T on the lower block triangle -> P (hi + lo), A.  Computed as
     // K Q^T and K K^T (= their transposes) so that each lane holds one query row i
     // and four consecutive keys m per accumulator quad: 8-byte LDS writes.
@@ -409,11 +422,11 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     if constexpr (!kSSD) {
       if (w == NW - 1) {      // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
         const int blk = lane >> 5, row = lane & 15, half = (lane >> 4) & 1;
-        *reinterpret_cast<uint4*>(&sTb[32 * blk + row][16 + 32 * blk + 8 * half]) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][16 + 32 * blk + 8 * half]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][20 + 32 * blk + 8 * half]) = make_uint2(0, 0);
       }
     }
     lds_sync();
-    if constexpr (kSSD) start_next();
 
     // ---- T = (I + A)^{-1} on the last wave (a single wave: no barrier inside)
     if constexpr (!kSSD) {
@@ -457,7 +470,8 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
             bf16x8 bT;
 #pragma unroll
             for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[16 * s + 8 * hh + e][l32]);
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sAB[32 + l32][16 * s + 8 * hh]));
+            const bf16x8 a = join(*reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh]),
+                                  *reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh + 4]));
             y = mfma32(a, bT, y);
           }
           f32x16 zz = {};
@@ -507,7 +521,6 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     }
     if constexpr (!kSSD) {
       lds_sync();                                   // T complete
-      start_next();
       // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
       bf16x8 Rb[2];
 #pragma unroll
@@ -572,7 +585,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         for (int e = 0; e < 4; ++e) Y[rt][e] = (Y[rt][e] + Dc * xv[e]) * zz[e];
       }
     }
-    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored after the next transfer
+    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored at the next chunk's start
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         opk[rt][0] = cvt2(Y[rt][0], Y[rt][1]);
@@ -615,16 +628,20 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         }
       }
     }
+    if (more) land(nQ, nK, nV, nZ, nGr, nBr);   // other buffer: last read in the previous chunk
   };
 
-  lds_u16 *lQ0 = (lds_u16*)sQ0, *lQ1 = (lds_u16*)sQ1, *lK0 = (lds_u16*)sK0, *lK1 = (lds_u16*)sK1;
-  lds_u16 *lV0 = (lds_u16*)sV0, *lV1 = (lds_u16*)sV1, *lZ0 = (lds_u16*)sZ0, *lZ1 = (lds_u16*)sZ1;
-  lds_f32 *lG0 = (lds_f32*)sGr0, *lG1 = (lds_f32*)sGr1, *lB0 = (lds_f32*)sBr0, *lB1 = (lds_f32*)sBr1;
-  if (tbeg < tend) issue(lQ0, lK0, lV0, lZ0, lG0, lB0, tbeg);
+  if (tbeg < tend) {
+    prefetch(tbeg);
+    land(sQ0, sK0, sV0, sZ0, sGr0, sBr0);
+  }
+  // entry state loads retired on every path here, so no wait inside the loop has to
+  // cover them (such a wait would also drain the next chunk's loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   for (int t0 = tbeg; t0 < tend; t0 += 2 * C) {
-    chunk(sQ0, sK0, sV0, sZ0, sGr0, sBr0, lQ1, lK1, lV1, lZ1, lG1, lB1, t0);
+    chunk(sQ0, sK0, sV0, sZ0, sGr0, sBr0, sQ1, sK1, sV1, sZ1, sGr1, sBr1, t0);
     if (t0 + C < tend)
-      chunk(sQ1, sK1, sV1, sZ1, sGr1, sBr1, lQ0, lK0, lV0, lZ0, lG0, lB0, t0 + C);
+      chunk(sQ1, sK1, sV1, sZ1, sGr1, sBr1, sQ0, sK0, sV0, sZ0, sGr0, sBr0, t0 + C);
   }
   flush_out();
 
