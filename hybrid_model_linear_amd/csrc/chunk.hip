@@ -76,6 +76,14 @@ __device__ __forceinline__ uint2 tr_read(const u16* p) {
 // the LDS banks while every address stays an affine function of the lane.
 template <int D>
 __device__ __forceinline__ int pidx(int r, int c) { return r * (D + 8) + c; }
+// Q, K and the C x C operand tiles keep each 32-column block with its 4-column
+// groups in the order 0, 4, 1, 5, 2, 6, 3, 7, so that the 8 k slots of a 16x16x32
+// MFMA operand (columns 4g .. 4g+3 and 16+4g .. 16+4g+3 of a block, the order of the
+// accumulator rows) are 16 contiguous bytes.  Logical column -> stored column:
+__device__ __forceinline__ int kperm(int c) {
+  const int q = (c >> 2) & 7;
+  return (c & ~31) | ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
+}
 // 4 consecutive bf16 (8 B), c % 4 == 0.
 template <int D>
 __device__ __forceinline__ uint2 ld4(const u16* t, int r, int c) {
@@ -86,16 +94,15 @@ template <int D>
 __device__ __forceinline__ bf16x8 ld8(const u16* t, int r, int c) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(t + pidx<D>(r, c)));
 }
+// 8 consecutive bf16 at an 8-byte aligned address (rows of the C x C tiles)
+__device__ __forceinline__ bf16x8 ld8u(const u16* p) {
+  return join(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 4));
+}
 // Transpose read: lane j of a 16-lane group receives elements (rows[e], c0 + j),
 // e = 0..3, when lane i of the group passes (rows[i / 4], c0 + 4 (i % 4)).
 template <int D>
 __device__ __forceinline__ uint2 ldtr(const u16* t, int r, int c) {
   return tr_read(t + pidx<D>(r, c));
-}
-// Operand in accumulator row order from a padded [.][kPS] tile: k slots 0..3 at
-// p[0..3], 4..7 at p[8..11] (p offset by 16 s + 4 hh).
-__device__ __forceinline__ bf16x8 lds_perm(const u16* p) {
-  return join(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 8));
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
@@ -145,6 +152,11 @@ __device__ __forceinline__ float f4get(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+// a + lo(w)^2 + hi(w)^2 for a packed bf16 pair w (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2sq(uint32_t w, float a) {
+  const bf16x2 x = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, a, false);
+}
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ------------------------------------------------------------------ chunk transfer
@@ -154,7 +166,7 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // read consecutive 16-byte segments of a row (coalesced); rows past the sequence
 // end re-read row t0 (always valid): their values are finite and every
 // coefficient that touches them is zero.
-template <int D, int NT>
+template <int D, int NT, bool kPerm>
 struct TileRegs {
   static constexpr int NSEG = D / 8;                  // 16-byte segments per row
   static constexpr int N = 64 * NSEG / NT;            // segments per thread
@@ -167,7 +179,12 @@ struct TileRegs {
   }
   __device__ __forceinline__ static void st(u16* tile, int i, uint4 v) {
     const int sidx = threadIdx.x + i * NT, r = sidx / NSEG, c = sidx % NSEG;
-    *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
+    if constexpr (kPerm) {   // the two 4-column halves land in separate groups
+      *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c)) = make_uint2(v.x, v.y);
+      *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c + 4)) = make_uint2(v.z, v.w);
+    } else {
+      *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
+    }
   }
   __device__ __forceinline__ void load(const u16* gbase, int64_t gstride, int t0, int n) {
     s0 = ld(gbase, gstride, t0, n, 0);
@@ -238,7 +255,16 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
   const u16* kg = reinterpret_cast<const u16*>(p.k) + (int64_t)j * DK;
   const u16* vg = reinterpret_cast<const u16*>(p.v) + (int64_t)h * DV;
   const u16* zg = reinterpret_cast<const u16*>(p.z) + (int64_t)h * DV;
-  OutT* ob = reinterpret_cast<OutT*>(p.out) + (int64_t)h * DV + col;
+  // Output rows: a wave-uniform base (a chunk's first row, this wave's 16 columns)
+  // plus 32-bit lane offsets, so that the stores use the scalar-base address form.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto out_base = [&](int t0) {
+    return reinterpret_cast<char*>(p.out) + ((int64_t)t0 * p.out_stride + (int64_t)h * DV + 16 * wu) * (int64_t)sizeof(OutT);
+  };
+  const uint32_t ostride_b = (uint32_t)p.out_stride * (uint32_t)sizeof(OutT);
+  auto out_off = [&](int i, int jj) {   // byte offset of row i of the chunk, column jj of the wave's 16
+    return (uint32_t)i * ostride_b + (uint32_t)jj * (uint32_t)sizeof(OutT);
+  };
 
   // S^T tiles in 16x16 accumulator layout: Sacc[tk][r] = S[col][16 tk + 4 g16 + r]
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
@@ -264,9 +290,9 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
   int o_t0 = -1, o_n = 0;
 
   // next chunk's raw data, in flight while the current chunk is computed
-  TileRegs<DK, NT> rq_, rk_;
-  TileRegs<DV, NT> rv_;
-  TileRegs<DV, NT> rz_;
+  TileRegs<DK, NT, true> rq_, rk_;
+  TileRegs<DV, NT, false> rv_;
+  TileRegs<DV, NT, false> rz_;
   float rg_ = 0.f, rb_ = 0.f;
   auto prefetch = [&](int t0) {
     const int n = min(C, tend - t0);
@@ -295,18 +321,23 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     }
   };
 
-  auto flush_out = [&]() {
+  // (lane indices passed in from the chunk body, where they are opaque to hoisting)
+  auto flush_out = [&](int gg, int jj) {
     if constexpr (sizeof(OutT) == 2) {
       if (o_t0 < 0) return;
-      u16* o16 = reinterpret_cast<u16*>(ob);
+      char* base = out_base(o_t0);
+      auto put = [&](bool masked) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * rt + 4 * g16 + r;
-          const uint32_t wv = opk[rt][r >> 1];
-          if (i < o_n) o16[(int64_t)(o_t0 + i) * p.out_stride] = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * rt + 4 * gg + r;
+            const uint32_t wv = opk[rt][r >> 1];
+            if (!masked || i < o_n)
+              *reinterpret_cast<u16*>(base + out_off(i, jj)) = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
+          }
+      };
+      if (o_n == C) put(false); else put(true);   // uniform branch
       o_t0 = -1;
     }
   };
@@ -328,7 +359,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     lds_sync();                                   // chunk data visible; previous chunk done
     // previous outputs first: a later wait on their store data then leaves the
     // loads of the next chunk in flight (the memory counter retires in order)
-    flush_out();
+    flush_out(g16, j16);
     const bool more = t0 + C < tend;
     if (more) prefetch(t0 + C);
 
@@ -344,14 +375,14 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
           const uint4 v = *reinterpret_cast<const uint4*>(src + pidx<DK>(rr, 8 * c8));
           const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a += bf_lo(ws[e]) * bf_lo(ws[e]) + bf_hi(ws[e]) * bf_hi(ws[e]);
+          for (int e = 0; e < 4; ++e) a = dot2sq(ws[e], a);   // squares of bf16 are exact in fp32
         }
         return a;
       };
       float ss = row < C ? rowsq(Q) : rowsq(K);
       ss = group_sum<TPR>(ss);
       if (part == 0) {
-        const float r = rr < n ? 1.0f / sqrtf(ss + 1e-6f) : 0.f;
+        const float r = rr < n ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 0.f;   // 1 ulp
         if (row < C) sRq[rr] = r; else sRk[rr] = r;
       }
     } else {
@@ -410,8 +441,8 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
         const uint32_t l0 = cvt2(pv[0] - bf_lo(h0), pv[1] - bf_hi(h0));
         const uint32_t l1 = cvt2(pv[2] - bf_lo(h1), pv[3] - bf_hi(h1));
-        *reinterpret_cast<uint2*>(&sPh[i][mb]) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(&sPl[i][mb]) = make_uint2(l0, l1);
+        *reinterpret_cast<uint2*>(&sPh[i][kperm(mb)]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(&sPl[i][kperm(mb)]) = make_uint2(l0, l1);
         if constexpr (!kSSD) {
           *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
           if ((i >> 4) == (mb >> 4))
@@ -422,8 +453,8 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     if constexpr (!kSSD) {
       if (w == NW - 1) {      // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
         const int blk = lane >> 5, row = lane & 15, half = (lane >> 4) & 1;
-        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][16 + 32 * blk + 8 * half]) = make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][20 + 32 * blk + 8 * half]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
       }
     }
     lds_sync();
@@ -441,7 +472,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
 #pragma unroll
             for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][mm][i] * x[i];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sTb[16 * b + i][16 * b + c] = f32_to_bf16(x[i]);
+          for (int i = 0; i < 16; ++i) sTb[16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
         }
         // 16 -> 32 inside both diagonal 32x32 tiles: T[16..31][0..15] = -D1 (A10 D0)
 #pragma unroll
@@ -450,16 +481,16 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
           // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
           bf16x4 bD;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[r0 + 4 * g16 + e][r0 + j16]);
+          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[r0 + 4 * g16 + e][kperm(r0 + j16)]);
           f32x4 y = {};
           y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
           bf16x4 yb;
 #pragma unroll
           for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
           f32x4 zz = {};
-          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[r0 + 16 + j16][r0 + 16 + 4 * g16])), yb, zz);
+          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sTb[r0 + 16 + 4 * g16 + e][r0 + j16] = f32_to_bf16(-zz[e]);
+          for (int e = 0; e < 4; ++e) sTb[r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
         }
         // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
         {
@@ -469,16 +500,21 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
             // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
             bf16x8 bT;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[16 * s + 8 * hh + e][l32]);
+            for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[16 * s + 8 * hh + e][kperm(l32)]);
             const bf16x8 a = join(*reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh]),
                                   *reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh + 4]));
             y = mfma32(a, bT, y);
           }
           f32x16 zz = {};
 #pragma unroll
-          for (int s = 0; s < 2; ++s) zz = mfma32(lds_perm(&sTb[32 + l32][32 + 16 * s + 4 * hh]), acc_to_op(y, s), zz);
+          for (int s = 0; s < 2; ++s) {
+            const u16* trow = &sTb[32 + l32][0];
+            const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
+            zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
+                             *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
+          }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sTb[32 + acc_row(r, hh)][l32] = f32_to_bf16(-zz[r]);
+          for (int r = 0; r < 16; ++r) sTb[32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
         }
       }
     }
@@ -495,10 +531,10 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       const int row = 16 * rt + j16;
 #pragma unroll
       for (int s2 = 0; s2 < NKS; ++s2) {
-        const bf16x8 aq = join(ld4<DK>(Q, row, 32 * s2 + 4 * g16), ld4<DK>(Q, row, 32 * s2 + 16 + 4 * g16));
+        const bf16x8 aq = ld8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
         Y[rt] = mfma1632(aq, Sb[s2], Y[rt]);
         if constexpr (!kSSD) {
-          const bf16x8 ak = join(ld4<DK>(K, row, 32 * s2 + 4 * g16), ld4<DK>(K, row, 32 * s2 + 16 + 4 * g16));
+          const bf16x8 ak = ld8<DK>(K, row, 32 * s2 + 8 * g16);
           U[rt] = mfma1632(ak, Sb[s2], U[rt]);                 // X = K S0^T
         }
       }
@@ -538,11 +574,9 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const u16* trow = &sTb[16 * rt + j16][4 * g16];
+        const u16* trow = &sTb[16 * rt + j16][8 * g16];
 #pragma unroll
-        for (int s2 = 0; s2 <= (rt >> 1); ++s2) U[rt] = mfma1632(join(*reinterpret_cast<const uint2*>(trow + 32 * s2),
-                                                                       *reinterpret_cast<const uint2*>(trow + 32 * s2 + 16)),
-                                                                  Rb[s2], U[rt]);
+        for (int s2 = 0; s2 <= (rt >> 1); ++s2) U[rt] = mfma1632(ld8u(trow + 32 * s2), Rb[s2], U[rt]);
       }
     }
     // O = CO (Q S0^T) + P U (two-term splits of P and U)
@@ -555,12 +589,12 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         const float4 co = ld_f4(&sCO[16 * rt + 4 * g16]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Y[rt][e] *= f4get(co, e);
-        const u16* phrow = &sPh[16 * rt + j16][4 * g16];
-        const u16* plrow = &sPl[16 * rt + j16][4 * g16];
+        const u16* phrow = &sPh[16 * rt + j16][8 * g16];
+        const u16* plrow = &sPl[16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
-          const bf16x8 ph = join(*reinterpret_cast<const uint2*>(phrow + 32 * s2), *reinterpret_cast<const uint2*>(phrow + 32 * s2 + 16));
-          const bf16x8 pl = join(*reinterpret_cast<const uint2*>(plrow + 32 * s2), *reinterpret_cast<const uint2*>(plrow + 32 * s2 + 16));
+          const bf16x8 ph = ld8u(phrow + 32 * s2);
+          const bf16x8 pl = ld8u(plrow + 32 * s2);
           Y[rt] = mfma1632(ph, Uh[s2], Y[rt]);
           Y[rt] = mfma1632(pl, Uh[s2], Y[rt]);
           Y[rt] = mfma1632(ph, Ul[s2], Y[rt]);
@@ -594,12 +628,13 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       o_t0 = t0;
       o_n = n;
     } else {
+      char* base = out_base(t0);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * rt + 4 * g16 + r;
-          if (i < n) Elem<OutT>::store(ob, (int64_t)(t0 + i) * p.out_stride, Y[rt][r]);
+          if (i < n) *reinterpret_cast<OutT*>(base + out_off(i, j16)) = Y[rt][r];
         }
     }
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
@@ -622,7 +657,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         const int ca = 16 * tk + 4 * (j16 & 3);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, ca), ldtr<DK>(K, 32 * s2 + 16 + rb, ca));
+          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, kperm(ca)), ldtr<DK>(K, 32 * s2 + 16 + rb, kperm(ca)));
           Sacc[tk] = mfma1632(kt, Wh[s2], Sacc[tk]);
           Sacc[tk] = mfma1632(kt, Wl[s2], Sacc[tk]);
         }
@@ -643,7 +678,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     if (t0 + C < tend)
       chunk(sQ1, sK1, sV1, sZ1, sGr1, sBr1, sQ0, sK0, sV0, sZ0, sGr0, sBr0, t0 + C);
   }
-  flush_out();
+  flush_out(lane >> 4, lane & 15);
 
 #pragma unroll
   for (int tk = 0; tk < NTK; ++tk)
@@ -662,6 +697,7 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
 
 bool chunked_supported(const SeqLaunch& p) {
   if (!p.in_bf16 || p.d_k != 128 || p.N > 65535) return false;
+  if (p.out_stride > (int64_t(1) << 31) / (C * 4)) return false;   // 32-bit output row offsets
   return p.ssd ? p.d_v == 64 : p.d_v == 128;
 }
 
