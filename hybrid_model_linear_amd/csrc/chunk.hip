@@ -21,24 +21,27 @@
 // two-term (hi + lo) bf16 splits of P, U and the scaled U.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
-// order; the state never leaves registers.  Each wave owns 16 of the d_v columns
-// (state rows are independent given the chunk's keys), held as S^T tiles in 16x16
-// MFMA accumulator layout and fed back as B operands directly: the reduction index
-// of an MFMA may be permuted freely when both operands agree, so A operands are
-// read from LDS in the accumulator's row order.
+// order.  Two kinds of waves run side by side:
+//  * state waves own 16 d_v columns each (state rows are independent given the
+//    chunk's keys); the state never leaves their registers, held as S^T tiles in
+//    16x16 MFMA accumulator layout and fed back as B operands directly (the
+//    reduction index of an MFMA may be permuted freely when both operands agree, so
+//    A operands are read from LDS in the accumulator's row order).  In the step for
+//    chunk c they compute X, Y, R, U, O and the new state: only the state-dependent
+//    part, with no barrier inside.
+//  * four producer waves prepare chunk c + 1 meanwhile: decay cumsum, row norms,
+//    Q K^T and K K^T tiles -> P (hi + lo) and A, the inversion T = (I + A)^{-1}, and
+//    the per-token coefficient vectors.
+// The raw rows of q, k, v (z) are staged from HBM through the state waves'
+// registers into LDS one step ahead.
+// Each step has two workgroup barriers: one ends the previous step, the second ends
+// the landing of the staged data.  P, T and the coefficients are double-buffered,
+// and so are Q and K (chunk c for the state waves, c + 1 for the producers).
 //
-// Data movement: q, k, v (and z) rows and gate values of chunk c+1 are loaded into
-// registers at the start of chunk c and written to the other LDS buffer at its end,
-// so their HBM latency hides behind a whole chunk of compute.  Tiles are row-major
-// and padded by one 16-byte segment per row.  K^T and V^T operands come from the
-// row-major tiles through the LDS transpose read (ds_read_b64_tr_b16): lane j of
-// each 16-lane group receives column c0 + j of the four rows addressed by the
-// group's lanes 4e + j/4.
-//
-// Per chunk: the state-independent part (Q K^T, K K^T, P, A) runs on three waves,
-// then one wave builds T (diagonal 16x16 blocks by fp32 forward substitution,
-// 16 -> 32 -> 64 merges T21 = -T22 A21 T11 on MFMA) while all waves form
-// X = K S0^T, Y = Q S0^T and R; the T-dependent rest follows one barrier later.
+// Data layout in LDS: tiles are row-major and padded by one 16-byte segment per
+// row.  K^T and V^T operands come from the row-major tiles through the LDS
+// transpose read (ds_read_b64_tr_b16): lane j of each 16-lane group receives column
+// c0 + j of the four rows addressed by the group's lanes 4e + j/4.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -49,6 +52,7 @@ namespace {
 constexpr int C = 64;            // chunk length
 constexpr int kPS = C + 4;       // row length (bf16) of the padded C x C tiles: 34 dwords,
                                  // so 16 consecutive rows hit distinct bank pairs
+constexpr int kNP = 4;           // producer waves
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -84,11 +88,6 @@ __device__ __forceinline__ int kperm(int c) {
   const int q = (c >> 2) & 7;
   return (c & ~31) | ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
 }
-// 4 consecutive bf16 (8 B), c % 4 == 0.
-template <int D>
-__device__ __forceinline__ uint2 ld4(const u16* t, int r, int c) {
-  return *reinterpret_cast<const uint2*>(t + pidx<D>(r, c));
-}
 // 8 consecutive bf16 (16 B), c % 8 == 0.
 template <int D>
 __device__ __forceinline__ bf16x8 ld8(const u16* t, int r, int c) {
@@ -115,32 +114,22 @@ __device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
   return as_bf16x8(make_uint4(cvt2(a[o], a[o + 1]), cvt2(a[o + 2], a[o + 3]), cvt2(a[o + 4], a[o + 5]),
                               cvt2(a[o + 6], a[o + 7])));
 }
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void acc_split(const f32x16& a, int half, bf16x8& hi, bf16x8& lo) {
-  const int o = 8 * half;
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float x0 = a[o + 2 * e], x1 = a[o + 2 * e + 1];
-    h[e] = cvt2(x0, x1);
-    l[e] = cvt2(x0 - __uint_as_float(h[e] << 16), x1 - __uint_as_float(h[e] & 0xffff0000u));
-  }
-  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
-  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
-}
 // Two 16x16 accumulator tiles (rows 4 g + r of tile t0 and of tile t1) as one B
 // operand of a 16x16x32 MFMA whose 32 k slots are (g, e): e < 4 -> tile t0 row
 // 4 g + e, e >= 4 -> tile t1 row 4 g + e - 4.
 __device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
   return as_bf16x8(make_uint4(cvt2(a[0], a[1]), cvt2(a[2], a[3]), cvt2(b[0], b[1]), cvt2(b[2], b[3])));
 }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi), for the pair layout above
 __device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   uint32_t h[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     h[e] = cvt2(x[2 * e], x[2 * e + 1]);
-    l[e] = cvt2(x[2 * e] - __uint_as_float(h[e] << 16), x[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u));
+    l[e] = cvt2(x[2 * e] - bf_lo(h[e]), x[2 * e + 1] - bf_hi(h[e]));
   }
   hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
   lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
@@ -151,34 +140,37 @@ __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_ca
 __device__ __forceinline__ float f4get(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-// a + lo(w)^2 + hi(w)^2 for a packed bf16 pair w (v_dot2_f32_bf16)
+// a + lo(w)^2 + hi(w)^2 for a packed bf16 pair w (v_dot2_f32_bf16; the squares of
+// bf16 values are exact in fp32)
 __device__ __forceinline__ float dot2sq(uint32_t w, float a) {
   const bf16x2 x = __builtin_bit_cast(bf16x2, w);
   return __builtin_amdgcn_fdot2_f32_bf16(x, x, a, false);
 }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float sumsq8(const bf16x8& v, float a) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  return dot2sq(u.w, dot2sq(u.z, dot2sq(u.y, dot2sq(u.x, a))));
+}
 
-// ------------------------------------------------------------------ chunk transfer
-// The next chunk's q, k, v (and z) rows and gate values are loaded into registers
-// at the start of the current chunk and stored into the other LDS buffer at its
-// end, so the HBM latency overlaps a whole chunk of compute.  Consecutive threads
-// read consecutive 16-byte segments of a row (coalesced); rows past the sequence
-// end re-read row t0 (always valid): their values are finite and every
-// coefficient that touches them is zero.
-template <int D, int NT, bool kPerm>
+// ------------------------------------------------------------------ chunk staging
+// The state waves (NST threads, staging index si) load a chunk's q, k, v (and z)
+// rows into registers one step before they store them into LDS (in the landing
+// phase, where they would otherwise wait), so the HBM latency hides behind a whole
+// step.  Consecutive threads read consecutive 16-byte
+// segments of a row (coalesced); rows past the sequence end re-read row t0 (always
+// valid): their values are finite and every coefficient that touches them is zero.
+template <int D, int NST, bool kPerm>
 struct TileRegs {
   static constexpr int NSEG = D / 8;                  // 16-byte segments per row
-  static constexpr int N = 64 * NSEG / NT;            // segments per thread
-  static_assert(N * NT == 64 * NSEG && (N == 2 || N == 4), "segments split evenly");
+  static constexpr int N = 64 * NSEG / NST;           // segments per thread
+  static_assert(N * NST == 64 * NSEG && (N == 2 || N == 4), "segments split evenly");
   uint4 s0, s1, s2, s3;                               // named registers, no array (kept out of scratch)
-  __device__ __forceinline__ static uint4 ld(const u16* gbase, int64_t gstride, int t0, int n, int i) {
-    const int sidx = threadIdx.x + i * NT, r = sidx / NSEG, c = sidx % NSEG;
+  __device__ __forceinline__ static uint4 ld(const u16* g, int64_t gs, int t0, int n, int si, int i) {
+    const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     const int64_t t = t0 + (r < n ? r : 0);
-    return *reinterpret_cast<const uint4*>(gbase + t * gstride + 8 * c);
+    return *reinterpret_cast<const uint4*>(g + t * gs + 8 * c);
   }
-  __device__ __forceinline__ static void st(u16* tile, int i, uint4 v) {
-    const int sidx = threadIdx.x + i * NT, r = sidx / NSEG, c = sidx % NSEG;
+  __device__ __forceinline__ static void st(u16* tile, int si, int i, uint4 v) {
+    const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     if constexpr (kPerm) {   // the two 4-column halves land in separate groups
       *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c)) = make_uint2(v.x, v.y);
       *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c + 4)) = make_uint2(v.z, v.w);
@@ -186,78 +178,83 @@ struct TileRegs {
       *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
     }
   }
-  __device__ __forceinline__ void load(const u16* gbase, int64_t gstride, int t0, int n) {
-    s0 = ld(gbase, gstride, t0, n, 0);
-    s1 = ld(gbase, gstride, t0, n, 1);
+  __device__ __forceinline__ void load(const u16* g, int64_t gs, int t0, int n, int si) {
+    s0 = ld(g, gs, t0, n, si, 0);
+    s1 = ld(g, gs, t0, n, si, 1);
     if constexpr (N == 4) {
-      s2 = ld(gbase, gstride, t0, n, 2);
-      s3 = ld(gbase, gstride, t0, n, 3);
+      s2 = ld(g, gs, t0, n, si, 2);
+      s3 = ld(g, gs, t0, n, si, 3);
     }
   }
-  __device__ __forceinline__ void store(u16* tile) const {
-    st(tile, 0, s0);
-    st(tile, 1, s1);
+  __device__ __forceinline__ void store(u16* tile, int si) const {
+    st(tile, si, 0, s0);
+    st(tile, si, 1, s1);
     if constexpr (N == 4) {
-      st(tile, 2, s2);
-      st(tile, 3, s3);
+      st(tile, si, 2, s2);
+      st(tile, si, 3, s3);
     }
   }
 };
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() is a workgroup-scope
-// fence and would also wait for the next chunk's global loads in flight; here the
-// wave's own LDS accesses are drained (lgkmcnt(0)) and the compiler is kept from
-// moving memory accesses across the barrier.
+// fence and would also wait for the staged global loads in flight; here the wave's
+// own LDS accesses are drained (lgkmcnt(0)) and the compiler is kept from moving
+// memory accesses across the barrier.
 __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// Order this wave's earlier LDS writes before its later LDS reads (the LDS executes
+// one wave's accesses in order; this keeps the compiler from reordering them).
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+template <int I> struct Par { static constexpr int value = I; };
 
 template <int DK, int DV, bool kSSD, typename OutT>
-__global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p) {
-  constexpr int NW = DV / 16;      // waves: 16 d_v columns each
-  constexpr int NT = NW * kWave;
+__global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLaunch p) {
+  constexpr int NSW = DV / 16;     // state waves: 16 d_v columns each
   constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64), "tile shapes");
-  static_assert(NW >= 4, "four or more waves");
 
-  // double-buffered chunk data
-  __shared__ __attribute__((aligned(16))) u16 sQ0[C * (DK + 8)], sQ1[C * (DK + 8)];
-  __shared__ __attribute__((aligned(16))) u16 sK0[C * (DK + 8)], sK1[C * (DK + 8)];
-  __shared__ __attribute__((aligned(16))) u16 sV0[C * (DV + 8)], sV1[C * (DV + 8)];
-  __shared__ __attribute__((aligned(16))) u16 sZ0[kSSD ? C * (DV + 8) : 8], sZ1[kSSD ? C * (DV + 8) : 8];
-  __shared__ __attribute__((aligned(16))) float sGr0[C], sGr1[C], sBr0[C], sBr1[C];
-  // per-chunk working set
-  __shared__ __attribute__((aligned(16))) u16 sPh[C][kPS], sPl[C][kPS];
-  __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS], sTb[kSSD ? 1 : C][kPS];
+  // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
+  __shared__ __attribute__((aligned(16))) u16 sQ[2][C * (DK + 8)], sK[2][C * (DK + 8)];
+  __shared__ __attribute__((aligned(16))) u16 sV[C * (DV + 8)], sZ[kSSD ? C * (DV + 8) : 8];
+  // producer outputs for the state waves, double-buffered
+  __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS], sPl[2][C][kPS];
+  __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
+  __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
+  // producer working set (per producer wave where private)
+  __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS];
   __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16][20];
-  __shared__ __attribute__((aligned(16))) float sG[C], sBeta[C], sRk[C], sRq[C];
-  __shared__ __attribute__((aligned(16))) float sCR[C], sCO[C], sCS[C];   // per-token coefficients
+  __shared__ __attribute__((aligned(16))) float sPG[kNP][C], sPBt[kNP][C], sPRk[kNP][C], sPRq[kNP][C];
+  __shared__ uint32_t sSync;                               // producer arrival counter
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
   const int sl = p.slot[nseq];
   if (sl < 0) return;                                      // uniform over the block
   const int tbeg = p.cu_seqlens[nseq], tend = p.cu_seqlens[nseq + 1];
+  const int nch = (tend - tbeg + C - 1) / C;
   const bool init = p.has_init ? (p.has_init[nseq] != 0) : true;
   const int j = h / (p.H_v / p.H_qk);
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, w = tid / kWave;
-  const int l32 = lane & 31, hh = lane >> 5;               // 32x32 MFMA lane split (phase A)
-  const int g16 = lane >> 4, j16 = lane & 15;              // 16x16 MFMA / transpose-read split
-  const int col = 16 * w + j16;                            // this lane's d_v column
+  const int lane = tid % kWave;
+  const int wu = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
+  const bool isP = wu >= NSW;                                   // producer wave (uniform)
+  const int g16 = lane >> 4, j16 = lane & 15;
 
   const u16* qg = reinterpret_cast<const u16*>(p.q) + (int64_t)j * DK;
   const u16* kg = reinterpret_cast<const u16*>(p.k) + (int64_t)j * DK;
   const u16* vg = reinterpret_cast<const u16*>(p.v) + (int64_t)h * DV;
   const u16* zg = reinterpret_cast<const u16*>(p.z) + (int64_t)h * DV;
+
+  // ================================================================ state waves
   // Output rows: a wave-uniform base (a chunk's first row, this wave's 16 columns)
   // plus 32-bit lane offsets, so that the stores use the scalar-base address form.
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto out_base = [&](int t0) {
     return reinterpret_cast<char*>(p.out) + ((int64_t)t0 * p.out_stride + (int64_t)h * DV + 16 * wu) * (int64_t)sizeof(OutT);
   };
@@ -267,259 +264,38 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
   };
 
   // S^T tiles in 16x16 accumulator layout: Sacc[tk][r] = S[col][16 tk + 4 g16 + r]
+  const int col = 16 * wu + j16;
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
   f32x4 Sacc[NTK];
 #pragma unroll
   for (int tk = 0; tk < NTK; ++tk) {
     Sacc[tk] = f32x4{};
-    if (init) {
+    if (!isP && init) {
       const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16);
       Sacc[tk] = f32x4{v.x, v.y, v.z, v.w};
     }
   }
-
-  // delta-off D skip coefficient of this lane's column (read once, outside the loop)
+  // delta-off D skip coefficient of this lane's column
   float Dc = 0.f;
   if constexpr (kSSD) {
     const u16* Db = reinterpret_cast<const u16*>(p.D);
-    if (Db) Dc = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
+    if (!isP && Db) Dc = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
   }
 
-  // bf16 outputs of the previous chunk, stored at the start of the next one
-  uint32_t opk[4][2];
-  int o_t0 = -1, o_n = 0;
-
-  // next chunk's raw data, in flight while the current chunk is computed
-  TileRegs<DK, NT, true> rq_, rk_;
-  TileRegs<DV, NT, false> rv_;
-  TileRegs<DV, NT, false> rz_;
-  float rg_ = 0.f, rb_ = 0.f;
-  auto prefetch = [&](int t0) {
-    const int n = min(C, tend - t0);
-    rq_.load(qg, p.q_stride, t0, n);
-    rk_.load(kg, p.k_stride, t0, n);
-    rv_.load(vg, p.v_stride, t0, n);
-    if constexpr (kSSD) {
-      if (p.z) rz_.load(zg, p.z_stride, t0, n);
-    }
-    if (tid < C) {
-      const int64_t gi = (int64_t)(t0 + (tid < n ? tid : 0)) * p.H_v + h;
-      rg_ = p.log_g[gi];
-      rb_ = p.beta[gi];
-    }
-  };
-  auto land = [&](u16* dQ, u16* dK, u16* dV, u16* dZ, float* dG, float* dB) {
-    rq_.store(dQ);
-    rk_.store(dK);
-    rv_.store(dV);
-    if constexpr (kSSD) {
-      if (p.z) rz_.store(dZ);
-    }
-    if (tid < C) {
-      dG[tid] = rg_;
-      dB[tid] = rb_;
-    }
-  };
-
-  // (lane indices passed in from the chunk body, where they are opaque to hoisting)
-  auto flush_out = [&](int gg, int jj) {
-    if constexpr (sizeof(OutT) == 2) {
-      if (o_t0 < 0) return;
-      char* base = out_base(o_t0);
-      auto put = [&](bool masked) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * rt + 4 * gg + r;
-            const uint32_t wv = opk[rt][r >> 1];
-            if (!masked || i < o_n)
-              *reinterpret_cast<u16*>(base + out_off(i, jj)) = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
-          }
-      };
-      if (o_n == C) put(false); else put(true);   // uniform branch
-      o_t0 = -1;
-    }
-  };
-
-  // One chunk on buffer set (Q, K, V, Z, Gr, Br); the following chunk's transfer
-  // goes to (nQ, nK, nV, nZ, nGr, nBr).
-  auto chunk = [&](const u16* Q, const u16* K, const u16* V, const u16* Z, const float* Gr,
-                   const float* Br, u16* nQ, u16* nK, u16* nV, u16* nZ, float* nGr, float* nBr,
-                   int t0) {
-    const int n = min(C, tend - t0);
-    // Lane-derived indices are recomputed in every chunk (an opaque copy of the lane
+  // State-dependent part of chunk c (buffers of parity PAR).
+  auto consume = [&](int c, auto parc) {
+    constexpr int PAR = decltype(parc)::value;
+    const int t0 = tbeg + c * C, n = min(C, tend - t0);
+    // Lane-derived indices are recomputed in every step (an opaque copy of the lane
     // id): hoisting the many per-lane LDS addresses out of the loop would keep them
     // all live at once and spill them.
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
-    const int l32 = lane_o & 31, hh = lane_o >> 5;
     const int g16 = lane_o >> 4, j16 = lane_o & 15;
-    const int tid = w * kWave + lane_o;
-    lds_sync();                                   // chunk data visible; previous chunk done
-    // previous outputs first: a later wait on their store data then leaves the
-    // loads of the next chunk in flight (the memory counter retires in order)
-    flush_out(g16, j16);
-    const bool more = t0 + C < tend;
-    if (more) prefetch(t0 + C);
+    const u16* Q = sQ[PAR];
+    const u16* K = sK[PAR];
+    const float gC = sGC[PAR][0];
 
-    // ---- per-token scalars: norms (all threads), cumulative decay (wave 0)
-    if constexpr (!kSSD) {
-      constexpr int TPR = NT / (2 * C);                // threads per row (q and k rows)
-      const int row = tid / TPR, part = tid % TPR;
-      const int rr = row % C;
-      auto rowsq = [&](const u16* src) {
-        float a = 0.f;
-#pragma unroll
-        for (int c8 = part; c8 < DK / 8; c8 += TPR) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src + pidx<DK>(rr, 8 * c8));
-          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a = dot2sq(ws[e], a);   // squares of bf16 are exact in fp32
-        }
-        return a;
-      };
-      float ss = row < C ? rowsq(Q) : rowsq(K);
-      ss = group_sum<TPR>(ss);
-      if (part == 0) {
-        const float r = rr < n ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 0.f;   // 1 ulp
-        if (row < C) sRq[rr] = r; else sRk[rr] = r;
-      }
-    } else {
-      if (tid < C) {
-        sRq[tid] = tid < n ? 1.f : 0.f;
-        sRk[tid] = tid < n ? 1.f : 0.f;
-      }
-    }
-    if (w == 0) {
-      float Gi = lane < n ? Gr[lane] : 0.f;           // padded tokens: log g = 0, beta = 0
-      sBeta[lane] = lane < n ? Br[lane] : 0.f;
-#pragma unroll
-      for (int off = 1; off < C; off <<= 1) {
-        const float o = __shfl_up(Gi, off, kWave);
-        if (lane >= off) Gi += o;
-      }
-      sG[lane] = Gi;
-    }
-    lds_sync();
-    const float gL = sG[C - 1];
-    if (w == 0) {   // per-token coefficients of the state-dependent part (read after the next barrier)
-      const float Gi = sG[lane], bt = sBeta[lane], rk = sRk[lane], rq = sRq[lane];
-      const float gam = __expf(Gi);
-      sCR[lane] = bt * gam * rk;                 // R = beta V - CR X
-      sCO[lane] = p.scale * gam * rq;            // O = CO (Q S0^T) + P U
-      sCS[lane] = __expf(gL - Gi) * rk;          // S1 = gamma_C S0 + K^T diag(CS) U
-    }
-    // ---- Q K^T and K K^T on the lower block triangle -> P (hi + lo), A.  Computed as
-    // K Q^T and K K^T (= their transposes) so that each lane holds one query row i
-    // and four consecutive keys m per accumulator quad: 8-byte LDS writes.
-    for (int tt = w; tt < 3; tt += NW) {
-      const int ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;     // rows i in tile ti, keys m in tile tj
-      f32x16 qk = {}, kk = {};
-#pragma unroll
-      for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
-        const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
-        qk = mfma32(a, ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
-        if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
-      }
-      const int i = 32 * ti + l32;                                // this lane's row
-      const float Gi = sG[i];
-      const float rowP = p.scale * sRq[i];
-      const float rowA = sBeta[i] * sRk[i];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
-        const float4 Gm = ld_f4(&sG[mb]), rkm = ld_f4(&sRk[mb]);
-        float pv[4], av[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e, m = mb + e;
-          const float t = m <= i ? __expf(Gi - f4get(Gm, e)) * f4get(rkm, e) : 0.f;   // masked before the exp
-          pv[e] = rowP * t * qk[r];
-          av[e] = m < i ? rowA * t * kk[r] : 0.f;
-        }
-        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
-        const uint32_t l0 = cvt2(pv[0] - bf_lo(h0), pv[1] - bf_hi(h0));
-        const uint32_t l1 = cvt2(pv[2] - bf_lo(h1), pv[3] - bf_hi(h1));
-        *reinterpret_cast<uint2*>(&sPh[i][kperm(mb)]) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(&sPl[i][kperm(mb)]) = make_uint2(l0, l1);
-        if constexpr (!kSSD) {
-          *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
-          if ((i >> 4) == (mb >> 4))
-            *reinterpret_cast<float4*>(&sAd[i >> 4][i & 15][mb & 15]) = make_float4(av[0], av[1], av[2], av[3]);
-        }
-      }
-    }
-    if constexpr (!kSSD) {
-      if (w == NW - 1) {      // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
-        const int blk = lane >> 5, row = lane & 15, half = (lane >> 4) & 1;
-        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(&sTb[32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
-      }
-    }
-    lds_sync();
-
-    // ---- T = (I + A)^{-1} on the last wave (a single wave: no barrier inside)
-    if constexpr (!kSSD) {
-      if (w == NW - 1) {
-        {   // diagonal 16x16 blocks: lane 16 b + c solves column c of block b in fp32
-          const int b = lane >> 4, c = lane & 15;
-          float x[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][mm][i] * x[i];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sTb[16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
-        }
-        // 16 -> 32 inside both diagonal 32x32 tiles: T[16..31][0..15] = -D1 (A10 D0)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int r0 = 32 * pp;
-          // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
-          bf16x4 bD;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[r0 + 4 * g16 + e][kperm(r0 + j16)]);
-          f32x4 y = {};
-          y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
-          bf16x4 yb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
-          f32x4 zz = {};
-          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sTb[r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
-        }
-        // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
-        {
-          f32x16 y = {};
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
-            bf16x8 bT;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[16 * s + 8 * hh + e][kperm(l32)]);
-            const bf16x8 a = join(*reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh]),
-                                  *reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh + 4]));
-            y = mfma32(a, bT, y);
-          }
-          f32x16 zz = {};
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const u16* trow = &sTb[32 + l32][0];
-            const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
-            zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
-                             *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sTb[32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
-        }
-      }
-    }
-
-    // ---- state-dependent part, this wave's 16 d_v columns (16x16x32 MFMAs)
     bf16x8 Sb[NKS];            // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
 #pragma unroll
     for (int s2 = 0; s2 < NKS; ++s2) Sb[s2] = pair_to_op(Sacc[2 * s2], Sacc[2 * s2 + 1]);
@@ -543,20 +319,19 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int ib = 16 * rt + 4 * g16;
-      const uint2 t = ldtr<DV>(V, ib + (j16 >> 2), 16 * w + 4 * (j16 & 3));
+      const uint2 t = ldtr<DV>(sV, ib + (j16 >> 2), 16 * wu + 4 * (j16 & 3));
       const float vv[4] = {bf_lo(t.x), bf_hi(t.x), bf_lo(t.y), bf_hi(t.y)};
-      const float4 bi = ld_f4(&sBeta[ib]);
+      const float4 bi = ld_f4(&sBeta[PAR][ib]);
       if constexpr (kSSD) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e];
       } else {
-        const float4 cr = ld_f4(&sCR[ib]);
+        const float4 cr = ld_f4(&sCR[PAR][ib]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e] - f4get(cr, e) * U[rt][e];
       }
     }
     if constexpr (!kSSD) {
-      lds_sync();                                   // T complete
       // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
       bf16x8 Rb[2];
 #pragma unroll
@@ -574,7 +349,7 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const u16* trow = &sTb[16 * rt + j16][8 * g16];
+        const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) U[rt] = mfma1632(ld8u(trow + 32 * s2), Rb[s2], U[rt]);
       }
@@ -586,11 +361,11 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
       for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Uh[s2], Ul[s2]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const float4 co = ld_f4(&sCO[16 * rt + 4 * g16]);
+        const float4 co = ld_f4(&sCO[PAR][16 * rt + 4 * g16]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Y[rt][e] *= f4get(co, e);
-        const u16* phrow = &sPh[16 * rt + j16][8 * g16];
-        const u16* plrow = &sPl[16 * rt + j16][8 * g16];
+        const u16* phrow = &sPh[PAR][16 * rt + j16][8 * g16];
+        const u16* plrow = &sPl[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
           const bf16x8 ph = ld8u(phrow + 32 * s2);
@@ -605,12 +380,12 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
     if constexpr (kSSD) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = 16 * w + 4 * (j16 & 3);
-        const uint2 tx = ldtr<DV>(V, ra, ca);
+        const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = 16 * wu + 4 * (j16 & 3);
+        const uint2 tx = ldtr<DV>(sV, ra, ca);
         const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
         float zz[4] = {1.f, 1.f, 1.f, 1.f};
         if (p.z) {
-          const uint2 tz = ldtr<DV>(Z, ra, ca);
+          const uint2 tz = ldtr<DV>(sZ, ra, ca);
           const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
 #pragma unroll
           for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
@@ -619,76 +394,349 @@ __global__ void __launch_bounds__((DV / 16) * kWave, 1) chunk_kernel(SeqLaunch p
         for (int e = 0; e < 4; ++e) Y[rt][e] = (Y[rt][e] + Dc * xv[e]) * zz[e];
       }
     }
-    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored at the next chunk's start
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        opk[rt][0] = cvt2(Y[rt][0], Y[rt][1]);
-        opk[rt][1] = cvt2(Y[rt][2], Y[rt][3]);
-      }
-      o_t0 = t0;
-      o_n = n;
-    } else {
+    {
       char* base = out_base(t0);
+      auto put = [&](bool masked) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+          uint32_t pk[2] = {0u, 0u};
+          if constexpr (sizeof(OutT) == 2) {
+            pk[0] = cvt2(Y[rt][0], Y[rt][1]);
+            pk[1] = cvt2(Y[rt][2], Y[rt][3]);
+          }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * rt + 4 * g16 + r;
-          if (i < n) *reinterpret_cast<OutT*>(base + out_off(i, j16)) = Y[rt][r];
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * rt + 4 * g16 + r;
+            if (masked && i >= n) continue;
+            if constexpr (sizeof(OutT) == 2)
+              *reinterpret_cast<u16*>(base + out_off(i, j16)) = (u16)((r & 1) ? (pk[r >> 1] >> 16) : (pk[r >> 1] & 0xffffu));
+            else
+              *reinterpret_cast<OutT*>(base + out_off(i, j16)) = Y[rt][r];
+          }
         }
+      };
+      if (n == C) put(false); else put(true);   // uniform branch
     }
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
     {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const float4 cs = ld_f4(&sCS[16 * rt + 4 * g16]);
+        const float4 cs = ld_f4(&sCS[PAR][16 * rt + 4 * g16]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) U[rt][e] *= f4get(cs, e);
       }
       bf16x8 Wh[2], Wl[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Wh[s2], Wl[s2]);
-      const float gC = __expf(gL);
       // A operand K^T: row d_k = 16 tk + j16; k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
       const int rb = 4 * g16 + (j16 >> 2);
 #pragma unroll
       for (int tk = 0; tk < NTK; ++tk) {
         Sacc[tk] *= gC;
-        const int ca = 16 * tk + 4 * (j16 & 3);
+        const int ca = kperm(16 * tk + 4 * (j16 & 3));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, kperm(ca)), ldtr<DK>(K, 32 * s2 + 16 + rb, kperm(ca)));
+          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, ca), ldtr<DK>(K, 32 * s2 + 16 + rb, ca));
           Sacc[tk] = mfma1632(kt, Wh[s2], Sacc[tk]);
           Sacc[tk] = mfma1632(kt, Wl[s2], Sacc[tk]);
         }
       }
     }
-    if (more) land(nQ, nK, nV, nZ, nGr, nBr);   // other buffer: last read in the previous chunk
   };
 
-  if (tbeg < tend) {
-    prefetch(tbeg);
-    land(sQ0, sK0, sV0, sZ0, sGr0, sBr0);
-  }
-  // entry state loads retired on every path here, so no wait inside the loop has to
-  // cover them (such a wait would also drain the next chunk's loads)
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  for (int t0 = tbeg; t0 < tend; t0 += 2 * C) {
-    chunk(sQ0, sK0, sV0, sZ0, sGr0, sBr0, sQ1, sK1, sV1, sZ1, sGr1, sBr1, t0);
-    if (t0 + C < tend)
-      chunk(sQ1, sK1, sV1, sZ1, sGr1, sBr1, sQ0, sK0, sV0, sZ0, sGr0, sBr0, t0 + C);
-  }
-  flush_out(lane >> 4, lane & 15);
+  // ================================================================ staging
+  constexpr int NST = NSW * kWave;
+  const int si = tid;                         // staging index (state waves)
+  TileRegs<DK, NST, true> rq_, rk_;           // Q, K of chunk c + 2 in flight during step c
+  TileRegs<DV, NST, false> rv_, rz_;          // V (Z) of chunk c + 1
+  float rg_ = 0.f, rb_ = 0.f;                 // producers: log g, beta of chunk c + 2 (lane = token)
+  auto stage_qk = [&](int cc) {
+    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
+    rq_.load(qg, p.q_stride, t0, n, si);
+    rk_.load(kg, p.k_stride, t0, n, si);
+  };
+  auto stage_gates = [&](int cc) {
+    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
+    const int64_t gi = (int64_t)(t0 + (lane < n ? lane : 0)) * p.H_v + h;
+    rg_ = p.log_g[gi];
+    rb_ = p.beta[gi];
+  };
+  auto stage_v = [&](int cc) {
+    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
+    rv_.load(vg, p.v_stride, t0, n, si);
+    if constexpr (kSSD) {
+      if (p.z) rz_.load(zg, p.z_stride, t0, n, si);
+    }
+  };
 
+  // ================================================================ producer waves
+
+  // Tile (ti, tj) of K Q^T and K K^T (the transposes of Q K^T and K K^T: each lane
+  // holds one query row i = 32 ti + l32 and keys m = 32 tj + 8 q4 + 4 hh + e), with
+  // the half-row sums of squares of its operand rows: K rows 32 tj + l32 (sqA), Q rows
+  // 32 ti + l32 (sqQ) and K rows 32 ti + l32 (sqK).
+  auto tile_mma = [&](const u16* Q, const u16* K, int ti, int tj, int l32, int hh, f32x16& qk,
+                      f32x16& kk, float& sqA, float& sqQ, float& sqK) {
+    qk = f32x16{};
+    kk = f32x16{};
+    sqA = 0.f;
+    sqQ = 0.f;
+    sqK = 0.f;
 #pragma unroll
-  for (int tk = 0; tk < NTK; ++tk)
-    *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
-        make_float4(Sacc[tk][0], Sacc[tk][1], Sacc[tk][2], Sacc[tk][3]);
+    for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
+      const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
+      const bf16x8 bq = ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh);
+      qk = mfma32(a, bq, qk);
+      if constexpr (!kSSD) {
+        const bf16x8 bk = ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh);
+        kk = mfma32(a, bk, kk);
+        sqA = sumsq8(a, sqA);
+        sqQ = sumsq8(bq, sqQ);
+        if (ti != tj) sqK = sumsq8(bk, sqK);
+      }
+    }
+    if (ti == tj) sqK = sqA;
+  };
+  // 1 / |row| from the two half-row sums of lanes l32 and l32 + 32 (zero past the end)
+  auto inv_norm = [&](float sq, int row, int n) {
+    if constexpr (kSSD) {
+      return row < n ? 1.f : 0.f;
+    } else {
+      sq += __shfl_xor(sq, 32, kWave);
+      return row < n ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;   // 1 ulp
+    }
+  };
+  // Hand-off between producer waves: an arrival counter in LDS.  A wave's LDS writes
+  // are performed before its later increment (the LDS executes one wave's accesses
+  // in order); the waiting wave reads the data only after seeing the count.  The
+  // wait is bounded: every producer arrives once per step unconditionally.
+  auto arrive = [&]() {
+    lds_order();
+    if (lane == 0) __hip_atomic_fetch_add(&sSync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto wait_count = [&](uint32_t target) {
+    for (int it = 0; it < (1 << 22); ++it) {
+      if (__hip_atomic_load(&sSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_order();
+  };
+  uint32_t pgen = 0;                          // producer steps so far (uniform)
+
+  // Prepare chunk cp into the buffers of parity PQ (producer role pr = wave - NSW):
+  //   pr 0, 1: diagonal tile t = pr of P and A, the coefficient vectors of its 32
+  //            tokens, T's diagonal 16x16 blocks 2t, 2t + 1 and their 16 -> 32 merge;
+  //   pr 2:    the off-diagonal tile (query rows 32..63, keys 0..31) of P and A;
+  //   pr 3:    after the other three have arrived, T[32..63][0..31] = -T11 A21 T00.
+  auto produce = [&](int cp, auto parq, float gcur, float bcur) {
+    constexpr int PQ = decltype(parq)::value;
+    const int t0 = tbeg + cp * C, n = min(C, tend - t0);
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int l32 = lane_o & 31, hh = lane_o >> 5;
+    const int g16 = lane_o >> 4, j16 = lane_o & 15;
+    const int pr = wu - NSW;
+    const u16* Q = sQ[PQ];
+    const u16* K = sK[PQ];
+    float* pG = sPG[pr];
+    float* pB = sPBt[pr];
+    float* pRk = sPRk[pr];
+    float* pRq = sPRq[pr];
+    ++pgen;
+
+    if (pr == 3) {
+      if constexpr (!kSSD) {
+        {   // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
+          const int blk = lane_o >> 5, row = lane_o & 15, half = (lane_o >> 4) & 1;
+          *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+          *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+        }
+        wait_count(3 * pgen);
+        // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
+        f32x16 y = {};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
+          bf16x8 bT;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[PQ][16 * s + 8 * hh + e][kperm(l32)]);
+          const bf16x8 a = join(*reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh]),
+                                *reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh + 4]));
+          y = mfma32(a, bT, y);
+        }
+        f32x16 zz = {};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u16* trow = &sTb[PQ][32 + l32][0];
+          const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
+          zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
+                           *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sTb[PQ][32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
+      }
+      return;
+    }
+
+    // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
+    float Gi = lane_o < n ? gcur : 0.f;
+    const float bt = lane_o < n ? bcur : 0.f;
+#pragma unroll
+    for (int off = 1; off < C; off <<= 1) {
+      const float o = __shfl_up(Gi, off, kWave);
+      if (lane_o >= off) Gi += o;
+    }
+    const float GC = __shfl(Gi, C - 1, kWave);
+    pG[lane_o] = Gi;
+    pB[lane_o] = bt;
+
+    const int ti = pr == 2 ? 1 : pr, tj = pr == 2 ? 0 : pr;
+    f32x16 qk, kk;
+    float sqA, sqQ, sqK;
+    tile_mma(Q, K, ti, tj, l32, hh, qk, kk, sqA, sqQ, sqK);
+    const float rkA = inv_norm(sqA, 32 * tj + l32, n);   // keys' rows
+    const float rq = inv_norm(sqQ, 32 * ti + l32, n);    // query rows
+    const float rk = inv_norm(sqK, 32 * ti + l32, n);    // query rows' keys
+    if (hh == 0) {
+      pRk[32 * tj + l32] = rkA;
+      pRk[32 * ti + l32] = rk;
+      pRq[32 * ti + l32] = rq;
+    }
+    lds_order();
+    {   // scale: P (hi + lo) and A (bf16, and fp32 diagonal 16x16 blocks)
+      const int i = 32 * ti + l32;                                // this lane's row
+      const float Gi_ = pG[i];
+      const float rowP = p.scale * pRq[i];
+      const float rowA = pB[i] * pRk[i];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
+        const float4 Gm = ld_f4(&pG[mb]), rkm = ld_f4(&pRk[mb]);
+        float pv[4], av[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e, m = mb + e;
+          const float t = m <= i ? __expf(Gi_ - f4get(Gm, e)) * f4get(rkm, e) : 0.f;   // masked before the exp
+          pv[e] = rowP * t * qk[r];
+          av[e] = m < i ? rowA * t * kk[r] : 0.f;
+        }
+        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
+        const uint32_t l0 = cvt2(pv[0] - bf_lo(h0), pv[1] - bf_hi(h0));
+        const uint32_t l1 = cvt2(pv[2] - bf_lo(h1), pv[3] - bf_hi(h1));
+        *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
+        if constexpr (!kSSD) {
+          *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
+          if ((i >> 4) == (mb >> 4))
+            *reinterpret_cast<float4*>(&sAd[i >> 4][i & 15][mb & 15]) = make_float4(av[0], av[1], av[2], av[3]);
+        }
+      }
+    }
+    if (pr < 2) {
+      const int t = pr;
+      if (hh == 0) {   // coefficient vectors of tokens 32 t .. 32 t + 31
+        const int i = 32 * t + l32;
+        const float Gt = pG[i], bt_i = pB[i];
+        const float gam = __expf(Gt);
+        sCR[PQ][i] = bt_i * gam * rk;                // R = beta V - CR X
+        sCO[PQ][i] = p.scale * gam * rq;             // O = CO (Q S0^T) + P U
+        sCS[PQ][i] = __expf(GC - Gt) * rk;           // S1 = gamma_C S0 + K^T diag(CS) U
+        sBeta[PQ][i] = bt_i;
+      }
+      if (t == 0 && lane_o == 0) sGC[PQ][0] = __expf(GC);
+      if constexpr (!kSSD) {
+        lds_order();
+        if (hh == 0) {   // diagonal 16x16 blocks 2t, 2t + 1: lane 16 b' + c solves column c in fp32
+          const int b = 2 * t + (l32 >> 4), c = l32 & 15;
+          float x[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][mm][i] * x[i];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
+        }
+        lds_order();
+        {   // 16 -> 32 inside diagonal tile t: T[16..31][0..15] = -D1 (A10 D0)
+          const int r0 = 32 * t;
+          // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
+          bf16x4 bD;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[PQ][r0 + 4 * g16 + e][kperm(r0 + j16)]);
+          f32x4 y = {};
+          y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
+          bf16x4 yb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+          f32x4 zz = {};
+          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[PQ][r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sTb[PQ][r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
+        }
+      }
+    }
+    if constexpr (!kSSD) arrive();
+  };
+
+  // ================================================================ step loop
+  // Step c: the state waves consume chunk c while the producers prepare chunk c + 1.
+  auto step = [&](int c, auto parc) {
+    constexpr int PAR = decltype(parc)::value;     // parity of chunk c
+    constexpr int PQ = PAR ^ 1;                    // parity of chunk c + 1
+    const bool hasS = c >= 0, hasP = c + 1 < nch;
+    float gcur = 0.f, bcur = 0.f;
+    lds_sync();                                    // previous step done
+    if (isP) {
+      gcur = rg_;
+      bcur = rb_;
+      if (c + 2 < nch) stage_gates(c + 2);
+    } else {
+      // land the staged data (Q, K of c + 1; V, Z of c), then stage the next
+      if (hasP) {
+        rq_.store(sQ[PQ], si);
+        rk_.store(sK[PQ], si);
+      }
+      if (hasS) {
+        rv_.store(sV, si);
+        if constexpr (kSSD) {
+          if (p.z) rz_.store(sZ, si);
+        }
+      }
+      if (c + 2 < nch) stage_qk(c + 2);
+      if (hasP) stage_v(c + 1);
+    }
+    lds_sync();                                    // landing done
+    if (isP) {
+      if (hasP) produce(c + 1, Par<PQ>{}, gcur, bcur);
+    } else {
+      if (hasS) consume(c, Par<PAR>{});
+    }
+  };
+
+  if (nch > 0) {
+    if (isP) stage_gates(0); else stage_qk(0);
+  }
+  if (tid == 0) sSync = 0u;   // visible to all after the first barrier
+  // entry state and first staged loads retired on every path here, so no wait inside
+  // the loop has to cover them
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  for (int c = -1; c < nch; c += 2) {
+    step(c, Par<1>{});                   // c odd (c = -1: landing and the first chunk's preparation only)
+    if (c + 1 < nch) step(c + 1, Par<0>{});
+  }
+  if (!isP) {
+#pragma unroll
+    for (int tk = 0; tk < NTK; ++tk)
+      *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
+          make_float4(Sacc[tk][0], Sacc[tk][1], Sacc[tk][2], Sacc[tk][3]);
+  }
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
 hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
-  dim3 grid(p.H_v, p.N), block((DV / 16) * kWave);
+  dim3 grid(p.H_v, p.N), block((DV / 16 + kNP) * kWave);
   hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
