@@ -22,8 +22,8 @@
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
 // order.  Two kinds of waves run side by side:
-//  * state waves own 16 d_v columns each (state rows are independent given the
-//    chunk's keys); the state never leaves their registers, held as S^T tiles in
+//  * state waves own 32 d_v columns each (16 in delta-off mode; state rows are
+//    independent given the chunk's keys); the state never leaves their registers, held as S^T tiles in
 //    16x16 MFMA accumulator layout and fed back as B operands directly (the
 //    reduction index of an MFMA may be permuted freely when both operands agree, so
 //    A operands are read from LDS in the accumulator's row order).  In the step for
@@ -32,8 +32,8 @@
 //  * four producer waves prepare chunk c + 1 meanwhile: decay cumsum, row norms,
 //    Q K^T and K K^T tiles -> P (hi + lo) and A, the inversion T = (I + A)^{-1}, and
 //    the per-token coefficient vectors.
-// The raw rows of q, k, v (z) are staged from HBM through the state waves'
-// registers into LDS one step ahead.
+// The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
+// step ahead.
 // Each step has two workgroup barriers: one ends the previous step, the second ends
 // the landing of the staged data.  P, T and the coefficients are double-buffered,
 // and so are Q and K (chunk c for the state waves, c + 1 for the producers).
@@ -152,23 +152,25 @@ __device__ __forceinline__ float sumsq8(const bf16x8& v, float a) {
 }
 
 // ------------------------------------------------------------------ chunk staging
-// The state waves (NST threads, staging index si) load a chunk's q, k, v (and z)
-// rows into registers one step before they store them into LDS (in the landing
-// phase, where they would otherwise wait), so the HBM latency hides behind a whole
-// step.  Consecutive threads read consecutive 16-byte
+// The waves of a workgroup (NST threads, staging index si) load a chunk's q, k, v
+// (and z) rows into registers one step before they store them into LDS, so the HBM
+// latency hides behind a whole step.  Consecutive threads read consecutive 16-byte
 // segments of a row (coalesced); rows past the sequence end re-read row t0 (always
 // valid): their values are finite and every coefficient that touches them is zero.
-template <int D, int NST, bool kPerm>
+template <int D, int NST>
 struct TileRegs {
   static constexpr int NSEG = D / 8;                  // 16-byte segments per row
   static constexpr int N = 64 * NSEG / NST;           // segments per thread
-  static_assert(N * NST == 64 * NSEG && (N == 2 || N == 4), "segments split evenly");
+  static_assert(N * NST == 64 * NSEG && (N == 1 || N == 2 || N == 4), "segments split evenly");
   uint4 s0, s1, s2, s3;                               // named registers, no array (kept out of scratch)
+  // (a uniform base at row t0 plus a 32-bit lane offset: the scalar-base address form)
   __device__ __forceinline__ static uint4 ld(const u16* g, int64_t gs, int t0, int n, int si, int i) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
-    const int64_t t = t0 + (r < n ? r : 0);
-    return *reinterpret_cast<const uint4*>(g + t * gs + 8 * c);
+    const char* base = reinterpret_cast<const char*>(g + (int64_t)t0 * gs);
+    const uint32_t off = ((uint32_t)(r < n ? r : 0) * (uint32_t)gs + 8u * (uint32_t)c) * 2u;
+    return *reinterpret_cast<const uint4*>(base + off);
   }
+  template <bool kPerm>
   __device__ __forceinline__ static void st(u16* tile, int si, int i, uint4 v) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     if constexpr (kPerm) {   // the two 4-column halves land in separate groups
@@ -180,18 +182,19 @@ struct TileRegs {
   }
   __device__ __forceinline__ void load(const u16* g, int64_t gs, int t0, int n, int si) {
     s0 = ld(g, gs, t0, n, si, 0);
-    s1 = ld(g, gs, t0, n, si, 1);
+    if constexpr (N >= 2) s1 = ld(g, gs, t0, n, si, 1);
     if constexpr (N == 4) {
       s2 = ld(g, gs, t0, n, si, 2);
       s3 = ld(g, gs, t0, n, si, 3);
     }
   }
+  template <bool kPerm>   // Q and K tiles: permuted column groups
   __device__ __forceinline__ void store(u16* tile, int si) const {
-    st(tile, si, 0, s0);
-    st(tile, si, 1, s1);
+    st<kPerm>(tile, si, 0, s0);
+    if constexpr (N >= 2) st<kPerm>(tile, si, 1, s1);
     if constexpr (N == 4) {
-      st(tile, si, 2, s2);
-      st(tile, si, 3, s3);
+      st<kPerm>(tile, si, 2, s2);
+      st<kPerm>(tile, si, 3, s3);
     }
   }
 };
@@ -212,12 +215,13 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 template <int I> struct Par { static constexpr int value = I; };
 
-template <int DK, int DV, bool kSSD, typename OutT>
-__global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLaunch p) {
-  constexpr int NSW = DV / 16;     // state waves: 16 d_v columns each
+template <int DK, int DV, bool kSSD, typename OutT, int CT>
+__global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kernel(SeqLaunch p) {
+  constexpr int CW = 16 * CT;      // d_v columns per state wave (CT tiles of 16)
+  constexpr int NSW = DV / CW;     // state waves
   constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
-  static_assert(DK == 128 && (DV == 128 || DV == 64), "tile shapes");
+  static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
   __shared__ __attribute__((aligned(16))) u16 sQ[2][C * (DK + 8)], sK[2][C * (DK + 8)];
@@ -226,6 +230,7 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
   __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS], sPl[2][C][kPS];
   __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
+  __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
   // producer working set (per producer wave where private)
   __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS];
   __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16][20];
@@ -245,44 +250,85 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
   const int lane = tid % kWave;
   const int wu = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave index, uniform
   const bool isP = wu >= NSW;                                   // producer wave (uniform)
+  // The producers' chain of dependent steps is the longer one per step; the state
+  // waves fill the issue slots it leaves.
+  if (isP) __builtin_amdgcn_s_setprio(3);
   const int g16 = lane >> 4, j16 = lane & 15;
 
   const u16* qg = reinterpret_cast<const u16*>(p.q) + (int64_t)j * DK;
   const u16* kg = reinterpret_cast<const u16*>(p.k) + (int64_t)j * DK;
   const u16* vg = reinterpret_cast<const u16*>(p.v) + (int64_t)h * DV;
-  const u16* zg = reinterpret_cast<const u16*>(p.z) + (int64_t)h * DV;
+  // (without z, its staging re-reads v, unused: the loads stay unconditional)
+  const u16* zg = reinterpret_cast<const u16*>(p.z ? p.z : p.v) + (int64_t)h * DV;
+  const int64_t z_stride = p.z ? p.z_stride : p.v_stride;
 
   // ================================================================ state waves
-  // Output rows: a wave-uniform base (a chunk's first row, this wave's 16 columns)
-  // plus 32-bit lane offsets, so that the stores use the scalar-base address form.
+  // Wave wu owns d_v columns CW wu .. CW wu + CW - 1 (CT tiles of 16).
+  // Output rows: a wave-uniform base (a chunk's first row, this wave's columns) plus
+  // 32-bit lane offsets, so that the stores use the scalar-base address form.
   auto out_base = [&](int t0) {
-    return reinterpret_cast<char*>(p.out) + ((int64_t)t0 * p.out_stride + (int64_t)h * DV + 16 * wu) * (int64_t)sizeof(OutT);
+    return reinterpret_cast<char*>(p.out) + ((int64_t)t0 * p.out_stride + (int64_t)h * DV + CW * wu) * (int64_t)sizeof(OutT);
   };
   const uint32_t ostride_b = (uint32_t)p.out_stride * (uint32_t)sizeof(OutT);
-  auto out_off = [&](int i, int jj) {   // byte offset of row i of the chunk, column jj of the wave's 16
+  auto out_off = [&](int i, int jj) {   // byte offset of row i of the chunk, column jj of the wave's
     return (uint32_t)i * ostride_b + (uint32_t)jj * (uint32_t)sizeof(OutT);
   };
 
-  // S^T tiles in 16x16 accumulator layout: Sacc[tk][r] = S[col][16 tk + 4 g16 + r]
-  const int col = 16 * wu + j16;
+  // S^T tiles in 16x16 accumulator layout: Sacc[ct][tk][r] = S[col_ct][16 tk + 4 g16 + r]
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
-  f32x4 Sacc[NTK];
+  f32x4 Sacc[CT][NTK];
 #pragma unroll
-  for (int tk = 0; tk < NTK; ++tk) {
-    Sacc[tk] = f32x4{};
-    if (!isP && init) {
-      const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16);
-      Sacc[tk] = f32x4{v.x, v.y, v.z, v.w};
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int tk = 0; tk < NTK; ++tk) {
+      Sacc[ct][tk] = f32x4{};
+      if (!isP && init) {
+        const int col = CW * wu + 16 * ct + j16;
+        const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16);
+        Sacc[ct][tk] = f32x4{v.x, v.y, v.z, v.w};
+      }
+    }
+  // delta-off D skip coefficient of this lane's columns
+  float Dc[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    Dc[ct] = 0.f;
+    if constexpr (kSSD) {
+      const u16* Db = reinterpret_cast<const u16*>(p.D);
+      const int col = CW * wu + 16 * ct + j16;
+      if (!isP && Db) Dc[ct] = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
     }
   }
-  // delta-off D skip coefficient of this lane's column
-  float Dc = 0.f;
-  if constexpr (kSSD) {
-    const u16* Db = reinterpret_cast<const u16*>(p.D);
-    if (!isP && Db) Dc = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
-  }
 
-  // State-dependent part of chunk c (buffers of parity PAR).
+  // bf16 outputs of chunk c, stored in the landing phase of the next step before the
+  // next loads are issued: the landing's wait for the staged loads then never waits
+  // for these stores (the memory counter retires in order).
+  uint32_t opk[CT][4][2];
+  int o_t0 = -1, o_n = 0;
+  auto flush_out = [&](int gg, int jj) {   // (lane indices from an opaque copy)
+    if constexpr (sizeof(OutT) == 2) {
+      if (o_t0 < 0) return;
+      char* base = out_base(o_t0);
+      auto put = [&](bool masked) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 16 * rt + 4 * gg + r;
+              const uint32_t wv = opk[ct][rt][r >> 1];
+              if (!masked || i < o_n)
+                *reinterpret_cast<u16*>(base + out_off(i, 16 * ct + jj)) = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
+            }
+      };
+      if (o_n == C) put(false); else put(true);   // uniform branch
+      o_t0 = -1;
+    }
+  };
+
+  // State-dependent part of chunk c (buffers of parity PAR).  A operands (rows of Q,
+  // K, T, P and K^T) are read once and shared by the wave's CT column tiles.
   auto consume = [&](int c, auto parc) {
     constexpr int PAR = decltype(parc)::value;
     const int t0 = tbeg + c * C, n = min(C, tend - t0);
@@ -296,22 +342,31 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
     const u16* K = sK[PAR];
     const float gC = sGC[PAR][0];
 
-    bf16x8 Sb[NKS];            // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
+    f32x4 Y[CT][4], U[CT][4];  // row tiles of 16 tokens: rows 16 rt + 4 g16 + r
+    {
+      bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
 #pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2) Sb[s2] = pair_to_op(Sacc[2 * s2], Sacc[2 * s2 + 1]);
-    f32x4 Y[4], U[4];          // row tiles of 16 tokens: rows 16 rt + 4 g16 + r
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Y[rt] = f32x4{};
-      U[rt] = f32x4{};
-      const int row = 16 * rt + j16;
+        for (int s2 = 0; s2 < NKS; ++s2) Sb[ct][s2] = pair_to_op(Sacc[ct][2 * s2], Sacc[ct][2 * s2 + 1]);
 #pragma unroll
-      for (int s2 = 0; s2 < NKS; ++s2) {
-        const bf16x8 aq = ld8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
-        Y[rt] = mfma1632(aq, Sb[s2], Y[rt]);
-        if constexpr (!kSSD) {
-          const bf16x8 ak = ld8<DK>(K, row, 32 * s2 + 8 * g16);
-          U[rt] = mfma1632(ak, Sb[s2], U[rt]);                 // X = K S0^T
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Y[ct][rt] = f32x4{};
+          U[ct][rt] = f32x4{};
+        }
+        const int row = 16 * rt + j16;
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+          const bf16x8 aq = ld8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632(aq, Sb[ct][s2], Y[ct][rt]);
+          if constexpr (!kSSD) {
+            const bf16x8 ak = ld8<DK>(K, row, 32 * s2 + 8 * g16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632(ak, Sb[ct][s2], U[ct][rt]);   // X = K S0^T
+          }
         }
       }
     }
@@ -319,101 +374,124 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int ib = 16 * rt + 4 * g16;
-      const uint2 t = ldtr<DV>(sV, ib + (j16 >> 2), 16 * wu + 4 * (j16 & 3));
-      const float vv[4] = {bf_lo(t.x), bf_hi(t.x), bf_lo(t.y), bf_hi(t.y)};
       const float4 bi = ld_f4(&sBeta[PAR][ib]);
-      if constexpr (kSSD) {
+      float4 cr = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (!kSSD) cr = ld_f4(&sCR[PAR][ib]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e];
-      } else {
-        const float4 cr = ld_f4(&sCR[PAR][ib]);
+      for (int ct = 0; ct < CT; ++ct) {
+        const uint2 t = ldtr<DV>(sV, ib + (j16 >> 2), CW * wu + 16 * ct + 4 * (j16 & 3));
+        const float vv[4] = {bf_lo(t.x), bf_hi(t.x), bf_lo(t.y), bf_hi(t.y)};
+        if constexpr (kSSD) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) U[rt][e] = f4get(bi, e) * vv[e] - f4get(cr, e) * U[rt][e];
+          for (int e = 0; e < 4; ++e) U[ct][rt][e] = f4get(bi, e) * vv[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) U[ct][rt][e] = f4get(bi, e) * vv[e] - f4get(cr, e) * U[ct][rt][e];
+        }
       }
     }
     if constexpr (!kSSD) {
       // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
-      bf16x8 Rb[2];
+      bf16x8 Rb[CT][2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        Rb[s2] = pair_to_op(U[2 * s2], U[2 * s2 + 1]);
-        const uint4 rw = __builtin_bit_cast(uint4, Rb[s2]);
-        U[2 * s2][0] -= bf_lo(rw.x);
-        U[2 * s2][1] -= bf_hi(rw.x);
-        U[2 * s2][2] -= bf_lo(rw.y);
-        U[2 * s2][3] -= bf_hi(rw.y);
-        U[2 * s2 + 1][0] -= bf_lo(rw.z);
-        U[2 * s2 + 1][1] -= bf_hi(rw.z);
-        U[2 * s2 + 1][2] -= bf_lo(rw.w);
-        U[2 * s2 + 1][3] -= bf_hi(rw.w);
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          f32x4& u0 = U[ct][2 * s2];
+          f32x4& u1 = U[ct][2 * s2 + 1];
+          Rb[ct][s2] = pair_to_op(u0, u1);
+          const uint4 rw = __builtin_bit_cast(uint4, Rb[ct][s2]);
+          u0[0] -= bf_lo(rw.x);
+          u0[1] -= bf_hi(rw.x);
+          u0[2] -= bf_lo(rw.y);
+          u0[3] -= bf_hi(rw.y);
+          u1[0] -= bf_lo(rw.z);
+          u1[1] -= bf_hi(rw.z);
+          u1[2] -= bf_lo(rw.w);
+          u1[3] -= bf_hi(rw.w);
+        }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
-        for (int s2 = 0; s2 <= (rt >> 1); ++s2) U[rt] = mfma1632(ld8u(trow + 32 * s2), Rb[s2], U[rt]);
+        for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+          const bf16x8 ta = ld8u(trow + 32 * s2);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632(ta, Rb[ct][s2], U[ct][rt]);
+        }
       }
     }
     // O = CO (Q S0^T) + P U (two-term splits of P and U)
     {
-      bf16x8 Uh[2], Ul[2];
+      bf16x8 Uh[CT][2], Ul[CT][2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Uh[s2], Ul[s2]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Uh[ct][s2], Ul[ct][s2]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const float4 co = ld_f4(&sCO[PAR][16 * rt + 4 * g16]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Y[rt][e] *= f4get(co, e);
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Y[ct][rt][e] *= f4get(co, e);
         const u16* phrow = &sPh[PAR][16 * rt + j16][8 * g16];
         const u16* plrow = &sPl[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
           const bf16x8 ph = ld8u(phrow + 32 * s2);
           const bf16x8 pl = ld8u(plrow + 32 * s2);
-          Y[rt] = mfma1632(ph, Uh[s2], Y[rt]);
-          Y[rt] = mfma1632(pl, Uh[s2], Y[rt]);
-          Y[rt] = mfma1632(ph, Ul[s2], Y[rt]);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            Y[ct][rt] = mfma1632(ph, Uh[ct][s2], Y[ct][rt]);
+            Y[ct][rt] = mfma1632(pl, Uh[ct][s2], Y[ct][rt]);
+            Y[ct][rt] = mfma1632(ph, Ul[ct][s2], Y[ct][rt]);
+          }
         }
       }
     }
     // epilogue (delta-off: D skip and silu(z) gate; x and z re-read from LDS)
     if constexpr (kSSD) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = 16 * wu + 4 * (j16 & 3);
-        const uint2 tx = ldtr<DV>(sV, ra, ca);
-        const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
-        float zz[4] = {1.f, 1.f, 1.f, 1.f};
-        if (p.z) {
-          const uint2 tz = ldtr<DV>(sZ, ra, ca);
-          const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
+        for (int rt = 0; rt < 4; ++rt) {
+          const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = CW * wu + 16 * ct + 4 * (j16 & 3);
+          const uint2 tx = ldtr<DV>(sV, ra, ca);
+          const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
+          float zz[4] = {1.f, 1.f, 1.f, 1.f};
+          if (p.z) {
+            const uint2 tz = ldtr<DV>(sZ, ra, ca);
+            const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Y[ct][rt][e] = (Y[ct][rt][e] + Dc[ct] * xv[e]) * zz[e];
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Y[rt][e] = (Y[rt][e] + Dc * xv[e]) * zz[e];
-      }
     }
-    {
+    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored in the next landing phase
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          opk[ct][rt][0] = cvt2(Y[ct][rt][0], Y[ct][rt][1]);
+          opk[ct][rt][1] = cvt2(Y[ct][rt][2], Y[ct][rt][3]);
+        }
+      o_t0 = t0;
+      o_n = n;
+    } else {
       char* base = out_base(t0);
       auto put = [&](bool masked) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          uint32_t pk[2] = {0u, 0u};
-          if constexpr (sizeof(OutT) == 2) {
-            pk[0] = cvt2(Y[rt][0], Y[rt][1]);
-            pk[1] = cvt2(Y[rt][2], Y[rt][3]);
-          }
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * rt + 4 * g16 + r;
-            if (masked && i >= n) continue;
-            if constexpr (sizeof(OutT) == 2)
-              *reinterpret_cast<u16*>(base + out_off(i, j16)) = (u16)((r & 1) ? (pk[r >> 1] >> 16) : (pk[r >> 1] & 0xffffu));
-            else
-              *reinterpret_cast<OutT*>(base + out_off(i, j16)) = Y[rt][r];
-          }
-        }
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 16 * rt + 4 * g16 + r;
+              if (!masked || i < n) *reinterpret_cast<OutT*>(base + out_off(i, 16 * ct + j16)) = Y[ct][rt][r];
+            }
       };
       if (n == C) put(false); else put(true);   // uniform branch
     }
@@ -423,40 +501,49 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
       for (int rt = 0; rt < 4; ++rt) {
         const float4 cs = ld_f4(&sCS[PAR][16 * rt + 4 * g16]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) U[rt][e] *= f4get(cs, e);
-      }
-      bf16x8 Wh[2], Wl[2];
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) pair_split(U[2 * s2], U[2 * s2 + 1], Wh[s2], Wl[s2]);
+          for (int e = 0; e < 4; ++e) U[ct][rt][e] *= f4get(cs, e);
+      }
+      bf16x8 Wh[CT][2], Wl[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Wh[ct][s2], Wl[ct][s2]);
       // A operand K^T: row d_k = 16 tk + j16; k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
       const int rb = 4 * g16 + (j16 >> 2);
 #pragma unroll
       for (int tk = 0; tk < NTK; ++tk) {
-        Sacc[tk] *= gC;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
         const int ca = kperm(16 * tk + 4 * (j16 & 3));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, ca), ldtr<DK>(K, 32 * s2 + 16 + rb, ca));
-          Sacc[tk] = mfma1632(kt, Wh[s2], Sacc[tk]);
-          Sacc[tk] = mfma1632(kt, Wl[s2], Sacc[tk]);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            Sacc[ct][tk] = mfma1632(kt, Wh[ct][s2], Sacc[ct][tk]);
+            Sacc[ct][tk] = mfma1632(kt, Wl[ct][s2], Sacc[ct][tk]);
+          }
         }
       }
     }
   };
 
   // ================================================================ staging
-  constexpr int NST = NSW * kWave;
-  const int si = tid;                         // staging index (state waves)
-  TileRegs<DK, NST, true> rq_, rk_;           // Q, K of chunk c + 2 in flight during step c
-  TileRegs<DV, NST, false> rv_, rz_;          // V (Z) of chunk c + 1
-  float rg_ = 0.f, rb_ = 0.f;                 // producers: log g, beta of chunk c + 2 (lane = token)
+  // Every wave stages an equal share of the raw rows: Q, K of chunk c + 2 and V (z)
+  // of chunk c + 1 are in flight in registers during step c.  The loads and the
+  // landing are the same code on every wave (no role branch), so the compiler's
+  // wait bookkeeping for them is the same on both roles' paths.
+  constexpr int NST = (NSW + kNP) * kWave;
+  const int si = tid;                         // staging index
+  TileRegs<DK, NST> rq_, rk_;
+  TileRegs<DV, NST> rv_, rz_;                 // (z: delta-off only)
+  float rg_ = 0.f, rb_ = 0.f;                 // log g, beta of chunk c + 2 (lane = token), for the producers
   auto stage_qk = [&](int cc) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     rq_.load(qg, p.q_stride, t0, n, si);
     rk_.load(kg, p.k_stride, t0, n, si);
-  };
-  auto stage_gates = [&](int cc) {
-    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     const int64_t gi = (int64_t)(t0 + (lane < n ? lane : 0)) * p.H_v + h;
     rg_ = p.log_g[gi];
     rb_ = p.beta[gi];
@@ -464,9 +551,7 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
   auto stage_v = [&](int cc) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     rv_.load(vg, p.v_stride, t0, n, si);
-    if constexpr (kSSD) {
-      if (p.z) rz_.load(zg, p.z_stride, t0, n, si);
-    }
+    if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
   };
 
   // ================================================================ producer waves
@@ -528,7 +613,7 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
   //            tokens, T's diagonal 16x16 blocks 2t, 2t + 1 and their 16 -> 32 merge;
   //   pr 2:    the off-diagonal tile (query rows 32..63, keys 0..31) of P and A;
   //   pr 3:    after the other three have arrived, T[32..63][0..31] = -T11 A21 T00.
-  auto produce = [&](int cp, auto parq, float gcur, float bcur) {
+  auto produce = [&](int cp, auto parq) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
     int lane_o = lane;
@@ -579,8 +664,8 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
     }
 
     // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
-    float Gi = lane_o < n ? gcur : 0.f;
-    const float bt = lane_o < n ? bcur : 0.f;
+    float Gi = lane_o < n ? sGr[PQ][lane_o] : 0.f;
+    const float bt = lane_o < n ? sBr[PQ][lane_o] : 0.f;
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
       const float o = __shfl_up(Gi, off, kWave);
@@ -686,58 +771,67 @@ __global__ void __launch_bounds__((DV / 16 + kNP) * kWave, 1) chunk_kernel(SeqLa
     constexpr int PAR = decltype(parc)::value;     // parity of chunk c
     constexpr int PQ = PAR ^ 1;                    // parity of chunk c + 1
     const bool hasS = c >= 0, hasP = c + 1 < nch;
-    float gcur = 0.f, bcur = 0.f;
     lds_sync();                                    // previous step done
-    if (isP) {
-      gcur = rg_;
-      bcur = rb_;
-      if (c + 2 < nch) stage_gates(c + 2);
-    } else {
-      // land the staged data (Q, K of c + 1; V, Z of c), then stage the next
-      if (hasP) {
-        rq_.store(sQ[PQ], si);
-        rk_.store(sK[PQ], si);
-      }
-      if (hasS) {
-        rv_.store(sV, si);
-        if constexpr (kSSD) {
-          if (p.z) rz_.store(sZ, si);
-        }
-      }
-      if (c + 2 < nch) stage_qk(c + 2);
-      if (hasP) stage_v(c + 1);
+    // Land the staged data (Q, K of c + 1; V, Z of c), then stage the next.  The
+    // loads are issued unconditionally (past the last chunk they re-read it, unused):
+    // a conditional load would merge with the old values and force a wait for it.
+    const int c1 = min(c + 1, nch - 1), c2 = min(c + 2, nch - 1);
+    if (hasP) {
+      rq_.template store<true>(sQ[PQ], si);
+      rk_.template store<true>(sK[PQ], si);
     }
+    if (hasS) {
+      rv_.template store<false>(sV, si);
+      if constexpr (kSSD) {
+        if (p.z) rz_.template store<false>(sZ, si);
+      }
+    }
+    if (hasP && wu == 0) {
+      sGr[PQ][lane] = rg_;
+      sBr[PQ][lane] = rb_;
+    }
+    if (!isP) {
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      flush_out(lane_o >> 4, lane_o & 15);
+    }
+    stage_qk(c2);
+    stage_v(c1);
     lds_sync();                                    // landing done
     if (isP) {
-      if (hasP) produce(c + 1, Par<PQ>{}, gcur, bcur);
+      if (hasP) produce(c + 1, Par<PQ>{});
     } else {
       if (hasS) consume(c, Par<PAR>{});
     }
   };
 
-  if (nch > 0) {
-    if (isP) stage_gates(0); else stage_qk(0);
-  }
+  if (nch > 0) stage_qk(0);
   if (tid == 0) sSync = 0u;   // visible to all after the first barrier
   // entry state and first staged loads retired on every path here, so no wait inside
   // the loop has to cover them
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  for (int c = -1; c < nch; c += 2) {
+  for (int c = -1; c < nch && nch > 0; c += 2) {   // (an empty sequence only stores its state)
     step(c, Par<1>{});                   // c odd (c = -1: landing and the first chunk's preparation only)
     if (c + 1 < nch) step(c + 1, Par<0>{});
   }
   if (!isP) {
+    flush_out(lane >> 4, lane & 15);
 #pragma unroll
-    for (int tk = 0; tk < NTK; ++tk)
-      *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
-          make_float4(Sacc[tk][0], Sacc[tk][1], Sacc[tk][2], Sacc[tk][3]);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int tk = 0; tk < NTK; ++tk) {
+        const int col = CW * wu + 16 * ct + j16;
+        *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
+            make_float4(Sacc[ct][tk][0], Sacc[ct][tk][1], Sacc[ct][tk][2], Sacc[ct][tk][3]);
+      }
   }
 }
 
 template <int DK, int DV, bool kSSD, typename OutT>
 hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
-  dim3 grid(p.H_v, p.N), block((DV / 16 + kNP) * kWave);
-  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT>), grid, block, 0, stream, p);
+  constexpr int CT = kSSD ? 1 : 2;   // d_v columns per state wave: 32 (GDN), 16 (delta-off)
+  dim3 grid(p.H_v, p.N), block((DV / (16 * CT) + kNP) * kWave);
+  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT, CT>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -745,7 +839,10 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
 
 bool chunked_supported(const SeqLaunch& p) {
   if (!p.in_bf16 || p.d_k != 128 || p.N > 65535) return false;
-  if (p.out_stride > (int64_t(1) << 31) / (C * 4)) return false;   // 32-bit output row offsets
+  // 32-bit row offsets within a chunk (outputs and staged input rows)
+  const int64_t lim = (int64_t(1) << 31) / (C * 4);
+  if (p.out_stride > lim || p.q_stride > lim || p.k_stride > lim || p.v_stride > lim) return false;
+  if (p.z && p.z_stride > lim) return false;
   return p.ssd ? p.d_v == 64 : p.d_v == 128;
 }
 
