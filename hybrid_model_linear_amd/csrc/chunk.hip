@@ -146,6 +146,23 @@ __device__ __forceinline__ float dot2sq(uint32_t w, float a) {
   const bf16x2 x = __builtin_bit_cast(bf16x2, w);
   return __builtin_amdgcn_fdot2_f32_bf16(x, x, a, false);
 }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (no LDS round trip): four shift-and-add steps within each row of 16
+// lanes, then the last lane of row 0 (2) is added to row 1 (3), and the last lane of
+// row 1 to rows 2 and 3.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, BOUND));
+}
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  v += dpp_mov<0x111, 0xf, true>(v);    // row_shr:1 (lanes shifted in from outside the row read 0)
+  v += dpp_mov<0x112, 0xf, true>(v);    // row_shr:2
+  v += dpp_mov<0x114, 0xf, true>(v);    // row_shr:4
+  v += dpp_mov<0x118, 0xf, true>(v);    // row_shr:8
+  v += dpp_mov<0x142, 0xa, false>(v);   // row_bcast:15 into rows 1 and 3 (others add 0)
+  v += dpp_mov<0x143, 0xc, false>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
 __device__ __forceinline__ float sumsq8(const bf16x8& v, float a) {
   const uint4 u = __builtin_bit_cast(uint4, v);
   return dot2sq(u.w, dot2sq(u.z, dot2sq(u.y, dot2sq(u.x, a))));
@@ -666,12 +683,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
     float Gi = lane_o < n ? sGr[PQ][lane_o] : 0.f;
     const float bt = lane_o < n ? sBr[PQ][lane_o] : 0.f;
-#pragma unroll
-    for (int off = 1; off < C; off <<= 1) {
-      const float o = __shfl_up(Gi, off, kWave);
-      if (lane_o >= off) Gi += o;
-    }
-    const float GC = __shfl(Gi, C - 1, kWave);
+    Gi = wave_inclusive_scan(Gi);
+    const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gi), C - 1));
     pG[lane_o] = Gi;
     pB[lane_o] = bt;
 
