@@ -11,10 +11,17 @@ value = (32768 + 256) tokens / step time, inputs resident in HBM.
 
 Prints ONE JSON line.  `roofline` covers the kernel with the largest share of the
 step (per-launch time from HIP events recorded on the launch stream, which is
-torch's current stream); `cpu_baseline` times the CPU oracle on a bounded sample.
+torch's current stream); its `traffic` comes from the committed hardware-counter
+summary under profiles/ when that summary was taken on the same kernel source.
+`cpu_baseline` times the CPU oracle on a bounded sample of the prefill workload.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --summarize-prof KT_DIR FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +42,14 @@ CHUNK = 64
 EXTEND_FLOP_PER_TOKEN = H_QK * 4 * CHUNK * D + H_V * 2 * (CHUNK * D + 2 * CHUNK * D + 3 * D * D)
 GATE_BYTES_PER_TOKEN = H_V * (2 + 2 + 4 + 4)                                    # a, b -> log_g, beta
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_traffic.txt")
+KERNEL_SOURCES = {"extend": "hybrid_model_linear_amd/csrc/chunk.hip",
+                  "decode": "hybrid_model_linear_amd/csrc/recurrent.hip"}
+KERNEL_NAMES = {"extend": "chunk_kernel<128, 128, false, unsigned short",
+                "decode": "recurrent_kernel<128, 128, unsigned short"}
+PROF_CMD = "python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy-mib 1024"
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -45,12 +60,98 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter scaling)")
+    ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="summarize rocprofv3 outputs of this script into profiles/ and exit")
     return ap.parse_args()
 
 
+def source_sha(kind):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+# ------------------------------------------------------------------ counter summaries
+def _csv_rows(d, pattern):
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not files:
+        raise SystemExit(f"no {pattern} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_prof(kt_dir, fetch_dir, write_dir):
+    """profiles/ text summaries of three rocprofv3 runs of PROF_CMD: the kernel-trace
+    statistics, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same
+    counters read for the 1 GiB copy kernel (torch.mul: reads and writes 1 GiB)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = _csv_rows(kt_dir, "*kernel_stats.csv")
+    lines = ["# rocprofv3 kernel-trace statistics of the bench command",
+             f"# command: cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             f"-d <dir> -o bench -- {PROF_CMD}",
+             f"# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
+             f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in stats:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    with open(os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(d, counter):
+        vals = {}
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(vals, needle):
+        for k, v in vals.items():
+            if needle in k:
+                return sum(v) / len(v), len(v)
+        raise SystemExit(f"kernel {needle!r} not found")
+    copy_kib = 1024 * 1024.0                       # 1 GiB read and written by the copy
+
+    def pick_copy(vals):                           # the largest MulFunctor dispatch
+        return max(max(v) for k, v in vals.items() if "MulFunctor" in k)
+    cf, cw = pick_copy(fetch), pick_copy(write)
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    out = ["# HBM traffic per dispatch from rocprofv3 counters (KiB), scaled by the copy calibration",
+           f"# command (fetch): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PROF_CMD}",
+           f"# command (write): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PROF_CMD}",
+           "# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
+           f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
+           f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]
+    for kind in ("extend", "decode"):
+        fk, n = pick(fetch, KERNEL_NAMES[kind])
+        wk, _ = pick(write, KERNEL_NAMES[kind])
+        out += [f"{kind}_source_sha256 {source_sha(kind)}", f"{kind}_dispatches {n}",
+                f"{kind}_fetch_kib {fk:.1f}", f"{kind}_write_kib {wk:.1f}",
+                f"{kind}_traffic_bytes {int(round((fk * f_scale + wk * w_scale) * 1024))}"]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + out))
+
+
+def measured_traffic(kind):
+    """Scaled counter traffic per launch of `kind`, or None when no summary exists or
+    it was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(None, 1) for l in f.read().splitlines() if l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get(f"{kind}_source_sha256", "").strip() != source_sha(kind):
+        return None
+    return int(kv[f"{kind}_traffic_bytes"])
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
 def cpu_baseline(ext, seconds):
-    """Oracle (float64, token by token, all 32 heads) on the first tokens of prefill
-    sequence 0, as many as fit in `seconds` of CPU time; tokens/s on one thread."""
+    """The float64 oracle, token by token over all 32 heads, on the prefill workload's
+    sequences in order (64-token blocks carrying the state), as many tokens as fit in
+    `seconds` of CPU time on one thread; tokens/s."""
     import numpy as np
     import oracle
     try:
@@ -58,36 +159,48 @@ def cpu_baseline(ext, seconds):
     except Exception:  # pragma: no cover
         threadpool_limits = None
     ctx = threadpool_limits(1) if threadpool_limits else None
-    n = 64
-    mixed = ext.mixed_qkv[:4096].float().cpu().numpy()
-    a = ext.a[:4096].float().cpu().numpy()
-    b = ext.b[:4096].float().cpu().numpy()
+    blk = 64
     nq = H_QK * D
-    done, spent = 0, 0.0
-    S = np.zeros((1, H_V, D, D))
+    cu = ext.cu_seqlens
+    done, spent, seqs = 0, 0.0, 0
     try:
-        while spent < seconds and done + n <= 4096:
-            sl = slice(done, done + n)
-            q = mixed[sl, :nq].reshape(n, H_QK, D)
-            k = mixed[sl, nq:2 * nq].reshape(n, H_QK, D)
-            v = mixed[sl, 2 * nq:].reshape(n, H_V, D)
-            t = time.perf_counter()
-            _, _, fin = oracle.gdn_extend(q, k, v, a[sl], b[sl], ext.A_log, ext.dt_bias,
-                                          np.array([0, n]), np.array([0]), np.array([int(done > 0)]),
-                                          S, ext.scale)
-            spent += time.perf_counter() - t
-            S = fin[0][None]
-            done += n
+        for s in range(len(cu) - 1):
+            t0, t1 = int(cu[s]), int(cu[s + 1])
+            S = np.zeros((1, H_V, D, D))
+            seqs += 1
+            for b0 in range(t0, t1, blk):
+                if spent >= seconds:
+                    break
+                b1 = min(t1, b0 + blk)
+                n = b1 - b0
+                mixed = ext.mixed_qkv[b0:b1].float().cpu().numpy()
+                a = ext.a[b0:b1].float().cpu().numpy()
+                b = ext.b[b0:b1].float().cpu().numpy()
+                q = mixed[:, :nq].reshape(n, H_QK, D)
+                k = mixed[:, nq:2 * nq].reshape(n, H_QK, D)
+                v = mixed[:, 2 * nq:].reshape(n, H_V, D)
+                t = time.perf_counter()
+                _, _, fin = oracle.gdn_extend(q, k, v, a, b, ext.A_log, ext.dt_bias,
+                                              np.array([0, n]), np.array([0]), np.array([int(b0 > t0)]),
+                                              S, ext.scale)
+                spent += time.perf_counter() - t
+                S = fin[0][None]
+                done += n
+            if spent >= seconds:
+                break
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    return {"value": done / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle, prefill sequence 0 tokens [0, {done}) x all {H_V} heads "
-                      f"({spent:.1f} s, one thread)"}
+    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle, first {done} tokens of the prefill workload ({seqs} sequence(s) "
+                      f"of 4096, state carried in 64-token blocks) x all {H_V} heads, {spent:.1f} s on one thread"}
 
 
 def main():
     args = parse()
+    if args.summarize_prof:
+        summarize_prof(*args.summarize_prof)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer needs no collective; heads and "
               f"sequences shard independently); --gpus {args.gpus} is not supported",
@@ -181,6 +294,8 @@ def main():
                       "flop": work[n]["flop"], "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 2),
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+    for n in ("extend", "decode"):
+        kernels[n]["traffic_bytes"] = measured_traffic(n)
     dom = max(("extend", "decode"), key=lambda n: per[n])
     kd = kernels[dom]
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -190,7 +305,7 @@ def main():
                 "peak": HBM_PEAK_GBS if ai < ridge else MFMA_BF16_PEAK_TFLOPS,
                 "unit": "GB/s" if ai < ridge else "TFLOP/s",
                 "frac": kd["hbm_frac"] if ai < ridge else kd["mfma_frac"],
-                "traffic": None, "arith_intensity": round(ai, 1),
+                "traffic": kd["traffic_bytes"], "arith_intensity": round(ai, 1),
                 "mfma_frac": kd["mfma_frac"], "avg_launch_us": kd["avg_us"]}
     tokens = T_e + T_d
     result = {
