@@ -305,15 +305,22 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         Sacc[ct][tk] = f32x4{v.x, v.y, v.z, v.w};
       }
     }
-  // delta-off D skip coefficient of this lane's columns
-  float Dc[CT];
+  // delta-off D skip coefficients of this lane's output columns (16 ct + 4 g16 + e)
+  float4 Dc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    Dc[ct] = 0.f;
+    Dc[ct] = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (kSSD) {
       const u16* Db = reinterpret_cast<const u16*>(p.D);
-      const int col = CW * wu + 16 * ct + j16;
-      if (!isP && Db) Dc[ct] = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
+      if (!isP && Db) {
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = CW * wu + 16 * ct + 4 * g16 + e;
+          d[e] = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * DV + col : (int64_t)h]);
+        }
+        Dc[ct] = make_float4(d[0], d[1], d[2], d[3]);
+      }
     }
   }
 
@@ -326,20 +333,14 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     if constexpr (sizeof(OutT) == 2) {
       if (o_t0 < 0) return;
       char* base = out_base(o_t0);
-      auto put = [&](bool masked) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 16 * rt + 4 * gg + r;
-              const uint32_t wv = opk[ct][rt][r >> 1];
-              if (!masked || i < o_n)
-                *reinterpret_cast<u16*>(base + out_off(i, 16 * ct + jj)) = (u16)((r & 1) ? (wv >> 16) : (wv & 0xffffu));
-            }
-      };
-      if (o_n == C) put(false); else put(true);   // uniform branch
+        for (int rt = 0; rt < 4; ++rt) {   // token 16 rt + jj, columns 16 ct + 4 gg .. + 3
+          const int i = 16 * rt + jj;
+          if (i < o_n)
+            *reinterpret_cast<uint2*>(base + out_off(i, 16 * ct + 4 * gg)) = make_uint2(opk[ct][rt][0], opk[ct][rt][1]);
+        }
       o_t0 = -1;
     }
   };
@@ -359,7 +360,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     const u16* K = sK[PAR];
     const float gC = sGC[PAR][0];
 
-    f32x4 Y[CT][4], U[CT][4];  // row tiles of 16 tokens: rows 16 rt + 4 g16 + r
+    // U: tiles of 16 tokens (rows 16 rt + 4 g16 + r) x 16 d_v columns (lane j16).
+    // Y: the output in transposed tiles (O^T: rows = d_v 16 ct + 4 g16 + r, lane j16 =
+    // token 16 rt + j16), from the same operands with A and B swapped, so that a lane
+    // holds 4 consecutive output columns of one token (8-byte stores).
+    f32x4 Y[CT][4], U[CT][4];
     {
       bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
 #pragma unroll
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         for (int s2 = 0; s2 < NKS; ++s2) {
           const bf16x8 aq = ld8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632(aq, Sb[ct][s2], Y[ct][rt]);
+          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632(Sb[ct][s2], aq, Y[ct][rt]);   // (Q S0^T)^T
           if constexpr (!kSSD) {
             const bf16x8 ak = ld8<DK>(K, row, 32 * s2 + 8 * g16);
 #pragma unroll
@@ -447,11 +452,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Uh[ct][s2], Ul[ct][s2]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const float4 co = ld_f4(&sCO[PAR][16 * rt + 4 * g16]);
+        const float co = sCO[PAR][16 * rt + j16];    // this lane's token
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Y[ct][rt][e] *= f4get(co, e);
+        for (int ct = 0; ct < CT; ++ct) Y[ct][rt] *= co;
         const u16* phrow = &sPh[PAR][16 * rt + j16][8 * g16];
         const u16* plrow = &sPl[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
@@ -459,10 +462,10 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           const bf16x8 ph = ld8u(phrow + 32 * s2);
           const bf16x8 pl = ld8u(plrow + 32 * s2);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            Y[ct][rt] = mfma1632(ph, Uh[ct][s2], Y[ct][rt]);
-            Y[ct][rt] = mfma1632(pl, Uh[ct][s2], Y[ct][rt]);
-            Y[ct][rt] = mfma1632(ph, Ul[ct][s2], Y[ct][rt]);
+          for (int ct = 0; ct < CT; ++ct) {   // (P U)^T = U^T P^T
+            Y[ct][rt] = mfma1632(Uh[ct][s2], ph, Y[ct][rt]);
+            Y[ct][rt] = mfma1632(Uh[ct][s2], pl, Y[ct][rt]);
+            Y[ct][rt] = mfma1632(Ul[ct][s2], ph, Y[ct][rt]);
           }
         }
       }
@@ -472,19 +475,19 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int ra = 16 * rt + 4 * g16 + (j16 >> 2), ca = CW * wu + 16 * ct + 4 * (j16 & 3);
-          const uint2 tx = ldtr<DV>(sV, ra, ca);
+        for (int rt = 0; rt < 4; ++rt) {   // token 16 rt + j16, columns 16 ct + 4 g16 + e
+          const int ra = 16 * rt + j16, ca = CW * wu + 16 * ct + 4 * g16;
+          const uint2 tx = *reinterpret_cast<const uint2*>(&sV[pidx<DV>(ra, ca)]);
           const float xv[4] = {bf_lo(tx.x), bf_hi(tx.x), bf_lo(tx.y), bf_hi(tx.y)};
           float zz[4] = {1.f, 1.f, 1.f, 1.f};
           if (p.z) {
-            const uint2 tz = ldtr<DV>(sZ, ra, ca);
+            const uint2 tz = *reinterpret_cast<const uint2*>(&sZ[pidx<DV>(ra, ca)]);
             const float zr[4] = {bf_lo(tz.x), bf_hi(tz.x), bf_lo(tz.y), bf_hi(tz.y)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) zz[e] = zr[e] * sigmoid_f(zr[e]);
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Y[ct][rt][e] = (Y[ct][rt][e] + Dc[ct] * xv[e]) * zz[e];
+          for (int e = 0; e < 4; ++e) Y[ct][rt][e] = (Y[ct][rt][e] + f4get(Dc[ct], e) * xv[e]) * zz[e];
         }
     }
     if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored in the next landing phase
@@ -499,18 +502,15 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       o_n = n;
     } else {
       char* base = out_base(t0);
-      auto put = [&](bool masked) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 16 * rt + 4 * g16 + r;
-              if (!masked || i < n) *reinterpret_cast<OutT*>(base + out_off(i, 16 * ct + j16)) = Y[ct][rt][r];
-            }
-      };
-      if (n == C) put(false); else put(true);   // uniform branch
+        for (int rt = 0; rt < 4; ++rt) {
+          const int i = 16 * rt + j16;
+          if (i < n)
+            *reinterpret_cast<float4*>(base + out_off(i, 16 * ct + 4 * g16)) =
+                make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
+        }
     }
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
     {
@@ -852,6 +852,10 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
 
 bool chunked_supported(const SeqLaunch& p) {
   if (!p.in_bf16 || p.d_k != 128 || p.N > 65535) return false;
+  // 16-byte row segments of q, k, v (z) are staged with single loads
+  const uintptr_t ptrs = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.k) |
+                         reinterpret_cast<uintptr_t>(p.v) | reinterpret_cast<uintptr_t>(p.z);
+  if (ptrs % 16 != 0 || (p.q_stride | p.k_stride | p.v_stride | (p.z ? p.z_stride : 0)) % 8 != 0) return false;
   // 32-bit row offsets within a chunk (outputs and staged input rows)
   const int64_t lim = (int64_t(1) << 31) / (C * 4);
   if (p.out_stride > lim || p.q_stride > lim || p.k_stride > lim || p.v_stride > lim) return false;

@@ -19,6 +19,11 @@ int hip_status(hipError_t e) {
 
 bool dtype_ok(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+// A row start aligned to 4 elements of its dtype (null pointers are checked elsewhere).
+bool aligned4(const void* ptr, int32_t dtype) {
+  const uintptr_t bytes = dtype == GDN_BF16 ? 8 : 16;
+  return reinterpret_cast<uintptr_t>(ptr) % bytes == 0;
+}
 
 // Checks shared by gdn_extend and gdn_decode; fills everything but the
 // per-call index fields.
@@ -30,6 +35,8 @@ int check_seq_common(int32_t in_dtype, int32_t out_dtype, int32_t H_qk, int32_t 
   if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return GDN_E_UNSUPPORTED;
   if (q_stride < (int64_t)H_qk * d_k || k_stride < (int64_t)H_qk * d_k) return GDN_E_SHAPE;
   if (v_stride < (int64_t)H_v * d_v || out_stride < (int64_t)H_v * d_v) return GDN_E_SHAPE;
+  // rows are accessed 4 elements at a time
+  if ((q_stride | k_stride | v_stride | out_stride) % 4 != 0) return GDN_E_SHAPE;
   if (num_slots <= 0) return GDN_E_SHAPE;
   if (!std::isfinite(scale)) return GDN_E_SHAPE;
   return GDN_OK;
@@ -107,6 +114,10 @@ int gdn_extend(const gdn_extend_args* a, void* stream) {
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->out))
     return GDN_E_NULL;
   if (a->T > INT32_MAX) return GDN_E_SHAPE;      // cu_seqlens is int32
+  if (!aligned4(a->q, a->in_dtype) || !aligned4(a->k, a->in_dtype) || !aligned4(a->v, a->in_dtype) ||
+      !aligned4(a->z, a->in_dtype) || !aligned4(a->out, a->out_dtype) || a->z_stride % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(a->pool) % 16 != 0)
+    return GDN_E_SHAPE;
 
   gdn::SeqLaunch p{};
   p.ssd = a->mode == GDN_MODE_SSD;
@@ -156,6 +167,9 @@ int gdn_decode(const gdn_decode_args* a, void* stream) {
   if (a->B == 0) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->slot || !a->pool || !a->out)
     return GDN_E_NULL;
+  if (!aligned4(a->q, a->in_dtype) || !aligned4(a->k, a->in_dtype) || !aligned4(a->v, a->in_dtype) ||
+      !aligned4(a->out, a->out_dtype) || reinterpret_cast<uintptr_t>(a->pool) % 16 != 0)
+    return GDN_E_SHAPE;
   gdn::SeqLaunch p{};
   p.ssd = 0;
   p.in_bf16 = a->in_dtype == GDN_BF16;

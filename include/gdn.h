@@ -22,6 +22,9 @@
  *     legacy default stream) and the call returns at once.
  *   - Strides and sizes are in elements, not bytes.  Within a token, heads are
  *     contiguous: element (t, head, i) of q is q[t * q_stride + head * d_k + i].
+ *   - Rows are accessed 4 elements at a time: q, k, v, z and out must be aligned
+ *     to 4 elements of their dtype (8 bytes bf16, 16 bytes fp32), the pool to 16
+ *     bytes, and every token stride must be a multiple of 4; otherwise GDN_E_SHAPE.
  *   - Host-side validation runs first; on any error the call returns a nonzero
  *     gdn_status, launches nothing and touches no buffer.  A failed launch returns
  *     GDN_E_HIP; gdn_last_hip_error() then gives the hipError_t (per thread).

@@ -87,6 +87,9 @@ FAKE = ct.c_void_p(0x1000)   # never dereferenced: every case below fails valida
     (dict(scale=float("nan")), _lib.GDN_E_SHAPE),
     (dict(D=FAKE), _lib.GDN_E_SHAPE),                            # SSD-only input in GDN mode
     (dict(N=-1), _lib.GDN_E_SHAPE),
+    (dict(q_stride=2 * 2 * 128 + 4 * 128 + 2), _lib.GDN_E_SHAPE),  # stride not a multiple of 4
+    (dict(cu_seqlens=FAKE, slot=FAKE, pool=FAKE, q=ct.c_void_p(0x1002), k=FAKE, v=FAKE, log_g=FAKE,
+          beta=FAKE, out=FAKE), _lib.GDN_E_SHAPE),               # q not 8-byte aligned (bf16)
 ])
 def test_extend_validation(kw, status):
     lib = gdn.load()
