@@ -48,14 +48,16 @@ KERNEL_SOURCES = {"extend": "hybrid_model_linear_amd/csrc/chunk.hip",
                   "decode": "hybrid_model_linear_amd/csrc/recurrent.hip"}
 KERNEL_NAMES = {"extend": "chunk_kernel<128, 128, false, unsigned short",
                 "decode": "recurrent_kernel<128, 128, unsigned short"}
-PROF_CMD = "python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy-mib 1024"
+PROF_CMD = "python bench.py --steps 20 --warmup 1000 --no-cpu-baseline --calibrate-copy-mib 1024"
+PMC_CMD = "python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy-mib 1024"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    # ~0.6 s of warm-up: the GPU's clocks settle before the timed region
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -118,8 +120,8 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
     cf, cw = pick_copy(fetch), pick_copy(write)
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
     out = ["# HBM traffic per dispatch from rocprofv3 counters (KiB), scaled by the copy calibration",
-           f"# command (fetch): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PROF_CMD}",
-           f"# command (write): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PROF_CMD}",
+           f"# command (fetch): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
+           f"# command (write): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
            "# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
            f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
            f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]

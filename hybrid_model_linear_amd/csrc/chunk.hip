@@ -324,25 +324,28 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
   }
 
-  // bf16 outputs of chunk c, stored in the landing phase of the next step before the
-  // next loads are issued: the landing's wait for the staged loads then never waits
-  // for these stores (the memory counter retires in order).
-  uint32_t opk[CT][4][2];
-  int o_t0 = -1, o_n = 0;
-  auto flush_out = [&](int gg, int jj) {   // (lane indices from an opaque copy)
-    if constexpr (sizeof(OutT) == 2) {
-      if (o_t0 < 0) return;
-      char* base = out_base(o_t0);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {   // token 16 rt + jj, columns 16 ct + 4 gg .. + 3
-          const int i = 16 * rt + jj;
-          if (i < o_n)
-            *reinterpret_cast<uint2*>(base + out_off(i, 16 * ct + 4 * gg)) = make_uint2(opk[ct][rt][0], opk[ct][rt][1]);
-        }
-      o_t0 = -1;
-    }
+  // ================================================================ staging
+  // Every wave stages an equal share of the raw rows: Q, K of chunk c + 2 and V (z)
+  // of chunk c + 1 are in flight in registers during step c (producers issue them in
+  // the landing phase, state waves in the middle of their step).  The landing is the
+  // same code on every wave.
+  constexpr int NST = (NSW + kNP) * kWave;
+  const int si = tid;                         // staging index
+  TileRegs<DK, NST> rq_, rk_;
+  TileRegs<DV, NST> rv_, rz_;                 // (z: delta-off only)
+  float rg_ = 0.f, rb_ = 0.f;                 // log g, beta of chunk c + 2 (lane = token), for the producers
+  auto stage_qk = [&](int cc) {
+    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
+    rq_.load(qg, p.q_stride, t0, n, si);
+    rk_.load(kg, p.k_stride, t0, n, si);
+    const int64_t gi = (int64_t)(t0 + (lane < n ? lane : 0)) * p.H_v + h;
+    rg_ = p.log_g[gi];
+    rb_ = p.beta[gi];
+  };
+  auto stage_v = [&](int cc) {
+    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
+    rv_.load(vg, p.v_stride, t0, n, si);
+    if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
   };
 
   // State-dependent part of chunk c (buffers of parity PAR).  A operands (rows of Q,
@@ -392,6 +395,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
     }
+    // This wave's share of the next staged rows (Q, K of chunk c + 2, V of c + 1):
+    // issued here rather than in the landing phase, so that the landing's LDS writes
+    // are all the state waves do between the two barriers, and before this step's
+    // output stores, so that the next landing's wait for these loads never includes
+    // the stores (the memory counter retires in order).
+    stage_qk(min(c + 2, nch - 1));
+    stage_v(min(c + 1, nch - 1));
     // R = beta V - CR X (GDN); U = beta V (delta-off).  V through transpose reads.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -490,26 +500,21 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           for (int e = 0; e < 4; ++e) Y[ct][rt][e] = (Y[ct][rt][e] + f4get(Dc[ct], e) * xv[e]) * zz[e];
         }
     }
-    if constexpr (sizeof(OutT) == 2) {   // bf16: packed now, stored in the next landing phase
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          opk[ct][rt][0] = cvt2(Y[ct][rt][0], Y[ct][rt][1]);
-          opk[ct][rt][1] = cvt2(Y[ct][rt][2], Y[ct][rt][3]);
-        }
-      o_t0 = t0;
-      o_n = n;
-    } else {
+    {
       char* base = out_base(t0);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const int i = 16 * rt + j16;
-          if (i < n)
-            *reinterpret_cast<float4*>(base + out_off(i, 16 * ct + 4 * g16)) =
-                make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
+          if (i < n) {
+            if constexpr (sizeof(OutT) == 2)
+              *reinterpret_cast<uint2*>(base + out_off(i, 16 * ct + 4 * g16)) =
+                  make_uint2(cvt2(Y[ct][rt][0], Y[ct][rt][1]), cvt2(Y[ct][rt][2], Y[ct][rt][3]));
+            else
+              *reinterpret_cast<float4*>(base + out_off(i, 16 * ct + 4 * g16)) =
+                  make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
+          }
         }
     }
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
@@ -545,30 +550,6 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
     }
-  };
-
-  // ================================================================ staging
-  // Every wave stages an equal share of the raw rows: Q, K of chunk c + 2 and V (z)
-  // of chunk c + 1 are in flight in registers during step c.  The loads and the
-  // landing are the same code on every wave (no role branch), so the compiler's
-  // wait bookkeeping for them is the same on both roles' paths.
-  constexpr int NST = (NSW + kNP) * kWave;
-  const int si = tid;                         // staging index
-  TileRegs<DK, NST> rq_, rk_;
-  TileRegs<DV, NST> rv_, rz_;                 // (z: delta-off only)
-  float rg_ = 0.f, rb_ = 0.f;                 // log g, beta of chunk c + 2 (lane = token), for the producers
-  auto stage_qk = [&](int cc) {
-    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
-    rq_.load(qg, p.q_stride, t0, n, si);
-    rk_.load(kg, p.k_stride, t0, n, si);
-    const int64_t gi = (int64_t)(t0 + (lane < n ? lane : 0)) * p.H_v + h;
-    rg_ = p.log_g[gi];
-    rb_ = p.beta[gi];
-  };
-  auto stage_v = [&](int cc) {
-    const int t0 = tbeg + cc * C, n = min(C, tend - t0);
-    rv_.load(vg, p.v_stride, t0, n, si);
-    if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
   };
 
   // ================================================================ producer waves
@@ -785,9 +766,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     constexpr int PQ = PAR ^ 1;                    // parity of chunk c + 1
     const bool hasS = c >= 0, hasP = c + 1 < nch;
     lds_sync();                                    // previous step done
-    // Land the staged data (Q, K of c + 1; V, Z of c), then stage the next.  The
-    // loads are issued unconditionally (past the last chunk they re-read it, unused):
-    // a conditional load would merge with the old values and force a wait for it.
+    // Land the staged data (Q, K of c + 1; V, Z of c).  Staging loads are issued
+    // unconditionally (past the last chunk they re-read it, unused): a conditional
+    // load would merge with the old values and force a wait for it.
     const int c1 = min(c + 1, nch - 1), c2 = min(c + 2, nch - 1);
     if (hasP) {
       rq_.template store<true>(sQ[PQ], si);
@@ -803,18 +784,19 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sGr[PQ][lane] = rg_;
       sBr[PQ][lane] = rb_;
     }
-    if (!isP) {
-      int lane_o = lane;
-      asm volatile("" : "+v"(lane_o));
-      flush_out(lane_o >> 4, lane_o & 15);
+    if (isP) {   // (the state waves stage theirs in the middle of the step)
+      stage_qk(c2);
+      stage_v(c1);
     }
-    stage_qk(c2);
-    stage_v(c1);
     lds_sync();                                    // landing done
     if (isP) {
       if (hasP) produce(c + 1, Par<PQ>{});
     } else {
       if (hasS) consume(c, Par<PAR>{});
+      else {   // step -1: no chunk to consume, stage chunk 1's rows here
+        stage_qk(c2);
+        stage_v(c1);
+      }
     }
   };
 
@@ -828,7 +810,6 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     if (c + 1 < nch) step(c + 1, Par<0>{});
   }
   if (!isP) {
-    flush_out(lane >> 4, lane & 15);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
