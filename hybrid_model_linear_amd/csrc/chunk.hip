@@ -122,6 +122,21 @@ __device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// x - (low / high bf16 of the packed pair w) in one v_dot2_f32_bf16 against the pair
+// (-1, 0) / (0, -1): the products are exact and the difference of a float and its
+// bf16 rounding is representable, so the result is exact.  The constant pair is
+// passed in a scalar register: as an inline constant the compiler would encode
+// (-1, 0) as "-1.0", which the hardware does not read as that bf16 pair.
+__device__ __forceinline__ bf16x2 sreg_pair(uint32_t v) {
+  asm("" : "+s"(v));
+  return __builtin_bit_cast(bf16x2, v);
+}
+__device__ __forceinline__ float sub_bf_lo(uint32_t w, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), sreg_pair(0x0000BF80u), x, false);
+}
+__device__ __forceinline__ float sub_bf_hi(uint32_t w, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), sreg_pair(0xBF800000u), x, false);
+}
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), for the pair layout above
 __device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -129,7 +144,7 @@ __device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     h[e] = cvt2(x[2 * e], x[2 * e + 1]);
-    l[e] = cvt2(x[2 * e] - bf_lo(h[e]), x[2 * e + 1] - bf_hi(h[e]));
+    l[e] = cvt2(sub_bf_lo(h[e], x[2 * e]), sub_bf_hi(h[e], x[2 * e + 1]));
   }
   hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
   lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
@@ -250,9 +265,12 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
   // producer working set (per producer wave where private)
   __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS];
-  __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16][20];
-  __shared__ __attribute__((aligned(16))) float sPG[kNP][C], sPBt[kNP][C], sPRk[kNP][C], sPRq[kNP][C];
-  __shared__ uint32_t sSync;                               // producer arrival counter
+  // fp32 diagonal 16x16 blocks of A, rows of 20 floats; the block stride of 336
+  // floats puts the four blocks on different banks (the solve reads all four at once)
+  __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16 * 20 + 16];
+  // vectors of the chunk being prepared, per token (see the producer roles)
+  __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
+  __shared__ uint32_t sSync[4];   // producer arrival counters: vectors, diagonal tiles, T's diagonal half
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
@@ -433,14 +451,14 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           f32x4& u1 = U[ct][2 * s2 + 1];
           Rb[ct][s2] = pair_to_op(u0, u1);
           const uint4 rw = __builtin_bit_cast(uint4, Rb[ct][s2]);
-          u0[0] -= bf_lo(rw.x);
-          u0[1] -= bf_hi(rw.x);
-          u0[2] -= bf_lo(rw.y);
-          u0[3] -= bf_hi(rw.y);
-          u1[0] -= bf_lo(rw.z);
-          u1[1] -= bf_hi(rw.z);
-          u1[2] -= bf_lo(rw.w);
-          u1[3] -= bf_hi(rw.w);
+          u0[0] = sub_bf_lo(rw.x, u0[0]);
+          u0[1] = sub_bf_hi(rw.x, u0[1]);
+          u0[2] = sub_bf_lo(rw.y, u0[2]);
+          u0[3] = sub_bf_hi(rw.y, u0[3]);
+          u1[0] = sub_bf_lo(rw.z, u1[0]);
+          u1[1] = sub_bf_hi(rw.z, u1[1]);
+          u1[2] = sub_bf_lo(rw.w, u1[2]);
+          u1[3] = sub_bf_hi(rw.w, u1[3]);
         }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -555,62 +573,43 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // ================================================================ producer waves
 
   // Tile (ti, tj) of K Q^T and K K^T (the transposes of Q K^T and K K^T: each lane
-  // holds one query row i = 32 ti + l32 and keys m = 32 tj + 8 q4 + 4 hh + e), with
-  // the half-row sums of squares of its operand rows: K rows 32 tj + l32 (sqA), Q rows
-  // 32 ti + l32 (sqQ) and K rows 32 ti + l32 (sqK).
-  auto tile_mma = [&](const u16* Q, const u16* K, int ti, int tj, int l32, int hh, f32x16& qk,
-                      f32x16& kk, float& sqA, float& sqQ, float& sqK) {
+  // holds one query row i = 32 ti + l32 and keys m = 32 tj + 8 q4 + 4 hh + e).
+  auto tile_mma = [&](const u16* Q, const u16* K, int ti, int tj, int l32, int hh, f32x16& qk, f32x16& kk) {
     qk = f32x16{};
     kk = f32x16{};
-    sqA = 0.f;
-    sqQ = 0.f;
-    sqK = 0.f;
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
       const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
-      const bf16x8 bq = ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh);
-      qk = mfma32(a, bq, qk);
-      if constexpr (!kSSD) {
-        const bf16x8 bk = ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh);
-        kk = mfma32(a, bk, kk);
-        sqA = sumsq8(a, sqA);
-        sqQ = sumsq8(bq, sqQ);
-        if (ti != tj) sqK = sumsq8(bk, sqK);
-      }
-    }
-    if (ti == tj) sqK = sqA;
-  };
-  // 1 / |row| from the two half-row sums of lanes l32 and l32 + 32 (zero past the end)
-  auto inv_norm = [&](float sq, int row, int n) {
-    if constexpr (kSSD) {
-      return row < n ? 1.f : 0.f;
-    } else {
-      sq += __shfl_xor(sq, 32, kWave);
-      return row < n ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;   // 1 ulp
+      qk = mfma32(a, ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
+      if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
     }
   };
-  // Hand-off between producer waves: an arrival counter in LDS.  A wave's LDS writes
+  // Hand-off between producer waves: arrival counters in LDS.  A wave's LDS writes
   // are performed before its later increment (the LDS executes one wave's accesses
-  // in order); the waiting wave reads the data only after seeing the count.  The
-  // wait is bounded: every producer arrives once per step unconditionally.
-  auto arrive = [&]() {
+  // in order); the waiting wave reads the data only after seeing the count.  Waits
+  // are bounded: every producer arrives unconditionally in every step.
+  auto arrive = [&](uint32_t* ctr) {
     lds_order();
-    if (lane == 0) __hip_atomic_fetch_add(&sSync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
-  auto wait_count = [&](uint32_t target) {
+  auto wait_count = [&](uint32_t* ctr, uint32_t target) {
     for (int it = 0; it < (1 << 22); ++it) {
-      if (__hip_atomic_load(&sSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
       __builtin_amdgcn_s_sleep(1);
     }
     lds_order();
   };
   uint32_t pgen = 0;                          // producer steps so far (uniform)
+  constexpr float kLog2e = 1.4426950408889634f;
 
-  // Prepare chunk cp into the buffers of parity PQ (producer role pr = wave - NSW):
-  //   pr 0, 1: diagonal tile t = pr of P and A, the coefficient vectors of its 32
-  //            tokens, T's diagonal 16x16 blocks 2t, 2t + 1 and their 16 -> 32 merge;
-  //   pr 2:    the off-diagonal tile (query rows 32..63, keys 0..31) of P and A;
-  //   pr 3:    after the other three have arrived, T[32..63][0..31] = -T11 A21 T00.
+  // Prepare chunk cp into the buffers of parity PQ.  Producer roles (pr = wave - NSW):
+  //   pr 3:    the chunk's vectors (lane = token): decay cumsum, row norms, the
+  //            coefficient vectors and the decay factors of the P / A tiles; then T's
+  //            zero blocks and, once T's diagonal half is done, T[32..63][0..31];
+  //   pr 0, 1: diagonal tile t = pr of P and A (one exp per element);
+  //   pr 2:    the off-diagonal tile (rows 32..63, keys 0..31), whose decay factors
+  //            into a row and a key factor split at token 31 (both <= 1); then T's four
+  //            diagonal 16x16 blocks and the two 16 -> 32 merges.
   auto produce = [&](int cp, auto parq) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
@@ -621,20 +620,50 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     const int pr = wu - NSW;
     const u16* Q = sQ[PQ];
     const u16* K = sK[PQ];
-    float* pG = sPG[pr];
-    float* pB = sPBt[pr];
-    float* pRk = sPRk[pr];
-    float* pRq = sPRq[pr];
     ++pgen;
 
     if (pr == 3) {
-      if constexpr (!kSSD) {
-        {   // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
-          const int blk = lane_o >> 5, row = lane_o & 15, half = (lane_o >> 4) & 1;
-          *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
-          *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+      if constexpr (!kSSD) {   // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
+        const int blk = lane_o >> 5, row = lane_o & 15, half = (lane_o >> 4) & 1;
+        *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+      }
+      // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
+      const int i = lane_o;
+      const float bt = i < n ? sBr[PQ][i] : 0.f;
+      const float G = wave_inclusive_scan(i < n ? sGr[PQ][i] : 0.f);
+      const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
+      const float G31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 31));
+      float rq = i < n ? 1.f : 0.f, rk = rq;
+      if constexpr (!kSSD) {   // 1 / |row| of q_i and k_i (zero past the end)
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int s = 0; s < DK / 8; ++s) {
+          sq = sumsq8(ld8<DK>(Q, i, 8 * s), sq);
+          sk = sumsq8(ld8<DK>(K, i, 8 * s), sk);
         }
-        wait_count(3 * pgen);
+        rq = i < n ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;   // 1 ulp
+        rk = i < n ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
+      }
+      const float gam = __expf(G);
+      sCR[PQ][i] = bt * gam * rk;                  // R = beta V - CR X
+      sCO[PQ][i] = p.scale * gam * rq;             // O = CO (Q S0^T) + P U
+      sCS[PQ][i] = __expf(GC - G) * rk;            // S1 = gamma_C S0 + K^T diag(CS) U
+      sBeta[PQ][i] = bt;
+      if (i == 0) sGC[PQ][0] = __expf(GC);
+      const float rowP = p.scale * rq, rowA = bt * rk;
+      // diagonal tiles: P_im = rowP_i 2^(EG_i - EB_m) (Q K^T)_im, A likewise with rowA_i
+      sEG[i] = G * kLog2e;
+      sEB[i] = G * kLog2e - __builtin_amdgcn_logf(rk);   // (r_k = 0: +inf, the key drops out)
+      sERp[i] = rowP;
+      sERa[i] = rowA;
+      // off-diagonal tile: exp(G_i - G_m) = exp(G_i - G_31) exp(G_31 - G_m)
+      const float F = __expf(i < 32 ? G31 - G : G - G31);
+      sEF[i] = (i < 32 ? rk : rowP) * F;
+      sEFa[i] = rowA * F;
+      arrive(&sSync[0]);
+      if constexpr (!kSSD) {
+        wait_count(&sSync[2], pgen);
         // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
         f32x16 y = {};
 #pragma unroll
@@ -661,102 +690,84 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       return;
     }
 
-    // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
-    float Gi = lane_o < n ? sGr[PQ][lane_o] : 0.f;
-    const float bt = lane_o < n ? sBr[PQ][lane_o] : 0.f;
-    Gi = wave_inclusive_scan(Gi);
-    const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gi), C - 1));
-    pG[lane_o] = Gi;
-    pB[lane_o] = bt;
-
-    const int ti = pr == 2 ? 1 : pr, tj = pr == 2 ? 0 : pr;
-    f32x16 qk, kk;
-    float sqA, sqQ, sqK;
-    tile_mma(Q, K, ti, tj, l32, hh, qk, kk, sqA, sqQ, sqK);
-    const float rkA = inv_norm(sqA, 32 * tj + l32, n);   // keys' rows
-    const float rq = inv_norm(sqQ, 32 * ti + l32, n);    // query rows
-    const float rk = inv_norm(sqK, 32 * ti + l32, n);    // query rows' keys
-    if (hh == 0) {
-      pRk[32 * tj + l32] = rkA;
-      pRk[32 * ti + l32] = rk;
-      pRq[32 * ti + l32] = rq;
-    }
-    lds_order();
-    {   // scale: P (hi + lo) and A (bf16, and fp32 diagonal 16x16 blocks)
+    // P (hi + lo) and A (bf16, and the fp32 diagonal 16x16 blocks) of tile (ti, tj)
+    auto emit = [&](auto kdiag) {
+      constexpr bool kDiag = decltype(kdiag)::value;
+      const int ti = kDiag ? pr : 1, tj = kDiag ? pr : 0;
+      f32x16 qk, kk;
+      tile_mma(Q, K, ti, tj, l32, hh, qk, kk);
+      wait_count(&sSync[0], pgen);
       const int i = 32 * ti + l32;                                // this lane's row
-      const float Gi_ = pG[i];
-      const float rowP = p.scale * pRq[i];
-      const float rowA = pB[i] * pRk[i];
+      const float gi = kDiag ? sEG[i] : 0.f;
+      const float rowP = kDiag ? sERp[i] : sEF[i];
+      const float rowA = kDiag ? sERa[i] : sEFa[i];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
-        const float4 Gm = ld_f4(&pG[mb]), rkm = ld_f4(&pRk[mb]);
+        const float4 km = ld_f4(kDiag ? &sEB[mb] : &sEF[mb]);
         float pv[4], av[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e, m = mb + e;
-          const float t = m <= i ? __expf(Gi_ - f4get(Gm, e)) * f4get(rkm, e) : 0.f;   // masked before the exp
-          pv[e] = rowP * t * qk[r];
-          av[e] = m < i ? rowA * t * kk[r] : 0.f;
+          const int r = 4 * q4 + e;
+          // decay and key norm of (i, m): diagonal tiles take one exp per element,
+          // masked before the exp; the off-diagonal tile has them factored
+          const float f = kDiag ? __builtin_amdgcn_exp2f(mb + e <= i ? gi - f4get(km, e) : -INFINITY) : f4get(km, e);
+          pv[e] = (rowP * f) * qk[r];
+          av[e] = (rowA * f) * kk[r];
         }
         const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
-        const uint32_t l0 = cvt2(pv[0] - bf_lo(h0), pv[1] - bf_hi(h0));
-        const uint32_t l1 = cvt2(pv[2] - bf_lo(h1), pv[3] - bf_hi(h1));
+        const uint32_t l0 = cvt2(sub_bf_lo(h0, pv[0]), sub_bf_hi(h0, pv[1]));
+        const uint32_t l1 = cvt2(sub_bf_lo(h1, pv[2]), sub_bf_hi(h1, pv[3]));
         *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
         *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
-        if constexpr (!kSSD) {
+        if constexpr (!kSSD) {   // (entries on and above the diagonal are never read)
           *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
-          if ((i >> 4) == (mb >> 4))
-            *reinterpret_cast<float4*>(&sAd[i >> 4][i & 15][mb & 15]) = make_float4(av[0], av[1], av[2], av[3]);
+          if (kDiag && (i >> 4) == (mb >> 4))
+            *reinterpret_cast<float4*>(&sAd[i >> 4][20 * (i & 15) + (mb & 15)]) = make_float4(av[0], av[1], av[2], av[3]);
         }
       }
+    };
+    const bool diag = pr < 2;
+    if (diag) emit(std::true_type{});
+    else emit(std::false_type{});
+    if constexpr (!kSSD) {
+      if (diag) {
+        arrive(&sSync[1]);
+        return;
+      }
+      wait_count(&sSync[1], 2 * pgen);
+      {   // diagonal 16x16 blocks of T in fp32: lane 16 b + c solves column c of block b
+        const int b = g16, c = j16;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][20 * mm + i] * x[i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
+      }
+      lds_order();
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t: T[16..31][0..15] = -D1 (A10 D0)
+        const int r0 = 32 * t;
+        // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
+        bf16x4 bD;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[PQ][r0 + 4 * g16 + e][kperm(r0 + j16)]);
+        f32x4 y = {};
+        y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
+        bf16x4 yb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+        f32x4 zz = {};
+        zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[PQ][r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sTb[PQ][r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
+      }
+      arrive(&sSync[2]);
     }
-    if (pr < 2) {
-      const int t = pr;
-      if (hh == 0) {   // coefficient vectors of tokens 32 t .. 32 t + 31
-        const int i = 32 * t + l32;
-        const float Gt = pG[i], bt_i = pB[i];
-        const float gam = __expf(Gt);
-        sCR[PQ][i] = bt_i * gam * rk;                // R = beta V - CR X
-        sCO[PQ][i] = p.scale * gam * rq;             // O = CO (Q S0^T) + P U
-        sCS[PQ][i] = __expf(GC - Gt) * rk;           // S1 = gamma_C S0 + K^T diag(CS) U
-        sBeta[PQ][i] = bt_i;
-      }
-      if (t == 0 && lane_o == 0) sGC[PQ][0] = __expf(GC);
-      if constexpr (!kSSD) {
-        lds_order();
-        if (hh == 0) {   // diagonal 16x16 blocks 2t, 2t + 1: lane 16 b' + c solves column c in fp32
-          const int b = 2 * t + (l32 >> 4), c = l32 & 15;
-          float x[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][mm][i] * x[i];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
-        }
-        lds_order();
-        {   // 16 -> 32 inside diagonal tile t: T[16..31][0..15] = -D1 (A10 D0)
-          const int r0 = 32 * t;
-          // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
-          bf16x4 bD;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[PQ][r0 + 4 * g16 + e][kperm(r0 + j16)]);
-          f32x4 y = {};
-          y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
-          bf16x4 yb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
-          f32x4 zz = {};
-          zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[PQ][r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sTb[PQ][r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
-        }
-      }
-    }
-    if constexpr (!kSSD) arrive();
   };
 
   // ================================================================ step loop
@@ -801,7 +812,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   };
 
   if (nch > 0) stage_qk(0);
-  if (tid == 0) sSync = 0u;   // visible to all after the first barrier
+  if (tid < 4) sSync[tid] = 0u;   // visible to all after the first barrier
   // entry state and first staged loads retired on every path here, so no wait inside
   // the loop has to cover them
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
