@@ -28,10 +28,11 @@
 //    reduction index of an MFMA may be permuted freely when both operands agree, so
 //    A operands are read from LDS in the accumulator's row order).  In the step for
 //    chunk c they compute X, Y, R, U, O and the new state: only the state-dependent
-//    part, with no barrier inside.
-//  * four producer waves prepare chunk c + 1 meanwhile: decay cumsum, row norms,
-//    Q K^T and K K^T tiles -> P (hi + lo) and A, the inversion T = (I + A)^{-1}, and
-//    the per-token coefficient vectors.
+//    part, with no barrier inside (they wait once, for T of chunk c).
+//  * four producer waves run meanwhile: three prepare chunk c + 1 (decay cumsum,
+//    row norms and the per-token coefficient vectors; Q K^T and K K^T tiles -> P
+//    (hi + lo) and A), the fourth turns chunk c's A into T = (I + A)^{-1} in place,
+//    early in the step, before the state waves need it.
 // The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
 // step ahead.
 // Each step has two workgroup barriers: one ends the previous step, the second ends
@@ -264,13 +265,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
   // producer working set (per producer wave where private)
-  __shared__ __attribute__((aligned(16))) u16 sAB[kSSD ? 1 : C][kPS];
-  // fp32 diagonal 16x16 blocks of A, rows of 20 floats; the block stride of 336
-  // floats puts the four blocks on different banks (the solve reads all four at once)
-  __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 4][16 * 20 + 16];
+  // fp32 diagonal 16x16 blocks of A, rows of 20 floats, double-buffered; the block
+  // stride of 336 floats puts the four blocks on different banks (the solve reads all
+  // four at once)
+  __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 2][4][16 * 20 + 16];
   // vectors of the chunk being prepared, per token (see the producer roles)
   __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
-  __shared__ uint32_t sSync[4];   // producer arrival counters: vectors, diagonal tiles, T's diagonal half
+  __shared__ uint32_t sSync[4];   // arrival counters: chunk vectors ready, T ready
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
@@ -366,6 +367,22 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
   };
 
+  // Hand-off between waves inside a step: arrival counters in LDS.  A wave's LDS
+  // writes are performed before its later increment (the LDS executes one wave's
+  // accesses in order); the waiting wave reads the data only after seeing the count.
+  // Waits are bounded: every counted arrival happens unconditionally.
+  auto arrive = [&](uint32_t* ctr) {
+    lds_order();
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto wait_count = [&](uint32_t* ctr, uint32_t target) {
+    for (int it = 0; it < (1 << 22); ++it) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_order();
+  };
+
   // State-dependent part of chunk c (buffers of parity PAR).  A operands (rows of Q,
   // K, T, P and K^T) are read once and shared by the wave's CT column tiles.
   auto consume = [&](int c, auto parc) {
@@ -441,6 +458,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       }
     }
     if constexpr (!kSSD) {
+      wait_count(&sSync[1], (uint32_t)(c + 1));   // T of chunk c (finished in this step)
       // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
       bf16x8 Rb[CT][2];
 #pragma unroll
@@ -584,50 +602,69 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
     }
   };
-  // Hand-off between producer waves: arrival counters in LDS.  A wave's LDS writes
-  // are performed before its later increment (the LDS executes one wave's accesses
-  // in order); the waiting wave reads the data only after seeing the count.  Waits
-  // are bounded: every producer arrives unconditionally in every step.
-  auto arrive = [&](uint32_t* ctr) {
-    lds_order();
-    if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  };
-  auto wait_count = [&](uint32_t* ctr, uint32_t target) {
-    for (int it = 0; it < (1 << 22); ++it) {
-      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    lds_order();
-  };
-  uint32_t pgen = 0;                          // producer steps so far (uniform)
+  uint32_t pgen = 0;                          // chunks prepared so far (uniform)
   constexpr float kLog2e = 1.4426950408889634f;
 
-  // Prepare chunk cp into the buffers of parity PQ.  Producer roles (pr = wave - NSW):
-  //   pr 3:    the chunk's vectors (lane = token): decay cumsum, row norms, the
-  //            coefficient vectors and the decay factors of the P / A tiles; then T's
-  //            zero blocks and, once T's diagonal half is done, T[32..63][0..31];
-  //   pr 0, 1: diagonal tile t = pr of P and A (one exp per element);
-  //   pr 2:    the off-diagonal tile (rows 32..63, keys 0..31), whose decay factors
-  //            into a row and a key factor split at token 31 (both <= 1); then T's four
-  //            diagonal 16x16 blocks and the two 16 -> 32 merges.
+  // Prepare chunk cp (buffers of parity PQ): its vectors, P (hi + lo), and A stored in
+  // T's buffer (bf16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
+  // (pr = wave - NSW):
+  //   pr 3:    the off-diagonal tile's products, then the chunk's vectors (lane =
+  //            token): decay cumsum, row norms, the coefficient vectors and the decay
+  //            factors of the tiles; then the off-diagonal tile (rows 32..63, keys
+  //            0..31), whose decay factors into a row and a key factor split at token
+  //            31 (both <= 1);
+  //   pr 0, 1: diagonal tile t = pr (one exp per element).
+  // Entries of A on and above the diagonal are not needed; those inside the diagonal
+  // 32x32 tiles come out as zeros or are overwritten by T's diagonal blocks.
   auto produce = [&](int cp, auto parq) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
     const int l32 = lane_o & 31, hh = lane_o >> 5;
-    const int g16 = lane_o >> 4, j16 = lane_o & 15;
     const int pr = wu - NSW;
     const u16* Q = sQ[PQ];
     const u16* K = sK[PQ];
     ++pgen;
 
-    if (pr == 3) {
-      if constexpr (!kSSD) {   // upper 16x16 blocks inside the diagonal 32x32 tiles of T are zero
-        const int blk = lane_o >> 5, row = lane_o & 15, half = (lane_o >> 4) & 1;
-        *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(16 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(&sTb[PQ][32 * blk + row][kperm(20 + 32 * blk + 8 * half)]) = make_uint2(0, 0);
+    // P (hi + lo) and A of tile (ti, tj) from its products
+    auto emit = [&](auto kdiag, const f32x16& qk, const f32x16& kk) {
+      constexpr bool kDiag = decltype(kdiag)::value;
+      const int ti = kDiag ? pr : 1, tj = kDiag ? pr : 0;
+      const int i = 32 * ti + l32;                                // this lane's row
+      const float gi = kDiag ? sEG[i] : 0.f;
+      const float rowP = kDiag ? sERp[i] : sEF[i];
+      const float rowA = kDiag ? sERa[i] : sEFa[i];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
+        const float4 km = ld_f4(kDiag ? &sEB[mb] : &sEF[mb]);
+        float pv[4], av[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          // decay and key norm of (i, m): diagonal tiles take one exp per element,
+          // masked before the exp; the off-diagonal tile has them factored
+          const float f = kDiag ? __builtin_amdgcn_exp2f(mb + e <= i ? gi - f4get(km, e) : -INFINITY) : f4get(km, e);
+          pv[e] = (rowP * f) * qk[r];
+          av[e] = (rowA * f) * kk[r];
+        }
+        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
+        const uint32_t l0 = cvt2(sub_bf_lo(h0, pv[0]), sub_bf_hi(h0, pv[1]));
+        const uint32_t l1 = cvt2(sub_bf_lo(h1, pv[2]), sub_bf_hi(h1, pv[3]));
+        *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
+        if constexpr (!kSSD) {
+          *reinterpret_cast<uint2*>(&sTb[PQ][i][kperm(mb)]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
+          if (kDiag && (i >> 4) == (mb >> 4))
+            *reinterpret_cast<float4*>(&sAd[PQ][i >> 4][20 * (i & 15) + (mb & 15)]) = make_float4(av[0], av[1], av[2], av[3]);
+        }
       }
+    };
+
+    f32x16 qk, kk;
+    if (pr == 3) {
+      tile_mma(Q, K, 1, 0, l32, hh, qk, kk);   // (runs on the matrix cores while the vectors are computed)
       // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
       const int i = lane_o;
       const float bt = i < n ? sBr[PQ][i] : 0.f;
@@ -662,112 +699,81 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sEF[i] = (i < 32 ? rk : rowP) * F;
       sEFa[i] = rowA * F;
       arrive(&sSync[0]);
-      if constexpr (!kSSD) {
-        wait_count(&sSync[2], pgen);
-        // 32 -> 64: T[32..63][0..31] = -T22 (A21 T11)
-        f32x16 y = {};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
-          bf16x8 bT;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, sTb[PQ][16 * s + 8 * hh + e][kperm(l32)]);
-          const bf16x8 a = join(*reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh]),
-                                *reinterpret_cast<const uint2*>(&sAB[32 + l32][16 * s + 8 * hh + 4]));
-          y = mfma32(a, bT, y);
-        }
-        f32x16 zz = {};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u16* trow = &sTb[PQ][32 + l32][0];
-          const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
-          zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
-                           *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sTb[PQ][32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
-      }
-      return;
-    }
-
-    // P (hi + lo) and A (bf16, and the fp32 diagonal 16x16 blocks) of tile (ti, tj)
-    auto emit = [&](auto kdiag) {
-      constexpr bool kDiag = decltype(kdiag)::value;
-      const int ti = kDiag ? pr : 1, tj = kDiag ? pr : 0;
-      f32x16 qk, kk;
-      tile_mma(Q, K, ti, tj, l32, hh, qk, kk);
+      emit(std::false_type{}, qk, kk);
+    } else {
+      tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
       wait_count(&sSync[0], pgen);
-      const int i = 32 * ti + l32;                                // this lane's row
-      const float gi = kDiag ? sEG[i] : 0.f;
-      const float rowP = kDiag ? sERp[i] : sEF[i];
-      const float rowA = kDiag ? sERa[i] : sEFa[i];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
-        const float4 km = ld_f4(kDiag ? &sEB[mb] : &sEF[mb]);
-        float pv[4], av[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          // decay and key norm of (i, m): diagonal tiles take one exp per element,
-          // masked before the exp; the off-diagonal tile has them factored
-          const float f = kDiag ? __builtin_amdgcn_exp2f(mb + e <= i ? gi - f4get(km, e) : -INFINITY) : f4get(km, e);
-          pv[e] = (rowP * f) * qk[r];
-          av[e] = (rowA * f) * kk[r];
-        }
-        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
-        const uint32_t l0 = cvt2(sub_bf_lo(h0, pv[0]), sub_bf_hi(h0, pv[1]));
-        const uint32_t l1 = cvt2(sub_bf_lo(h1, pv[2]), sub_bf_hi(h1, pv[3]));
-        *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
-        if constexpr (!kSSD) {   // (entries on and above the diagonal are never read)
-          *reinterpret_cast<uint2*>(&sAB[i][mb]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
-          if (kDiag && (i >> 4) == (mb >> 4))
-            *reinterpret_cast<float4*>(&sAd[i >> 4][20 * (i & 15) + (mb & 15)]) = make_float4(av[0], av[1], av[2], av[3]);
-        }
-      }
-    };
-    const bool diag = pr < 2;
-    if (diag) emit(std::true_type{});
-    else emit(std::false_type{});
-    if constexpr (!kSSD) {
-      if (diag) {
-        arrive(&sSync[1]);
-        return;
-      }
-      wait_count(&sSync[1], 2 * pgen);
-      {   // diagonal 16x16 blocks of T in fp32: lane 16 b + c solves column c of block b
-        const int b = g16, c = j16;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-          for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[b][20 * mm + i] * x[i];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
-      }
-      lds_order();
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t: T[16..31][0..15] = -D1 (A10 D0)
-        const int r0 = 32 * t;
-        // B operand: column r0 + j16 of D0, rows r0 + 4 g16 + e
-        bf16x4 bD;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, sTb[PQ][r0 + 4 * g16 + e][kperm(r0 + j16)]);
-        f32x4 y = {};
-        y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sAB[r0 + 16 + j16][r0 + 4 * g16])), bD, y);
-        bf16x4 yb;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
-        f32x4 zz = {};
-        zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&sTb[PQ][r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sTb[PQ][r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
-      }
-      arrive(&sSync[2]);
+      emit(std::true_type{}, qk, kk);
     }
+  };
+
+  // T = (I + A)^{-1} of chunk c in place of A (buffers of parity PAR), one wave:
+  // the four diagonal 16x16 blocks in fp32 (lane 16 b + c solves column c of block
+  // b), the two 16 -> 32 merges T10 = -T11 A10 T00 and the 32 -> 64 merge
+  // T[32..63][0..31] = -T22 A21 T11.  Each merge reads its A block before it writes
+  // the T block in its place.
+  auto finish_T = [&](auto parc) {
+    constexpr int PAR = decltype(parc)::value;
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int l32 = lane_o & 31, hh = lane_o >> 5;
+    const int g16 = lane_o >> 4, j16 = lane_o & 15;
+    auto T = sTb[PAR];
+    {
+      const int b = g16, c = j16;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[PAR][b][20 * mm + i] * x[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) T[16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
+    }
+    lds_order();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t
+      const int r0 = 32 * t;
+      // B operand: column r0 + j16 of T00, rows r0 + 4 g16 + e
+      bf16x4 bD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, T[r0 + 4 * g16 + e][kperm(r0 + j16)]);
+      f32x4 y = {};
+      y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 4 * g16)])), bD, y);
+      bf16x4 yb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+      f32x4 zz = {};
+      zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
+    }
+    lds_order();
+    {   // 32 -> 64
+      f32x16 y = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
+        bf16x8 bT;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, T[16 * s + 8 * hh + e][kperm(l32)]);
+        const bf16x8 a = join(*reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh)]),
+                              *reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh + 4)]));
+        y = mfma32(a, bT, y);
+      }
+      f32x16 zz = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u16* trow = &T[32 + l32][0];
+        const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
+        zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
+                         *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T[32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
+    }
+    arrive(&sSync[1]);
   };
 
   // ================================================================ step loop
@@ -801,7 +807,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
     lds_sync();                                    // landing done
     if (isP) {
-      if (hasP) produce(c + 1, Par<PQ>{});
+      if (wu - NSW == 2) {   // T of chunk c (delta rule only)
+        if constexpr (!kSSD) {
+          if (hasS) finish_T(Par<PAR>{});
+        }
+      } else if (hasP) {
+        produce(c + 1, Par<PQ>{});
+      }
     } else {
       if (hasS) consume(c, Par<PAR>{});
       else {   // step -1: no chunk to consume, stage chunk 1's rows here
