@@ -89,10 +89,21 @@ __device__ __forceinline__ int kperm(int c) {
   const int q = (c >> 2) & 7;
   return (c & ~31) | ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
 }
+// Q and K tiles: rows of D bf16 without padding; the 16-byte chunk j of row r is
+// stored at chunk position j ^ qswz(r).  This keeps the state waves' operand reads
+// (16 rows x 4 chunks per instruction) and their transpose reads free of LDS bank
+// conflicts (the producers' 32-row reads see two-way conflicts).
+__device__ __forceinline__ int qswz(int r) { return (((r & 3) << 2) ^ r) & 15; }
+template <int D>
+__device__ __forceinline__ int qidx(int r, int c) { return r * D + ((((c >> 3) ^ qswz(r)) << 3) | (c & 7)); }
 // 8 consecutive bf16 (16 B), c % 8 == 0.
 template <int D>
 __device__ __forceinline__ bf16x8 ld8(const u16* t, int r, int c) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(t + pidx<D>(r, c)));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 ldq8(const u16* t, int r, int c) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(t + qidx<D>(r, c)));
 }
 // 8 consecutive bf16 at an 8-byte aligned address (rows of the C x C tiles)
 __device__ __forceinline__ bf16x8 ld8u(const u16* p) {
@@ -103,6 +114,10 @@ __device__ __forceinline__ bf16x8 ld8u(const u16* p) {
 template <int D>
 __device__ __forceinline__ uint2 ldtr(const u16* t, int r, int c) {
   return tr_read(t + pidx<D>(r, c));
+}
+template <int D>
+__device__ __forceinline__ uint2 ldqtr(const u16* t, int r, int c) {
+  return tr_read(t + qidx<D>(r, c));
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
@@ -207,8 +222,8 @@ struct TileRegs {
   __device__ __forceinline__ static void st(u16* tile, int si, int i, uint4 v) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     if constexpr (kPerm) {   // the two 4-column halves land in separate groups
-      *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c)) = make_uint2(v.x, v.y);
-      *reinterpret_cast<uint2*>(tile + r * (D + 8) + kperm(8 * c + 4)) = make_uint2(v.z, v.w);
+      *reinterpret_cast<uint2*>(tile + qidx<D>(r, kperm(8 * c))) = make_uint2(v.x, v.y);
+      *reinterpret_cast<uint2*>(tile + qidx<D>(r, kperm(8 * c + 4))) = make_uint2(v.z, v.w);
     } else {
       *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
     }
@@ -221,7 +236,7 @@ struct TileRegs {
       s3 = ld(g, gs, t0, n, si, 3);
     }
   }
-  template <bool kPerm>   // Q and K tiles: permuted column groups
+  template <bool kPerm>   // Q and K tiles: permuted column groups, swizzled chunks
   __device__ __forceinline__ void store(u16* tile, int si) const {
     st<kPerm>(tile, si, 0, s0);
     if constexpr (N >= 2) st<kPerm>(tile, si, 1, s1);
@@ -257,7 +272,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
-  __shared__ __attribute__((aligned(16))) u16 sQ[2][C * (DK + 8)], sK[2][C * (DK + 8)];
+  __shared__ __attribute__((aligned(16))) u16 sQ[2][C * DK], sK[2][C * DK];
   __shared__ __attribute__((aligned(16))) u16 sV[C * (DV + 8)], sZ[kSSD ? C * (DV + 8) : 8];
   // producer outputs for the state waves, double-buffered
   __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS], sPl[2][C][kPS];
@@ -306,9 +321,6 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     return reinterpret_cast<char*>(p.out) + ((int64_t)t0 * p.out_stride + (int64_t)h * DV + CW * wu) * (int64_t)sizeof(OutT);
   };
   const uint32_t ostride_b = (uint32_t)p.out_stride * (uint32_t)sizeof(OutT);
-  auto out_off = [&](int i, int jj) {   // byte offset of row i of the chunk, column jj of the wave's
-    return (uint32_t)i * ostride_b + (uint32_t)jj * (uint32_t)sizeof(OutT);
-  };
 
   // S^T tiles in 16x16 accumulator layout: Sacc[ct][tk][r] = S[col_ct][16 tk + 4 g16 + r]
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
@@ -419,11 +431,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         const int row = 16 * rt + j16;
 #pragma unroll
         for (int s2 = 0; s2 < NKS; ++s2) {
-          const bf16x8 aq = ld8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
+          const bf16x8 aq = ldq8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632(Sb[ct][s2], aq, Y[ct][rt]);   // (Q S0^T)^T
           if constexpr (!kSSD) {
-            const bf16x8 ak = ld8<DK>(K, row, 32 * s2 + 8 * g16);
+            const bf16x8 ak = ldq8<DK>(K, row, 32 * s2 + 8 * g16);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632(ak, Sb[ct][s2], U[ct][rt]);   // X = K S0^T
           }
@@ -537,22 +549,31 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
     }
     {
+      // row j16 + 16 rt, columns 16 ct + 4 g16 ..: a lane offset plus uniform row-tile
+      // steps (the column tiles are instruction offsets)
       char* base = out_base(t0);
+      const uint32_t o0 = (uint32_t)j16 * ostride_b + (uint32_t)(4 * g16 * sizeof(OutT));
+      auto store = [&](int ct, int rt) {
+        char* a = base + (o0 + (uint32_t)rt * (16u * ostride_b)) + 16 * ct * (int)sizeof(OutT);
+        if constexpr (sizeof(OutT) == 2)
+          *reinterpret_cast<uint2*>(a) = make_uint2(cvt2(Y[ct][rt][0], Y[ct][rt][1]), cvt2(Y[ct][rt][2], Y[ct][rt][3]));
+        else
+          *reinterpret_cast<float4*>(a) = make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
+      };
+      if (n == C) {   // whole chunk: no per-row guard
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int i = 16 * rt + j16;
-          if (i < n) {
-            if constexpr (sizeof(OutT) == 2)
-              *reinterpret_cast<uint2*>(base + out_off(i, 16 * ct + 4 * g16)) =
-                  make_uint2(cvt2(Y[ct][rt][0], Y[ct][rt][1]), cvt2(Y[ct][rt][2], Y[ct][rt][3]));
-            else
-              *reinterpret_cast<float4*>(base + out_off(i, 16 * ct + 4 * g16)) =
-                  make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
-          }
-        }
+          for (int rt = 0; rt < 4; ++rt) store(ct, rt);
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            if (16 * rt + j16 < n) store(ct, rt);
+      }
     }
+
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
     {
 #pragma unroll
@@ -577,7 +598,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         const int ca = kperm(16 * tk + 4 * (j16 & 3));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 kt = join(ldtr<DK>(K, 32 * s2 + rb, ca), ldtr<DK>(K, 32 * s2 + 16 + rb, ca));
+          const bf16x8 kt = join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca));
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             Sacc[ct][tk] = mfma1632(kt, Wh[ct][s2], Sacc[ct][tk]);
@@ -597,9 +618,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     kk = f32x16{};
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
-      const bf16x8 a = ld8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
-      qk = mfma32(a, ld8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
-      if constexpr (!kSSD) kk = mfma32(a, ld8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
+      const bf16x8 a = ldq8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
+      qk = mfma32(a, ldq8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
+      if constexpr (!kSSD) kk = mfma32(a, ldq8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
     }
   };
   uint32_t pgen = 0;                          // chunks prepared so far (uniform)
@@ -676,8 +697,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int s = 0; s < DK / 8; ++s) {
-          sq = sumsq8(ld8<DK>(Q, i, 8 * s), sq);
-          sk = sumsq8(ld8<DK>(K, i, 8 * s), sk);
+          sq = sumsq8(ldq8<DK>(Q, i, 8 * s), sq);
+          sk = sumsq8(ldq8<DK>(K, i, 8 * s), sk);
         }
         rq = i < n ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;   // 1 ulp
         rk = i < n ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
