@@ -88,7 +88,7 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
     os.makedirs(PROFILES, exist_ok=True)
     stats = _csv_rows(kt_dir, "*kernel_stats.csv")
     lines = ["# rocprofv3 kernel-trace statistics of the bench command",
-             f"# command: cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             f"# command (repository root): export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o bench -- {PROF_CMD}",
              f"# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
              f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}",
@@ -120,8 +120,8 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
     cf, cw = pick_copy(fetch), pick_copy(write)
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
     out = ["# HBM traffic per dispatch from rocprofv3 counters (KiB), scaled by the copy calibration",
-           f"# command (fetch): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
-           f"# command (write): cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
+           f"# command (fetch, repository root): export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
+           f"# command (write, repository root): export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
            "# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
            f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
            f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]
