@@ -138,21 +138,10 @@ __device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-// x - (low / high bf16 of the packed pair w) in one v_dot2_f32_bf16 against the pair
-// (-1, 0) / (0, -1): the products are exact and the difference of a float and its
-// bf16 rounding is representable, so the result is exact.  The constant pair is
-// passed in a scalar register: as an inline constant the compiler would encode
-// (-1, 0) as "-1.0", which the hardware does not read as that bf16 pair.
-__device__ __forceinline__ bf16x2 sreg_pair(uint32_t v) {
-  asm("" : "+s"(v));
-  return __builtin_bit_cast(bf16x2, v);
-}
-__device__ __forceinline__ float sub_bf_lo(uint32_t w, float x) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), sreg_pair(0x0000BF80u), x, false);
-}
-__device__ __forceinline__ float sub_bf_hi(uint32_t w, float x) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), sreg_pair(0xBF800000u), x, false);
-}
+// x minus the low / high bf16 of the packed pair w (exact: a float minus its own
+// bf16 rounding is representable)
+__device__ __forceinline__ float sub_bf_lo(uint32_t w, float x) { return x - bf_lo(w); }
+__device__ __forceinline__ float sub_bf_hi(uint32_t w, float x) { return x - bf_hi(w); }
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), for the pair layout above
 __device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
