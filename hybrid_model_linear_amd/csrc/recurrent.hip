@@ -13,7 +13,10 @@
 // Memory layout: the state row r of (slot, head) is 4*d_k contiguous bytes of the
 // pool [slot][head][d_v][d_k]; d_k/4 lanes own one row, each a float4 of it, so a
 // wave streams 64 * 16 B = 1 KiB per instruction, fully coalesced.  The state stays
-// in registers across the tokens of a sequence and is written back once.
+// in registers across the tokens of a sequence and is written back once.  Its loads
+// are non-temporal (each byte of the pool is read once per launch); the stores keep
+// the default policy (measured faster for an extend + decode step than streaming
+// them past the caches).
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -68,12 +71,17 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   const int j = h / (p.H_v / p.H_qk);          // qk-head of this v-head
 
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
+  typedef float nf4 __attribute__((ext_vector_type(4)));   // (the nontemporal builtin takes native vectors)
   float4 st[kRowSteps];
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int row = row0 + s * L::kRowsPerStep;
-    st[s] = init ? *reinterpret_cast<const float4*>(state + (int64_t)row * DK + 4 * c)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init) {
+      const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(state + (int64_t)row * DK + 4 * c));
+      st[s] = make_float4(v.x, v.y, v.z, v.w);
+    } else {
+      st[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 
   const InT* qb = reinterpret_cast<const InT*>(p.q);
