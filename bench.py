@@ -3,10 +3,12 @@
 
 One step = one pass of the whole GDN hot path on Qwen3-Next-shaped synthetic inputs
 (H_qk = 16, H_v = 32, d_k = d_v = 128, bf16 inputs, fp32 state pool):
-  prefill : gdn_gate + gdn_extend over 8 sequences x 4096 tokens (packed varlen,
-            zero initial states, final states into 8 slots of a 16-slot pool)
-  decode  : gdn_gate + gdn_decode for 256 sequences x 1 token, in place on a
+  prefill : gdn_extend_gated over 8 sequences x 4096 tokens (packed varlen, zero
+            initial states, final states into 8 slots of a 16-slot pool)
+  decode  : gdn_decode_gated for 256 sequences x 1 token, in place on a
             [1024, 32, 128, 128] fp32 pool (256 slots touched)
+Both calls take the raw gate inputs a, b (with A_log, dt_bias) and compute the decay
+and write strength inside the layer kernel (the gdn_gate arithmetic, folded in).
 value = (32768 + 256) tokens / step time, inputs resident in HBM.
 
 Prints ONE JSON line.  `roofline` covers the kernel with the largest share of the
@@ -36,11 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 # algorithmic work per token at the Qwen3-Next shape (H_qk=16, H_v=32, d=128)
 H_QK, H_V, D = 16, 32, 128
-IO_BYTES_PER_TOKEN = 2 * H_QK * D * 2 + H_V * D * 2 + H_V * D * 2 + H_V * 8   # q,k + v + out + log_g,beta
+IO_BYTES_PER_TOKEN = 2 * H_QK * D * 2 + H_V * D * 2 + H_V * D * 2 + H_V * 4   # q,k + v + out + a,b (bf16)
 STATE_BYTES = H_V * D * D * 4                                                   # one slot, all heads
 CHUNK = 64
 EXTEND_FLOP_PER_TOKEN = H_QK * 4 * CHUNK * D + H_V * 2 * (CHUNK * D + 2 * CHUNK * D + 3 * D * D)
-GATE_BYTES_PER_TOKEN = H_V * (2 + 2 + 4 + 4)                                    # a, b -> log_g, beta
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_traffic.txt")
@@ -227,8 +228,6 @@ def main():
         return dict(q=q, k=k, v=v, a=case.a, b=case.b, A_log=t(case.A_log, torch.float32),
                     dt_bias=t(case.dt_bias, torch.float32), cu=t(case.cu_seqlens, torch.int32),
                     slot=t(case.slot, torch.int32), has_init=t(case.has_init, torch.int32),
-                    log_g=torch.empty((case.T, case.H_v), dtype=torch.float32, device=dev),
-                    beta=torch.empty((case.T, case.H_v), dtype=torch.float32, device=dev),
                     out=torch.empty((case.T, case.H_v, case.d_v), dtype=torch.bfloat16, device=dev))
     E, Dd = prep(ext), prep(dec)
     T_e, T_d = ext.T, dec.T
@@ -243,30 +242,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    names = ["gate_extend", "extend", "gate_decode", "decode"]
+    names = ["extend", "decode"]
+    gate_e = gdn.gdn_gate_inputs(E["a"], E["b"], E["A_log"], E["dt_bias"])
+    gate_d = gdn.gdn_gate_inputs(Dd["a"], Dd["b"], Dd["A_log"], Dd["dt_bias"])
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        gdn.gate(E["a"], E["b"], E["A_log"], E["dt_bias"], log_g=E["log_g"], beta=E["beta"])
+        gdn.extend(E["q"], E["k"], E["v"], None, None, E["cu"], E["slot"], pool_e,
+                   has_init=E["has_init"], scale=ext.scale, out=E["out"], max_seqlen=maxlen,
+                   gate=gate_e)
         mark(1)
-        gdn.extend(E["q"], E["k"], E["v"], E["log_g"], E["beta"], E["cu"], E["slot"], pool_e,
-                   has_init=E["has_init"], scale=ext.scale, out=E["out"], max_seqlen=maxlen)
+        gdn.decode(Dd["q"], Dd["k"], Dd["v"], None, None, Dd["slot"], pool_d,
+                   scale=dec.scale, out=Dd["out"], gate=gate_d)
         mark(2)
-        gdn.gate(Dd["a"], Dd["b"], Dd["A_log"], Dd["dt_bias"], log_g=Dd["log_g"], beta=Dd["beta"])
-        mark(3)
-        gdn.decode(Dd["q"], Dd["k"], Dd["v"], Dd["log_g"], Dd["beta"], Dd["slot"], pool_d,
-                   scale=dec.scale, out=Dd["out"])
-        mark(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -281,10 +279,8 @@ def main():
 
     # ---------------- algorithmic work per launch
     work = {
-        "gate_extend": dict(bytes=T_e * GATE_BYTES_PER_TOKEN, flop=0),
         "extend": dict(bytes=T_e * IO_BYTES_PER_TOKEN + ext.N * STATE_BYTES,   # zero init: write only
                        flop=T_e * EXTEND_FLOP_PER_TOKEN),
-        "gate_decode": dict(bytes=T_d * GATE_BYTES_PER_TOKEN, flop=0),
         "decode": dict(bytes=T_d * (IO_BYTES_PER_TOKEN + 2 * STATE_BYTES), flop=T_d * 7 * H_V * D * D),
     }
     kernels = {}
@@ -320,8 +316,8 @@ def main():
                    "H_qk": H_QK, "H_v": H_V, "d_k": D, "d_v": D, "chunk": CHUNK,
                    "extend_tokens": T_e, "decode_tokens": T_d, "state": "fp32"},
         "roofline": roofline,
-        "phases": {"extend_tokens_per_s": round(T_e / ((per["gate_extend"] + per["extend"]) * 1e-3), 1),
-                   "decode_tokens_per_s": round(T_d / ((per["gate_decode"] + per["decode"]) * 1e-3), 1)},
+        "phases": {"extend_tokens_per_s": round(T_e / (per["extend"] * 1e-3), 1),
+                   "decode_tokens_per_s": round(T_d / (per["decode"] * 1e-3), 1)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

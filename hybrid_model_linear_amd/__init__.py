@@ -100,63 +100,83 @@ def split_mixed_qkv(mixed_qkv: torch.Tensor, H_qk: int, H_v: int, d_k: int, d_v:
 
 
 # ------------------------------------------------------------------ gdn_gate
+class GateInputs:
+    """Raw gate inputs of one call (tensors kept alive with their ctypes description):
+    GDN a, b [T, H] with A_log, dt_bias [H]; delta-off dt [T, H] with A, dt_bias [H] and
+    the softplus / clamp settings.  Passed as `gate=` to extend / decode to fold the
+    gate into those kernels, or used by gate() / ssd_gate() to materialise log g, beta."""
+
+    def __init__(self, mode, a, b, A, dt_bias, dt_softplus, dt_limit):
+        T, H = a.shape
+        self.dev = _on_gpu(a, b, A, dt_bias)
+        if b is not None and b.dtype != a.dtype:
+            raise ValueError("a and b must share a dtype")
+        for t, nm in ((A, "A_log" if mode == GDN_MODE_GDN else "A"), (dt_bias, "dt_bias")):
+            if t is not None and (t.dtype != torch.float32 or t.shape != (H,) or not t.is_contiguous()):
+                raise ValueError(f"{nm} must be contiguous fp32 [{H}]")
+        self.T, self.H, self.mode, self.dtype = T, H, mode, a.dtype
+        self._keep = (a, b, A, dt_bias)
+        self.args = _lib.GateArgs(
+            mode=mode, in_dtype=_dtype_code(a), T=T, H=H, a=_ptr(a),
+            a_stride=_mat_rows(a, "a" if mode == GDN_MODE_GDN else "dt", T, H),
+            b=_ptr(b), b_stride=_mat_rows(b, "b", T, H) if b is not None else 0, A=_ptr(A),
+            dt_bias=_ptr(dt_bias), dt_softplus=int(bool(dt_softplus)),
+            dt_min=float(dt_limit[0]), dt_max=float(dt_limit[1]), log_g=None, beta=None)
+
+
+def gdn_gate_inputs(a, b, A_log, dt_bias=None) -> GateInputs:
+    """GDN gate inputs: log_g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)."""
+    return GateInputs(GDN_MODE_GDN, a, b, A_log, dt_bias, 1, (0.0, math.inf))
+
+
+def ssd_gate_inputs(dt, A, dt_bias=None, dt_softplus=False, dt_limit=(0.0, math.inf)) -> GateInputs:
+    """Delta-off gate inputs: dt' = clamp(softplus?(dt + dt_bias), dt_limit); log_g = dt' A; beta = dt'."""
+    return GateInputs(GDN_MODE_SSD, dt, None, A, dt_bias, dt_softplus, dt_limit)
+
+
+def _run_gate(g: GateInputs, log_g, beta):
+    lib = _lib.load()
+    _on_gpu(log_g, beta)
+    log_g = torch.empty((g.T, g.H), dtype=torch.float32, device=g.dev) if log_g is None else log_g
+    beta = torch.empty((g.T, g.H), dtype=torch.float32, device=g.dev) if beta is None else beta
+    for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.shape != (g.T, g.H) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous fp32 [{g.T}, {g.H}]")
+    args = _lib.GateArgs.from_buffer_copy(g.args)
+    args.log_g, args.beta = _ptr(log_g), _ptr(beta)
+    _lib.check("gdn_gate", lib.gdn_gate(ct.byref(args), _stream(g.dev)))
+    return log_g, beta
+
+
 def gate(a: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor | None = None,
          *, log_g: torch.Tensor | None = None, beta: torch.Tensor | None = None):
     """GDN gate: log_g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); fp32 [T, H]."""
-    lib = _lib.load()
-    T, H = a.shape
-    dev = _on_gpu(a, b, A_log, dt_bias, log_g, beta)
-    if b.dtype != a.dtype:
-        raise ValueError("a and b must share a dtype")
-    for t, nm in ((A_log, "A_log"), (dt_bias, "dt_bias")):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (H,) or not t.is_contiguous()):
-            raise ValueError(f"{nm} must be contiguous fp32 [{H}]")
-    log_g = torch.empty((T, H), dtype=torch.float32, device=dev) if log_g is None else log_g
-    beta = torch.empty((T, H), dtype=torch.float32, device=dev) if beta is None else beta
-    for t, nm in ((log_g, "log_g"), (beta, "beta")):
-        if t.dtype != torch.float32 or t.shape != (T, H) or not t.is_contiguous():
-            raise ValueError(f"{nm} must be contiguous fp32 [{T}, {H}]")
-    args = _lib.GateArgs(mode=GDN_MODE_GDN, in_dtype=_dtype_code(a), T=T, H=H, a=_ptr(a),
-                         a_stride=_mat_rows(a, "a", T, H), b=_ptr(b),
-                         b_stride=_mat_rows(b, "b", T, H), A=_ptr(A_log), dt_bias=_ptr(dt_bias),
-                         dt_softplus=1, dt_min=0.0, dt_max=math.inf, log_g=_ptr(log_g),
-                         beta=_ptr(beta))
-    _lib.check("gdn_gate", lib.gdn_gate(ct.byref(args), _stream(dev)))
-    return log_g, beta
+    return _run_gate(gdn_gate_inputs(a, b, A_log, dt_bias), log_g, beta)
 
 
 def ssd_gate(dt: torch.Tensor, A: torch.Tensor, dt_bias: torch.Tensor | None = None,
              dt_softplus: bool = False, dt_limit=(0.0, math.inf), *,
              log_g: torch.Tensor | None = None, beta: torch.Tensor | None = None):
     """Delta-off gate: dt' = clamp(softplus?(dt + dt_bias), dt_limit); log_g = dt' A; beta = dt'."""
-    lib = _lib.load()
-    T, H = dt.shape
-    dev = _on_gpu(dt, A, dt_bias, log_g, beta)
-    for t, nm in ((A, "A"), (dt_bias, "dt_bias")):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (H,) or not t.is_contiguous()):
-            raise ValueError(f"{nm} must be contiguous fp32 [{H}]")
-    log_g = torch.empty((T, H), dtype=torch.float32, device=dev) if log_g is None else log_g
-    beta = torch.empty((T, H), dtype=torch.float32, device=dev) if beta is None else beta
-    args = _lib.GateArgs(mode=GDN_MODE_SSD, in_dtype=_dtype_code(dt), T=T, H=H, a=_ptr(dt),
-                         a_stride=_mat_rows(dt, "dt", T, H), b=None, b_stride=0, A=_ptr(A),
-                         dt_bias=_ptr(dt_bias), dt_softplus=int(bool(dt_softplus)),
-                         dt_min=float(dt_limit[0]), dt_max=float(dt_limit[1]),
-                         log_g=_ptr(log_g), beta=_ptr(beta))
-    _lib.check("gdn_gate", lib.gdn_gate(ct.byref(args), _stream(dev)))
-    return log_g, beta
+    return _run_gate(ssd_gate_inputs(dt, A, dt_bias, dt_softplus, dt_limit), log_g, beta)
 
 
 # ------------------------------------------------------------------ gdn_extend
 def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
-           out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0):
+           out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
+           gate: GateInputs | None = None):
     """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
     cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
-    (updated in place).  Returns out [T, H_v, d_v]."""
+    (updated in place).  With `gate` (GateInputs of the same mode, dtype and [T, H_v]) the
+    gate is folded into the kernel and log_g / beta are not used (pass None).
+    Returns out [T, H_v, d_v]."""
     lib = _lib.load()
     T, H_qk, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     N = cu_seqlens.shape[0] - 1
     dev = _on_gpu(q, k, v, log_g, beta, cu_seqlens, slot, pool, has_init, out, D, z)
+    if gate is not None and gate.dev != dev:
+        raise ValueError("gate inputs live on another device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     ssd = mode == "ssd"
@@ -175,6 +195,8 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
     if has_init is not None:
         _i32(has_init, "has_init", N)
     for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if gate is not None and t is None:
+            continue
         if t.dtype != torch.float32 or t.shape != (T, H_v) or not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous fp32 [{T}, {H_v}]")
     if D is not None and (D.dtype != q.dtype or not D.is_contiguous()
@@ -192,17 +214,24 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         out_stride=_rows(out, "out", H_v, d_v), scale=float(scale),
         D_per_dim=int(D is not None and D.dim() == 2), D=_ptr(D), z=_ptr(z),
         z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0)
-    _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
+    if gate is None:
+        _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
+    else:
+        _lib.check("gdn_extend_gated", lib.gdn_extend_gated(ct.byref(args), ct.byref(gate.args), _stream(dev)))
     return out
 
 
 # ------------------------------------------------------------------ gdn_decode
-def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=None):
-    """One token per sequence; pool slots are read and written in place."""
+def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=None,
+           gate: GateInputs | None = None):
+    """One token per sequence; pool slots are read and written in place.  With `gate`
+    (GDN GateInputs of [B, H_v]) the gate is folded into the kernel (log_g, beta None)."""
     lib = _lib.load()
     B, H_qk, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     dev = _on_gpu(q, k, v, log_g, beta, slot, pool, out)
+    if gate is not None and gate.dev != dev:
+        raise ValueError("gate inputs live on another device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     if pool.dtype != torch.float32 or pool.dim() != 4 or pool.shape[1:] != (H_v, d_v, d_k) \
@@ -210,6 +239,8 @@ def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=
         raise ValueError(f"pool must be contiguous fp32 [num_slots, {H_v}, {d_v}, {d_k}]")
     _i32(slot, "slot", B)
     for t, nm in ((log_g, "log_g"), (beta, "beta")):
+        if gate is not None and t is None:
+            continue
         if t.dtype != torch.float32 or t.shape != (B, H_v) or not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous fp32 [{B}, {H_v}]")
     out_dtype = q.dtype if out_dtype is None else out_dtype
@@ -223,7 +254,10 @@ def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=
         log_g=_ptr(log_g), beta=_ptr(beta), slot=_ptr(slot), pool=_ptr(pool),
         num_slots=pool.shape[0], out=_ptr(out), out_stride=_rows(out, "out", H_v, d_v),
         scale=float(scale))
-    _lib.check("gdn_decode", lib.gdn_decode(ct.byref(args), _stream(dev)))
+    if gate is None:
+        _lib.check("gdn_decode", lib.gdn_decode(ct.byref(args), _stream(dev)))
+    else:
+        _lib.check("gdn_decode_gated", lib.gdn_decode_gated(ct.byref(args), ct.byref(gate.args), _stream(dev)))
     return out
 
 
@@ -291,13 +325,18 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     T = mixed_qkv.shape[0]
     if T == 0:
         return mixed_qkv.new_empty((0, H_v * d_v))
-    log_g, beta = gate(a, b, layer.A_log, layer.dt_bias)
+    g = gdn_gate_inputs(a, b, layer.A_log, layer.dt_bias)
+    # the gate is folded into the layer kernel when a, b share q's dtype (else its own launch)
+    log_g = beta = None
+    if g.dtype != q.dtype:
+        log_g, beta = _run_gate(g, None, None)
+        g = None
     if kind == "decode":
-        o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale)
+        o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale, gate=g)
     else:
         o = extend(q, k, v, log_g, beta, forward_batch.cu_seqlens, forward_batch.state_slots, pool,
                    has_init=getattr(forward_batch, "has_initial_state", None), scale=scale,
-                   max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0))
+                   max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0), gate=g)
     return o.view(T, H_v * d_v)
 
 
@@ -329,7 +368,11 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     for t, nm in ((x, "x"), (dt, "dt"), (B, "B"), (C, "C"), (z, "z")):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
-    log_g, dtp = ssd_gate(dt.view(T, H), A, dt_bias, dt_softplus, dt_limit)
+    g = ssd_gate_inputs(dt.view(T, H), A, dt_bias, dt_softplus, dt_limit)
+    log_g = dtp = None
+    if g.dtype != x.dtype:   # folded into the extend kernel only when dt shares x's dtype
+        log_g, dtp = _run_gate(g, None, None)
+        g = None
     if initial_states is not None:
         pool = initial_states.to(torch.float32).contiguous().clone()
     else:
@@ -339,5 +382,5 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     has_init = torch.full((batch,), int(initial_states is not None), dtype=torch.int32, device=dev)
     o = extend(C.view(T, G, Nst), B.view(T, G, Nst), x.view(T, H, P), log_g, dtp, cu, slot, pool,
                has_init=has_init, mode="ssd", D=D, z=None if z is None else z.view(T, H, P),
-               max_seqlen=L, out_dtype=out_dtype)
+               max_seqlen=L, out_dtype=out_dtype, gate=g)
     return o.view(batch, L, H, P), (pool if return_final_states else None)

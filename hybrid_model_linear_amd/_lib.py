@@ -12,8 +12,8 @@ GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
 ABI_VERSION = 1
 
-EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_validate_slots", "gdn_status_str",
-            "gdn_last_hip_error", "gdn_abi_version"]
+EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
+            "gdn_validate_slots", "gdn_status_str", "gdn_last_hip_error", "gdn_abi_version"]
 
 
 class GateArgs(C.Structure):
@@ -65,9 +65,11 @@ def load(path: str | None = None) -> C.CDLL:
     lib.gdn_gate.argtypes = [C.POINTER(GateArgs), C.c_void_p]
     lib.gdn_extend.argtypes = [C.POINTER(ExtendArgs), C.c_void_p]
     lib.gdn_decode.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
+    lib.gdn_extend_gated.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.c_void_p]
+    lib.gdn_decode_gated.argtypes = [C.POINTER(DecodeArgs), C.POINTER(GateArgs), C.c_void_p]
     lib.gdn_validate_slots.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p]
-    for fn in ("gdn_gate", "gdn_extend", "gdn_decode", "gdn_validate_slots",
-               "gdn_last_hip_error", "gdn_abi_version"):
+    for fn in ("gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
+               "gdn_validate_slots", "gdn_last_hip_error", "gdn_abi_version"):
         getattr(lib, fn).restype = C.c_int
     lib.gdn_status_str.argtypes = [C.c_int]
     lib.gdn_status_str.restype = C.c_char_p

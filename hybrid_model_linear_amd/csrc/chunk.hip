@@ -252,7 +252,7 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 template <int I> struct Par { static constexpr int value = I; };
 
-template <int DK, int DV, bool kSSD, typename OutT, int CT>
+template <int DK, int DV, bool kSSD, typename OutT, int CT, bool kGate>
 __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kernel(SeqLaunch p) {
   constexpr int CW = 16 * CT;      // d_v columns per state wave (CT tiles of 16)
   constexpr int NSW = DV / CW;     // state waves
@@ -285,6 +285,12 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   const int nch = (tend - tbeg + C - 1) / C;
   const bool init = p.has_init ? (p.has_init[nseq] != 0) : true;
   const int j = h / (p.H_v / p.H_qk);
+  // gate folded in: the head's gate parameters (the raw a, b / dt are staged per token)
+  float gA = 0.f, gBias = 0.f;   // GDN: exp(A_log); delta-off: A
+  if constexpr (kGate) {
+    gA = kSSD ? p.gA[h] : expf(p.gA[h]);
+    gBias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -354,13 +360,41 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   TileRegs<DK, NST> rq_, rk_;
   TileRegs<DV, NST> rv_, rz_;                 // (z: delta-off only)
   float rg_ = 0.f, rb_ = 0.f;                 // log g, beta of chunk c + 2 (lane = token), for the producers
+  // (gate folded in: the aligned 32-bit words holding the raw bf16 a, b / dt, kept
+  // exactly as loaded -- any instruction on the loaded value, even a zero-extension
+  // of a 16-bit load, would make every wave wait for these loads at the step's end)
+  uint32_t ra_ = 0u, rbr_ = 0u;
+  // Gate folded in: producer 2, idle once T is done, turns its staged raw inputs of
+  // chunk c + 2 into log g, beta at the end of step c and stores them at once into the
+  // gate buffer of that chunk's parity (free during step c: its previous chunk was
+  // prepared in step c - 1), so the arithmetic stays off every wave's path.
+  auto gate_store = [&](int par) {
+    if constexpr (kGate) {
+      float lg, bt;
+      // head h's bf16 is the low (h even) or high (h odd) half of the word
+      const float ga = __uint_as_float((h & 1) ? (ra_ & 0xffff0000u) : (ra_ << 16));
+      if constexpr (kSSD) {
+        gate_ssd(ga, gA, gBias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
+      } else {
+        const float gb = __uint_as_float((h & 1) ? (rbr_ & 0xffff0000u) : (rbr_ << 16));
+        gate_gdn(ga, gb, gA, gBias, lg, bt);
+      }
+      sGr[par][lane] = lg;
+      sBr[par][lane] = bt;
+    }
+  };
   auto stage_qk = [&](int cc) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     rq_.load(qg, p.q_stride, t0, n, si);
     rk_.load(kg, p.k_stride, t0, n, si);
-    const int64_t gi = (int64_t)(t0 + (lane < n ? lane : 0)) * p.H_v + h;
-    rg_ = p.log_g[gi];
-    rb_ = p.beta[gi];
+    const int64_t tt = (int64_t)(t0 + (lane < n ? lane : 0));
+    if constexpr (kGate) {   // raw gate inputs (bf16)
+      ra_ = reinterpret_cast<const uint32_t*>(p.ga)[tt * (p.ga_stride >> 1) + (h >> 1)];
+      if constexpr (!kSSD) rbr_ = reinterpret_cast<const uint32_t*>(p.gb)[tt * (p.gb_stride >> 1) + (h >> 1)];
+    } else {
+      rg_ = p.log_g[tt * p.H_v + h];
+      rb_ = p.beta[tt * p.H_v + h];
+    }
   };
   auto stage_v = [&](int cc) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
@@ -807,7 +841,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         if (p.z) rz_.template store<false>(sZ, si);
       }
     }
-    if (hasP && wu == 0) {
+    if (!kGate && hasP && wu == 0) {
       sGr[PQ][lane] = rg_;
       sBr[PQ][lane] = rb_;
     }
@@ -821,6 +855,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         if constexpr (!kSSD) {
           if (hasS) finish_T(Par<PAR>{});
         }
+        gate_store(PAR);       // (gate folded in) chunk c + 2, staged in this landing
       } else if (hasP) {
         produce(c + 1, Par<PQ>{});
       }
@@ -838,6 +873,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // entry state and first staged loads retired on every path here, so no wait inside
   // the loop has to cover them
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  if (wu == NSW + 2) gate_store(0);    // (gate folded in) chunk 0
   for (int c = -1; c < nch && nch > 0; c += 2) {   // (an empty sequence only stores its state)
     step(c, Par<1>{});                   // c odd (c = -1: landing and the first chunk's preparation only)
     if (c + 1 < nch) step(c + 1, Par<0>{});
@@ -854,12 +890,17 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   }
 }
 
-template <int DK, int DV, bool kSSD, typename OutT>
-hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
+template <int DK, int DV, bool kSSD, typename OutT, bool kGate>
+hipError_t launch_gated(const SeqLaunch& p, hipStream_t stream) {
   constexpr int CT = kSSD ? 1 : 2;   // d_v columns per state wave: 32 (GDN), 16 (delta-off)
   dim3 grid(p.H_v, p.N), block((DV / (16 * CT) + kNP) * kWave);
-  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT, CT>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT, CT, kGate>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+template <int DK, int DV, bool kSSD, typename OutT>
+hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
+  return p.gate_fused ? launch_gated<DK, DV, kSSD, OutT, true>(p, stream)
+                      : launch_gated<DK, DV, kSSD, OutT, false>(p, stream);
 }
 
 }  // namespace
@@ -874,6 +915,11 @@ bool chunked_supported(const SeqLaunch& p) {
   const int64_t lim = (int64_t(1) << 31) / (C * 4);
   if (p.out_stride > lim || p.q_stride > lim || p.k_stride > lim || p.v_stride > lim) return false;
   if (p.z && p.z_stride > lim) return false;
+  // gate folded in: the raw bf16 gate inputs are read as aligned 32-bit words
+  if (p.gate_fused) {
+    if ((reinterpret_cast<uintptr_t>(p.ga) | reinterpret_cast<uintptr_t>(p.gb)) % 4 != 0) return false;
+    if ((p.ga_stride | (p.gb ? p.gb_stride : 0)) % 2 != 0) return false;
+  }
   return p.ssd ? p.d_v == 64 : p.d_v == 128;
 }
 

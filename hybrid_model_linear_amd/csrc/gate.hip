@@ -23,17 +23,13 @@ __global__ void __launch_bounds__(256) gate_kernel(int64_t T, int H, const InT* 
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = idx / H;
     const int h = int(idx - t * H);
-    float x = Elem<InT>::load(a, t * a_stride + h);
-    if (dt_bias) x += dt_bias[h];
-    if constexpr (kSSD) {
-      if (softplus_on) x = softplus_f(x);
-      x = fminf(fmaxf(x, lo), hi);
-      log_g[idx] = x * A[h];
-      beta[idx] = x;
-    } else {
-      log_g[idx] = -expf(A[h]) * softplus_f(x);
-      beta[idx] = sigmoid_f(Elem<InT>::load(b, t * b_stride + h));
-    }
+    const float x = Elem<InT>::load(a, t * a_stride + h);
+    const float bias = dt_bias ? dt_bias[h] : 0.0f;
+    float lg, bt;
+    if constexpr (kSSD) gate_ssd(x, A[h], bias, softplus_on, lo, hi, lg, bt);
+    else gate_gdn(x, Elem<InT>::load(b, t * b_stride + h), expf(A[h]), bias, lg, bt);
+    log_g[idx] = lg;
+    beta[idx] = bt;
   }
 }
 

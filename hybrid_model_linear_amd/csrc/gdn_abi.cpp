@@ -42,6 +42,52 @@ int check_seq_common(int32_t in_dtype, int32_t out_dtype, int32_t H_qk, int32_t 
   return GDN_OK;
 }
 
+// Checks of a gdn_gate_args description of the raw gate inputs (pointers only when
+// T > 0); `outputs` asks for the log_g / beta outputs of gdn_gate as well.
+int check_gate(const gdn_gate_args* a, bool outputs) {
+  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
+  if (!dtype_ok(a->in_dtype)) return GDN_E_DTYPE;
+  if (a->T < 0 || a->H <= 0) return GDN_E_SHAPE;
+  if (a->T == 0) return GDN_OK;
+  if (!a->a || !a->A) return GDN_E_NULL;
+  if (outputs && (!a->log_g || !a->beta)) return GDN_E_NULL;
+  if (a->a_stride < a->H) return GDN_E_SHAPE;
+  if (a->mode == GDN_MODE_GDN) {
+    if (!a->b) return GDN_E_NULL;
+    if (a->b_stride < a->H) return GDN_E_SHAPE;
+  } else {
+    if (a->b) return GDN_E_SHAPE;            // SSD mode has no b input
+    if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
+      return GDN_E_SHAPE;
+  }
+  return GDN_OK;
+}
+
+// The gate of a gated extend / decode call: same mode, dtype and [T, H_v] as the call.
+int check_fused_gate(const gdn_gate_args* g, int32_t mode, int32_t in_dtype, int64_t T, int32_t H_v) {
+  if (!g) return GDN_E_NULL;
+  if (g->mode != mode) return GDN_E_UNSUPPORTED;
+  if (g->in_dtype != in_dtype) return GDN_E_DTYPE;
+  if (g->T != T || g->H != H_v) return GDN_E_SHAPE;
+  return check_gate(g, false);
+}
+
+void fill_fused_gate(gdn::SeqLaunch& p, const gdn_gate_args* g) {
+  p.gate_fused = 1;
+  p.ga = g->a;
+  p.ga_stride = g->a_stride;
+  p.gb = g->b;
+  p.gb_stride = g->b_stride;
+  p.gA = g->A;
+  p.gdt_bias = g->dt_bias;
+  p.g_softplus = g->dt_softplus;
+  p.g_lo = g->dt_min;
+  p.g_hi = g->dt_max;
+}
+
+int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream);
+int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -65,20 +111,8 @@ const char* gdn_status_str(int status) {
 
 int gdn_gate(const gdn_gate_args* a, void* stream) {
   if (!a) return GDN_E_NULL;
-  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
-  if (!dtype_ok(a->in_dtype)) return GDN_E_DTYPE;
-  if (a->T < 0 || a->H <= 0) return GDN_E_SHAPE;
-  if (a->T == 0) return GDN_OK;
-  if (!a->a || !a->A || !a->log_g || !a->beta) return GDN_E_NULL;
-  if (a->a_stride < a->H) return GDN_E_SHAPE;
-  if (a->mode == GDN_MODE_GDN) {
-    if (!a->b) return GDN_E_NULL;
-    if (a->b_stride < a->H) return GDN_E_SHAPE;
-  } else {
-    if (a->b) return GDN_E_SHAPE;            // SSD mode has no b input
-    if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
-      return GDN_E_SHAPE;
-  }
+  const int st = check_gate(a, true);
+  if (st != GDN_OK || a->T == 0) return st;
   gdn::GateLaunch p{};
   p.T = a->T;
   p.H = a->H;
@@ -98,7 +132,22 @@ int gdn_gate(const gdn_gate_args* a, void* stream) {
   return hip_status(gdn::launch_gate(p, (hipStream_t)stream));
 }
 
-int gdn_extend(const gdn_extend_args* a, void* stream) {
+int gdn_extend(const gdn_extend_args* a, void* stream) { return extend_impl(a, nullptr, stream); }
+int gdn_extend_gated(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
+  if (!gate) return GDN_E_NULL;
+  return extend_impl(a, gate, stream);
+}
+int gdn_decode(const gdn_decode_args* a, void* stream) { return decode_impl(a, nullptr, stream); }
+int gdn_decode_gated(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream) {
+  if (!gate) return GDN_E_NULL;
+  return decode_impl(a, gate, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
   if (!a) return GDN_E_NULL;
   if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
   int st = check_seq_common(a->in_dtype, a->out_dtype, a->H_qk, a->H_v, a->d_k, a->d_v,
@@ -109,10 +158,14 @@ int gdn_extend(const gdn_extend_args* a, void* stream) {
   if (a->chunk != 0 && a->chunk != 64) return GDN_E_UNSUPPORTED;
   if (a->mode == GDN_MODE_GDN && (a->D || a->z)) return GDN_E_SHAPE;   // SSD-only inputs
   if (a->z && a->z_stride < (int64_t)a->H_v * a->d_v) return GDN_E_SHAPE;
+  if (gate) {
+    st = check_fused_gate(gate, a->mode, a->in_dtype, a->T, a->H_v);
+    if (st != GDN_OK) return st;
+  }
   if (a->N == 0) return GDN_OK;
   if (!a->cu_seqlens || !a->slot || !a->pool) return GDN_E_NULL;
-  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->out))
-    return GDN_E_NULL;
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->out)) return GDN_E_NULL;
+  if (a->T > 0 && !gate && (!a->log_g || !a->beta)) return GDN_E_NULL;
   if (a->T > INT32_MAX) return GDN_E_SHAPE;      // cu_seqlens is int32
   if (!aligned4(a->q, a->in_dtype) || !aligned4(a->k, a->in_dtype) || !aligned4(a->v, a->in_dtype) ||
       !aligned4(a->z, a->in_dtype) || !aligned4(a->out, a->out_dtype) || a->z_stride % 4 != 0 ||
@@ -150,6 +203,7 @@ int gdn_extend(const gdn_extend_args* a, void* stream) {
   p.z = a->z;
   p.z_stride = a->z_stride;
   p.max_seqlen = a->max_seqlen;
+  if (gate) fill_fused_gate(p, gate);
 
   const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
   if (p.in_bf16 && !short_batch && gdn::chunked_supported(p))
@@ -157,16 +211,20 @@ int gdn_extend(const gdn_extend_args* a, void* stream) {
   return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
 }
 
-int gdn_decode(const gdn_decode_args* a, void* stream) {
+int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream) {
   if (!a) return GDN_E_NULL;
   int st = check_seq_common(a->in_dtype, a->out_dtype, a->H_qk, a->H_v, a->d_k, a->d_v,
                             a->q_stride, a->k_stride, a->v_stride, a->out_stride, a->num_slots,
                             a->scale);
   if (st != GDN_OK) return st;
   if (a->B < 0) return GDN_E_SHAPE;
+  if (gate) {
+    st = check_fused_gate(gate, GDN_MODE_GDN, a->in_dtype, a->B, a->H_v);
+    if (st != GDN_OK) return st;
+  }
   if (a->B == 0) return GDN_OK;
-  if (!a->q || !a->k || !a->v || !a->log_g || !a->beta || !a->slot || !a->pool || !a->out)
-    return GDN_E_NULL;
+  if (!a->q || !a->k || !a->v || !a->slot || !a->pool || !a->out) return GDN_E_NULL;
+  if (!gate && (!a->log_g || !a->beta)) return GDN_E_NULL;
   if (!aligned4(a->q, a->in_dtype) || !aligned4(a->k, a->in_dtype) || !aligned4(a->v, a->in_dtype) ||
       !aligned4(a->out, a->out_dtype) || reinterpret_cast<uintptr_t>(a->pool) % 16 != 0)
     return GDN_E_SHAPE;
@@ -197,8 +255,13 @@ int gdn_decode(const gdn_decode_args* a, void* stream) {
   p.out_stride = a->out_stride;
   p.scale = a->scale;
   p.max_seqlen = 1;
+  if (gate) fill_fused_gate(p, gate);
   return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
                        void* stream) {

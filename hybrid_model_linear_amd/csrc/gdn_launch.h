@@ -54,6 +54,18 @@ struct SeqLaunch {
   const void* z;              // delta-off: like v, or null
   int64_t z_stride;
   int max_seqlen;             // host hint, 0 = unknown
+  // Gate folded in (gate_fused != 0): log g and beta are computed from these raw
+  // inputs (in_dtype, [T, H_v] with the given row strides) instead of read from
+  // log_g / beta, with the gate kernel's arithmetic.
+  int gate_fused;
+  const void* ga;             // GDN: a; SSD: dt
+  int64_t ga_stride;
+  const void* gb;             // GDN: b; SSD: null
+  int64_t gb_stride;
+  const float* gA;            // [H_v]: GDN A_log, SSD A
+  const float* gdt_bias;      // [H_v] or null
+  int g_softplus;
+  float g_lo, g_hi;
 };
 
 hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);

@@ -101,9 +101,21 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       qv.x *= rq; qv.y *= rq; qv.z *= rq; qv.w *= rq;
     }
     const float kq = group_sum<L::kLanesPerRow>(dot4(kv, qv));
-    const int64_t gi = (int64_t)t * p.H_v + h;
-    const float g = __expf(p.log_g[gi]);
-    const float bt = p.beta[gi];
+    float lg, bt;
+    if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
+      const float x = Elem<InT>::load(reinterpret_cast<const InT*>(p.ga), (int64_t)t * p.ga_stride + h);
+      const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
+      if constexpr (kSSD)
+        gate_ssd(x, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
+      else
+        gate_gdn(x, Elem<InT>::load(reinterpret_cast<const InT*>(p.gb), (int64_t)t * p.gb_stride + h),
+                 expf(p.gA[h]), bias, lg, bt);
+    } else {
+      const int64_t gi = (int64_t)t * p.H_v + h;
+      lg = p.log_g[gi];
+      bt = p.beta[gi];
+    }
+    const float g = __expf(lg);
     const int64_t vrow = (int64_t)t * p.v_stride + (int64_t)h * DV;
     const int64_t orow = (int64_t)t * p.out_stride + (int64_t)h * DV;
 #pragma unroll

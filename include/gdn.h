@@ -180,6 +180,27 @@ int gdn_gate(const gdn_gate_args* args, void* stream);
 int gdn_extend(const gdn_extend_args* args, void* stream);
 int gdn_decode(const gdn_decode_args* args, void* stream);
 
+/* ---------------------------------------------------------------- gated calls
+ * gdn_extend / gdn_decode with the gate folded in: the kernels compute log g and
+ * beta from the raw gate inputs that `gate` describes, with the arithmetic of
+ * gdn_gate, instead of reading args->log_g / args->beta (ignored, may be NULL).
+ * This is the same computation as gdn_gate followed by gdn_extend / gdn_decode
+ * (the gate hyperbolic and exponential functions are shared source; one launch and
+ * the fp32 [T, H_v] round trip fewer).  Gate of a decode, hybrid_backend page
+ * (section on the GDN layer's gate parameters): a, b per token and v-head,
+ * A_log and dt_bias per v-head.
+ *   gate->mode     : args->mode (extend) / GDN_MODE_GDN (decode), else
+ *                    GDN_E_UNSUPPORTED
+ *   gate->in_dtype : args->in_dtype, else GDN_E_DTYPE
+ *   gate->T, H     : args->T (extend) or args->B (decode), and args->H_v, else
+ *                    GDN_E_SHAPE
+ *   gate->a, b, A, dt_bias, dt_softplus, dt_min, dt_max : as for gdn_gate
+ *   gate->log_g, beta : not written, may be NULL
+ * A NULL `gate` returns GDN_E_NULL; everything else is validated as for the
+ * ungated call. */
+int gdn_extend_gated(const gdn_extend_args* args, const gdn_gate_args* gate, void* stream);
+int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, void* stream);
+
 /* Device-side check of slot[0..n): *flag (device int32) receives 0 when every
  * non-negative slot is < num_slots and no non-negative slot repeats, 1 when one
  * is out of range, 2 when one repeats (3 when both).  Negative slots are padding

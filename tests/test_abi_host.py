@@ -133,6 +133,33 @@ def test_gate_and_decode_validation():
     assert lib.gdn_status_str(_lib.GDN_E_HIP) == b"HIP runtime error"
 
 
+def test_gated_calls_validation():
+    lib = gdn.load()
+    e = _ext(cu_seqlens=FAKE, slot=FAKE, pool=FAKE, q=FAKE, k=FAKE, v=FAKE, out=FAKE)   # no log_g/beta
+    g = _lib.GateArgs(mode=0, in_dtype=1, T=4, H=4, a=FAKE, a_stride=4, b=FAKE, b_stride=4, A=FAKE)
+    assert lib.gdn_extend_gated(ct.byref(e), None, None) == _lib.GDN_E_NULL
+    assert lib.gdn_extend(ct.byref(e), None) == _lib.GDN_E_NULL                 # ungated needs log_g
+    for kw, status in ((dict(mode=1, b=None), _lib.GDN_E_UNSUPPORTED),        # mode differs
+                       (dict(in_dtype=0), _lib.GDN_E_DTYPE),                   # dtype differs
+                       (dict(T=5), _lib.GDN_E_SHAPE),                          # token count differs
+                       (dict(H=2, a_stride=2, b_stride=2), _lib.GDN_E_SHAPE),  # head count differs
+                       (dict(a=None), _lib.GDN_E_NULL),
+                       (dict(b=None), _lib.GDN_E_NULL),
+                       (dict(a_stride=3), _lib.GDN_E_SHAPE)):
+        bad = _lib.GateArgs.from_buffer_copy(g)
+        for f, val in kw.items():
+            setattr(bad, f, val)
+        assert lib.gdn_extend_gated(ct.byref(e), ct.byref(bad), None) == status, kw
+    d = _lib.DecodeArgs(in_dtype=1, out_dtype=1, B=4, H_qk=2, H_v=4, d_k=128, d_v=128,
+                        q_stride=1024, k_stride=1024, v_stride=1024, num_slots=4, out_stride=512,
+                        scale=0.1)
+    assert lib.gdn_decode_gated(ct.byref(d), None, None) == _lib.GDN_E_NULL
+    assert lib.gdn_decode_gated(ct.byref(d), ct.byref(g), None) == _lib.GDN_E_NULL   # q .. missing
+    gs = _lib.GateArgs.from_buffer_copy(g)
+    gs.mode, gs.b = 1, None
+    assert lib.gdn_decode_gated(ct.byref(d), ct.byref(gs), None) == _lib.GDN_E_UNSUPPORTED   # decode is GDN only
+
+
 def test_binding_rejects_cpu_tensors():
     q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
@@ -179,28 +206,40 @@ def _layer():
 
 @pytest.mark.parametrize("mode,expect", [("DECODE", "decode"), ("TARGET_VERIFY", "extend"),
                                          ("EXTEND", "extend")])
-def test_forward_gdn_routes_by_mode(mode, expect):
+@pytest.mark.parametrize("gate_dtype_matches", [True, False])
+def test_forward_gdn_routes_by_mode(mode, expect, gate_dtype_matches):
     T = 5
     mixed = torch.zeros(T, 2 * 2 * 128 + 4 * 128)
     a, b = torch.zeros(T, 4), torch.zeros(T, 4)
     pool, slots, cu, hi = object(), object(), object(), object()
     fb = SimpleNamespace(forward_mode=_Mode(mode), state_pool={3: pool}, state_slots=slots,
                          cu_seqlens=cu, has_initial_state=hi, max_seqlen=7)
+    layer = _layer()
+    gsent = SimpleNamespace(dtype=mixed.dtype if gate_dtype_matches else torch.bfloat16)
     lg, bt = object(), object()
     out = torch.zeros(T, 4, 128)
-    with mock.patch.object(gdn, "gate", return_value=(lg, bt)) as mg, \
+    with mock.patch.object(gdn, "gdn_gate_inputs", return_value=gsent) as mg, \
+            mock.patch.object(gdn, "_run_gate", return_value=(lg, bt)) as mr, \
             mock.patch.object(gdn, "decode", return_value=out) as md, \
             mock.patch.object(gdn, "extend", return_value=out) as me:
-        res = gdn.forward_gdn(_layer(), fb, mixed, a, b)
+        res = gdn.forward_gdn(layer, fb, mixed, a, b)
     assert res.shape == (T, 512)
     mg.assert_called_once()
     assert mg.call_args.args[0] is a and mg.call_args.args[1] is b
+    assert mg.call_args.args[2] is layer.A_log and mg.call_args.args[3] is layer.dt_bias
     called, other = (md, me) if expect == "decode" else (me, md)
     called.assert_called_once()
     other.assert_not_called()
     sent = list(called.call_args.args) + list(called.call_args.kwargs.values())
     assert any(x is pool for x in sent) and any(x is slots for x in sent)
-    assert any(x is lg for x in sent) and any(x is bt for x in sent)
+    if gate_dtype_matches:   # gate folded into the layer kernel
+        mr.assert_not_called()
+        assert called.call_args.kwargs["gate"] is gsent
+        assert called.call_args.args[3] is None and called.call_args.args[4] is None
+    else:                    # gate launched on its own, its outputs passed on
+        mr.assert_called_once()
+        assert called.call_args.kwargs["gate"] is None
+        assert called.call_args.args[3] is lg and called.call_args.args[4] is bt
     if expect == "extend":
         assert any(x is cu for x in sent) and any(x is hi for x in sent)
         assert called.call_args.kwargs["max_seqlen"] == 7
@@ -213,7 +252,7 @@ def test_forward_gdn_routes_by_mode(mode, expect):
 
 def test_forward_gdn_invalid_mode_raises_before_any_call():
     fb = SimpleNamespace(forward_mode=_Mode("DUMMY_FIRST"))
-    with mock.patch.object(gdn, "gate") as mg:
+    with mock.patch.object(gdn, "gdn_gate_inputs") as mg:
         with pytest.raises(ValueError, match="Invalid forward mode"):
             gdn.forward_gdn(_layer(), fb, torch.zeros(1, 1024), torch.zeros(1, 4), torch.zeros(1, 4))
     mg.assert_not_called()

@@ -56,6 +56,83 @@ def test_gate_parity(gdn_lib, dtype):
         assert np.allclose(lg.cpu().numpy(), rlg, rtol=2e-6, atol=1e-6)
 
 
+# ------------------------------------------------------------------ gate folded into the kernels
+# The gated calls take the raw a, b (dt) and compute log g, beta with the gate
+# kernel's own arithmetic, so they must reproduce gate + extend / decode exactly.
+@pytest.mark.parametrize("dtype,max_seqlen", [("bf16", 0), ("bf16", 8), ("f32", 0)])
+def test_gate_folded_extend_matches_separate(gdn_lib, dtype, max_seqlen):
+    gdn = gdn_lib
+    _announce(f"gate folded into extend {dtype} max_seqlen={max_seqlen}")
+    lens = (5, 64, 65, 130) if max_seqlen == 0 else (3, 8, 1, 7)
+    case = synth.make_gdn_case("fold", seed=21, lens=lens, has_init=(1, 0, 1, 1), H_qk=2, H_v=4,
+                               d_k=128, d_v=128, dtype=dtype, num_slots=6, pool_sigma=0.05)
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    runs = []
+    for folded in (False, True):
+        pool = d["pool"].clone()
+        if folded:
+            lg = bt = None
+            g = gdn.gdn_gate_inputs(d["a"], d["b"], d["A_log"], d["dt_bias"])
+        else:
+            lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+            g = None
+        out = gdn.extend(q, k, v, lg, bt, d["cu"], d["slot"], pool, has_init=d["has_init"],
+                         scale=case.scale, max_seqlen=max_seqlen, gate=g)
+        runs.append((out, pool))
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0].view(torch.int16 if dtype == "bf16" else torch.int32),
+                       runs[1][0].view(torch.int16 if dtype == "bf16" else torch.int32)), "outputs differ"
+    assert torch.equal(runs[0][1].view(torch.int32), runs[1][1].view(torch.int32)), "states differ"
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale)
+    bar = (2e-3, 1e-2) if dtype == "bf16" else (1e-3, 2e-3)
+    assert_close(runs[1][0].float().cpu().numpy(), ref, "folded out", *bar)
+
+
+def test_gate_folded_decode_and_ssd_match_separate(gdn_lib):
+    gdn = gdn_lib
+    _announce("gate folded into decode and delta-off extend")
+    case = synth.make_gdn_case("fold-dec", seed=23, lens=(1,) * 9, has_init=1, H_qk=2, H_v=4,
+                               d_k=128, d_v=128, dtype="bf16", num_slots=12, pool_sigma=0.05)
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    outs = []
+    for folded in (False, True):
+        pool = d["pool"].clone()
+        if folded:
+            out = gdn.decode(q, k, v, None, None, d["slot"], pool, scale=case.scale,
+                             gate=gdn.gdn_gate_inputs(d["a"], d["b"], d["A_log"], d["dt_bias"]))
+        else:
+            lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+            out = gdn.decode(q, k, v, lg, bt, d["slot"], pool, scale=case.scale)
+        outs.append((out, pool))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16)), "decode outputs differ"
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32)), "decode states differ"
+    # delta-off: ssd_combined_fwd (gate folded) against ssd_gate + extend
+    c = synth.config4_ssd(seed=5, batch=2, L=100, H=6, P=64, G=2, Nst=128, initial=True)
+    tb = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
+    tf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.float32)
+    lim = (0.05, 2.0)
+    out, fin = gdn.ssd_combined_fwd(tb(c.x), tb(c.dt), tf(c.A), tb(c.B), tb(c.C), tb(c.D), tb(c.z),
+                                    tf(c.dt_bias), True, lim, tf(c.initial_states))
+    batch, L, H, P = c.x.shape
+    G, Nst = c.B.shape[2], c.B.shape[3]
+    T = batch * L
+    lg, dtp = gdn.ssd_gate(tb(c.dt).view(T, H), tf(c.A), tf(c.dt_bias), True, lim)
+    pool = tf(c.initial_states).contiguous().clone()
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    slot = torch.arange(batch, dtype=torch.int32, device="cuda")
+    hi = torch.ones(batch, dtype=torch.int32, device="cuda")
+    out2 = gdn.extend(tb(c.C).view(T, G, Nst), tb(c.B).view(T, G, Nst), tb(c.x).view(T, H, P), lg, dtp,
+                      cu, slot, pool, has_init=hi, mode="ssd", D=tb(c.D), z=tb(c.z).view(T, H, P),
+                      max_seqlen=L)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(T, H, P).view(torch.int16), out2.view(torch.int16)), "ssd outputs differ"
+    assert torch.equal(fin.view(torch.int32), pool.view(torch.int32)), "ssd states differ"
+
+
 # ------------------------------------------------------------------ tiny fp32 (extend + decode)
 def test_config0_tiny_fp32_extend_then_decode(gdn_lib):
     gdn = gdn_lib
