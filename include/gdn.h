@@ -184,11 +184,13 @@ int gdn_decode(const gdn_decode_args* args, void* stream);
  * gdn_extend / gdn_decode with the gate folded in: the kernels compute log g and
  * beta from the raw gate inputs that `gate` describes, with the arithmetic of
  * gdn_gate, instead of reading args->log_g / args->beta (ignored, may be NULL).
- * This is the same computation as gdn_gate followed by gdn_extend / gdn_decode
- * (the gate hyperbolic and exponential functions are shared source; one launch and
- * the fp32 [T, H_v] round trip fewer).  Gate of a decode, hybrid_backend page
- * (section on the GDN layer's gate parameters): a, b per token and v-head,
- * A_log and dt_bias per v-head.
+ * This is the same computation as gdn_gate followed by gdn_extend / gdn_decode,
+ * bit for bit (one shared definition of the gate functions), with one launch and
+ * the fp32 [T, H_v] round trip fewer: the shape of forward_gdn(layer,
+ * forward_batch, mixed_qkv, a, b) on the hybrid_backend page, whose a, b are the
+ * gate inputs.  The chunked kernel reads bf16 a, b as aligned 32-bit words: with a,
+ * b not 4-byte aligned or an odd row stride the call runs the token-recurrent
+ * kernel instead (speed only).
  *   gate->mode     : args->mode (extend) / GDN_MODE_GDN (decode), else
  *                    GDN_E_UNSUPPORTED
  *   gate->in_dtype : args->in_dtype, else GDN_E_DTYPE
