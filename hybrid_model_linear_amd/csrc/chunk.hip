@@ -17,8 +17,10 @@
 //
 // Precision: q, k, v enter the MFMAs as their exact bf16 values; norms, beta and
 // decays are fp32 row/column scalings applied around the products; S0, T and the
-// correction operand bf16(R) are single bf16 operands; P U and the state update use
-// two-term (hi + lo) bf16 splits of P, U and the scaled U.
+// correction operand bf16(R) are single bf16 operands; the state update uses two-term
+// (hi + lo) bf16 splits of the scaled U.  P U takes single fp16 operands when the
+// output is bf16 (|P| <= scale; fp16's 11-bit significand keeps its error below the
+// output rounding) and two-term bf16 splits of P and U otherwise.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
 // order.  Two kinds of waves run side by side:
@@ -31,7 +33,7 @@
 //    part, with no barrier inside (they wait once, for T of chunk c).
 //  * four producer waves run meanwhile: three prepare chunk c + 1 (decay cumsum,
 //    row norms and the per-token coefficient vectors; Q K^T and K K^T tiles -> P
-//    (hi + lo) and A), the fourth turns chunk c's A into T = (I + A)^{-1} in place,
+//    and A), the fourth turns chunk c's A into T = (I + A)^{-1} in place,
 //    early in the step, before the state waves need it.
 // The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
 // step ahead.
@@ -66,6 +68,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma1632(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma1632h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
@@ -125,6 +132,11 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+// two fp32 -> packed fp16 pair (one v_cvt_pk_f16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t cvt2h(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
 __device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
   const int o = 8 * half;
   return as_bf16x8(make_uint4(cvt2(a[o], a[o + 1]), cvt2(a[o + 2], a[o + 3]), cvt2(a[o + 4], a[o + 5]),
@@ -135,6 +147,9 @@ __device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
 // 4 g + e, e >= 4 -> tile t1 row 4 g + e - 4.
 __device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
   return as_bf16x8(make_uint4(cvt2(a[0], a[1]), cvt2(a[2], a[3]), cvt2(b[0], b[1]), cvt2(b[2], b[3])));
+}
+__device__ __forceinline__ f16x8 pair_to_op_h(const f32x4& a, const f32x4& b) {
+  return __builtin_bit_cast(f16x8, make_uint4(cvt2h(a[0], a[1]), cvt2h(a[2], a[3]), cvt2h(b[0], b[1]), cvt2h(b[2], b[3])));
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -259,12 +274,17 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
+  // P U with single fp16 operands (GDN with bf16 output): |P| <= scale by construction
+  // (unit rows, decays <= 1) and fp16's 2^-12 rounding stays well below the output's
+  // own bf16 rounding.  fp32 output and the delta-off mode keep the two-term bf16 splits.
+  constexpr bool kPU16 = !kSSD && sizeof(OutT) == 2;
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
   __shared__ __attribute__((aligned(16))) u16 sQ[2][C * DK], sK[2][C * DK];
   __shared__ __attribute__((aligned(16))) u16 sV[C * (DV + 8)], sZ[kSSD ? C * (DV + 8) : 8];
   // producer outputs for the state waves, double-buffered
-  __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS], sPl[2][C][kPS];
+  __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS];                 // P (hi, or fp16)
+  __shared__ __attribute__((aligned(16))) u16 sPl[kPU16 ? 1 : 2][kPU16 ? 1 : C][kPS];   // P lo
   __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
@@ -524,8 +544,27 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
     }
-    // O = CO (Q S0^T) + P U (two-term splits of P and U)
-    {
+    // O = CO (Q S0^T) + P U (fp16 operands, or two-term bf16 splits of P and U)
+    if constexpr (kPU16) {
+      f16x8 Uf[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) Uf[ct][s2] = pair_to_op_h(U[ct][2 * s2], U[ct][2 * s2 + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float co = sCO[PAR][16 * rt + j16];    // this lane's token
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[ct][rt] *= co;
+        const u16* prow = &sPh[PAR][16 * rt + j16][8 * g16];
+#pragma unroll
+        for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+          const f16x8 pf = __builtin_bit_cast(f16x8, ld8u(prow + 32 * s2));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632h(Uf[ct][s2], pf, Y[ct][rt]);   // (P U)^T = U^T P^T
+        }
+      }
+    } else {
       bf16x8 Uh[CT][2], Ul[CT][2];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -649,7 +688,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   uint32_t pgen = 0;                          // chunks prepared so far (uniform)
   constexpr float kLog2e = 1.4426950408889634f;
 
-  // Prepare chunk cp (buffers of parity PQ): its vectors, P (hi + lo), and A stored in
+  // Prepare chunk cp (buffers of parity PQ): its vectors, P (fp16, or bf16 hi + lo), and A stored in
   // T's buffer (bf16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
   // (pr = wave - NSW):
   //   pr 3:    the off-diagonal tile's products, then the chunk's vectors (lane =
@@ -671,7 +710,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     const u16* K = sK[PQ];
     ++pgen;
 
-    // P (hi + lo) and A of tile (ti, tj) from its products
+    // P and A of tile (ti, tj) from its products
     auto emit = [&](auto kdiag, const f32x16& qk, const f32x16& kk) {
       constexpr bool kDiag = decltype(kdiag)::value;
       const int ti = kDiag ? pr : 1, tj = kDiag ? pr : 0;
@@ -693,11 +732,15 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           pv[e] = (rowP * f) * qk[r];
           av[e] = (rowA * f) * kk[r];
         }
-        const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
-        const uint32_t l0 = cvt2(sub_bf_lo(h0, pv[0]), sub_bf_hi(h0, pv[1]));
-        const uint32_t l1 = cvt2(sub_bf_lo(h1, pv[2]), sub_bf_hi(h1, pv[3]));
-        *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
+        if constexpr (kPU16) {
+          *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(cvt2h(pv[0], pv[1]), cvt2h(pv[2], pv[3]));
+        } else {
+          const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
+          const uint32_t l0 = cvt2(sub_bf_lo(h0, pv[0]), sub_bf_hi(h0, pv[1]));
+          const uint32_t l1 = cvt2(sub_bf_lo(h1, pv[2]), sub_bf_hi(h1, pv[3]));
+          *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
+        }
         if constexpr (!kSSD) {
           *reinterpret_cast<uint2*>(&sTb[PQ][i][kperm(mb)]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
           if (kDiag && (i >> 4) == (mb >> 4))
