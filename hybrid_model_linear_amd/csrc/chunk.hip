@@ -37,9 +37,10 @@
 //    early in the step, before the state waves need it.
 // The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
 // step ahead.
-// Each step has two workgroup barriers: one ends the previous step, the second ends
-// the landing of the staged data.  P, T and the coefficients are double-buffered,
-// and so are Q and K (chunk c for the state waves, c + 1 for the producers).
+// Each step has one workgroup barrier, which ends the previous step; the landing of
+// the staged rows that follows is announced on an arrival counter, so the state
+// waves start on chunk c (its Q and K landed a step earlier) while it is under way.  P, T and the coefficients are double-buffered, and so are Q and K (chunk c
+// for the state waves, c + 1 for the producers).
 //
 // Data layout in LDS: tiles are row-major and padded by one 16-byte segment per
 // row.  K^T and V^T operands come from the row-major tiles through the LDS
@@ -58,6 +59,10 @@ constexpr int kPS = C + 4;       // row length (bf16) of the padded C x C tiles:
 constexpr int kNP = 4;           // producer waves
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// Buffer resource word 3 for untyped dword accesses on gfx9 (32-bit data format)
+constexpr int kBufWord3 = 0x00020000;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -274,20 +279,25 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
-  // P U with single fp16 operands (GDN with bf16 output): |P| <= scale by construction
-  // (unit rows, decays <= 1) and fp16's 2^-12 rounding stays well below the output's
-  // own bf16 rounding.  fp32 output and the delta-off mode keep the two-term bf16 splits.
-  constexpr bool kPU16 = !kSSD && sizeof(OutT) == 2;
+  // fp16 operands (GDN with bf16 output): the state waves take Q^ = diag(CO) Q and
+  // K^ = diag(r_k) K (converted in place by the producers, one step ahead), S0, the
+  // scaled U of the state update and P U as single fp16 operands.  Every operand is
+  // bounded by construction or by the values (|K^| <= 1, |P| <= scale, decays <= 1),
+  // and fp16's 11-bit significand keeps each product's error well below the output's
+  // bf16 rounding.  fp32 output and the delta-off mode keep raw bf16 Q, K with bf16
+  // S0 and two-term bf16 splits.
+  constexpr bool kF16 = !kSSD && sizeof(OutT) == 2;
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
   __shared__ __attribute__((aligned(16))) u16 sQ[2][C * DK], sK[2][C * DK];
   __shared__ __attribute__((aligned(16))) u16 sV[C * (DV + 8)], sZ[kSSD ? C * (DV + 8) : 8];
   // producer outputs for the state waves, double-buffered
   __shared__ __attribute__((aligned(16))) u16 sPh[2][C][kPS];                 // P (hi, or fp16)
-  __shared__ __attribute__((aligned(16))) u16 sPl[kPU16 ? 1 : 2][kPU16 ? 1 : C][kPS];   // P lo
+  __shared__ __attribute__((aligned(16))) u16 sPl[kF16 ? 1 : 2][kF16 ? 1 : C][kPS];   // P lo
   __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
+  __shared__ __attribute__((aligned(16))) float sRk[kF16 ? 2 : 1][kF16 ? C : 4];   // r_k (fp16 operands)
   // producer working set (per producer wave where private)
   // fp32 diagonal 16x16 blocks of A, rows of 20 floats, double-buffered; the block
   // stride of 336 floats puts the four blocks on different banks (the solve reads all
@@ -295,7 +305,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 2][4][16 * 20 + 16];
   // vectors of the chunk being prepared, per token (see the producer roles)
   __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
-  __shared__ uint32_t sSync[4];   // arrival counters: chunk vectors ready, T ready
+  // arrival counters: chunk vectors ready, T ready, raw Q/K read, landing done
+  __shared__ uint32_t sSync[4];
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
@@ -372,9 +383,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 
   // ================================================================ staging
   // Every wave stages an equal share of the raw rows: Q, K of chunk c + 2 and V (z)
-  // of chunk c + 1 are in flight in registers during step c (producers issue them in
-  // the landing phase, state waves in the middle of their step).  The landing is the
-  // same code on every wave.
+  // of chunk c + 1 are in flight in registers during step c (producers issue them
+  // right after the landing, state waves in the middle of their step).  Every wave
+  // lands its share right after the step's barrier and announces it on an arrival
+  // counter; the producers wait for the whole landing before their first products,
+  // the state waves only before they first read V.
   constexpr int NST = (NSW + kNP) * kWave;
   const int si = tid;                         // staging index
   TileRegs<DK, NST> rq_, rk_;
@@ -388,7 +401,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // chunk c + 2 into log g, beta at the end of step c and stores them at once into the
   // gate buffer of that chunk's parity (free during step c: its previous chunk was
   // prepared in step c - 1), so the arithmetic stays off every wave's path.
-  auto gate_store = [&](int par) {
+  auto gate_store = [&](int par) __attribute__((always_inline)) {
     if constexpr (kGate) {
       float lg, bt;
       // head h's bf16 is the low (h even) or high (h odd) half of the word
@@ -403,7 +416,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sBr[par][lane] = bt;
     }
   };
-  auto stage_qk = [&](int cc) {
+  auto stage_qk = [&](int cc) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     rq_.load(qg, p.q_stride, t0, n, si);
     rk_.load(kg, p.k_stride, t0, n, si);
@@ -416,7 +429,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       rb_ = p.beta[tt * p.H_v + h];
     }
   };
-  auto stage_v = [&](int cc) {
+  auto stage_v = [&](int cc) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
     rv_.load(vg, p.v_stride, t0, n, si);
     if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
@@ -426,11 +439,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // writes are performed before its later increment (the LDS executes one wave's
   // accesses in order); the waiting wave reads the data only after seeing the count.
   // Waits are bounded: every counted arrival happens unconditionally.
-  auto arrive = [&](uint32_t* ctr) {
+  auto arrive = [&](uint32_t* ctr) __attribute__((always_inline)) {
     lds_order();
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
-  auto wait_count = [&](uint32_t* ctr, uint32_t target) {
+  auto wait_count = [&](uint32_t* ctr, uint32_t target) __attribute__((always_inline)) {
     for (int it = 0; it < (1 << 22); ++it) {
       if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
       __builtin_amdgcn_s_sleep(1);
@@ -440,7 +453,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 
   // State-dependent part of chunk c (buffers of parity PAR).  A operands (rows of Q,
   // K, T, P and K^T) are read once and shared by the wave's CT column tiles.
-  auto consume = [&](int c, auto parc) {
+  auto consume = [&](int c, auto parc) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;
     const int t0 = tbeg + c * C, n = min(C, tend - t0);
     // Lane-derived indices are recomputed in every step (an opaque copy of the lane
@@ -458,7 +471,31 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     // token 16 rt + j16), from the same operands with A and B swapped, so that a lane
     // holds 4 consecutive output columns of one token (8-byte stores).
     f32x4 Y[CT][4], U[CT][4];
-    {
+    if constexpr (kF16) {   // Y = Q^ S0^T (CO folded in), X = K^ S0^T (r_k folded in)
+      f16x8 Sb[CT][NKS];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) Sb[ct][s2] = pair_to_op_h(Sacc[ct][2 * s2], Sacc[ct][2 * s2 + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Y[ct][rt] = f32x4{};
+          U[ct][rt] = f32x4{};
+        }
+        const int row = 16 * rt + j16;
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+          const f16x8 aq = __builtin_bit_cast(f16x8, ldq8<DK>(Q, row, 32 * s2 + 8 * g16));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632h(Sb[ct][s2], aq, Y[ct][rt]);
+          const f16x8 ak = __builtin_bit_cast(f16x8, ldq8<DK>(K, row, 32 * s2 + 8 * g16));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632h(ak, Sb[ct][s2], U[ct][rt]);
+        }
+      }
+    } else {
       bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -486,12 +523,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       }
     }
     // This wave's share of the next staged rows (Q, K of chunk c + 2, V of c + 1):
-    // issued here rather than in the landing phase, so that the landing's LDS writes
-    // are all the state waves do between the two barriers, and before this step's
-    // output stores, so that the next landing's wait for these loads never includes
-    // the stores (the memory counter retires in order).
+    // issued before this step's output stores, so that the next landing's wait for
+    // these loads never includes the stores (the memory counter retires in order).
     stage_qk(min(c + 2, nch - 1));
     stage_v(min(c + 1, nch - 1));
+    wait_count(&sSync[3], 8u * (uint32_t)(c + 2));   // this step's landing (V of chunk c) done
     // R = beta V - CR X (GDN); U = beta V (delta-off).  V through transpose reads.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -545,17 +581,14 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       }
     }
     // O = CO (Q S0^T) + P U (fp16 operands, or two-term bf16 splits of P and U)
-    if constexpr (kPU16) {
+    if constexpr (kF16) {
       f16x8 Uf[CT][2];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) Uf[ct][s2] = pair_to_op_h(U[ct][2 * s2], U[ct][2 * s2 + 1]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float co = sCO[PAR][16 * rt + j16];    // this lane's token
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Y[ct][rt] *= co;
+      for (int rt = 0; rt < 4; ++rt) {   // (CO is folded into Q^)
         const u16* prow = &sPh[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
@@ -612,31 +645,31 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
     {
       // row j16 + 16 rt, columns 16 ct + 4 g16 ..: a lane offset plus uniform row-tile
-      // steps (the column tiles are instruction offsets)
-      char* base = out_base(t0);
+      // steps (the column tiles are instruction offsets).  Bounds-checked buffer stores
+      // whose record range is the chunk's n rows: the hardware drops the rows past the
+      // sequence end, so every step issues the same stores without a branch, which
+      // keeps the count of memory operations in flight the same on every path (the
+      // next landing then waits for the staged loads only, never for these stores).
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(out_base(t0), (short)0, (int)((uint32_t)n * ostride_b), kBufWord3);
       const uint32_t o0 = (uint32_t)j16 * ostride_b + (uint32_t)(4 * g16 * sizeof(OutT));
-      auto store = [&](int ct, int rt) {
-        char* a = base + (o0 + (uint32_t)rt * (16u * ostride_b)) + 16 * ct * (int)sizeof(OutT);
-        if constexpr (sizeof(OutT) == 2)
-          *reinterpret_cast<uint2*>(a) = make_uint2(cvt2(Y[ct][rt][0], Y[ct][rt][1]), cvt2(Y[ct][rt][2], Y[ct][rt][3]));
-        else
-          *reinterpret_cast<float4*>(a) = make_float4(Y[ct][rt][0], Y[ct][rt][1], Y[ct][rt][2], Y[ct][rt][3]);
-      };
-      if (n == C) {   // whole chunk: no per-row guard
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) store(ct, rt);
-      } else {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-            if (16 * rt + j16 < n) store(ct, rt);
-      }
+        for (int rt = 0; rt < 4; ++rt) {
+          const int off = (int)(o0 + (uint32_t)rt * (16u * ostride_b)) + 16 * ct * (int)sizeof(OutT);
+          if constexpr (sizeof(OutT) == 2) {
+            const u32x2 w = {cvt2(Y[ct][rt][0], Y[ct][rt][1]), cvt2(Y[ct][rt][2], Y[ct][rt][3])};
+            __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+          } else {
+            const u32x4 w = {__float_as_uint(Y[ct][rt][0]), __float_as_uint(Y[ct][rt][1]),
+                             __float_as_uint(Y[ct][rt][2]), __float_as_uint(Y[ct][rt][3])};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, 0);
+          }
+        }
     }
 
-    // state update: S^T = gamma_C S^T + K^T diag(CS) U  (split hi + lo)
+    // state update: S^T = gamma_C S^T + K^T diag(CS) U  (fp16 K^ and CS U, or bf16 K with hi + lo splits)
     {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -646,25 +679,45 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
           for (int e = 0; e < 4; ++e) U[ct][rt][e] *= f4get(cs, e);
       }
-      bf16x8 Wh[CT][2], Wl[CT][2];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Wh[ct][s2], Wl[ct][s2]);
       // A operand K^T: row d_k = 16 tk + j16; k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
       const int rb = 4 * g16 + (j16 >> 2);
+      if constexpr (kF16) {   // K^^T (r_k folded in) times the scaled U, fp16
+        f16x8 Wf[CT][2];
 #pragma unroll
-      for (int tk = 0; tk < NTK; ++tk) {
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
-        const int ca = kperm(16 * tk + 4 * (j16 & 3));
+          for (int s2 = 0; s2 < 2; ++s2) Wf[ct][s2] = pair_to_op_h(U[ct][2 * s2], U[ct][2 * s2 + 1]);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 kt = join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca));
+        for (int tk = 0; tk < NTK; ++tk) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            Sacc[ct][tk] = mfma1632(kt, Wh[ct][s2], Sacc[ct][tk]);
-            Sacc[ct][tk] = mfma1632(kt, Wl[ct][s2], Sacc[ct][tk]);
+          for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
+          const int ca = kperm(16 * tk + 4 * (j16 & 3));
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const f16x8 kt = __builtin_bit_cast(f16x8, join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca)));
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] = mfma1632h(kt, Wf[ct][s2], Sacc[ct][tk]);
+          }
+        }
+      } else {
+        bf16x8 Wh[CT][2], Wl[CT][2];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Wh[ct][s2], Wl[ct][s2]);
+#pragma unroll
+        for (int tk = 0; tk < NTK; ++tk) {
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
+          const int ca = kperm(16 * tk + 4 * (j16 & 3));
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 kt = join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca));
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              Sacc[ct][tk] = mfma1632(kt, Wh[ct][s2], Sacc[ct][tk]);
+              Sacc[ct][tk] = mfma1632(kt, Wl[ct][s2], Sacc[ct][tk]);
+            }
           }
         }
       }
@@ -675,7 +728,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 
   // Tile (ti, tj) of K Q^T and K K^T (the transposes of Q K^T and K K^T: each lane
   // holds one query row i = 32 ti + l32 and keys m = 32 tj + 8 q4 + 4 hh + e).
-  auto tile_mma = [&](const u16* Q, const u16* K, int ti, int tj, int l32, int hh, f32x16& qk, f32x16& kk) {
+  auto tile_mma = [&](const u16* Q, const u16* K, int ti, int tj, int l32, int hh, f32x16& qk, f32x16& kk) __attribute__((always_inline)) {
     qk = f32x16{};
     kk = f32x16{};
 #pragma unroll
@@ -699,7 +752,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   //   pr 0, 1: diagonal tile t = pr (one exp per element).
   // Entries of A on and above the diagonal are not needed; those inside the diagonal
   // 32x32 tiles come out as zeros or are overwritten by T's diagonal blocks.
-  auto produce = [&](int cp, auto parq) {
+  auto produce = [&](int cp, auto parq) __attribute__((always_inline)) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
     int lane_o = lane;
@@ -711,7 +764,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     ++pgen;
 
     // P and A of tile (ti, tj) from its products
-    auto emit = [&](auto kdiag, const f32x16& qk, const f32x16& kk) {
+    auto emit = [&](auto kdiag, const f32x16& qk, const f32x16& kk) __attribute__((always_inline)) {
       constexpr bool kDiag = decltype(kdiag)::value;
       const int ti = kDiag ? pr : 1, tj = kDiag ? pr : 0;
       const int i = 32 * ti + l32;                                // this lane's row
@@ -732,7 +785,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           pv[e] = (rowP * f) * qk[r];
           av[e] = (rowA * f) * kk[r];
         }
-        if constexpr (kPU16) {
+        if constexpr (kF16) {
           *reinterpret_cast<uint2*>(&sPh[PQ][i][kperm(mb)]) = make_uint2(cvt2h(pv[0], pv[1]), cvt2h(pv[2], pv[3]));
         } else {
           const uint32_t h0 = cvt2(pv[0], pv[1]), h1 = cvt2(pv[2], pv[3]);
@@ -770,9 +823,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         rk = i < n ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
       }
       const float gam = __expf(G);
-      sCR[PQ][i] = bt * gam * rk;                  // R = beta V - CR X
-      sCO[PQ][i] = p.scale * gam * rq;             // O = CO (Q S0^T) + P U
-      sCS[PQ][i] = __expf(GC - G) * rk;            // S1 = gamma_C S0 + K^T diag(CS) U
+      // (fp16 operands: r_k moves into K^, CO into Q^)
+      sCR[PQ][i] = kF16 ? bt * gam : bt * gam * rk;                  // R = beta V - CR X
+      sCO[PQ][i] = p.scale * gam * rq;                               // O = CO (Q S0^T) + P U
+      sCS[PQ][i] = kF16 ? __expf(GC - G) : __expf(GC - G) * rk;      // S1 = gamma_C S0 + K^T diag(CS) U
+      if constexpr (kF16) sRk[PQ][i] = rk;
       sBeta[PQ][i] = bt;
       if (i == 0) sGC[PQ][0] = __expf(GC);
       const float rowP = p.scale * rq, rowA = bt * rk;
@@ -787,10 +842,40 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sEFa[i] = rowA * F;
       arrive(&sSync[0]);
       emit(std::false_type{}, qk, kk);
+      if constexpr (kF16) arrive(&sSync[2]);   // raw Q, K of chunk cp read
     } else {
       tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
       wait_count(&sSync[0], pgen);
       emit(std::true_type{}, qk, kk);
+      if constexpr (kF16) arrive(&sSync[2]);
+    }
+  };
+
+  // fp16 operands: once the three Gram-tile producers have read chunk cp's raw Q and K
+  // (arrival count 3 per chunk), the four producers turn them in place into
+  // Q^ = diag(CO) Q and K^ = diag(r_k) K in fp16, 16 rows each (lane: 16-byte segment
+  // lane % 16 of row 4 j + lane / 16; the element order within a row is unchanged).
+  // The state waves read them in the next step.  Rows past the sequence end have
+  // CO = r_k = 0.
+  auto to_f16 = [&](int cp, auto parq) __attribute__((always_inline)) {
+    constexpr int PQ = decltype(parq)::value;
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    wait_count(&sSync[2], 3u * (uint32_t)(cp + 1));
+    const int pr = wu - NSW;
+    auto scaled = [](const uint4 w, float f) {
+      return make_uint4(cvt2h(bf_lo(w.x) * f, bf_hi(w.x) * f), cvt2h(bf_lo(w.y) * f, bf_hi(w.y) * f),
+                        cvt2h(bf_lo(w.z) * f, bf_hi(w.z) * f), cvt2h(bf_lo(w.w) * f, bf_hi(w.w) * f));
+    };
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * pr + 4 * jj + (lane_o >> 4);
+      const int o = r * DK + 8 * (lane_o & 15);
+      uint4* q = reinterpret_cast<uint4*>(&sQ[PQ][o]);
+      uint4* k = reinterpret_cast<uint4*>(&sK[PQ][o]);
+      const uint4 wq = *q, wk = *k;
+      *q = scaled(wq, sCO[PQ][r]);
+      *k = scaled(wk, sRk[PQ][r]);
     }
   };
 
@@ -799,7 +884,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // b), the two 16 -> 32 merges T10 = -T11 A10 T00 and the 32 -> 64 merge
   // T[32..63][0..31] = -T22 A21 T11.  Each merge reads its A block before it writes
   // the T block in its place.
-  auto finish_T = [&](auto parc) {
+  auto finish_T = [&](auto parc) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
@@ -865,46 +950,56 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 
   // ================================================================ step loop
   // Step c: the state waves consume chunk c while the producers prepare chunk c + 1.
-  auto step = [&](int c, auto parc) {
+  // Each role runs its own copy of the loop (kProd): the compiler's count of memory
+  // operations in flight, and the waits it derives for the landing, then follow one
+  // role's code only.
+  auto step = [&](int c, auto parc, auto rolep, auto firstp) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;     // parity of chunk c
     constexpr int PQ = PAR ^ 1;                    // parity of chunk c + 1
-    const bool hasS = c >= 0, hasP = c + 1 < nch;
-    lds_sync();                                    // previous step done
-    // Land the staged data (Q, K of c + 1; V, Z of c).  Staging loads are issued
-    // unconditionally (past the last chunk they re-read it, unused): a conditional
-    // load would merge with the old values and force a wait for it.
+    constexpr bool kProd = decltype(rolep)::value;
+    constexpr bool hasS = !decltype(firstp)::value;   // step -1 has no chunk to consume
+    const bool hasP = c + 1 < nch;
+    lds_sync();                                    // previous step done (the step's one barrier)
+    // Land the staged data (Q, K of c + 1; V, Z of c) and announce it.  Staging loads
+    // are issued unconditionally (past the last chunk they re-read it, unused): a
+    // conditional load would merge with the old values and force a wait for it.
     const int c1 = min(c + 1, nch - 1), c2 = min(c + 2, nch - 1);
     if (hasP) {
       rq_.template store<true>(sQ[PQ], si);
       rk_.template store<true>(sK[PQ], si);
     }
-    if (hasS) {
+    if constexpr (hasS) {
       rv_.template store<false>(sV, si);
       if constexpr (kSSD) {
         if (p.z) rz_.template store<false>(sZ, si);
       }
     }
-    if (!kGate && hasP && wu == 0) {
-      sGr[PQ][lane] = rg_;
-      sBr[PQ][lane] = rb_;
+    if constexpr (!kGate && !kProd) {
+      if (hasP && wu == 0) {
+        sGr[PQ][lane] = rg_;
+        sBr[PQ][lane] = rb_;
+      }
     }
-    if (isP) {   // (the state waves stage theirs in the middle of the step)
-      stage_qk(c2);
+    arrive(&sSync[3]);
+    if constexpr (kProd) {
+      stage_qk(c2);   // (the state waves stage theirs in the middle of the step)
       stage_v(c1);
-    }
-    lds_sync();                                    // landing done
-    if (isP) {
-      if (wu - NSW == 2) {   // T of chunk c (delta rule only)
+      if (wu - NSW == 2) {   // T of chunk c (delta rule only); reads nothing landed here
         if constexpr (!kSSD) {
-          if (hasS) finish_T(Par<PAR>{});
+          if constexpr (hasS) finish_T(Par<PAR>{});
         }
         gate_store(PAR);       // (gate folded in) chunk c + 2, staged in this landing
       } else if (hasP) {
+        wait_count(&sSync[3], 8u * (uint32_t)(c + 2));   // the landing of this step done
         produce(c + 1, Par<PQ>{});
       }
+      if constexpr (kF16) {
+        if (hasP) to_f16(c + 1, Par<PQ>{});
+      }
     } else {
-      if (hasS) consume(c, Par<PAR>{});
-      else {   // step -1: no chunk to consume, stage chunk 1's rows here
+      if constexpr (hasS) {
+        consume(c, Par<PAR>{});
+      } else {   // step -1: no chunk to consume, stage chunk 1's rows here
         stage_qk(c2);
         stage_v(c1);
       }
@@ -917,10 +1012,20 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // the loop has to cover them
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (wu == NSW + 2) gate_store(0);    // (gate folded in) chunk 0
-  for (int c = -1; c < nch && nch > 0; c += 2) {   // (an empty sequence only stores its state)
-    step(c, Par<1>{});                   // c odd (c = -1: landing and the first chunk's preparation only)
-    if (c + 1 < nch) step(c + 1, Par<0>{});
-  }
+  // Step -1 (landing and the first chunk's preparation only) runs before the loop and
+  // retires its loads, so that every step inside the loop has the same memory
+  // operations in flight at its landing.
+  auto run = [&](auto rolep) __attribute__((always_inline)) {
+    if (nch == 0) return;   // (an empty sequence only stores its state)
+    step(-1, Par<1>{}, rolep, std::true_type{});
+    if constexpr (!decltype(rolep)::value) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int c = 0; c < nch; c += 2) {
+      step(c, Par<0>{}, rolep, std::false_type{});
+      if (c + 1 < nch) step(c + 1, Par<1>{}, rolep, std::false_type{});
+    }
+  };
+  if (isP) run(std::true_type{});
+  else run(std::false_type{});
   if (!isP) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)

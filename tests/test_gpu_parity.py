@@ -220,6 +220,28 @@ def test_skipped_sequences_and_sentinels(gdn_lib):
     assert_close(got[[4, 7]], np.stack([fin[4], fin[7]]), "states")
 
 
+@pytest.mark.parametrize("decay", [1e-2, 1e-3])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_extend_long_memory(gdn_lib, decay, out_dtype):
+    """Weak decay (A_log shifted by log(decay)): the state keeps its history for
+    thousands of tokens, so the precision of the state operand of every chunk shows
+    in the outputs.  Both output types are held to the general float bar."""
+    gdn = gdn_lib
+    _announce(f"long memory decay x{decay} out={out_dtype}")
+    rng = np.random.default_rng(5)
+    A_log = (np.log(rng.uniform(1, 16, 4)) + np.log(decay)).astype(np.float32)
+    case = synth.make_gdn_case("long-memory", seed=11, lens=(1000, 777), has_init=(1, 1), H_qk=2, H_v=4,
+                               d_k=128, d_v=128, A_log=A_log, num_slots=5)
+    d = upload(case)
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = run_extend(gdn, case, d, out_dtype=odt)
+    torch.cuda.synchronize()
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale)
+    assert_close(out.float().cpu().numpy(), ref, "out")
+    assert_close(d["pool"].cpu().numpy()[case.slot], np.stack([fin[s] for s in case.slot]), "states")
+
+
 def test_has_init_zero_ignores_pool_content(gdn_lib):
     gdn = gdn_lib
     _announce("has_init=0 ignores pool")
