@@ -93,16 +93,17 @@ __device__ __forceinline__ uint2 tr_read(const u16* p) {
 // the LDS banks while every address stays an affine function of the lane.
 template <int D>
 __device__ __forceinline__ int pidx(int r, int c) { return r * (D + 8) + c; }
-// Q, K and the C x C operand tiles keep each 32-column block with its 4-column
-// groups in the order 0, 4, 1, 5, 2, 6, 3, 7, so that the 8 k slots of a 16x16x32
-// MFMA operand (columns 4g .. 4g+3 and 16+4g .. 16+4g+3 of a block, the order of the
-// accumulator rows) are 16 contiguous bytes.  Logical column -> stored column:
+// The C x C operand tiles keep each 32-column block with its 4-column groups in the
+// order 0, 4, 1, 5, 2, 6, 3, 7, so that the 8 k slots of a 16x16x32 MFMA operand
+// (columns 4g .. 4g+3 and 16+4g .. 16+4g+3 of a block, the order of the accumulator
+// rows) are 16 contiguous bytes.  Logical column -> stored column:
 __device__ __forceinline__ int kperm(int c) {
   const int q = (c >> 2) & 7;
   return (c & ~31) | ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
 }
-// Q and K tiles: rows of D bf16 without padding; the 16-byte chunk j of row r is
-// stored at chunk position j ^ qswz(r).  This keeps the state waves' operand reads
+// Q and K tiles: rows of D bf16 in natural column order without padding (the
+// state's accumulator rows are ordered to match, see Sacc); the 16-byte chunk j of
+// row r is stored at chunk position j ^ qswz(r).  This keeps the state waves' operand reads
 // (16 rows x 4 chunks per instruction) and their transpose reads free of LDS bank
 // conflicts (the producers' 32-row reads see two-way conflicts).
 __device__ __forceinline__ int qswz(int r) { return (((r & 3) << 2) ^ r) & 15; }
@@ -227,12 +228,11 @@ struct TileRegs {
     const uint32_t off = ((uint32_t)(r < n ? r : 0) * (uint32_t)gs + 8u * (uint32_t)c) * 2u;
     return *reinterpret_cast<const uint4*>(base + off);
   }
-  template <bool kPerm>
+  template <bool kSwz>
   __device__ __forceinline__ static void st(u16* tile, int si, int i, uint4 v) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
-    if constexpr (kPerm) {   // the two 4-column halves land in separate groups
-      *reinterpret_cast<uint2*>(tile + qidx<D>(r, kperm(8 * c))) = make_uint2(v.x, v.y);
-      *reinterpret_cast<uint2*>(tile + qidx<D>(r, kperm(8 * c + 4))) = make_uint2(v.z, v.w);
+    if constexpr (kSwz) {   // Q and K tiles: unpadded rows, swizzled 16-byte chunks
+      *reinterpret_cast<uint4*>(tile + qidx<D>(r, 8 * c)) = v;
     } else {
       *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
     }
@@ -348,7 +348,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   };
   const uint32_t ostride_b = (uint32_t)p.out_stride * (uint32_t)sizeof(OutT);
 
-  // S^T tiles in 16x16 accumulator layout: Sacc[ct][tk][r] = S[col_ct][16 tk + 4 g16 + r]
+  // S^T tiles in 16x16 accumulator layout: Sacc[ct][tk][r] = S[col_ct][dk(tk) + 8 g16 + r]
+  // with dk(tk) = 32 (tk / 2) + 4 (tk % 2): the two tiles 2 s2, 2 s2 + 1 together hold
+  // d_k 32 s2 + 8 g16 + 0..7 in a lane, the natural column order of the Q, K tiles.
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
   f32x4 Sacc[CT][NTK];
 #pragma unroll
@@ -358,7 +360,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       Sacc[ct][tk] = f32x4{};
       if (!isP && init) {
         const int col = CW * wu + 16 * ct + j16;
-        const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16);
+        const float4 v = *reinterpret_cast<const float4*>(state + (int64_t)col * DK + 32 * (tk >> 1) + 4 * (tk & 1) + 8 * g16);
         Sacc[ct][tk] = f32x4{v.x, v.y, v.z, v.w};
       }
     }
@@ -496,7 +498,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
     } else {
-      bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 16 (e / 4) + 4 g16 + e % 4
+      bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 8 g16 + e
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -679,7 +681,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
           for (int e = 0; e < 4; ++e) U[ct][rt][e] *= f4get(cs, e);
       }
-      // A operand K^T: row d_k = 16 tk + j16; k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
+      // A operand K^T: row j16 = d_k 32 (tk / 2) + 8 (j16 / 4) + 4 (tk % 2) + j16 % 4 (the
+      // state's row order; a transpose read may take its four 4-column chunks from
+      // anywhere); k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
       const int rb = 4 * g16 + (j16 >> 2);
       if constexpr (kF16) {   // K^^T (r_k folded in) times the scaled U, fp16
         f16x8 Wf[CT][2];
@@ -691,7 +695,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         for (int tk = 0; tk < NTK; ++tk) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
-          const int ca = kperm(16 * tk + 4 * (j16 & 3));
+          const int ca = 32 * (tk >> 1) + 8 * (j16 & 3) + 4 * (tk & 1);   // A row j16 = d_k ca + j16 % 4
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             const f16x8 kt = __builtin_bit_cast(f16x8, join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca)));
@@ -709,7 +713,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         for (int tk = 0; tk < NTK; ++tk) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) Sacc[ct][tk] *= gC;
-          const int ca = kperm(16 * tk + 4 * (j16 & 3));
+          const int ca = 32 * (tk >> 1) + 8 * (j16 & 3) + 4 * (tk & 1);   // A row j16 = d_k ca + j16 % 4
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             const bf16x8 kt = join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca));
@@ -1032,7 +1036,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
       for (int tk = 0; tk < NTK; ++tk) {
         const int col = CW * wu + 16 * ct + j16;
-        *reinterpret_cast<float4*>(state + (int64_t)col * DK + 16 * tk + 4 * g16) =
+        *reinterpret_cast<float4*>(state + (int64_t)col * DK + 32 * (tk >> 1) + 4 * (tk & 1) + 8 * g16) =
             make_float4(Sacc[ct][tk][0], Sacc[ct][tk][1], Sacc[ct][tk][2], Sacc[ct][tk][3]);
       }
   }
