@@ -305,8 +305,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 2][4][16 * 20 + 16];
   // vectors of the chunk being prepared, per token (see the producer roles)
   __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
+  __shared__ __attribute__((aligned(16))) float sNq[C], sNk[C];   // squared row norms of q, k
   // arrival counters: chunk vectors ready, T ready, raw Q/K read, landing done
-  __shared__ uint32_t sSync[4];
+  __shared__ uint32_t sSync[8];
 
   const int h = blockIdx.x;
   const int nseq = blockIdx.y;
@@ -745,17 +746,44 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   uint32_t pgen = 0;                          // chunks prepared so far (uniform)
   constexpr float kLog2e = 1.4426950408889634f;
 
+  // T = (I + A)^{-1} in place of A, in two parts.  The diagonal 16x16 blocks 2 t,
+  // 2 t + 1 in fp32, by the wave that emitted diagonal tile t, right after it (lane
+  // 16 b' + c of the lower half-wave solves column c of block 2 t + b'); the blocks of
+  // A it reads were written by the same wave.
+  auto solve_diag = [&](auto parq, int t) __attribute__((always_inline)) {
+    constexpr int PQ = decltype(parq)::value;
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    lds_order();
+    const int b = 2 * t + ((lane_o >> 4) & 1), c = lane_o & 15;   // (the upper half-wave repeats the lower)
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[PQ][b][20 * mm + i] * x[i];
+    if (lane_o < 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
+    }
+  };
   // Prepare chunk cp (buffers of parity PQ): its vectors, P (fp16, or bf16 hi + lo), and A stored in
   // T's buffer (bf16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
   // (pr = wave - NSW):
   //   pr 3:    the off-diagonal tile's products, then the chunk's vectors (lane =
-  //            token): decay cumsum, row norms, the coefficient vectors and the decay
+  //            token): decay cumsum, row norms (from the squared norms that pr 0, 1
+  //            provide), the coefficient vectors and the decay
   //            factors of the tiles; then the off-diagonal tile (rows 32..63, keys
   //            0..31), whose decay factors into a row and a key factor split at token
   //            31 (both <= 1);
-  //   pr 0, 1: diagonal tile t = pr (one exp per element).
-  // Entries of A on and above the diagonal are not needed; those inside the diagonal
-  // 32x32 tiles come out as zeros or are overwritten by T's diagonal blocks.
+  //   pr 0, 1: diagonal tile t = pr: its products, the squared norms of its 32 rows
+  //            of q and k, then P and A (one exp per element) and the two diagonal
+  //            16x16 blocks of T = (I + A)^{-1} inside it.
+  // Every Gram-tile producer announces on an arrival counter when it has read the raw
+  // Q, K of the chunk (for their in-place fp16 conversion).  Entries of A on and above
+  // the diagonal are not needed; those inside the diagonal 32x32 tiles come out as
+  // zeros or are overwritten by T's diagonal blocks.
   auto produce = [&](int cp, auto parq) __attribute__((always_inline)) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
@@ -816,15 +844,10 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
       const float G31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 31));
       float rq = i < n ? 1.f : 0.f, rk = rq;
-      if constexpr (!kSSD) {   // 1 / |row| of q_i and k_i (zero past the end)
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int s = 0; s < DK / 8; ++s) {
-          sq = sumsq8(ldq8<DK>(Q, i, 8 * s), sq);
-          sk = sumsq8(ldq8<DK>(K, i, 8 * s), sk);
-        }
-        rq = i < n ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 0.f;   // 1 ulp
-        rk = i < n ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 0.f;
+      if constexpr (!kSSD) {   // 1 / |row| of q_i and k_i (zero past the end), from the squared norms
+        wait_count(&sSync[4], 2u * (uint32_t)(cp + 1));
+        rq = i < n ? __builtin_amdgcn_rsqf(sNq[i] + 1e-6f) : 0.f;   // 1 ulp
+        rk = i < n ? __builtin_amdgcn_rsqf(sNk[i] + 1e-6f) : 0.f;
       }
       const float gam = __expf(G);
       // (fp16 operands: r_k moves into K^, CO into Q^)
@@ -845,35 +868,54 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sEF[i] = (i < 32 ? rk : rowP) * F;
       sEFa[i] = rowA * F;
       arrive(&sSync[0]);
+      arrive(&sSync[2]);   // raw Q, K of chunk cp read (tile operands, norms)
       emit(std::false_type{}, qk, kk);
-      if constexpr (kF16) arrive(&sSync[2]);   // raw Q, K of chunk cp read
     } else {
       tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
+      if constexpr (!kSSD) {
+        // squared norms of the tile's 32 rows for the vectors: |k_i|^2 is the diagonal
+        // of K K^T (held by the lane with hh = bit 2 of l32), |q_i|^2 two half-row sums
+        const int i = 32 * pr + l32;
+        if (hh == ((l32 >> 2) & 1)) {
+          const int rd = 4 * (l32 >> 3) + (l32 & 3);
+          float d = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) d = r == rd ? kk[r] : d;
+          sNk[i] = d;
+        }
+        float sq = 0.f;
+#pragma unroll
+        for (int s = 0; s < DK / 16; ++s) sq = sumsq8(ldq8<DK>(Q, i, (DK / 2) * hh + 8 * s), sq);
+        sq += __shfl_xor(sq, 32);
+        if (hh == 0) sNq[i] = sq;
+        arrive(&sSync[4]);
+      }
+      arrive(&sSync[2]);   // raw Q, K of chunk cp read (tile operands, q norms)
       wait_count(&sSync[0], pgen);
       emit(std::true_type{}, qk, kk);
-      if constexpr (kF16) arrive(&sSync[2]);
+      if constexpr (!kSSD) solve_diag(Par<PQ>{}, pr);
     }
   };
 
   // fp16 operands: once the three Gram-tile producers have read chunk cp's raw Q and K
-  // (arrival count 3 per chunk), the four producers turn them in place into
-  // Q^ = diag(CO) Q and K^ = diag(r_k) K in fp16, 16 rows each (lane: 16-byte segment
-  // lane % 16 of row 4 j + lane / 16; the element order within a row is unchanged).
-  // The state waves read them in the next step.  Rows past the sequence end have
-  // CO = r_k = 0.
-  auto to_f16 = [&](int cp, auto parq) __attribute__((always_inline)) {
+  // (arrival count 3 per chunk) and its vectors are out, Q and K are turned in place
+  // into Q^ = diag(CO) Q and K^ = diag(r_k) K in fp16, rows r0 .. r0 + 31 by one wave
+  // (lane: 16-byte segment lane % 16 of row r0 + 4 j + lane / 16; the element order
+  // within a row is unchanged).  The state waves read them in the next step.  Rows past
+  // the sequence end have CO = r_k = 0.
+  auto to_f16 = [&](int cp, auto parq, int r0) __attribute__((always_inline)) {
     constexpr int PQ = decltype(parq)::value;
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
     wait_count(&sSync[2], 3u * (uint32_t)(cp + 1));
-    const int pr = wu - NSW;
+    wait_count(&sSync[0], (uint32_t)(cp + 1));
     auto scaled = [](const uint4 w, float f) {
       return make_uint4(cvt2h(bf_lo(w.x) * f, bf_hi(w.x) * f), cvt2h(bf_lo(w.y) * f, bf_hi(w.y) * f),
                         cvt2h(bf_lo(w.z) * f, bf_hi(w.z) * f), cvt2h(bf_lo(w.w) * f, bf_hi(w.w) * f));
     };
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = 16 * pr + 4 * jj + (lane_o >> 4);
+#pragma unroll 2   // (fully unrolled, the loads of all rows would be hoisted at once)
+    for (int jj = 0; jj < 8; ++jj) {
+      const int r = r0 + 4 * jj + (lane_o >> 4);
       const int o = r * DK + 8 * (lane_o & 15);
       uint4* q = reinterpret_cast<uint4*>(&sQ[PQ][o]);
       uint4* k = reinterpret_cast<uint4*>(&sK[PQ][o]);
@@ -883,31 +925,17 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
   };
 
-  // T = (I + A)^{-1} of chunk c in place of A (buffers of parity PAR), one wave:
-  // the four diagonal 16x16 blocks in fp32 (lane 16 b + c solves column c of block
-  // b), the two 16 -> 32 merges T10 = -T11 A10 T00 and the 32 -> 64 merge
-  // T[32..63][0..31] = -T22 A21 T11.  Each merge reads its A block before it writes
-  // the T block in its place.
-  auto finish_T = [&](auto parc) __attribute__((always_inline)) {
+  // Then, early in the step that consumes the chunk, one wave merges them: the two
+  // 16 -> 32 merges T10 = -T11 A10 T00 and the 32 -> 64 merge T[32..63][0..31] =
+  // -T22 A21 T11.  Each merge reads its A block before it writes the T block in its
+  // place.
+  auto merge_T = [&](auto parc) __attribute__((always_inline)) {
     constexpr int PAR = decltype(parc)::value;
     int lane_o = lane;
     asm volatile("" : "+v"(lane_o));
     const int l32 = lane_o & 31, hh = lane_o >> 5;
     const int g16 = lane_o >> 4, j16 = lane_o & 15;
     auto T = sTb[PAR];
-    {
-      const int b = g16, c = j16;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[PAR][b][20 * mm + i] * x[i];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) T[16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
-    }
-    lds_order();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t
       const int r0 = 32 * t;
@@ -990,15 +1018,18 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       stage_v(c1);
       if (wu - NSW == 2) {   // T of chunk c (delta rule only); reads nothing landed here
         if constexpr (!kSSD) {
-          if constexpr (hasS) finish_T(Par<PAR>{});
+          if constexpr (hasS) merge_T(Par<PAR>{});
         }
         gate_store(PAR);       // (gate folded in) chunk c + 2, staged in this landing
+        if constexpr (kF16) {
+          if (hasP) to_f16(c + 1, Par<PQ>{}, 32);
+        }
       } else if (hasP) {
         wait_count(&sSync[3], 8u * (uint32_t)(c + 2));   // the landing of this step done
         produce(c + 1, Par<PQ>{});
-      }
-      if constexpr (kF16) {
-        if (hasP) to_f16(c + 1, Par<PQ>{});
+        if constexpr (kF16) {
+          if (wu - NSW == 3) to_f16(c + 1, Par<PQ>{}, 0);
+        }
       }
     } else {
       if constexpr (hasS) {
@@ -1011,7 +1042,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   };
 
   if (nch > 0) stage_qk(0);
-  if (tid < 4) sSync[tid] = 0u;   // visible to all after the first barrier
+  if (tid < 8) sSync[tid] = 0u;   // visible to all after the first barrier
   // entry state and first staged loads retired on every path here, so no wait inside
   // the loop has to cover them
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
