@@ -8,7 +8,7 @@
 //
 //   A  = strict_lower( beta_i r_k,i r_k,m Gam_im (K K^T)_im ),   T = (I + A)^{-1}
 //   X  = K S0^T,   R = diag(beta) V - diag(beta gamma r_k) X      (first-order innovations)
-//   U  = T R = (R - bf16(R)) + T bf16(R)                           (delta-rule corrected values)
+//   U  = T R = R + (T - I) bf16(R)                                 (delta-rule corrected values)
 //   O  = diag(scale gamma r_q) Q S0^T + P U,  P = lower( scale r_q,i r_k,m Gam_im (Q K^T)_im )
 //   S1 = gamma_C S0 + U^T diag(exp(G_C - G_i) r_k,i) K
 //
@@ -475,27 +475,28 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     // holds 4 consecutive output columns of one token (8-byte stores).
     f32x4 Y[CT][4], U[CT][4];
     if constexpr (kF16) {   // Y = Q^ S0^T (CO folded in), X = K^ S0^T (r_k folded in)
-      f16x8 Sb[CT][NKS];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int s2 = 0; s2 < NKS; ++s2) Sb[ct][s2] = pair_to_op_h(Sacc[ct][2 * s2], Sacc[ct][2 * s2 + 1]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           Y[ct][rt] = f32x4{};
           U[ct][rt] = f32x4{};
         }
-        const int row = 16 * rt + j16;
+      // k-steps outermost: one k-step's S0 operand is live at a time
 #pragma unroll
-        for (int s2 = 0; s2 < NKS; ++s2) {
+      for (int s2 = 0; s2 < NKS; ++s2) {
+        f16x8 Sb[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Sb[ct] = pair_to_op_h(Sacc[ct][2 * s2], Sacc[ct][2 * s2 + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int row = 16 * rt + j16;
           const f16x8 aq = __builtin_bit_cast(f16x8, ldq8<DK>(Q, row, 32 * s2 + 8 * g16));
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632h(Sb[ct][s2], aq, Y[ct][rt]);
+          for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632h(Sb[ct], aq, Y[ct][rt]);
           const f16x8 ak = __builtin_bit_cast(f16x8, ldq8<DK>(K, row, 32 * s2 + 8 * g16));
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632h(ak, Sb[ct][s2], U[ct][rt]);
+          for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632h(ak, Sb[ct], U[ct][rt]);
         }
       }
     } else {
@@ -553,25 +554,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
     if constexpr (!kSSD) {
       wait_count(&sSync[1], (uint32_t)(c + 1));   // T of chunk c (finished in this step)
-      // U = (R - bf16(R)) + T bf16(R); T is unit lower: row tile rt needs k-steps <= rt / 2
+      // U = T R = R + L bf16(R) with L = T - I (stored with a zero diagonal): R stays
+      // exact in the accumulator; L is strictly lower, so row tile rt needs k-steps <= rt / 2
       bf16x8 Rb[CT][2];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          f32x4& u0 = U[ct][2 * s2];
-          f32x4& u1 = U[ct][2 * s2 + 1];
-          Rb[ct][s2] = pair_to_op(u0, u1);
-          const uint4 rw = __builtin_bit_cast(uint4, Rb[ct][s2]);
-          u0[0] = sub_bf_lo(rw.x, u0[0]);
-          u0[1] = sub_bf_hi(rw.x, u0[1]);
-          u0[2] = sub_bf_lo(rw.y, u0[2]);
-          u0[3] = sub_bf_hi(rw.y, u0[3]);
-          u1[0] = sub_bf_lo(rw.z, u1[0]);
-          u1[1] = sub_bf_hi(rw.z, u1[1]);
-          u1[2] = sub_bf_lo(rw.w, u1[2]);
-          u1[3] = sub_bf_hi(rw.w, u1[3]);
-        }
+        for (int s2 = 0; s2 < 2; ++s2) Rb[ct][s2] = pair_to_op(U[ct][2 * s2], U[ct][2 * s2 + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
@@ -977,6 +966,10 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
       for (int r = 0; r < 16; ++r) T[32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
     }
+    // the state waves apply L = T - I (U = R + L bf16(R)): the unit diagonal, needed by
+    // the merges above, is stored as zero once they are done
+    lds_order();
+    T[lane_o][kperm(lane_o)] = 0;
     arrive(&sSync[1]);
   };
 
