@@ -1,4 +1,4 @@
-// Chunked GDN extend kernel (bf16 inputs, fp32 state), MFMA bf16 -> fp32 on gfx950.
+// Chunked GDN extend kernel (bf16 inputs, fp32 state), MFMA bf16/fp16 -> fp32 on gfx950.
 //
 // Chunked form of the gated delta rule (Gated DeltaNet, ICLR 2025; the WY / UT
 // representation of products of generalised Householder transitions).  Within a
@@ -15,37 +15,41 @@
 // Delta-off mode (Mamba2 SSD, flashinfer.mamba.ssd_combined_fwd): no norms, T = I,
 // U = diag(dt') X, scale 1, then O += D x and O *= silu(z).
 //
-// Precision: q, k, v enter the MFMAs as their exact bf16 values; norms, beta and
-// decays are fp32 row/column scalings applied around the products; S0, T and the
-// correction operand bf16(R) are single bf16 operands; the state update uses two-term
-// (hi + lo) bf16 splits of the scaled U.  P U takes single fp16 operands when the
-// output is bf16 (|P| <= scale; fp16's 11-bit significand keeps its error below the
-// output rounding) and two-term bf16 splits of P and U otherwise.
+// Precision.  bf16 output: the state waves take Q^ = diag(CO) Q and K^ = diag(r_k) K,
+// S0, P, U and the scaled U of the state update as single fp16 operands (each bounded
+// by construction or by the values; fp16's 11-bit significand keeps every product's
+// rounding below the output's bf16 rounding).  fp32 output and the delta-off mode:
+// q, k, v enter the MFMAs as their exact bf16 values, norms, beta and decays are fp32
+// scalings around the products, S0 is a single bf16 operand and P U and the state
+// update use two-term (hi + lo) bf16 splits.  T and the correction operand bf16(R)
+// are bf16 in both.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
 // order.  Two kinds of waves run side by side:
 //  * state waves own 32 d_v columns each (16 in delta-off mode; state rows are
-//    independent given the chunk's keys); the state never leaves their registers, held as S^T tiles in
-//    16x16 MFMA accumulator layout and fed back as B operands directly (the
-//    reduction index of an MFMA may be permuted freely when both operands agree, so
-//    A operands are read from LDS in the accumulator's row order).  In the step for
-//    chunk c they compute X, Y, R, U, O and the new state: only the state-dependent
-//    part, with no barrier inside (they wait once, for T of chunk c).
-//  * four producer waves run meanwhile: three prepare chunk c + 1 (decay cumsum,
-//    row norms and the per-token coefficient vectors; Q K^T and K K^T tiles -> P
-//    and A), the fourth turns chunk c's A into T = (I + A)^{-1} in place,
-//    early in the step, before the state waves need it.
+//    independent given the chunk's keys); the state never leaves their registers,
+//    held as S^T tiles in 16x16 MFMA accumulator layout and fed back as B operands
+//    directly (the reduction index of an MFMA may be permuted freely when both
+//    operands agree, so the accumulator's rows are ordered to match the A operands'
+//    reads from LDS).  In the step for chunk c they compute X, Y, R, U, O and the new
+//    state: only the state-dependent part, with no barrier inside.
+//  * four producer waves run meanwhile on chunk c + 1: the Q K^T and K K^T tiles,
+//    row norms, decay cumsum and the per-token coefficient vectors, P and A, the
+//    diagonal blocks of T = (I + A)^{-1}, the in-place fp16 conversion of Q and K;
+//    and, early in step c, the merges that finish chunk c's T.
 // The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
 // step ahead.
 // Each step has one workgroup barrier, which ends the previous step; the landing of
-// the staged rows that follows is announced on an arrival counter, so the state
-// waves start on chunk c (its Q and K landed a step earlier) while it is under way.  P, T and the coefficients are double-buffered, and so are Q and K (chunk c
-// for the state waves, c + 1 for the producers).
+// the staged rows that follows, like every other hand-off, is announced on an LDS
+// arrival counter, so the state waves start on chunk c (its Q and K landed a step
+// earlier) while it is under way.  P, T and the coefficients are double-buffered,
+// and so are Q and K (chunk c for the state waves, c + 1 for the producers).
 //
-// Data layout in LDS: tiles are row-major and padded by one 16-byte segment per
-// row.  K^T and V^T operands come from the row-major tiles through the LDS
-// transpose read (ds_read_b64_tr_b16): lane j of each 16-lane group receives column
-// c0 + j of the four rows addressed by the group's lanes 4e + j/4.
+// Data layout in LDS: tiles are row-major; V, Z and the C x C tiles padded per row,
+// Q and K unpadded with swizzled 16-byte chunks.  K^T and V^T operands come from the
+// row-major tiles through the LDS transpose read (ds_read_b64_tr_b16): lane j of each
+// 16-lane group receives column c0 + j of the four rows addressed by the group's
+// lanes 4e + j/4.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
