@@ -770,8 +770,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   //            factors of the tiles; then the off-diagonal tile (rows 32..63, keys
   //            0..31), whose decay factors into a row and a key factor split at token
   //            31 (both <= 1);
-  //   pr 0, 1: diagonal tile t = pr: its products, the squared norms of its 32 rows
-  //            of q and k, then P and A (one exp per element) and the two diagonal
+  //   pr 0, 1: diagonal tile t = pr: the squared norms of its 32 rows of q and k, its
+  //            products, then P and A (one exp per element) and the two diagonal
   //            16x16 blocks of T = (I + A)^{-1} inside it.
   // Every Gram-tile producer announces on an arrival counter when it has read the raw
   // Q, K of the chunk (for their in-place fp16 conversion).  Entries of A on and above
@@ -864,26 +864,26 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       arrive(&sSync[2]);   // raw Q, K of chunk cp read (tile operands, norms)
       emit(std::false_type{}, qk, kk);
     } else {
-      tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
       if constexpr (!kSSD) {
-        // squared norms of the tile's 32 rows for the vectors: |k_i|^2 is the diagonal
-        // of K K^T (held by the lane with hh = bit 2 of l32), |q_i|^2 two half-row sums
+        // squared norms of the tile's 32 rows (two half-row sums each), ahead of its
+        // products: the chunk's vectors wait for them
         const int i = 32 * pr + l32;
-        if (hh == ((l32 >> 2) & 1)) {
-          const int rd = 4 * (l32 >> 3) + (l32 & 3);
-          float d = 0.f;
+        float sq = 0.f, sk = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) d = r == rd ? kk[r] : d;
-          sNk[i] = d;
+        for (int s = 0; s < DK / 16; ++s) {
+          sq = sumsq8(ldq8<DK>(Q, i, (DK / 2) * hh + 8 * s), sq);
+          sk = sumsq8(ldq8<DK>(K, i, (DK / 2) * hh + 8 * s), sk);
         }
-        float sq = 0.f;
-#pragma unroll
-        for (int s = 0; s < DK / 16; ++s) sq = sumsq8(ldq8<DK>(Q, i, (DK / 2) * hh + 8 * s), sq);
         sq += __shfl_xor(sq, 32);
-        if (hh == 0) sNq[i] = sq;
+        sk += __shfl_xor(sk, 32);
+        if (hh == 0) {
+          sNq[i] = sq;
+          sNk[i] = sk;
+        }
         arrive(&sSync[4]);
       }
-      arrive(&sSync[2]);   // raw Q, K of chunk cp read (tile operands, q norms)
+      tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
+      arrive(&sSync[2]);   // raw Q, K of chunk cp read (norms, tile operands)
       wait_count(&sSync[0], pgen);
       emit(std::true_type{}, qk, kk);
       if constexpr (!kSSD) solve_diag(Par<PQ>{}, pr);
