@@ -78,7 +78,8 @@ def l2_normalize(x, eps=1e-6):
 
 # ---------------------------------------------------------------- GDN layer
 def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
-               scale, eps=1e-6, heads=None, seqs=None):
+               scale, eps=1e-6, heads=None, seqs=None, ckpt_token=None, ckpt_slot=None,
+               ckpts=None):
     """Packed-varlen GDN extend, token by token.
 
     q, k : [T, H_qk, d_k]; v : [T, H_v, d_v]; a, b : [T, H_v]
@@ -86,6 +87,13 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
     pool : anything indexable as pool[slot] -> [H_v, d_v, d_k] (initial states).
     heads : optional list of v-heads to compute (heads are independent);
     seqs  : optional list of sequence indices to compute.
+    ckpt_token, ckpt_slot : optional [N] state checkpoints after the
+      checkpoint_token_indices / checkpoint_state_slots arguments of the
+      ssd_combined_fwd page: sequence n records the state after its tokens before
+      the absolute token index ckpt_token[n] (an exclusive boundary in
+      [cu[n], cu[n+1]]) under the key ckpt_slot[n] of the dict `ckpts`; a negative
+      entry (either one), a skipped sequence or a boundary outside the sequence
+      records nothing.
 
     Returns (out, written, finals):
       out     float64 [T, len(heads), d_v]   (NaN where not written)
@@ -116,11 +124,16 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
         if s < 0:
             continue
         t0, t1 = int(cu[n]), int(cu[n + 1])
+        ck = -1
+        if ckpt_token is not None and int(ckpt_token[n]) >= 0 and int(ckpt_slot[n]) >= 0:
+            ck = int(ckpt_token[n])
         if has_init[n]:
             S = np.array(pool[s], dtype=F64)[hsel].copy()          # [Hs, d_v, d_k]
         else:
             S = np.zeros((len(heads), d_v, d_k), dtype=F64)
         for t in range(t0, t1):
+            if t == ck:                                            # state before token t
+                ckpts[int(ckpt_slot[n])] = S.copy()
             log_g, beta = gdn_gate(np.asarray(a[t:t + 1])[:, hsel], np.asarray(b[t:t + 1])[:, hsel],
                                    np.asarray(A_log)[hsel], np.asarray(dt_bias)[hsel])
             g = np.exp(log_g[0])[:, None, None]                    # [Hs,1,1]
@@ -133,6 +146,8 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
             S = S + np.einsum("hv,hk->hvk", bt * (vt - u), kh)     # delta-rule write
             out[t] = scale * np.einsum("hvk,hk->hv", S, qh)        # read with S_t
             written[t] = True
+        if ck == t1:                                               # boundary at the end
+            ckpts[int(ckpt_slot[n])] = S.copy()
         finals[s] = S
     return out, written, finals
 
@@ -160,7 +175,7 @@ def apply_final_states(pool, finals, heads=None):
 # ---------------------------------------------------------------- delta-off (SSD) mode
 def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
                  dt_limit=(0.0, float("inf")), initial_states=None, return_final_states=True,
-                 heads=None):
+                 heads=None, ckpt_token=None, ckpt_slot=None, ckpts=None):
     """Mamba2 SSD scan, token by token, batched mode of ssd_combined_fwd.
 
     x [batch, L, H, P], dt [batch, L, H], A [H], B/C [batch, L, G, N],
@@ -171,6 +186,9 @@ def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False
         S   = exp(dt' A) S + dt' x_t B_t^T            ([P, N] per head)
         y_t = S C_t + D x_t ;  out_t = y_t * silu(z_t)
     Returns (out float64 [batch, L, Hs, P], final float64 [batch, Hs, P, N] | None).
+    ckpt_token, ckpt_slot : optional [batch] checkpoints as in gdn_extend, with the
+    boundary relative to the batch element's first token (batched mode of the
+    ssd_combined_fwd page); the states go to the dict `ckpts`.
     """
     x = np.asarray(x)
     batch, L, H, P = x.shape
@@ -190,7 +208,12 @@ def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False
             S = np.zeros((len(heads), P, Nst), dtype=F64)
         else:
             S = np.array(initial_states[bi], dtype=F64)[hsel].copy()
+        ck = -1
+        if ckpt_token is not None and int(ckpt_token[bi]) >= 0 and int(ckpt_slot[bi]) >= 0:
+            ck = int(ckpt_token[bi])
         for t in range(L):
+            if t == ck:
+                ckpts[int(ckpt_slot[bi])] = S.copy()
             log_g, dtp = ssd_gate(np.asarray(dt[bi, t], dtype=F64)[hsel],
                                   np.asarray(A, dtype=F64)[hsel], bias, dt_softplus, dt_limit)
             xt = np.asarray(x[bi, t], dtype=F64)[hsel]             # [Hs, P]
@@ -204,5 +227,7 @@ def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False
                 zt = np.asarray(z[bi, t], dtype=F64)[hsel]
                 y = y * zt * sigmoid(zt)
             out[bi, t] = y
+        if ck == L:
+            ckpts[int(ckpt_slot[bi])] = S.copy()
         finals[bi] = S
     return out, (finals if return_final_states else None)

@@ -505,3 +505,85 @@ def test_generators_shapes_and_rounding():
     assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0078125 and np.isinf(r[4])
     c = synth.edge_case("e", (3, 2))
     assert np.array_equal(synth.bf16_round(c.mixed_qkv), c.mixed_qkv)
+
+
+# ------------------------------------------------------------------ state checkpoints
+def _dense_prefix_state(c, n, h, b):
+    """State of sequence n, head h after its tokens before absolute index b, by the
+    dense transition-matrix recurrence (independent of the oracle's loop)."""
+    r = c.H_v // c.H_qk
+    j = h // r
+    S = c.pool[c.slot[n], h].astype(np.float64) if c.has_init[n] else np.zeros((c.d_v, c.d_k))
+    for t in range(int(c.cu_seqlens[n]), b):
+        sp = np.logaddexp(0.0, float(c.a[t, h]) + float(c.dt_bias[h]))
+        g = np.exp(-np.exp(float(c.A_log[h])) * sp)
+        beta = scipy.special.expit(float(c.b[t, h]))
+        kk = c.k[t, j].astype(np.float64)
+        kk = kk / np.sqrt(kk @ kk + 1e-6)
+        S = S @ (g * (np.eye(c.d_k) - beta * np.outer(kk, kk))) + beta * np.outer(c.v[t, h].astype(np.float64), kk)
+    return S
+
+
+def test_checkpoint_states_every_boundary():
+    """A checkpoint at exclusive boundary b holds the state after the sequence's tokens
+    before b, for every b from the first token (the initial state, or zeros) to the end
+    (the final state); the outputs and final states are unchanged by capturing."""
+    c = tiny_case(lens=(5, 3, 4), has_init=(1, 0, 1))
+    ref_out, _, ref_fin = _run(oracle.gdn_extend, c)
+    for n in range(c.N):
+        t0, t1 = int(c.cu_seqlens[n]), int(c.cu_seqlens[n + 1])
+        for b in range(t0, t1 + 1):
+            tok = np.full(c.N, -1, np.int64)
+            tok[n] = b
+            ck_slot = np.full(c.N, -1, np.int64)
+            ck_slot[n] = 7
+            ck = {}
+            out, _, fin = _run(oracle.gdn_extend, c, ckpt_token=tok, ckpt_slot=ck_slot, ckpts=ck)
+            assert list(ck) == [7]
+            for h in range(c.H_v):
+                _close(ck[7][h], _dense_prefix_state(c, n, h, b))
+            _close(out, ref_out)
+            for s in fin:
+                _close(fin[s], ref_fin[s])
+        _close(ck[7], ref_fin[c.slot[n]])            # b = end: the final state
+
+
+def test_checkpoint_disabled_entries():
+    """Negative boundary or slot, a skipped sequence, or a boundary outside the
+    sequence records nothing; several sequences record into their own rows."""
+    c = tiny_case(lens=(5, 3, 4), has_init=(1, 0, 1))
+    cu = c.cu_seqlens
+    ck = {}
+    _run(oracle.gdn_extend, c, ckpt_token=np.array([-1, cu[1] + 1, cu[2] + 2]),
+         ckpt_slot=np.array([0, -1, 4]), ckpts=ck)
+    assert list(ck) == [4]
+    c.slot[2] = -1
+    ck = {}
+    _run(oracle.gdn_extend, c, ckpt_token=np.array([cu[0] + 2, cu[1] + 4, cu[2] + 2]),
+         ckpt_slot=np.array([1, 2, 3]), ckpts=ck)
+    assert list(ck) == [1]                           # seq 1: 4 > its 3 tokens; seq 2 skipped
+
+
+def test_ssd_checkpoint_relative_boundary():
+    """Delta-off checkpoints (batched, boundary relative to the batch element): the
+    state after the first b tokens is gamma_b S0 + sum_{j<b} exp(G_{b-1} - G_j) dt'_j x_j B_j^T."""
+    c = _ssd_small(initial=True, with_D=False, with_z=False)
+    H = c.x.shape[2]
+    G = c.B.shape[2]
+    L = c.x.shape[1]
+    for b in (0, 1, 4, L):
+        ck = {}
+        oracle.ssd_combined(c.x, c.dt, c.A, c.B, c.C, None, None, c.dt_bias, True, (0.0, np.inf),
+                            c.initial_states, True, ckpt_token=np.array([b, -1]),
+                            ckpt_slot=np.array([5, 6]), ckpts=ck)
+        assert list(ck) == [5]
+        for h in range(H):
+            dtp = np.logaddexp(0.0, c.dt[0, :b, h].astype(np.float64) + c.dt_bias[h])
+            Gc = np.cumsum(dtp * c.A[h])
+            Gb = Gc[-1] if b else 0.0
+            S = np.exp(Gb) * c.initial_states[0, h].astype(np.float64)
+            if b:
+                X = c.x[0, :b, h].astype(np.float64)
+                Bm = c.B[0, :b, h // (H // G)].astype(np.float64)
+                S = S + ((np.exp(Gb - Gc) * dtp)[:, None] * X).T @ Bm
+            _close(ck[5][h], S, 1e-11)
