@@ -164,11 +164,15 @@ def ssd_gate(dt: torch.Tensor, A: torch.Tensor, dt_bias: torch.Tensor | None = N
 # ------------------------------------------------------------------ gdn_extend
 def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
            out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
-           gate: GateInputs | None = None):
+           gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
+           ckpt_relative: bool = False):
     """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
     cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
     (updated in place).  With `gate` (GateInputs of the same mode, dtype and [T, H_v]) the
     gate is folded into the kernel and log_g / beta are not used (pass None).
+    State checkpoints (all three or none): ckpt_token [N] int32 exclusive token boundaries
+    (absolute, or per sequence with ckpt_relative), ckpt_slot [N] int32 rows of ckpt_states
+    fp32 [num_ckpt, H_v, d_v, d_k]; negative entries disable.
     Returns out [T, H_v, d_v]."""
     lib = _lib.load()
     T, H_qk, d_k = q.shape
@@ -204,6 +208,17 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         raise ValueError(f"D must be contiguous [{H_v}] or [{H_v}, {d_v}] in the input dtype")
     if z is not None and z.dtype != q.dtype:
         raise ValueError("z must share the input dtype")
+    nck = sum(t is not None for t in (ckpt_token, ckpt_slot, ckpt_states))
+    if nck not in (0, 3):
+        raise ValueError("ckpt_token, ckpt_slot and ckpt_states go together")
+    if nck:
+        if _on_gpu(ckpt_token, ckpt_slot, ckpt_states) != dev:
+            raise ValueError("checkpoint tensors live on another device")
+        _i32(ckpt_token, "ckpt_token", N)
+        _i32(ckpt_slot, "ckpt_slot", N)
+        if ckpt_states.dtype != torch.float32 or ckpt_states.dim() != 4 \
+                or ckpt_states.shape[1:] != (H_v, d_v, d_k) or not ckpt_states.is_contiguous():
+            raise ValueError(f"ckpt_states must be contiguous fp32 [num_ckpt, {H_v}, {d_v}, {d_k}]")
     args = _lib.ExtendArgs(
         mode=GDN_MODE_SSD if ssd else GDN_MODE_GDN, in_dtype=_dtype_code(q),
         out_dtype=_dtype_code(out), N=N, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, chunk=chunk,
@@ -213,7 +228,9 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         has_init=_ptr(has_init), pool=_ptr(pool), num_slots=pool.shape[0], out=_ptr(out),
         out_stride=_rows(out, "out", H_v, d_v), scale=float(scale),
         D_per_dim=int(D is not None and D.dim() == 2), D=_ptr(D), z=_ptr(z),
-        z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0)
+        z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0,
+        ckpt_token=_ptr(ckpt_token), ckpt_slot=_ptr(ckpt_slot), ckpt_states=_ptr(ckpt_states),
+        num_ckpt=ckpt_states.shape[0] if nck else 0, ckpt_relative=int(bool(ckpt_relative)))
     if gate is None:
         _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
     else:
@@ -352,13 +369,15 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     x [batch, L, H, P] bf16; dt [batch, L, H]; A [H] fp32; B, C [batch, L, G, N];
     D [H] or [H, P]; z like x; initial_states [batch, H, P, N].  States are fp32.
     Returns (out [batch, L, H, P], final_states fp32 [batch, H, P, N] or None).
-    The packed-varlen metadata, checkpoint capture and the caller-owned 5-D `out`
-    storage are not supported and raise NotImplementedError.  out_dtype (an
-    extension) selects the output dtype; default x's dtype."""
+    Checkpoints (batched mode: boundaries relative to each batch element, all three
+    arguments together): checkpoint_token_indices, checkpoint_state_slots [batch] int32,
+    checkpoint_states fp32 [num_checkpoints, H, P, N] (the state dtype here is fp32).
+    The packed-varlen metadata and the caller-owned 5-D `out` storage are not
+    supported and raise NotImplementedError.  out_dtype (an extension) selects the
+    output dtype; default x's dtype."""
     if any(t is not None for t in (seq_idx, chunk_indices, chunk_offsets, seq_chunk_cumsum,
-                                   checkpoint_token_indices, checkpoint_state_slots,
-                                   checkpoint_states, out)) or update_seq_chunk_cumsum:
-        raise NotImplementedError("varlen metadata, checkpoints and caller-owned out are not supported")
+                                   out)) or update_seq_chunk_cumsum:
+        raise NotImplementedError("varlen metadata and caller-owned out are not supported")
     batch, L, H, P = x.shape
     G, Nst = B.shape[2], B.shape[3]
     dev = _on_gpu(x, dt, A, B, C, D, z, dt_bias, initial_states)
@@ -382,5 +401,6 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     has_init = torch.full((batch,), int(initial_states is not None), dtype=torch.int32, device=dev)
     o = extend(C.view(T, G, Nst), B.view(T, G, Nst), x.view(T, H, P), log_g, dtp, cu, slot, pool,
                has_init=has_init, mode="ssd", D=D, z=None if z is None else z.view(T, H, P),
-               max_seqlen=L, out_dtype=out_dtype, gate=g)
+               max_seqlen=L, out_dtype=out_dtype, gate=g, ckpt_token=checkpoint_token_indices,
+               ckpt_slot=checkpoint_state_slots, ckpt_states=checkpoint_states, ckpt_relative=True)
     return o.view(batch, L, H, P), (pool if return_final_states else None)

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_validate_slots", "gdn_status_str", "gdn_last_hip_error", "gdn_abi_version"]
@@ -35,7 +35,9 @@ class ExtendArgs(C.Structure):
                 ("cu_seqlens", C.c_void_p), ("slot", C.c_void_p), ("has_init", C.c_void_p),
                 ("pool", C.c_void_p), ("num_slots", C.c_int64), ("out", C.c_void_p),
                 ("out_stride", C.c_int64), ("scale", C.c_float), ("D_per_dim", C.c_int32),
-                ("D", C.c_void_p), ("z", C.c_void_p), ("z_stride", C.c_int64)]
+                ("D", C.c_void_p), ("z", C.c_void_p), ("z_stride", C.c_int64),
+                ("ckpt_token", C.c_void_p), ("ckpt_slot", C.c_void_p), ("ckpt_states", C.c_void_p),
+                ("num_ckpt", C.c_int64), ("ckpt_relative", C.c_int32), ("_pad_ckpt", C.c_int32)]
 
 
 class DecodeArgs(C.Structure):

@@ -276,7 +276,7 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 template <int I> struct Par { static constexpr int value = I; };
 
-template <int DK, int DV, bool kSSD, typename OutT, int CT, bool kGate>
+template <int DK, int DV, bool kSSD, typename OutT, int CT, bool kGate, bool kCk>
 __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kernel(SeqLaunch p) {
   constexpr int CW = 16 * CT;      // d_v columns per state wave (CT tiles of 16)
   constexpr int NSW = DV / CW;     // state waves
@@ -301,7 +301,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
-  __shared__ __attribute__((aligned(16))) float sRk[kF16 ? 2 : 1][kF16 ? C : 4];   // r_k (fp16 operands)
+  __shared__ __attribute__((aligned(16))) float sRk[2][C];   // r_k (fp16 operands, checkpoints)
+  __shared__ __attribute__((aligned(16))) float sGc[2][C];   // G_i, the in-chunk decay cumsum (checkpoints)
   // producer working set (per producer wave where private)
   // fp32 diagonal 16x16 blocks of A, rows of 20 floats, double-buffered; the block
   // stride of 336 floats puts the four blocks on different banks (the solve reads all
@@ -369,6 +370,27 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         Sacc[ct][tk] = f32x4{v.x, v.y, v.z, v.w};
       }
     }
+  // One S^T tile of this lane in the pool's [d_v, d_k] layout at `dst` (a pool slot
+  // or a checkpoint row of this head).
+  // (an opaque copy of the lane id: the addresses are computed where they are used,
+  // not hoisted out of the step loop and kept live through it)
+  auto store_tile = [&](float* dst, int ct, int tk, const f32x4& v) __attribute__((always_inline)) {
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int col = CW * wu + 16 * ct + (lane_o & 15);
+    *reinterpret_cast<float4*>(dst + (int64_t)col * DK + 32 * (tk >> 1) + 4 * (tk & 1) + 8 * (lane_o >> 4)) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  };
+  auto store_state = [&](float* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int tk = 0; tk < NTK; ++tk) store_tile(dst, ct, tk, Sacc[ct][tk]);
+  };
+  // State checkpoint (state waves): the state after ck_b tokens of the sequence goes
+  // to ck_st; ck_b = -1 when none is requested.
+  int ck_b = -1;
+  float* ck_st = nullptr;
   // delta-off D skip coefficients of this lane's output columns (16 ct + 4 g16 + e)
   float4 Dc[CT];
 #pragma unroll
@@ -472,6 +494,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     const u16* Q = sQ[PAR];
     const u16* K = sK[PAR];
     const float gC = sGC[PAR][0];
+    if constexpr (kCk) {
+      if (c > 0 && ck_b == C * c) store_state(ck_st);   // checkpoint at this chunk's start
+    }
 
     // U: tiles of 16 tokens (rows 16 rt + 4 g16 + r) x 16 d_v columns (lane j16).
     // Y: the output in transposed tiles (O^T: rows = d_v 16 ct + 4 g16 + r, lane j16 =
@@ -665,6 +690,66 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
     }
 
+    // checkpoint inside the chunk, after its first m tokens: the state update with the
+    // decays taken to token m - 1 and the later tokens left out,
+    //   S_m^T = exp(G_{m-1}) S0^T + K^T diag(exp(G_{m-1} - G_i) r_k,i [i < m]) U
+    // (r_k already in K^ on the fp16 path), written out tile by tile
+    if (kCk && ck_b > C * c && ck_b < C * c + n) {
+      __builtin_amdgcn_sched_barrier(0);   // (kept apart from the regular update: register pressure)
+      const int m = ck_b - C * c;
+      const float Gm = sGc[PAR][m - 1];
+      const float gm = __expf(Gm);
+      float cf[4][4];   // per token 16 rt + 4 g16 + e
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * rt + 4 * g16 + e;
+          cf[rt][e] = i < m ? __expf(Gm - sGc[PAR][i]) * (kF16 ? 1.f : sRk[PAR][i]) : 0.f;
+        }
+      const int rb = 4 * g16 + (j16 >> 2);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {   // one column tile at a time (register pressure)
+        f32x4 Uc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Uc[rt][e] = U[ct][rt][e] * cf[rt][e];
+        if constexpr (kF16) {
+          f16x8 Wc[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) Wc[s2] = pair_to_op_h(Uc[2 * s2], Uc[2 * s2 + 1]);
+#pragma unroll
+          for (int tk = 0; tk < NTK; ++tk) {
+            const int ca = 32 * (tk >> 1) + 8 * (j16 & 3) + 4 * (tk & 1);
+            f32x4 acc = Sacc[ct][tk] * gm;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              acc = mfma1632h(__builtin_bit_cast(f16x8, join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca))),
+                              Wc[s2], acc);
+            store_tile(ck_st, ct, tk, acc);
+          }
+        } else {
+          bf16x8 Wh[2], Wl[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pair_split(Uc[2 * s2], Uc[2 * s2 + 1], Wh[s2], Wl[s2]);
+#pragma unroll
+          for (int tk = 0; tk < NTK; ++tk) {
+            const int ca = 32 * (tk >> 1) + 8 * (j16 & 3) + 4 * (tk & 1);
+            f32x4 acc = Sacc[ct][tk] * gm;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const bf16x8 kt = join(ldqtr<DK>(K, 32 * s2 + rb, ca), ldqtr<DK>(K, 32 * s2 + 16 + rb, ca));
+              acc = mfma1632(kt, Wh[s2], acc);
+              acc = mfma1632(kt, Wl[s2], acc);
+            }
+            store_tile(ck_st, ct, tk, acc);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // state update: S^T = gamma_C S^T + K^T diag(CS) U  (fp16 K^ and CS U, or bf16 K with hi + lo splits)
     {
 #pragma unroll
@@ -847,7 +932,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sCR[PQ][i] = kF16 ? bt * gam : bt * gam * rk;                  // R = beta V - CR X
       sCO[PQ][i] = p.scale * gam * rq;                               // O = CO (Q S0^T) + P U
       sCS[PQ][i] = kF16 ? __expf(GC - G) : __expf(GC - G) * rk;      // S1 = gamma_C S0 + K^T diag(CS) U
-      if constexpr (kF16) sRk[PQ][i] = rk;
+      if constexpr (kF16 || kCk) sRk[PQ][i] = rk;
+      if constexpr (kCk) sGc[PQ][i] = G;
       sBeta[PQ][i] = bt;
       if (i == 0) sGC[PQ][0] = __expf(GC);
       const float rowP = p.scale * rq, rowA = bt * rk;
@@ -1056,31 +1142,41 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       if (c + 1 < nch) step(c + 1, Par<1>{}, rolep, std::false_type{});
     }
   };
-  if (isP) run(std::true_type{});
-  else run(std::false_type{});
-  if (!isP) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int tk = 0; tk < NTK; ++tk) {
-        const int col = CW * wu + 16 * ct + j16;
-        *reinterpret_cast<float4*>(state + (int64_t)col * DK + 32 * (tk >> 1) + 4 * (tk & 1) + 8 * g16) =
-            make_float4(Sacc[ct][tk][0], Sacc[ct][tk][1], Sacc[ct][tk][2], Sacc[ct][tk][3]);
+  if (isP) {
+    run(std::true_type{});
+  } else {
+    if (kCk) {   // checkpoint after ck_b tokens, ck_b in [0, len]
+      const int tok = p.ck_token[nseq], cks = p.ck_slot[nseq];
+      const int b = p.ck_relative ? tok : tok - tbeg;
+      if (tok >= 0 && cks >= 0 && b >= 0 && b <= tend - tbeg) {
+        ck_b = b;
+        ck_st = p.ck_states + ((int64_t)cks * p.H_v + h) * (int64_t)(DV * DK);
       }
+    }
+    if (ck_b == 0) store_state(ck_st);
+    run(std::false_type{});
+    if (ck_b > 0 && ck_b == tend - tbeg) store_state(ck_st);
+    store_state(state);
   }
 }
 
-template <int DK, int DV, bool kSSD, typename OutT, bool kGate>
+template <int DK, int DV, bool kSSD, typename OutT, bool kGate, bool kCk>
 hipError_t launch_gated(const SeqLaunch& p, hipStream_t stream) {
   constexpr int CT = kSSD ? 1 : 2;   // d_v columns per state wave: 32 (GDN), 16 (delta-off)
   dim3 grid(p.H_v, p.N), block((DV / (16 * CT) + kNP) * kWave);
-  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT, CT, kGate>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((chunk_kernel<DK, DV, kSSD, OutT, CT, kGate, kCk>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+// (checkpoint capture is a separate instantiation: calls without it run no trace of it)
+template <int DK, int DV, bool kSSD, typename OutT, bool kGate>
+hipError_t launch_ck(const SeqLaunch& p, hipStream_t stream) {
+  return p.ck_token ? launch_gated<DK, DV, kSSD, OutT, kGate, true>(p, stream)
+                    : launch_gated<DK, DV, kSSD, OutT, kGate, false>(p, stream);
 }
 template <int DK, int DV, bool kSSD, typename OutT>
 hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
-  return p.gate_fused ? launch_gated<DK, DV, kSSD, OutT, true>(p, stream)
-                      : launch_gated<DK, DV, kSSD, OutT, false>(p, stream);
+  return p.gate_fused ? launch_ck<DK, DV, kSSD, OutT, true>(p, stream)
+                      : launch_ck<DK, DV, kSSD, OutT, false>(p, stream);
 }
 
 }  // namespace

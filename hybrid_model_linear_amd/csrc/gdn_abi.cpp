@@ -162,6 +162,11 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
     st = check_fused_gate(gate, a->mode, a->in_dtype, a->T, a->H_v);
     if (st != GDN_OK) return st;
   }
+  // checkpoints: all three pointers or none
+  const int nck = (a->ckpt_token != nullptr) + (a->ckpt_slot != nullptr) + (a->ckpt_states != nullptr);
+  if (nck != 0 && nck != 3) return GDN_E_NULL;
+  if (a->num_ckpt < 0) return GDN_E_SHAPE;
+  if (nck == 3 && reinterpret_cast<uintptr_t>(a->ckpt_states) % 16 != 0) return GDN_E_SHAPE;
   if (a->N == 0) return GDN_OK;
   if (!a->cu_seqlens || !a->slot || !a->pool) return GDN_E_NULL;
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->out)) return GDN_E_NULL;
@@ -204,6 +209,12 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
   p.z_stride = a->z_stride;
   p.max_seqlen = a->max_seqlen;
   if (gate) fill_fused_gate(p, gate);
+  if (nck == 3 && a->num_ckpt > 0) {
+    p.ck_token = a->ckpt_token;
+    p.ck_slot = a->ckpt_slot;
+    p.ck_states = a->ckpt_states;
+    p.ck_relative = a->ckpt_relative != 0;
+  }
 
   const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
   if (p.in_bf16 && !short_batch && gdn::chunked_supported(p))

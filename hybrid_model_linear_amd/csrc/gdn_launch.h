@@ -66,6 +66,13 @@ struct SeqLaunch {
   const float* gdt_bias;      // [H_v] or null
   int g_softplus;
   float g_lo, g_hi;
+  // State checkpoints (ck_token null = none): sequence n with a boundary b in
+  // [0, len] (absolute ck_token[n] - cu[n], or ck_token[n] when ck_relative) and
+  // ck_slot[n] >= 0 writes its state after b tokens to ck_states[ck_slot[n]].
+  const int32_t* ck_token;    // [N]
+  const int32_t* ck_slot;     // [N]
+  float* ck_states;           // [*, H_v, d_v, d_k]
+  int ck_relative;
 };
 
 hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);

@@ -9,6 +9,8 @@
 // (gated delta rule, Gated DeltaNet, ICLR 2025) with both dot products taken from
 // the same read of S_{t-1}.  Delta-off mode (flashinfer.mamba.ssd_combined_fwd
 // semantics): u = beta v_r (beta = dt'), no L2 norm, then o += D v and o *= silu(z).
+// A requested state checkpoint is the state after the sequence's first b tokens
+// (the lane's rows, written when token b - 1 is done, or before the first token).
 //
 // Memory layout: the state row r of (slot, head) is 4*d_k contiguous bytes of the
 // pool [slot][head][d_v][d_k]; d_k/4 lanes own one row, each a float4 of it, so a
@@ -84,6 +86,24 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     }
   }
 
+  // state checkpoint: the state after ckb tokens of the sequence (ckb in [0, len])
+  int ckb = -1;
+  float* ckst = nullptr;
+  if (p.ck_token) {
+    const int tok = p.ck_token[n], cks = p.ck_slot[n];
+    const int b = p.ck_relative ? tok : tok - t0;
+    if (tok >= 0 && cks >= 0 && b >= 0 && b <= t1 - t0) {
+      ckb = b;
+      ckst = p.ck_states + ((int64_t)cks * p.H_v + h) * (int64_t)(DV * DK);
+    }
+  }
+  auto write_ck = [&]() {
+#pragma unroll
+    for (int s = 0; s < kRowSteps; ++s)
+      *reinterpret_cast<float4*>(ckst + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
+  };
+  if (ckb == 0) write_ck();
+
   const InT* qb = reinterpret_cast<const InT*>(p.q);
   const InT* kb = reinterpret_cast<const InT*>(p.k);
   const InT* vb = reinterpret_cast<const InT*>(p.v);
@@ -149,6 +169,7 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       }
       if (c == 0) Elem<OutT>::store(ob, orow + row, o);
     }
+    if (t - t0 + 1 == ckb) write_ck();
   }
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {

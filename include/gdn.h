@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -115,7 +115,22 @@ typedef struct gdn_gate_args {
  * out_dtype bf16 or fp32.  chunk: 0 (default) or 64; bf16 inputs use the chunked
  * MFMA kernel (chunk 64), fp32 inputs and short batches (max_seqlen in 1..8) the
  * token-recurrent kernel.  max_seqlen is a host-side hint (an upper bound of the
- * longest sequence, 0 = unknown); a wrong hint changes speed, never results. */
+ * longest sequence, 0 = unknown); a wrong hint changes speed, never results.
+ *
+ * State checkpoints (optional; the checkpoint_token_indices / checkpoint_state_slots
+ * / checkpoint_states arguments of the ssd_combined_fwd page, in both modes):
+ *   ckpt_token  : int32 [N], one exclusive token boundary per sequence: absolute
+ *                 packed-token index, or relative to the sequence's first token
+ *                 when ckpt_relative != 0; negative disables the sequence's capture
+ *   ckpt_slot   : int32 [N], row of ckpt_states; negative disables
+ *   ckpt_states : fp32 [num_ckpt, H_v, d_v, d_k] (the pool's layout), caller-owned
+ * Sequence n (slot[n] >= 0) with a boundary b inside [its first token, its end]
+ * writes the state after its tokens before b to ckpt_states[ckpt_slot[n]]: its start
+ * state for b at the first token, its final state for b at the end.  A boundary
+ * outside the sequence captures nothing.  The three pointers are given together or
+ * not at all (else GDN_E_NULL); num_ckpt >= 0.  As for the pool, ckpt_slot values
+ * are device data and not range-checked: they must be < num_ckpt and distinct among
+ * capturing sequences. */
 typedef struct gdn_extend_args {
   int32_t mode;          /* GDN_MODE_GDN | GDN_MODE_SSD          */
   int32_t in_dtype;      /* q, k, v (and D, z)                   */
@@ -145,6 +160,12 @@ typedef struct gdn_extend_args {
   const void* D;         /* SSD only, or NULL                    */
   const void* z;         /* SSD only, or NULL                    */
   int64_t z_stride;
+  const int32_t* ckpt_token; /* [N] or NULL (no checkpoints)     */
+  const int32_t* ckpt_slot;  /* [N] or NULL                      */
+  float* ckpt_states;        /* [num_ckpt, H_v, d_v, d_k] or NULL */
+  int64_t num_ckpt;
+  int32_t ckpt_relative;     /* boundaries relative to each sequence's first token */
+  int32_t _pad_ckpt;
 } gdn_extend_args;
 
 /* ---------------------------------------------------------------- gdn_decode

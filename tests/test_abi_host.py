@@ -90,6 +90,12 @@ FAKE = ct.c_void_p(0x1000)   # never dereferenced: every case below fails valida
     (dict(q_stride=2 * 2 * 128 + 4 * 128 + 2), _lib.GDN_E_SHAPE),  # stride not a multiple of 4
     (dict(cu_seqlens=FAKE, slot=FAKE, pool=FAKE, q=ct.c_void_p(0x1002), k=FAKE, v=FAKE, log_g=FAKE,
           beta=FAKE, out=FAKE), _lib.GDN_E_SHAPE),               # q not 8-byte aligned (bf16)
+    (dict(ckpt_token=FAKE), _lib.GDN_E_NULL),                    # checkpoint arguments: all or none
+    (dict(ckpt_token=FAKE, ckpt_slot=FAKE), _lib.GDN_E_NULL),
+    (dict(ckpt_token=FAKE, ckpt_slot=FAKE, ckpt_states=FAKE, num_ckpt=-1), _lib.GDN_E_SHAPE),
+    (dict(ckpt_token=FAKE, ckpt_slot=FAKE, ckpt_states=ct.c_void_p(0x1008), num_ckpt=2),
+     _lib.GDN_E_SHAPE),                                          # checkpoint states not 16-byte aligned
+    (dict(N=0, ckpt_states=FAKE), _lib.GDN_E_NULL),              # checked before the empty-call exit
 ])
 def test_extend_validation(kw, status):
     lib = gdn.load()
@@ -263,4 +269,6 @@ def test_ssd_combined_rejects_unsupported_arguments():
     with pytest.raises(NotImplementedError):
         gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, seq_idx=torch.zeros(1, 4))
     with pytest.raises(NotImplementedError):
-        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, checkpoint_states=x)
+        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, out=x)
+    with pytest.raises(NotImplementedError):
+        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, update_seq_chunk_cumsum=True)

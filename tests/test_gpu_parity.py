@@ -440,3 +440,83 @@ def test_validate_slots(gdn_lib):
     assert gdn.validate_slots(s([2, 1, 2]), 4) == 2
     assert gdn.validate_slots(s([9, 9]), 4) == 3
     assert gdn.validate_slots(s([]), 4) == 0
+
+
+# ------------------------------------------------------------------ state checkpoints
+# One sequence per boundary kind: a chunk boundary, the start (zero state), inside the
+# first chunk, the end of a one-chunk sequence, inside a later chunk, the first token of
+# a chunk (m = 1), disabled (negative boundary), outside the sequence.
+CKPT_LENS = (150, 64, 200, 7, 90, 130, 20, 30)
+CKPT_INIT = (1, 0, 1, 1, 1, 0, 1, 1)
+CKPT_REL = (64, 0, 37, 7, 70, 129, -1, 31)
+CKPT_SLOT = (3, 0, 5, 1, 4, 2, 6, 6)
+
+
+def _ckpt_args(case, relative):
+    cu = case.cu_seqlens
+    tok = np.array([r if (relative or r < 0) else cu[n] + r for n, r in enumerate(CKPT_REL)], np.int32)
+    return tok, np.array(CKPT_SLOT, np.int32)
+
+
+@pytest.mark.parametrize("path", ["chunked-bf16out", "chunked-f32out", "recurrent"])
+def test_extend_checkpoints(gdn_lib, path):
+    """Checkpoint states against the oracle's; outputs, final states and untouched
+    checkpoint rows unchanged by the capture."""
+    gdn = gdn_lib
+    _announce(f"extend checkpoints {path}")
+    dtype = "f32" if path == "recurrent" else "bf16"
+    case = synth.edge_case("ckpt", CKPT_LENS, has_init=CKPT_INIT, seed=31, num_slots=11, dtype=dtype)
+    odt = torch.float32 if path == "chunked-f32out" else None
+    relative = path == "recurrent"
+    tok, cks = _ckpt_args(case, relative)
+    d = upload(case)
+    base = run_extend(gdn, case, d, out_dtype=odt)
+    pool_base = d["pool"].clone()
+    d2 = upload(case)
+    states = torch.full((8, case.H_v, case.d_v, case.d_k), SENTINEL, dtype=torch.float32, device="cuda")
+    q, k, v = gdn.split_mixed_qkv(d2["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d2["a"], d2["b"], d2["A_log"], d2["dt_bias"])
+    ti = lambda x: torch.from_numpy(x).to("cuda")
+    out = gdn.extend(q, k, v, lg, bt, d2["cu"], d2["slot"], d2["pool"], has_init=d2["has_init"],
+                     scale=case.scale, out_dtype=odt, ckpt_token=ti(tok), ckpt_slot=ti(cks),
+                     ckpt_states=states, ckpt_relative=relative)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32 if out.dtype == torch.float32 else torch.int16),
+                       base.view(torch.int32 if base.dtype == torch.float32 else torch.int16)), "outputs changed"
+    assert torch.equal(d2["pool"], pool_base), "final states changed"
+    ck = {}
+    abs_tok = np.array([r if r < 0 else case.cu_seqlens[n] + r for n, r in enumerate(CKPT_REL)])
+    oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                      case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale,
+                      ckpt_token=abs_tok, ckpt_slot=np.array(CKPT_SLOT), ckpts=ck)
+    assert sorted(ck) == [0, 1, 2, 3, 4, 5]
+    got = states.cpu().numpy()
+    bar = (2e-3, 1e-2) if path == "chunked-bf16out" else (1e-3, 2e-3)
+    for s in ck:
+        assert_close(got[s], ck[s], f"checkpoint row {s}", *bar)
+    assert (got[6:] == SENTINEL).all(), "rows without a capture were written"
+
+
+def test_ssd_checkpoints(gdn_lib):
+    """ssd_combined_fwd checkpoint arguments (batched: boundaries relative to each batch
+    element) against the oracle."""
+    gdn = gdn_lib
+    _announce("ssd checkpoints")
+    c = synth.config4_ssd(seed=41, batch=4, L=150, H=6, P=64, G=2, Nst=128, initial=True)
+    tb = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
+    tf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.float32)
+    rel = np.array([37, 64, 150, 0], np.int32)
+    cks = np.array([2, 0, 3, 1], np.int32)
+    states = torch.full((5, 6, 64, 128), SENTINEL, dtype=torch.float32, device="cuda")
+    out, fin = gdn.ssd_combined_fwd(tb(c.x), tb(c.dt), tf(c.A), tb(c.B), tb(c.C), tb(c.D), tb(c.z),
+                                    tf(c.dt_bias), True, (0.0, float("inf")), tf(c.initial_states),
+                                    checkpoint_token_indices=torch.from_numpy(rel).cuda(),
+                                    checkpoint_state_slots=torch.from_numpy(cks).cuda(),
+                                    checkpoint_states=states)
+    ck = {}
+    oracle.ssd_combined(c.x, c.dt, c.A, c.B, c.C, c.D, c.z, c.dt_bias, True, (0.0, float("inf")),
+                        c.initial_states, True, ckpt_token=rel, ckpt_slot=cks, ckpts=ck)
+    got = states.cpu().numpy()
+    for s in ck:
+        assert_close(got[s], ck[s], f"ssd checkpoint row {s}")
+    assert (got[4] == SENTINEL).all()
