@@ -79,7 +79,7 @@ def l2_normalize(x, eps=1e-6):
 # ---------------------------------------------------------------- GDN layer
 def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
                scale, eps=1e-6, heads=None, seqs=None, ckpt_token=None, ckpt_slot=None,
-               ckpts=None):
+               ckpts=None, spec_slot=None, spec_parent=None, spec=None):
     """Packed-varlen GDN extend, token by token.
 
     q, k : [T, H_qk, d_k]; v : [T, H_v, d_v]; a, b : [T, H_v]
@@ -94,6 +94,13 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
       [cu[n], cu[n+1]]) under the key ckpt_slot[n] of the dict `ckpts`; a negative
       entry (either one), a skipped sequence or a boundary outside the sequence
       records nothing.
+    spec_slot : optional [N] rows for the target-verify states: sequence n with
+      spec_slot[n] >= 0 records the state after each of its tokens (index i within the
+      sequence) under spec[(spec_slot[n], i)].
+    spec_parent : optional [T] token tree (requires spec_slot for every sequence with
+      tokens): token i of a sequence starts from the state after token spec_parent[t]
+      of the same sequence (an earlier index), or from the sequence's start state for
+      -1, instead of from the state after token i - 1 (a chain).
 
     Returns (out, written, finals):
       out     float64 [T, len(heads), d_v]   (NaN where not written)
@@ -131,9 +138,14 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
             S = np.array(pool[s], dtype=F64)[hsel].copy()          # [Hs, d_v, d_k]
         else:
             S = np.zeros((len(heads), d_v, d_k), dtype=F64)
+        S_start = S.copy()
+        row = -1 if spec_slot is None else int(spec_slot[n])
         for t in range(t0, t1):
             if t == ck:                                            # state before token t
                 ckpts[int(ckpt_slot[n])] = S.copy()
+            if spec_parent is not None:                            # token tree: start from the parent
+                par = int(spec_parent[t])
+                S = (S_start if par < 0 else spec[(row, par)]).copy()
             log_g, beta = gdn_gate(np.asarray(a[t:t + 1])[:, hsel], np.asarray(b[t:t + 1])[:, hsel],
                                    np.asarray(A_log)[hsel], np.asarray(dt_bias)[hsel])
             g = np.exp(log_g[0])[:, None, None]                    # [Hs,1,1]
@@ -146,6 +158,8 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
             S = S + np.einsum("hv,hk->hvk", bt * (vt - u), kh)     # delta-rule write
             out[t] = scale * np.einsum("hvk,hk->hv", S, qh)        # read with S_t
             written[t] = True
+            if row >= 0:
+                spec[(row, t - t0)] = S.copy()
         if ck == t1:                                               # boundary at the end
             ckpts[int(ckpt_slot[n])] = S.copy()
         finals[s] = S

@@ -587,3 +587,60 @@ def test_ssd_checkpoint_relative_boundary():
                 Bm = c.B[0, :b, h // (H // G)].astype(np.float64)
                 S = S + ((np.exp(Gb - Gc) * dtp)[:, None] * X).T @ Bm
             _close(ck[5][h], S, 1e-11)
+
+
+# ------------------------------------------------------------------ target-verify states
+def _dense_path_state(c, n, h, path):
+    """State of sequence n, head h after applying its tokens `path` (absolute indices,
+    in order) to its start state, by the dense transition-matrix recurrence."""
+    r = c.H_v // c.H_qk
+    j = h // r
+    S = c.pool[c.slot[n], h].astype(np.float64) if c.has_init[n] else np.zeros((c.d_v, c.d_k))
+    for t in path:
+        sp = np.logaddexp(0.0, float(c.a[t, h]) + float(c.dt_bias[h]))
+        g = np.exp(-np.exp(float(c.A_log[h])) * sp)
+        beta = scipy.special.expit(float(c.b[t, h]))
+        kk = c.k[t, j].astype(np.float64)
+        kk = kk / np.sqrt(kk @ kk + 1e-6)
+        S = S @ (g * (np.eye(c.d_k) - beta * np.outer(kk, kk))) + beta * np.outer(c.v[t, h].astype(np.float64), kk)
+    return S
+
+
+def test_verify_chain_states():
+    """Chain verify: the state after token i of each sequence is the dense recurrence over
+    its first i + 1 tokens; outputs and final states equal the plain extend's."""
+    c = tiny_case(lens=(4, 3, 5), has_init=(1, 1, 0))
+    ref_out, _, ref_fin = _run(oracle.gdn_extend, c)
+    spec = {}
+    out, _, fin = _run(oracle.gdn_extend, c, spec_slot=np.array([2, -1, 0]), spec=spec)
+    _close(out, ref_out)
+    assert sorted(spec) == [(0, i) for i in range(5)] + [(2, i) for i in range(4)]
+    for n, row in ((0, 2), (2, 0)):
+        t0 = int(c.cu_seqlens[n])
+        for i in range(int(c.cu_seqlens[n + 1]) - t0):
+            for h in range(c.H_v):
+                _close(spec[(row, i)][h], _dense_path_state(c, n, h, range(t0, t0 + i + 1)))
+
+
+def test_verify_tree_states_and_outputs():
+    """Tree verify: each token continues its parent's state; its state and output equal
+    the dense recurrence over the path root -> token alone (siblings do not see each
+    other)."""
+    c = tiny_case(lens=(5, 4), has_init=(1, 0))
+    parents = np.array([-1, 0, 0, 1, 2, -1, 0, 1, 1])        # per token, within its sequence
+    spec = {}
+    out, _, _ = _run(oracle.gdn_extend, c, spec_slot=np.array([1, 0]), spec_parent=parents, spec=spec)
+    for n, row in ((0, 1), (1, 0)):
+        t0, t1 = int(c.cu_seqlens[n]), int(c.cu_seqlens[n + 1])
+        for i in range(t1 - t0):
+            path, x = [], i
+            while x >= 0:
+                path.append(t0 + x)
+                x = int(parents[t0 + x])
+            path = path[::-1]
+            r = c.H_v // c.H_qk
+            for h in range(c.H_v):
+                S = _dense_path_state(c, n, h, path)
+                _close(spec[(row, i)][h], S)
+                qq = c.q[t0 + i, h // r].astype(np.float64)
+                _close(out[t0 + i, h], c.scale * S @ (qq / np.sqrt(qq @ qq + 1e-6)))
