@@ -165,7 +165,8 @@ def ssd_gate(dt: torch.Tensor, A: torch.Tensor, dt_bias: torch.Tensor | None = N
 def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
            out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
            gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
-           ckpt_relative: bool = False):
+           ckpt_relative: bool = False, spec_states=None, spec_slot=None, spec_parent=None,
+           keep_pool: bool = False):
     """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
     cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
     (updated in place).  With `gate` (GateInputs of the same mode, dtype and [T, H_v]) the
@@ -173,6 +174,9 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
     State checkpoints (all three or none): ckpt_token [N] int32 exclusive token boundaries
     (absolute, or per sequence with ckpt_relative), ckpt_slot [N] int32 rows of ckpt_states
     fp32 [num_ckpt, H_v, d_v, d_k]; negative entries disable.
+    Target verify: spec_states fp32 [num_spec, steps, H_v, d_v, d_k] and spec_slot [N] int32
+    record the state after every token; spec_parent [T] int32 (optional) makes the tokens
+    of a sequence a tree; keep_pool leaves the pool unwritten.
     Returns out [T, H_v, d_v]."""
     lib = _lib.load()
     T, H_qk, d_k = q.shape
@@ -219,6 +223,17 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         if ckpt_states.dtype != torch.float32 or ckpt_states.dim() != 4 \
                 or ckpt_states.shape[1:] != (H_v, d_v, d_k) or not ckpt_states.is_contiguous():
             raise ValueError(f"ckpt_states must be contiguous fp32 [num_ckpt, {H_v}, {d_v}, {d_k}]")
+    if (spec_states is None) != (spec_slot is None) or (spec_parent is not None and spec_states is None):
+        raise ValueError("spec_states and spec_slot go together; spec_parent needs them")
+    if spec_states is not None:
+        if _on_gpu(spec_states, spec_slot, spec_parent) != dev:
+            raise ValueError("target-verify tensors live on another device")
+        _i32(spec_slot, "spec_slot", N)
+        if spec_parent is not None:
+            _i32(spec_parent, "spec_parent", T)
+        if spec_states.dtype != torch.float32 or spec_states.dim() != 5 \
+                or spec_states.shape[2:] != (H_v, d_v, d_k) or not spec_states.is_contiguous():
+            raise ValueError(f"spec_states must be contiguous fp32 [num_spec, steps, {H_v}, {d_v}, {d_k}]")
     args = _lib.ExtendArgs(
         mode=GDN_MODE_SSD if ssd else GDN_MODE_GDN, in_dtype=_dtype_code(q),
         out_dtype=_dtype_code(out), N=N, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, chunk=chunk,
@@ -230,7 +245,10 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         D_per_dim=int(D is not None and D.dim() == 2), D=_ptr(D), z=_ptr(z),
         z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0,
         ckpt_token=_ptr(ckpt_token), ckpt_slot=_ptr(ckpt_slot), ckpt_states=_ptr(ckpt_states),
-        num_ckpt=ckpt_states.shape[0] if nck else 0, ckpt_relative=int(bool(ckpt_relative)))
+        num_ckpt=ckpt_states.shape[0] if nck else 0, ckpt_relative=int(bool(ckpt_relative)),
+        keep_pool=int(bool(keep_pool)), spec_states=_ptr(spec_states), spec_slot=_ptr(spec_slot),
+        spec_parent=_ptr(spec_parent), num_spec=spec_states.shape[0] if spec_states is not None else 0,
+        spec_steps=spec_states.shape[1] if spec_states is not None else 0)
     if gate is None:
         _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
     else:
@@ -295,6 +313,13 @@ _EXTEND_MODES = {"extend", "mixed", "draft_extend", "draft_extend_v2", "target_v
                  "split_prefill", "dllm_extend"}
 
 
+def _is_target_verify(forward_mode) -> bool:
+    if hasattr(forward_mode, "is_target_verify"):
+        return bool(forward_mode.is_target_verify())
+    name = getattr(forward_mode, "name", forward_mode)
+    return isinstance(name, str) and name.lower() == "target_verify"
+
+
 def _mode_kind(forward_mode) -> str:
     """'decode' or 'extend' for the legal forward modes, else ValueError.
 
@@ -329,7 +354,12 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
            dt_bias [H_v] fp32, optional scale (default head_k_dim ** -0.5), layer_id.
     forward_batch: forward_mode; state_slots int32 [N]; state_pool indexable by
            layer_id -> fp32 [num_slots, H_v, d_v, d_k]; for extend modes also
-           cu_seqlens int32 [N+1], optional has_initial_state int32 [N] and max_seqlen.
+           cu_seqlens int32 [N+1], optional has_initial_state int32 [N] and max_seqlen;
+           for target verify optionally the speculative state buffer spec_states
+           (indexable by layer_id -> fp32 [rows, steps, H_v, d_v, d_k]) with
+           spec_state_slots int32 [N] and spec_parents int32 [T] (token trees): the
+           state after every draft token is recorded there and the pool is left
+           unwritten.
     mixed_qkv: [T, 2 H_qk d_k + H_v d_v], already convolved; a, b: [T, H_v].
     Returns out [T, H_v * d_v] in mixed_qkv's dtype."""
     kind = _mode_kind(forward_batch.forward_mode)
@@ -351,9 +381,15 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     if kind == "decode":
         o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale, gate=g)
     else:
+        spec = getattr(forward_batch, "spec_states", None)
+        verify = spec is not None and _is_target_verify(forward_batch.forward_mode)
         o = extend(q, k, v, log_g, beta, forward_batch.cu_seqlens, forward_batch.state_slots, pool,
                    has_init=getattr(forward_batch, "has_initial_state", None), scale=scale,
-                   max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0), gate=g)
+                   max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0), gate=g,
+                   spec_states=spec[layer.layer_id] if verify else None,
+                   spec_slot=forward_batch.spec_state_slots if verify else None,
+                   spec_parent=getattr(forward_batch, "spec_parents", None) if verify else None,
+                   keep_pool=verify)
     return o.view(T, H_v * d_v)
 
 

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_validate_slots", "gdn_status_str", "gdn_last_hip_error", "gdn_abi_version"]
@@ -37,7 +37,9 @@ class ExtendArgs(C.Structure):
                 ("out_stride", C.c_int64), ("scale", C.c_float), ("D_per_dim", C.c_int32),
                 ("D", C.c_void_p), ("z", C.c_void_p), ("z_stride", C.c_int64),
                 ("ckpt_token", C.c_void_p), ("ckpt_slot", C.c_void_p), ("ckpt_states", C.c_void_p),
-                ("num_ckpt", C.c_int64), ("ckpt_relative", C.c_int32), ("_pad_ckpt", C.c_int32)]
+                ("num_ckpt", C.c_int64), ("ckpt_relative", C.c_int32), ("keep_pool", C.c_int32),
+                ("spec_states", C.c_void_p), ("spec_slot", C.c_void_p), ("spec_parent", C.c_void_p),
+                ("num_spec", C.c_int64), ("spec_steps", C.c_int32), ("_pad_spec", C.c_int32)]
 
 
 class DecodeArgs(C.Structure):

@@ -1156,7 +1156,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     if (ck_b == 0) store_state(ck_st);
     run(std::false_type{});
     if (ck_b > 0 && ck_b == tend - tbeg) store_state(ck_st);
-    store_state(state);
+    if (!p.keep_pool) store_state(state);
   }
 }
 

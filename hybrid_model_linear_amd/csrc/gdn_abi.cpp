@@ -167,6 +167,12 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
   if (nck != 0 && nck != 3) return GDN_E_NULL;
   if (a->num_ckpt < 0) return GDN_E_SHAPE;
   if (nck == 3 && reinterpret_cast<uintptr_t>(a->ckpt_states) % 16 != 0) return GDN_E_SHAPE;
+  // target-verify states: spec_states and spec_slot together; spec_parent needs them
+  const bool spec = a->spec_states != nullptr;
+  if (spec != (a->spec_slot != nullptr) || (a->spec_parent && !spec)) return GDN_E_NULL;
+  if (spec && (a->num_spec < 0 || a->spec_steps < 1 ||
+               reinterpret_cast<uintptr_t>(a->spec_states) % 16 != 0))
+    return GDN_E_SHAPE;
   if (a->N == 0) return GDN_OK;
   if (!a->cu_seqlens || !a->slot || !a->pool) return GDN_E_NULL;
   if (a->T > 0 && (!a->q || !a->k || !a->v || !a->out)) return GDN_E_NULL;
@@ -215,9 +221,16 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
     p.ck_states = a->ckpt_states;
     p.ck_relative = a->ckpt_relative != 0;
   }
+  p.keep_pool = a->keep_pool != 0;
+  if (spec && a->num_spec > 0) {
+    p.sp_states = a->spec_states;
+    p.sp_slot = a->spec_slot;
+    p.sp_parent = a->spec_parent;
+    p.sp_steps = a->spec_steps;
+  }
 
   const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
-  if (p.in_bf16 && !short_batch && gdn::chunked_supported(p))
+  if (p.in_bf16 && !short_batch && !spec && gdn::chunked_supported(p))
     return hip_status(gdn::launch_chunked(p, (hipStream_t)stream));
   return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
 }

@@ -73,6 +73,15 @@ struct SeqLaunch {
   const int32_t* ck_slot;     // [N]
   float* ck_states;           // [*, H_v, d_v, d_k]
   int ck_relative;
+  // Target-verify states (token-recurrent kernel only): the state after token i of
+  // sequence n goes to sp_states[sp_slot[n], i] (i < sp_steps); with sp_parent a
+  // token starts from its parent's recorded state (-1: the start state).  keep_pool:
+  // the pool is not written.
+  float* sp_states;           // [*, sp_steps, H_v, d_v, d_k] or null
+  const int32_t* sp_slot;     // [N]
+  const int32_t* sp_parent;   // [T] or null
+  int sp_steps;
+  int keep_pool;
 };
 
 hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);

@@ -11,6 +11,8 @@
 // semantics): u = beta v_r (beta = dt'), no L2 norm, then o += D v and o *= silu(z).
 // A requested state checkpoint is the state after the sequence's first b tokens
 // (the lane's rows, written when token b - 1 is done, or before the first token).
+// Target verify records the state after every token; with a token tree each token
+// starts from its parent's recorded state.
 //
 // Memory layout: the state row r of (slot, head) is 4*d_k contiguous bytes of the
 // pool [slot][head][d_v][d_k]; d_k/4 lanes own one row, each a float4 of it, so a
@@ -54,7 +56,7 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-template <int DK, int DV, typename InT, typename OutT, bool kSSD>
+template <int DK, int DV, typename InT, typename OutT, bool kSSD, bool kAux>
 __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   using L = RecLayout<DK>;
   const int lane = threadIdx.x % kWave;
@@ -89,7 +91,7 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   // state checkpoint: the state after ckb tokens of the sequence (ckb in [0, len])
   int ckb = -1;
   float* ckst = nullptr;
-  if (p.ck_token) {
+  if (kAux && p.ck_token) {
     const int tok = p.ck_token[n], cks = p.ck_slot[n];
     const int b = p.ck_relative ? tok : tok - t0;
     if (tok >= 0 && cks >= 0 && b >= 0 && b <= t1 - t0) {
@@ -102,7 +104,19 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     for (int s = 0; s < kRowSteps; ++s)
       *reinterpret_cast<float4*>(ckst + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
   };
-  if (ckb == 0) write_ck();
+  if (kAux && ckb == 0) write_ck();
+  // target-verify states: the state after token i goes to row spr, step i; with a
+  // token tree each token starts from its parent's recorded state (rows this thread
+  // wrote itself) or from the start state
+  float* spr = nullptr;
+  if (kAux && p.sp_states) {
+    const int r = p.sp_slot[n];
+    if (r >= 0) spr = p.sp_states + (int64_t)r * p.sp_steps * p.H_v * (DV * DK) + (int64_t)h * (DV * DK);
+  }
+  const int64_t sp_step = (int64_t)p.H_v * (DV * DK);
+  float4 st0[kRowSteps];
+#pragma unroll
+  for (int s = 0; s < kRowSteps; ++s) st0[s] = kAux ? st[s] : make_float4(0.f, 0.f, 0.f, 0.f);
 
   const InT* qb = reinterpret_cast<const InT*>(p.q);
   const InT* kb = reinterpret_cast<const InT*>(p.k);
@@ -110,6 +124,17 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   OutT* ob = reinterpret_cast<OutT*>(p.out);
 
   for (int t = t0; t < t1; ++t) {
+    if (kAux && p.sp_parent && spr) {   // token tree (uniform branch)
+      const int par = p.sp_parent[t];
+      if (par < 0) {
+#pragma unroll
+        for (int s = 0; s < kRowSteps; ++s) st[s] = st0[s];
+      } else if (par != t - t0 - 1) {
+#pragma unroll
+        for (int s = 0; s < kRowSteps; ++s)
+          st[s] = *reinterpret_cast<const float4*>(spr + par * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c);
+      }
+    }
     float4 kv = load4<InT>(kb + (int64_t)t * p.k_stride + (int64_t)j * DK + 4 * c);
     float4 qv = load4<InT>(qb + (int64_t)t * p.q_stride + (int64_t)j * DK + 4 * c);
     if constexpr (!kSSD) {
@@ -169,8 +194,14 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       }
       if (c == 0) Elem<OutT>::store(ob, orow + row, o);
     }
-    if (t - t0 + 1 == ckb) write_ck();
+    if (kAux && t - t0 + 1 == ckb) write_ck();
+    if (kAux && spr && t - t0 < p.sp_steps) {
+#pragma unroll
+      for (int s = 0; s < kRowSteps; ++s)
+        *reinterpret_cast<float4*>(spr + (t - t0) * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
+    }
   }
+  if (p.keep_pool) return;
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int row = row0 + s * L::kRowsPerStep;
@@ -183,7 +214,12 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
   using L = RecLayout<DK>;
   static_assert(DV % L::kRowsPerBlock == 0, "d_v must be a multiple of the rows per block");
   dim3 grid(DV / L::kRowsPerBlock, p.H_v, p.N), block(kThreads);
-  hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD>), grid, block, 0, stream, p);
+  // checkpoints and target-verify states are a separate instantiation: the decode
+  // step runs none of their code
+  if (p.ck_token || p.sp_states)
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -130,7 +130,24 @@ typedef struct gdn_gate_args {
  * outside the sequence captures nothing.  The three pointers are given together or
  * not at all (else GDN_E_NULL); num_ckpt >= 0.  As for the pool, ckpt_slot values
  * are device data and not range-checked: they must be < num_ckpt and distinct among
- * capturing sequences. */
+ * capturing sequences.
+ *
+ * Target-verify states (optional; the speculative state buffer of the target-verify
+ * path in the SGLang GDN test article, chains and EAGLE trees):
+ *   spec_states : fp32 [num_spec, spec_steps, H_v, d_v, d_k], caller-owned
+ *   spec_slot   : int32 [N], row of spec_states; negative: the sequence records nothing
+ *   spec_parent : int32 [T] or NULL; token tree: token i of a sequence (index within
+ *                 it) starts from the state after its token spec_parent[t] (an earlier
+ *                 index), or from the sequence's start state for -1; NULL = a chain
+ *   keep_pool   : non-zero leaves the pool unwritten (read only)
+ * Sequence n with spec_slot[n] >= 0 writes the state after its token i to
+ * spec_states[spec_slot[n], i] for i < spec_steps.  With spec_parent every sequence
+ * with tokens needs spec_slot[n] >= 0 and at most spec_steps tokens (device data, not
+ * checked).  The pool receives the state after the sequence's last token (a chain's
+ * final state) unless keep_pool.  spec_states and spec_slot go together, spec_parent
+ * needs them (else GDN_E_NULL); spec_steps >= 1 with them.  Calls with target-verify
+ * states run the token-recurrent kernel (verify batches are a few tokens per
+ * sequence). */
 typedef struct gdn_extend_args {
   int32_t mode;          /* GDN_MODE_GDN | GDN_MODE_SSD          */
   int32_t in_dtype;      /* q, k, v (and D, z)                   */
@@ -165,7 +182,13 @@ typedef struct gdn_extend_args {
   float* ckpt_states;        /* [num_ckpt, H_v, d_v, d_k] or NULL */
   int64_t num_ckpt;
   int32_t ckpt_relative;     /* boundaries relative to each sequence's first token */
-  int32_t _pad_ckpt;
+  int32_t keep_pool;         /* non-zero: the pool is not written   */
+  float* spec_states;        /* [num_spec, spec_steps, H_v, d_v, d_k] or NULL */
+  const int32_t* spec_slot;  /* [N] or NULL                      */
+  const int32_t* spec_parent;/* [T] or NULL (chain)              */
+  int64_t num_spec;
+  int32_t spec_steps;
+  int32_t _pad_spec;
 } gdn_extend_args;
 
 /* ---------------------------------------------------------------- gdn_decode

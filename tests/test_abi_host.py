@@ -96,6 +96,11 @@ FAKE = ct.c_void_p(0x1000)   # never dereferenced: every case below fails valida
     (dict(ckpt_token=FAKE, ckpt_slot=FAKE, ckpt_states=ct.c_void_p(0x1008), num_ckpt=2),
      _lib.GDN_E_SHAPE),                                          # checkpoint states not 16-byte aligned
     (dict(N=0, ckpt_states=FAKE), _lib.GDN_E_NULL),              # checked before the empty-call exit
+    (dict(spec_states=FAKE, spec_steps=4), _lib.GDN_E_NULL),     # target-verify states need their rows
+    (dict(spec_slot=FAKE), _lib.GDN_E_NULL),
+    (dict(spec_parent=FAKE), _lib.GDN_E_NULL),                   # a token tree needs the state buffer
+    (dict(spec_states=FAKE, spec_slot=FAKE, spec_steps=0, num_spec=2), _lib.GDN_E_SHAPE),
+    (dict(spec_states=ct.c_void_p(0x1008), spec_slot=FAKE, spec_steps=4, num_spec=2), _lib.GDN_E_SHAPE),
 ])
 def test_extend_validation(kw, status):
     lib = gdn.load()

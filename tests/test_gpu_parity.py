@@ -520,3 +520,78 @@ def test_ssd_checkpoints(gdn_lib):
     for s in ck:
         assert_close(got[s], ck[s], f"ssd checkpoint row {s}")
     assert (got[4] == SENTINEL).all()
+
+
+# ------------------------------------------------------------------ target verify
+@pytest.mark.parametrize("tree", [False, True], ids=["chain", "tree"])
+@pytest.mark.parametrize("keep_pool", [True, False])
+def test_target_verify_states(gdn_lib, tree, keep_pool):
+    """Verify batches (4 draft tokens per sequence, 8 sequences, one without a row):
+    outputs and the state after every draft token against the oracle, for a chain and
+    for a token tree (EAGLE topk = 2 shape: parents -1, 0, 0, 1); keep_pool leaves the
+    pool untouched."""
+    gdn = gdn_lib
+    _announce(f"target verify tree={tree} keep_pool={keep_pool}")
+    N, L = 8, 4
+    case = synth.edge_case("verify", (L,) * N, has_init=1, seed=77, num_slots=12)
+    rows = np.array([3, 0, 7, -1, 5, 1, 6, 2], np.int32)
+    parents = np.tile(np.array([-1, 0, 0, 1], np.int32), N) if tree else None
+    if tree:
+        rows[3] = 4                                        # a tree needs every sequence's row
+    d = upload(case)
+    pool_before = d["pool"].clone()
+    states = torch.full((9, L, case.H_v, case.d_v, case.d_k), SENTINEL, dtype=torch.float32, device="cuda")
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    out = gdn.extend(q, k, v, lg, bt, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                     scale=case.scale, max_seqlen=L, spec_states=states,
+                     spec_slot=torch.from_numpy(rows).cuda(),
+                     spec_parent=None if parents is None else torch.from_numpy(parents).cuda(),
+                     keep_pool=keep_pool)
+    torch.cuda.synchronize()
+    spec = {}
+    ref, _, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                    case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale,
+                                    spec_slot=rows, spec_parent=parents, spec=spec)
+    assert_close(out.float().cpu().numpy(), ref, "verify out")
+    got = states.cpu().numpy()
+    for (r, i), S in spec.items():
+        assert_close(got[r, i], S, f"verify state row {r} step {i}")
+    if not tree:
+        assert (got[8] == SENTINEL).all() and (got[4] == SENTINEL).all(), "row without a sequence written"
+    if keep_pool:
+        assert torch.equal(d["pool"], pool_before), "keep_pool: the pool changed"
+    else:
+        newpool = oracle.apply_final_states(case.pool, fin)
+        assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "verify final states")
+
+
+def test_forward_gdn_target_verify(gdn_lib):
+    """forward_gdn in TARGET_VERIFY mode with a speculative state buffer: states per draft
+    token recorded, pool untouched."""
+    from types import SimpleNamespace
+    gdn = gdn_lib
+    _announce("forward_gdn target verify")
+    N, L = 4, 3
+    case = synth.edge_case("fwd-verify", (L,) * N, has_init=1, seed=79, num_slots=6)
+    d = upload(case)
+    pool_before = d["pool"].clone()
+    rows = torch.tensor([1, 0, 3, 2], dtype=torch.int32, device="cuda")
+    buf = torch.zeros((4, L, case.H_v, case.d_v, case.d_k), dtype=torch.float32, device="cuda")
+    layer = SimpleNamespace(num_k_heads=case.H_qk, num_v_heads=case.H_v, head_k_dim=case.d_k,
+                            head_v_dim=case.d_v, A_log=d["A_log"], dt_bias=d["dt_bias"], scale=case.scale,
+                            layer_id=0)
+    fb = SimpleNamespace(forward_mode="TARGET_VERIFY", state_slots=d["slot"], state_pool=[d["pool"]],
+                         cu_seqlens=d["cu"], has_initial_state=d["has_init"], max_seqlen=L,
+                         spec_states=[buf], spec_state_slots=rows)
+    out = gdn.forward_gdn(layer, fb, d["mixed"], d["a"], d["b"])
+    torch.cuda.synchronize()
+    spec = {}
+    ref, _, _ = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                  case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale,
+                                  spec_slot=rows.cpu().numpy(), spec=spec)
+    assert_close(out.float().cpu().numpy().reshape(ref.shape), ref, "forward_gdn verify out")
+    got = buf.cpu().numpy()
+    for (r, i), S in spec.items():
+        assert_close(got[r, i], S, f"forward_gdn verify state {r},{i}")
+    assert torch.equal(d["pool"], pool_before)
