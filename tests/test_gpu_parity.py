@@ -595,3 +595,60 @@ def test_forward_gdn_target_verify(gdn_lib):
     for (r, i), S in spec.items():
         assert_close(got[r, i], S, f"forward_gdn verify state {r},{i}")
     assert torch.equal(d["pool"], pool_before)
+
+
+# ------------------------------------------------------------------ graph-captured decode
+def test_decode_graph_capture_padded(gdn_lib):
+    """gdn_decode (gate folded in) captured once in a HIP graph over static buffers of 32
+    rows of which 20 are live (slot -1 pads the rest), then replayed three times with new
+    inputs copied into the static buffers and eager work in between.  Every replay is
+    checked against the oracle step from the previous states; padded rows stay untouched."""
+    gdn = gdn_lib
+    _announce("decode graph capture, 20 live of 32 static rows")
+    rows, live, H_qk, H_v, d = 32, 20, 2, 4, 128
+    width = 2 * H_qk * d + H_v * d
+    rng = np.random.default_rng(91)
+    pool = torch.from_numpy(rng.normal(0, 0.1, (40, H_v, d, d)).astype(np.float32)).cuda()
+    slot_h = np.full(rows, -1, np.int32)
+    slot_h[:live] = rng.permutation(40)[:live]
+    slot = torch.from_numpy(slot_h).cuda()
+    A_log = torch.from_numpy(np.log(rng.uniform(1, 16, H_v)).astype(np.float32)).cuda()
+    dt_bias = torch.from_numpy(rng.normal(0, 0.5, H_v).astype(np.float32)).cuda()
+    mixed = torch.zeros((rows, width), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((rows, H_v), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((rows, H_v), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((rows, H_v, d), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    out0 = out.clone()
+    q, k, v = gdn.split_mixed_qkv(mixed, H_qk, H_v, d, d)
+    g_in = gdn.gdn_gate_inputs(a, b, A_log, dt_bias)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # (capture happens off the default stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            gdn.decode(q, k, v, None, None, slot, pool, scale=d ** -0.5, out=out, gate=g_in)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0), "capture must not run the kernel"
+    states = pool.cpu().numpy().astype(np.float64)
+    for rep in range(3):
+        m = rng.standard_normal((rows, width)).astype(np.float32)
+        av = rng.standard_normal((rows, H_v)).astype(np.float32)
+        bv = rng.standard_normal((rows, H_v)).astype(np.float32)
+        mixed.copy_(torch.from_numpy(m).to(torch.bfloat16))
+        a.copy_(torch.from_numpy(av).to(torch.bfloat16))
+        b.copy_(torch.from_numpy(bv).to(torch.bfloat16))
+        _ = (mixed.float() * 2).sum()          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        mh = mixed[:live].float().cpu().numpy()
+        nq = H_qk * d
+        ref, _, fin = oracle.gdn_decode(mh[:, :nq].reshape(live, H_qk, d), mh[:, nq:2 * nq].reshape(live, H_qk, d),
+                                        mh[:, 2 * nq:].reshape(live, H_v, d), a[:live].float().cpu().numpy(),
+                                        b[:live].float().cpu().numpy(), A_log.cpu().numpy(),
+                                        dt_bias.cpu().numpy(), slot_h[:live], states, d ** -0.5)
+        assert_close(out[:live].float().cpu().numpy(), ref, f"replay {rep} out")
+        assert torch.equal(out[live:], out0[live:]), "padded rows were written"
+        states = oracle.apply_final_states(states, fin)
+        assert_close(pool.cpu().numpy()[slot_h[:live]], states[slot_h[:live]], f"replay {rep} states")
