@@ -29,7 +29,7 @@ Parity pins: every function here is pinned by tests in tests/test_oracle_pins.py
 is "parity unpinned".
 """
 from .gdn import (softplus, sigmoid, gdn_gate, ssd_gate, l2_normalize, gdn_extend,
-                  gdn_decode, apply_final_states, ssd_combined)
+                  gdn_decode, apply_final_states, ssd_combined, causal_conv1d)
 
 __all__ = ["softplus", "sigmoid", "gdn_gate", "ssd_gate", "l2_normalize", "gdn_extend",
-           "gdn_decode", "apply_final_states", "ssd_combined"]
+           "gdn_decode", "apply_final_states", "ssd_combined", "causal_conv1d"]

@@ -245,3 +245,45 @@ def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False
             ckpts[int(ckpt_slot[bi])] = S.copy()
         finals[bi] = S
     return out, (finals if return_final_states else None)
+
+
+# ---------------------------------------------------------------- short causal conv1d
+def causal_conv1d(x, weight, bias, cu_seqlens, slot, has_init, conv_pool, activation=True,
+                  seqs=None):
+    """Depthwise causal conv1d over packed sequences with a per-slot conv state (the
+    short convolution in front of the GDN layer; the plain reading of the conv[0]
+    state buffer of the SGLang GDN test article).
+
+    x [T, C]; weight [C, K]; bias [C] or None; conv_pool[slot] -> [C, K - 1] holds the
+    last K - 1 inputs of the slot's sequence so far, oldest first.  Sequence n with
+    slot[n] >= 0 sees the window w = (conv_pool[slot[n]] if has_init[n] else zeros)
+    followed by its own inputs:
+        y_t = sum_j weight[:, j] * w[t - t0 + j] + bias     (j = 0 .. K-1)
+        out_t = silu(y_t) if activation else y_t
+    and its new state is the last K - 1 rows of w (for a short sequence partly the
+    old state).  slot[n] < 0 skips the sequence.
+    Returns (out float64 [T, C] (NaN where not written), states dict slot -> [C, K-1]).
+    """
+    x = np.asarray(x, dtype=F64)
+    w = np.asarray(weight, dtype=F64)
+    T, Cn = x.shape
+    K = w.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    b = np.zeros(Cn) if bias is None else np.asarray(bias, dtype=F64)
+    has_init = np.ones(N, np.int64) if has_init is None else np.asarray(has_init, np.int64)
+    out = np.full((T, Cn), np.nan, dtype=F64)
+    states = {}
+    for n in (range(N) if seqs is None else seqs):
+        s = int(slot[n])
+        if s < 0:
+            continue
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        prev = np.asarray(conv_pool[s], dtype=F64).T if has_init[n] else np.zeros((K - 1, Cn))
+        win = np.concatenate([prev, x[t0:t1]], axis=0)              # [K-1 + len, C]
+        for t in range(t0, t1):
+            i = t - t0
+            y = b + np.sum(win[i:i + K] * w.T, axis=0)
+            out[t] = y / (1.0 + np.exp(-y)) if activation else y
+        states[s] = win[len(win) - (K - 1):].T.copy()               # [C, K-1]
+    return out, states

@@ -644,3 +644,58 @@ def test_verify_tree_states_and_outputs():
                 _close(spec[(row, i)][h], S)
                 qq = c.q[t0 + i, h // r].astype(np.float64)
                 _close(out[t0 + i, h], c.scale * S @ (qq / np.sqrt(qq @ qq + 1e-6)))
+
+
+# ------------------------------------------------------------------ short causal conv1d
+def _conv_case(seed=4, lens=(6, 2, 5, 0), C=7, K=4, has_init=(1, 1, 0, 1)):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return dict(x=rng.standard_normal((T, C)), w=rng.standard_normal((C, K)), b=rng.standard_normal(C),
+                cu=cu, slot=np.array([3, 0, 2, 1]), has_init=np.array(has_init),
+                pool=rng.standard_normal((5, C, K - 1)))
+
+
+def test_conv_matches_numpy_convolve():
+    """Each channel of each sequence equals numpy's full convolution of [state; x] with the
+    reversed kernel (valid part), plus bias, through silu (scipy expit); the new state is
+    the last K-1 window rows."""
+    c = _conv_case()
+    out, st = oracle.causal_conv1d(c["x"], c["w"], c["b"], c["cu"], c["slot"], c["has_init"], c["pool"])
+    K = c["w"].shape[1]
+    for n in range(4):
+        t0, t1 = c["cu"][n], c["cu"][n + 1]
+        s = c["slot"][n]
+        prev = c["pool"][s].T if c["has_init"][n] else np.zeros((K - 1, c["x"].shape[1]))
+        win = np.concatenate([prev, c["x"][t0:t1]])
+        for ch in range(c["x"].shape[1] if t1 > t0 else 0):
+            y = np.convolve(win[:, ch], c["w"][ch, ::-1], mode="valid") + c["b"][ch]
+            _close(out[t0:t1, ch], y * scipy.special.expit(y))
+        _close(st[s], win[-(K - 1):].T)
+    assert list(st) == [3, 0, 2, 1]                  # the empty sequence keeps its state
+    _close(st[1], c["pool"][1])
+
+
+def test_conv_split_resume_and_decode():
+    """conv(A || B) == conv(A) then conv(B) from the state == conv(A) then one token at a
+    time; without activation the map is linear in x (bias 0)."""
+    c = _conv_case(lens=(9,), has_init=(1,))
+    c["slot"] = np.array([2])
+    full, fst = oracle.causal_conv1d(c["x"], c["w"], c["b"], np.array([0, 9]), c["slot"], None, c["pool"])
+    for cut in range(10):
+        pool = c["pool"].copy()
+        outs = []
+        for (a0, a1) in ((0, cut), (cut, 9)):
+            o, st = oracle.causal_conv1d(c["x"][a0:a1], c["w"], c["b"], np.array([0, a1 - a0]), c["slot"], None, pool)
+            outs.append(o)
+            pool[2] = st[2]
+        _close(np.concatenate(outs), full)
+        _close(pool[2], fst[2])
+    pool = c["pool"].copy()
+    for t in range(9):
+        o, st = oracle.causal_conv1d(c["x"][t:t + 1], c["w"], c["b"], np.array([0, 1]), c["slot"], None, pool)
+        _close(o[0], full[t])
+        pool[2] = st[2]
+    o1, _ = oracle.causal_conv1d(c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
+    o2, _ = oracle.causal_conv1d(2 * c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
+    _close(o2, 2 * o1)
