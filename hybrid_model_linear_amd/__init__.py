@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
   gate / ssd_gate      a, b -> (log g, beta)               -> gdn_gate
   extend               packed varlen extend over a pool   -> gdn_extend
   decode               one token per sequence, in place   -> gdn_decode
+  conv1d               short causal conv, varlen          -> gdn_conv1d
+  conv1d_update        short causal conv, one token/row   -> gdn_conv1d_update
   validate_slots       opt-in device check of slots       -> gdn_validate_slots
 and the two call shapes of the pages:
   forward_gdn(layer, forward_batch, mixed_qkv, a, b)  (pymllm HybridAttnBackend.forward_gdn)
@@ -24,7 +26,8 @@ import torch
 from . import _lib
 from ._lib import GDN_BF16, GDN_F32, GDN_MODE_GDN, GDN_MODE_SSD, GDNError
 
-__all__ = ["load", "gate", "ssd_gate", "extend", "decode", "validate_slots", "forward_gdn",
+__all__ = ["load", "gate", "ssd_gate", "extend", "decode", "conv1d", "conv1d_update",
+           "validate_slots", "forward_gdn",
            "ssd_combined_fwd", "GDNError", "split_mixed_qkv"]
 
 
@@ -307,6 +310,71 @@ def validate_slots(slot: torch.Tensor, num_slots: int) -> int:
     return int(flag.item())
 
 
+# ------------------------------------------------------------------ short causal conv
+def _conv_args(x, weight, bias, slot, pool, activation, out, keep_pool, T, N):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"x must be [T, D] with unit channel stride, got {tuple(x.shape)} / {x.stride()}")
+    D = x.shape[1]
+    if weight.dim() != 2 or weight.shape[0] != D or not weight.is_contiguous():
+        raise ValueError(f"weight must be a contiguous [{D}, K] tensor, got {tuple(weight.shape)}")
+    K = weight.shape[1]
+    if pool.dim() != 3 or pool.shape[1:] != (D, K - 1) or pool.stride(2) != 1 or pool.stride(1) != K - 1:
+        raise ValueError(f"pool must be [num_slots, {D}, {K - 1}] with contiguous slots' rows, got "
+                         f"{tuple(pool.shape)} / {pool.stride()}")
+    for t, nm in ((weight, "weight"), (bias, "bias"), (pool, "pool")):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bf16")
+    if bias is not None and (bias.shape != (D,) or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous [{D}] vector")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (T, D) or out.dtype != torch.bfloat16 or out.stride(1) != 1:
+        raise ValueError(f"out must be bf16 [{T}, {D}] with unit channel stride")
+    _i32(slot, "slot", N)
+    a = _lib.ConvArgs(dtype=GDN_BF16, K=K, activation=int(bool(activation)), N=N, T=T, D=D,
+                      x=_ptr(x), x_stride=x.stride(0) if T > 1 else D, weight=_ptr(weight),
+                      bias=_ptr(bias), slot=_ptr(slot), pool=_ptr(pool), num_slots=pool.shape[0],
+                      pool_stride=pool.stride(0) if pool.shape[0] > 1 else D * (K - 1),
+                      out=_ptr(out), out_stride=out.stride(0) if T > 1 else D,
+                      keep_pool=int(bool(keep_pool)))
+    return a, out
+
+
+def conv1d(x, weight, bias, cu_seqlens, slot, pool, *, has_init=None, activation=True, out=None,
+           keep_pool=False):
+    """Short causal depthwise conv1d over packed sequences with a conv-state pool
+    (gdn_conv1d).  x [T, D] bf16; weight [D, K] bf16 (K in 2..4, the last tap on the
+    current input); bias [D] bf16 or None; cu_seqlens int32 [N+1]; slot int32 [N]
+    (negative skips the sequence); pool bf16 [num_slots, D, K-1], the last K-1 inputs
+    per slot, updated in place unless keep_pool; has_init int32 [N] or None (= all 1).
+    Returns out [T, D] bf16 = silu(conv) (or the plain conv without activation)."""
+    lib = _lib.load()
+    dev = _on_gpu(x, weight, bias, cu_seqlens, slot, pool, has_init, out)
+    N = slot.shape[0]
+    T = x.shape[0]
+    _i32(cu_seqlens, "cu_seqlens", N + 1)
+    if has_init is not None:
+        _i32(has_init, "has_init", N)
+    a, out = _conv_args(x, weight, bias, slot, pool, activation, out, keep_pool, T, N)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.has_init = _ptr(has_init)
+    _lib.check("gdn_conv1d", lib.gdn_conv1d(ct.byref(a), _stream(dev)))
+    return out
+
+
+def conv1d_update(x, weight, bias, slot, pool, *, activation=True, out=None, keep_pool=False):
+    """One token per row (gdn_conv1d_update): x [B, D] bf16, row b continues
+    pool[slot[b]] (negative = padding row, left untouched); out may be x itself."""
+    lib = _lib.load()
+    dev = _on_gpu(x, weight, bias, slot, pool, out)
+    B = x.shape[0]
+    a, out = _conv_args(x, weight, bias, slot, pool, activation, out, keep_pool, B, B)
+    _lib.check("gdn_conv1d_update", lib.gdn_conv1d_update(ct.byref(a), _stream(dev)))
+    return out
+
+
 # ------------------------------------------------------------------ forward_gdn adapter
 _DECODE_MODES = {"decode", "idle"}
 _EXTEND_MODES = {"extend", "mixed", "draft_extend", "draft_extend_v2", "target_verify",
@@ -360,7 +428,13 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
            spec_state_slots int32 [N] and spec_parents int32 [T] (token trees): the
            state after every draft token is recorded there and the pool is left
            unwritten.
-    mixed_qkv: [T, 2 H_qk d_k + H_v d_v], already convolved; a, b: [T, H_v].
+    mixed_qkv: [T, 2 H_qk d_k + H_v d_v]; a, b: [T, H_v].  mixed_qkv is taken as
+    already convolved unless the layer carries the short conv's taps: conv_weight
+    bf16 [D, K] (or [D, 1, K]) with optional conv_bias [D]; then forward_batch.conv_pool
+    (indexable by layer_id -> bf16 [num_slots, D, K-1]) holds the conv states of the
+    same slots, and the conv (with silu) runs first -- gdn_conv1d / gdn_conv1d_update,
+    leaving the conv pool unwritten in target verify (token trees are not supported
+    with the conv).
     Returns out [T, H_v * d_v] in mixed_qkv's dtype."""
     kind = _mode_kind(forward_batch.forward_mode)
     H_qk, H_v = layer.num_k_heads, layer.num_v_heads
@@ -368,10 +442,26 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     scale = getattr(layer, "scale", None)
     scale = d_k ** -0.5 if scale is None else scale
     pool = forward_batch.state_pool[layer.layer_id]
-    q, k, v = split_mixed_qkv(mixed_qkv, H_qk, H_v, d_k, d_v)
     T = mixed_qkv.shape[0]
     if T == 0:
         return mixed_qkv.new_empty((0, H_v * d_v))
+    verify = kind == "extend" and _is_target_verify(forward_batch.forward_mode)
+    conv_w = getattr(layer, "conv_weight", None)
+    if conv_w is not None:
+        if conv_w.dim() == 3:
+            conv_w = conv_w.reshape(conv_w.shape[0], conv_w.shape[2])
+        cpool = forward_batch.conv_pool[layer.layer_id]
+        cbias = getattr(layer, "conv_bias", None)
+        if kind == "decode":
+            mixed_qkv = conv1d_update(mixed_qkv, conv_w, cbias, forward_batch.state_slots, cpool)
+        else:
+            if verify and getattr(forward_batch, "spec_parents", None) is not None:
+                raise NotImplementedError("the short conv over token trees is not supported")
+            mixed_qkv = conv1d(mixed_qkv, conv_w, cbias, forward_batch.cu_seqlens,
+                               forward_batch.state_slots, cpool,
+                               has_init=getattr(forward_batch, "has_initial_state", None),
+                               keep_pool=verify)
+    q, k, v = split_mixed_qkv(mixed_qkv, H_qk, H_v, d_k, d_v)
     g = gdn_gate_inputs(a, b, layer.A_log, layer.dt_bias)
     # the gate is folded into the layer kernel when a, b share q's dtype (else its own launch)
     log_g = beta = None
@@ -382,7 +472,7 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
         o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale, gate=g)
     else:
         spec = getattr(forward_batch, "spec_states", None)
-        verify = spec is not None and _is_target_verify(forward_batch.forward_mode)
+        verify = verify and spec is not None
         o = extend(q, k, v, log_g, beta, forward_batch.cu_seqlens, forward_batch.state_slots, pool,
                    has_init=getattr(forward_batch, "has_initial_state", None), scale=scale,
                    max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0), gate=g,

@@ -10,10 +10,11 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
-            "gdn_validate_slots", "gdn_status_str", "gdn_last_hip_error", "gdn_abi_version"]
+            "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_status_str",
+            "gdn_last_hip_error", "gdn_abi_version"]
 
 
 class GateArgs(C.Structure):
@@ -53,6 +54,15 @@ class DecodeArgs(C.Structure):
                 ("_pad1", C.c_int32)]
 
 
+class ConvArgs(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("K", C.c_int32), ("activation", C.c_int32), ("N", C.c_int32),
+                ("T", C.c_int64), ("D", C.c_int64), ("x", C.c_void_p), ("x_stride", C.c_int64),
+                ("weight", C.c_void_p), ("bias", C.c_void_p), ("cu_seqlens", C.c_void_p),
+                ("slot", C.c_void_p), ("has_init", C.c_void_p), ("pool", C.c_void_p),
+                ("num_slots", C.c_int64), ("pool_stride", C.c_int64), ("out", C.c_void_p),
+                ("out_stride", C.c_int64), ("keep_pool", C.c_int32), ("_pad0", C.c_int32)]
+
+
 _lib = None
 
 
@@ -71,9 +81,12 @@ def load(path: str | None = None) -> C.CDLL:
     lib.gdn_decode.argtypes = [C.POINTER(DecodeArgs), C.c_void_p]
     lib.gdn_extend_gated.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.c_void_p]
     lib.gdn_decode_gated.argtypes = [C.POINTER(DecodeArgs), C.POINTER(GateArgs), C.c_void_p]
+    lib.gdn_conv1d.argtypes = [C.POINTER(ConvArgs), C.c_void_p]
+    lib.gdn_conv1d_update.argtypes = [C.POINTER(ConvArgs), C.c_void_p]
     lib.gdn_validate_slots.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p]
     for fn in ("gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
-               "gdn_validate_slots", "gdn_last_hip_error", "gdn_abi_version"):
+               "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_last_hip_error",
+               "gdn_abi_version"):
         getattr(lib, fn).restype = C.c_int
     lib.gdn_status_str.argtypes = [C.c_int]
     lib.gdn_status_str.restype = C.c_char_p

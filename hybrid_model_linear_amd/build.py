@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gate.hip", "recurrent.hip", "chunk.hip", "validate.hip", "gdn_abi.cpp"]
+SOURCES = ["gate.hip", "recurrent.hip", "chunk.hip", "conv.hip", "validate.hip", "gdn_abi.cpp"]
 ARCH = "gfx950"
 
 

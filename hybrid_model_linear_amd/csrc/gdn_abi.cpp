@@ -283,9 +283,72 @@ int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* strea
   return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
 }
 
+// Short causal conv: host checks shared by gdn_conv1d and gdn_conv1d_update.
+bool aligned16(const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; }
+
+// Byte ranges [lo, hi) of rows 0..rows-1 of a [rows, width] bf16 matrix with a row stride.
+bool rows_overlap(const void* a, int64_t a_rows, int64_t a_stride, int64_t a_width, const void* b,
+                  int64_t b_rows, int64_t b_stride, int64_t b_width) {
+  if (a_rows <= 0 || b_rows <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = a0 + (uintptr_t)((a_rows - 1) * a_stride + a_width) * 2;
+  const uintptr_t b1 = b0 + (uintptr_t)((b_rows - 1) * b_stride + b_width) * 2;
+  return a0 < b1 && b0 < a1;
+}
+
+int conv_impl(const gdn_conv_args* a, bool update, void* stream) {
+  if (!a) return GDN_E_NULL;
+  if (a->dtype != GDN_BF16) return GDN_E_DTYPE;
+  if (a->K < 2 || a->K > 4) return GDN_E_UNSUPPORTED;
+  if (a->N < 0 || a->T < 0 || a->T > INT32_MAX || a->D < 8 || a->D % 8 != 0 ||
+      a->D > (int64_t)INT32_MAX / 8 || a->num_slots <= 0)
+    return GDN_E_SHAPE;
+  if (update ? a->T != a->N : (a->N == 0 && a->T != 0)) return GDN_E_SHAPE;
+  if (a->x_stride < a->D || a->x_stride % 8 != 0 || a->out_stride < a->D || a->out_stride % 8 != 0 ||
+      a->pool_stride < a->D * (a->K - 1) || a->pool_stride % 8 != 0)
+    return GDN_E_SHAPE;
+  if (a->N == 0) return GDN_OK;
+  if (!a->weight || !a->slot || !a->pool || (!update && !a->cu_seqlens)) return GDN_E_NULL;
+  if (a->T > 0 && (!a->x || !a->out)) return GDN_E_NULL;
+  if (!aligned16(a->x) || !aligned16(a->out) || !aligned16(a->weight) || !aligned16(a->bias) ||
+      !aligned16(a->pool))
+    return GDN_E_SHAPE;
+  if (!update) {
+    // out rows are written while later tiles still read x rows before them, and the
+    // pool is read by the output pass: out may overlap neither
+    if (rows_overlap(a->out, a->T, a->out_stride, a->D, a->x, a->T, a->x_stride, a->D) ||
+        rows_overlap(a->out, a->T, a->out_stride, a->D, a->pool, a->num_slots, a->pool_stride,
+                     a->D * (a->K - 1)))
+      return GDN_E_SHAPE;
+  }
+  gdn::ConvLaunch p{};
+  p.K = a->K;
+  p.act = a->activation != 0;
+  p.T = a->T;
+  p.N = a->N;
+  p.D = (int)a->D;
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.x_stride = a->x_stride;
+  p.weight = static_cast<const uint16_t*>(a->weight);
+  p.bias = static_cast<const uint16_t*>(a->bias);
+  p.cu = a->cu_seqlens;
+  p.slot = a->slot;
+  p.has_init = a->has_init;
+  p.pool = static_cast<uint16_t*>(a->pool);
+  p.pool_stride = a->pool_stride;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.out_stride = a->out_stride;
+  p.keep_pool = a->keep_pool != 0;
+  return hip_status(update ? gdn::launch_conv_update(p, (hipStream_t)stream)
+                           : gdn::launch_conv(p, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+int gdn_conv1d(const gdn_conv_args* a, void* stream) { return conv_impl(a, false, stream); }
+int gdn_conv1d_update(const gdn_conv_args* a, void* stream) { return conv_impl(a, true, stream); }
 
 int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
                        void* stream) {

@@ -84,11 +84,34 @@ struct SeqLaunch {
   int keep_pool;
 };
 
+// Short causal conv1d (bf16, width K) over packed sequences with a conv-state pool.
+struct ConvLaunch {
+  int K;
+  int act;                     // silu after the sum
+  int64_t T;
+  int N;
+  int D;
+  const uint16_t* x;
+  int64_t x_stride;
+  const uint16_t* weight;      // [D, K]
+  const uint16_t* bias;        // [D] or null
+  const int32_t* cu;           // [N + 1] (extend)
+  const int32_t* slot;         // [N]
+  const int32_t* has_init;     // [N] or null (extend)
+  uint16_t* pool;              // [*, D, K - 1], slot stride pool_stride
+  int64_t pool_stride;
+  uint16_t* out;
+  int64_t out_stride;
+  int keep_pool;
+};
+
 hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);
 hipError_t launch_recurrent(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_chunked(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_validate_slots(const int32_t* slot, int n, int64_t num_slots, int32_t* flag,
                                  hipStream_t stream);
 bool chunked_supported(const SeqLaunch& p);
+hipError_t launch_conv(const ConvLaunch& p, hipStream_t stream);          // varlen: outputs, then states
+hipError_t launch_conv_update(const ConvLaunch& p, hipStream_t stream);   // one token per row
 
 }  // namespace gdn

@@ -176,6 +176,46 @@ def make_gdn_case(name, *, seed, lens, has_init, H_qk, H_v, d_k, d_v, dtype="bf1
                    pool=pool, pool_sigma=pool_sigma, pool_seed=pool_seed, meta=dict(meta or {}))
 
 
+@dataclass
+class ConvCase:
+    """Inputs of one short causal conv call (gdn_conv1d), bf16 values held as fp32.
+
+    x is the projected mixed_qkv before the conv (standard normal); weight [D, K] and
+    bias [D] are uniform in +-1/sqrt(K), the default init of a depthwise Conv1d with
+    K taps; pool [num_slots, D, K-1] holds earlier inputs (standard normal)."""
+    x: np.ndarray
+    weight: np.ndarray
+    bias: np.ndarray
+    cu_seqlens: np.ndarray
+    slot: np.ndarray
+    has_init: np.ndarray
+    pool: np.ndarray
+
+    @property
+    def T(self) -> int:
+        return int(self.x.shape[0])
+
+
+def make_conv_case(*, seed, lens, D, K=4, has_init=1, num_slots=None, slot=None) -> ConvCase:
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    N = len(lens)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    x = bf16_round(rng.standard_normal((int(lens.sum()), D), dtype=np.float32))
+    lim = np.float32(1.0 / np.sqrt(K))
+    weight = bf16_round(rng.uniform(-lim, lim, (D, K)).astype(np.float32))
+    bias = bf16_round(rng.uniform(-lim, lim, D).astype(np.float32))
+    if num_slots is None:
+        num_slots = max(8, 2 * N)
+    if slot is None:
+        slot = rng.permutation(num_slots)[:N].astype(np.int32)
+    pool = bf16_round(rng.standard_normal((num_slots, D, K - 1), dtype=np.float32))
+    return ConvCase(x=x, weight=weight, bias=bias, cu_seqlens=cu,
+                    slot=np.asarray(slot, np.int32),
+                    has_init=np.broadcast_to(np.asarray(has_init, np.int32), (N,)).copy(), pool=pool)
+
+
 def config0_tiny(seed: int = 1000):
     """Tiny fp32 extend followed by one decode token per sequence.
 

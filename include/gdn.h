@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -246,6 +246,67 @@ int gdn_decode(const gdn_decode_args* args, void* stream);
  * ungated call. */
 int gdn_extend_gated(const gdn_extend_args* args, const gdn_gate_args* gate, void* stream);
 int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, void* stream);
+
+/* ---------------------------------------------------------------- short causal conv
+ * The depthwise causal conv1d of width K (and SiLU) that turns the input projection
+ * into mixed_qkv in front of the layer, with each sequence's last K - 1 inputs kept
+ * per slot in a conv-state pool: the per-layer conv state that sits next to the
+ * temporal state in the hybrid model's memory pool (SGLang GDN test-matrix article,
+ * framerc.cn, memory-pool section, its conv[0] buffer).  Channel c of sequence n
+ * sees the window  w = (has_init[n] ? pool[slot[n]][c] : zeros) || its own inputs,
+ * and its token i (= t - cu_seqlens[n]) gives
+ *     out[t, c] = act(bias[c] + sum_{j < K} weight[c, j] * w[i + j])
+ *     act(y) = y * sigmoid(y) when activation != 0, y otherwise
+ * (the causal convolution: weight[c, K - 1] multiplies the current input).  The
+ * slot's new state is the last K - 1 entries of w: partly the old state for a
+ * sequence shorter than K - 1, the start state for an empty one.
+ *   x      : bf16 [T, D], token stride x_stride (the projected mixed_qkv, before the conv)
+ *   weight : bf16 [D, K], a channel's K taps contiguous, oldest input first
+ *   bias   : bf16 [D], or NULL for none
+ *   pool   : bf16 [num_slots, D, K - 1] with slot stride pool_stride (>= D (K - 1)),
+ *            a channel's entries contiguous, oldest first; read, and written in place
+ *            unless keep_pool != 0 (then only read: target-verify passes whose
+ *            accepted prefix the caller commits later)
+ *   out    : bf16 [T, D], token stride out_stride; the fp32 result rounded to nearest even
+ * cu_seqlens, slot, has_init (NULL = all 1) and num_slots follow gdn_extend, with
+ * the same rules for negative slots and device-resident indices.
+ * Supported: dtype GDN_BF16 (else GDN_E_DTYPE); K in {2, 3, 4} (else
+ * GDN_E_UNSUPPORTED).  D >= 8 and a multiple of 8; x, out, weight, bias and pool
+ * 16-byte aligned; x_stride, out_stride >= D and pool_stride multiples of 8
+ * (else GDN_E_SHAPE).  The fp32 arithmetic: the K products and the bias summed in
+ * fp32, then the activation. */
+typedef struct gdn_conv_args {
+  int32_t dtype;
+  int32_t K;
+  int32_t activation;
+  int32_t N;             /* sequences (gdn_conv1d) or rows (gdn_conv1d_update) */
+  int64_t T;             /* tokens; gdn_conv1d_update: must equal N */
+  int64_t D;             /* channels */
+  const void* x;
+  int64_t x_stride;
+  const void* weight;
+  const void* bias;
+  const int32_t* cu_seqlens; /* [N + 1]; ignored by gdn_conv1d_update */
+  const int32_t* slot;       /* [N] */
+  const int32_t* has_init;   /* [N] or NULL; ignored by gdn_conv1d_update */
+  void* pool;
+  int64_t num_slots;
+  int64_t pool_stride;
+  void* out;
+  int64_t out_stride;
+  int32_t keep_pool;
+  int32_t _pad0;
+} gdn_conv_args;
+
+/* Packed varlen (prefill / extend): two launches on `stream`, the outputs (which
+ * read the old states) and then the new states.  out must not overlap x or the pool
+ * (else GDN_E_SHAPE).  T = 0 launches only the state pass (empty sequences keep or
+ * clear their slot as above); N = 0 launches nothing. */
+int gdn_conv1d(const gdn_conv_args* args, void* stream);
+/* Decode: one token per row (T = N = rows), row b always starts from pool[slot[b]]
+ * (cu_seqlens, has_init ignored); slot[b] < 0 marks a padding row whose output row
+ * and slot stay untouched.  One launch; out may be x itself (same rows). */
+int gdn_conv1d_update(const gdn_conv_args* args, void* stream);
 
 /* Device-side check of slot[0..n): *flag (device int32) receives 0 when every
  * non-negative slot is < num_slots and no non-negative slot repeats, 1 when one

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     """offsetof/sizeof from the C compiler == ctypes layout used by the binding."""
     structs = {"gdn_gate_args": _lib.GateArgs, "gdn_extend_args": _lib.ExtendArgs,
-               "gdn_decode_args": _lib.DecodeArgs}
+               "gdn_decode_args": _lib.DecodeArgs, "gdn_conv_args": _lib.ConvArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void){']
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -113,6 +113,49 @@ def test_extend_null_and_empty():
     assert lib.gdn_extend(ct.byref(_ext(N=0)), None) == _lib.GDN_OK      # nothing to do
     a = _ext(cu_seqlens=FAKE, slot=FAKE, pool=FAKE)                      # q..out missing
     assert lib.gdn_extend(ct.byref(a), None) == _lib.GDN_E_NULL
+
+
+def _conv(**kw):
+    base = dict(dtype=1, K=4, activation=1, N=2, T=10, D=64, x=ct.c_void_p(0x10000), x_stride=64,
+                weight=ct.c_void_p(0x20000), cu_seqlens=FAKE, slot=FAKE, pool=ct.c_void_p(0x30000),
+                num_slots=4, pool_stride=192, out=ct.c_void_p(0x40000), out_stride=64)
+    base.update(kw)
+    return _lib.ConvArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), _lib.GDN_E_DTYPE),                           # bf16 only
+    (dict(K=5), _lib.GDN_E_UNSUPPORTED),
+    (dict(K=1), _lib.GDN_E_UNSUPPORTED),
+    (dict(D=12), _lib.GDN_E_SHAPE),                              # channels in vectors of 8
+    (dict(D=0), _lib.GDN_E_SHAPE),
+    (dict(x_stride=60), _lib.GDN_E_SHAPE),                       # row stride < D
+    (dict(out_stride=72 + 4), _lib.GDN_E_SHAPE),                 # not a multiple of 8
+    (dict(pool_stride=184), _lib.GDN_E_SHAPE),                   # < D (K - 1)
+    (dict(num_slots=0), _lib.GDN_E_SHAPE),
+    (dict(N=0), _lib.GDN_E_SHAPE),                               # tokens without sequences
+    (dict(N=0, T=0), _lib.GDN_OK),                               # nothing to do
+    (dict(weight=None), _lib.GDN_E_NULL),
+    (dict(cu_seqlens=None), _lib.GDN_E_NULL),
+    (dict(x=None), _lib.GDN_E_NULL),
+    (dict(x=ct.c_void_p(0x10008)), _lib.GDN_E_SHAPE),            # not 16-byte aligned
+    (dict(bias=ct.c_void_p(0x50004)), _lib.GDN_E_SHAPE),
+    (dict(out=ct.c_void_p(0x10000 + 2 * 64 * 9)), _lib.GDN_E_SHAPE),   # out overlaps x's last row
+    (dict(out=ct.c_void_p(0x30000 + 16)), _lib.GDN_E_SHAPE),     # out overlaps the pool
+])
+def test_conv_validation(kw, status):
+    lib = gdn.load()
+    assert lib.gdn_conv1d(ct.byref(_conv(**kw)), None) == status
+
+
+def test_conv_update_validation():
+    lib = gdn.load()
+    assert lib.gdn_conv1d_update(None, None) == _lib.GDN_E_NULL
+    assert lib.gdn_conv1d_update(ct.byref(_conv(N=3, T=4)), None) == _lib.GDN_E_SHAPE   # T != rows
+    assert lib.gdn_conv1d_update(ct.byref(_conv(N=0, T=0)), None) == _lib.GDN_OK
+    # cu_seqlens is not needed; out may be x itself (checked only for the varlen call)
+    a = _conv(N=3, T=3, cu_seqlens=None, out=ct.c_void_p(0x10000), slot=None)
+    assert lib.gdn_conv1d_update(ct.byref(a), None) == _lib.GDN_E_NULL                # slot missing
 
 
 def test_gate_and_decode_validation():
