@@ -199,6 +199,43 @@ def cpu_baseline(ext, seconds):
                       f"of 4096, state carried in 64-token blocks) x all {H_V} heads, {spent:.1f} s on one thread"}
 
 
+def bench_conv(torch, gdn, T_e, n_seq, T_d, steps):
+    """The short causal conv in front of the layer (width 4, silu, bf16 conv states),
+    timed on its own: it is not part of the step.  Prefill: the step's 8 x 4096 tokens
+    of the q | k | v width (8192 channels) from earlier states; decode: 256 rows on a
+    1024-slot conv pool.  HIP events on torch's current stream, the launch stream."""
+    dev, K, Dc = "cuda", 4, 2 * H_QK * D + H_V * D
+    g = torch.Generator(device=dev).manual_seed(5)
+    bf = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    w, b = bf(Dc, K) * 0.5, bf(Dc) * 0.5
+    L = T_e // n_seq
+    cu = torch.arange(0, T_e + 1, L, dtype=torch.int32, device=dev)
+    x_e, out_e, pool_e = bf(T_e, Dc), torch.empty((T_e, Dc), dtype=torch.bfloat16, device=dev), bf(16, Dc, K - 1)
+    slot_e = torch.arange(n_seq, dtype=torch.int32, device=dev)
+    x_d, out_d, pool_d = bf(T_d, Dc), torch.empty((T_d, Dc), dtype=torch.bfloat16, device=dev), bf(1024, Dc, K - 1)
+    slot_d = torch.randperm(1024, generator=g, device=dev)[:T_d].to(torch.int32)
+    calls = {"prefill": lambda: gdn.conv1d(x_e, w, b, cu, slot_e, pool_e, out=out_e),
+             "decode": lambda: gdn.conv1d_update(x_d, w, b, slot_d, pool_d, out=out_d)}
+    state = Dc * (K - 1) * 2
+    work = {"prefill": T_e * Dc * 4 + n_seq * 2 * state, "decode": T_d * (Dc * 4 + 2 * state)}
+    res = {"workload": f"prefill {n_seq}x{L} and decode {T_d}x1, {Dc} channels, width {K}"}
+    for name, fn in calls.items():
+        for _ in range(20):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = work[name] / (us * 1e-6) / 1e9
+        res[name] = {"avg_us": round(us, 2), "bytes": work[name], "GB_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_prof:
@@ -320,6 +357,7 @@ def main():
                    "decode_tokens_per_s": round(T_d / (per["decode"] * 1e-3), 1)},
         "kernels": kernels,
     }
+    result["conv1d"] = bench_conv(torch, gdn, T_e, ext.N, T_d, args.steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(ext, args.cpu_seconds)

@@ -70,7 +70,7 @@ def _run_and_check(gdn, c, K, act, use_bias, keep_pool=False):
     return got
 
 
-# lengths: empty, shorter than K - 1, tile-crossing (32-token tiles), several
+# lengths: empty, shorter than K - 1, tile-crossing (64-token tiles), several
 # sequences inside one tile, one skipped; D = 1032 leaves a ragged channel block
 LENS = (0, 1, 2, 3, 31, 33, 70, 5, 100, 0, 64, 9)
 INIT = (1, 1, 0, 1, 1, 0, 1, 1, 1, 0, 1, 0)
