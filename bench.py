@@ -46,9 +46,11 @@ EXTEND_FLOP_PER_TOKEN = H_QK * 4 * CHUNK * D + H_V * 2 * (CHUNK * D + 2 * CHUNK 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_traffic.txt")
 KERNEL_SOURCES = {"extend": "hybrid_model_linear_amd/csrc/chunk.hip",
-                  "decode": "hybrid_model_linear_amd/csrc/recurrent.hip"}
+                  "decode": "hybrid_model_linear_amd/csrc/recurrent.hip",
+                  "conv_prefill": "hybrid_model_linear_amd/csrc/conv.hip"}
 KERNEL_NAMES = {"extend": "chunk_kernel<128, 128, false, unsigned short",
-                "decode": "recurrent_kernel<128, 128, unsigned short"}
+                "decode": "recurrent_kernel<128, 128, unsigned short",
+                "conv_prefill": "conv_out_kernel<4, true>"}
 PROF_CMD = "python bench.py --steps 20 --warmup 1000 --no-cpu-baseline --calibrate-copy-mib 1024"
 PMC_CMD = "python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy-mib 1024"
 
@@ -92,7 +94,8 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
              f"# command (repository root): export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
              f"-d <dir> -o bench -- {PROF_CMD}",
              f"# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
-             f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}",
+             f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}, "
+             f"conv.hip sha256 {source_sha('conv_prefill')}",
              f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
     for r in stats:
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
@@ -126,7 +129,7 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
            "# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
            f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
            f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]
-    for kind in ("extend", "decode"):
+    for kind in ("extend", "decode", "conv_prefill"):
         fk, n = pick(fetch, KERNEL_NAMES[kind])
         wk, _ = pick(write, KERNEL_NAMES[kind])
         out += [f"{kind}_source_sha256 {source_sha(kind)}", f"{kind}_dispatches {n}",
@@ -233,6 +236,8 @@ def bench_conv(torch, gdn, T_e, n_seq, T_d, steps):
         gbs = work[name] / (us * 1e-6) / 1e9
         res[name] = {"avg_us": round(us, 2), "bytes": work[name], "GB_s": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # counter traffic of the output pass (the state pass moves 0.4 MB)
+    res["prefill"]["traffic_bytes_output_pass"] = measured_traffic("conv_prefill")
     return res
 
 
