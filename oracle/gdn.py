@@ -249,7 +249,7 @@ def ssd_combined(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False
 
 # ---------------------------------------------------------------- short causal conv1d
 def causal_conv1d(x, weight, bias, cu_seqlens, slot, has_init, conv_pool, activation=True,
-                  seqs=None):
+                  seqs=None, parent=None):
     """Depthwise causal conv1d over packed sequences with a per-slot conv state (the
     short convolution in front of the GDN layer; the plain reading of the conv[0]
     state buffer of the SGLang GDN test article).
@@ -262,6 +262,11 @@ def causal_conv1d(x, weight, bias, cu_seqlens, slot, has_init, conv_pool, activa
         out_t = silu(y_t) if activation else y_t
     and its new state is the last K - 1 rows of w (for a short sequence partly the
     old state).  slot[n] < 0 skips the sequence.
+    parent: optional [T] token tree of target verify (the reading of the SGLang GDN test
+    article's tree verify): token i of a sequence continues token parent[t] (an earlier
+    index within the sequence, -1 = the state), so its window is the state followed by
+    the inputs along its root path; no state is returned (the caller commits the
+    accepted branch).
     Returns (out float64 [T, C] (NaN where not written), states dict slot -> [C, K-1]).
     """
     x = np.asarray(x, dtype=F64)
@@ -280,6 +285,15 @@ def causal_conv1d(x, weight, bias, cu_seqlens, slot, has_init, conv_pool, activa
             continue
         t0, t1 = int(cu[n]), int(cu[n + 1])
         prev = np.asarray(conv_pool[s], dtype=F64).T if has_init[n] else np.zeros((K - 1, Cn))
+        if parent is not None:
+            for t in range(t0, t1):
+                path = [t - t0]                                      # root path, newest first
+                while int(parent[t0 + path[-1]]) >= 0:
+                    path.append(int(parent[t0 + path[-1]]))
+                win = np.concatenate([prev, x[[t0 + i for i in reversed(path)]]], axis=0)
+                y = b + np.sum(win[len(win) - K:] * w.T, axis=0)
+                out[t] = y / (1.0 + np.exp(-y)) if activation else y
+            continue
         win = np.concatenate([prev, x[t0:t1]], axis=0)              # [K-1 + len, C]
         for t in range(t0, t1):
             i = t - t0

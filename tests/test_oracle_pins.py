@@ -699,3 +699,30 @@ def test_conv_split_resume_and_decode():
     o1, _ = oracle.causal_conv1d(c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
     o2, _ = oracle.causal_conv1d(2 * c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
     _close(o2, 2 * o1)
+
+
+def test_conv_token_tree():
+    """A chain given as a tree (parent = i - 1) is the plain conv; every token of a tree
+    gives the last output of the plain conv over its explicit root path; no states."""
+    c = _conv_case(lens=(7, 5), has_init=(1, 0))
+    c["slot"] = np.array([2, 4])
+    cu = np.array([0, 7, 12])
+    chain = np.array([-1, 0, 1, 2, 3, 4, 5, -1, 0, 1, 2, 3])
+    ref, _ = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"])
+    got, st = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"],
+                                   parent=chain)
+    _close(got, ref)
+    assert st == {}
+    tree = np.array([-1, 0, 0, 1, 2, 2, -1, -1, 0, 0, 1, 3])     # two branches, a second root
+    got, _ = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"],
+                                  parent=tree)
+    for n in range(2):
+        t0 = cu[n]
+        for i in range(cu[n + 1] - t0):
+            path = [i]
+            while tree[t0 + path[-1]] >= 0:
+                path.append(tree[t0 + path[-1]])
+            xs = c["x"][[t0 + j for j in reversed(path)]]
+            o, _ = oracle.causal_conv1d(xs, c["w"], c["b"], np.array([0, len(xs)]), c["slot"][n:n + 1],
+                                        c["has_init"][n:n + 1], c["pool"])
+            _close(got[t0 + i], o[-1])
