@@ -130,6 +130,8 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
            f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
            f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]
     for kind in ("extend", "decode", "conv_prefill"):
+        if kind == "conv_prefill" and not any(KERNEL_NAMES[kind] in k for k in fetch):
+            continue                                # a profile without the conv leg
         fk, n = pick(fetch, KERNEL_NAMES[kind])
         wk, _ = pick(write, KERNEL_NAMES[kind])
         out += [f"{kind}_source_sha256 {source_sha(kind)}", f"{kind}_dispatches {n}",

@@ -343,23 +343,28 @@ def _conv_args(x, weight, bias, slot, pool, activation, out, keep_pool, T, N):
 
 
 def conv1d(x, weight, bias, cu_seqlens, slot, pool, *, has_init=None, activation=True, out=None,
-           keep_pool=False):
+           keep_pool=False, parent=None):
     """Short causal depthwise conv1d over packed sequences with a conv-state pool
     (gdn_conv1d).  x [T, D] bf16; weight [D, K] bf16 (K in 2..4, the last tap on the
     current input); bias [D] bf16 or None; cu_seqlens int32 [N+1]; slot int32 [N]
     (negative skips the sequence); pool bf16 [num_slots, D, K-1], the last K-1 inputs
     per slot, updated in place unless keep_pool; has_init int32 [N] or None (= all 1).
+    parent: optional int32 [T] token tree (target verify; needs keep_pool): token i of a
+    sequence continues its token parent[t] (an earlier index, -1 = the state).
     Returns out [T, D] bf16 = silu(conv) (or the plain conv without activation)."""
     lib = _lib.load()
-    dev = _on_gpu(x, weight, bias, cu_seqlens, slot, pool, has_init, out)
+    dev = _on_gpu(x, weight, bias, cu_seqlens, slot, pool, has_init, out, parent)
     N = slot.shape[0]
     T = x.shape[0]
     _i32(cu_seqlens, "cu_seqlens", N + 1)
     if has_init is not None:
         _i32(has_init, "has_init", N)
+    if parent is not None:
+        _i32(parent, "parent", T)
     a, out = _conv_args(x, weight, bias, slot, pool, activation, out, keep_pool, T, N)
     a.cu_seqlens = _ptr(cu_seqlens)
     a.has_init = _ptr(has_init)
+    a.parent = _ptr(parent)
     _lib.check("gdn_conv1d", lib.gdn_conv1d(ct.byref(a), _stream(dev)))
     return out
 
@@ -433,8 +438,8 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     bf16 [D, K] (or [D, 1, K]) with optional conv_bias [D]; then forward_batch.conv_pool
     (indexable by layer_id -> bf16 [num_slots, D, K-1]) holds the conv states of the
     same slots, and the conv (with silu) runs first -- gdn_conv1d / gdn_conv1d_update,
-    leaving the conv pool unwritten in target verify (token trees are not supported
-    with the conv).
+    leaving the conv pool unwritten in target verify (with spec_parents the conv
+    windows follow the token tree).
     Returns out [T, H_v * d_v] in mixed_qkv's dtype."""
     kind = _mode_kind(forward_batch.forward_mode)
     H_qk, H_v = layer.num_k_heads, layer.num_v_heads
@@ -455,12 +460,11 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
         if kind == "decode":
             mixed_qkv = conv1d_update(mixed_qkv, conv_w, cbias, forward_batch.state_slots, cpool)
         else:
-            if verify and getattr(forward_batch, "spec_parents", None) is not None:
-                raise NotImplementedError("the short conv over token trees is not supported")
             mixed_qkv = conv1d(mixed_qkv, conv_w, cbias, forward_batch.cu_seqlens,
                                forward_batch.state_slots, cpool,
                                has_init=getattr(forward_batch, "has_initial_state", None),
-                               keep_pool=verify)
+                               keep_pool=verify,
+                               parent=getattr(forward_batch, "spec_parents", None) if verify else None)
     q, k, v = split_mixed_qkv(mixed_qkv, H_qk, H_v, d_k, d_v)
     g = gdn_gate_inputs(a, b, layer.A_log, layer.dt_bias)
     # the gate is folded into the layer kernel when a, b share q's dtype (else its own launch)

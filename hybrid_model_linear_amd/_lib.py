@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_status_str",
@@ -60,7 +60,8 @@ class ConvArgs(C.Structure):
                 ("weight", C.c_void_p), ("bias", C.c_void_p), ("cu_seqlens", C.c_void_p),
                 ("slot", C.c_void_p), ("has_init", C.c_void_p), ("pool", C.c_void_p),
                 ("num_slots", C.c_int64), ("pool_stride", C.c_int64), ("out", C.c_void_p),
-                ("out_stride", C.c_int64), ("keep_pool", C.c_int32), ("_pad0", C.c_int32)]
+                ("out_stride", C.c_int64), ("keep_pool", C.c_int32), ("_pad0", C.c_int32),
+                ("parent", C.c_void_p)]
 
 
 _lib = None

@@ -219,6 +219,68 @@ __global__ void __launch_bounds__(kCThreads) conv_out_kernel(const ConvLaunch p)
   }
 }
 
+// ------------------------------------------------------------------ token trees
+// Target verify with a token tree: workgroup (token, 1024-channel block).  The window
+// follows the token's parents back to the sequence start and then the slot's state;
+// a few tokens per sequence, so each token walks its own path (K - 1 parent reads).
+template <int K, bool kAct>
+__global__ void __launch_bounds__(kCThreads) conv_tree_kernel(const ConvLaunch p) {
+  const int c0 = (blockIdx.y * kCThreads + threadIdx.x) * kCV;
+  if (c0 >= p.D) return;
+  const int64_t t = blockIdx.x;
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo;
+  const int s = p.slot[n];
+  if (s < 0) return;
+  const int64_t s0 = p.cu[n];
+  Block8<K> tap;
+  float bias[kCV];
+  load_taps<K>(p, c0, tap, bias);
+  const V8 xv = unpack(ld16(p.x + t * p.x_stride + c0));
+  // rows of the K - 1 inputs before t on its root path, newest first; -1 once the
+  // path has passed the start (a parent outside [0, index) ends the path there)
+  int64_t row[K - 1];
+  int64_t cur = t - s0;
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    if (cur >= 0) {
+      const int64_t par = p.parent[s0 + cur];
+      cur = (par >= 0 && par < cur) ? par : -1;
+    }
+    row[j] = cur >= 0 ? s0 + cur : -1;
+  }
+  Block8<K - 1> st;
+  if (row[K - 2] < 0 && (!p.has_init || p.has_init[n] != 0))
+    st.load(p.pool + (int64_t)s * p.pool_stride + (int64_t)c0 * (K - 1));
+  else
+    st.zero();
+  // window oldest first: entry K - 2 - j is path input j; past the start, path input
+  // j is state entry K - 2 - m for the m-th step beyond it
+  float win[K - 1][kCV];
+  int m = 0;
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    if (row[j] >= 0) {
+      const V8 v = unpack(ld16(p.x + row[j] * p.x_stride + c0));
+#pragma unroll
+      for (int c = 0; c < kCV; ++c) win[K - 2 - j][c] = v.f[c];
+    } else {
+#pragma unroll
+      for (int e = 0; e < K - 1; ++e)
+        if (e == K - 2 - m) {
+#pragma unroll
+          for (int c = 0; c < kCV; ++c) win[K - 2 - j][c] = st.v[e][c];
+        }
+      ++m;
+    }
+  }
+  st16(p.out + t * p.out_stride + c0, conv_row<K, kAct>(tap, bias, win, xv));
+}
+
 // ------------------------------------------------------------------ varlen states
 // Workgroup (sequence, 1024-channel block): the last K - 1 window entries of the
 // sequence, partly its old state when it is shorter than K - 1.
@@ -294,6 +356,14 @@ hipError_t launch_k(const ConvLaunch& p, bool update, hipStream_t stream) {
       const dim3 grid((unsigned)p.N, cblocks);
       if (p.act) hipLaunchKernelGGL((conv_update_kernel<K, true>), grid, dim3(kCThreads), 0, stream, p);
       else hipLaunchKernelGGL((conv_update_kernel<K, false>), grid, dim3(kCThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+  }
+  if (p.parent) {   // token tree: per-token windows, the pool only read
+    if (p.T > 0) {
+      const dim3 grid((unsigned)p.T, cblocks);
+      if (p.act) hipLaunchKernelGGL((conv_tree_kernel<K, true>), grid, dim3(kCThreads), 0, stream, p);
+      else hipLaunchKernelGGL((conv_tree_kernel<K, false>), grid, dim3(kCThreads), 0, stream, p);
     }
     return hipGetLastError();
   }

@@ -307,6 +307,7 @@ int conv_impl(const gdn_conv_args* a, bool update, void* stream) {
   if (a->x_stride < a->D || a->x_stride % 8 != 0 || a->out_stride < a->D || a->out_stride % 8 != 0 ||
       a->pool_stride < a->D * (a->K - 1) || a->pool_stride % 8 != 0)
     return GDN_E_SHAPE;
+  if (!update && a->parent && !a->keep_pool) return GDN_E_SHAPE;   // a tree keeps the pool
   if (a->N == 0) return GDN_OK;
   if (!a->weight || !a->slot || !a->pool || (!update && !a->cu_seqlens)) return GDN_E_NULL;
   if (a->T > 0 && (!a->x || !a->out)) return GDN_E_NULL;
@@ -339,6 +340,7 @@ int conv_impl(const gdn_conv_args* a, bool update, void* stream) {
   p.out = static_cast<uint16_t*>(a->out);
   p.out_stride = a->out_stride;
   p.keep_pool = a->keep_pool != 0;
+  p.parent = update ? nullptr : a->parent;
   return hip_status(update ? gdn::launch_conv_update(p, (hipStream_t)stream)
                            : gdn::launch_conv(p, (hipStream_t)stream));
 }

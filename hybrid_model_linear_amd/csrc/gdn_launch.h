@@ -103,6 +103,7 @@ struct ConvLaunch {
   uint16_t* out;
   int64_t out_stride;
   int keep_pool;
+  const int32_t* parent;       // [T] token tree or null (extend)
 };
 
 hipError_t launch_gate(const GateLaunch& p, hipStream_t stream);

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -268,6 +268,12 @@ int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, voi
  *            unless keep_pool != 0 (then only read: target-verify passes whose
  *            accepted prefix the caller commits later)
  *   out    : bf16 [T, D], token stride out_stride; the fp32 result rounded to nearest even
+ *   parent : int32 [T] or NULL (gdn_conv1d only): a target-verify token tree, in the
+ *            convention of gdn_extend's spec_parent (token i of a sequence continues
+ *            its token parent[t], an earlier index, or the state for -1); the window of
+ *            a token is then the state followed by the inputs along its root path.  A
+ *            parent outside [0, i) counts as -1.  Requires keep_pool != 0 (which branch
+ *            to keep is the caller's choice), else GDN_E_SHAPE.
  * cu_seqlens, slot, has_init (NULL = all 1) and num_slots follow gdn_extend, with
  * the same rules for negative slots and device-resident indices.
  * Supported: dtype GDN_BF16 (else GDN_E_DTYPE); K in {2, 3, 4} (else
@@ -296,6 +302,7 @@ typedef struct gdn_conv_args {
   int64_t out_stride;
   int32_t keep_pool;
   int32_t _pad0;
+  const int32_t* parent;     /* [T] or NULL; ignored by gdn_conv1d_update */
 } gdn_conv_args;
 
 /* Packed varlen (prefill / extend): two launches on `stream`, the outputs (which

@@ -142,6 +142,7 @@ def _conv(**kw):
     (dict(bias=ct.c_void_p(0x50004)), _lib.GDN_E_SHAPE),
     (dict(out=ct.c_void_p(0x10000 + 2 * 64 * 9)), _lib.GDN_E_SHAPE),   # out overlaps x's last row
     (dict(out=ct.c_void_p(0x30000 + 16)), _lib.GDN_E_SHAPE),     # out overlaps the pool
+    (dict(parent=FAKE), _lib.GDN_E_SHAPE),                       # a token tree must keep the pool
 ])
 def test_conv_validation(kw, status):
     lib = gdn.load()

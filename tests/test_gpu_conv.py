@@ -211,3 +211,153 @@ def test_forward_gdn_with_conv(gdn_lib):
                                 m1[:, 2 * Hk:].reshape(N, case.H_v, case.d_v), a1, b1, case.A_log,
                                 case.dt_bias, case.slot, pool_ref, case.scale)
     assert_close(out1.float().cpu().numpy().reshape(ref1.shape), ref1, "forward_gdn+conv decode")
+
+
+def test_forward_gdn_conv_decode_graph(gdn_lib):
+    """forward_gdn decode with the short conv in front, captured once in a HIP graph over
+    static buffers of 32 rows of which 20 are live (slot -1 pads the rest), replayed three
+    times with new raw inputs and eager work in between.  Every replay is checked against
+    the oracle (conv from the previous conv states, stored as bf16, then the GDN step from
+    the previous states); padded rows' conv and GDN state slots stay untouched."""
+    from types import SimpleNamespace
+    gdn = gdn_lib
+    _announce("forward_gdn + conv decode graph capture, 20 live of 32 static rows")
+    rows, live, H_qk, H_v, d, K, nslot = 32, 20, 2, 4, 128, 4, 40
+    D = 2 * H_qk * d + H_v * d
+    rng = np.random.default_rng(93)
+    pool = torch.from_numpy(rng.normal(0, 0.1, (nslot, H_v, d, d)).astype(np.float32)).cuda()
+    cpool_h = synth.bf16_round(rng.standard_normal((nslot, D, K - 1)).astype(np.float32))
+    cpool = _dev(cpool_h)
+    slot_h = np.full(rows, -1, np.int32)
+    slot_h[:live] = rng.permutation(nslot)[:live]
+    lim = 1.0 / np.sqrt(K)
+    w_h = synth.bf16_round(rng.uniform(-lim, lim, (D, K)).astype(np.float32))
+    b_h = synth.bf16_round(rng.uniform(-lim, lim, D).astype(np.float32))
+    A_log = np.log(rng.uniform(1, 16, H_v)).astype(np.float32)
+    dt_bias = rng.normal(0, 0.5, H_v).astype(np.float32)
+    layer = SimpleNamespace(num_k_heads=H_qk, num_v_heads=H_v, head_k_dim=d, head_v_dim=d,
+                            A_log=torch.from_numpy(A_log).cuda(), dt_bias=torch.from_numpy(dt_bias).cuda(),
+                            scale=d ** -0.5, layer_id=0, conv_weight=_dev(w_h), conv_bias=_dev(b_h))
+    fb = SimpleNamespace(forward_mode="decode", state_pool=[pool], conv_pool=[cpool],
+                         state_slots=torch.from_numpy(slot_h).cuda())
+    raw = torch.zeros((rows, D), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((rows, H_v), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((rows, H_v), dtype=torch.bfloat16, device="cuda")
+    pool_pad = pool.clone()
+    cpool_pad = cpool.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            out = gdn.forward_gdn(layer, fb, raw, a, b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(cpool, cpool_pad) and torch.equal(pool, pool_pad), "capture must not run kernels"
+    states = pool.cpu().numpy().astype(np.float64)
+    cstates = cpool_h.astype(np.float64)
+    nq = H_qk * d
+    for rep in range(3):
+        x = synth.bf16_round(rng.standard_normal((rows, D)).astype(np.float32))
+        av = synth.bf16_round(rng.standard_normal((rows, H_v)).astype(np.float32))
+        bv = synth.bf16_round(rng.standard_normal((rows, H_v)).astype(np.float32))
+        raw.copy_(_dev(x))
+        a.copy_(_dev(av))
+        b.copy_(_dev(bv))
+        _ = (raw.float() * 2).sum()            # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        c, cfin = oracle.causal_conv1d(x[:live], w_h, b_h, np.arange(live + 1), slot_h[:live], None, cstates)
+        m = synth.bf16_round(c.astype(np.float32))
+        ref, _, fin = oracle.gdn_decode(m[:, :nq].reshape(live, H_qk, d), m[:, nq:2 * nq].reshape(live, H_qk, d),
+                                        m[:, 2 * nq:].reshape(live, H_v, d), av[:live], bv[:live], A_log,
+                                        dt_bias, slot_h[:live], states, d ** -0.5)
+        assert_close(out[:live].float().cpu().numpy().reshape(ref.shape), ref, f"replay {rep} out")
+        for s, st in cfin.items():
+            cstates[s] = st
+        states = oracle.apply_final_states(states, fin)
+        got_c = cpool.cpu()
+        assert torch.equal(got_c, torch.from_numpy(cstates.astype(np.float32)).to(torch.bfloat16)), \
+            f"replay {rep} conv states"
+        assert_close(pool.cpu().numpy()[slot_h[:live]], states[slot_h[:live]], f"replay {rep} states")
+        unused = np.setdiff1d(np.arange(nslot), slot_h[:live])
+        assert torch.equal(pool[unused], pool_pad[unused])
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_conv1d_token_tree(gdn_lib, K):
+    """Target verify with token trees: each token's window follows its parents and then
+    the slot's state; a chain given as a tree gives the plain conv's bits; the pool is
+    only read."""
+    gdn = gdn_lib
+    _announce(f"conv1d token tree K={K}")
+    lens = (5, 1, 0, 8, 4, 6)
+    c = synth.make_conv_case(seed=350 + K, lens=lens, D=1032, K=K, has_init=(1, 0, 1, 1, 1, 0),
+                             num_slots=12)
+    c.slot[4] = -1
+    rng = np.random.default_rng(K)
+    tree = np.concatenate([[-1] + [int(rng.integers(-1, i)) for i in range(1, L)] for L in lens if L])
+    chain = np.concatenate([np.arange(-1, L - 1) for L in lens if L])
+    d = _upload_conv(c)
+    pool_before = d["pool"].clone()
+    outs = {}
+    for name, par in (("tree", tree), ("chain", chain)):
+        out = torch.randn((c.T, c.x.shape[1]), device="cuda").to(torch.bfloat16)
+        out_before = out.clone()
+        gdn.conv1d(d["x"], d["w"], d["b"], d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                   out=out, keep_pool=True, parent=_dev(par, torch.int32))
+        torch.cuda.synchronize()
+        ref, st = oracle.causal_conv1d(c.x, c.weight, c.bias, c.cu_seqlens, c.slot, c.has_init, c.pool,
+                                       parent=par)
+        live = ~np.isnan(ref[:, 0])
+        _check_out(out.float().cpu().numpy()[live], ref[live], f"conv {name} K={K}")
+        assert torch.equal(out[torch.from_numpy(~live).cuda()], out_before[torch.from_numpy(~live).cuda()])
+        assert torch.equal(d["pool"], pool_before)
+        outs[name] = out[torch.from_numpy(live).cuda()]
+    plain = gdn.conv1d(d["x"], d["w"], d["b"], d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                       keep_pool=True)
+    live_t = torch.from_numpy(live).cuda()
+    assert torch.equal(outs["chain"], plain[live_t])
+
+
+def test_forward_gdn_conv_target_verify_tree(gdn_lib):
+    """forward_gdn in TARGET_VERIFY mode with the short conv and a token tree: the conv
+    windows and the GDN states both follow the tree; both pools are left unwritten."""
+    from types import SimpleNamespace
+    gdn = gdn_lib
+    _announce("forward_gdn + conv target verify, token tree")
+    N, L = 3, 5
+    case = synth.edge_case("fwd-conv-tree", (L,) * N, has_init=1, seed=83, num_slots=6)
+    D = case.mixed_qkv.shape[1]
+    cc = synth.make_conv_case(seed=84, lens=(L,) * N, D=D, K=4, has_init=1, num_slots=6, slot=case.slot)
+    tree = np.array([-1, 0, 0, 1, 2] * N, np.int32)
+    d = upload(case)
+    cpool = _dev(cc.pool)
+    pool_before, cpool_before = d["pool"].clone(), cpool.clone()
+    rows = torch.tensor([2, 0, 1], dtype=torch.int32, device="cuda")
+    buf = torch.zeros((N, L, case.H_v, case.d_v, case.d_k), dtype=torch.float32, device="cuda")
+    layer = SimpleNamespace(num_k_heads=case.H_qk, num_v_heads=case.H_v, head_k_dim=case.d_k,
+                            head_v_dim=case.d_v, A_log=d["A_log"], dt_bias=d["dt_bias"], scale=case.scale,
+                            layer_id=0, conv_weight=_dev(cc.weight), conv_bias=_dev(cc.bias))
+    fb = SimpleNamespace(forward_mode="TARGET_VERIFY", state_slots=d["slot"], state_pool=[d["pool"]],
+                         conv_pool=[cpool], cu_seqlens=d["cu"], has_initial_state=d["has_init"],
+                         max_seqlen=L, spec_states=[buf], spec_state_slots=rows,
+                         spec_parents=_dev(tree, torch.int32))
+    out = gdn.forward_gdn(layer, fb, _dev(cc.x), d["a"], d["b"])
+    torch.cuda.synchronize()
+    conv_ref, _ = oracle.causal_conv1d(cc.x, cc.weight, cc.bias, cc.cu_seqlens, cc.slot, cc.has_init,
+                                       cc.pool, parent=tree)
+    m = synth.bf16_round(conv_ref.astype(np.float32))
+    Hk = case.H_qk * case.d_k
+    spec = {}
+    ref, _, _ = oracle.gdn_extend(m[:, :Hk].reshape(-1, case.H_qk, case.d_k),
+                                  m[:, Hk:2 * Hk].reshape(-1, case.H_qk, case.d_k),
+                                  m[:, 2 * Hk:].reshape(-1, case.H_v, case.d_v), case.a, case.b, case.A_log,
+                                  case.dt_bias, case.cu_seqlens, case.slot, case.has_init, case.pool,
+                                  case.scale, spec_slot=rows.cpu().numpy(), spec_parent=tree, spec=spec)
+    assert_close(out.float().cpu().numpy().reshape(ref.shape), ref, "forward_gdn+conv tree out")
+    got = buf.cpu().numpy()
+    for (r, i), S in spec.items():
+        assert_close(got[r, i], S, f"tree state {r},{i}")
+    assert torch.equal(d["pool"], pool_before) and torch.equal(cpool, cpool_before)
