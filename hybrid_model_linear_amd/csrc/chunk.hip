@@ -315,7 +315,26 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ uint32_t sSync[8];
 
   const int h = blockIdx.x;
-  const int nseq = blockIdx.y;
+  // Workgroups are dispatched sequence by sequence.  With lpt set, blockIdx.y is a
+  // rank in descending length (ties by index), so the longest sequences start first
+  // and a ragged batch ends without a long tail (longest-processing-time first).
+  // Thread m ranks sequence m in O(N); the host sets lpt only for small N.
+  int nseq = blockIdx.y;
+  if (p.lpt) {
+    __shared__ int sSel;
+    const int m = threadIdx.x;
+    if (m < p.N) {
+      const int lm = p.cu_seqlens[m + 1] - p.cu_seqlens[m];
+      int rank = 0;
+      for (int q = 0; q < p.N; ++q) {
+        const int lq = p.cu_seqlens[q + 1] - p.cu_seqlens[q];
+        rank += (lq > lm) | ((lq == lm) & (q < m));
+      }
+      if (rank == (int)blockIdx.y) sSel = m;
+    }
+    __syncthreads();
+    nseq = __builtin_amdgcn_readfirstlane(sSel);
+  }
   const int sl = p.slot[nseq];
   if (sl < 0) return;                                      // uniform over the block
   const int tbeg = p.cu_seqlens[nseq], tend = p.cu_seqlens[nseq + 1];

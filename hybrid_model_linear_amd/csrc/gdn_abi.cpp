@@ -230,6 +230,7 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
   }
 
   const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
+  p.lpt = a->N >= 2 && a->N <= 128;
   if (p.in_bf16 && !short_batch && !spec && gdn::chunked_supported(p))
     return hip_status(gdn::launch_chunked(p, (hipStream_t)stream));
   return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));

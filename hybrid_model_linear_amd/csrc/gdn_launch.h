@@ -82,6 +82,7 @@ struct SeqLaunch {
   const int32_t* sp_parent;   // [T] or null
   int sp_steps;
   int keep_pool;
+  int lpt;                    // chunked kernel: longest sequences first (small N)
 };
 
 // Short causal conv1d (bf16, width K) over packed sequences with a conv-state pool.
