@@ -142,6 +142,7 @@ __global__ void __launch_bounds__(kCThreads) conv_out_kernel(const ConvLaunch p)
   if (c0 >= p.D) return;
   const int64_t t0 = (int64_t)blockIdx.x * kCTok;
   const int64_t tend = t0 + kCTok < p.T ? t0 + kCTok : p.T;
+  if (t0 >= p.cu[p.N]) return;     // tokens past the last sequence are padding
 
   Block8<K> tap;
   float bias[kCV];
@@ -198,10 +199,13 @@ __global__ void __launch_bounds__(kCThreads) conv_out_kernel(const ConvLaunch p)
     for (int u = 0; u < kCAhead; ++u) {
       const int64_t t = tb + u;
       if (t >= tend) break;
-      if (t == nb) {               // the next non-empty sequence starts at t
-        do {
-          ++n;
-        } while (p.cu[n + 1] <= t);
+      if (t == nb) {               // sequence n ends before t
+        while (n + 1 < p.N && p.cu[n + 2] <= t) ++n;   // skip empty ones
+        if (n + 1 >= p.N) {        // past the last sequence: padding, nothing written
+          tb = tend;
+          break;
+        }
+        ++n;                       // the sequence starting at t
         s0 = t;
         nb = p.cu[n + 1];
         live = p.slot[n] >= 0;
@@ -235,7 +239,7 @@ __global__ void __launch_bounds__(kCThreads) conv_tree_kernel(const ConvLaunch p
   }
   const int n = lo;
   const int s = p.slot[n];
-  if (s < 0) return;
+  if (s < 0 || t >= p.cu[n + 1]) return;    // skipped sequence, or padding past the last
   const int64_t s0 = p.cu[n];
   Block8<K> tap;
   float bias[kCV];

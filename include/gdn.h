@@ -93,7 +93,9 @@ typedef struct gdn_gate_args {
 
 /* ---------------------------------------------------------------- gdn_extend
  * Packed-varlen prefill / extend.  Sequence n owns tokens [cu_seqlens[n],
- * cu_seqlens[n+1]) (cu_seqlens[0] = 0, non-decreasing, last = T).  It starts from
+ * cu_seqlens[n+1]) (cu_seqlens[0] = 0, non-decreasing, last <= T: tokens after the
+ * last sequence are padding of a static buffer, e.g. under graph capture, and their
+ * output rows are not written).  It starts from
  * pool[slot[n]] when has_init[n] != 0 (has_init NULL = all 1) and from zeros
  * otherwise, and writes its final state to pool[slot[n]] -- also for a
  * zero-length sequence, which writes its start state back.  slot[n] < 0 skips it.
@@ -275,7 +277,8 @@ int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, voi
  *            parent outside [0, i) counts as -1.  Requires keep_pool != 0 (which branch
  *            to keep is the caller's choice), else GDN_E_SHAPE.
  * cu_seqlens, slot, has_init (NULL = all 1) and num_slots follow gdn_extend, with
- * the same rules for negative slots and device-resident indices.
+ * the same rules for negative slots, padding tokens after the last sequence and
+ * device-resident indices.
  * Supported: dtype GDN_BF16 (else GDN_E_DTYPE); K in {2, 3, 4} (else
  * GDN_E_UNSUPPORTED).  D >= 8 and a multiple of 8; x, out, weight, bias and pool
  * 16-byte aligned; x_stride, out_stride >= D and pool_stride multiples of 8

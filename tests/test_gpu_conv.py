@@ -361,3 +361,79 @@ def test_forward_gdn_conv_target_verify_tree(gdn_lib):
     for (r, i), S in spec.items():
         assert_close(got[r, i], S, f"tree state {r},{i}")
     assert torch.equal(d["pool"], pool_before) and torch.equal(cpool, cpool_before)
+
+
+def test_forward_gdn_conv_extend_graph_static_buffer(gdn_lib):
+    """The split-op extend case of the SGLang GDN test article (prefixes 0, 8, 16; extends
+    15, 8, 1; a static token buffer of 32): forward_gdn with the short conv captured once
+    in a HIP graph over the static buffer, replayed with those live lengths and then with
+    (10, 3, 9) written into the same cu_seqlens.  Tokens after the last sequence are
+    padding: their output rows stay untouched.  Every replay continues from the pools
+    the previous one left and is checked against the oracle."""
+    from types import SimpleNamespace
+    gdn = gdn_lib
+    _announce("forward_gdn + conv extend graph over a static 32-token buffer")
+    Tst, N, H_qk, H_v, d, K, nslot = 32, 3, 2, 4, 128, 4, 8
+    D = 2 * H_qk * d + H_v * d
+    rng = np.random.default_rng(97)
+    slot_h = rng.permutation(nslot)[:N].astype(np.int32)
+    has_init_h = np.array([0, 1, 1], np.int32)                # prefix 0 has no state
+    pool = torch.from_numpy(rng.normal(0, 0.1, (nslot, H_v, d, d)).astype(np.float32)).cuda()
+    cpool_h = synth.bf16_round(rng.standard_normal((nslot, D, K - 1)).astype(np.float32))
+    cpool = _dev(cpool_h)
+    lim = 1.0 / np.sqrt(K)
+    w_h = synth.bf16_round(rng.uniform(-lim, lim, (D, K)).astype(np.float32))
+    b_h = synth.bf16_round(rng.uniform(-lim, lim, D).astype(np.float32))
+    A_log = np.log(rng.uniform(1, 16, H_v)).astype(np.float32)
+    dt_bias = rng.normal(0, 0.5, H_v).astype(np.float32)
+    layer = SimpleNamespace(num_k_heads=H_qk, num_v_heads=H_v, head_k_dim=d, head_v_dim=d,
+                            A_log=torch.from_numpy(A_log).cuda(), dt_bias=torch.from_numpy(dt_bias).cuda(),
+                            scale=d ** -0.5, layer_id=0, conv_weight=_dev(w_h), conv_bias=_dev(b_h))
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    fb = SimpleNamespace(forward_mode="extend", state_pool=[pool], conv_pool=[cpool],
+                         state_slots=torch.from_numpy(slot_h).cuda(), cu_seqlens=cu,
+                         has_initial_state=torch.from_numpy(has_init_h).cuda(), max_seqlen=0)
+    raw = torch.zeros((Tst, D), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((Tst, H_v), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((Tst, H_v), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            out = gdn.forward_gdn(layer, fb, raw, a, b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    out.fill_(SENT := -7.0)
+    states = pool.cpu().numpy().astype(np.float64)
+    cstates = cpool_h.astype(np.float64)
+    nq = H_qk * d
+    for rep, lens in enumerate([(15, 8, 1), (10, 3, 9)]):
+        cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        live = int(cu_h[-1])
+        x = synth.bf16_round(rng.standard_normal((Tst, D)).astype(np.float32))
+        av = synth.bf16_round(rng.standard_normal((Tst, H_v)).astype(np.float32))
+        bv = synth.bf16_round(rng.standard_normal((Tst, H_v)).astype(np.float32))
+        cu.copy_(torch.from_numpy(cu_h))
+        raw.copy_(_dev(x))
+        a.copy_(_dev(av))
+        b.copy_(_dev(bv))
+        _ = (raw.float() * 2).sum()            # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        c, cfin = oracle.causal_conv1d(x[:live], w_h, b_h, cu_h, slot_h, has_init_h, cstates)
+        m = synth.bf16_round(c.astype(np.float32))
+        ref, _, fin = oracle.gdn_extend(m[:, :nq].reshape(live, H_qk, d), m[:, nq:2 * nq].reshape(live, H_qk, d),
+                                        m[:, 2 * nq:].reshape(live, H_v, d), av[:live], bv[:live], A_log,
+                                        dt_bias, cu_h, slot_h, has_init_h, states, d ** -0.5)
+        got = out.float().cpu().numpy()
+        assert_close(got[:live].reshape(ref.shape), ref, f"replay {rep} out")
+        assert (got[live:] == SENT).all(), f"replay {rep}: padding rows were written"
+        for s, st in cfin.items():
+            cstates[s] = st
+        states = oracle.apply_final_states(states, fin)
+        assert torch.equal(cpool.cpu(), torch.from_numpy(cstates.astype(np.float32)).to(torch.bfloat16)), \
+            f"replay {rep} conv states"
+        assert_close(pool.cpu().numpy()[slot_h], states[slot_h], f"replay {rep} states")
+        out.fill_(SENT)
