@@ -647,6 +647,8 @@ def test_verify_tree_states_and_outputs():
 
 
 # ------------------------------------------------------------------ short causal conv1d
+# The checks take the implementation as an argument so that the same checks can be
+# run against re-typed versions with planted mistakes (below).
 def _conv_case(seed=4, lens=(6, 2, 5, 0), C=7, K=4, has_init=(1, 1, 0, 1)):
     rng = np.random.default_rng(seed)
     T = sum(lens)
@@ -656,12 +658,12 @@ def _conv_case(seed=4, lens=(6, 2, 5, 0), C=7, K=4, has_init=(1, 1, 0, 1)):
                 pool=rng.standard_normal((5, C, K - 1)))
 
 
-def test_conv_matches_numpy_convolve():
+def _check_conv_convolve(impl):
     """Each channel of each sequence equals numpy's full convolution of [state; x] with the
     reversed kernel (valid part), plus bias, through silu (scipy expit); the new state is
     the last K-1 window rows."""
     c = _conv_case()
-    out, st = oracle.causal_conv1d(c["x"], c["w"], c["b"], c["cu"], c["slot"], c["has_init"], c["pool"])
+    out, st = impl(c["x"], c["w"], c["b"], c["cu"], c["slot"], c["has_init"], c["pool"])
     K = c["w"].shape[1]
     for n in range(4):
         t0, t1 = c["cu"][n], c["cu"][n + 1]
@@ -676,46 +678,44 @@ def test_conv_matches_numpy_convolve():
     _close(st[1], c["pool"][1])
 
 
-def test_conv_split_resume_and_decode():
+def _check_conv_split_resume(impl):
     """conv(A || B) == conv(A) then conv(B) from the state == conv(A) then one token at a
     time; without activation the map is linear in x (bias 0)."""
     c = _conv_case(lens=(9,), has_init=(1,))
     c["slot"] = np.array([2])
-    full, fst = oracle.causal_conv1d(c["x"], c["w"], c["b"], np.array([0, 9]), c["slot"], None, c["pool"])
+    full, fst = impl(c["x"], c["w"], c["b"], np.array([0, 9]), c["slot"], None, c["pool"])
     for cut in range(10):
         pool = c["pool"].copy()
         outs = []
         for (a0, a1) in ((0, cut), (cut, 9)):
-            o, st = oracle.causal_conv1d(c["x"][a0:a1], c["w"], c["b"], np.array([0, a1 - a0]), c["slot"], None, pool)
+            o, st = impl(c["x"][a0:a1], c["w"], c["b"], np.array([0, a1 - a0]), c["slot"], None, pool)
             outs.append(o)
             pool[2] = st[2]
         _close(np.concatenate(outs), full)
         _close(pool[2], fst[2])
     pool = c["pool"].copy()
     for t in range(9):
-        o, st = oracle.causal_conv1d(c["x"][t:t + 1], c["w"], c["b"], np.array([0, 1]), c["slot"], None, pool)
+        o, st = impl(c["x"][t:t + 1], c["w"], c["b"], np.array([0, 1]), c["slot"], None, pool)
         _close(o[0], full[t])
         pool[2] = st[2]
-    o1, _ = oracle.causal_conv1d(c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
-    o2, _ = oracle.causal_conv1d(2 * c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
+    o1, _ = impl(c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
+    o2, _ = impl(2 * c["x"], c["w"], None, np.array([0, 9]), c["slot"], np.array([0]), c["pool"], False)
     _close(o2, 2 * o1)
 
 
-def test_conv_token_tree():
+def _check_conv_token_tree(impl):
     """A chain given as a tree (parent = i - 1) is the plain conv; every token of a tree
     gives the last output of the plain conv over its explicit root path; no states."""
     c = _conv_case(lens=(7, 5), has_init=(1, 0))
     c["slot"] = np.array([2, 4])
     cu = np.array([0, 7, 12])
     chain = np.array([-1, 0, 1, 2, 3, 4, 5, -1, 0, 1, 2, 3])
-    ref, _ = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"])
-    got, st = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"],
-                                   parent=chain)
+    ref, _ = impl(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"])
+    got, st = impl(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"], parent=chain)
     _close(got, ref)
     assert st == {}
     tree = np.array([-1, 0, 0, 1, 2, 2, -1, -1, 0, 0, 1, 3])     # two branches, a second root
-    got, _ = oracle.causal_conv1d(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"],
-                                  parent=tree)
+    got, _ = impl(c["x"][:12], c["w"], c["b"], cu, c["slot"], c["has_init"][:2], c["pool"], parent=tree)
     for n in range(2):
         t0 = cu[n]
         for i in range(cu[n + 1] - t0):
@@ -723,6 +723,82 @@ def test_conv_token_tree():
             while tree[t0 + path[-1]] >= 0:
                 path.append(tree[t0 + path[-1]])
             xs = c["x"][[t0 + j for j in reversed(path)]]
-            o, _ = oracle.causal_conv1d(xs, c["w"], c["b"], np.array([0, len(xs)]), c["slot"][n:n + 1],
-                                        c["has_init"][n:n + 1], c["pool"])
+            o, _ = impl(xs, c["w"], c["b"], np.array([0, len(xs)]), c["slot"][n:n + 1],
+                        c["has_init"][n:n + 1], c["pool"])
             _close(got[t0 + i], o[-1])
+
+
+CONV_CHECKS = [_check_conv_convolve, _check_conv_split_resume, _check_conv_token_tree]
+
+
+def test_conv_matches_numpy_convolve():
+    _check_conv_convolve(oracle.causal_conv1d)
+
+
+def test_conv_split_resume_and_decode():
+    _check_conv_split_resume(oracle.causal_conv1d)
+
+
+def test_conv_token_tree():
+    _check_conv_token_tree(oracle.causal_conv1d)
+
+
+def _conv_mutant(kind):
+    """A re-typed conv with one planted mistake (kind); kind=None must equal the oracle."""
+    def impl(x, weight, bias, cu_seqlens, slot, has_init, conv_pool, activation=True, parent=None):
+        x = np.asarray(x, np.float64)
+        w = np.asarray(weight, np.float64)
+        if kind == "reversed_taps":
+            w = w[:, ::-1]
+        T, C = x.shape
+        K = w.shape[1]
+        b = np.zeros(C) if (bias is None or kind == "no_bias") else np.asarray(bias, np.float64)
+        N = len(cu_seqlens) - 1
+        hi = np.ones(N, np.int64) if has_init is None else np.asarray(has_init)
+        out = np.full((T, C), np.nan)
+        states = {}
+        for n in range(N):
+            s = int(slot[n])
+            if s < 0:
+                continue
+            t0, t1 = int(cu_seqlens[n]), int(cu_seqlens[n + 1])
+            prev = np.asarray(conv_pool[s], np.float64).T if hi[n] else np.zeros((K - 1, C))
+            if kind == "state_newest_first":
+                prev = prev[::-1]
+            for t in range(t0, t1):
+                rows = list(range(t0, t + 1))
+                if parent is not None and kind != "tree_as_chain":
+                    rows = [t]
+                    while int(parent[rows[0]]) >= 0:
+                        rows.insert(0, t0 + int(parent[rows[0]]))
+                win = np.concatenate([prev, x[rows]])[-K:]
+                y = b + np.einsum("ck,kc->c", w, win)
+                if activation:
+                    y = scipy.special.expit(y) if kind == "sigmoid_not_silu" else y * scipy.special.expit(y)
+                out[t] = y
+            if parent is None:
+                allrows = np.concatenate([prev, x[t0:t1]])
+                states[s] = (prev.T.copy() if kind == "stale_state" else allrows[-(K - 1):].T.copy())
+        return out, states
+    return impl
+
+
+CONV_MUTANTS = ["reversed_taps", "no_bias", "state_newest_first", "tree_as_chain",
+                "sigmoid_not_silu", "stale_state"]
+
+
+def test_conv_mutant_baseline_passes():
+    for check in CONV_CHECKS:
+        check(_conv_mutant(None))
+
+
+@pytest.mark.parametrize("kind", CONV_MUTANTS)
+def test_conv_pins_reject_mutants(kind):
+    impl = _conv_mutant(kind)
+    failed = 0
+    for check in CONV_CHECKS:
+        try:
+            check(impl)
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed > 0, f"no pin rejects the planted mistake {kind!r}"
