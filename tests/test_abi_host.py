@@ -305,6 +305,51 @@ def test_forward_gdn_routes_by_mode(mode, expect, gate_dtype_matches):
     assert v.data_ptr() == mixed.data_ptr() + 4 * 128 * mixed.element_size()
 
 
+@pytest.mark.parametrize("mode,tree", [("DECODE", False), ("EXTEND", False), ("TARGET_VERIFY", False),
+                                       ("TARGET_VERIFY", True)])
+def test_forward_gdn_runs_the_conv_first(mode, tree):
+    """With conv taps on the layer, forward_gdn convolves mixed_qkv first (decode ->
+    conv1d_update, extend family -> conv1d with the same slots; target verify leaves the
+    conv pool unwritten and passes the token tree) and splits q, k, v from the result."""
+    T = 5
+    mixed = torch.zeros(T, 2 * 2 * 128 + 4 * 128)
+    conv_out = torch.ones_like(mixed)
+    a, b = torch.zeros(T, 4), torch.zeros(T, 4)
+    cpool, slots, cu, hi, par = object(), object(), object(), object(), object()
+    fb = SimpleNamespace(forward_mode=_Mode(mode), state_pool={3: object()}, conv_pool={3: cpool},
+                         state_slots=slots, cu_seqlens=cu, has_initial_state=hi, max_seqlen=7)
+    if tree:
+        fb.spec_states, fb.spec_state_slots, fb.spec_parents = {3: object()}, object(), par
+    layer = _layer()
+    layer.conv_weight = torch.zeros(1024, 1, 4)
+    layer.conv_bias = object()
+    out = torch.zeros(T, 4, 128)
+    with mock.patch.object(gdn, "gdn_gate_inputs", return_value=SimpleNamespace(dtype=mixed.dtype)), \
+            mock.patch.object(gdn, "conv1d", return_value=conv_out) as mc, \
+            mock.patch.object(gdn, "conv1d_update", return_value=conv_out) as mu, \
+            mock.patch.object(gdn, "decode", return_value=out) as md, \
+            mock.patch.object(gdn, "extend", return_value=out) as me:
+        gdn.forward_gdn(layer, fb, mixed, a, b)
+    if mode == "DECODE":
+        mu.assert_called_once()
+        mc.assert_not_called()
+        args = mu.call_args.args
+        assert args[0] is mixed and args[1].shape == (1024, 4) and args[2] is layer.conv_bias
+        assert args[3] is slots and args[4] is cpool
+        layer_call = md
+    else:
+        mc.assert_called_once()
+        mu.assert_not_called()
+        args, kw = mc.call_args.args, mc.call_args.kwargs
+        assert args[0] is mixed and args[1].shape == (1024, 4) and args[3] is cu and args[4] is slots
+        assert args[5] is cpool and kw["has_init"] is hi
+        assert kw["keep_pool"] == (mode == "TARGET_VERIFY")
+        assert kw["parent"] is (par if tree else None)
+        layer_call = me
+    q = layer_call.call_args.args[0]
+    assert q.data_ptr() == conv_out.data_ptr()      # q, k, v come from the conv output
+
+
 def test_forward_gdn_invalid_mode_raises_before_any_call():
     fb = SimpleNamespace(forward_mode=_Mode("DUMMY_FIRST"))
     with mock.patch.object(gdn, "gdn_gate_inputs") as mg:
