@@ -494,20 +494,26 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
                      update_seq_chunk_cumsum=False, checkpoint_token_indices=None,
                      checkpoint_state_slots=None, checkpoint_states=None, out=None,
                      return_final_states=True, out_dtype=None):
-    """Batched-mode subset of flashinfer.mamba.ssd_combined_fwd on the delta-off kernels.
+    """flashinfer.mamba.ssd_combined_fwd on the delta-off kernels, batched and packed.
 
     x [batch, L, H, P] bf16; dt [batch, L, H]; A [H] fp32; B, C [batch, L, G, N];
-    D [H] or [H, P]; z like x; initial_states [batch, H, P, N].  States are fp32.
-    Returns (out [batch, L, H, P], final_states fp32 [batch, H, P, N] or None).
-    Checkpoints (batched mode: boundaries relative to each batch element, all three
-    arguments together): checkpoint_token_indices, checkpoint_state_slots [batch] int32,
-    checkpoint_states fp32 [num_checkpoints, H, P, N] (the state dtype here is fp32).
-    The packed-varlen metadata and the caller-owned 5-D `out` storage are not
-    supported and raise NotImplementedError.  out_dtype (an extension) selects the
-    output dtype; default x's dtype."""
-    if any(t is not None for t in (seq_idx, chunk_indices, chunk_offsets, seq_chunk_cumsum,
-                                   out)) or update_seq_chunk_cumsum:
-        raise NotImplementedError("varlen metadata and caller-owned out are not supported")
+    D [H] or [H, P]; z like x.  States are fp32.
+    Batched mode: initial_states [batch, H, P, N]; returns (out [batch, L, H, P],
+    final_states [batch, H, P, N] or None); checkpoint boundaries are relative to each
+    batch element.
+    Packed-varlen mode (seq_idx [1, L] given): the sequences are the runs of equal ids,
+    0, 1, ... in order (ids non-decreasing); initial_states [num_seqs, H, P, N];
+    final_states [num_seqs, H, P, N]; checkpoint boundaries are absolute token indices.
+    num_seqs is initial_states' first dimension, else the last id + 1 (read back to the
+    host).  chunk_indices, chunk_offsets and seq_chunk_cumsum describe another kernel's
+    physical chunk layout and are not needed here (accepted, unused).
+    Checkpoints: checkpoint_token_indices, checkpoint_state_slots [sequences] int32,
+    checkpoint_states fp32 [num_checkpoints, H, P, N], all three together.
+    update_seq_chunk_cumsum and the caller-owned 5-D `out` storage raise
+    NotImplementedError.  out_dtype (an extension) selects the output dtype; default
+    x's dtype."""
+    if out is not None or update_seq_chunk_cumsum:
+        raise NotImplementedError("caller-owned out and update_seq_chunk_cumsum are not supported")
     batch, L, H, P = x.shape
     G, Nst = B.shape[2], B.shape[3]
     dev = _on_gpu(x, dt, A, B, C, D, z, dt_bias, initial_states)
@@ -522,15 +528,29 @@ def ssd_combined_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=F
     if g.dtype != x.dtype:   # folded into the extend kernel only when dt shares x's dtype
         log_g, dtp = _run_gate(g, None, None)
         g = None
+    if seq_idx is not None:                     # packed varlen: runs of equal ids
+        if batch != 1 or seq_idx.shape != (1, L):
+            raise ValueError("packed-varlen mode takes batch 1 and seq_idx [1, seqlen]")
+        if seq_idx.device != dev:
+            raise ValueError("seq_idx must be on x's device")
+        ids = seq_idx[0].to(torch.int64).contiguous()
+        nseq = (initial_states.shape[0] if initial_states is not None
+                else (int(ids[-1].item()) + 1 if L > 0 else 0))
+        cu = torch.searchsorted(ids, torch.arange(nseq + 1, device=dev)).to(torch.int32)
+        relative = False
+    else:
+        nseq = batch
+        cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+        relative = True
     if initial_states is not None:
         pool = initial_states.to(torch.float32).contiguous().clone()
     else:
-        pool = torch.empty((batch, H, P, Nst), dtype=torch.float32, device=dev)
-    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
-    slot = torch.arange(batch, dtype=torch.int32, device=dev)
-    has_init = torch.full((batch,), int(initial_states is not None), dtype=torch.int32, device=dev)
+        pool = torch.empty((nseq, H, P, Nst), dtype=torch.float32, device=dev)
+    slot = torch.arange(nseq, dtype=torch.int32, device=dev)
+    has_init = torch.full((nseq,), int(initial_states is not None), dtype=torch.int32, device=dev)
     o = extend(C.view(T, G, Nst), B.view(T, G, Nst), x.view(T, H, P), log_g, dtp, cu, slot, pool,
                has_init=has_init, mode="ssd", D=D, z=None if z is None else z.view(T, H, P),
-               max_seqlen=L, out_dtype=out_dtype, gate=g, ckpt_token=checkpoint_token_indices,
-               ckpt_slot=checkpoint_state_slots, ckpt_states=checkpoint_states, ckpt_relative=True)
+               max_seqlen=L if seq_idx is None else 0, out_dtype=out_dtype, gate=g,
+               ckpt_token=checkpoint_token_indices, ckpt_slot=checkpoint_state_slots,
+               ckpt_states=checkpoint_states, ckpt_relative=relative)
     return o.view(batch, L, H, P), (pool if return_final_states else None)

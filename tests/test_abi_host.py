@@ -361,8 +361,6 @@ def test_forward_gdn_invalid_mode_raises_before_any_call():
 def test_ssd_combined_rejects_unsupported_arguments():
     x = torch.zeros(1, 4, 2, 64)
     with pytest.raises(NotImplementedError):
-        gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, seq_idx=torch.zeros(1, 4))
-    with pytest.raises(NotImplementedError):
         gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, out=x)
     with pytest.raises(NotImplementedError):
         gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, update_seq_chunk_cumsum=True)

@@ -652,3 +652,46 @@ def test_decode_graph_capture_padded(gdn_lib):
         assert torch.equal(out[live:], out0[live:]), "padded rows were written"
         states = oracle.apply_final_states(states, fin)
         assert_close(pool.cpu().numpy()[slot_h[:live]], states[slot_h[:live]], f"replay {rep} states")
+
+
+@pytest.mark.parametrize("with_init", [True, False])
+def test_ssd_packed_varlen(gdn_lib, with_init):
+    """ssd_combined_fwd in packed-varlen mode (seq_idx): three sequences of 100, 37 and 200
+    tokens packed in one row (chunk boundaries inside and across sequences), each from its
+    own initial state, with an absolute checkpoint boundary per sequence; against the
+    oracle run on each sequence as a batch of one."""
+    gdn = gdn_lib
+    _announce(f"ssd packed varlen init={with_init}")
+    lens, H, P, G, Nst = (100, 37, 200), 4, 64, 1, 128
+    L = sum(lens)
+    c = synth.config4_ssd(seed=123, batch=1, L=L, H=H, P=P, G=G, Nst=Nst, initial=False)
+    rng = np.random.default_rng(124)
+    init = rng.normal(0, 0.1, (3, H, P, Nst)).astype(np.float32) if with_init else None
+    seq_idx = np.repeat(np.arange(3), lens)[None].astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    bnd = np.array([cu[0] + 64, cu[1] + 37, cu[2] + 150], np.int32)    # absolute boundaries
+    tb = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
+    tf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.float32)
+    ck = torch.zeros((3, H, P, Nst), dtype=torch.float32, device="cuda")
+    out, fin = gdn.ssd_combined_fwd(tb(c.x), tb(c.dt), tf(c.A), tb(c.B), tb(c.C), tb(c.D), tb(c.z),
+                                    tf(c.dt_bias), True, (0.0, float("inf")),
+                                    None if init is None else tf(init),
+                                    seq_idx=torch.from_numpy(seq_idx).cuda(),
+                                    checkpoint_token_indices=torch.from_numpy(bnd).cuda(),
+                                    checkpoint_state_slots=torch.tensor([2, 0, 1], dtype=torch.int32,
+                                                                        device="cuda"),
+                                    checkpoint_states=ck)
+    assert out.shape == (1, L, H, P) and fin.shape == (3, H, P, Nst)
+    got, gfin, gck = out.float().cpu().numpy(), fin.cpu().numpy(), ck.cpu().numpy()
+    for n, row in enumerate((2, 0, 1)):
+        t0, t1 = cu[n], cu[n + 1]
+        sl = lambda a: None if a is None else a[:, t0:t1]
+        i0 = None if init is None else init[n:n + 1]
+        ref, rfin = oracle.ssd_combined(sl(c.x), sl(c.dt), c.A, sl(c.B), sl(c.C), c.D, sl(c.z), c.dt_bias,
+                                        True, (0.0, float("inf")), i0, True)
+        assert_close(got[:, t0:t1], ref, f"ssd packed out seq {n}")
+        assert_close(gfin[n], rfin[0], f"ssd packed final seq {n}")
+        b = int(bnd[n] - t0)                    # the state after the first b tokens
+        _, rck = oracle.ssd_combined(sl(c.x)[:, :b], sl(c.dt)[:, :b], c.A, sl(c.B)[:, :b], sl(c.C)[:, :b],
+                                     c.D, sl(c.z)[:, :b], c.dt_bias, True, (0.0, float("inf")), i0, True)
+        assert_close(gck[row], rck[0], f"ssd packed checkpoint seq {n}")
