@@ -437,3 +437,32 @@ def test_forward_gdn_conv_extend_graph_static_buffer(gdn_lib):
             f"replay {rep} conv states"
         assert_close(pool.cpu().numpy()[slot_h], states[slot_h], f"replay {rep} states")
         out.fill_(SENT)
+
+
+def test_conv1d_empty_batches(gdn_lib):
+    """T = 0 with sequences: only the state pass runs; an empty sequence keeps its slot
+    (has_init) or clears it (no initial state), a skipped one touches nothing.  An empty
+    decode batch is a no-op."""
+    gdn = gdn_lib
+    _announce("conv1d empty batches")
+    D, K = 1032, 4
+    c = synth.make_conv_case(seed=360, lens=(0, 0, 0), D=D, K=K, has_init=(1, 0, 0), num_slots=6,
+                             slot=np.array([4, 1, -1]))
+    d = _upload_conv(c)
+    before = d["pool"].clone()
+    x = torch.empty((0, D), dtype=torch.bfloat16, device="cuda")
+    out = gdn.conv1d(x, d["w"], d["b"], d["cu"], d["slot"], d["pool"], has_init=d["has_init"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, D)
+    _, states = oracle.causal_conv1d(np.zeros((0, D)), c.weight, c.bias, c.cu_seqlens, c.slot, c.has_init,
+                                     c.pool)
+    pool = d["pool"].cpu()
+    assert torch.equal(pool[4], before.cpu()[4]) and torch.equal(pool[1], torch.zeros_like(pool[1]))
+    for s, st in states.items():
+        assert torch.equal(pool[s], torch.from_numpy(st.astype(np.float32)).to(torch.bfloat16))
+    for s in (0, 2, 3, 5):
+        assert torch.equal(pool[s], before.cpu()[s])
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    o = gdn.conv1d_update(x, d["w"], d["b"], empty, d["pool"])
+    torch.cuda.synchronize()
+    assert o.shape == (0, D) and torch.equal(d["pool"].cpu(), pool)
