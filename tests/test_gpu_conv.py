@@ -122,13 +122,15 @@ def test_conv1d_split_resume_and_decode(gdn_lib, cut):
     _check_out(one.float().cpu().numpy(), ref, "conv one call")
 
 
-@pytest.mark.parametrize("inplace", [False, True])
-def test_conv1d_update(gdn_lib, inplace):
-    """Decode: 256 rows of 8192 channels (one token per sequence), padding rows skipped."""
+@pytest.mark.parametrize("K,D,inplace", [(4, 8192, False), (4, 8192, True), (2, 1032, False),
+                                         (3, 1032, True)])
+def test_conv1d_update(gdn_lib, K, D, inplace):
+    """Decode: 256 rows (one token per sequence) of 8192 channels, or 1032 (a ragged
+    channel block) for the narrower widths; padding rows skipped."""
     gdn = gdn_lib
-    _announce(f"conv1d_update inplace={inplace}")
-    B, D = 256, 8192
-    c = synth.make_conv_case(seed=330, lens=(1,) * B, D=D, K=4, has_init=1, num_slots=300)
+    _announce(f"conv1d_update K={K} D={D} inplace={inplace}")
+    B = 256
+    c = synth.make_conv_case(seed=330 + K, lens=(1,) * B, D=D, K=K, has_init=1, num_slots=300)
     c.slot[5] = c.slot[77] = -1
     d = _upload_conv(c)
     pool_before = d["pool"].clone()
