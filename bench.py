@@ -15,7 +15,9 @@ Prints ONE JSON line.  `roofline` covers the kernel with the largest share of th
 step (per-launch time from HIP events recorded on the launch stream, which is
 torch's current stream); its `traffic` comes from the committed hardware-counter
 summary under profiles/ when that summary was taken on the same kernel source.
-`cpu_baseline` times the CPU oracle on a bounded sample of the prefill workload.
+`cpu_baseline` times the float64 CPU oracle on the whole prefill workload over the
+host's cores (one single-threaded worker process per unit; the one-thread rate beside
+it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --summarize-prof KT_DIR FETCH_DIR WRITE_DIR   (writes profiles/)
@@ -62,7 +64,6 @@ def parse():
     # ~0.6 s of warm-up: the GPU's clocks settle before the timed region
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter scaling)")
     ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -156,52 +157,80 @@ def measured_traffic(kind):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(ext, seconds):
-    """The float64 oracle, token by token over all 32 heads, on the prefill workload's
-    sequences in order (64-token blocks carrying the state), as many tokens as fit in
-    `seconds` of CPU time on one thread; tokens/s."""
+def _cpu_unit(unit):
+    """One (sequence, block of v-heads) unit of the prefill workload through the
+    float64 oracle: inputs of the workload's shapes and distributions (q, k, v, a, b ~
+    N(0, 1) rounded to bf16, A_log = log U(1, 16), dt_bias ~ N(0, 0.5), zero initial
+    state), the whole sequence in one call.  Returns (token-heads, seconds spent in the
+    oracle)."""
+    seq, hb, L, hpu, seed = unit
     import numpy as np
     import oracle
+    from hybrid_model_linear_amd import synth
+    rng = np.random.default_rng([seed, seq, hb])
+    hq = max(1, hpu // (H_V // H_QK))
+    f = lambda *shape: synth.bf16_round(rng.standard_normal(shape, dtype=np.float32))
+    q, k, v = f(L, hq, D), f(L, hq, D), f(L, hpu, D)
+    a, b = f(L, hpu), f(L, hpu)
+    A_log = np.log(rng.uniform(1.0, 16.0, hpu)).astype(np.float32)
+    dt_bias = (rng.standard_normal(hpu) * 0.5).astype(np.float32)
+    pool = np.zeros((1, hpu, D, D))
+    t = time.perf_counter()
+    oracle.gdn_extend(q, k, v, a, b, A_log, dt_bias, np.array([0, L]), np.array([0]), np.array([0]),
+                      pool, D ** -0.5)
+    return L * hpu, time.perf_counter() - t
+
+
+def cpu_workers():
+    """Worker processes for the CPU baseline: the host cores this process may run on,
+    at most 16 (one GPU's share of a shared host)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
+def cpu_baseline(nseq=8, seqlen=4096, workers=None, seed=77):
+    """The float64 oracle on the whole prefill workload (nseq sequences x seqlen tokens x
+    all H_V heads) over a pool of single-threaded worker processes on the host's cores.
+    A unit is one sequence with a block of its heads (the oracle is vectorised over the
+    heads of a token, so whole sequences are the cheapest units; the heads are split only
+    as far as needed to give every worker a unit).  tokens/s over the pool's wall time
+    (input generation inside the workers included); the one-thread rate (tokens over the
+    summed oracle time) is reported beside it.  Runs before anything touches the GPU
+    (the workers are forked)."""
+    import multiprocessing as mp
+    import numpy  # noqa: F401  (imported before the fork, shared by the workers)
+    import oracle  # noqa: F401
+    from hybrid_model_linear_amd import synth  # noqa: F401
+    workers = cpu_workers() if workers is None else workers
+    hpu = H_V
+    while hpu > 1 and nseq * (H_V // hpu) < workers:
+        hpu //= 2
+    units = [(n, hb, seqlen, hpu, seed) for n in range(nseq) for hb in range(H_V // hpu)]
+    used = min(workers, len(units))
     try:
         from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)          # one BLAS thread, inherited by the workers
     except Exception:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    blk = 64
-    nq = H_QK * D
-    cu = ext.cu_seqlens
-    done, spent, seqs = 0, 0.0, 0
+        limit = None
     try:
-        for s in range(len(cu) - 1):
-            t0, t1 = int(cu[s]), int(cu[s + 1])
-            S = np.zeros((1, H_V, D, D))
-            seqs += 1
-            for b0 in range(t0, t1, blk):
-                if spent >= seconds:
-                    break
-                b1 = min(t1, b0 + blk)
-                n = b1 - b0
-                mixed = ext.mixed_qkv[b0:b1].float().cpu().numpy()
-                a = ext.a[b0:b1].float().cpu().numpy()
-                b = ext.b[b0:b1].float().cpu().numpy()
-                q = mixed[:, :nq].reshape(n, H_QK, D)
-                k = mixed[:, nq:2 * nq].reshape(n, H_QK, D)
-                v = mixed[:, 2 * nq:].reshape(n, H_V, D)
-                t = time.perf_counter()
-                _, _, fin = oracle.gdn_extend(q, k, v, a, b, ext.A_log, ext.dt_bias,
-                                              np.array([0, n]), np.array([0]), np.array([int(b0 > t0)]),
-                                              S, ext.scale)
-                spent += time.perf_counter() - t
-                S = fin[0][None]
-                done += n
-            if spent >= seconds:
-                break
+        with mp.get_context("fork").Pool(used) as pool:
+            t = time.perf_counter()
+            res = pool.map(_cpu_unit, units, chunksize=1)
+            wall = time.perf_counter() - t
     finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle, first {done} tokens of the prefill workload ({seqs} sequence(s) "
-                      f"of 4096, state carried in 64-token blocks) x all {H_V} heads, {spent:.1f} s on one thread"}
+        if limit is not None:
+            limit.__exit__(None, None, None)
+    tokens = sum(r[0] for r in res) / H_V
+    spent = sum(r[1] for r in res)
+    return {"value": round(tokens / wall, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "one_thread_value": round(tokens / spent, 1),
+            "sample": f"float64 oracle on the whole prefill workload ({nseq} sequences x {seqlen} "
+                      f"tokens x {H_V} heads, zero initial states) as {len(units)} (sequence, "
+                      f"{hpu}-head) units over {used} single-threaded worker processes: "
+                      f"{wall:.1f} s wall, {spent:.1f} s of oracle time"}
 
 
 def bench_conv(torch, gdn, T_e, n_seq, T_d, steps):
@@ -253,6 +282,11 @@ def main():
               f"sequences shard independently); --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)
+    cpu = None
+    if not args.no_cpu_baseline:   # (before anything touches the GPU: its workers are forked)
+        print(f"[bench] timing the CPU oracle baseline on {cpu_workers()} worker(s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+        print(f"[bench] CPU oracle baseline: {cpu['value']} tokens/s", file=sys.stderr, flush=True)
     import torch
     import hybrid_model_linear_amd as gdn
     from hybrid_model_linear_amd import synth
@@ -365,9 +399,8 @@ def main():
         "kernels": kernels,
     }
     result["conv1d"] = bench_conv(torch, gdn, T_e, ext.N, T_d, args.steps)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(ext, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -428,11 +428,11 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     forward_batch: forward_mode; state_slots int32 [N]; state_pool indexable by
            layer_id -> fp32 [num_slots, H_v, d_v, d_k]; for extend modes also
            cu_seqlens int32 [N+1], optional has_initial_state int32 [N] and max_seqlen;
-           for target verify optionally the speculative state buffer spec_states
-           (indexable by layer_id -> fp32 [rows, steps, H_v, d_v, d_k]) with
-           spec_state_slots int32 [N] and spec_parents int32 [T] (token trees): the
-           state after every draft token is recorded there and the pool is left
-           unwritten.
+           for target verify the speculative state buffer spec_states (indexable by
+           layer_id -> fp32 [rows, steps, H_v, d_v, d_k]) with spec_state_slots int32
+           [N] and optionally spec_parents int32 [T] (token trees): the state after
+           every draft token is recorded there and the pool is left unwritten (without
+           spec_states / spec_state_slots target verify raises ValueError).
     mixed_qkv: [T, 2 H_qk d_k + H_v d_v]; a, b: [T, H_v].  mixed_qkv is taken as
     already convolved unless the layer carries the short conv's taps: conv_weight
     bf16 [D, K] (or [D, 1, K]) with optional conv_bias [D]; then forward_batch.conv_pool
@@ -451,6 +451,11 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     if T == 0:
         return mixed_qkv.new_empty((0, H_v * d_v))
     verify = kind == "extend" and _is_target_verify(forward_batch.forward_mode)
+    spec = getattr(forward_batch, "spec_states", None)
+    if verify and (spec is None or getattr(forward_batch, "spec_state_slots", None) is None):
+        # without a speculative buffer the verify pass would write the state after the
+        # rejected draft tokens into the pool (and read a token tree as a chain)
+        raise ValueError("target verify needs forward_batch.spec_states and spec_state_slots")
     conv_w = getattr(layer, "conv_weight", None)
     if conv_w is not None:
         if conv_w.dim() == 3:
@@ -475,8 +480,6 @@ def forward_gdn(layer, forward_batch, mixed_qkv: torch.Tensor, a: torch.Tensor, 
     if kind == "decode":
         o = decode(q, k, v, log_g, beta, forward_batch.state_slots, pool, scale=scale, gate=g)
     else:
-        spec = getattr(forward_batch, "spec_states", None)
-        verify = verify and spec is not None
         o = extend(q, k, v, log_g, beta, forward_batch.cu_seqlens, forward_batch.state_slots, pool,
                    has_init=getattr(forward_batch, "has_initial_state", None), scale=scale,
                    max_seqlen=int(getattr(forward_batch, "max_seqlen", 0) or 0), gate=g,

@@ -311,8 +311,10 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // vectors of the chunk being prepared, per token (see the producer roles)
   __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
   __shared__ __attribute__((aligned(16))) float sNq[C], sNk[C];   // squared row norms of q, k
-  // arrival counters: chunk vectors ready, T ready, raw Q/K read, landing done
+  // arrival counters: chunk vectors ready, T ready, raw Q/K read, landing done; and
+  // (entry kFailFlag) the flag of a bounded wait that ran out
   __shared__ uint32_t sSync[8];
+  constexpr int kFailFlag = 7;
 
   const int h = blockIdx.x;
   // Workgroups are dispatched sequence by sequence.  With lpt set, blockIdx.y is a
@@ -486,14 +488,21 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // Hand-off between waves inside a step: arrival counters in LDS.  A wave's LDS
   // writes are performed before its later increment (the LDS executes one wave's
   // accesses in order); the waiting wave reads the data only after seeing the count.
-  // Waits are bounded: every counted arrival happens unconditionally.
+  // Waits are bounded: every counted arrival happens unconditionally.  A wait that
+  // runs out (~0.1 s; an arrival was lost) raises the fail flag and goes on; at the
+  // end the workgroup then overwrites its output rows and final state with NaN, so
+  // the failure shows in the results instead of passing as plausible numbers.
   auto arrive = [&](uint32_t* ctr) __attribute__((always_inline)) {
     lds_order();
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
   auto wait_count = [&](uint32_t* ctr, uint32_t target) __attribute__((always_inline)) {
-    for (int it = 0; it < (1 << 22); ++it) {
+    for (int it = 0;; ++it) {
       if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+      if (it == (1 << 22)) {
+        if (lane == 0) __hip_atomic_store(&sSync[kFailFlag], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     lds_order();
@@ -1175,8 +1184,20 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     if (ck_b == 0) store_state(ck_st);
     run(std::false_type{});
     if (ck_b > 0 && ck_b == tend - tbeg) store_state(ck_st);
-    if (!p.keep_pool) store_state(state);
   }
+  lds_sync();   // every wave's last wait is over
+  if (isP) return;
+  if (sSync[kFailFlag] != 0u) {   // a bounded wait ran out: poison this wave's results
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int tk = 0; tk < NTK; ++tk) Sacc[ct][tk] = f32x4{nan, nan, nan, nan};
+    OutT* ob = reinterpret_cast<OutT*>(p.out);
+    for (int t = tbeg + lane / CW; t < tend; t += kWave / CW)
+      Elem<OutT>::store(ob, (int64_t)t * p.out_stride + (int64_t)h * DV + CW * wu + lane % CW, nan);
+  }
+  if (!p.keep_pool) store_state(state);
 }
 
 template <int DK, int DV, bool kSSD, typename OutT, bool kGate, bool kCk>

@@ -12,7 +12,8 @@
 // A requested state checkpoint is the state after the sequence's first b tokens
 // (the lane's rows, written when token b - 1 is done, or before the first token).
 // Target verify records the state after every token; with a token tree each token
-// starts from its parent's recorded state.
+// starts from its parent's recorded state (a parent outside [0, index) or past the
+// recorded steps: from the start state).
 //
 // Memory layout: the state row r of (slot, head) is 4*d_k contiguous bytes of the
 // pool [slot][head][d_v][d_k]; d_k/4 lanes own one row, each a float4 of it, so a
@@ -125,8 +126,10 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
 
   for (int t = t0; t < t1; ++t) {
     if (kAux && p.sp_parent && spr) {   // token tree (uniform branch)
+      // a parent outside [0, i) (i = the token's index in its sequence) or past the
+      // recorded steps counts as -1: only rows this thread wrote earlier are read
       const int par = p.sp_parent[t];
-      if (par < 0) {
+      if (par < 0 || par >= t - t0 || par >= p.sp_steps) {
 #pragma unroll
         for (int s = 0; s < kRowSteps; ++s) st[s] = st0[s];
       } else if (par != t - t0 - 1) {

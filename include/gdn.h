@@ -140,7 +140,10 @@ typedef struct gdn_gate_args {
  *   spec_slot   : int32 [N], row of spec_states; negative: the sequence records nothing
  *   spec_parent : int32 [T] or NULL; token tree: token i of a sequence (index within
  *                 it) starts from the state after its token spec_parent[t] (an earlier
- *                 index), or from the sequence's start state for -1; NULL = a chain
+ *                 index), or from the sequence's start state for -1; NULL = a chain.
+ *                 A parent outside [0, i) or not below spec_steps counts as -1 (the
+ *                 rule of gdn_conv1d's parent), so only recorded rows are ever read; a
+ *                 sequence without a speculative row (spec_slot[n] < 0) runs as a chain
  *   keep_pool   : non-zero leaves the pool unwritten (read only)
  * Sequence n with spec_slot[n] >= 0 writes the state after its token i to
  * spec_states[spec_slot[n], i] for i < spec_steps.  With spec_parent every sequence

@@ -79,7 +79,7 @@ def l2_normalize(x, eps=1e-6):
 # ---------------------------------------------------------------- GDN layer
 def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
                scale, eps=1e-6, heads=None, seqs=None, ckpt_token=None, ckpt_slot=None,
-               ckpts=None, spec_slot=None, spec_parent=None, spec=None):
+               ckpts=None, spec_slot=None, spec_parent=None, spec=None, spec_steps=None):
     """Packed-varlen GDN extend, token by token.
 
     q, k : [T, H_qk, d_k]; v : [T, H_v, d_v]; a, b : [T, H_v]
@@ -97,10 +97,12 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
     spec_slot : optional [N] rows for the target-verify states: sequence n with
       spec_slot[n] >= 0 records the state after each of its tokens (index i within the
       sequence) under spec[(spec_slot[n], i)].
-    spec_parent : optional [T] token tree (requires spec_slot for every sequence with
-      tokens): token i of a sequence starts from the state after token spec_parent[t]
-      of the same sequence (an earlier index), or from the sequence's start state for
-      -1, instead of from the state after token i - 1 (a chain).
+    spec_parent : optional [T] token tree: token i of a sequence starts from the state
+      after token spec_parent[t] of the same sequence (an earlier index), or from the
+      sequence's start state for -1, instead of from the state after token i - 1 (a
+      chain).  A parent outside [0, i), or not below spec_steps when that is given
+      (the number of recorded steps per row), counts as -1; a sequence without a row
+      (spec_slot[n] < 0) runs as a chain.
 
     Returns (out, written, finals):
       out     float64 [T, len(heads), d_v]   (NaN where not written)
@@ -143,8 +145,11 @@ def gdn_extend(q, k, v, a, b, A_log, dt_bias, cu_seqlens, slot, has_init, pool,
         for t in range(t0, t1):
             if t == ck:                                            # state before token t
                 ckpts[int(ckpt_slot[n])] = S.copy()
-            if spec_parent is not None:                            # token tree: start from the parent
+            if spec_parent is not None and row >= 0:               # token tree: start from the parent
                 par = int(spec_parent[t])
+                i = t - t0
+                if par < 0 or par >= i or (spec_steps is not None and par >= spec_steps):
+                    par = -1                                       # outside the recorded past
                 S = (S_start if par < 0 else spec[(row, par)]).copy()
             log_g, beta = gdn_gate(np.asarray(a[t:t + 1])[:, hsel], np.asarray(b[t:t + 1])[:, hsel],
                                    np.asarray(A_log)[hsel], np.asarray(dt_bias)[hsel])

@@ -269,6 +269,9 @@ def test_forward_gdn_routes_by_mode(mode, expect, gate_dtype_matches):
     pool, slots, cu, hi = object(), object(), object(), object()
     fb = SimpleNamespace(forward_mode=_Mode(mode), state_pool={3: pool}, state_slots=slots,
                          cu_seqlens=cu, has_initial_state=hi, max_seqlen=7)
+    spec_buf, spec_rows = object(), object()
+    if mode == "TARGET_VERIFY":
+        fb.spec_states, fb.spec_state_slots = {3: spec_buf}, spec_rows
     layer = _layer()
     gsent = SimpleNamespace(dtype=mixed.dtype if gate_dtype_matches else torch.bfloat16)
     lg, bt = object(), object()
@@ -298,6 +301,12 @@ def test_forward_gdn_routes_by_mode(mode, expect, gate_dtype_matches):
     if expect == "extend":
         assert any(x is cu for x in sent) and any(x is hi for x in sent)
         assert called.call_args.kwargs["max_seqlen"] == 7
+        kw = called.call_args.kwargs
+        verify = mode == "TARGET_VERIFY"
+        assert kw["keep_pool"] == verify
+        assert kw["spec_states"] is (spec_buf if verify else None)
+        assert kw["spec_slot"] is (spec_rows if verify else None)
+        assert kw["spec_parent"] is None
     # q, k, v are views of mixed_qkv, not copies
     q, k, v = called.call_args.args[:3]
     assert q.data_ptr() == mixed.data_ptr()
@@ -318,8 +327,10 @@ def test_forward_gdn_runs_the_conv_first(mode, tree):
     cpool, slots, cu, hi, par = object(), object(), object(), object(), object()
     fb = SimpleNamespace(forward_mode=_Mode(mode), state_pool={3: object()}, conv_pool={3: cpool},
                          state_slots=slots, cu_seqlens=cu, has_initial_state=hi, max_seqlen=7)
+    if mode == "TARGET_VERIFY":
+        fb.spec_states, fb.spec_state_slots = {3: object()}, object()
     if tree:
-        fb.spec_states, fb.spec_state_slots, fb.spec_parents = {3: object()}, object(), par
+        fb.spec_parents = par
     layer = _layer()
     layer.conv_weight = torch.zeros(1024, 1, 4)
     layer.conv_bias = object()
@@ -346,8 +357,33 @@ def test_forward_gdn_runs_the_conv_first(mode, tree):
         assert kw["keep_pool"] == (mode == "TARGET_VERIFY")
         assert kw["parent"] is (par if tree else None)
         layer_call = me
+        ekw = me.call_args.kwargs
+        assert ekw["keep_pool"] == (mode == "TARGET_VERIFY")
+        assert ekw["spec_parent"] is (par if tree else None)
     q = layer_call.call_args.args[0]
     assert q.data_ptr() == conv_out.data_ptr()      # q, k, v come from the conv output
+
+
+@pytest.mark.parametrize("missing", ["spec_states", "spec_state_slots", "both"])
+def test_forward_gdn_target_verify_without_buffer_raises_before_any_call(missing):
+    """Target verify without a speculative state buffer would commit the rejected draft
+    tokens' state to the pool: it raises before the conv or the layer runs."""
+    fb = SimpleNamespace(forward_mode=_Mode("TARGET_VERIFY"), state_pool={3: object()},
+                         conv_pool={3: object()}, state_slots=object(), cu_seqlens=object(),
+                         max_seqlen=4, spec_states={3: object()}, spec_state_slots=object())
+    if missing in ("spec_states", "both"):
+        del fb.spec_states
+    if missing in ("spec_state_slots", "both"):
+        del fb.spec_state_slots
+    layer = _layer()
+    layer.conv_weight = torch.zeros(1024, 4)
+    with mock.patch.object(gdn, "conv1d") as mc, mock.patch.object(gdn, "extend") as me, \
+            mock.patch.object(gdn, "gdn_gate_inputs") as mg:
+        with pytest.raises(ValueError, match="target verify needs"):
+            gdn.forward_gdn(layer, fb, torch.zeros(3, 1024), torch.zeros(3, 4), torch.zeros(3, 4))
+    mc.assert_not_called()
+    me.assert_not_called()
+    mg.assert_not_called()
 
 
 def test_forward_gdn_invalid_mode_raises_before_any_call():

@@ -4,6 +4,7 @@ bench line.  Runs on CPU with synthetic CSV files shaped like rocprofv3's."""
 import csv
 import importlib.util
 import os
+import sys
 
 import pytest
 
@@ -13,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def load_bench(tmp_path, monkeypatch):
     spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
     mod = importlib.util.module_from_spec(spec)
+    monkeypatch.setitem(sys.modules, "bench_mod", mod)   # (the CPU baseline's workers look it up)
     spec.loader.exec_module(mod)
     monkeypatch.setattr(mod, "PROFILES", str(tmp_path / "profiles"))
     monkeypatch.setattr(mod, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.txt"))
@@ -82,3 +84,17 @@ def test_multi_gpu_request_exits(monkeypatch, capsys):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_runs_the_oracle_over_workers(tmp_path, monkeypatch):
+    """The CPU baseline splits the prefill workload into (sequence, head-block) units
+    over forked single-threaded workers and reports tokens/s, the workers used, the
+    host's CPU count and the one-thread rate."""
+    bench = load_bench(tmp_path, monkeypatch)
+    res = bench.cpu_baseline(nseq=2, seqlen=16, workers=4)
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s"
+    assert res["cores"] == 4 and res["host_cpus"] == os.cpu_count()
+    assert res["value"] > 0 and res["one_thread_value"] > 0
+    assert "4 (sequence, 16-head) units" in res["sample"]
+    assert 1 <= bench.cpu_workers() <= 16
+

@@ -392,8 +392,8 @@ def test_ssd_small(gdn_lib, shape, out_dtype):
     ref, rfin = oracle.ssd_combined(c.x, c.dt, c.A, c.B, c.C, c.D, c.z, c.dt_bias, True,
                                     (0.0, float("inf")), c.initial_states, True)
     bar = (2e-3, 1e-2) if out_dtype == "bf16" else (1e-3, 2e-3)
-    assert_close(out.float().cpu().numpy(), ref, "ssd out", *bar)
-    assert_close(fin.cpu().numpy(), rfin, "ssd states", *bar)
+    assert_close(out.float().cpu().numpy(), ref, "ssd out", *bar, peak_rel=True)
+    assert_close(fin.cpu().numpy(), rfin, "ssd states", *bar, peak_rel=True)
 
 
 @pytest.mark.slow
@@ -408,8 +408,8 @@ def test_config4_ssd_sampled(gdn_lib):
     h = lambda t: t.float().cpu().numpy()
     ref, rfin = oracle.ssd_combined(h(c.x), h(c.dt), h(c.A), h(c.B), h(c.C), h(c.D), h(c.z),
                                     h(c.dt_bias), True, (0.0, float("inf")), None, True, heads=heads)
-    assert_close(h(out[:, :, heads]), ref, "ssd out")
-    assert_close(h(fin[:, heads]), rfin, "ssd states")
+    assert_close(h(out[:, :, heads]), ref, "ssd out", peak_rel=True)
+    assert_close(h(fin[:, heads]), rfin, "ssd states", peak_rel=True)
 
 
 # ------------------------------------------------------------------ adapter and helpers
@@ -518,7 +518,7 @@ def test_ssd_checkpoints(gdn_lib):
                         c.initial_states, True, ckpt_token=rel, ckpt_slot=cks, ckpts=ck)
     got = states.cpu().numpy()
     for s in ck:
-        assert_close(got[s], ck[s], f"ssd checkpoint row {s}")
+        assert_close(got[s], ck[s], f"ssd checkpoint row {s}", peak_rel=True)
     assert (got[4] == SENTINEL).all()
 
 
@@ -564,6 +564,38 @@ def test_target_verify_states(gdn_lib, tree, keep_pool):
     else:
         newpool = oracle.apply_final_states(case.pool, fin)
         assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "verify final states")
+
+
+def test_target_verify_tree_forward_parents(gdn_lib):
+    """Token trees whose parents point forward or at the token itself (inside the
+    recorded rows, so a kernel that followed them would read rows not yet written): such
+    a parent counts as -1 and the token starts from the sequence's start state."""
+    gdn = gdn_lib
+    _announce("target verify tree with forward parents")
+    N, L = 6, 4
+    case = synth.edge_case("verify-fwd", (L,) * N, has_init=1, seed=81, num_slots=10)
+    rows = np.array([2, 0, 5, 1, 4, 3], np.int32)
+    per_seq = [[-1, 2, 3, 1], [-1, 1, 0, 3], [3, 0, 1, 2], [-1, 0, 0, 1], [0, 3, 1, 2], [-1, 2, 2, 0]]
+    parents = np.array(per_seq, np.int32).reshape(-1)
+    d = upload(case)
+    pool_before = d["pool"].clone()
+    states = torch.full((6, L, case.H_v, case.d_v, case.d_k), SENTINEL, dtype=torch.float32, device="cuda")
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    out = gdn.extend(q, k, v, lg, bt, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                     scale=case.scale, max_seqlen=L, spec_states=states,
+                     spec_slot=torch.from_numpy(rows).cuda(), spec_parent=torch.from_numpy(parents).cuda(),
+                     keep_pool=True)
+    torch.cuda.synchronize()
+    spec = {}
+    ref, _, _ = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log, case.dt_bias,
+                                  case.cu_seqlens, case.slot, case.has_init, case.pool, case.scale,
+                                  spec_slot=rows, spec_parent=parents, spec=spec, spec_steps=L)
+    assert_close(out.float().cpu().numpy(), ref, "verify out")
+    got = states.cpu().numpy()
+    for (r, i), S in spec.items():
+        assert_close(got[r, i], S, f"verify state row {r} step {i}")
+    assert torch.equal(d["pool"], pool_before), "keep_pool: the pool changed"
 
 
 def test_forward_gdn_target_verify(gdn_lib):
@@ -689,9 +721,9 @@ def test_ssd_packed_varlen(gdn_lib, with_init):
         i0 = None if init is None else init[n:n + 1]
         ref, rfin = oracle.ssd_combined(sl(c.x), sl(c.dt), c.A, sl(c.B), sl(c.C), c.D, sl(c.z), c.dt_bias,
                                         True, (0.0, float("inf")), i0, True)
-        assert_close(got[:, t0:t1], ref, f"ssd packed out seq {n}")
-        assert_close(gfin[n], rfin[0], f"ssd packed final seq {n}")
+        assert_close(got[:, t0:t1], ref, f"ssd packed out seq {n}", peak_rel=True)
+        assert_close(gfin[n], rfin[0], f"ssd packed final seq {n}", peak_rel=True)
         b = int(bnd[n] - t0)                    # the state after the first b tokens
         _, rck = oracle.ssd_combined(sl(c.x)[:, :b], sl(c.dt)[:, :b], c.A, sl(c.B)[:, :b], sl(c.C)[:, :b],
                                      c.D, sl(c.z)[:, :b], c.dt_bias, True, (0.0, float("inf")), i0, True)
-        assert_close(gck[row], rck[0], f"ssd packed checkpoint seq {n}")
+        assert_close(gck[row], rck[0], f"ssd packed checkpoint seq {n}", peak_rel=True)

@@ -646,6 +646,46 @@ def test_verify_tree_states_and_outputs():
                 _close(out[t0 + i, h], c.scale * S @ (qq / np.sqrt(qq @ qq + 1e-6)))
 
 
+def test_verify_tree_parent_outside_the_past_is_the_start():
+    """A parent outside [0, i) (forward, self or far past the end) or not below the
+    recorded steps counts as -1: the token's state is the dense recurrence from the
+    sequence's start state over the token alone, or over its root path where the chain of
+    parents stays inside the past."""
+    c = tiny_case(lens=(6, 4), has_init=(1, 1))
+    # seq 0: token 1 -> 3 (forward), 2 -> 2 (itself), 3 -> 1, 4 -> 99 (past the end),
+    # 5 -> 4 (whose own parent was forward); seq 1: token 2 -> 3 (forward), 3 -> 2
+    parents = np.array([-1, 3, 2, 1, 99, 4, -1, 0, 3, 2])
+    spec = {}
+    out, _, _ = _run(oracle.gdn_extend, c, spec_slot=np.array([0, 1]), spec_parent=parents, spec=spec)
+
+    def path_of(t0, i, steps=None):
+        path, x = [], i
+        while x >= 0:
+            path.append(t0 + x)
+            p_ = int(parents[t0 + x])
+            x = p_ if (0 <= p_ < x and (steps is None or p_ < steps)) else -1
+        return path[::-1]
+    r = c.H_v // c.H_qk
+    for n, row in ((0, 0), (1, 1)):
+        t0, t1 = int(c.cu_seqlens[n]), int(c.cu_seqlens[n + 1])
+        for i in range(t1 - t0):
+            for h in range(c.H_v):
+                S = _dense_path_state(c, n, h, path_of(t0, i))
+                _close(spec[(row, i)][h], S)
+                qq = c.q[t0 + i, h // r].astype(np.float64)
+                _close(out[t0 + i, h], c.scale * S @ (qq / np.sqrt(qq @ qq + 1e-6)))
+    # with 3 recorded steps, token 5's parent 4 is not recorded: it starts from the start
+    spec3 = {}
+    _run(oracle.gdn_extend, c, spec_slot=np.array([0, 1]), spec_parent=parents, spec=spec3, spec_steps=3)
+    for h in range(c.H_v):
+        _close(spec3[(0, 5)][h], _dense_path_state(c, 0, h, path_of(0, 5, steps=3)))
+        _close(spec3[(0, 3)][h], _dense_path_state(c, 0, h, path_of(0, 3, steps=3)))
+    # the root paths the rule gives (token indices)
+    assert path_of(0, 1) == [1] and path_of(0, 2) == [2] and path_of(0, 3) == [1, 3]
+    assert path_of(0, 4) == [4] and path_of(0, 5) == [4, 5] and path_of(6, 3) == [8, 9]
+    assert path_of(0, 5, steps=3) == [5] and path_of(0, 3, steps=3) == [1, 3]
+
+
 # ------------------------------------------------------------------ short causal conv1d
 # The checks take the implementation as an argument so that the same checks can be
 # run against re-typed versions with planted mistakes (below).
@@ -802,3 +842,26 @@ def test_conv_pins_reject_mutants(kind):
         except (AssertionError, ValueError, IndexError):
             failed += 1
     assert failed > 0, f"no pin rejects the planted mistake {kind!r}"
+
+
+# ------------------------------------------------------------------ committed fixture
+def test_oracle_reproduces_committed_config0_fixture():
+    """tests/golden/config0_oracle.npz (written by tests/golden/make_golden.py through the
+    oracle alone) is a regression fixture: any later change to the oracle's arithmetic
+    that moves the tiny fp32 extend + decode case shows up here as a difference from the
+    committed values (the oracle is float64 throughout; 1e-12 allows for BLAS order)."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "config0_oracle.npz")
+    ref = np.load(path)
+    ext, dec = synth.config0_tiny()
+    out_e, _, fin_e = oracle.gdn_extend(ext.q, ext.k, ext.v, ext.a, ext.b, ext.A_log, ext.dt_bias,
+                                        ext.cu_seqlens, ext.slot, ext.has_init, ext.pool, ext.scale)
+    pool1 = oracle.apply_final_states(ext.pool, fin_e)
+    out_d, _, fin_d = oracle.gdn_decode(dec.q, dec.k, dec.v, dec.a, dec.b, dec.A_log, dec.dt_bias,
+                                        dec.slot, pool1, dec.scale)
+    pool2 = oracle.apply_final_states(pool1, fin_d)
+    assert np.array_equal(ref["slots"], ext.slot)
+    for name, got in (("extend_out", out_e), ("decode_out", out_d),
+                      ("state_after_extend", pool1[ext.slot]), ("state_after_decode", pool2[ext.slot])):
+        np.testing.assert_allclose(got, ref[name], rtol=1e-12, atol=1e-14, err_msg=name)
+
