@@ -8,6 +8,8 @@ stream.  There is no fallback: without the built library every call raises.
 Entry points (same names as the C ABI):
   gate / ssd_gate      a, b -> (log g, beta)               -> gdn_gate
   extend               packed varlen extend over a pool   -> gdn_extend
+  extend_kernel        which kernel an extend call takes  -> gdn_extend_kernel
+  extend_workspace_size  delta-off chunk-128 workspace    -> gdn_extend_workspace_size
   decode               one token per sequence, in place   -> gdn_decode
   conv1d               short causal conv, varlen          -> gdn_conv1d
   conv1d_update        short causal conv, one token/row   -> gdn_conv1d_update
@@ -26,8 +28,8 @@ import torch
 from . import _lib
 from ._lib import GDN_BF16, GDN_F32, GDN_MODE_GDN, GDN_MODE_SSD, GDNError
 
-__all__ = ["load", "gate", "ssd_gate", "extend", "decode", "conv1d", "conv1d_update",
-           "validate_slots", "forward_gdn",
+__all__ = ["load", "gate", "ssd_gate", "extend", "extend_kernel", "extend_workspace_size", "decode",
+           "conv1d", "conv1d_update", "validate_slots", "forward_gdn",
            "ssd_combined_fwd", "GDNError", "split_mixed_qkv"]
 
 
@@ -37,12 +39,14 @@ def load():
 
 
 # ------------------------------------------------------------------ helpers
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dtype_code(t) -> int:
+    """gdn_dtype of a tensor or a torch dtype."""
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    if dt == torch.bfloat16:
         return GDN_BF16
-    if t.dtype == torch.float32:
+    if dt == torch.float32:
         return GDN_F32
-    raise ValueError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+    raise ValueError(f"unsupported dtype {dt} (bf16 or fp32)")
 
 
 def _ptr(t):
@@ -165,23 +169,12 @@ def ssd_gate(dt: torch.Tensor, A: torch.Tensor, dt_bias: torch.Tensor | None = N
 
 
 # ------------------------------------------------------------------ gdn_extend
-def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
-           out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
-           gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
-           ckpt_relative: bool = False, spec_states=None, spec_slot=None, spec_parent=None,
-           keep_pool: bool = False):
-    """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
-    cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
-    (updated in place).  With `gate` (GateInputs of the same mode, dtype and [T, H_v]) the
-    gate is folded into the kernel and log_g / beta are not used (pass None).
-    State checkpoints (all three or none): ckpt_token [N] int32 exclusive token boundaries
-    (absolute, or per sequence with ckpt_relative), ckpt_slot [N] int32 rows of ckpt_states
-    fp32 [num_ckpt, H_v, d_v, d_k]; negative entries disable.
-    Target verify: spec_states fp32 [num_spec, steps, H_v, d_v, d_k] and spec_slot [N] int32
-    record the state after every token; spec_parent [T] int32 (optional) makes the tokens
-    of a sequence a tree; keep_pool leaves the pool unwritten.
-    Returns out [T, H_v, d_v]."""
-    lib = _lib.load()
+def _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
+                 out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
+                 gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
+                 ckpt_relative: bool = False, spec_states=None, spec_slot=None, spec_parent=None,
+                 keep_pool: bool = False, alloc_out: bool = True):
+    """Checks and the ctypes argument struct of one gdn_extend call: (args, out, device)."""
     T, H_qk, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     N = cu_seqlens.shape[0] - 1
@@ -197,7 +190,7 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
             or not pool.is_contiguous():
         raise ValueError(f"pool must be contiguous fp32 [num_slots, {H_v}, {d_v}, {d_k}]")
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if out is None:
+    if out is None and alloc_out:
         out = torch.empty((T, H_v, d_v), dtype=out_dtype, device=dev)
     if scale is None:
         scale = 1.0 if ssd else d_k ** -0.5
@@ -239,12 +232,13 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
             raise ValueError(f"spec_states must be contiguous fp32 [num_spec, steps, {H_v}, {d_v}, {d_k}]")
     args = _lib.ExtendArgs(
         mode=GDN_MODE_SSD if ssd else GDN_MODE_GDN, in_dtype=_dtype_code(q),
-        out_dtype=_dtype_code(out), N=N, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, chunk=chunk,
+        out_dtype=_dtype_code(out if out is not None else out_dtype),
+        N=N, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, chunk=chunk,
         max_seqlen=int(max_seqlen), q=_ptr(q), q_stride=_rows(q, "q", H_qk, d_k), k=_ptr(k),
         k_stride=_rows(k, "k", H_qk, d_k), v=_ptr(v), v_stride=_rows(v, "v", H_v, d_v),
         log_g=_ptr(log_g), beta=_ptr(beta), cu_seqlens=_ptr(cu_seqlens), slot=_ptr(slot),
         has_init=_ptr(has_init), pool=_ptr(pool), num_slots=pool.shape[0], out=_ptr(out),
-        out_stride=_rows(out, "out", H_v, d_v), scale=float(scale),
+        out_stride=_rows(out, "out", H_v, d_v) if out is not None else H_v * d_v, scale=float(scale),
         D_per_dim=int(D is not None and D.dim() == 2), D=_ptr(D), z=_ptr(z),
         z_stride=_rows(z, "z", H_v, d_v) if z is not None else 0,
         ckpt_token=_ptr(ckpt_token), ckpt_slot=_ptr(ckpt_slot), ckpt_states=_ptr(ckpt_states),
@@ -252,11 +246,103 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
         keep_pool=int(bool(keep_pool)), spec_states=_ptr(spec_states), spec_slot=_ptr(spec_slot),
         spec_parent=_ptr(spec_parent), num_spec=spec_states.shape[0] if spec_states is not None else 0,
         spec_steps=spec_states.shape[1] if spec_states is not None else 0)
+    return args, out, dev
+
+
+def _gate_ref(gate):
+    return None if gate is None else ct.byref(gate.args)
+
+
+def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale=None, out=None,
+           out_dtype=None, max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
+           gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
+           ckpt_relative: bool = False, spec_states=None, spec_slot=None, spec_parent=None,
+           keep_pool: bool = False, workspace: torch.Tensor | None = None):
+    """Packed-varlen extend.  q, k [T, H_qk, d_k]; v [T, H_v, d_v]; log_g, beta [T, H_v] fp32;
+    cu_seqlens [N+1], slot [N], has_init [N] int32; pool fp32 [num_slots, H_v, d_v, d_k]
+    (updated in place).  With `gate` (GateInputs of the same mode, dtype and [T, H_v]) the
+    gate is folded into the kernel and log_g / beta are not used (pass None).
+    State checkpoints (all three or none): ckpt_token [N] int32 exclusive token boundaries
+    (absolute, or per sequence with ckpt_relative), ckpt_slot [N] int32 rows of ckpt_states
+    fp32 [num_ckpt, H_v, d_v, d_k]; negative entries disable.
+    Target verify: spec_states fp32 [num_spec, steps, H_v, d_v, d_k] and spec_slot [N] int32
+    record the state after every token; spec_parent [T] int32 (optional) makes the tokens
+    of a sequence a tree; keep_pool leaves the pool unwritten.
+    Delta-off mode (mode="ssd"): chunk 0 or 128 runs the chunk-128 kernel, which needs a
+    workspace of gdn_extend_workspace_size bytes: pass a uint8 device tensor as `workspace`
+    (e.g. a static buffer under graph capture), else one is allocated for the call.
+    Returns out [T, H_v, d_v]."""
+    lib = _lib.load()
+    args, out, dev = _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, has_init=has_init,
+                                  scale=scale, out=out, out_dtype=out_dtype, max_seqlen=max_seqlen,
+                                  mode=mode, D=D, z=z, chunk=chunk, gate=gate, ckpt_token=ckpt_token,
+                                  ckpt_slot=ckpt_slot, ckpt_states=ckpt_states,
+                                  ckpt_relative=ckpt_relative, spec_states=spec_states,
+                                  spec_slot=spec_slot, spec_parent=spec_parent, keep_pool=keep_pool)
+    ws = _workspace(lib, args, gate, dev, workspace)
     if gate is None:
         _lib.check("gdn_extend", lib.gdn_extend(ct.byref(args), _stream(dev)))
     else:
         _lib.check("gdn_extend_gated", lib.gdn_extend_gated(ct.byref(args), ct.byref(gate.args), _stream(dev)))
+    del ws
     return out
+
+
+def _workspace(lib, args, gate, dev, workspace):
+    """Attach the chunk-128 delta-off kernel's workspace to args: the caller's uint8 tensor,
+    or (when the call wants one) a fresh allocation on the current stream."""
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous() \
+                or workspace.device != dev:
+            raise ValueError("workspace must be a contiguous uint8 vector on the call's device")
+        args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel()
+        return workspace
+    need = lib.gdn_extend_workspace_size(ct.byref(args), _gate_ref(gate)) if args.mode == GDN_MODE_SSD else 0
+    if need <= 0:
+        return None
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    args.workspace, args.workspace_bytes = _ptr(ws), need
+    return ws
+
+
+def extend_workspace_size(q, k, v, log_g, beta, cu_seqlens, slot, pool, **kw) -> int:
+    """Bytes of workspace the delta-off chunk-128 kernel wants for extend(...) with these
+    arguments (0 when the call runs another kernel): gdn_extend_workspace_size."""
+    lib = _lib.load()
+    kw.pop("workspace", None)
+    args, _, _ = _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, alloc_out=False, **kw)
+    _placeholder_out(args)
+    return int(lib.gdn_extend_workspace_size(ct.byref(args), _gate_ref(kw.get("gate"))))
+
+
+def _placeholder_out(args):
+    """The host-side queries read no buffer; a call without `out` gets its output from
+    extend(), so they are shown an aligned stand-in address."""
+    if not args.out:
+        args.out = ct.c_void_p(256)
+
+
+def extend_kernel(q, k, v, log_g, beta, cu_seqlens, slot, pool, **kw):
+    """(kernel, reasons): which kernel extend(...) with these arguments runs -- "chunked64",
+    "ssd_chunked128" or "recurrent" -- and the names of the GDN_WHY_* reasons that keep it
+    from the fastest kernel of its mode (empty when it takes that one).  Decided on the
+    host exactly as the call decides it (gdn_extend_kernel); launches nothing."""
+    lib = _lib.load()
+    workspace = kw.pop("workspace", None)
+    args, _, dev = _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, alloc_out=False, **kw)
+    _placeholder_out(args)
+    gate = kw.get("gate")
+    if workspace is not None:
+        args.workspace, args.workspace_bytes = _ptr(workspace), workspace.numel()
+    elif args.mode == GDN_MODE_SSD:   # extend() would allocate what the call wants
+        need = lib.gdn_extend_workspace_size(ct.byref(args), _gate_ref(gate))
+        if need > 0:
+            args.workspace, args.workspace_bytes = ct.c_void_p(256), need
+    why = ct.c_int32(0)
+    kern = lib.gdn_extend_kernel(ct.byref(args), _gate_ref(gate), ct.byref(why))
+    if kern < 0:
+        _lib.check("gdn_extend_kernel", -kern)
+    return _lib.KERNEL_NAMES[kern], [n for i, n in enumerate(_lib.WHY_NAMES) if why.value >> i & 1]
 
 
 # ------------------------------------------------------------------ gdn_decode

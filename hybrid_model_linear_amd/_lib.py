@@ -10,11 +10,18 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_status_str",
-            "gdn_last_hip_error", "gdn_abi_version"]
+            "gdn_last_hip_error", "gdn_abi_version", "gdn_extend_workspace_size", "gdn_extend_kernel"]
+
+# gdn_extend_kernel results and reason bits (include/gdn.h)
+GDN_KERNEL_RECURRENT, GDN_KERNEL_CHUNKED, GDN_KERNEL_SSD_CHUNKED = 1, 2, 3
+KERNEL_NAMES = {0: "none", GDN_KERNEL_RECURRENT: "recurrent", GDN_KERNEL_CHUNKED: "chunked64",
+                GDN_KERNEL_SSD_CHUNKED: "ssd_chunked128"}
+WHY_NAMES = ["fp32_inputs", "short_batch", "target_verify", "head_dims", "alignment", "stride",
+             "batch", "gate_alignment", "no_workspace", "chunk64_requested"]
 
 
 class GateArgs(C.Structure):
@@ -40,7 +47,8 @@ class ExtendArgs(C.Structure):
                 ("ckpt_token", C.c_void_p), ("ckpt_slot", C.c_void_p), ("ckpt_states", C.c_void_p),
                 ("num_ckpt", C.c_int64), ("ckpt_relative", C.c_int32), ("keep_pool", C.c_int32),
                 ("spec_states", C.c_void_p), ("spec_slot", C.c_void_p), ("spec_parent", C.c_void_p),
-                ("num_spec", C.c_int64), ("spec_steps", C.c_int32), ("_pad_spec", C.c_int32)]
+                ("num_spec", C.c_int64), ("spec_steps", C.c_int32), ("_pad_spec", C.c_int32),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_int64)]
 
 
 class DecodeArgs(C.Structure):
@@ -89,6 +97,10 @@ def load(path: str | None = None) -> C.CDLL:
                "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_last_hip_error",
                "gdn_abi_version"):
         getattr(lib, fn).restype = C.c_int
+    lib.gdn_extend_workspace_size.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs)]
+    lib.gdn_extend_workspace_size.restype = C.c_int64
+    lib.gdn_extend_kernel.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.POINTER(C.c_int32)]
+    lib.gdn_extend_kernel.restype = C.c_int
     lib.gdn_status_str.argtypes = [C.c_int]
     lib.gdn_status_str.restype = C.c_char_p
     lib.gdn_last_hip_error.argtypes = []

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "gdn_launch.h"
@@ -85,6 +86,7 @@ void fill_fused_gate(gdn::SeqLaunch& p, const gdn_gate_args* g) {
   p.g_hi = g->dt_max;
 }
 
+int plan_extend(const gdn_extend_args* a, const gdn_gate_args* gate, gdn::SeqLaunch& p, int& why);
 int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream);
 int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream);
 
@@ -137,6 +139,23 @@ int gdn_extend_gated(const gdn_extend_args* a, const gdn_gate_args* gate, void* 
   if (!gate) return GDN_E_NULL;
   return extend_impl(a, gate, stream);
 }
+int gdn_extend_kernel(const gdn_extend_args* a, const gdn_gate_args* gate, int32_t* why) {
+  gdn::SeqLaunch p{};
+  int w = 0;
+  const int k = plan_extend(a, gate, p, w);
+  if (why) *why = w;
+  return k;
+}
+int64_t gdn_extend_workspace_size(const gdn_extend_args* a, const gdn_gate_args* gate) {
+  if (!a || a->mode != GDN_MODE_SSD || a->chunk == 64 || a->N <= 0) return 0;
+  gdn::SeqLaunch p{};
+  int w = 0;
+  gdn_extend_args probe = *a;                     // as if a large workspace were given
+  probe.workspace = reinterpret_cast<void*>(uintptr_t(256));
+  probe.workspace_bytes = INT64_MAX;
+  if (plan_extend(&probe, gate, p, w) != GDN_KERNEL_SSD_CHUNKED) return 0;
+  return gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, p.ssd_segs);
+}
 int gdn_decode(const gdn_decode_args* a, void* stream) { return decode_impl(a, nullptr, stream); }
 int gdn_decode_gated(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream) {
   if (!gate) return GDN_E_NULL;
@@ -147,44 +166,91 @@ int gdn_decode_gated(const gdn_decode_args* a, const gdn_gate_args* gate, void* 
 
 namespace {
 
-int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
-  if (!a) return GDN_E_NULL;
-  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return GDN_E_UNSUPPORTED;
+// Compute units of the current device (cached per device; 256, an MI355X, when the
+// runtime cannot tell): the segment plan of the chunk-128 delta-off kernel fills them.
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Segments per sequence for the chunk-128 delta-off kernel: the count (1..16) that
+// minimises the estimated makespan in chunk steps -- ceil(N H_v s / CUs) rounds of
+// ceil(chunks / s) chunk steps for the full pass, plus for s > 1 the state-only pass
+// over all but the last segment (about a third of a full step per chunk) -- among
+// those whose workspace fits in `budget` bytes.  Unknown lengths (max_seqlen 0): one.
+void ssd_plan(gdn::SeqLaunch& p, int max_seqlen, int64_t budget) {
+  p.ssd_segs = 1;
+  p.ssd_seg_chunks = 1 << 30;
+  if (max_seqlen <= 0) return;
+  const int nch = (max_seqlen + 127) / 128;
+  const double units = (double)p.N * p.H_v, cus = (double)device_cus();
+  double best = 1e300;
+  for (int s = 1; s <= 16 && s <= nch; ++s) {
+    const int sc = (nch + s - 1) / s;
+    const int se = (nch + sc - 1) / sc;           // segments that hold chunks
+    if ((int64_t)p.N * se > 65535 || gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, se) > budget) break;
+    double cost = std::ceil(units * se / cus) * sc;
+    if (se > 1) cost += std::ceil(units * (se - 1) / cus) * sc * 0.35;
+    if (cost < best * 0.98) {                     // (ties go to fewer segments)
+      best = cost;
+      p.ssd_segs = se;
+      p.ssd_seg_chunks = se > 1 ? sc : 1 << 30;
+    }
+  }
+}
+
+// Host-side plan of an extend call: every check, the launch descriptor and the kernel
+// choice.  Returns the GDN_KERNEL_* to launch, 0 when the call launches nothing, or
+// minus a gdn_status; `why` collects the GDN_WHY_* bits that keep it from the fastest
+// kernel of its mode.
+int plan_extend(const gdn_extend_args* a, const gdn_gate_args* gate, gdn::SeqLaunch& p, int& why) {
+  why = 0;
+  if (!a) return -GDN_E_NULL;
+  if (a->mode != GDN_MODE_GDN && a->mode != GDN_MODE_SSD) return -GDN_E_UNSUPPORTED;
   int st = check_seq_common(a->in_dtype, a->out_dtype, a->H_qk, a->H_v, a->d_k, a->d_v,
                             a->q_stride, a->k_stride, a->v_stride, a->out_stride, a->num_slots,
                             a->scale);
-  if (st != GDN_OK) return st;
-  if (a->N < 0 || a->T < 0 || a->max_seqlen < 0) return GDN_E_SHAPE;
-  if (a->chunk != 0 && a->chunk != 64) return GDN_E_UNSUPPORTED;
-  if (a->mode == GDN_MODE_GDN && (a->D || a->z)) return GDN_E_SHAPE;   // SSD-only inputs
-  if (a->z && a->z_stride < (int64_t)a->H_v * a->d_v) return GDN_E_SHAPE;
+  if (st != GDN_OK) return -st;
+  if (a->N < 0 || a->T < 0 || a->max_seqlen < 0) return -GDN_E_SHAPE;
+  const bool ssd = a->mode == GDN_MODE_SSD;
+  if (a->chunk != 0 && a->chunk != 64 && !(ssd && a->chunk == 128)) return -GDN_E_UNSUPPORTED;
+  if (!ssd && (a->D || a->z)) return -GDN_E_SHAPE;   // SSD-only inputs
+  if (a->z && a->z_stride < (int64_t)a->H_v * a->d_v) return -GDN_E_SHAPE;
   if (gate) {
     st = check_fused_gate(gate, a->mode, a->in_dtype, a->T, a->H_v);
-    if (st != GDN_OK) return st;
+    if (st != GDN_OK) return -st;
   }
   // checkpoints: all three pointers or none
   const int nck = (a->ckpt_token != nullptr) + (a->ckpt_slot != nullptr) + (a->ckpt_states != nullptr);
-  if (nck != 0 && nck != 3) return GDN_E_NULL;
-  if (a->num_ckpt < 0) return GDN_E_SHAPE;
-  if (nck == 3 && reinterpret_cast<uintptr_t>(a->ckpt_states) % 16 != 0) return GDN_E_SHAPE;
+  if (nck != 0 && nck != 3) return -GDN_E_NULL;
+  if (a->num_ckpt < 0) return -GDN_E_SHAPE;
+  if (nck == 3 && reinterpret_cast<uintptr_t>(a->ckpt_states) % 16 != 0) return -GDN_E_SHAPE;
   // target-verify states: spec_states and spec_slot together; spec_parent needs them
   const bool spec = a->spec_states != nullptr;
-  if (spec != (a->spec_slot != nullptr) || (a->spec_parent && !spec)) return GDN_E_NULL;
+  if (spec != (a->spec_slot != nullptr) || (a->spec_parent && !spec)) return -GDN_E_NULL;
   if (spec && (a->num_spec < 0 || a->spec_steps < 1 ||
                reinterpret_cast<uintptr_t>(a->spec_states) % 16 != 0))
-    return GDN_E_SHAPE;
-  if (a->N == 0) return GDN_OK;
-  if (!a->cu_seqlens || !a->slot || !a->pool) return GDN_E_NULL;
-  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->out)) return GDN_E_NULL;
-  if (a->T > 0 && !gate && (!a->log_g || !a->beta)) return GDN_E_NULL;
-  if (a->T > INT32_MAX) return GDN_E_SHAPE;      // cu_seqlens is int32
+    return -GDN_E_SHAPE;
+  if (a->workspace_bytes < 0 || reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return -GDN_E_SHAPE;
+  if (a->N == 0) return 0;
+  if (!a->cu_seqlens || !a->slot || !a->pool) return -GDN_E_NULL;
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->out)) return -GDN_E_NULL;
+  if (a->T > 0 && !gate && (!a->log_g || !a->beta)) return -GDN_E_NULL;
+  if (a->T > INT32_MAX) return -GDN_E_SHAPE;      // cu_seqlens is int32
   if (!aligned4(a->q, a->in_dtype) || !aligned4(a->k, a->in_dtype) || !aligned4(a->v, a->in_dtype) ||
       !aligned4(a->z, a->in_dtype) || !aligned4(a->out, a->out_dtype) || a->z_stride % 4 != 0 ||
       reinterpret_cast<uintptr_t>(a->pool) % 16 != 0)
-    return GDN_E_SHAPE;
+    return -GDN_E_SHAPE;
 
-  gdn::SeqLaunch p{};
-  p.ssd = a->mode == GDN_MODE_SSD;
+  p = gdn::SeqLaunch{};
+  p.ssd = ssd;
   p.in_bf16 = a->in_dtype == GDN_BF16;
   p.out_bf16 = a->out_dtype == GDN_BF16;
   p.N = a->N;
@@ -208,7 +274,7 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
   p.num_slots = a->num_slots;
   p.out = a->out;
   p.out_stride = a->out_stride;
-  p.scale = a->mode == GDN_MODE_SSD ? 1.0f : a->scale;
+  p.scale = ssd ? 1.0f : a->scale;
   p.D = a->D;
   p.D_per_dim = a->D_per_dim;
   p.z = a->z;
@@ -228,12 +294,44 @@ int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* strea
     p.sp_parent = a->spec_parent;
     p.sp_steps = a->spec_steps;
   }
-
-  const bool short_batch = a->max_seqlen > 0 && a->max_seqlen <= 8;
   p.lpt = a->N >= 2 && a->N <= 128;
-  if (p.in_bf16 && !short_batch && !spec && gdn::chunked_supported(p))
-    return hip_status(gdn::launch_chunked(p, (hipStream_t)stream));
-  return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
+
+  const int common = (a->max_seqlen > 0 && a->max_seqlen <= 8 ? GDN_WHY_SHORT : 0) | (spec ? GDN_WHY_VERIFY : 0);
+  if (ssd && a->chunk != 64) {                    // the chunk-128 delta-off kernel
+    const int w = gdn::ssd_obstacles(p) | common;
+    const bool ws = a->workspace && a->workspace_bytes >= gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 1);
+    if (a->chunk == 128) {
+      if (w) return -GDN_E_UNSUPPORTED;
+      if (!a->workspace) return -GDN_E_NULL;
+      if (!ws) return -GDN_E_SHAPE;
+    }
+    if (!w && ws) {
+      ssd_plan(p, a->max_seqlen, a->workspace_bytes);
+      return GDN_KERNEL_SSD_CHUNKED;
+    }
+    why |= w | (ws ? 0 : GDN_WHY_WORKSPACE);
+  } else if (ssd) {
+    why |= GDN_WHY_CHUNK;
+  }
+  const int w = gdn::chunked_obstacles(p) | common;
+  why |= w;
+  return w ? GDN_KERNEL_RECURRENT : GDN_KERNEL_CHUNKED;
+}
+
+int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
+  gdn::SeqLaunch p{};
+  int why = 0;
+  const int k = plan_extend(a, gate, p, why);
+  if (k <= 0) return -k;
+  switch (k) {
+    case GDN_KERNEL_SSD_CHUNKED:
+      gdn::ssd_bind_workspace(p, a->workspace);
+      return hip_status(gdn::launch_ssd(p, (hipStream_t)stream));
+    case GDN_KERNEL_CHUNKED:
+      return hip_status(gdn::launch_chunked(p, (hipStream_t)stream));
+    default:
+      return hip_status(gdn::launch_recurrent(p, (hipStream_t)stream));
+  }
 }
 
 int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream) {

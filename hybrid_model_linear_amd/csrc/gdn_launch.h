@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn.h"
+#include "gdn_common.h"
+
 namespace gdn {
 
 struct GateLaunch {
@@ -83,6 +86,16 @@ struct SeqLaunch {
   int sp_steps;
   int keep_pool;
   int lpt;                    // chunked kernel: longest sequences first (small N)
+  // Chunk-128 delta-off kernel: fp16 copies of B (k) and C (q), [T, H_qk, d_k], in the
+  // caller's workspace; each sequence cut into ssd_segs segments of ssd_seg_chunks
+  // chunks (the last takes the rest) with the states segR [N, segs - 1, H_v, d_v, d_k]
+  // and log decays segL [N, segs - 1, H_v] of all but the last segment.
+  const u16* ssd_Bh;
+  const u16* ssd_Ch;
+  float* segR;
+  float* segL;
+  int ssd_segs;
+  int ssd_seg_chunks;
 };
 
 // Short causal conv1d (bf16, width K) over packed sequences with a conv-state pool.
@@ -112,7 +125,16 @@ hipError_t launch_recurrent(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_chunked(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_validate_slots(const int32_t* slot, int n, int64_t num_slots, int32_t* flag,
                                  hipStream_t stream);
-bool chunked_supported(const SeqLaunch& p);
+// Why the chunk-64 kernel cannot run this call (GDN_WHY_* bits of gdn.h), 0 if it can.
+int chunked_obstacles(const SeqLaunch& p);
+// Chunk-128 delta-off kernel: whether it has a tile plan for the head dims, what else
+// keeps it from this call (GDN_WHY_* bits), its workspace bytes for `segs` segments per
+// sequence, how a workspace is carved up, and the launch (prep, segment states, full pass).
+bool ssd_chunked_shape(const SeqLaunch& p);
+int ssd_obstacles(const SeqLaunch& p);
+int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int segs);
+void ssd_bind_workspace(SeqLaunch& p, void* ws);
+hipError_t launch_ssd(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_conv(const ConvLaunch& p, hipStream_t stream);          // varlen: outputs, then states
 hipError_t launch_conv_update(const ConvLaunch& p, hipStream_t stream);   // one token per row
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -114,10 +114,21 @@ typedef struct gdn_gate_args {
  * log_g / beta from gdn_gate in SSD mode.
  *
  * Supported: d_k, d_v in {64, 128}; H_v % H_qk == 0; in_dtype bf16 or fp32 with
- * out_dtype bf16 or fp32.  chunk: 0 (default) or 64; bf16 inputs use the chunked
- * MFMA kernel (chunk 64), fp32 inputs and short batches (max_seqlen in 1..8) the
- * token-recurrent kernel.  max_seqlen is a host-side hint (an upper bound of the
- * longest sequence, 0 = unknown); a wrong hint changes speed, never results.
+ * out_dtype bf16 or fp32.  bf16 inputs use the chunked MFMA kernels, fp32 inputs and
+ * short batches (max_seqlen in 1..8) the token-recurrent kernel; gdn_extend_kernel()
+ * tells which kernel a call takes and why.  max_seqlen is a host-side hint (an upper
+ * bound of the longest sequence, 0 = unknown); a wrong hint changes speed, never
+ * results.
+ *   chunk, GDN mode : 0 (default) or 64 (the chunk-64 kernel; d_k = d_v = 128).
+ *   chunk, SSD mode : 64, 128 or 0 (default: 128 when the call can take it, else 64).
+ *     The chunk-128 delta-off kernel (d_k = dstate = 128, d_v = headdim = 64, the
+ *     ssd_combined_fwd chunk size) needs a caller workspace: fp16 copies of B and C
+ *     (every head of a group reads them) and, to run the segments of a sequence in
+ *     parallel, their states.  gdn_extend_workspace_size() gives the bytes it wants;
+ *     a smaller workspace (at least the size for one segment) means fewer segments,
+ *     i.e. speed only.  chunk = 128 without a usable workspace: GDN_E_NULL (none) or
+ *     GDN_E_SHAPE (too small for one segment).  Its fp16 operands need |C.B|, |dt' x|
+ *     and the state below 65504 (beyond that the outputs turn inf / NaN).
  *
  * State checkpoints (optional; the checkpoint_token_indices / checkpoint_state_slots
  * / checkpoint_states arguments of the ssd_combined_fwd page, in both modes):
@@ -194,7 +205,43 @@ typedef struct gdn_extend_args {
   int64_t num_spec;
   int32_t spec_steps;
   int32_t _pad_spec;
+  void* workspace;           /* device scratch of the chunk-128 delta-off kernel, or NULL */
+  int64_t workspace_bytes;
 } gdn_extend_args;
+
+/* Workspace bytes the chunk-128 delta-off kernel wants for a gdn_extend (gate NULL) or
+ * gdn_extend_gated call with these arguments (fp16 B and C copies, and the states of
+ * the segments the library would run: it grows with T and with N x H_v x segments), or
+ * 0 when the call would run another kernel or is invalid.  Host-side, launches nothing;
+ * args->workspace / workspace_bytes are ignored.  The workspace must be 256-byte
+ * aligned (else GDN_E_SHAPE) and is overwritten by the call (its contents need not be
+ * initialised and mean nothing afterwards); calls in flight at once need their own. */
+int64_t gdn_extend_workspace_size(const gdn_extend_args* args, const gdn_gate_args* gate);
+
+/* Kernels of gdn_extend / gdn_extend_gated, and what keeps a call from a faster one. */
+enum {
+  GDN_KERNEL_RECURRENT = 1,   /* token-recurrent (decode kernel, a token at a time)   */
+  GDN_KERNEL_CHUNKED = 2,     /* chunk-64 MFMA kernel                                 */
+  GDN_KERNEL_SSD_CHUNKED = 3  /* chunk-128 delta-off MFMA kernel                      */
+};
+enum {
+  GDN_WHY_FP32 = 1 << 0,        /* fp32 inputs                                          */
+  GDN_WHY_SHORT = 1 << 1,       /* max_seqlen hint in 1..8 (short or verify batches)    */
+  GDN_WHY_VERIFY = 1 << 2,      /* target-verify states requested                       */
+  GDN_WHY_HEAD_DIMS = 1 << 3,   /* head sizes without a chunked tile plan               */
+  GDN_WHY_ALIGN = 1 << 4,       /* rows not 16-byte aligned or strides not multiples of 8 */
+  GDN_WHY_STRIDE = 1 << 5,      /* token strides beyond 32-bit in-chunk offsets         */
+  GDN_WHY_BATCH = 1 << 6,       /* more than 65535 sequences                            */
+  GDN_WHY_GATE_ALIGN = 1 << 7,  /* folded gate (GDN): a, b not 4-byte aligned, odd strides */
+  GDN_WHY_WORKSPACE = 1 << 8,   /* delta-off: no workspace for the chunk-128 kernel     */
+  GDN_WHY_CHUNK = 1 << 9        /* delta-off: chunk 64 requested                        */
+};
+/* The kernel a gdn_extend (gate NULL) or gdn_extend_gated call with these arguments
+ * runs, decided on the host exactly as the call decides it; launches nothing.
+ * Returns GDN_KERNEL_* (> 0), or minus the gdn_status the call would return.  *why
+ * (may be NULL) receives the GDN_WHY_* bits of everything that keeps the call from
+ * the fastest kernel of its mode (0 when it takes that kernel). */
+int gdn_extend_kernel(const gdn_extend_args* args, const gdn_gate_args* gate, int32_t* why);
 
 /* ---------------------------------------------------------------- gdn_decode
  * One token per sequence: token b belongs to sequence b, which always starts from

@@ -25,7 +25,7 @@ HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(gdn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|int64_t)\s+(gdn_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -113,6 +113,110 @@ def test_extend_null_and_empty():
     assert lib.gdn_extend(ct.byref(_ext(N=0)), None) == _lib.GDN_OK      # nothing to do
     a = _ext(cu_seqlens=FAKE, slot=FAKE, pool=FAKE)                      # q..out missing
     assert lib.gdn_extend(ct.byref(a), None) == _lib.GDN_E_NULL
+
+
+# ------------------------------------------------------------------ kernel choice and workspace
+# Host-side planning only: gdn_extend_kernel and gdn_extend_workspace_size decide exactly
+# as gdn_extend does and launch nothing, so fake (aligned, never dereferenced) pointers do.
+def _ptrs(**kw):
+    d = dict(q=ct.c_void_p(0x10000), k=ct.c_void_p(0x20000), v=ct.c_void_p(0x30000),
+             log_g=ct.c_void_p(0x40000), beta=ct.c_void_p(0x50000), cu_seqlens=FAKE, slot=FAKE,
+             pool=ct.c_void_p(0x60000), out=ct.c_void_p(0x70000))
+    d.update(kw)
+    return d
+
+
+def _ssd(**kw):
+    """Delta-off arguments shaped like the Mamba2 workload (2 x 8192 tokens, 80 heads of
+    headdim 64, one group of dstate 128)."""
+    base = dict(mode=1, in_dtype=1, out_dtype=1, N=2, T=16384, H_qk=1, H_v=80, d_k=128, d_v=64,
+                chunk=0, max_seqlen=8192, q_stride=128, k_stride=128, v_stride=80 * 64,
+                num_slots=2, out_stride=80 * 64, scale=1.0, **_ptrs())
+    base.update(kw)
+    return _lib.ExtendArgs(**base)
+
+
+def _kernel(args, gate=None):
+    lib = gdn.load()
+    why = ct.c_int32(-1)
+    k = lib.gdn_extend_kernel(ct.byref(args), None if gate is None else ct.byref(gate), ct.byref(why))
+    return k, why.value
+
+
+W = {n: 1 << i for i, n in enumerate(_lib.WHY_NAMES)}
+
+
+@pytest.mark.parametrize("kw,kernel,why", [
+    (dict(), _lib.GDN_KERNEL_CHUNKED, 0),
+    (dict(in_dtype=0, out_dtype=0), _lib.GDN_KERNEL_RECURRENT, W["fp32_inputs"]),
+    (dict(max_seqlen=4), _lib.GDN_KERNEL_RECURRENT, W["short_batch"]),
+    (dict(d_k=64, q_stride=2 * 2 * 64 + 4 * 128, k_stride=2 * 2 * 64 + 4 * 128, v_stride=2 * 2 * 64 + 4 * 128),
+     _lib.GDN_KERNEL_RECURRENT, W["head_dims"]),
+    (dict(q=ct.c_void_p(0x10008)), _lib.GDN_KERNEL_RECURRENT, W["alignment"]),
+    (dict(q_stride=16 * 1024 * 1024), _lib.GDN_KERNEL_RECURRENT, W["stride"]),
+    (dict(spec_states=ct.c_void_p(0x80000), spec_slot=FAKE, num_spec=1, spec_steps=4),
+     _lib.GDN_KERNEL_RECURRENT, W["target_verify"]),
+    (dict(N=0), 0, 0),                                            # launches nothing
+    (dict(chunk=128), -_lib.GDN_E_UNSUPPORTED, 0),                # GDN mode has chunk 64 only
+])
+def test_extend_kernel_choice_gdn(kw, kernel, why):
+    a = _ext(**_ptrs())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    assert _kernel(a) == (kernel, why)
+
+
+def test_extend_kernel_choice_folded_gate_alignment():
+    g = _lib.GateArgs(mode=0, in_dtype=1, T=4, H=4, a=ct.c_void_p(0x90002), a_stride=4,
+                      b=ct.c_void_p(0xA0000), b_stride=4, A=FAKE)
+    a = _ext(**_ptrs(log_g=None, beta=None))
+    assert _kernel(a, g) == (_lib.GDN_KERNEL_RECURRENT, W["gate_alignment"])
+    g.a = ct.c_void_p(0x90000)
+    assert _kernel(a, g) == (_lib.GDN_KERNEL_CHUNKED, 0)
+
+
+def test_ssd_kernel_choice_and_workspace():
+    lib = gdn.load()
+    a = _ssd()
+    need = lib.gdn_extend_workspace_size(ct.byref(a), None)
+    # fp16 B and C copies (16384 x 128 x 2 bytes each) plus segment states of 64 KiB...
+    bc = 16384 * 128 * 2
+    assert need > 2 * bc and (need - 2 * bc) % 256 == 0
+    assert _kernel(a) == (_lib.GDN_KERNEL_CHUNKED, W["no_workspace"])          # chunk 64 without it
+    a.workspace, a.workspace_bytes = ct.c_void_p(0x1000000), need
+    assert _kernel(a) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
+    a.workspace_bytes = 2 * bc                                                 # one segment still fits
+    assert _kernel(a) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
+    a.workspace_bytes = 2 * bc - 256                                           # too small: chunk 64
+    assert _kernel(a) == (_lib.GDN_KERNEL_CHUNKED, W["no_workspace"])
+    a.chunk = 128                                                              # ... unless 128 is asked for
+    assert _kernel(a)[0] == -_lib.GDN_E_SHAPE
+    a.workspace, a.workspace_bytes = None, 0
+    assert _kernel(a)[0] == -_lib.GDN_E_NULL
+    a.workspace, a.workspace_bytes, a.chunk = ct.c_void_p(0x1000000), need, 64
+    assert _kernel(a) == (_lib.GDN_KERNEL_CHUNKED, W["chunk64_requested"])
+    assert lib.gdn_extend_workspace_size(ct.byref(a), None) == 0              # chunk 64 needs none
+    a.chunk = 0
+    a.workspace = ct.c_void_p(0x1000010)                                      # not 256-byte aligned
+    assert _kernel(a)[0] == -_lib.GDN_E_SHAPE
+    a.workspace = ct.c_void_p(0x1000000)
+    a.in_dtype = a.out_dtype = 0                                               # fp32 inputs: token-recurrent
+    assert _kernel(a) == (_lib.GDN_KERNEL_RECURRENT, W["fp32_inputs"])
+    assert lib.gdn_extend_workspace_size(ct.byref(a), None) == 0
+    a.chunk = 128
+    assert _kernel(a)[0] == -_lib.GDN_E_UNSUPPORTED
+    assert lib.gdn_extend_workspace_size(ct.byref(_ext(**_ptrs())), None) == 0  # GDN mode: none
+
+
+def test_ssd_workspace_grows_with_segments_and_unknown_length_needs_one():
+    """Without a length hint the kernel runs one segment per sequence: the workspace holds
+    only the B and C copies.  With the hint, the segment states come on top."""
+    lib = gdn.load()
+    a = _ssd(max_seqlen=0)
+    one = lib.gdn_extend_workspace_size(ct.byref(a), None)
+    assert one == 2 * 16384 * 128 * 2
+    a.max_seqlen = 8192
+    assert lib.gdn_extend_workspace_size(ct.byref(a), None) > one
 
 
 def _conv(**kw):
