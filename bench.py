@@ -64,6 +64,8 @@ def parse():
     # ~0.6 s of warm-up: the GPU's clocks settle before the timed region
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the ragged, verify and delta-off workloads")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter scaling)")
     ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -272,6 +274,107 @@ def bench_conv(torch, gdn, T_e, n_seq, T_d, steps):
     return res
 
 
+def _rate(us, nbytes, flop):
+    sec = us * 1e-6
+    gbs, tfs = nbytes / sec / 1e9, flop / sec / 1e12
+    return {"GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def _time_calls(torch, fn, steps, warm=10):
+    """Average microseconds per call of fn over `steps` back-to-back calls, from HIP events
+    recorded on torch's current stream (the stream the calls launch on)."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+SSD_H, SSD_P, SSD_N, SSD_G, SSD_CHUNK = 80, 64, 128, 1, 128
+SSD_BYTES_PER_TOKEN = 3 * SSD_H * SSD_P * 2 + SSD_H * 2 + 2 * SSD_G * SSD_N * 2   # x, z, out; dt; B, C
+SSD_FLOP_PER_TOKEN = SSD_H * 2 * (SSD_CHUNK * SSD_P + 2 * SSD_N * SSD_P) + 2 * SSD_CHUNK * SSD_N * SSD_G
+
+
+def bench_configs(torch, gdn, synth, steps, only=None):
+    """The other workloads, each timed on its own (not part of the step): the ragged
+    extend from pooled states (64 sequences, ~131k tokens) and its verify batch (32 x 4
+    tokens), and the delta-off (SSD) call at chunk 128 (x [2, 8192, 80, 64]).  Inputs
+    resident in HBM; outputs, pools and the delta-off workspace allocated before timing."""
+    dev = "cuda"
+    t32 = lambda x: torch.from_numpy(x).to(dev, torch.float32)
+    ti = lambda x: torch.from_numpy(x).to(dev, torch.int32)
+    res = {}
+
+    def gdn_leg(case, pool, max_seqlen):
+        q, k, v = gdn.split_mixed_qkv(case.mixed_qkv, case.H_qk, case.H_v, case.d_k, case.d_v)
+        g = gdn.gdn_gate_inputs(case.a, case.b, t32(case.A_log), t32(case.dt_bias))
+        out = torch.empty((case.T, case.H_v, case.d_v), dtype=torch.bfloat16, device=dev)
+        cu, slot, hi = ti(case.cu_seqlens), ti(case.slot), ti(case.has_init)
+        kern = gdn.extend_kernel(q, k, v, None, None, cu, slot, pool, has_init=hi, scale=case.scale,
+                                 max_seqlen=max_seqlen, gate=g)
+        fn = lambda: gdn.extend(q, k, v, None, None, cu, slot, pool, has_init=hi, scale=case.scale,
+                                out=out, max_seqlen=max_seqlen, gate=g)
+        return _time_calls(torch, fn, steps), kern
+
+    # ragged extend from pooled states, then its verify batch on other slots of the pool
+    if only is not None and "ssd_chunk128" in only:
+        return {"ssd_chunk128": bench_ssd(torch, gdn, synth, steps)}
+    rag = synth.device_config3_ragged()
+    pool3 = synth.device_pool(rag)
+    lens = rag.cu_seqlens[1:] - rag.cu_seqlens[:-1]
+    us, kern = gdn_leg(rag, pool3, int(lens.max()))
+    nbytes = rag.T * IO_BYTES_PER_TOKEN + rag.N * 2 * STATE_BYTES        # states read and written
+    flop = rag.T * EXTEND_FLOP_PER_TOKEN
+    res["ragged_extend"] = dict(workload=f"extend {rag.N} ragged sequences (log-uniform lengths "
+                                         f"{int(lens.min())}..{int(lens.max())}, {rag.T} tokens) from "
+                                         f"pooled states, pool [512,32,128,128] fp32",
+                                kernel=kern[0], avg_us=round(us, 2), tokens_per_s=round(rag.T / (us * 1e-6), 1),
+                                bytes=nbytes, flop=flop, **_rate(us, nbytes, flop))
+    ver = synth.device_config3_verify()
+    us, kern = gdn_leg(ver, pool3, 4)
+    nbytes = ver.T * IO_BYTES_PER_TOKEN + ver.N * 2 * STATE_BYTES
+    flop = ver.T * 7 * H_V * D * D
+    res["verify_extend"] = dict(workload="extend 32 sequences x 4 tokens from pooled states",
+                                kernel=kern[0], avg_us=round(us, 2), tokens_per_s=round(ver.T / (us * 1e-6), 1),
+                                bytes=nbytes, flop=flop, **_rate(us, nbytes, flop))
+    del rag, ver, pool3
+    res["ssd_chunk128"] = bench_ssd(torch, gdn, synth, steps)
+    return res
+
+
+def bench_ssd(torch, gdn, synth, steps):
+    """The delta-off (Mamba2 SSD) call at chunk 128 on x [2, 8192, 80, 64]."""
+    dev = "cuda"
+    c = synth.device_config4_ssd()
+    batch, L = c.x.shape[0], c.x.shape[1]
+    T = batch * L
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+    slot = torch.arange(batch, dtype=torch.int32, device=dev)
+    hi = torch.zeros(batch, dtype=torch.int32, device=dev)
+    pool = torch.zeros((batch, SSD_H, SSD_P, SSD_N), dtype=torch.float32, device=dev)
+    out = torch.empty((T, SSD_H, SSD_P), dtype=torch.bfloat16, device=dev)
+    g = gdn.ssd_gate_inputs(c.dt.view(T, SSD_H), c.A, c.dt_bias, True, (0.0, float("inf")))
+    qkv = (c.C.view(T, SSD_G, SSD_N), c.B.view(T, SSD_G, SSD_N), c.x.view(T, SSD_H, SSD_P))
+    kw = dict(has_init=hi, mode="ssd", D=c.D, z=c.z.view(T, SSD_H, SSD_P), max_seqlen=L, gate=g)
+    need = gdn.extend_workspace_size(*qkv, None, None, cu, slot, pool, **kw)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    kern = gdn.extend_kernel(*qkv, None, None, cu, slot, pool, workspace=ws, **kw)
+    us = _time_calls(torch, lambda: gdn.extend(*qkv, None, None, cu, slot, pool, out=out, workspace=ws, **kw),
+                     steps)
+    nbytes = T * SSD_BYTES_PER_TOKEN + batch * SSD_H * SSD_P * SSD_N * 4   # zero init: states written
+    flop = T * SSD_FLOP_PER_TOKEN
+    return dict(workload=f"delta-off (SSD) x [{batch},{L},{SSD_H},{SSD_P}], B/C [{batch},{L},{SSD_G},{SSD_N}], "
+                         f"D, silu(z), chunk 128, zero initial states", kernel=kern[0], workspace_bytes=int(need),
+                avg_us=round(us, 2), tokens_per_s=round(T / (us * 1e-6), 1), bytes=nbytes, flop=flop,
+                **_rate(us, nbytes, flop))
+
+
 def main():
     args = parse()
     if args.summarize_prof:
@@ -399,6 +502,9 @@ def main():
         "kernels": kernels,
     }
     result["conv1d"] = bench_conv(torch, gdn, T_e, ext.N, T_d, args.steps)
+    if not args.no_configs:
+        print("[bench] ragged, verify and delta-off workloads", file=sys.stderr, flush=True)
+        result["configs"] = bench_configs(torch, gdn, synth, args.steps)
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

@@ -181,7 +181,8 @@ int device_cus() {
 }
 
 // Segments per sequence for the chunk-128 delta-off kernel: the count (1..16) that
-// minimises the estimated makespan in chunk steps -- ceil(N H_v s / CUs) rounds of
+// minimises the estimated makespan in chunk steps -- ceil(N U s / CUs) rounds (U the
+// workgroups per sequence and segment, one per pair of heads) of
 // ceil(chunks / s) chunk steps for the full pass, plus for s > 1 the state-only pass
 // over all but the last segment (about a third of a full step per chunk) -- among
 // those whose workspace fits in `budget` bytes.  Unknown lengths (max_seqlen 0): one.
@@ -190,13 +191,15 @@ void ssd_plan(gdn::SeqLaunch& p, int max_seqlen, int64_t budget) {
   p.ssd_seg_chunks = 1 << 30;
   if (max_seqlen <= 0) return;
   const int nch = (max_seqlen + 127) / 128;
-  const double units = (double)p.N * p.H_v, cus = (double)device_cus();
+  const double units = (double)p.N * gdn::ssd_units_per_seq(p), cus = (double)device_cus();
   double best = 1e300;
   for (int s = 1; s <= 16 && s <= nch; ++s) {
     const int sc = (nch + s - 1) / s;
     const int se = (nch + sc - 1) / sc;           // segments that hold chunks
     if ((int64_t)p.N * se > 65535 || gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, se) > budget) break;
-    double cost = std::ceil(units * se / cus) * sc;
+    // (a segment's workgroup also folds the states of the segments before it: about a
+    // quarter of a chunk step per pair of them)
+    double cost = std::ceil(units * se / cus) * (sc + 0.125 * (se - 1));
     if (se > 1) cost += std::ceil(units * (se - 1) / cus) * sc * 0.35;
     if (cost < best * 0.98) {                     // (ties go to fewer segments)
       best = cost;

@@ -131,6 +131,7 @@ int chunked_obstacles(const SeqLaunch& p);
 // keeps it from this call (GDN_WHY_* bits), its workspace bytes for `segs` segments per
 // sequence, how a workspace is carved up, and the launch (prep, segment states, full pass).
 bool ssd_chunked_shape(const SeqLaunch& p);
+int ssd_units_per_seq(const SeqLaunch& p);
 int ssd_obstacles(const SeqLaunch& p);
 int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int segs);
 void ssd_bind_workspace(SeqLaunch& p, void* ws);
