@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
   extend               packed varlen extend over a pool   -> gdn_extend
   extend_kernel        which kernel an extend call takes  -> gdn_extend_kernel
   extend_workspace_size  delta-off chunk-128 workspace    -> gdn_extend_workspace_size
+  extend_noalloc       extend with the library's scratch  -> gdn_extend_noalloc
   decode               one token per sequence, in place   -> gdn_decode
   conv1d               short causal conv, varlen          -> gdn_conv1d
   conv1d_update        short causal conv, one token/row   -> gdn_conv1d_update
@@ -28,8 +29,8 @@ import torch
 from . import _lib
 from ._lib import GDN_BF16, GDN_F32, GDN_MODE_GDN, GDN_MODE_SSD, GDNError
 
-__all__ = ["load", "gate", "ssd_gate", "extend", "extend_kernel", "extend_workspace_size", "decode",
-           "conv1d", "conv1d_update", "validate_slots", "forward_gdn",
+__all__ = ["load", "gate", "ssd_gate", "extend", "extend_noalloc", "extend_kernel",
+           "extend_workspace_size", "decode", "conv1d", "conv1d_update", "validate_slots", "forward_gdn",
            "ssd_combined_fwd", "GDNError", "split_mixed_qkv"]
 
 
@@ -285,6 +286,28 @@ def extend(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None, scale
     else:
         _lib.check("gdn_extend_gated", lib.gdn_extend_gated(ct.byref(args), ct.byref(gate.args), _stream(dev)))
     del ws
+    return out
+
+
+def extend_noalloc(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, out, has_init=None, scale=None,
+                   max_seqlen: int = 0, mode: str = "gdn", D=None, z=None, chunk: int = 0,
+                   gate: GateInputs | None = None, ckpt_token=None, ckpt_slot=None, ckpt_states=None,
+                   ckpt_relative: bool = False, spec_states=None, spec_slot=None, spec_parent=None,
+                   keep_pool: bool = False):
+    """extend() for callers that cannot allocate (gdn_extend_noalloc): the caller passes
+    `out` ([T, H_v, d_v], bf16 or fp32), and the chunk-128 delta-off kernel's workspace
+    comes from the library's static per-device scratch.  Calls that overlap in time on one
+    device race on that scratch.  Returns out."""
+    if out is None:
+        raise ValueError("extend_noalloc writes into a caller-given out")
+    lib = _lib.load()
+    args, out, dev = _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, has_init=has_init,
+                                  scale=scale, out=out, max_seqlen=max_seqlen, mode=mode, D=D, z=z,
+                                  chunk=chunk, gate=gate, ckpt_token=ckpt_token, ckpt_slot=ckpt_slot,
+                                  ckpt_states=ckpt_states, ckpt_relative=ckpt_relative,
+                                  spec_states=spec_states, spec_slot=spec_slot,
+                                  spec_parent=spec_parent, keep_pool=keep_pool)
+    _lib.check("gdn_extend_noalloc", lib.gdn_extend_noalloc(ct.byref(args), _gate_ref(gate), _stream(dev)))
     return out
 
 

@@ -7,14 +7,15 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
-GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP = range(7)
+GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP, GDN_E_SCRATCH = range(8)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_status_str",
-            "gdn_last_hip_error", "gdn_abi_version", "gdn_extend_workspace_size", "gdn_extend_kernel"]
+            "gdn_last_hip_error", "gdn_abi_version", "gdn_extend_workspace_size", "gdn_extend_kernel",
+            "gdn_extend_noalloc"]
 
 # gdn_extend_kernel results and reason bits (include/gdn.h)
 GDN_KERNEL_RECURRENT, GDN_KERNEL_CHUNKED, GDN_KERNEL_SSD_CHUNKED = 1, 2, 3
@@ -101,6 +102,8 @@ def load(path: str | None = None) -> C.CDLL:
     lib.gdn_extend_workspace_size.restype = C.c_int64
     lib.gdn_extend_kernel.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.POINTER(C.c_int32)]
     lib.gdn_extend_kernel.restype = C.c_int
+    lib.gdn_extend_noalloc.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.c_void_p]
+    lib.gdn_extend_noalloc.restype = C.c_int
     lib.gdn_status_str.argtypes = [C.c_int]
     lib.gdn_status_str.restype = C.c_char_p
     lib.gdn_last_hip_error.argtypes = []
@@ -124,7 +127,7 @@ def check(fn: str, status: int) -> None:
     lib = load()
     msg = lib.gdn_status_str(status).decode()
     hip = lib.gdn_last_hip_error()
-    if status in (GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_NULL, GDN_E_UNSUPPORTED, GDN_E_INDEX):
+    if status in (GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_NULL, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_SCRATCH):
         err = ValueError(f"{fn} rejected its arguments: {msg} (status {status})")
         err.status = status
         raise err

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "gdn_launch.h"
 
@@ -90,6 +91,37 @@ int plan_extend(const gdn_extend_args* a, const gdn_gate_args* gate, gdn::SeqLau
 int extend_impl(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream);
 int decode_impl(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream);
 
+// Workspace of gdn_extend_noalloc, for callers that cannot allocate: one copy per
+// device, resolved on the first call on that device.  Host code never passes the
+// array's name to a kernel or copy (on the host it is only a stand-in for the
+// symbol): every use goes through the per-device address that scratch_address gives.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return GDN_E_UNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return GDN_E_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +139,7 @@ const char* gdn_status_str(int status) {
     case GDN_E_UNSUPPORTED: return "unsupported configuration";
     case GDN_E_INDEX: return "index argument out of range";
     case GDN_E_HIP: return "HIP runtime error";
+    case GDN_E_SCRATCH: return "input needs more than the static scratch of gdn_extend_noalloc";
     default: return "unknown status";
   }
 }
@@ -155,6 +188,27 @@ int64_t gdn_extend_workspace_size(const gdn_extend_args* a, const gdn_gate_args*
   probe.workspace_bytes = INT64_MAX;
   if (plan_extend(&probe, gate, p, w) != GDN_KERNEL_SSD_CHUNKED) return 0;
   return gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, p.ssd_segs);
+}
+int gdn_extend_noalloc(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
+  if (!a) return GDN_E_NULL;
+  if (a->workspace || a->workspace_bytes != 0) return GDN_E_SHAPE;   // the library supplies it
+  // the kernel the allocating entry point takes when given all the workspace it wants
+  gdn_extend_args b = *a;
+  b.workspace = reinterpret_cast<void*>(uintptr_t(256));
+  b.workspace_bytes = INT64_MAX;
+  gdn::SeqLaunch p{};
+  int why = 0;
+  const int k = plan_extend(&b, gate, p, why);
+  if (k <= 0) return -k;
+  if (k == GDN_KERNEL_SSD_CHUNKED &&
+      gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 1) > GDN_NOALLOC_SCRATCH_BYTES)
+    return GDN_E_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != GDN_OK) return st;
+  b.workspace = ws;
+  b.workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+  return extend_impl(&b, gate, stream);
 }
 int gdn_decode(const gdn_decode_args* a, void* stream) { return decode_impl(a, nullptr, stream); }
 int gdn_decode_gated(const gdn_decode_args* a, const gdn_gate_args* gate, void* stream) {

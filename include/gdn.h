@@ -17,9 +17,9 @@
  *
  * Conventions shared by every call
  *   - Every pointer in an args struct is DEVICE memory owned by the caller.  The
- *     library allocates nothing, keeps no state between calls and never
- *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
- *     legacy default stream) and the call returns at once.
+ *     library allocates nothing, keeps no state between calls (gdn_extend_noalloc's
+ *     static scratch aside) and never synchronises: work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the legacy default stream) and the call returns at once.
  *   - Strides and sizes are in elements, not bytes.  Within a token, heads are
  *     contiguous: element (t, head, i) of q is q[t * q_stride + head * d_k + i].
  *   - Rows are accessed 4 elements at a time: q, k, v, z and out must be aligned
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -54,7 +54,8 @@ typedef enum gdn_status {
   GDN_E_DTYPE = 3,       /* unsupported dtype combination                     */
   GDN_E_UNSUPPORTED = 4, /* valid request this build has no kernel for        */
   GDN_E_INDEX = 5,       /* index argument out of range (host-checkable ones) */
-  GDN_E_HIP = 6          /* the HIP runtime reported an error at launch        */
+  GDN_E_HIP = 6,         /* the HIP runtime reported an error at launch        */
+  GDN_E_SCRATCH = 7      /* gdn_extend_noalloc: needs more than its static scratch */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -298,6 +299,29 @@ int gdn_decode(const gdn_decode_args* args, void* stream);
  * ungated call. */
 int gdn_extend_gated(const gdn_extend_args* args, const gdn_gate_args* gate, void* stream);
 int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, void* stream);
+
+/* ---------------------------------------------------------------- extend without allocation
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  gdn_extend_gated (gate may be NULL:
+ * then gdn_extend) with the chunk-128 delta-off kernel's workspace taken from a static
+ * device array of the library, GDN_NOALLOC_SCRATCH_BYTES per device, instead of from
+ * args->workspace, which must be NULL with workspace_bytes 0 (else GDN_E_SHAPE).  The
+ * call allocates and frees nothing.
+ *   - A call whose chunk-128 kernel needs more than the array holds at one segment per
+ *     sequence (about T x H_qk > 131072 token-groups) returns GDN_E_SCRATCH and launches
+ *     nothing; gdn_extend_gated with a workspace of gdn_extend_workspace_size bytes
+ *     runs it.  A need between one segment's and gdn_extend_workspace_size's means
+ *     fewer segments per sequence (speed only).
+ *   - The first call on a device, with that device current, resolves the device's copy
+ *     of the array (a failure returns GDN_E_HIP); the copy stays allocated until the
+ *     process ends.
+ *   - Every call on one device shares its copy, which keeps the last call's contents:
+ *     calls that overlap in time on one device (two streams, two threads) race and give
+ *     undefined results, so the caller orders them.  No part of it needs to start at
+ *     zero: a call writes every byte it reads before reading it, in stream order.
+ * Every other argument, result and error as gdn_extend_gated. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int gdn_extend_noalloc(const gdn_extend_args* args, const gdn_gate_args* gate, void* stream);
 
 /* ---------------------------------------------------------------- short causal conv
  * The depthwise causal conv1d of width K (and SiLU) that turns the input projection

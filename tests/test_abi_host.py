@@ -219,6 +219,36 @@ def test_ssd_workspace_grows_with_segments_and_unknown_length_needs_one():
     assert lib.gdn_extend_workspace_size(ct.byref(a), None) > one
 
 
+def test_extend_noalloc_host_checks_come_before_any_device_call():
+    """gdn_extend_noalloc validates everything on the host before it touches a device:
+    the workspace fields are its own (a caller's workspace is refused), invalid
+    arguments fail as in gdn_extend, and a delta-off call whose chunk-128 kernel needs
+    more than the static scratch at one segment per sequence is refused."""
+    lib = gdn.load()
+    assert _lib.GDN_E_SCRATCH == 7
+    assert lib.gdn_extend_noalloc(None, None, None) == _lib.GDN_E_NULL
+    a = _ssd(workspace=ct.c_void_p(0x1000000), workspace_bytes=1 << 20)
+    assert lib.gdn_extend_noalloc(ct.byref(a), None, None) == _lib.GDN_E_SHAPE
+    a = _ssd(workspace_bytes=256)
+    assert lib.gdn_extend_noalloc(ct.byref(a), None, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_extend_noalloc(ct.byref(_ext(H_v=3)), None, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_extend_noalloc(ct.byref(_ext(N=0)), None, None) == _lib.GDN_OK   # nothing to do
+    limit = 64 << 20
+    # B and C copies: 2 x T x H_qk x 128 x 2 bytes at one segment
+    T = limit // (2 * 128 * 2) + 256
+    big = _ssd(T=T, max_seqlen=0, N=2)
+    assert lib.gdn_extend_workspace_size(ct.byref(big), None) > limit
+    assert lib.gdn_extend_noalloc(ct.byref(big), None, None) == _lib.GDN_E_SCRATCH
+    with pytest.raises(ValueError, match="static scratch"):
+        _lib.check("gdn_extend_noalloc", _lib.GDN_E_SCRATCH)
+    big.chunk = 128
+    assert lib.gdn_extend_noalloc(ct.byref(big), None, None) == _lib.GDN_E_SCRATCH
+    big.chunk, big.in_dtype, big.out_dtype = 0, 0, 0            # fp32: another kernel, no scratch
+    assert _kernel(big)[0] == _lib.GDN_KERNEL_RECURRENT
+    big.chunk = 128                                             # fp32 has no chunk-128 kernel
+    assert lib.gdn_extend_noalloc(ct.byref(big), None, None) == _lib.GDN_E_UNSUPPORTED
+
+
 def _conv(**kw):
     base = dict(dtype=1, K=4, activation=1, N=2, T=10, D=64, x=ct.c_void_p(0x10000), x_stride=64,
                 weight=ct.c_void_p(0x20000), cu_seqlens=FAKE, slot=FAKE, pool=ct.c_void_p(0x30000),
