@@ -19,7 +19,10 @@ summary under profiles/ when that summary was taken on the same kernel source.
 host's cores (one single-threaded worker process per unit; the one-thread rate beside
 it).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline]
+
+Before the W warm-up steps the step runs back to back for --settle-ms (default 250
+ms, untimed): the GPU's clocks ramp up over the first ~50 ms of sustained load.
        python bench.py --summarize-prof KT_DIR FETCH_DIR WRITE_DIR   (writes profiles/)
 """
 import argparse
@@ -48,28 +51,39 @@ EXTEND_FLOP_PER_TOKEN = H_QK * 4 * CHUNK * D + H_V * 2 * (CHUNK * D + 2 * CHUNK 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_traffic.txt")
 KERNEL_SOURCES = {"extend": "hybrid_model_linear_amd/csrc/chunk.hip",
+                  "ssd": "hybrid_model_linear_amd/csrc/ssd.hip",
                   "decode": "hybrid_model_linear_amd/csrc/recurrent.hip",
                   "conv_prefill": "hybrid_model_linear_amd/csrc/conv.hip"}
 KERNEL_NAMES = {"extend": "chunk_kernel<128, 128, false, unsigned short",
                 "decode": "recurrent_kernel<128, 128, unsigned short",
                 "conv_prefill": "conv_out_kernel<4, true>"}
-PROF_CMD = "python bench.py --steps 20 --warmup 1000 --no-cpu-baseline --calibrate-copy-mib 1024"
-PMC_CMD = "python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy-mib 1024"
+PROF_CMD = "python bench.py --steps 20 --warmup 20 --no-cpu-baseline --no-configs --calibrate-copy-mib 1024"
+PMC_CMD = "python bench.py --steps 5 --warmup 2 --settle-ms 0 --no-cpu-baseline --no-configs --calibrate-copy-mib 1024"
+CONFIGS_PROF_CMD = "python bench.py --steps 20 --no-cpu-baseline --configs-only"
+CONFIGS_STATS_FILE = os.path.join(PROFILES, "gdn_ragged_verify_ssd128_kernel_stats.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # ~0.6 s of warm-up: the GPU's clocks settle before the timed region
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    # The GPU's clocks ramp up over the first ~50 ms of sustained load (the extend
+    # kernel's time falls from ~360 to ~265 us per call): before the warm-up steps, the
+    # step runs back to back for this long, untimed, so that the timed steps see the
+    # sustained clock that a serving loop runs at.
+    ap.add_argument("--settle-ms", type=float, default=250.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the ragged, verify and delta-off workloads")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter scaling)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="time only the ragged, verify and delta-off workloads")
     ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 outputs of this script into profiles/ and exit")
+    ap.add_argument("--summarize-configs-prof", metavar="KT_DIR",
+                    help="summarize a kernel trace of the --configs-only command into profiles/ and exit")
     return ap.parse_args()
 
 
@@ -87,22 +101,36 @@ def _csv_rows(d, pattern):
         return list(csv.DictReader(f))
 
 
+def _stats_lines(kt_dir, cmd):
+    lines = [f"# command (repository root): export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             f"-d <dir> -o bench -- {cmd}",
+             f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}, "
+             f"ssd.hip sha256 {source_sha('ssd')}, conv.hip sha256 {source_sha('conv_prefill')}",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in _csv_rows(kt_dir, "*kernel_stats.csv"):
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    return lines
+
+
+def summarize_configs_prof(kt_dir):
+    """profiles/ summary of a kernel trace of CONFIGS_PROF_CMD: per-kernel statistics of the
+    ragged extend, its verify batch and the delta-off chunk-128 call."""
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = ["# rocprofv3 kernel-trace statistics of the ragged, verify and delta-off workloads",
+             "# summarized by: python bench.py --summarize-configs-prof <kt_dir>"] + _stats_lines(kt_dir, CONFIGS_PROF_CMD)
+    with open(CONFIGS_STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_prof(kt_dir, fetch_dir, write_dir):
     """profiles/ text summaries of three rocprofv3 runs of PROF_CMD: the kernel-trace
     statistics, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same
     counters read for the 1 GiB copy kernel (torch.mul: reads and writes 1 GiB)."""
     os.makedirs(PROFILES, exist_ok=True)
-    stats = _csv_rows(kt_dir, "*kernel_stats.csv")
     lines = ["# rocprofv3 kernel-trace statistics of the bench command",
-             f"# command (repository root): export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             f"-d <dir> -o bench -- {PROF_CMD}",
-             f"# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>",
-             f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}, "
-             f"conv.hip sha256 {source_sha('conv_prefill')}",
-             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
-    for r in stats:
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
-                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+             "# summarized by: python bench.py --summarize-prof <kt_dir> <fetch_dir> <write_dir>"] + _stats_lines(kt_dir, PROF_CMD)
     with open(os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -281,11 +309,16 @@ def _rate(us, nbytes, flop):
             "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def _time_calls(torch, fn, steps, warm=10):
+def _time_calls(torch, fn, steps, warm=10, settle_ms=100.0):
     """Average microseconds per call of fn over `steps` back-to-back calls, from HIP events
-    recorded on torch's current stream (the stream the calls launch on)."""
-    for _ in range(warm):
+    recorded on torch's current stream (the stream the calls launch on), after at least
+    `warm` calls and `settle_ms` of back-to-back calls (clocks settled)."""
+    n, t0 = 0, time.time()
+    while n < warm or (time.time() - t0) * 1e3 < settle_ms:
         fn()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -380,6 +413,9 @@ def main():
     if args.summarize_prof:
         summarize_prof(*args.summarize_prof)
         return
+    if args.summarize_configs_prof:
+        summarize_configs_prof(args.summarize_configs_prof)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer needs no collective; heads and "
               f"sequences shard independently); --gpus {args.gpus} is not supported",
@@ -397,6 +433,9 @@ def main():
     gdn.load()
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.configs_only:
+        print(json.dumps({"configs": bench_configs(torch, gdn, synth, args.steps)}), flush=True)
+        return
     # ---------------- inputs (resident in HBM before timing)
     ext = synth.device_config2_prefill()
     dec = synth.device_config1_decode()
@@ -440,10 +479,18 @@ def main():
                    scale=dec.scale, out=Dd["out"], gate=gate_d)
         mark(2)
 
+    settle_steps, t0 = 0, time.time()
+    while (time.time() - t0) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    settle_ms = (time.time() - t0) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] clocks settled ({settle_steps} steps, {settle_ms:.0f} ms); warmup done "
+          f"({args.warmup} steps)", file=sys.stderr, flush=True)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -490,6 +537,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "GDN layer step: extend 8x4096 (zero init) + decode 256x1 "

@@ -15,10 +15,12 @@
 // Delta-off mode (Mamba2 SSD, flashinfer.mamba.ssd_combined_fwd): no norms, T = I,
 // U = diag(dt') X, scale 1, then O += D x and O *= silu(z).
 //
-// Precision.  bf16 output: the state waves take Q^ = diag(CO) Q and K^ = diag(r_k) K,
-// S0, P, U and the scaled U of the state update as single fp16 operands (each bounded
-// by construction or by the values; fp16's 11-bit significand keeps every product's
-// rounding below the output's bf16 rounding).  fp32 output and the delta-off mode:
+// Precision.  bf16 output: q and k land in LDS normalised, Q^ = diag(r_q) Q and
+// K^ = diag(r_k) K in fp16, and every product takes them, S0, P, U and the scaled U
+// of the state update as single fp16 operands (each bounded by construction or by
+// the values; fp16's 11-bit significand keeps every product's rounding below the
+// output's bf16 rounding, and the Gram tiles' below the bf16 rounding of T).  fp32
+// output and the delta-off mode:
 // q, k, v enter the MFMAs as their exact bf16 values, norms, beta and decays are fp32
 // scalings around the products, S0 is a single bf16 operand and P U and the state
 // update use two-term (hi + lo) bf16 splits.  T and the correction operand bf16(R)
@@ -34,11 +36,11 @@
 //    reads from LDS).  In the step for chunk c they compute X, Y, R, U, O and the new
 //    state: only the state-dependent part, with no barrier inside.
 //  * four producer waves run meanwhile on chunk c + 1: the Q K^T and K K^T tiles,
-//    row norms, decay cumsum and the per-token coefficient vectors, P and A, the
-//    diagonal blocks of T = (I + A)^{-1}, the in-place fp16 conversion of Q and K;
-//    and, early in step c, the merges that finish chunk c's T.
+//    decay cumsum and the per-token coefficient vectors, P and A, the diagonal
+//    blocks of T = (I + A)^{-1}; and, early in step c, the merges that finish chunk
+//    c's T.
 // The raw rows of q, k, v (z) are staged from HBM through registers into LDS one
-// step ahead.
+// step ahead; the row norms of q and k are taken from the registers as they land.
 // Each step has one workgroup barrier, which ends the previous step; the landing of
 // the staged rows that follows, like every other hand-off, is announced on an LDS
 // arrival counter, so the state waves start on chunk c (its Q and K landed a step
@@ -73,7 +75,7 @@ __device__ __forceinline__ int kperm(int c) {
 }
 
 // ------------------------------------------------------------------ chunk staging
-// The waves of a workgroup (NST threads, staging index si) load a chunk's q, k, v
+// The waves of one role (NST threads, staging index si) load a chunk's q, k or v
 // (and z) rows into registers one step before they store them into LDS, so the HBM
 // latency hides behind a whole step.  Consecutive threads read consecutive 16-byte
 // segments of a row (coalesced); rows past the sequence end re-read row t0 (always
@@ -83,21 +85,23 @@ struct TileRegs {
   static constexpr int NSEG = D / 8;                  // 16-byte segments per row
   static constexpr int N = 64 * NSEG / NST;           // segments per thread
   static_assert(N * NST == 64 * NSEG && (N == 1 || N == 2 || N == 4), "segments split evenly");
-  uint4 s0, s1, s2, s3;                               // named registers, no array (kept out of scratch)
+  // named registers, no array, and native vectors rather than uint4 structs (whose
+  // copies can go through scratch)
+  u32x4 s0, s1, s2, s3;
   // (a uniform base at row t0 plus a 32-bit lane offset: the scalar-base address form)
-  __device__ __forceinline__ static uint4 ld(const u16* g, int64_t gs, int t0, int n, int si, int i) {
+  __device__ __forceinline__ static u32x4 ld(const u16* g, int64_t gs, int t0, int n, int si, int i) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     const char* base = reinterpret_cast<const char*>(g + (int64_t)t0 * gs);
     const uint32_t off = ((uint32_t)(r < n ? r : 0) * (uint32_t)gs + 8u * (uint32_t)c) * 2u;
-    return *reinterpret_cast<const uint4*>(base + off);
+    return *reinterpret_cast<const u32x4*>(base + off);
   }
   template <bool kSwz>
-  __device__ __forceinline__ static void st(u16* tile, int si, int i, uint4 v) {
+  __device__ __forceinline__ static void st(u16* tile, int si, int i, u32x4 v) {
     const int sidx = si + i * NST, r = sidx / NSEG, c = sidx % NSEG;
     if constexpr (kSwz) {   // Q and K tiles: unpadded rows, swizzled 16-byte chunks
-      *reinterpret_cast<uint4*>(tile + qidx<D>(r, 8 * c)) = v;
+      *reinterpret_cast<u32x4*>(tile + qidx<D>(r, 8 * c)) = v;
     } else {
-      *reinterpret_cast<uint4*>(tile + r * (D + 8) + 8 * c) = v;
+      *reinterpret_cast<u32x4*>(tile + r * (D + 8) + 8 * c) = v;
     }
   }
   __device__ __forceinline__ void load(const u16* g, int64_t gs, int t0, int n, int si) {
@@ -107,6 +111,19 @@ struct TileRegs {
       s2 = ld(g, gs, t0, n, si, 2);
       s3 = ld(g, gs, t0, n, si, 3);
     }
+  }
+  // 1 / sqrt(|row|^2 + 1e-6) of the row that segment v (staging slot i) belongs to, 0
+  // for rows >= n.  The 16 segments of a row (D = 128) are held by 16 consecutive lanes,
+  // so its squared norm is a sum over a row of 16 lanes.
+  __device__ __forceinline__ static float rnorm(u32x4 v, int si, int i, int n) {
+    static_assert(NSEG == 16 && NST % 16 == 0, "a row's segments in one row of 16 lanes");
+    const float a = row16_sum(dot2sq(v[3], dot2sq(v[2], dot2sq(v[1], dot2sq(v[0], 0.f)))));
+    return (si + i * NST) / NSEG < n ? __builtin_amdgcn_rsqf(a + 1e-6f) : 0.f;   // 1 ulp
+  }
+  // the 8 bf16 of v times f, as fp16
+  __device__ __forceinline__ static u32x4 scale_h(u32x4 v, float f) {
+    return u32x4{cvt2h(bf_lo(v[0]) * f, bf_hi(v[0]) * f), cvt2h(bf_lo(v[1]) * f, bf_hi(v[1]) * f),
+                 cvt2h(bf_lo(v[2]) * f, bf_hi(v[2]) * f), cvt2h(bf_lo(v[3]) * f, bf_hi(v[3]) * f)};
   }
   template <bool kPerm>   // Q and K tiles: permuted column groups, swizzled chunks
   __device__ __forceinline__ void store(u16* tile, int si) const {
@@ -127,13 +144,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   constexpr int NKS = DK / 32;     // 32-wide k-steps over d_k
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
-  // fp16 operands (GDN with bf16 output): the state waves take Q^ = diag(CO) Q and
-  // K^ = diag(r_k) K (converted in place by the producers, one step ahead), S0, the
-  // scaled U of the state update and P U as single fp16 operands.  Every operand is
-  // bounded by construction or by the values (|K^| <= 1, |P| <= scale, decays <= 1),
-  // and fp16's 11-bit significand keeps each product's error well below the output's
-  // bf16 rounding.  fp32 output and the delta-off mode keep raw bf16 Q, K with bf16
-  // S0 and two-term bf16 splits.
+  // fp16 operands (GDN with bf16 output): Q^ = diag(r_q) Q and K^ = diag(r_k) K land
+  // in fp16 (normalised as they land), and the products take them, S0, the scaled U
+  // of the state update and P U as single fp16 operands.  Every operand is bounded by
+  // construction or by the values (|Q^|, |K^| <= 1, |P| <= scale, decays <= 1), and
+  // fp16's 11-bit significand keeps each product's error well below the output's bf16
+  // rounding.  fp32 output and the delta-off mode keep raw bf16 Q, K with bf16 S0 and
+  // two-term bf16 splits.
   constexpr bool kF16 = !kSSD && sizeof(OutT) == 2;
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
@@ -145,7 +162,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) u16 sTb[kSSD ? 1 : 2][C][kPS];
   __shared__ __attribute__((aligned(16))) float sCR[2][C], sCO[2][C], sCS[2][C], sBeta[2][C], sGC[2][4];
   __shared__ __attribute__((aligned(16))) float sGr[2][C], sBr[2][C];    // raw log g, beta (staged)
-  __shared__ __attribute__((aligned(16))) float sRk[2][C];   // r_k (fp16 operands, checkpoints)
+  // 1 / |q_i|, 1 / |k_i| from the landing (raw bf16 operands only: the fp16 operands
+  // land normalised)
+  __shared__ __attribute__((aligned(16))) float sRq[kF16 ? 1 : 2][kF16 ? 1 : C], sRk[kF16 ? 1 : 2][kF16 ? 1 : C];
   __shared__ __attribute__((aligned(16))) float sGc[2][C];   // G_i, the in-chunk decay cumsum (checkpoints)
   // producer working set (per producer wave where private)
   // fp32 diagonal 16x16 blocks of A, rows of 20 floats, double-buffered; the block
@@ -154,18 +173,37 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   __shared__ __attribute__((aligned(16))) float sAd[kSSD ? 1 : 2][4][16 * 20 + 16];
   // vectors of the chunk being prepared, per token (see the producer roles)
   __shared__ __attribute__((aligned(16))) float sEG[C], sEB[C], sERp[C], sERa[C], sEF[C], sEFa[C];
-  __shared__ __attribute__((aligned(16))) float sNq[C], sNk[C];   // squared row norms of q, k
-  // arrival counters: chunk vectors ready, T ready, raw Q/K read, landing done; and
+  // arrival counters: chunk vectors ready (0), T ready (1), state waves' landing
+  // done (2), producers' landing done (3); and
   // (entry kFailFlag) the flag of a bounded wait that ran out
   __shared__ uint32_t sSync[8];
   constexpr int kFailFlag = 7;
 
-  const int h = blockIdx.x;
-  // Workgroups are dispatched sequence by sequence.  With lpt set, blockIdx.y is a
-  // rank in descending length (ties by index), so the longest sequences start first
-  // and a ragged batch ends without a long tail (longest-processing-time first).
-  // Thread m ranks sequence m in O(N); the host sets lpt only for small N.
-  int nseq = blockIdx.y;
+  // Work item (v-head h, sequence position yr).  Workgroups go to the 8 XCDs in turn
+  // (linear id % 8), each XCD with its own L2, and the r = H_v / H_qk v-heads of a
+  // qk-head read the same q, k rows: they take the linear ids i, i + 8, .., i + 8 (r - 1)
+  // -- one XCD, dispatched together, so all but one read q, k from that XCD's L2.
+  // (With (sequences x qk-heads) not a multiple of 8, the plain order is kept.)
+  int h, yr;
+  {
+    const int r = p.H_v / p.H_qk;
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    if ((gridDim.y * p.H_qk) % 8 == 0) {
+      const int blk = lin / (8 * r), o = lin % (8 * r);
+      const int u = 8 * blk + (o & 7);             // (sequence position, qk-head) unit
+      yr = u / p.H_qk;
+      h = (u % p.H_qk) * r + (o >> 3);
+    } else {
+      h = blockIdx.x;
+      yr = blockIdx.y;
+    }
+  }
+  // Workgroups are dispatched sequence by sequence.  With lpt set, the sequence
+  // position yr is a rank in descending length (ties by index), so the longest
+  // sequences start first and a ragged batch ends without a long tail (longest-
+  // processing-time first).  Thread m ranks sequence m in O(N); the host sets lpt only
+  // for small N.
+  int nseq = yr;
   if (p.lpt) {
     __shared__ int sSel;
     const int m = threadIdx.x;
@@ -176,7 +214,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         const int lq = p.cu_seqlens[q + 1] - p.cu_seqlens[q];
         rank += (lq > lm) | ((lq == lm) & (q < m));
       }
-      if (rank == (int)blockIdx.y) sSel = m;
+      if (rank == yr) sSel = m;
     }
     __syncthreads();
     nseq = __builtin_amdgcn_readfirstlane(sSel);
@@ -276,20 +314,22 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   }
 
   // ================================================================ staging
-  // Every wave stages an equal share of the raw rows: Q, K of chunk c + 2 and V (z)
-  // of chunk c + 1 are in flight in registers during step c (producers issue them
-  // right after the landing, state waves in the middle of their step).  Every wave
-  // lands its share right after the step's barrier and announces it on an arrival
-  // counter; the producers wait for the whole landing before their first products,
-  // the state waves only before they first read V.
-  constexpr int NST = (NSW + kNP) * kWave;
-  const int si = tid;                         // staging index
-  TileRegs<DK, NST> rq_, rk_;
-  TileRegs<DV, NST> rv_, rz_;                 // (z: delta-off only)
+  // Each role stages the raw rows it consumes: the producers Q, K (and the gate
+  // inputs) of chunk c + 2, issued right after the landing of step c; the state waves
+  // V (z) of chunk c + 1, issued in the middle of their step.  Both stay in flight in
+  // registers during step c.  Each role lands its rows right after the step's barrier
+  // and announces them on its own arrival counter, so neither waits for the other's
+  // landing: the producers wait for theirs before their first products, the state
+  // waves for theirs before they first read V.
+  constexpr int NSTQ = kNP * kWave, NSTV = NSW * kWave;
+  const int siq = tid - NSW * kWave;          // staging index of a producer thread
+  const int siv = tid;                        // staging index of a state-wave thread
+  TileRegs<DK, NSTQ> rq_, rk_;                // (producers)
+  TileRegs<DV, NSTV> rv_, rz_;                // (state waves; z: delta-off only)
   float rg_ = 0.f, rb_ = 0.f;                 // log g, beta of chunk c + 2 (lane = token), for the producers
   // (gate folded in: the aligned 32-bit words holding the raw bf16 a, b / dt, kept
   // exactly as loaded -- any instruction on the loaded value, even a zero-extension
-  // of a 16-bit load, would make every wave wait for these loads at the step's end)
+  // of a 16-bit load, would make the producers wait for these loads at the step's end)
   uint32_t ra_ = 0u, rbr_ = 0u;
   // Gate folded in: producer 2, idle once T is done, turns its staged raw inputs of
   // chunk c + 2 into log g, beta at the end of step c and stores them at once into the
@@ -310,10 +350,49 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sBr[par][lane] = bt;
     }
   };
+  // Landing of a chunk's Q and K rows (delta rule; n rows in the sequence): every
+  // thread holds two 16-byte segments of each, of rows r and r + 32, and takes their
+  // row norms from the staged values.  fp16 operands: the rows land normalised,
+  // q / |q| and k / |k| (|entries| <= 1) in fp16, zero past the end; raw bf16
+  // operands: the rows land as they are and 1 / |row| goes to sRq, sRk.
+  auto land_qk = [&](auto parq, int n) __attribute__((always_inline)) {
+    constexpr int PQ = decltype(parq)::value;
+    using Reg = TileRegs<DK, NSTQ>;
+    static_assert(Reg::N == 4, "four segments of each tile per thread");
+    constexpr int RS = NSTQ / Reg::NSEG;      // rows between a thread's segments
+    const float q0 = Reg::rnorm(rq_.s0, siq, 0, n), q1 = Reg::rnorm(rq_.s1, siq, 1, n);
+    const float q2 = Reg::rnorm(rq_.s2, siq, 2, n), q3 = Reg::rnorm(rq_.s3, siq, 3, n);
+    const float k0 = Reg::rnorm(rk_.s0, siq, 0, n), k1 = Reg::rnorm(rk_.s1, siq, 1, n);
+    const float k2 = Reg::rnorm(rk_.s2, siq, 2, n), k3 = Reg::rnorm(rk_.s3, siq, 3, n);
+    if constexpr (kF16) {
+      Reg::template st<true>(sQ[PQ], siq, 0, Reg::scale_h(rq_.s0, q0));
+      Reg::template st<true>(sQ[PQ], siq, 1, Reg::scale_h(rq_.s1, q1));
+      Reg::template st<true>(sQ[PQ], siq, 2, Reg::scale_h(rq_.s2, q2));
+      Reg::template st<true>(sQ[PQ], siq, 3, Reg::scale_h(rq_.s3, q3));
+      Reg::template st<true>(sK[PQ], siq, 0, Reg::scale_h(rk_.s0, k0));
+      Reg::template st<true>(sK[PQ], siq, 1, Reg::scale_h(rk_.s1, k1));
+      Reg::template st<true>(sK[PQ], siq, 2, Reg::scale_h(rk_.s2, k2));
+      Reg::template st<true>(sK[PQ], siq, 3, Reg::scale_h(rk_.s3, k3));
+    } else {
+      rq_.template store<true>(sQ[PQ], siq);
+      rk_.template store<true>(sK[PQ], siq);
+      if ((siq & 15) == 0) {
+        const int r = siq / Reg::NSEG;
+        sRq[PQ][r] = q0;
+        sRq[PQ][r + RS] = q1;
+        sRq[PQ][r + 2 * RS] = q2;
+        sRq[PQ][r + 3 * RS] = q3;
+        sRk[PQ][r] = k0;
+        sRk[PQ][r + RS] = k1;
+        sRk[PQ][r + 2 * RS] = k2;
+        sRk[PQ][r + 3 * RS] = k3;
+      }
+    }
+  };
   auto stage_qk = [&](int cc) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
-    rq_.load(qg, p.q_stride, t0, n, si);
-    rk_.load(kg, p.k_stride, t0, n, si);
+    rq_.load(qg, p.q_stride, t0, n, siq);
+    rk_.load(kg, p.k_stride, t0, n, siq);
     const int64_t tt = (int64_t)(t0 + (lane < n ? lane : 0));
     if constexpr (kGate) {   // raw gate inputs (bf16)
       ra_ = reinterpret_cast<const uint32_t*>(p.ga)[tt * (p.ga_stride >> 1) + (h >> 1)];
@@ -325,8 +404,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   };
   auto stage_v = [&](int cc) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * C, n = min(C, tend - t0);
-    rv_.load(vg, p.v_stride, t0, n, si);
-    if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, si);
+    rv_.load(vg, p.v_stride, t0, n, siv);
+    if constexpr (kSSD) rz_.load(zg, z_stride, t0, n, siv);
   };
 
   // Hand-off between waves inside a step: arrival counters in LDS.  A wave's LDS
@@ -375,7 +454,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     // token 16 rt + j16), from the same operands with A and B swapped, so that a lane
     // holds 4 consecutive output columns of one token (8-byte stores).
     f32x4 Y[CT][4], U[CT][4];
-    if constexpr (kF16) {   // Y = Q^ S0^T (CO folded in), X = K^ S0^T (r_k folded in)
+    if constexpr (kF16) {   // Y = Q^ S0^T, X = K^ S0^T (Q^, K^ the normalised rows)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -427,12 +506,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
     }
-    // This wave's share of the next staged rows (Q, K of chunk c + 2, V of c + 1):
-    // issued before this step's output stores, so that the next landing's wait for
-    // these loads never includes the stores (the memory counter retires in order).
-    stage_qk(min(c + 2, nch - 1));
+    // This wave's share of the next staged rows (V, z of chunk c + 1): issued before
+    // this step's output stores, so that the next landing's wait for these loads never
+    // includes the stores (the memory counter retires in order).
     stage_v(min(c + 1, nch - 1));
-    wait_count(&sSync[3], 8u * (uint32_t)(c + 2));   // this step's landing (V of chunk c) done
+    wait_count(&sSync[2], (uint32_t)NSW * (uint32_t)(c + 2));   // this step's landing (V of chunk c) done
     // R = beta V - CR X (GDN); U = beta V (delta-off).  V through transpose reads.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -481,7 +559,10 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) Uf[ct][s2] = pair_to_op_h(U[ct][2 * s2], U[ct][2 * s2 + 1]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {   // (CO is folded into Q^)
+      for (int rt = 0; rt < 4; ++rt) {
+        const float co = sCO[PAR][16 * rt + j16];    // this lane's token
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Y[ct][rt] *= co;
         const u16* prow = &sPh[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
         for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
@@ -577,7 +658,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * rt + 4 * g16 + e;
-          cf[rt][e] = i < m ? __expf(Gm - sGc[PAR][i]) * (kF16 ? 1.f : sRk[PAR][i]) : 0.f;
+          float rk = 1.f;
+          if constexpr (!kF16) rk = sRk[PAR][i];
+          cf[rt][e] = i < m ? __expf(Gm - sGc[PAR][i]) * rk : 0.f;
         }
       const int rb = 4 * g16 + (j16 >> 2);
 #pragma unroll
@@ -636,7 +719,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       // state's row order; a transpose read may take its four 4-column chunks from
       // anywhere); k slots: tokens 32 s2 + 4 g16 + e and 32 s2 + 16 + 4 g16 + e
       const int rb = 4 * g16 + (j16 >> 2);
-      if constexpr (kF16) {   // K^^T (r_k folded in) times the scaled U, fp16
+      if constexpr (kF16) {   // K^^T (normalised rows) times the scaled U, fp16
         f16x8 Wf[CT][2];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -689,8 +772,15 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
     for (int s = 0; s < DK / 16; ++s) {                        // 16-wide k-steps (32x32x16)
       const bf16x8 a = ldq8<DK>(K, 32 * tj + l32, 16 * s + 8 * hh);
-      qk = mfma32(a, ldq8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh), qk);
-      if constexpr (!kSSD) kk = mfma32(a, ldq8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
+      const bf16x8 bq = ldq8<DK>(Q, 32 * ti + l32, 16 * s + 8 * hh);
+      if constexpr (kF16) {   // normalised fp16 rows
+        const f16x8 ah = __builtin_bit_cast(f16x8, a);
+        qk = mfma32h(ah, __builtin_bit_cast(f16x8, bq), qk);
+        kk = mfma32h(ah, __builtin_bit_cast(f16x8, ldq8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh)), kk);
+      } else {
+        qk = mfma32(a, bq, qk);
+        if constexpr (!kSSD) kk = mfma32(a, ldq8<DK>(K, 32 * ti + l32, 16 * s + 8 * hh), kk);
+      }
     }
   };
   uint32_t pgen = 0;                          // chunks prepared so far (uniform)
@@ -706,13 +796,35 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     asm volatile("" : "+v"(lane_o));
     lds_order();
     const int b = 2 * t + ((lane_o >> 4) & 1), c = lane_o & 15;   // (the upper half-wave repeats the lower)
+    // The block's entries below the diagonal, row by row in 16-byte pieces, all read
+    // up front (no wait for a read between the products), then forward substitution:
+    // x_m = [m == c] - sum_{i < m} A_mi x_i.
+    const float* Ab = sAd[PQ][b];
+    float4 ar[36];
+    {
+      int k = 0;
+#pragma unroll
+      for (int mm = 1; mm < 16; ++mm)
+#pragma unroll
+        for (int q = 0; 4 * q < mm; ++q) ar[k++] = ld_f4(&Ab[20 * mm + 4 * q]);
+    }
     float x[16];
+    x[0] = c == 0 ? 1.f : 0.f;
+    {
+      int k = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+      for (int mm = 1; mm < 16; ++mm) {
+        float acc = mm == c ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+        for (int q = 0; 4 * q < mm; ++q) {
+          const float4 a4 = ar[k++];
 #pragma unroll
-      for (int mm = i + 1; mm < 16; ++mm) x[mm] -= sAd[PQ][b][20 * mm + i] * x[i];
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e < mm) acc -= f4get(a4, e) * x[4 * q + e];
+        }
+        x[mm] = acc;
+      }
+    }
     if (lane_o < 32) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
@@ -721,19 +833,14 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   // Prepare chunk cp (buffers of parity PQ): its vectors, P (fp16, or bf16 hi + lo), and A stored in
   // T's buffer (bf16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
   // (pr = wave - NSW):
-  //   pr 3:    the off-diagonal tile's products, then the chunk's vectors (lane =
-  //            token): decay cumsum, row norms (from the squared norms that pr 0, 1
-  //            provide), the coefficient vectors and the decay
-  //            factors of the tiles; then the off-diagonal tile (rows 32..63, keys
-  //            0..31), whose decay factors into a row and a key factor split at token
-  //            31 (both <= 1);
-  //   pr 0, 1: diagonal tile t = pr: the squared norms of its 32 rows of q and k, its
-  //            products, then P and A (one exp per element) and the two diagonal
-  //            16x16 blocks of T = (I + A)^{-1} inside it.
-  // Every Gram-tile producer announces on an arrival counter when it has read the raw
-  // Q, K of the chunk (for their in-place fp16 conversion).  Entries of A on and above
-  // the diagonal are not needed; those inside the diagonal 32x32 tiles come out as
-  // zeros or are overwritten by T's diagonal blocks.
+  //   pr 3:    the chunk's vectors (lane = token): decay cumsum, the coefficient
+  //            vectors (with the row norms from the landing) and the decay factors of
+  //            the tiles; then the off-diagonal tile (rows 32..63, keys 0..31), whose
+  //            decay factors into a row and a key factor split at token 31 (both <= 1);
+  //   pr 0, 1: diagonal tile t = pr: its products, then P and A (one exp per
+  //            element) and the two diagonal 16x16 blocks of T = (I + A)^{-1} inside it.
+  // Entries of A on and above the diagonal are not needed; those inside the diagonal
+  // 32x32 tiles come out as zeros or are overwritten by T's diagonal blocks.
   auto produce = [&](int cp, auto parq) __attribute__((always_inline)) {
     constexpr int PQ = decltype(parq)::value;
     const int t0 = tbeg + cp * C, n = min(C, tend - t0);
@@ -753,10 +860,22 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       const float gi = kDiag ? sEG[i] : 0.f;
       const float rowP = kDiag ? sERp[i] : sEF[i];
       const float rowA = kDiag ? sERa[i] : sEFa[i];
+      // every key factor is read before the first store (LDS accesses complete in
+      // order: a read after the stores would wait for them)
+      float4 kmv[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int mb = 32 * tj + 8 * q4 + 4 * hh;
+        kmv[q4] = ld_f4(kDiag ? &sEB[mb] : &sEF[mb]);
+      }
+      // A's entries inside the diagonal 16x16 blocks: keys 16 (l32 / 16) + 4 hh + 0..3
+      // (q4 = 2 (l32 / 16)) and + 8 (q4 + 1) of this lane's row
+      f32x4 ad0 = {}, ad1 = {};   // (native vectors: selects of float4 structs go through scratch)
+      const bool upper = l32 >= 16;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int mb = 32 * tj + 8 * q4 + 4 * hh;                 // keys mb .. mb + 3
-        const float4 km = ld_f4(kDiag ? &sEB[mb] : &sEF[mb]);
+        const float4 km = kmv[q4];
         float pv[4], av[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -778,40 +897,51 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
         if constexpr (!kSSD) {
           *reinterpret_cast<uint2*>(&sTb[PQ][i][kperm(mb)]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
-          if (kDiag && (i >> 4) == (mb >> 4))
-            *reinterpret_cast<float4*>(&sAd[PQ][i >> 4][20 * (i & 15) + (mb & 15)]) = make_float4(av[0], av[1], av[2], av[3]);
+          if constexpr (kDiag) {
+            const f32x4 a4 = {av[0], av[1], av[2], av[3]};
+            if (q4 == 0) ad0 = a4;
+            if (q4 == 1) ad1 = a4;
+            if (q4 == 2) ad0 = upper ? a4 : ad0;
+            if (q4 == 3) ad1 = upper ? a4 : ad1;
+          }
         }
+      }
+      if constexpr (kDiag && !kSSD) {   // (branch-free: both stores from every lane)
+        float* arow = &sAd[PQ][i >> 4][20 * (i & 15) + 4 * hh];
+        *reinterpret_cast<f32x4*>(arow) = ad0;
+        *reinterpret_cast<f32x4*>(arow + 8) = ad1;
       }
     };
 
     f32x16 qk, kk;
     if (pr == 3) {
-      tile_mma(Q, K, 1, 0, l32, hh, qk, kk);   // (runs on the matrix cores while the vectors are computed)
       // cumulative decay within the chunk (padded tokens: log g = 0, beta = 0)
       const int i = lane_o;
       const float bt = i < n ? sBr[PQ][i] : 0.f;
       const float G = wave_inclusive_scan(i < n ? sGr[PQ][i] : 0.f);
       const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
       const float G31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 31));
-      float rq = i < n ? 1.f : 0.f, rk = rq;
-      if constexpr (!kSSD) {   // 1 / |row| of q_i and k_i (zero past the end), from the squared norms
-        wait_count(&sSync[4], 2u * (uint32_t)(cp + 1));
-        rq = i < n ? __builtin_amdgcn_rsqf(sNq[i] + 1e-6f) : 0.f;   // 1 ulp
-        rk = i < n ? __builtin_amdgcn_rsqf(sNk[i] + 1e-6f) : 0.f;
+      // 1 / |row| of q_i and k_i: from the landing (raw bf16 rows, zero past the end);
+      // 1 with the fp16 operands, which land normalised (zero rows past the end); the
+      // delta-off mode has no norms (zero past the end)
+      float rq = 1.f, rk = 1.f;
+      if constexpr (kSSD) {
+        rq = rk = i < n ? 1.f : 0.f;
+      } else if constexpr (!kF16) {
+        rq = sRq[PQ][i];
+        rk = sRk[PQ][i];
       }
       const float gam = __expf(G);
-      // (fp16 operands: r_k moves into K^, CO into Q^)
-      sCR[PQ][i] = kF16 ? bt * gam : bt * gam * rk;                  // R = beta V - CR X
-      sCO[PQ][i] = p.scale * gam * rq;                               // O = CO (Q S0^T) + P U
-      sCS[PQ][i] = kF16 ? __expf(GC - G) : __expf(GC - G) * rk;      // S1 = gamma_C S0 + K^T diag(CS) U
-      if constexpr (kF16 || kCk) sRk[PQ][i] = rk;
+      sCR[PQ][i] = bt * gam * rk;                   // R = beta V - CR X
+      sCO[PQ][i] = p.scale * gam * rq;              // O = CO (Q S0^T) + P U
+      sCS[PQ][i] = __expf(GC - G) * rk;             // S1 = gamma_C S0 + K^T diag(CS) U
       if constexpr (kCk) sGc[PQ][i] = G;
       sBeta[PQ][i] = bt;
       if (i == 0) sGC[PQ][0] = __expf(GC);
       const float rowP = p.scale * rq, rowA = bt * rk;
       // diagonal tiles: P_im = rowP_i 2^(EG_i - EB_m) (Q K^T)_im, A likewise with rowA_i
       sEG[i] = G * kLog2e;
-      sEB[i] = G * kLog2e - __builtin_amdgcn_logf(rk);   // (r_k = 0: +inf, the key drops out)
+      sEB[i] = kF16 ? G * kLog2e : G * kLog2e - __builtin_amdgcn_logf(rk);   // (r_k = 0: +inf, the key drops out)
       sERp[i] = rowP;
       sERa[i] = rowA;
       // off-diagonal tile: exp(G_i - G_m) = exp(G_i - G_31) exp(G_31 - G_m)
@@ -819,60 +949,13 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       sEF[i] = (i < 32 ? rk : rowP) * F;
       sEFa[i] = rowA * F;
       arrive(&sSync[0]);
-      arrive(&sSync[2]);   // raw Q, K of chunk cp read (tile operands, norms)
+      tile_mma(Q, K, 1, 0, l32, hh, qk, kk);
       emit(std::false_type{}, qk, kk);
     } else {
-      if constexpr (!kSSD) {
-        // squared norms of the tile's 32 rows (two half-row sums each), ahead of its
-        // products: the chunk's vectors wait for them
-        const int i = 32 * pr + l32;
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int s = 0; s < DK / 16; ++s) {
-          sq = sumsq8(ldq8<DK>(Q, i, (DK / 2) * hh + 8 * s), sq);
-          sk = sumsq8(ldq8<DK>(K, i, (DK / 2) * hh + 8 * s), sk);
-        }
-        sq += __shfl_xor(sq, 32);
-        sk += __shfl_xor(sk, 32);
-        if (hh == 0) {
-          sNq[i] = sq;
-          sNk[i] = sk;
-        }
-        arrive(&sSync[4]);
-      }
       tile_mma(Q, K, pr, pr, l32, hh, qk, kk);
-      arrive(&sSync[2]);   // raw Q, K of chunk cp read (norms, tile operands)
       wait_count(&sSync[0], pgen);
       emit(std::true_type{}, qk, kk);
       if constexpr (!kSSD) solve_diag(Par<PQ>{}, pr);
-    }
-  };
-
-  // fp16 operands: once the three Gram-tile producers have read chunk cp's raw Q and K
-  // (arrival count 3 per chunk) and its vectors are out, Q and K are turned in place
-  // into Q^ = diag(CO) Q and K^ = diag(r_k) K in fp16, rows r0 .. r0 + 31 by one wave
-  // (lane: 16-byte segment lane % 16 of row r0 + 4 j + lane / 16; the element order
-  // within a row is unchanged).  The state waves read them in the next step.  Rows past
-  // the sequence end have CO = r_k = 0.
-  auto to_f16 = [&](int cp, auto parq, int r0) __attribute__((always_inline)) {
-    constexpr int PQ = decltype(parq)::value;
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
-    wait_count(&sSync[2], 3u * (uint32_t)(cp + 1));
-    wait_count(&sSync[0], (uint32_t)(cp + 1));
-    auto scaled = [](const uint4 w, float f) {
-      return make_uint4(cvt2h(bf_lo(w.x) * f, bf_hi(w.x) * f), cvt2h(bf_lo(w.y) * f, bf_hi(w.y) * f),
-                        cvt2h(bf_lo(w.z) * f, bf_hi(w.z) * f), cvt2h(bf_lo(w.w) * f, bf_hi(w.w) * f));
-    };
-#pragma unroll 2   // (fully unrolled, the loads of all rows would be hoisted at once)
-    for (int jj = 0; jj < 8; ++jj) {
-      const int r = r0 + 4 * jj + (lane_o >> 4);
-      const int o = r * DK + 8 * (lane_o & 15);
-      uint4* q = reinterpret_cast<uint4*>(&sQ[PQ][o]);
-      uint4* k = reinterpret_cast<uint4*>(&sK[PQ][o]);
-      const uint4 wq = *q, wk = *k;
-      *q = scaled(wq, sCO[PQ][r]);
-      *k = scaled(wk, sRk[PQ][r]);
     }
   };
 
@@ -947,56 +1030,54 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     constexpr bool hasS = !decltype(firstp)::value;   // step -1 has no chunk to consume
     const bool hasP = c + 1 < nch;
     lds_sync();                                    // previous step done (the step's one barrier)
-    // Land the staged data (Q, K of c + 1; V, Z of c) and announce it.  Staging loads
-    // are issued unconditionally (past the last chunk they re-read it, unused): a
-    // conditional load would merge with the old values and force a wait for it.
-    const int c1 = min(c + 1, nch - 1), c2 = min(c + 2, nch - 1);
-    if (hasP) {
-      rq_.template store<true>(sQ[PQ], si);
-      rk_.template store<true>(sK[PQ], si);
-    }
-    if constexpr (hasS) {
-      rv_.template store<false>(sV, si);
-      if constexpr (kSSD) {
-        if (p.z) rz_.template store<false>(sZ, si);
-      }
-    }
-    if constexpr (!kGate && !kProd) {
-      if (hasP && wu == 0) {
-        sGr[PQ][lane] = rg_;
-        sBr[PQ][lane] = rb_;
-      }
-    }
-    arrive(&sSync[3]);
+    // Each role lands its staged rows and announces them.  Staging loads are issued
+    // unconditionally (past the last chunk they re-read it, unused): a conditional
+    // load would merge with the old values and force a wait for it.
     if constexpr (kProd) {
-      stage_qk(c2);   // (the state waves stage theirs in the middle of the step)
-      stage_v(c1);
+      // Q, K of chunk c + 1 (and, gate not folded in, its log g, beta)
+      if (hasP) {
+        if constexpr (kSSD) {
+          rq_.template store<true>(sQ[PQ], siq);
+          rk_.template store<true>(sK[PQ], siq);
+        } else {
+          land_qk(Par<PQ>{}, min(C, tend - (tbeg + (c + 1) * C)));
+        }
+      }
+      if constexpr (!kGate) {
+        if (hasP && wu - NSW == 2) {
+          sGr[PQ][lane] = rg_;
+          sBr[PQ][lane] = rb_;
+        }
+      }
+      arrive(&sSync[3]);
+      stage_qk(min(c + 2, nch - 1));
       if (wu - NSW == 2) {   // T of chunk c (delta rule only); reads nothing landed here
         if constexpr (!kSSD) {
           if constexpr (hasS) merge_T(Par<PAR>{});
         }
         gate_store(PAR);       // (gate folded in) chunk c + 2, staged in this landing
-        if constexpr (kF16) {
-          if (hasP) to_f16(c + 1, Par<PQ>{}, 32);
-        }
       } else if (hasP) {
-        wait_count(&sSync[3], 8u * (uint32_t)(c + 2));   // the landing of this step done
+        wait_count(&sSync[3], (uint32_t)kNP * (uint32_t)(c + 2));   // the producers' landing of this step done
         produce(c + 1, Par<PQ>{});
-        if constexpr (kF16) {
-          if (wu - NSW == 3) to_f16(c + 1, Par<PQ>{}, 0);
-        }
       }
     } else {
+      // V, z of chunk c
+      if constexpr (hasS) {
+        rv_.template store<false>(sV, siv);
+        if constexpr (kSSD) {
+          if (p.z) rz_.template store<false>(sZ, siv);
+        }
+      }
+      arrive(&sSync[2]);
       if constexpr (hasS) {
         consume(c, Par<PAR>{});
-      } else {   // step -1: no chunk to consume, stage chunk 1's rows here
-        stage_qk(c2);
-        stage_v(c1);
+      } else {   // step -1: no chunk to consume, stage chunk 0's rows here
+        stage_v(min(c + 1, nch - 1));
       }
     }
   };
 
-  if (nch > 0) stage_qk(0);
+  if (nch > 0 && isP) stage_qk(0);
   if (tid < 8) sSync[tid] = 0u;   // visible to all after the first barrier
   // entry state and first staged loads retired on every path here, so no wait inside
   // the loop has to cover them
@@ -1014,23 +1095,25 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       if (c + 1 < nch) step(c + 1, Par<1>{}, rolep, std::false_type{});
     }
   };
+  // (each role ends in its own branch: no state-wave value stays live through the
+  // producers' loop)
   if (isP) {
     run(std::true_type{});
-  } else {
-    if (kCk) {   // checkpoint after ck_b tokens, ck_b in [0, len]
-      const int tok = p.ck_token[nseq], cks = p.ck_slot[nseq];
-      const int b = p.ck_relative ? tok : tok - tbeg;
-      if (tok >= 0 && cks >= 0 && b >= 0 && b <= tend - tbeg) {
-        ck_b = b;
-        ck_st = p.ck_states + ((int64_t)cks * p.H_v + h) * (int64_t)(DV * DK);
-      }
-    }
-    if (ck_b == 0) store_state(ck_st);
-    run(std::false_type{});
-    if (ck_b > 0 && ck_b == tend - tbeg) store_state(ck_st);
+    lds_sync();   // every wave's last wait is over
+    return;
   }
+  if (kCk) {   // checkpoint after ck_b tokens, ck_b in [0, len]
+    const int tok = p.ck_token[nseq], cks = p.ck_slot[nseq];
+    const int b = p.ck_relative ? tok : tok - tbeg;
+    if (tok >= 0 && cks >= 0 && b >= 0 && b <= tend - tbeg) {
+      ck_b = b;
+      ck_st = p.ck_states + ((int64_t)cks * p.H_v + h) * (int64_t)(DV * DK);
+    }
+  }
+  if (ck_b == 0) store_state(ck_st);
+  run(std::false_type{});
+  if (ck_b > 0 && ck_b == tend - tbeg) store_state(ck_st);
   lds_sync();   // every wave's last wait is over
-  if (isP) return;
   if (sSync[kFailFlag] != 0u) {   // a bounded wait ran out: poison this wave's results
     const float nan = __builtin_nanf("");
 #pragma unroll

@@ -35,6 +35,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4 mfma1632h(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -150,6 +153,15 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   v += dpp_mov<0x118, 0xf, true>(v);    // row_shr:8
   v += dpp_mov<0x142, 0xa, false>(v);   // row_bcast:15 into rows 1 and 3 (others add 0)
   v += dpp_mov<0x143, 0xc, false>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// Sum over each row of 16 lanes, in every lane of the row (DPP: swaps within pairs
+// and quads, then the half-row and row mirrors).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1, 0xf, true>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E, 0xf, true>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141, 0xf, true>(v);   // row_half_mirror (lane i <- 7 - i within 8)
+  v += dpp_mov<0x140, 0xf, true>(v);   // row_mirror (lane i <- 15 - i)
   return v;
 }
 __device__ __forceinline__ float sumsq8(const bf16x8& v, float a) {
