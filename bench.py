@@ -59,6 +59,12 @@ KERNEL_NAMES = {"extend": "chunk_kernel<128, 128, false, unsigned short",
                 "conv_prefill": "conv_out_kernel<4, true>"}
 PROF_CMD = "python bench.py --steps 20 --warmup 20 --no-cpu-baseline --no-configs --calibrate-copy-mib 1024"
 PMC_CMD = "python bench.py --steps 5 --warmup 2 --settle-ms 0 --no-cpu-baseline --no-configs --calibrate-copy-mib 1024"
+SQ_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_MFMA",
+              "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS"),
+             ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_INSTS_SALU",
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_COEXEC_CYCLES",
+              "SQ_WAIT_ANY"))
+SQ_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_sq_counters.txt")
 CONFIGS_PROF_CMD = "python bench.py --steps 20 --no-cpu-baseline --configs-only"
 CONFIGS_STATS_FILE = os.path.join(PROFILES, "gdn_ragged_verify_ssd128_kernel_stats.txt")
 
@@ -82,6 +88,8 @@ def parse():
                     help="time only the ragged, verify and delta-off workloads")
     ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 outputs of this script into profiles/ and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="summarize the two SQ counter passes of PMC_CMD into profiles/ and exit")
     ap.add_argument("--summarize-configs-prof", metavar="KT_DIR",
                     help="summarize a kernel trace of the --configs-only command into profiles/ and exit")
     return ap.parse_args()
@@ -120,6 +128,47 @@ def summarize_configs_prof(kt_dir):
     lines = ["# rocprofv3 kernel-trace statistics of the ragged, verify and delta-off workloads",
              "# summarized by: python bench.py --summarize-configs-prof <kt_dir>"] + _stats_lines(kt_dir, CONFIGS_PROF_CMD)
     with open(CONFIGS_STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_sq(dir1, dir2, launch_us=None):
+    """profiles/ summary of the two SQ counter passes (SQ_PASSES) of PMC_CMD: the average
+    per dispatch of every counter for the extend, decode and conv kernels, and derived
+    ratios for the extend kernel."""
+    vals = {}
+    for d in (dir1, dir2):
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            for kind in ("extend", "decode", "conv_prefill"):
+                if KERNEL_NAMES[kind] in r["Kernel_Name"]:
+                    vals.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    cmd = PMC_CMD
+    lines = ["# SQ counters per dispatch (average over the dispatches of the profiled command)"]
+    for i, counters in enumerate(SQ_PASSES):
+        lines.append(f"# pass {i + 1} (repository root): export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(counters)} "
+                     f"--output-format csv -d <dir{i + 1}> -o bench -- {cmd}")
+    lines += ["# summarized by: python bench.py --summarize-sq <dir1> <dir2>",
+              f"# kernel sources: chunk.hip sha256 {source_sha('extend')}, recurrent.hip sha256 {source_sha('decode')}",
+              f"{'kernel':<14} {'counter':<32} {'dispatches':>10} {'avg':>12}"]
+    for (kind, ctr), v in sorted(vals.items()):
+        lines.append(f"{kind:<14} {ctr:<32} {len(v):10d} {sum(v) / len(v):12.4e}")
+    a = {ctr: sum(v) / len(v) for (kind, ctr), v in vals.items() if kind == "extend"}
+    if a:
+        lines.append("# derived (extend):")
+        if a.get("SQ_BUSY_CU_CYCLES"):
+            lines.append(f"#   MFMA busy cycles / (busy CU cycles x 4 SIMDs): "
+                         f"{a.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (4 * a['SQ_BUSY_CU_CYCLES']):.3f}")
+        mops = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) + a.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0)
+        lines.append(f"#   MFMA FLOP from MOPS (x512): {mops * 512 / 1e9:.1f} GFLOP per dispatch")
+        if a.get("SQ_ACTIVE_INST_LDS"):
+            lines.append(f"#   LDS bank-conflict cycles / LDS-active cycles: "
+                         f"{a.get('SQ_LDS_BANK_CONFLICT', 0) / a['SQ_ACTIVE_INST_LDS']:.2f}")
+        if a.get("SQ_WAVE_CYCLES"):
+            lines.append(f"#   wait cycles / wave cycles: {a.get('SQ_WAIT_ANY', 0) / a['SQ_WAVE_CYCLES']:.2f}")
+        if a.get("SQ_INSTS_MFMA"):
+            lines.append(f"#   VALU instructions per MFMA instruction: {a.get('SQ_INSTS_VALU', 0) / a['SQ_INSTS_MFMA']:.1f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(SQ_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -412,6 +461,9 @@ def main():
     args = parse()
     if args.summarize_prof:
         summarize_prof(*args.summarize_prof)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
         return
     if args.summarize_configs_prof:
         summarize_configs_prof(args.summarize_configs_prof)

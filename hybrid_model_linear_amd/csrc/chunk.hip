@@ -8,23 +8,24 @@
 //
 //   A  = strict_lower( beta_i r_k,i r_k,m Gam_im (K K^T)_im ),   T = (I + A)^{-1}
 //   X  = K S0^T,   R = diag(beta) V - diag(beta gamma r_k) X      (first-order innovations)
-//   U  = T R = R + (T - I) bf16(R)                                 (delta-rule corrected values)
+//   U  = T R = R + (T - I) R                                       (delta-rule corrected values)
 //   O  = diag(scale gamma r_q) Q S0^T + P U,  P = lower( scale r_q,i r_k,m Gam_im (Q K^T)_im )
 //   S1 = gamma_C S0 + U^T diag(exp(G_C - G_i) r_k,i) K
 //
 // Delta-off mode (Mamba2 SSD, flashinfer.mamba.ssd_combined_fwd): no norms, T = I,
 // U = diag(dt') X, scale 1, then O += D x and O *= silu(z).
 //
-// Precision.  bf16 output: q and k land in LDS normalised, Q^ = diag(r_q) Q and
-// K^ = diag(r_k) K in fp16, and every product takes them, S0, P, U and the scaled U
-// of the state update as single fp16 operands (each bounded by construction or by
-// the values; fp16's 11-bit significand keeps every product's rounding below the
-// output's bf16 rounding, and the Gram tiles' below the bf16 rounding of T).  fp32
-// output and the delta-off mode:
-// q, k, v enter the MFMAs as their exact bf16 values, norms, beta and decays are fp32
-// scalings around the products, S0 is a single bf16 operand and P U and the state
-// update use two-term (hi + lo) bf16 splits.  T and the correction operand bf16(R)
-// are bf16 in both.
+// Precision.  T = (I + A)^{-1} is built and kept in fp16 in both (A and T entries
+// are bounded by one in magnitude: decays <= 1, beta <= 1, unit keys), with its
+// diagonal blocks solved in fp32 and the merges on fp16 MFMAs.  bf16 output: q and k
+// land in LDS normalised, Q^ = diag(r_q) Q and K^ = diag(r_k) K in fp16, and every
+// product takes them, S0, R, P, U and the scaled U of the state update as single
+// fp16 operands (each bounded by construction or by the values; fp16's 11-bit
+// significand keeps every product's rounding below the output's bf16 rounding).  fp32
+// output: q, k, v enter the MFMAs as their exact bf16 values, norms, beta and decays
+// are fp32 scalings around the products, and S0, T - I, R, P, U and the state update
+// use two-term (hi + lo) bf16 splits.  The delta-off mode (no T) takes S0 as a single
+// bf16 operand.
 //
 // Work split: one workgroup per (sequence, v-head) walks the sequence's chunks in
 // order.  Two kinds of waves run side by side:
@@ -145,12 +146,12 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
   constexpr int NTK = DK / 16;     // S^T row tiles (16 d_k rows each)
   static_assert(DK == 128 && (DV == 128 || DV == 64) && NSW * CW == DV, "tile shapes");
   // fp16 operands (GDN with bf16 output): Q^ = diag(r_q) Q and K^ = diag(r_k) K land
-  // in fp16 (normalised as they land), and the products take them, S0, the scaled U
-  // of the state update and P U as single fp16 operands.  Every operand is bounded by
-  // construction or by the values (|Q^|, |K^| <= 1, |P| <= scale, decays <= 1), and
+  // in fp16 (normalised as they land), and the products take them, S0, R, the scaled
+  // U of the state update and P U as single fp16 operands.  Every operand is bounded
+  // by construction or by the values (|Q^|, |K^| <= 1, |P| <= scale, decays <= 1), and
   // fp16's 11-bit significand keeps each product's error well below the output's bf16
-  // rounding.  fp32 output and the delta-off mode keep raw bf16 Q, K with bf16 S0 and
-  // two-term bf16 splits.
+  // rounding.  fp32 output keeps raw bf16 Q, K with two-term bf16 splits of the rest;
+  // the delta-off mode, raw bf16 Q, K with a bf16 S0.
   constexpr bool kF16 = !kSSD && sizeof(OutT) == 2;
 
   // chunk data: Q and K of chunk c (state waves) and c + 1 (producers); V, Z of chunk c
@@ -479,7 +480,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632h(ak, Sb[ct], U[ct][rt]);
         }
       }
-    } else {
+    } else if constexpr (kSSD) {
       bf16x8 Sb[CT][NKS];      // S0^T as B operand: k = d_k 32 s2 + 8 g16 + e
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -498,10 +499,35 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           const bf16x8 aq = ldq8<DK>(Q, row, 32 * s2 + 8 * g16);   // stored columns: k slots in order
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) Y[ct][rt] = mfma1632(Sb[ct][s2], aq, Y[ct][rt]);   // (Q S0^T)^T
-          if constexpr (!kSSD) {
-            const bf16x8 ak = ldq8<DK>(K, row, 32 * s2 + 8 * g16);
+        }
+      }
+    } else {   // raw operands, delta rule: S0 as hi + lo bf16, k-steps outermost
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632(ak, Sb[ct][s2], U[ct][rt]);   // X = K S0^T
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Y[ct][rt] = f32x4{};
+          U[ct][rt] = f32x4{};
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2) {
+        bf16x8 Sh[CT], Sl[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) pair_split(Sacc[ct][2 * s2], Sacc[ct][2 * s2 + 1], Sh[ct], Sl[ct]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int row = 16 * rt + j16;
+          const bf16x8 aq = ldq8<DK>(Q, row, 32 * s2 + 8 * g16);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {   // (Q S0^T)^T
+            Y[ct][rt] = mfma1632(Sh[ct], aq, Y[ct][rt]);
+            Y[ct][rt] = mfma1632(Sl[ct], aq, Y[ct][rt]);
+          }
+          const bf16x8 ak = ldq8<DK>(K, row, 32 * s2 + 8 * g16);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {   // X = K S0^T
+            U[ct][rt] = mfma1632(ak, Sh[ct], U[ct][rt]);
+            U[ct][rt] = mfma1632(ak, Sl[ct], U[ct][rt]);
           }
         }
       }
@@ -533,21 +559,45 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
     if constexpr (!kSSD) {
       wait_count(&sSync[1], (uint32_t)(c + 1));   // T of chunk c (finished in this step)
-      // U = T R = R + L bf16(R) with L = T - I (stored with a zero diagonal): R stays
-      // exact in the accumulator; L is strictly lower, so row tile rt needs k-steps <= rt / 2
-      bf16x8 Rb[CT][2];
+      // U = T R = R + L R with L = T - I (fp16, stored with a zero diagonal): R stays
+      // exact in the accumulator; L is strictly lower, so row tile rt needs k-steps <= rt / 2.
+      // fp16 operands: R in fp16; raw operands: L and R each as hi + lo bf16, three products.
+      if constexpr (kF16) {
+        f16x8 Rh[CT][2];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) Rb[ct][s2] = pair_to_op(U[ct][2 * s2], U[ct][2 * s2 + 1]);
+          for (int s2 = 0; s2 < 2; ++s2) Rh[ct][s2] = pair_to_op_h(U[ct][2 * s2], U[ct][2 * s2 + 1]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
+        for (int rt = 0; rt < 4; ++rt) {
+          const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
 #pragma unroll
-        for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
-          const bf16x8 ta = ld8u(trow + 32 * s2);
+          for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+            const f16x8 ta = __builtin_bit_cast(f16x8, ld8u(trow + 32 * s2));
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632(ta, Rb[ct][s2], U[ct][rt]);
+            for (int ct = 0; ct < CT; ++ct) U[ct][rt] = mfma1632h(ta, Rh[ct][s2], U[ct][rt]);
+          }
+        }
+      } else {
+        bf16x8 Rh[CT][2], Rl[CT][2];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pair_split(U[ct][2 * s2], U[ct][2 * s2 + 1], Rh[ct][s2], Rl[ct][s2]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const u16* trow = &sTb[PAR][16 * rt + j16][8 * g16];
+#pragma unroll
+          for (int s2 = 0; s2 <= (rt >> 1); ++s2) {
+            bf16x8 th, tl;
+            h8_split(__builtin_bit_cast(uint4, ld8u(trow + 32 * s2)), th, tl);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              U[ct][rt] = mfma1632(th, Rh[ct][s2], U[ct][rt]);
+              U[ct][rt] = mfma1632(th, Rl[ct][s2], U[ct][rt]);
+              U[ct][rt] = mfma1632(tl, Rh[ct][s2], U[ct][rt]);
+            }
+          }
         }
       }
     }
@@ -827,11 +877,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     }
     if (lane_o < 32) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_bf16(x[i]);
+      for (int i = 0; i < 16; ++i) sTb[PQ][16 * b + i][kperm(16 * b + c)] = f32_to_f16(x[i]);
     }
   };
   // Prepare chunk cp (buffers of parity PQ): its vectors, P (fp16, or bf16 hi + lo), and A stored in
-  // T's buffer (bf16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
+  // T's buffer (fp16, kperm columns) plus A's fp32 diagonal 16x16 blocks.  Roles
   // (pr = wave - NSW):
   //   pr 3:    the chunk's vectors (lane = token): decay cumsum, the coefficient
   //            vectors (with the row norms from the landing) and the decay factors of
@@ -896,7 +946,7 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
           *reinterpret_cast<uint2*>(&sPl[PQ][i][kperm(mb)]) = make_uint2(l0, l1);
         }
         if constexpr (!kSSD) {
-          *reinterpret_cast<uint2*>(&sTb[PQ][i][kperm(mb)]) = make_uint2(cvt2(av[0], av[1]), cvt2(av[2], av[3]));
+          *reinterpret_cast<uint2*>(&sTb[PQ][i][kperm(mb)]) = make_uint2(cvt2h(av[0], av[1]), cvt2h(av[2], av[3]));
           if constexpr (kDiag) {
             const f32x4 a4 = {av[0], av[1], av[2], av[3]};
             if (q4 == 0) ad0 = a4;
@@ -974,18 +1024,18 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
     for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t
       const int r0 = 32 * t;
       // B operand: column r0 + j16 of T00, rows r0 + 4 g16 + e
-      bf16x4 bD;
+      f16x4 bD;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(__bf16, T[r0 + 4 * g16 + e][kperm(r0 + j16)]);
+      for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(_Float16, T[r0 + 4 * g16 + e][kperm(r0 + j16)]);
       f32x4 y = {};
-      y = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 4 * g16)])), bD, y);
-      bf16x4 yb;
+      y = mfma16h(__builtin_bit_cast(f16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 4 * g16)])), bD, y);
+      f16x4 yb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) yb[e] = (__bf16)y[e];
+      for (int e = 0; e < 4; ++e) yb[e] = (_Float16)y[e];
       f32x4 zz = {};
-      zz = mfma16(__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
+      zz = mfma16h(__builtin_bit_cast(f16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 16 + 4 * g16)])), yb, zz);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) T[r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_bf16(-zz[e]);
+      for (int e = 0; e < 4; ++e) T[r0 + 16 + 4 * g16 + e][kperm(r0 + j16)] = f32_to_f16(-zz[e]);
     }
     lds_order();
     {   // 32 -> 64
@@ -993,25 +1043,26 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
-        bf16x8 bT;
+        f16x8 bT;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(__bf16, T[16 * s + 8 * hh + e][kperm(l32)]);
-        const bf16x8 a = join(*reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh)]),
-                              *reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh + 4)]));
-        y = mfma32(a, bT, y);
+        for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(_Float16, T[16 * s + 8 * hh + e][kperm(l32)]);
+        const f16x8 a = __builtin_bit_cast(f16x8, join(*reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh)]),
+                                                       *reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh + 4)])));
+        y = mfma32h(a, bT, y);
       }
       f32x16 zz = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const u16* trow = &T[32 + l32][0];
         const int c0 = 32 + 16 * s + 4 * hh;      // k slots 0..3: columns c0.., 4..7: c0 + 8..
-        zz = mfma32(join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
-                         *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8))), acc_to_op(y, s), zz);
+        zz = mfma32h(__builtin_bit_cast(f16x8, join(*reinterpret_cast<const uint2*>(trow + kperm(c0)),
+                                                    *reinterpret_cast<const uint2*>(trow + kperm(c0 + 8)))),
+                     acc_to_op_h(y, s), zz);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) T[32 + acc_row(r, hh)][kperm(l32)] = f32_to_bf16(-zz[r]);
+      for (int r = 0; r < 16; ++r) T[32 + acc_row(r, hh)][kperm(l32)] = f32_to_f16(-zz[r]);
     }
-    // the state waves apply L = T - I (U = R + L bf16(R)): the unit diagonal, needed by
+    // the state waves apply L = T - I (U = R + L R): the unit diagonal, needed by
     // the merges above, is stored as zero once they are done
     lds_order();
     T[lane_o][kperm(lane_o)] = 0;

@@ -38,6 +38,12 @@ __device__ __forceinline__ f32x4 mfma1632h(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16h(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// fp32 -> fp16 bits (round to nearest even)
+__device__ __forceinline__ u16 f32_to_f16(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -105,6 +111,11 @@ __device__ __forceinline__ bf16x8 acc_to_op(const f32x16& a, int half) {
 __device__ __forceinline__ bf16x8 pair_to_op(const f32x4& a, const f32x4& b) {
   return as_bf16x8(make_uint4(cvt2(a[0], a[1]), cvt2(a[2], a[3]), cvt2(b[0], b[1]), cvt2(b[2], b[3])));
 }
+__device__ __forceinline__ f16x8 acc_to_op_h(const f32x16& a, int half) {
+  const int o = 8 * half;
+  return __builtin_bit_cast(f16x8, make_uint4(cvt2h(a[o], a[o + 1]), cvt2h(a[o + 2], a[o + 3]),
+                                              cvt2h(a[o + 4], a[o + 5]), cvt2h(a[o + 6], a[o + 7])));
+}
 __device__ __forceinline__ f16x8 pair_to_op_h(const f32x4& a, const f32x4& b) {
   return __builtin_bit_cast(f16x8, make_uint4(cvt2h(a[0], a[1]), cvt2h(a[2], a[3]), cvt2h(b[0], b[1]), cvt2h(b[2], b[3])));
 }
@@ -125,6 +136,20 @@ __device__ __forceinline__ void pair_split(const f32x4& a, const f32x4& b, bf16x
   }
   hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
   lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+// 8 fp16 values as hi + lo bf16 operands (exact: fp16's 11-bit significand splits into
+// a bf16 and a bf16 remainder)
+__device__ __forceinline__ void h8_split(const uint4 w, bf16x8& hi, bf16x8& lo) {
+  const f16x8 h = __builtin_bit_cast(f16x8, w);
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = (float)h[2 * e], b = (float)h[2 * e + 1];
+    hw[e] = cvt2(a, b);
+    lw[e] = cvt2(sub_bf_lo(hw[e], a), sub_bf_hi(hw[e], b));
+  }
+  hi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  lo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 }
 // Row (token / d_k index) of accumulator element r held by lane half hh.
 __device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }

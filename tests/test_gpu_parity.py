@@ -242,6 +242,40 @@ def test_extend_long_memory(gdn_lib, decay, out_dtype):
     assert_close(d["pool"].cpu().numpy()[case.slot], np.stack([fin[s] for s in case.slot]), "states")
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_extend_precision_at_length(gdn_lib, out_dtype):
+    """One 8192-token sequence at the layer's shape (H_qk 16, H_v 32, d 128) with weak
+    decay (A_log shifted by log 1e-3: the state keeps thousands of tokens of history)
+    through the gated chunked kernel, from a nonzero pool state; sampled v-heads
+    (both v-heads of one qk-head, and heads at either end) against the float64 oracle.
+    The fp32 output is held to rel-L2 1e-3, the bf16 output to 2e-3; final states to
+    the output's bar."""
+    gdn = gdn_lib
+    _announce(f"precision at length 8192 out={out_dtype}")
+    rng = np.random.default_rng(23)
+    A_log = (np.log(rng.uniform(1, 16, 32)) + np.log(1e-3)).astype(np.float32)
+    case = synth.make_gdn_case("length-8192", seed=31, lens=(8192,), has_init=(1,), H_qk=16, H_v=32,
+                               d_k=128, d_v=128, A_log=A_log, num_slots=3)
+    d = upload(case)
+    init = case.pool[case.slot[0]].copy()
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], 16, 32, 128, 128)
+    g = gdn.gdn_gate_inputs(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    assert gdn.extend_kernel(q, k, v, None, None, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                             scale=case.scale, out_dtype=odt, max_seqlen=8192, gate=g) == ("chunked64", [])
+    out = gdn.extend(q, k, v, None, None, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                     scale=case.scale, out_dtype=odt, max_seqlen=8192, gate=g)
+    torch.cuda.synchronize()
+    heads = [0, 6, 7, 31]
+    ref, fin = oracle_seq(case, 0, heads, init)
+    rel = 2e-3 if out_dtype == "bf16" else 1e-3
+    got = out.float().cpu().numpy()[:, heads]
+    assert_close(got, ref, "out", rel=rel)
+    for i in (0, 4095, 8191):   # the rows at the start, middle and end, each on its own
+        assert rel_l2(got[i], ref[i]) <= 2 * rel, f"row {i}: rel-L2 {rel_l2(got[i], ref[i]):.3e}"
+    assert_close(d["pool"].cpu().numpy()[case.slot[0]][heads], fin, "state", rel=rel)
+
+
 def test_has_init_zero_ignores_pool_content(gdn_lib):
     gdn = gdn_lib
     _announce("has_init=0 ignores pool")
