@@ -1023,10 +1023,8 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 #pragma unroll
     for (int t = 0; t < 2; ++t) {   // 16 -> 32 inside diagonal tile t
       const int r0 = 32 * t;
-      // B operand: column r0 + j16 of T00, rows r0 + 4 g16 + e
-      f16x4 bD;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bD[e] = __builtin_bit_cast(_Float16, T[r0 + 4 * g16 + e][kperm(r0 + j16)]);
+      // B operand: column r0 + j16 of T00, rows r0 + 4 g16 + e (one transpose read)
+      const f16x4 bD = __builtin_bit_cast(f16x4, tr_read(&T[r0 + 4 * g16 + (j16 >> 2)][kperm(r0 + 4 * (j16 & 3))]));
       f32x4 y = {};
       y = mfma16h(__builtin_bit_cast(f16x4, *reinterpret_cast<const uint2*>(&T[r0 + 16 + j16][kperm(r0 + 4 * g16)])), bD, y);
       f16x4 yb;
@@ -1042,10 +1040,11 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
       f32x16 y = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7
-        f16x8 bT;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bT[e] = __builtin_bit_cast(_Float16, T[16 * s + 8 * hh + e][kperm(l32)]);
+        // B operand: column l32 of T11, rows 16 s + 8 hh + 0..7 (two transpose reads; a
+        // 16-lane group covers columns 16 (l32 / 16) .. + 15)
+        const int cb = kperm((l32 & 16) + 4 * (j16 & 3));
+        const f16x8 bT = __builtin_bit_cast(f16x8, join(tr_read(&T[16 * s + 8 * hh + (j16 >> 2)][cb]),
+                                                        tr_read(&T[16 * s + 8 * hh + 4 + (j16 >> 2)][cb])));
         const f16x8 a = __builtin_bit_cast(f16x8, join(*reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh)]),
                                                        *reinterpret_cast<const uint2*>(&T[32 + l32][kperm(16 * s + 8 * hh + 4)])));
         y = mfma32h(a, bT, y);
