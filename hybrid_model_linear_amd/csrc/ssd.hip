@@ -332,18 +332,20 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   };
 
   // ---------------------------------------------------------------- per-chunk pieces
+  // Lane-derived LDS addresses are recomputed once per chunk step from an opaque copy of
+  // the lane id, lane_s, set at the top of every step: the reads of one step share them
+  // (one computation per step), and they are not kept live across the chunk loop.
+  int lane_s = lane;
   // X operand (16x16x32, as A = X^T or B = X): lane (g16, j16) holds x[m][16 pt + j16] of
   // this wave's head for the k slots m = 32 s2 + 4 g16 + e (e < 4), 32 s2 + 16 + 4 g16 + e - 4
   auto x_op = [&](int s2) __attribute__((always_inline)) {
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
+    const int lane_o = lane_s;
     const int rb = 4 * (lane_o >> 4) + ((lane_o & 15) >> 2), cp = 16 * pt + 4 * (lane_o & 3);
     return join_h(ldtr<PH>(sm.X[hs], 32 * s2 + rb, cp), ldtr<PH>(sm.X[hs], 32 * s2 + 16 + rb, cp));
   };
   // B^T operand for state tile tk (rows n in the tile's order, k slots as x_op)
   auto bt_op = [&](int tk, int s2) __attribute__((always_inline)) {
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
+    const int lane_o = lane_s;
     const int rb = 4 * (lane_o >> 4) + ((lane_o & 15) >> 2);
     const int ca = 32 * (tk >> 1) + 8 * (lane_o & 3) + 4 * (tk & 1);
     return join_h(ldqtr<NS>(sm.B, 32 * s2 + rb, ca), ldqtr<NS>(sm.B, 32 * s2 + 16 + rb, ca));
@@ -468,6 +470,8 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   if (kCk && ck_b >= 0 && ck_b == CS * c0 && ck_b < tend - tbeg) store_state(ck_st, Sacc);
 
   for (int c = c0; c < c1; ++c) {
+    lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
     const int par = c & 1;
     const SsdVec& V = sm.vec[par][hs];
     const int t0 = tbeg + c * CS, n = min(CS, tend - t0);
