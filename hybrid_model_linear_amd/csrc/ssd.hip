@@ -34,7 +34,9 @@
 //     earlier block from the raw C B^T tile with the decay factored at the block's last
 //     token r, e^{G_i - G_m} = e^{G_i - G_r} e^{G_r - G_m} (both <= 1: the key factor
 //     scales X, the query factor the block's partial sum);
-//   * D x, silu(z) and the output rows.
+//   * the epilogue: the y tiles go through LDS (over the C and B rows, read by then), so
+//     that each thread finishes (y + D x) silu(z) for 8 columns of a token row, with z
+//     read and the output written in whole 128-byte rows.
 // The chunk's C, B and x rows are staged from memory through registers one chunk
 // ahead.  Operand precision: C, B, x exact in fp16 (bf16 values in fp16's normal
 // range); S0, P and the scaled X carry fp16's 11-bit significand (2^-12 relative
@@ -92,6 +94,11 @@ __device__ __forceinline__ int pperm(int c) {
   const int q = c >> 2;
   return ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
 }
+// y row buffer of the epilogue: token row r, 16-byte chunk q (p = 4 q .. 4 q + 3) at
+// chunk q ^ (r % 16) of the row, so that both the owner waves' 16-byte writes (16 rows
+// x 4 chunks) and the epilogue's reads (8 rows x 8 chunk pairs) spread over the banks.
+__device__ __forceinline__ int yidx(int r, int q) { return r * PH + 4 * (q ^ (r & 15)); }
+
 // Off-diagonal 32x32 tiles of C B^T (i-block d > m-block s2), in the order
 // (1,0), (2,0), (2,1), (3,0), (3,1), (3,2): index d (d - 1) / 2 + s2.
 __device__ __forceinline__ int offdiag_i(int o) { return o == 0 ? 1 : o < 3 ? 2 : 3; }
@@ -111,8 +118,16 @@ template <bool kFull>
 struct SsdSmem;
 template <>
 struct SsdSmem<true> {
-  u16 C[CS * NS];                 // fp16 C rows, swizzled 16-byte chunks (qidx)
-  u16 B[CS * NS];                 // fp16 B rows, same layout
+  union {
+    struct {
+      u16 C[CS * NS];             // fp16 C rows, swizzled 16-byte chunks (qidx)
+      u16 B[CS * NS];             // fp16 B rows, same layout
+    };
+    // (epilogue, once C and B are read) both head slots' y rows, [token][p] in fp32
+    // with the 16-byte chunks of a row swizzled (yidx)
+    float Yx[2][CS * PH];
+  };
+  float Dv[2][PH];                // D per output column of each head slot (0 without D)
   u16 X[2][CS * (PH + 8)];        // fp16 x rows per head slot, padded (pidx)
   u16 CB[6][32 * kTP];            // off-diagonal 32x32 tiles of C B^T, pperm columns
   u16 Pd[2][4][32 * kTP];         // per head slot: the diagonal tiles of P (masked, decayed)
@@ -440,21 +455,21 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     }
   };
 
-  // per-lane output columns 16 pt + 4 g16 + e
-  float4 Dc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if constexpr (kFull) {
-    if (p.D) {
+  // The epilogue's work split: thread tid finishes output columns 8 (tid % 8) .. + 7
+  // of token rows tid / 8 and tid / 8 + 64 of both head slots (slice i = 0..3: head
+  // slot i / 2, row tid / 8 + 64 (i % 2)) -- 8 threads per 128-byte row of a head, so
+  // that z is read and the output written in whole rows.
+  const int ek = tid & 7, er = tid >> 3;
+  if constexpr (kFull) {   // D of the two head slots (visible after the first barrier)
+    if (tid < 2 * PH) {
+      const int hsl = tid / PH, col = tid % PH, hd = hsl ? hB : hA;
       const u16* Db = reinterpret_cast<const u16*>(p.D);
-      float d[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        d[e] = bf16_to_f32(Db[p.D_per_dim ? (int64_t)h * PH + 16 * pt + 4 * g16 + e : (int64_t)h]);
-      Dc = make_float4(d[0], d[1], d[2], d[3]);
+      sm.Dv[hsl][col] = Db ? bf16_to_f32(Db[p.D_per_dim ? (int64_t)hd * PH + col : (int64_t)hd]) : 0.f;
     }
   }
   const uint32_t ostride_b = (uint32_t)p.out_stride * (uint32_t)sizeof(OutT);
-  // z rows of this wave's columns (token 16 it + j16), or x again when there is no z
-  const u16* zrow = p.z ? reinterpret_cast<const u16*>(p.z) + (int64_t)h * PH + 16 * pt : xg + (int64_t)h * PH + 16 * pt;
+  // z rows (x again when there is no z: valid memory, unused)
+  const u16* zg = p.z ? reinterpret_cast<const u16*>(p.z) : xg;
   const uint32_t zs_b = (uint32_t)(p.z ? p.z_stride : p.v_stride) * 2u;
 
   // ---------------------------------------------------------------- chunk loop
@@ -477,17 +492,17 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const int t0 = tbeg + c * CS, n = min(CS, tend - t0);
     lds_sync();                              // the previous chunk's LDS reads are done
     land();
-    // the epilogue's z of this chunk, issued before the next chunk's staging so that
-    // their use waits for them only
-    uint2 ez0, ez1, ez2, ez3, ez4, ez5, ez6, ez7;
+    // the epilogue's z of this chunk (its four slices), issued before the next chunk's
+    // staging so that their use waits for them only
+    uint4 ez0, ez1, ez2, ez3;
     if constexpr (kFull) {
-      const char* zb = reinterpret_cast<const char*>(zrow + (int64_t)t0 * (zs_b / 2));
-      auto ldz = [&](int it) __attribute__((always_inline)) {
-        const int i = 16 * it + j16;
-        return *reinterpret_cast<const uint2*>(zb + (uint32_t)(i < n ? i : 0) * zs_b + 8u * (uint32_t)g16);
+      const char* zb = reinterpret_cast<const char*>(zg + (int64_t)t0 * (zs_b / 2));
+      auto ldz = [&](int i) __attribute__((always_inline)) {
+        const int r = er + 64 * (i & 1);
+        const uint32_t col = (uint32_t)((i >> 1 ? hB : hA) * PH + 8 * ek);
+        return *reinterpret_cast<const uint4*>(zb + (uint32_t)(r < n ? r : 0) * zs_b + 2u * col);
       };
       ez0 = ldz(0); ez1 = ldz(1); ez2 = ldz(2); ez3 = ldz(3);
-      ez4 = ldz(4); ez5 = ldz(5); ez6 = ldz(6); ez7 = ldz(7);
     }
     stage(min(c + 1, c1 - 1));               // (unconditional: past the last chunk it re-reads it)
     lds_sync();                              // landing visible
@@ -564,35 +579,48 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
           Y[it] += t * __builtin_amdgcn_exp2f(V.G2[row] - V.G2[32 * s2 + 31]);
         }
       }
-      // epilogue: (y + D x) silu(z), rows past the sequence end dropped by the bounded
-      // buffer stores (record = the chunk's n rows)
-      if (owner) {
-        char* obase = reinterpret_cast<char*>(p.out) +
-                      ((int64_t)t0 * p.out_stride + (int64_t)h * PH + 16 * pt) * (int64_t)sizeof(OutT);
+      // epilogue: every wave's y tiles into Yx (C and B are no longer read in this
+      // chunk), then per slice (y + D x) silu(z) in whole rows; rows past the sequence
+      // end are dropped by the bounded buffer stores (record = the chunk's n rows)
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+        *reinterpret_cast<f32x4*>(&sm.Yx[hs][yidx(16 * it + j16, 4 * pt + g16)]) = Y[it];
+      lds_sync();
+      {
+        char* obase = reinterpret_cast<char*>(p.out) + (int64_t)t0 * p.out_stride * (int64_t)sizeof(OutT);
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)((uint32_t)n * ostride_b), kBufWord3);
-        const uint2 ez[8] = {ez0, ez1, ez2, ez3, ez4, ez5, ez6, ez7};
+        const uint4 ez[4] = {ez0, ez1, ez2, ez3};
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int row = 16 * it + j16;
-          const uint2 xw = *reinterpret_cast<const uint2*>(sm.X[hs] + pidx<PH>(row, 16 * pt + 4 * g16));
-          const float xv[4] = {h_lo(xw.x), h_hi(xw.x), h_lo(xw.y), h_hi(xw.y)};
-          float y[4];
+        for (int i = 0; i < 4; ++i) {
+          const int hsl = i >> 1, r = er + 64 * (i & 1);
+          if (hsl == 1 && !two) continue;   // (a lone head: its mirror slot stores nothing)
+          const f32x4 ya = *reinterpret_cast<const f32x4*>(&sm.Yx[hsl][yidx(r, 2 * ek)]);
+          const f32x4 yb = *reinterpret_cast<const f32x4*>(&sm.Yx[hsl][yidx(r, 2 * ek + 1)]);
+          const f32x4 da = *reinterpret_cast<const f32x4*>(&sm.Dv[hsl][8 * ek]);
+          const f32x4 db = *reinterpret_cast<const f32x4*>(&sm.Dv[hsl][8 * ek + 4]);
+          const uint4 xw = *reinterpret_cast<const uint4*>(sm.X[hsl] + pidx<PH>(r, 8 * ek));
+          const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
+          const uint32_t zs[4] = {ez[i].x, ez[i].y, ez[i].z, ez[i].w};
+          float y[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = Y[it][e] + f4get(Dc, e) * xv[e];
-          if (p.z) {
-            const float zv[4] = {bf_lo(ez[it].x), bf_hi(ez[it].x), bf_lo(ez[it].y), bf_hi(ez[it].y)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] *= silu_f(zv[e]);
+          for (int e = 0; e < 4; ++e) {
+            y[e] = ya[e] + da[e] * (e & 1 ? h_hi(xs[e >> 1]) : h_lo(xs[e >> 1]));
+            y[4 + e] = yb[e] + db[e] * (e & 1 ? h_hi(xs[2 + (e >> 1)]) : h_lo(xs[2 + (e >> 1)]));
           }
-          const int off = (int)((uint32_t)row * ostride_b + (uint32_t)(4 * g16 * sizeof(OutT)));
+          if (p.z) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= silu_f(e & 1 ? bf_hi(zs[e >> 1]) : bf_lo(zs[e >> 1]));
+          }
+          const int off = (int)((uint32_t)r * ostride_b + (uint32_t)(((hsl ? hB : hA) * PH + 8 * ek) * sizeof(OutT)));
           if constexpr (sizeof(OutT) == 2) {
-            const u32x2 w = {cvt2(y[0], y[1]), cvt2(y[2], y[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
-          } else {
-            const u32x4 w = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
-                             __float_as_uint(y[3])};
+            const u32x4 w = {cvt2(y[0], y[1]), cvt2(y[2], y[3]), cvt2(y[4], y[5]), cvt2(y[6], y[7])};
             __builtin_amdgcn_raw_buffer_store_b128(w, rs, off, 0, 0);
+          } else {
+            const u32x4 w0 = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+            const u32x4 w1 = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])};
+            __builtin_amdgcn_raw_buffer_store_b128(w0, rs, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(w1, rs, off + 16, 0, 0);
           }
         }
       }
@@ -699,10 +727,15 @@ int ssd_obstacles(const SeqLaunch& p) {
   if (!p.in_bf16) why |= GDN_WHY_FP32;
   if (!ssd_chunked_shape(p)) why |= GDN_WHY_HEAD_DIMS;
   if (p.N > 65535) why |= GDN_WHY_BATCH;
-  // B, C (prep kernel) and x rows are read as 16-byte segments
+  // B, C (prep kernel), x and z rows are read, and the output rows written, as 16-byte
+  // segments
   const uintptr_t ptrs = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.k) |
-                         reinterpret_cast<uintptr_t>(p.v);
-  if (ptrs % 16 != 0 || (p.q_stride | p.k_stride | p.v_stride) % 8 != 0) why |= GDN_WHY_ALIGN;
+                         reinterpret_cast<uintptr_t>(p.v) | reinterpret_cast<uintptr_t>(p.z) |
+                         reinterpret_cast<uintptr_t>(p.out);
+  const int64_t out_elems16 = p.out_bf16 ? 8 : 4;   // output elements per 16 bytes
+  if (ptrs % 16 != 0 || (p.q_stride | p.k_stride | p.v_stride | (p.z ? p.z_stride : 0)) % 8 != 0 ||
+      p.out_stride % out_elems16 != 0)
+    why |= GDN_WHY_ALIGN;
   // 32-bit offsets of the output rows of a chunk (bounded buffer stores)
   if (p.out_stride > (int64_t(1) << 31) / (CS * 4)) why |= GDN_WHY_STRIDE;
   return why;
