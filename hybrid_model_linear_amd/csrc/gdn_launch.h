@@ -86,12 +86,14 @@ struct SeqLaunch {
   int sp_steps;
   int keep_pool;
   int lpt;                    // chunked kernel: longest sequences first (small N)
-  // Chunk-128 delta-off kernel: fp16 copies of B (k) and C (q), [T, H_qk, d_k], in the
-  // caller's workspace; each sequence cut into ssd_segs segments of ssd_seg_chunks
-  // chunks (the last takes the rest) with the states segR [N, segs - 1, H_v, d_v, d_k]
-  // and log decays segL [N, segs - 1, H_v] of all but the last segment.
+  // Chunk-128 delta-off kernel: fp16 copies of B (k) and C (q), [T, H_qk, d_k], and the
+  // chunks' raw C B^T tiles, in the caller's workspace; each sequence cut into ssd_segs
+  // segments of ssd_seg_chunks chunks (the last takes the rest) with the states segR
+  // [N, segs - 1, H_v, d_v, d_k] and log decays segL [N, segs - 1, H_v] of all but the
+  // last segment.
   const u16* ssd_Bh;
   const u16* ssd_Ch;
+  const u16* ssd_CB;          // raw C B^T tiles per chunk slot and group (fp16)
   float* segR;
   float* segL;
   int ssd_segs;

@@ -104,6 +104,17 @@ __device__ __forceinline__ int yidx(int r, int q) { return r * PH + 4 * (q ^ (r 
 __device__ __forceinline__ int offdiag_i(int o) { return o == 0 ? 1 : o < 3 ? 2 : 3; }
 __device__ __forceinline__ int offdiag_m(int o) { return o == 0 ? 0 : o < 3 ? o - 1 : o - 3; }
 
+// The raw C B^T tiles of every chunk (computed once per call for all heads of a group):
+// chunk c of sequence s, starting at token tbeg_s + 128 c, has the slot
+// floor(tbeg_s / 128) + s + c -- consecutive within a sequence, increasing from one
+// sequence to the next, all below floor(T / 128) + N.  A slot holds per group the ten
+// 32x32 tiles (the six off-diagonal ones in offdiag order, then the four diagonal
+// ones), each as fp16 in 32x32 accumulator order: lane l32 + 32 hh holds query row l32
+// and keys 8 q4 + 4 hh + e at position 4 q4 + e (32 bytes per lane).
+constexpr int kCBTiles = 10;
+constexpr int kCBTileElems = 32 * 32;
+__device__ __forceinline__ int64_t cb_slot_base(int tbeg, int s) { return (int64_t)(tbeg / CS) + s; }
+
 // One head's per-token coefficients of one chunk (token m of the chunk).
 struct SsdVec {
   float G2[CS];      // G_m log2 e (G: in-chunk cumulative log decay)
@@ -112,6 +123,12 @@ struct SsdVec {
   u16 wfac[CS];      // e^{G_C - G_m} dt'_m in fp16: the state update's token weights
   u16 ufac[CS];      // e^{G_r - G_m} dt'_m in fp16, r the last token of m's 32-token block
   float gC[2];       // e^{G_C}, G_C (natural log)
+};
+
+// One chunk's staged rows in registers (16-byte segments; named members, no arrays,
+// so that they stay in registers): C, B and both heads' x.
+struct SsdStage {
+  uint4 c0, c1, c2, c3, b0, b1, b2, b3, x0, x1, x2, x3;
 };
 
 template <bool kFull>
@@ -259,7 +276,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   const u16* Cg = p.ssd_Ch + (int64_t)j * NS;
   const u16* Bg = p.ssd_Bh + (int64_t)j * NS;
   const u16* xg = reinterpret_cast<const u16*>(p.v);
-  uint4 rC0, rC1, rC2, rC3, rB0, rB1, rB2, rB3, rX0, rX1, rX2, rX3;
+  SsdStage rs0;
   auto ld_cb = [&](const u16* g, int t0, int n, int i) __attribute__((always_inline)) {
     const int sidx = tid + i * kThreads, r = sidx >> 4, c = sidx & 15;
     const char* base = reinterpret_cast<const char*>(g + (int64_t)t0 * bcs);
@@ -272,22 +289,22 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const uint32_t off = ((uint32_t)(r < n ? r : 0) * (uint32_t)p.v_stride + 8u * (uint32_t)c) * 2u;
     return *reinterpret_cast<const uint4*>(base + off);
   };
-  auto stage = [&](int cc) __attribute__((always_inline)) {
+  auto stage = [&](SsdStage& r, int cc) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * CS, n = min(CS, tend - t0);
     if constexpr (kFull) {
-      rC0 = ld_cb(Cg, t0, n, 0);
-      rC1 = ld_cb(Cg, t0, n, 1);
-      rC2 = ld_cb(Cg, t0, n, 2);
-      rC3 = ld_cb(Cg, t0, n, 3);
+      r.c0 = ld_cb(Cg, t0, n, 0);
+      r.c1 = ld_cb(Cg, t0, n, 1);
+      r.c2 = ld_cb(Cg, t0, n, 2);
+      r.c3 = ld_cb(Cg, t0, n, 3);
     }
-    rB0 = ld_cb(Bg, t0, n, 0);
-    rB1 = ld_cb(Bg, t0, n, 1);
-    rB2 = ld_cb(Bg, t0, n, 2);
-    rB3 = ld_cb(Bg, t0, n, 3);
-    rX0 = ld_x(t0, n, 0);
-    rX1 = ld_x(t0, n, 1);
-    rX2 = ld_x(t0, n, 2);
-    rX3 = ld_x(t0, n, 3);
+    r.b0 = ld_cb(Bg, t0, n, 0);
+    r.b1 = ld_cb(Bg, t0, n, 1);
+    r.b2 = ld_cb(Bg, t0, n, 2);
+    r.b3 = ld_cb(Bg, t0, n, 3);
+    r.x0 = ld_x(t0, n, 0);
+    r.x1 = ld_x(t0, n, 1);
+    r.x2 = ld_x(t0, n, 2);
+    r.x3 = ld_x(t0, n, 3);
   };
   // raw gate inputs of one chunk for a vector wave (lane l: tokens 2 l, 2 l + 1), kept
   // as loaded until their use a step later (an instruction on a loaded value makes the
@@ -382,7 +399,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   };
 
   // landing of the staged rows: C, B as they are, x converted to fp16
-  auto land = [&]() __attribute__((always_inline)) {
+  auto land = [&](const SsdStage& r) __attribute__((always_inline)) {
     auto st_cb = [&](u16* tile, int i, uint4 v) __attribute__((always_inline)) {
       const int sidx = tid + i * kThreads, r = sidx >> 4, c = sidx & 15;
       *reinterpret_cast<uint4*>(tile + qidx<NS>(r, 8 * c)) = v;
@@ -392,44 +409,44 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
       *reinterpret_cast<uint4*>(sm.X[i >> 1] + pidx<PH>(r, 8 * c)) = make_uint4(bf2h(w.x), bf2h(w.y), bf2h(w.z), bf2h(w.w));
     };
     if constexpr (kFull) {
-      st_cb(sm.C, 0, rC0);
-      st_cb(sm.C, 1, rC1);
-      st_cb(sm.C, 2, rC2);
-      st_cb(sm.C, 3, rC3);
+      st_cb(sm.C, 0, r.c0);
+      st_cb(sm.C, 1, r.c1);
+      st_cb(sm.C, 2, r.c2);
+      st_cb(sm.C, 3, r.c3);
     }
-    st_cb(sm.B, 0, rB0);
-    st_cb(sm.B, 1, rB1);
-    st_cb(sm.B, 2, rB2);
-    st_cb(sm.B, 3, rB3);
-    st_x(0, rX0);
-    st_x(1, rX1);
-    st_x(2, rX2);
-    st_x(3, rX3);
+    st_cb(sm.B, 0, r.b0);
+    st_cb(sm.B, 1, r.b1);
+    st_cb(sm.B, 2, r.b2);
+    st_cb(sm.B, 3, r.b3);
+    st_x(0, r.x0);
+    st_x(1, r.x1);
+    st_x(2, r.x2);
+    st_x(3, r.x3);
   };
 
-  // One 32x32 tile of C B^T for query block ti, key block tm: each lane holds query row
-  // i = 32 ti + l32 and keys m = 32 tm + 8 q4 + 4 hh + e (acc[4 q4 + e]).
-  auto cb_tile = [&](int ti, int tm, int l32, int hh) __attribute__((always_inline)) {
-    f32x16 acc = {};
+  // This wave's raw C B^T tiles of the chunk, loaded at the top of its step: the
+  // diagonal tile pt, and for waves 0-5 the off-diagonal tile wu (16 fp16 per lane).
+  auto load_tiles = [&](int cc, uint4& d0, uint4& d1, uint4& o0, uint4& o1) __attribute__((always_inline)) {
     if constexpr (kFull) {
-#pragma unroll
-      for (int s = 0; s < NS / 16; ++s) {
-        const f16x8 a = as_f16x8(__builtin_bit_cast(uint4, ldq8<NS>(sm.B, 32 * tm + l32, 16 * s + 8 * hh)));
-        const f16x8 b = as_f16x8(__builtin_bit_cast(uint4, ldq8<NS>(sm.C, 32 * ti + l32, 16 * s + 8 * hh)));
-        acc = mfma32h(a, b, acc);
+      const u16* base = p.ssd_CB + ((cb_slot_base(tbeg, nseq) + cc) * p.H_qk + j) * (int64_t)(kCBTiles * kCBTileElems) +
+                        16 * lane;
+      d0 = *reinterpret_cast<const uint4*>(base + (6 + pt) * kCBTileElems);
+      d1 = *reinterpret_cast<const uint4*>(base + (6 + pt) * kCBTileElems + 8);
+      if (wu < 6) {
+        o0 = *reinterpret_cast<const uint4*>(base + wu * kCBTileElems);
+        o1 = *reinterpret_cast<const uint4*>(base + wu * kCBTileElems + 8);
       }
     }
-    return acc;
   };
-  // this wave's tiles: its head's diagonal tile pt of P (masked, decayed) and, waves
-  // 0-5, the raw off-diagonal tile wu of C B^T
-  auto make_tiles = [&](const SsdVec& V) __attribute__((always_inline)) {
+  // ... and from them this wave's head's diagonal tile pt of P (masked, decayed) and,
+  // waves 0-5, the raw off-diagonal tile wu in LDS
+  auto make_tiles = [&](const SsdVec& V, uint4 d0, uint4 d1, uint4 o0, uint4 o1) __attribute__((always_inline)) {
     if constexpr (kFull) {
       int lane_o = lane;
       asm volatile("" : "+v"(lane_o));
       const int l32 = lane_o & 31, hh = lane_o >> 5;
       {
-        const f32x16 acc = cb_tile(pt, pt, l32, hh);
+        const uint32_t w[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         const int i = 32 * pt + l32;
         const float gi = V.G2[i];
         u16* dst = sm.Pd[hs][pt] + l32 * kTP;
@@ -439,18 +456,19 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
           const float4 gm = ld_f4(&V.G2[mb]);
           float pv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pv[e] = __builtin_amdgcn_exp2f(mb + e <= i ? gi - f4get(gm, e) : -INFINITY) * acc[4 * q4 + e];
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t we = w[2 * q4 + (e >> 1)];
+            pv[e] = __builtin_amdgcn_exp2f(mb + e <= i ? gi - f4get(gm, e) : -INFINITY) * (e & 1 ? h_hi(we) : h_lo(we));
+          }
           *reinterpret_cast<uint2*>(dst + pperm(8 * q4 + 4 * hh)) = make_uint2(cvt2h(pv[0], pv[1]), cvt2h(pv[2], pv[3]));
         }
       }
       if (wu < 6) {
-        const f32x16 acc = cb_tile(offdiag_i(wu), offdiag_m(wu), l32, hh);
+        const uint32_t w[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
         u16* dst = sm.CB[wu] + l32 * kTP;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<uint2*>(dst + pperm(8 * q4 + 4 * hh)) =
-              make_uint2(cvt2h(acc[4 * q4], acc[4 * q4 + 1]), cvt2h(acc[4 * q4 + 2], acc[4 * q4 + 3]));
+          *reinterpret_cast<uint2*>(dst + pperm(8 * q4 + 4 * hh)) = make_uint2(w[2 * q4], w[2 * q4 + 1]);
       }
     }
   };
@@ -474,7 +492,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
 
   // ---------------------------------------------------------------- chunk loop
   if (c0 < c1) {
-    stage(c0);
+    stage(rs0, c0);
     if (vwave) stage_gate(c0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
@@ -491,7 +509,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const SsdVec& V = sm.vec[par][hs];
     const int t0 = tbeg + c * CS, n = min(CS, tend - t0);
     lds_sync();                              // the previous chunk's LDS reads are done
-    land();
+    land(rs0);
     // the epilogue's z of this chunk (its four slices), issued before the next chunk's
     // staging so that their use waits for them only
     uint4 ez0, ez1, ez2, ez3;
@@ -504,10 +522,13 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
       };
       ez0 = ldz(0); ez1 = ldz(1); ez2 = ldz(2); ez3 = ldz(3);
     }
-    stage(min(c + 1, c1 - 1));               // (unconditional: past the last chunk it re-reads it)
+    // this chunk's raw C B^T tiles (made into LDS tiles after the update; with
+    // checkpoints, loaded after the in-chunk checkpoint, whose registers they would add to)
+    uint4 td0, td1, to0 = {}, to1 = {};
+    if constexpr (!kCk) load_tiles(c, td0, td1, to0, to1);
+    stage(rs0, min(c + 1, c1 - 1));          // (unconditional: past the last chunk it re-reads it)
     lds_sync();                              // landing visible
     const float gamma = V.gC[0];
-    make_tiles(V);
     if (vwave) {
       if (c + 1 < c1) make_vectors(c + 1, sm.vec[par ^ 1][wu - 6]);
       stage_gate(min(c + 2, c1 - 1));
@@ -555,12 +576,14 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
         update(Sc, __builtin_amdgcn_exp2f(Gm2), Wc);
         store_state(ck_st, Sc);
       }
+      if constexpr (kCk) load_tiles(c, td0, td1, to0, to1);
       {
         f16x8 W[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) W[s2] = scale_h(x_op(s2), fac_op(V.wfac, s2));
         update(Sacc, gamma, W);
       }
+      make_tiles(V, td0, td1, to0, to1);
       lds_sync();                            // P and C B^T tiles complete
       f16x8 xo[4];
 #pragma unroll
@@ -647,33 +670,76 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   }
 }
 
-// fp16 copies of B and C ([T, G, N] contiguous) for the chunked delta-off kernels:
-// every head of a group reads them, so they are converted once per call.  One thread
-// per 8 elements.
+// Per chunk, once per call (every head of a group shares it): the fp16 copies of the
+// chunk's B and C rows ([T, G, N] contiguous) and its raw C B^T tiles.  Workgroup =
+// (chunk slot, group): the rows land converted in LDS and go out as the copies, then
+// wave w computes the tiles w, w + 4, w + 8 from LDS.  Rows past the sequence end take
+// the chunk's first row, as the chunk kernel's landing does (and are not copied out).
 __global__ void __launch_bounds__(256) ssd_prep_kernel(SeqLaunch p) {
-  const int64_t seg = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte output segment
-  const int per_tok = p.H_qk * NS / 8;
-  const int64_t t = seg / per_tok;
-  if (t >= p.T) return;
-  const int r = (int)(seg % per_tok);
-  const int g = r / (NS / 8), c = r % (NS / 8);
-  const u16* src[2] = {reinterpret_cast<const u16*>(p.k), reinterpret_cast<const u16*>(p.q)};
-  const int64_t str[2] = {p.k_stride, p.q_stride};
-  u16* dst[2] = {const_cast<u16*>(p.ssd_Bh), const_cast<u16*>(p.ssd_Ch)};
+  __shared__ __attribute__((aligned(16))) u16 sC[CS * NS], sB[CS * NS];
+  const int q = blockIdx.x, g = blockIdx.y;
+  // the sequence whose chunk has slot q: the last s with cb_slot_base(tbeg_s, s) <= q
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cb_slot_base(p.cu_seqlens[mid], mid) <= q) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo, tbeg = p.cu_seqlens[s], len = p.cu_seqlens[s + 1] - tbeg;
+  const int64_t c = q - cb_slot_base(tbeg, s);
+  if (p.slot[s] < 0 || c < 0 || c * CS >= len) return;   // a slot no chunk has, or a skipped sequence
+  const int t0 = tbeg + (int)c * CS, n = min(CS, len - (int)c * CS);
+  const int tid = threadIdx.x;
+  const u16* kin = reinterpret_cast<const u16*>(p.k) + (int64_t)g * NS;
+  const u16* qin = reinterpret_cast<const u16*>(p.q) + (int64_t)g * NS;
+  u16* bout = const_cast<u16*>(p.ssd_Bh) + (int64_t)g * NS;
+  u16* cout = const_cast<u16*>(p.ssd_Ch) + (int64_t)g * NS;
+  const int64_t rs = (int64_t)p.H_qk * NS;
+  // 128 rows x 16 segments of 16 bytes per tile: 8 per thread and tile
+  uint4 wb[8], wc[8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint4 w = *reinterpret_cast<const uint4*>(src[k] + t * str[k] + (int64_t)g * NS + 8 * c);
-    *reinterpret_cast<uint4*>(dst[k] + (t * p.H_qk + g) * NS + 8 * c) =
-        make_uint4(cvt2h(bf_lo(w.x), bf_hi(w.x)), cvt2h(bf_lo(w.y), bf_hi(w.y)),
-                   cvt2h(bf_lo(w.z), bf_hi(w.z)), cvt2h(bf_lo(w.w), bf_hi(w.w)));
+  for (int i = 0; i < 8; ++i) {
+    const int sidx = tid + 256 * i, r = sidx >> 4, cs = sidx & 15;
+    const int64_t t = t0 + (r < n ? r : 0);
+    wb[i] = *reinterpret_cast<const uint4*>(kin + t * p.k_stride + 8 * cs);
+    wc[i] = *reinterpret_cast<const uint4*>(qin + t * p.q_stride + 8 * cs);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int sidx = tid + 256 * i, r = sidx >> 4, cs = sidx & 15;
+    const uint4 hb = make_uint4(bf2h(wb[i].x), bf2h(wb[i].y), bf2h(wb[i].z), bf2h(wb[i].w));
+    const uint4 hc = make_uint4(bf2h(wc[i].x), bf2h(wc[i].y), bf2h(wc[i].z), bf2h(wc[i].w));
+    *reinterpret_cast<uint4*>(sB + qidx<NS>(r, 8 * cs)) = hb;
+    *reinterpret_cast<uint4*>(sC + qidx<NS>(r, 8 * cs)) = hc;
+    if (r < n) {
+      *reinterpret_cast<uint4*>(bout + (int64_t)(t0 + r) * rs + 8 * cs) = hb;
+      *reinterpret_cast<uint4*>(cout + (int64_t)(t0 + r) * rs + 8 * cs) = hc;
+    }
+  }
+  __syncthreads();
+  const int lane = tid % kWave, w = tid / kWave;
+  const int l32 = lane & 31, hh = lane >> 5;
+  u16* dst = const_cast<u16*>(p.ssd_CB) + ((int64_t)q * p.H_qk + g) * (int64_t)(kCBTiles * kCBTileElems) + 16 * lane;
+  for (int t = w; t < kCBTiles; t += 4) {
+    const int ti = t < 6 ? offdiag_i(t) : t - 6, tm = t < 6 ? offdiag_m(t) : t - 6;
+    f32x16 acc = {};
+#pragma unroll
+    for (int k = 0; k < NS / 16; ++k) {
+      const f16x8 a = as_f16x8(__builtin_bit_cast(uint4, ldq8<NS>(sB, 32 * tm + l32, 16 * k + 8 * hh)));
+      const f16x8 b = as_f16x8(__builtin_bit_cast(uint4, ldq8<NS>(sC, 32 * ti + l32, 16 * k + 8 * hh)));
+      acc = mfma32h(a, b, acc);
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = cvt2h(acc[2 * k], acc[2 * k + 1]);
+    *reinterpret_cast<uint4*>(dst + t * kCBTileElems) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + t * kCBTileElems + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
 template <typename OutT, bool kGate, bool kCk>
 hipError_t launch_ssd_typed(const SeqLaunch& p, hipStream_t stream) {
-  const int64_t segs16 = p.T * p.H_qk * (NS / 8);
-  if (segs16 > 0) {
-    hipLaunchKernelGGL(ssd_prep_kernel, dim3((unsigned)((segs16 + 255) / 256)), dim3(256), 0, stream, p);
+  if (p.T > 0) {
+    hipLaunchKernelGGL(ssd_prep_kernel, dim3((unsigned)(p.T / CS + p.N), (unsigned)p.H_qk), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -698,23 +764,27 @@ hipError_t launch_ssd_ck(const SeqLaunch& p, hipStream_t stream) {
 }  // namespace
 
 // Workspace of a chunk-128 delta-off call with `segs` segments per sequence: the fp16
-// copies of B and C, then the segment states and log decays (segs - 1 per sequence).
+// copies of B and C, the raw C B^T tiles of every chunk slot, then the segment states
+// and log decays (segs - 1 per sequence).
 int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int segs) {
   auto up = [](int64_t b) { return (b + 255) & ~int64_t(255); };
   const int64_t bc = up(T * H_qk * NS * 2);
+  const int64_t cb = up((T / CS + N) * H_qk * kCBTiles * kCBTileElems * 2);
   const int64_t r = up((int64_t)N * (segs - 1) * H_v * PH * NS * 4);
   const int64_t l = up((int64_t)N * (segs - 1) * H_v * 4);
-  return 2 * bc + r + l;
+  return 2 * bc + cb + r + l;
 }
 
 void ssd_bind_workspace(SeqLaunch& p, void* ws) {
   auto up = [](int64_t b) { return (b + 255) & ~int64_t(255); };
   char* base = static_cast<char*>(ws);
   const int64_t bc = up(p.T * p.H_qk * NS * 2);
+  const int64_t cb = up((p.T / CS + p.N) * p.H_qk * kCBTiles * kCBTileElems * 2);
   p.ssd_Bh = reinterpret_cast<const u16*>(base);
   p.ssd_Ch = reinterpret_cast<const u16*>(base + bc);
-  p.segR = reinterpret_cast<float*>(base + 2 * bc);
-  p.segL = reinterpret_cast<float*>(base + 2 * bc + up((int64_t)p.N * (p.ssd_segs - 1) * p.H_v * PH * NS * 4));
+  p.ssd_CB = reinterpret_cast<const u16*>(base + 2 * bc);
+  p.segR = reinterpret_cast<float*>(base + 2 * bc + cb);
+  p.segL = reinterpret_cast<float*>(base + 2 * bc + cb + up((int64_t)p.N * (p.ssd_segs - 1) * p.H_v * PH * NS * 4));
 }
 
 bool ssd_chunked_shape(const SeqLaunch& p) { return p.ssd && p.d_k == NS && p.d_v == PH; }

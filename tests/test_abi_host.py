@@ -179,15 +179,18 @@ def test_ssd_kernel_choice_and_workspace():
     lib = gdn.load()
     a = _ssd()
     need = lib.gdn_extend_workspace_size(ct.byref(a), None)
-    # fp16 B and C copies (16384 x 128 x 2 bytes each) plus segment states of 64 KiB...
+    # fp16 B and C copies (16384 x 128 x 2 bytes each), the raw C B^T tiles of the
+    # 16384 / 128 + 2 chunk slots (ten 32 x 32 fp16 tiles each), plus segment states
     bc = 16384 * 128 * 2
-    assert need > 2 * bc and (need - 2 * bc) % 256 == 0
+    cb = (16384 // 128 + 2) * 10 * 32 * 32 * 2
+    one = 2 * bc + cb                                                          # one segment's workspace
+    assert need > one and (need - one) % 256 == 0
     assert _kernel(a) == (_lib.GDN_KERNEL_CHUNKED, W["no_workspace"])          # chunk 64 without it
     a.workspace, a.workspace_bytes = ct.c_void_p(0x1000000), need
     assert _kernel(a) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
-    a.workspace_bytes = 2 * bc                                                 # one segment still fits
+    a.workspace_bytes = one                                                    # one segment still fits
     assert _kernel(a) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
-    a.workspace_bytes = 2 * bc - 256                                           # too small: chunk 64
+    a.workspace_bytes = one - 256                                              # too small: chunk 64
     assert _kernel(a) == (_lib.GDN_KERNEL_CHUNKED, W["no_workspace"])
     a.chunk = 128                                                              # ... unless 128 is asked for
     assert _kernel(a)[0] == -_lib.GDN_E_SHAPE
@@ -210,11 +213,12 @@ def test_ssd_kernel_choice_and_workspace():
 
 def test_ssd_workspace_grows_with_segments_and_unknown_length_needs_one():
     """Without a length hint the kernel runs one segment per sequence: the workspace holds
-    only the B and C copies.  With the hint, the segment states come on top."""
+    only the B and C copies and the chunks' raw C B^T tiles.  With the hint, the segment
+    states come on top."""
     lib = gdn.load()
     a = _ssd(max_seqlen=0)
     one = lib.gdn_extend_workspace_size(ct.byref(a), None)
-    assert one == 2 * 16384 * 128 * 2
+    assert one == 2 * 16384 * 128 * 2 + (16384 // 128 + 2) * 10 * 32 * 32 * 2
     a.max_seqlen = 8192
     assert lib.gdn_extend_workspace_size(ct.byref(a), None) > one
 
@@ -234,7 +238,7 @@ def test_extend_noalloc_host_checks_come_before_any_device_call():
     assert lib.gdn_extend_noalloc(ct.byref(_ext(H_v=3)), None, None) == _lib.GDN_E_SHAPE
     assert lib.gdn_extend_noalloc(ct.byref(_ext(N=0)), None, None) == _lib.GDN_OK   # nothing to do
     limit = 64 << 20
-    # B and C copies: 2 x T x H_qk x 128 x 2 bytes at one segment
+    # B and C copies alone: 2 x T x H_qk x 128 x 2 bytes at one segment
     T = limit // (2 * 128 * 2) + 256
     big = _ssd(T=T, max_seqlen=0, N=2)
     assert lib.gdn_extend_workspace_size(ct.byref(big), None) > limit

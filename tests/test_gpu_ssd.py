@@ -156,14 +156,16 @@ def test_ssd_chunk128_workspace_sizes(gdn_lib, ws):
     lens = (1000, 600)
     c = _ragged_case(29, lens)
     pool = torch.zeros((2, 6, 64, 128), dtype=torch.float32, device="cuda")
-    need = 2 * sum(lens) * 2 * 128 * 2                      # fp16 B and C copies, G = 2
+    # one segment per sequence: fp16 B and C copies and the raw C B^T tiles of the
+    # T / 128 + N chunk slots (ten 32 x 32 fp16 tiles per slot and group), G = 2
+    need = 2 * sum(lens) * 2 * 128 * 2 + (sum(lens) // 128 + 2) * 2 * 10 * 32 * 32 * 2
     if ws == "full":
         cu = torch.tensor([0, 1000, 1600], dtype=torch.int32, device="cuda")
         g = gdn.ssd_gate_inputs(_tb(c.dt[0]), _tf(c.A), _tf(c.dt_bias), True, (0.0, float("inf")))
         need = gdn.extend_workspace_size(_tb(c.C[0]), _tb(c.B[0]), _tb(c.x[0]), None, None, cu,
                                          torch.tensor([0, 1], dtype=torch.int32, device="cuda"), pool,
                                          mode="ssd", max_seqlen=1000, gate=g, D=_tb(c.D), z=_tb(c.z[0]))
-        assert need > 2 * sum(lens) * 2 * 128 * 2
+        assert need > 2 * sum(lens) * 2 * 128 * 2 + (sum(lens) // 128 + 2) * 2 * 10 * 32 * 32 * 2
     workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
     out, kern = _run_extend(c, lens, slot=[0, 1], has_init=[0, 0], pool=pool, max_seqlen=1000,
                             workspace=workspace, gdn=gdn)
