@@ -392,10 +392,30 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   auto update = [&](f32x4* acc, float gamma, const f16x8* W) __attribute__((always_inline)) {
 #pragma unroll
     for (int tk = 0; tk < 8; ++tk) acc[tk] = acc[tk] * gamma;
+    if constexpr (!kFull) {
+      // state-only pass (registers to spare): one k step's eight B^T operands are read
+      // while the previous step's MFMAs run (sched_barrier keeps the compiler from
+      // pairing each read with its MFMA)
+      f16x8 a[2][8];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
+      for (int tk = 0; tk < 8; ++tk) a[0][tk] = bt_op(tk, 0);
 #pragma unroll
-      for (int tk = 0; tk < 8; ++tk) acc[tk] = mfma1632h(bt_op(tk, s2), W[s2], acc[tk]);
+      for (int s2 = 0; s2 < 4; ++s2) {
+        if (s2 < 3) {
+#pragma unroll
+          for (int tk = 0; tk < 8; ++tk) a[(s2 + 1) & 1][tk] = bt_op(tk, s2 + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tk = 0; tk < 8; ++tk) acc[tk] = mfma1632h(a[s2 & 1][tk], W[s2], acc[tk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int tk = 0; tk < 8; ++tk) acc[tk] = mfma1632h(bt_op(tk, s2), W[s2], acc[tk]);
+    }
   };
 
   // landing of the staged rows: C, B as they are, x converted to fp16
