@@ -124,12 +124,15 @@ typedef struct gdn_gate_args {
  *   chunk, SSD mode : 64, 128 or 0 (default: 128 when the call can take it, else 64).
  *     The chunk-128 delta-off kernel (d_k = dstate = 128, d_v = headdim = 64, the
  *     ssd_combined_fwd chunk size) needs a caller workspace: fp16 copies of B and C
- *     (every head of a group reads them) and, to run the segments of a sequence in
- *     parallel, their states.  gdn_extend_workspace_size() gives the bytes it wants;
+ *     and the chunks' C B^T tiles (every head of a group reads them) and, to run the
+ *     segments of a sequence in parallel, their states.  gdn_extend_workspace_size() gives the bytes it wants;
  *     a smaller workspace (at least the size for one segment) means fewer segments,
  *     i.e. speed only.  chunk = 128 without a usable workspace: GDN_E_NULL (none) or
  *     GDN_E_SHAPE (too small for one segment).  Its fp16 operands need |C.B|, |dt' x|
- *     and the state below 65504 (beyond that the outputs turn inf / NaN).
+ *     and the state below 65504 (beyond that the outputs turn inf / NaN).  It reads z
+ *     and writes out in 16-byte pieces: with z or out not 16-byte aligned, or a row
+ *     stride of either that is not a multiple of 16 bytes, chunk 0 takes the chunk-64
+ *     kernel and chunk 128 returns GDN_E_UNSUPPORTED.
  *
  * State checkpoints (optional; the checkpoint_token_indices / checkpoint_state_slots
  * / checkpoint_states arguments of the ssd_combined_fwd page, in both modes):
@@ -211,8 +214,9 @@ typedef struct gdn_extend_args {
 } gdn_extend_args;
 
 /* Workspace bytes the chunk-128 delta-off kernel wants for a gdn_extend (gate NULL) or
- * gdn_extend_gated call with these arguments (fp16 B and C copies, and the states of
- * the segments the library would run: it grows with T and with N x H_v x segments), or
+ * gdn_extend_gated call with these arguments (fp16 B and C copies, the C B^T tiles of
+ * every chunk, and the states of the segments the library would run: it grows with T
+ * and with N x H_v x segments), or
  * 0 when the call would run another kernel or is invalid.  Host-side, launches nothing;
  * args->workspace / workspace_bytes are ignored.  The workspace must be 256-byte
  * aligned (else GDN_E_SHAPE) and is overwritten by the call (its contents need not be
@@ -308,9 +312,9 @@ int gdn_decode_gated(const gdn_decode_args* args, const gdn_gate_args* gate, voi
  * args->workspace, which must be NULL with workspace_bytes 0 (else GDN_E_SHAPE).  The
  * call allocates and frees nothing.
  *   - A call whose chunk-128 kernel needs more than the array holds at one segment per
- *     sequence (about T x H_qk > 131072 token-groups) returns GDN_E_SCRATCH and launches
- *     nothing; gdn_extend_gated with a workspace of gdn_extend_workspace_size bytes
- *     runs it.  A need between one segment's and gdn_extend_workspace_size's means
+ *     sequence (about T x H_qk > 99000 token-groups: 672 bytes per token and group)
+ *     returns GDN_E_SCRATCH and launches nothing; gdn_extend_gated with a workspace of
+ *     gdn_extend_workspace_size bytes runs it.  A need between one segment's and gdn_extend_workspace_size's means
  *     fewer segments per sequence (speed only).
  *   - The first call on a device, with that device current, resolves the device's copy
  *     of the array (a failure returns GDN_E_HIP); the copy stays allocated until the
