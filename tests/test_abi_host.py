@@ -211,6 +211,31 @@ def test_ssd_kernel_choice_and_workspace():
     assert lib.gdn_extend_workspace_size(ct.byref(_ext(**_ptrs())), None) == 0  # GDN mode: none
 
 
+def test_ssd_chunk128_needs_16_byte_rows_of_z_and_out():
+    """The chunk-128 delta-off kernel reads z and writes out as 16-byte pieces of whole
+    rows: an out pointer or row stride off 16 bytes sends chunk 0 to the chunk-64 kernel
+    (reason: alignment; a z off 16 bytes, which the chunk-64 kernel also stages in
+    16-byte segments, to the token-recurrent one) and makes chunk 128 unsupported."""
+    lib = gdn.load()
+    a = _ssd(z=ct.c_void_p(0x80000), z_stride=80 * 64)
+    a.workspace = ct.c_void_p(0x1000000)
+    a.workspace_bytes = lib.gdn_extend_workspace_size(ct.byref(a), None)
+    assert _kernel(a) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
+    for field, value, kernel in (("out_stride", 80 * 64 + 4, _lib.GDN_KERNEL_CHUNKED),
+                                 ("out", ct.c_void_p(0x70008), _lib.GDN_KERNEL_CHUNKED),
+                                 ("z_stride", 80 * 64 + 4, _lib.GDN_KERNEL_RECURRENT),
+                                 ("z", ct.c_void_p(0x80008), _lib.GDN_KERNEL_RECURRENT)):
+        b = _ssd(z=ct.c_void_p(0x80000), z_stride=80 * 64, workspace=a.workspace,
+                 workspace_bytes=a.workspace_bytes)
+        setattr(b, field, value)
+        assert _kernel(b) == (kernel, W["alignment"]), field
+        b.chunk = 128
+        assert _kernel(b)[0] == -_lib.GDN_E_UNSUPPORTED, field
+    f = _ssd(out_dtype=0, out_stride=80 * 64 + 4, workspace=a.workspace,   # fp32 out: 16-byte rows
+             workspace_bytes=a.workspace_bytes)
+    assert _kernel(f) == (_lib.GDN_KERNEL_SSD_CHUNKED, 0)
+
+
 def test_ssd_workspace_grows_with_segments_and_unknown_length_needs_one():
     """Without a length hint the kernel runs one segment per sequence: the workspace holds
     only the B and C copies and the chunks' raw C B^T tiles.  With the hint, the segment
