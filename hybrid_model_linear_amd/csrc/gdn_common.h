@@ -101,11 +101,24 @@ __device__ __forceinline__ void gate_ssd(float dt, float A, float dt_bias, int s
 }
 
 // ------------------------------------------------------------------ wave reductions
-// Sum over aligned groups of W lanes (W a power of two <= 64).
+// Sum over aligned groups of W lanes (W a power of two <= 64), in every lane of the
+// group; every lane of the wave must be active.  Within a row of 16 lanes by DPP
+// moves (swaps within pairs and quads, then the half-row and row mirrors: each step
+// adds a lane whose partial sum covers the other half of the span), across rows by
+// lane permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "a power of two <= 64");
+  if constexpr (W >= 2) v += dpp_row<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) v += dpp_row<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) v += dpp_row<0x141>(v);   // row_half_mirror (lane i <- 7 - i within 8)
+  if constexpr (W >= 16) v += dpp_row<0x140>(v);  // row_mirror (lane i <- 15 - i)
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

@@ -57,7 +57,7 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-template <int DK, int DV, typename InT, typename OutT, bool kSSD, bool kAux>
+template <int DK, int DV, typename InT, typename OutT, bool kSSD, bool kAux, int kPre>
 __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   using L = RecLayout<DK>;
   const int lane = threadIdx.x % kWave;
@@ -123,8 +123,47 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   const InT* kb = reinterpret_cast<const InT*>(p.k);
   const InT* vb = reinterpret_cast<const InT*>(p.v);
   OutT* ob = reinterpret_cast<OutT*>(p.out);
+  // delta-off D of this lane's rows (constant over the tokens)
+  float Dr[kRowSteps];
+#pragma unroll
+  for (int s = 0; s < kRowSteps; ++s) {
+    Dr[s] = 0.f;
+    if (kSSD && p.D) {
+      const int row = row0 + s * L::kRowsPerStep;
+      Dr[s] = Elem<InT>::load(reinterpret_cast<const InT*>(p.D), p.D_per_dim ? (int64_t)h * DV + row : (int64_t)h);
+    }
+  }
 
-  for (int t = t0; t < t1; ++t) {
+  // A token's inputs: this lane's columns of k and q, its rows' v (and z), the gate's
+  // inputs (raw a, b / dt with the gate folded in, else log g and beta).
+  struct Tok {
+    float4 k, q;
+    float v[kRowSteps], z[kRowSteps];
+    float a, b;
+  };
+  auto load_tok = [&](int t, Tok& in) __attribute__((always_inline)) {
+    in.k = load4<InT>(kb + (int64_t)t * p.k_stride + (int64_t)j * DK + 4 * c);
+    in.q = load4<InT>(qb + (int64_t)t * p.q_stride + (int64_t)j * DK + 4 * c);
+    const int64_t vrow = (int64_t)t * p.v_stride + (int64_t)h * DV;
+#pragma unroll
+    for (int s = 0; s < kRowSteps; ++s) {
+      const int row = row0 + s * L::kRowsPerStep;
+      in.v[s] = Elem<InT>::load(vb, vrow + row);
+      in.z[s] = 0.f;
+      if (kSSD && p.z)
+        in.z[s] = Elem<InT>::load(reinterpret_cast<const InT*>(p.z), (int64_t)t * p.z_stride + (int64_t)h * DV + row);
+    }
+    if (p.gate_fused) {   // (uniform branch)
+      in.a = Elem<InT>::load(reinterpret_cast<const InT*>(p.ga), (int64_t)t * p.ga_stride + h);
+      in.b = kSSD ? 0.f : Elem<InT>::load(reinterpret_cast<const InT*>(p.gb), (int64_t)t * p.gb_stride + h);
+    } else {
+      const int64_t gi = (int64_t)t * p.H_v + h;
+      in.a = p.log_g[gi];
+      in.b = p.beta[gi];
+    }
+  };
+
+  auto step = [&](int t, const Tok& in) __attribute__((always_inline)) {
     if (kAux && p.sp_parent && spr) {   // token tree (uniform branch)
       // a parent outside [0, i) (i = the token's index in its sequence) or past the
       // recorded steps counts as -1: only rows this thread wrote earlier are read
@@ -138,8 +177,7 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
           st[s] = *reinterpret_cast<const float4*>(spr + par * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c);
       }
     }
-    float4 kv = load4<InT>(kb + (int64_t)t * p.k_stride + (int64_t)j * DK + 4 * c);
-    float4 qv = load4<InT>(qb + (int64_t)t * p.q_stride + (int64_t)j * DK + 4 * c);
+    float4 kv = in.k, qv = in.q;
     if constexpr (!kSSD) {
       const float nk = group_sum<L::kLanesPerRow>(dot4(kv, kv));
       const float nq = group_sum<L::kLanesPerRow>(dot4(qv, qv));
@@ -151,25 +189,21 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     const float kq = group_sum<L::kLanesPerRow>(dot4(kv, qv));
     float lg, bt;
     if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
-      const float x = Elem<InT>::load(reinterpret_cast<const InT*>(p.ga), (int64_t)t * p.ga_stride + h);
       const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
       if constexpr (kSSD)
-        gate_ssd(x, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
+        gate_ssd(in.a, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
       else
-        gate_gdn(x, Elem<InT>::load(reinterpret_cast<const InT*>(p.gb), (int64_t)t * p.gb_stride + h),
-                 expf(p.gA[h]), bias, lg, bt);
+        gate_gdn(in.a, in.b, expf(p.gA[h]), bias, lg, bt);
     } else {
-      const int64_t gi = (int64_t)t * p.H_v + h;
-      lg = p.log_g[gi];
-      bt = p.beta[gi];
+      lg = in.a;
+      bt = in.b;
     }
     const float g = __expf(lg);
-    const int64_t vrow = (int64_t)t * p.v_stride + (int64_t)h * DV;
     const int64_t orow = (int64_t)t * p.out_stride + (int64_t)h * DV;
 #pragma unroll
     for (int s = 0; s < kRowSteps; ++s) {
       const int row = row0 + s * L::kRowsPerStep;
-      const float vr = Elem<InT>::load(vb, vrow + row);
+      const float vr = in.v[s];
       const float y = group_sum<L::kLanesPerRow>(dot4(st[s], qv));
       float u, o;
       if constexpr (kSSD) {
@@ -185,15 +219,8 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       st[s].z = g * st[s].z + u * kv.z;
       st[s].w = g * st[s].w + u * kv.w;
       if constexpr (kSSD) {
-        if (p.D) {
-          const InT* Db = reinterpret_cast<const InT*>(p.D);
-          o += Elem<InT>::load(Db, p.D_per_dim ? (int64_t)h * DV + row : (int64_t)h) * vr;
-        }
-        if (p.z) {
-          const float zz = Elem<InT>::load(reinterpret_cast<const InT*>(p.z),
-                                           (int64_t)t * p.z_stride + (int64_t)h * DV + row);
-          o *= zz * sigmoid_f(zz);
-        }
+        o += Dr[s] * vr;
+        if (p.z) o *= in.z[s] * sigmoid_f(in.z[s]);
       }
       if (c == 0) Elem<OutT>::store(ob, orow + row, o);
     }
@@ -203,6 +230,23 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       for (int s = 0; s < kRowSteps; ++s)
         *reinterpret_cast<float4*>(spr + (t - t0) * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
     }
+  };
+
+  // The first kPre tokens' inputs are loaded together (issued right after the state's
+  // loads), so that a short extend (a verify batch) waits for memory once rather than
+  // once per token; later tokens load as they come.  (A decode step, one token per
+  // sequence, takes kPre = 1: registers for more would cost occupancy.)
+  Tok pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    if (t0 + i < t1) load_tok(t0 + i, pre[i]);
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    if (t0 + i < t1) step(t0 + i, pre[i]);
+  for (int t = t0 + kPre; t < t1; ++t) {
+    Tok in;
+    load_tok(t, in);
+    step(t, in);
   }
   if (p.keep_pool) return;
 #pragma unroll
@@ -218,11 +262,18 @@ hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
   static_assert(DV % L::kRowsPerBlock == 0, "d_v must be a multiple of the rows per block");
   dim3 grid(DV / L::kRowsPerBlock, p.H_v, p.N), block(kThreads);
   // checkpoints and target-verify states are a separate instantiation: the decode
-  // step runs none of their code
-  if (p.ck_token || p.sp_states)
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true>), grid, block, 0, stream, p);
+  // step runs none of their code; short extends (at most 8 tokens per sequence by the
+  // host's hint) load their first 4 tokens' inputs up front
+  const bool aux = p.ck_token || p.sp_states;
+  const bool shrt = p.max_seqlen > 1 && p.max_seqlen <= 8;
+  if (aux && shrt)
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 4>), grid, block, 0, stream, p);
+  else if (aux)
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 1>), grid, block, 0, stream, p);
+  else if (shrt)
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 4>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 1>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
