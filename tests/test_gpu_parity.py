@@ -196,6 +196,39 @@ def test_extend_edges(gdn_lib, name, lens, has_init, out_dtype):
     assert torch.equal(d["pool"][untouched], pool_before[untouched]), "untouched slots changed"
 
 
+SHORT = [
+    ("short-tails", (8, 5, 1, 4, 0, 7, 3), 8),      # past the four tokens loaded up front
+    ("short-wrong-hint", (4, 9, 2, 6), 4),          # a hint below the longest sequence
+]
+
+
+@pytest.mark.parametrize("name,lens,hint", SHORT, ids=[e[0] for e in SHORT])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_short_extend_token_recurrent(gdn_lib, name, lens, hint, out_dtype):
+    """Short extends (host hint <= 8 tokens) take the token-recurrent kernel that loads
+    its first four tokens' inputs with the state: sequences longer than four (and longer
+    than the hint) continue token by token; outputs and states against the oracle."""
+    gdn = gdn_lib
+    _announce(f"short extend {name} out={out_dtype}")
+    case = synth.edge_case(name, lens, has_init=(1,) * len(lens), seed=sum(lens) + 11,
+                           num_slots=len(lens) + 3)
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    assert gdn.extend_kernel(q, k, v, lg, bt, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                             scale=case.scale, max_seqlen=hint)[0] == "recurrent"
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = run_extend(gdn, case, d, out_dtype=odt, max_seqlen=hint)
+    torch.cuda.synchronize()
+    ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
+                                          case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
+                                          case.pool, case.scale)
+    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (1e-3, 2e-3)
+    assert_close(out.float().cpu().numpy(), ref, "out", *bar)
+    newpool = oracle.apply_final_states(case.pool, fin)
+    assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", 1e-3, 1e-2)
+
+
 def test_skipped_sequences_and_sentinels(gdn_lib):
     gdn = gdn_lib
     _announce("skipped sequences")

@@ -146,6 +146,30 @@ def test_ssd_chunk128_skipped_rows_keep_sentinel(gdn_lib):
     assert_close(out[350:].float().cpu().numpy(), ref, "seq 2 out", peak_rel=True)
 
 
+def test_ssd_short_extend_token_recurrent(gdn_lib):
+    """Short delta-off extends (host hint 8) take the token-recurrent kernel, which loads
+    the first four tokens' inputs with the state and continues token by token past
+    them: outputs and final states from random initial states against the oracle."""
+    gdn = gdn_lib
+    _announce("ssd short extend (token-recurrent)")
+    lens = (6, 3, 8, 1, 0, 5)
+    c = _ragged_case(41, lens, H=4, G=1)
+    rng = np.random.default_rng(41)
+    init = rng.standard_normal((len(lens), 4, 64, 128)).astype(np.float32)
+    pool = torch.from_numpy(init.copy()).cuda()
+    out, kern = _run_extend(c, lens, slot=list(range(len(lens))), has_init=[1] * len(lens), pool=pool,
+                            max_seqlen=8, gdn=gdn)
+    torch.cuda.synchronize()
+    assert kern[0] == "recurrent", kern
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    got, st = out.float().cpu().numpy(), pool.cpu().numpy()
+    for n in range(len(lens)):
+        ref, fin, _ = _oracle_seq(c, lens, n, init[n])
+        if lens[n]:
+            assert_close(got[cu[n]:cu[n + 1]], ref, f"seq {n} out", peak_rel=True)
+        assert_close(st[n], fin, f"seq {n} state", peak_rel=True)
+
+
 @pytest.mark.parametrize("ws", ["full", "one_segment"])
 def test_ssd_chunk128_workspace_sizes(gdn_lib, ws):
     """A caller-given workspace: the size the library asks for (several segments) and the
