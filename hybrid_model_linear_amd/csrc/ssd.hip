@@ -347,16 +347,18 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const float incl = wave_inclusive_scan(lg0 + lg1);      // G at token 2 l + 1
     const float G1 = incl, G0 = incl - lg1;
     const float GC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), kWave - 1));
-    // G at the last token of this lane's 32-token block (token 32 q + 31: lane 16 q + 15)
-    const int blk_lane = (lane & ~15) | 15;
-    const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * blk_lane, __builtin_bit_cast(int, incl)));
-    V.G2[i0] = G0 * kLog2e;
-    V.G2[i1] = G1 * kLog2e;
-    V.eG[i0] = __expf(G0);
-    V.eG[i1] = __expf(G1);
-    *reinterpret_cast<uint32_t*>(&V.dtp[i0]) = cvt2h(d0, d1);
     *reinterpret_cast<uint32_t*>(&V.wfac[i0]) = cvt2h(__expf(GC - G0) * d0, __expf(GC - G1) * d1);
-    *reinterpret_cast<uint32_t*>(&V.ufac[i0]) = cvt2h(__expf(Gr - G0) * d0, __expf(Gr - G1) * d1);
+    if constexpr (kFull) {   // (the state-only pass needs the update's weights and e^{G_C} only)
+      // G at the last token of this lane's 32-token block (token 32 q + 31: lane 16 q + 15)
+      const int blk_lane = (lane & ~15) | 15;
+      const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * blk_lane, __builtin_bit_cast(int, incl)));
+      V.G2[i0] = G0 * kLog2e;
+      V.G2[i1] = G1 * kLog2e;
+      V.eG[i0] = __expf(G0);
+      V.eG[i1] = __expf(G1);
+      *reinterpret_cast<uint32_t*>(&V.dtp[i0]) = cvt2h(d0, d1);
+      *reinterpret_cast<uint32_t*>(&V.ufac[i0]) = cvt2h(__expf(Gr - G0) * d0, __expf(Gr - G1) * d1);
+    }
     if (lane == 0) {
       V.gC[0] = __expf(GC);
       V.gC[1] = GC;
