@@ -18,18 +18,23 @@
 // and the full pass of segment s starts from S_in(s), folded from the segments before
 // it (S <- e^{Lambda_s'} S + R_s', s' < s).
 //
-// A workgroup takes two heads of one group (they share B, C and C B^T) for one segment
-// of one sequence: grid (group x head pair, sequence x segment).  Wave w owns the
-// state columns p = 16 pt .. 16 pt + 15 (pt = w % 4) of head slot w / 4 over all of N:
-// eight 16x16 accumulator tiles of S^T in registers.  Per chunk:
-//   * landing: the chunk's fp16 C and B rows (converted once per call into the
-//     workspace) and both heads' x rows (as fp16) into LDS;
-//   * the C B^T tiles of the chunk (32x32x16 MFMA): each wave the diagonal 32x32 tile
-//     of its head slot, masked and decayed into that head's P; six waves one raw
-//     off-diagonal tile each (shared by both heads); two waves prepare the next
-//     chunk's gate, decay cumsum and per-token factors, one head each;
+// Once per call, per chunk and group (every head of the group shares them), a prep
+// kernel converts the chunk's B and C rows to fp16 and computes the chunk's raw C B^T
+// tiles on and below the diagonal (32x32x16 MFMA), both kept in the workspace.
+//
+// A workgroup takes two heads of one group for one segment of one sequence: grid
+// (group x head pair, sequence x segment).  Wave w owns the state columns
+// p = 16 pt .. 16 pt + 15 (pt = w % 4) of head slot w / 4 over all of N: eight 16x16
+// accumulator tiles of S^T in registers.  Per chunk:
+//   * landing: the chunk's fp16 C and B rows and both heads' x rows (as fp16) into LDS,
+//     with the chunk's z rows and this wave's raw C B^T tiles loaded alongside; two
+//     waves prepare the next chunk's gate, decay cumsum and per-token factors, one
+//     head each;
 //   * Y^T = S0 C^T diag(e^G) for the 128 tokens, then S^T <- e^{G_C} S^T +
 //     B^T diag(e^{G_C - G} dt') X;
+//   * the LDS tiles from the raw ones: each wave the diagonal 32x32 tile pt of its
+//     head's P (masked, decayed), waves 0-5 one off-diagonal tile each (shared by both
+//     heads);
 //   * the intra-chunk term: the diagonal 32-token blocks from the head's P, every
 //     earlier block from the raw C B^T tile with the decay factored at the block's last
 //     token r, e^{G_i - G_m} = e^{G_i - G_r} e^{G_r - G_m} (both <= 1: the key factor
@@ -38,7 +43,8 @@
 //     that each thread finishes (y + D x) silu(z) for 8 columns of a token row, with z
 //     read and the output written in whole 128-byte rows.
 // The chunk's C, B and x rows are staged from memory through registers one chunk
-// ahead.  Operand precision: C, B, x exact in fp16 (bf16 values in fp16's normal
+// ahead.  The state-only pass (segment states from zero) runs the same loop with B, x
+// and the update alone.  Operand precision: C, B, x exact in fp16 (bf16 values in fp16's normal
 // range); S0, P and the scaled X carry fp16's 11-bit significand (2^-12 relative
 // rounding, well below the bf16 output's); every product accumulates in fp32.  fp16's
 // range bounds the magnitudes: |C.B|, |x|, |dt' x| and |S| must stay below 65504
