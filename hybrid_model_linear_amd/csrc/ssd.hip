@@ -295,22 +295,28 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const uint32_t off = ((uint32_t)(r < n ? r : 0) * (uint32_t)p.v_stride + 8u * (uint32_t)c) * 2u;
     return *reinterpret_cast<const uint4*>(base + off);
   };
-  auto stage = [&](SsdStage& r, int cc) __attribute__((always_inline)) {
+  // parts: kStC | kStB | kStX (a constant at every call)
+  enum { kStC = 1, kStB = 2, kStX = 4, kStAll = 7 };
+  auto stage = [&](SsdStage& r, int cc, int parts) __attribute__((always_inline)) {
     const int t0 = tbeg + cc * CS, n = min(CS, tend - t0);
-    if constexpr (kFull) {
+    if (kFull && (parts & kStC)) {
       r.c0 = ld_cb(Cg, t0, n, 0);
       r.c1 = ld_cb(Cg, t0, n, 1);
       r.c2 = ld_cb(Cg, t0, n, 2);
       r.c3 = ld_cb(Cg, t0, n, 3);
     }
-    r.b0 = ld_cb(Bg, t0, n, 0);
-    r.b1 = ld_cb(Bg, t0, n, 1);
-    r.b2 = ld_cb(Bg, t0, n, 2);
-    r.b3 = ld_cb(Bg, t0, n, 3);
-    r.x0 = ld_x(t0, n, 0);
-    r.x1 = ld_x(t0, n, 1);
-    r.x2 = ld_x(t0, n, 2);
-    r.x3 = ld_x(t0, n, 3);
+    if (parts & kStB) {
+      r.b0 = ld_cb(Bg, t0, n, 0);
+      r.b1 = ld_cb(Bg, t0, n, 1);
+      r.b2 = ld_cb(Bg, t0, n, 2);
+      r.b3 = ld_cb(Bg, t0, n, 3);
+    }
+    if (parts & kStX) {
+      r.x0 = ld_x(t0, n, 0);
+      r.x1 = ld_x(t0, n, 1);
+      r.x2 = ld_x(t0, n, 2);
+      r.x3 = ld_x(t0, n, 3);
+    }
   };
   // raw gate inputs of one chunk for a vector wave (lane l: tokens 2 l, 2 l + 1), kept
   // as loaded until their use a step later (an instruction on a loaded value makes the
@@ -520,7 +526,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
 
   // ---------------------------------------------------------------- chunk loop
   if (c0 < c1) {
-    stage(rs0, c0);
+    stage(rs0, c0, kStAll);
     if (vwave) stage_gate(c0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
@@ -538,10 +544,10 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     const int t0 = tbeg + c * CS, n = min(CS, tend - t0);
     lds_sync();                              // the previous chunk's LDS reads are done
     land(rs0);
-    // the epilogue's z of this chunk (its four slices), issued before the next chunk's
-    // staging so that their use waits for them only
+    // the epilogue's z of this chunk (its four slices), loaded after Y (the update, the
+    // tiles and the intra-chunk term cover their latency)
     uint4 ez0, ez1, ez2, ez3;
-    if constexpr (kFull) {
+    auto load_z = [&]() __attribute__((always_inline)) {
       const char* zb = reinterpret_cast<const char*>(zg + (int64_t)t0 * (zs_b / 2));
       auto ldz = [&](int i) __attribute__((always_inline)) {
         const int r = er + 64 * (i & 1);
@@ -549,12 +555,18 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
         return *reinterpret_cast<const uint4*>(zb + (uint32_t)(r < n ? r : 0) * zs_b + 2u * col);
       };
       ez0 = ldz(0); ez1 = ldz(1); ez2 = ldz(2); ez3 = ldz(3);
-    }
+    };
     // this chunk's raw C B^T tiles (made into LDS tiles after the update; with
     // checkpoints, loaded after the in-chunk checkpoint, whose registers they would add to)
     uint4 td0, td1, to0 = {}, to1 = {};
     if constexpr (!kCk) load_tiles(c, td0, td1, to0, to1);
-    stage(rs0, min(c + 1, c1 - 1));          // (unconditional: past the last chunk it re-reads it)
+    // The next chunk's rows (staging loads are unconditional: past the last chunk they
+    // re-read it).  The full pass spreads them over the step -- C rows after Y, B rows
+    // after the tiles, x rows after the intra-chunk term -- so that the vector memory
+    // pipeline streams them while the waves compute: issued in one burst here they
+    // stalled every wave for ~3k cycles per chunk (about a seventh of the step).
+    const int cn = min(c + 1, c1 - 1);
+    if constexpr (!kFull) stage(rs0, cn, kStAll);
     lds_sync();                              // landing visible
     const float gamma = V.gC[0];
     if (vwave) {
@@ -576,6 +588,8 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
       }
 #pragma unroll
       for (int it = 0; it < 8; ++it) Y[it] = Y[it] * V.eG[16 * it + j16];
+      load_z();
+      stage(rs0, cn, kStC);
       // checkpoint inside the chunk, after its first m tokens:
       //   S_m^T = e^{G_{m-1}} S0^T + B^T diag(e^{G_{m-1} - G_i} dt'_i [i < m]) X
       if (kCk && ck_b > CS * c && ck_b < CS * c + n) {
@@ -612,6 +626,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
         update(Sacc, gamma, W);
       }
       make_tiles(V, td0, td1, to0, to1);
+      stage(rs0, cn, kStB);
       lds_sync();                            // P and C B^T tiles complete
       f16x8 xo[4];
 #pragma unroll
@@ -633,6 +648,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
       // epilogue: every wave's y tiles into Yx (C and B are no longer read in this
       // chunk), then per slice (y + D x) silu(z) in whole rows; rows past the sequence
       // end are dropped by the bounded buffer stores (record = the chunk's n rows)
+      stage(rs0, cn, kStX);
 #pragma unroll
       for (int it = 0; it < 8; ++it)
         *reinterpret_cast<f32x4*>(&sm.Yx[hs][yidx(16 * it + j16, 4 * pt + g16)]) = Y[it];
