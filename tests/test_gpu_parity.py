@@ -253,6 +253,49 @@ def test_skipped_sequences_and_sentinels(gdn_lib):
     assert_close(got[[4, 7]], np.stack([fin[4], fin[7]]), "states")
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_extend_many_sequences(gdn_lib, out_dtype):
+    """150 packed sequences (log-uniform lengths up to ~300, every 23rd empty, two
+    skipped, mixed initial states): more sequences than the longest-first ordering takes,
+    so workgroups follow the plain order with the qk-head pairs grouped per XCD; every
+    written row and state against the oracle, untouched slots and skipped rows
+    bit-exact."""
+    gdn = gdn_lib
+    _announce(f"extend many sequences out={out_dtype}")
+    rng = np.random.default_rng(8)
+    lens = np.exp(rng.uniform(0, np.log(300), 150)).astype(np.int64)
+    lens[::23] = 0
+    hi = (rng.random(150) < 0.6).astype(np.int32)
+    case = synth.edge_case("many", tuple(int(x) for x in lens), has_init=tuple(int(x) for x in hi), seed=77,
+                           H_qk=4, H_v=8, num_slots=160)
+    case.slot[[12, 99]] = -1
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    assert gdn.extend_kernel(q, k, v, lg, bt, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                             scale=case.scale)[0] == "chunked64"
+    pool_before = d["pool"].clone()
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.full((case.T, case.H_v, case.d_v), SENTINEL, dtype=odt, device="cuda")
+    out_before = out.clone()
+    run_extend(gdn, case, d, out=out)
+    torch.cuda.synchronize()
+    ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
+                                          case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
+                                          case.pool, case.scale)
+    bar = (2e-3, 1e-2) if out_dtype == "bf16" else (1e-3, 2e-3)
+    assert_close(out.float().cpu().numpy()[written], ref[written], "out", *bar)
+    skipped = torch.from_numpy(~written).cuda()
+    assert torch.equal(out[skipped].view(torch.int16 if out_dtype == "bf16" else torch.int32),
+                       out_before[skipped].view(torch.int16 if out_dtype == "bf16" else torch.int32)), \
+        "rows of skipped sequences were written"
+    used = case.slot[case.slot >= 0]
+    newpool = oracle.apply_final_states(case.pool, fin)
+    assert_close(d["pool"].cpu().numpy()[used], newpool[used], "states", *bar)
+    untouched = np.setdiff1d(np.arange(case.num_slots), used)
+    assert torch.equal(d["pool"][untouched], pool_before[untouched]), "untouched slots changed"
+
+
 @pytest.mark.parametrize("decay", [1e-2, 1e-3])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_extend_long_memory(gdn_lib, decay, out_dtype):
