@@ -318,8 +318,9 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
 
   // ================================================================ staging
   // Each role stages the raw rows it consumes: the producers Q, K (and the gate
-  // inputs) of chunk c + 2, issued right after the landing of step c; the state waves
-  // V (z) of chunk c + 1, issued in the middle of their step.  Both stay in flight in
+  // inputs) of chunk c + 2, issued right after the landing of step c (producer 2 right
+  // after its merge of T); the state waves V (z) of chunk c + 1, issued in the middle
+  // of their step.  Both stay in flight in
   // registers during step c.  Each role lands its rows right after the step's barrier
   // and announces them on its own arrival counter, so neither waits for the other's
   // landing: the producers wait for theirs before their first products, the state
@@ -1102,15 +1103,20 @@ __global__ void __launch_bounds__((DV / (16 * CT) + kNP) * kWave, 1) chunk_kerne
         }
       }
       arrive(&sSync[3]);
-      stage_qk(min(c + 2, nch - 1));
       if (wu - NSW == 2) {   // T of chunk c (delta rule only); reads nothing landed here
         if constexpr (!kSSD) {
           if constexpr (hasS) merge_T(Par<PAR>{});
         }
-        gate_store(PAR);       // (gate folded in) chunk c + 2, staged in this landing
-      } else if (hasP) {
-        wait_count(&sSync[3], (uint32_t)kNP * (uint32_t)(c + 2));   // the producers' landing of this step done
-        produce(c + 1, Par<PQ>{});
+        // (staged after the merge: issuing the loads first held T back by their issue
+        // time, while the state waves wait for it)
+        stage_qk(min(c + 2, nch - 1));
+        gate_store(PAR);       // (gate folded in) chunk c + 2, staged just above
+      } else {
+        stage_qk(min(c + 2, nch - 1));
+        if (hasP) {
+          wait_count(&sSync[3], (uint32_t)kNP * (uint32_t)(c + 2));   // the producers' landing of this step done
+          produce(c + 1, Par<PQ>{});
+        }
       }
     } else {
       // V, z of chunk c
