@@ -16,12 +16,17 @@
 // recorded steps: from the start state).
 //
 // Memory layout: the state row r of (slot, head) is 4*d_k contiguous bytes of the
-// pool [slot][head][d_v][d_k]; d_k/4 lanes own one row, each a float4 of it, so a
-// wave streams 64 * 16 B = 1 KiB per instruction, fully coalesced.  The state stays
-// in registers across the tokens of a sequence and is written back once.  Its loads
-// are non-temporal (each byte of the pool is read once per launch); the stores keep
-// the default policy (measured faster for an extend + decode step than streaming
-// them past the caches).
+// pool [slot][head][d_v][d_k].  A decode step (one token) gives a row to d_k/4 lanes,
+// each a float4 of it, so a wave streams 64 * 16 B = 1 KiB per instruction, fully
+// coalesced.  Short extends (a verify batch: a few tokens per sequence, where the
+// token loop's arithmetic rather than the state's traffic sets the time) give a row
+// to 16 lanes, each d_k/64 float4 of it (columns 4 (c + 16 f)): the per-row sums then
+// take four lane steps instead of five (no cross-row permute), and the per-token work
+// every wave repeats (the norms, q.k, the gate) is shared by twice the rows.  The
+// state stays in registers across the tokens of a sequence and is written back once.
+// Its loads are non-temporal (each byte of the pool is read once per launch); the
+// stores keep the default policy (measured faster for an extend + decode step than
+// streaming them past the caches).
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -32,38 +37,50 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowSteps = 4;  // rows per lane
 
-template <int DK>
+// LR lanes own a row, each kVec float4 of it
+template <int DK, int LR>
 struct RecLayout {
-  static constexpr int kLanesPerRow = DK / 4;                       // float4 per lane
+  static constexpr int kLanesPerRow = LR;
+  static constexpr int kVec = DK / (4 * LR);                        // float4 per lane and row
   static constexpr int kRowsPerStep = kWave / kLanesPerRow;         // rows per wave instr
   static constexpr int kRowsPerWave = kRowsPerStep * kRowSteps;
   static constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / kWave);
+  static_assert(kVec * 4 * LR == DK, "whole float4 per lane");
 };
 
+// Four consecutive inputs as loaded (bf16 kept packed until used: a staged token then
+// holds half the registers) and as float4.
 template <typename InT>
-__device__ __forceinline__ float4 load4(const InT* p);
+struct Raw4;
 template <>
-__device__ __forceinline__ float4 load4<float>(const float* p) {
-  return *reinterpret_cast<const float4*>(p);
-}
+struct Raw4<float> {
+  typedef float4 type;
+  __device__ __forceinline__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ static float4 cvt(float4 v) { return v; }
+};
 template <>
-__device__ __forceinline__ float4 load4<u16>(const u16* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-}
+struct Raw4<u16> {
+  typedef uint2 type;
+  __device__ __forceinline__ static uint2 load(const u16* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ static float4 cvt(uint2 w) {
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  }
+};
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-template <int DK, int DV, typename InT, typename OutT, bool kSSD, bool kAux, int kPre>
+template <int DK, int DV, typename InT, typename OutT, bool kSSD, bool kAux, int kPre, int LR>
 __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
-  using L = RecLayout<DK>;
+  using L = RecLayout<DK, LR>;
+  constexpr int V = L::kVec;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int c = lane % L::kLanesPerRow;       // column group: columns 4c .. 4c+3
+  const int c = lane % L::kLanesPerRow;       // column groups: columns 4 (c + LR f) .. + 3, f < V
   const int rsub = lane / L::kLanesPerRow;
+  auto col = [&](int f) { return 4 * (c + LR * f); };
   const int h = blockIdx.y;
   const int n = blockIdx.z;
   const int row0 = blockIdx.x * L::kRowsPerBlock + wave * L::kRowsPerWave + rsub;
@@ -77,15 +94,18 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
 
   float* state = p.pool + ((int64_t)sl * p.H_v + h) * (int64_t)(DV * DK);
   typedef float nf4 __attribute__((ext_vector_type(4)));   // (the nontemporal builtin takes native vectors)
-  float4 st[kRowSteps];
+  float4 st[kRowSteps][V];
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int row = row0 + s * L::kRowsPerStep;
-    if (init) {
-      const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(state + (int64_t)row * DK + 4 * c));
-      st[s] = make_float4(v.x, v.y, v.z, v.w);
-    } else {
-      st[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int f = 0; f < V; ++f) {
+      if (init) {
+        const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(state + (int64_t)row * DK + col(f)));
+        st[s][f] = make_float4(v.x, v.y, v.z, v.w);
+      } else {
+        st[s][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
 
@@ -103,7 +123,9 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   auto write_ck = [&]() {
 #pragma unroll
     for (int s = 0; s < kRowSteps; ++s)
-      *reinterpret_cast<float4*>(ckst + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
+#pragma unroll
+      for (int f = 0; f < V; ++f)
+        *reinterpret_cast<float4*>(ckst + (int64_t)(row0 + s * L::kRowsPerStep) * DK + col(f)) = st[s][f];
   };
   if (kAux && ckb == 0) write_ck();
   // target-verify states: the state after token i goes to row spr, step i; with a
@@ -115,9 +137,11 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     if (r >= 0) spr = p.sp_states + (int64_t)r * p.sp_steps * p.H_v * (DV * DK) + (int64_t)h * (DV * DK);
   }
   const int64_t sp_step = (int64_t)p.H_v * (DV * DK);
-  float4 st0[kRowSteps];
+  float4 st0[kRowSteps][V];
 #pragma unroll
-  for (int s = 0; s < kRowSteps; ++s) st0[s] = kAux ? st[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < kRowSteps; ++s)
+#pragma unroll
+    for (int f = 0; f < V; ++f) st0[s][f] = kAux ? st[s][f] : make_float4(0.f, 0.f, 0.f, 0.f);
 
   const InT* qb = reinterpret_cast<const InT*>(p.q);
   const InT* kb = reinterpret_cast<const InT*>(p.k);
@@ -137,13 +161,16 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   // A token's inputs: this lane's columns of k and q, its rows' v (and z), the gate's
   // inputs (raw a, b / dt with the gate folded in, else log g and beta).
   struct Tok {
-    float4 k, q;
+    typename Raw4<InT>::type k[V], q[V];
     float v[kRowSteps], z[kRowSteps];
     float a, b;
   };
   auto load_tok = [&](int t, Tok& in) __attribute__((always_inline)) {
-    in.k = load4<InT>(kb + (int64_t)t * p.k_stride + (int64_t)j * DK + 4 * c);
-    in.q = load4<InT>(qb + (int64_t)t * p.q_stride + (int64_t)j * DK + 4 * c);
+#pragma unroll
+    for (int f = 0; f < V; ++f) {
+      in.k[f] = Raw4<InT>::load(kb + (int64_t)t * p.k_stride + (int64_t)j * DK + col(f));
+      in.q[f] = Raw4<InT>::load(qb + (int64_t)t * p.q_stride + (int64_t)j * DK + col(f));
+    }
     const int64_t vrow = (int64_t)t * p.v_stride + (int64_t)h * DV;
 #pragma unroll
     for (int s = 0; s < kRowSteps; ++s) {
@@ -170,23 +197,42 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
       const int par = p.sp_parent[t];
       if (par < 0 || par >= t - t0 || par >= p.sp_steps) {
 #pragma unroll
-        for (int s = 0; s < kRowSteps; ++s) st[s] = st0[s];
+        for (int s = 0; s < kRowSteps; ++s)
+#pragma unroll
+          for (int f = 0; f < V; ++f) st[s][f] = st0[s][f];
       } else if (par != t - t0 - 1) {
 #pragma unroll
         for (int s = 0; s < kRowSteps; ++s)
-          st[s] = *reinterpret_cast<const float4*>(spr + par * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c);
+#pragma unroll
+          for (int f = 0; f < V; ++f)
+            st[s][f] = *reinterpret_cast<const float4*>(spr + par * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + col(f));
       }
     }
-    float4 kv = in.k, qv = in.q;
-    if constexpr (!kSSD) {
-      const float nk = group_sum<L::kLanesPerRow>(dot4(kv, kv));
-      const float nq = group_sum<L::kLanesPerRow>(dot4(qv, qv));
-      const float rk = 1.0f / sqrtf(nk + 1e-6f);
-      const float rq = 1.0f / sqrtf(nq + 1e-6f);
-      kv.x *= rk; kv.y *= rk; kv.z *= rk; kv.w *= rk;
-      qv.x *= rq; qv.y *= rq; qv.z *= rq; qv.w *= rq;
+    // this lane's part of a row dot product (its V float4 of the row)
+    auto dotv = [&](const float4* a, const float4* b) __attribute__((always_inline)) {
+      float d = dot4(a[0], b[0]);
+#pragma unroll
+      for (int f = 1; f < V; ++f) d += dot4(a[f], b[f]);
+      return d;
+    };
+    float4 kv[V], qv[V];
+#pragma unroll
+    for (int f = 0; f < V; ++f) {
+      kv[f] = Raw4<InT>::cvt(in.k[f]);
+      qv[f] = Raw4<InT>::cvt(in.q[f]);
     }
-    const float kq = group_sum<L::kLanesPerRow>(dot4(kv, qv));
+    if constexpr (!kSSD) {
+      const float nk = group_sum<L::kLanesPerRow>(dotv(kv, kv));
+      const float nq = group_sum<L::kLanesPerRow>(dotv(qv, qv));
+      const float rk = __builtin_amdgcn_rsqf(nk + 1e-6f);   // (1 ulp, as the chunked kernel's norms)
+      const float rq = __builtin_amdgcn_rsqf(nq + 1e-6f);
+#pragma unroll
+      for (int f = 0; f < V; ++f) {
+        kv[f].x *= rk; kv[f].y *= rk; kv[f].z *= rk; kv[f].w *= rk;
+        qv[f].x *= rq; qv[f].y *= rq; qv[f].z *= rq; qv[f].w *= rq;
+      }
+    }
+    const float kq = group_sum<L::kLanesPerRow>(dotv(kv, qv));
     float lg, bt;
     if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
       const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
@@ -204,20 +250,23 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     for (int s = 0; s < kRowSteps; ++s) {
       const int row = row0 + s * L::kRowsPerStep;
       const float vr = in.v[s];
-      const float y = group_sum<L::kLanesPerRow>(dot4(st[s], qv));
+      const float y = group_sum<L::kLanesPerRow>(dotv(st[s], qv));
       float u, o;
       if constexpr (kSSD) {
         u = bt * vr;
         o = g * y + u * kq;
       } else {
-        const float x = group_sum<L::kLanesPerRow>(dot4(st[s], kv));
+        const float x = group_sum<L::kLanesPerRow>(dotv(st[s], kv));
         u = bt * (vr - g * x);
         o = p.scale * (g * y + u * kq);
       }
-      st[s].x = g * st[s].x + u * kv.x;
-      st[s].y = g * st[s].y + u * kv.y;
-      st[s].z = g * st[s].z + u * kv.z;
-      st[s].w = g * st[s].w + u * kv.w;
+#pragma unroll
+      for (int f = 0; f < V; ++f) {
+        st[s][f].x = g * st[s][f].x + u * kv[f].x;
+        st[s][f].y = g * st[s][f].y + u * kv[f].y;
+        st[s][f].z = g * st[s][f].z + u * kv[f].z;
+        st[s][f].w = g * st[s][f].w + u * kv[f].w;
+      }
       if constexpr (kSSD) {
         o += Dr[s] * vr;
         if (p.z) o *= in.z[s] * sigmoid_f(in.z[s]);
@@ -228,7 +277,9 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     if (kAux && spr && t - t0 < p.sp_steps) {
 #pragma unroll
       for (int s = 0; s < kRowSteps; ++s)
-        *reinterpret_cast<float4*>(spr + (t - t0) * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + 4 * c) = st[s];
+#pragma unroll
+        for (int f = 0; f < V; ++f)
+          *reinterpret_cast<float4*>(spr + (t - t0) * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + col(f)) = st[s][f];
     }
   };
 
@@ -252,28 +303,32 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
 #pragma unroll
   for (int s = 0; s < kRowSteps; ++s) {
     const int row = row0 + s * L::kRowsPerStep;
-    *reinterpret_cast<float4*>(state + (int64_t)row * DK + 4 * c) = st[s];
+#pragma unroll
+    for (int f = 0; f < V; ++f) *reinterpret_cast<float4*>(state + (int64_t)row * DK + col(f)) = st[s][f];
   }
 }
 
 template <int DK, int DV, typename InT, typename OutT, bool kSSD>
 hipError_t launch_typed(const SeqLaunch& p, hipStream_t stream) {
-  using L = RecLayout<DK>;
-  static_assert(DV % L::kRowsPerBlock == 0, "d_v must be a multiple of the rows per block");
-  dim3 grid(DV / L::kRowsPerBlock, p.H_v, p.N), block(kThreads);
+  constexpr int LRd = DK / 4;                  // decode layout: a float4 per lane and row
+  constexpr int LRs = DK / 4 < 16 ? DK / 4 : 16;   // short extends: 16 lanes per row
+  static_assert(DV % RecLayout<DK, LRd>::kRowsPerBlock == 0 && DV % RecLayout<DK, LRs>::kRowsPerBlock == 0,
+                "d_v must be a multiple of the rows per block");
+  const dim3 gd(DV / RecLayout<DK, LRd>::kRowsPerBlock, p.H_v, p.N);
+  const dim3 gs(DV / RecLayout<DK, LRs>::kRowsPerBlock, p.H_v, p.N), block(kThreads);
   // checkpoints and target-verify states are a separate instantiation: the decode
   // step runs none of their code; short extends (at most 8 tokens per sequence by the
   // host's hint) load their first 4 tokens' inputs up front
   const bool aux = p.ck_token || p.sp_states;
   const bool shrt = p.max_seqlen > 1 && p.max_seqlen <= 8;
   if (aux && shrt)
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 4, LRs>), gs, block, 0, stream, p);
   else if (aux)
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 1>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, true, 1, LRd>), gd, block, 0, stream, p);
   else if (shrt)
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 4, LRs>), gs, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 1>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, InT, OutT, kSSD, false, 1, LRd>), gd, block, 0, stream, p);
   return hipGetLastError();
 }
 
