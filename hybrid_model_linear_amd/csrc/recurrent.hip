@@ -190,7 +190,54 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
     }
   };
 
-  auto step = [&](int t, const Tok& in) __attribute__((always_inline)) {
+  // this lane's part of a row dot product (its V float4 of the row)
+  auto dotv = [&](const float4* a, const float4* b) __attribute__((always_inline)) {
+    float d = dot4(a[0], b[0]);
+#pragma unroll
+    for (int f = 1; f < V; ++f) d += dot4(a[f], b[f]);
+    return d;
+  };
+  // A token's scalars, the same for every row: 1 / |k|, 1 / |q| (1 in delta-off mode),
+  // khat . qhat, log g and beta.  Every lane group of a row computes them for the token
+  // whose inputs its lanes hold (the staged tokens of a short extend, one per group).
+  struct TokS {
+    float rk, rq, kq, lg, bt;
+  };
+  auto scalars = [&](const typename Raw4<InT>::type* kr, const typename Raw4<InT>::type* qr, float a, float b)
+      __attribute__((always_inline)) {
+    TokS sc;
+    float4 kv[V], qv[V];
+#pragma unroll
+    for (int f = 0; f < V; ++f) {
+      kv[f] = Raw4<InT>::cvt(kr[f]);
+      qv[f] = Raw4<InT>::cvt(qr[f]);
+    }
+    sc.rk = sc.rq = 1.f;
+    if constexpr (!kSSD) {
+      const float nk = group_sum<L::kLanesPerRow>(dotv(kv, kv));
+      const float nq = group_sum<L::kLanesPerRow>(dotv(qv, qv));
+      sc.rk = __builtin_amdgcn_rsqf(nk + 1e-6f);   // (1 ulp, as the chunked kernel's norms)
+      sc.rq = __builtin_amdgcn_rsqf(nq + 1e-6f);
+    }
+    sc.kq = group_sum<L::kLanesPerRow>(dotv(kv, qv)) * sc.rk * sc.rq;
+    if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
+      const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
+      if constexpr (kSSD)
+        gate_ssd(a, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, sc.lg, sc.bt);
+      else
+        gate_gdn(a, b, expf(p.gA[h]), bias, sc.lg, sc.bt);
+    } else {
+      sc.lg = a;
+      sc.bt = b;
+    }
+    return sc;
+  };
+
+  // step(t, in, hasp, sc): with hasp (std::true_type) the token's scalars come in sc,
+  // else the step computes them itself (the decode step: its inputs' conversion and
+  // normalisation then serve the scalars and the rows alike)
+  auto step = [&](int t, const Tok& in, auto hasp, const TokS& sc) __attribute__((always_inline)) {
+    constexpr bool kHasS = decltype(hasp)::value;
     if (kAux && p.sp_parent && spr) {   // token tree (uniform branch)
       // a parent outside [0, i) (i = the token's index in its sequence) or past the
       // recorded steps counts as -1: only rows this thread wrote earlier are read
@@ -208,41 +255,46 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
             st[s][f] = *reinterpret_cast<const float4*>(spr + par * sp_step + (int64_t)(row0 + s * L::kRowsPerStep) * DK + col(f));
       }
     }
-    // this lane's part of a row dot product (its V float4 of the row)
-    auto dotv = [&](const float4* a, const float4* b) __attribute__((always_inline)) {
-      float d = dot4(a[0], b[0]);
-#pragma unroll
-      for (int f = 1; f < V; ++f) d += dot4(a[f], b[f]);
-      return d;
-    };
     float4 kv[V], qv[V];
 #pragma unroll
     for (int f = 0; f < V; ++f) {
       kv[f] = Raw4<InT>::cvt(in.k[f]);
       qv[f] = Raw4<InT>::cvt(in.q[f]);
     }
+    float rk = 1.f, rq = 1.f;
     if constexpr (!kSSD) {
-      const float nk = group_sum<L::kLanesPerRow>(dotv(kv, kv));
-      const float nq = group_sum<L::kLanesPerRow>(dotv(qv, qv));
-      const float rk = __builtin_amdgcn_rsqf(nk + 1e-6f);   // (1 ulp, as the chunked kernel's norms)
-      const float rq = __builtin_amdgcn_rsqf(nq + 1e-6f);
+      if constexpr (kHasS) {
+        rk = sc.rk;
+        rq = sc.rq;
+      } else {
+        const float nk = group_sum<L::kLanesPerRow>(dotv(kv, kv));
+        const float nq = group_sum<L::kLanesPerRow>(dotv(qv, qv));
+        rk = __builtin_amdgcn_rsqf(nk + 1e-6f);   // (1 ulp, as the chunked kernel's norms)
+        rq = __builtin_amdgcn_rsqf(nq + 1e-6f);
+      }
 #pragma unroll
       for (int f = 0; f < V; ++f) {
         kv[f].x *= rk; kv[f].y *= rk; kv[f].z *= rk; kv[f].w *= rk;
         qv[f].x *= rq; qv[f].y *= rq; qv[f].z *= rq; qv[f].w *= rq;
       }
     }
-    const float kq = group_sum<L::kLanesPerRow>(dotv(kv, qv));
-    float lg, bt;
-    if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
-      const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
-      if constexpr (kSSD)
-        gate_ssd(in.a, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
-      else
-        gate_gdn(in.a, in.b, expf(p.gA[h]), bias, lg, bt);
+    float kq, lg, bt;
+    if constexpr (kHasS) {
+      kq = sc.kq;
+      lg = sc.lg;
+      bt = sc.bt;
     } else {
-      lg = in.a;
-      bt = in.b;
+      kq = group_sum<L::kLanesPerRow>(dotv(kv, qv));
+      if (p.gate_fused) {   // the gate's arithmetic on the raw inputs (uniform branch)
+        const float bias = p.gdt_bias ? p.gdt_bias[h] : 0.f;
+        if constexpr (kSSD)
+          gate_ssd(in.a, p.gA[h], bias, p.g_softplus, p.g_lo, p.g_hi, lg, bt);
+        else
+          gate_gdn(in.a, in.b, expf(p.gA[h]), bias, lg, bt);
+      } else {
+        lg = in.a;
+        bt = in.b;
+      }
     }
     const float g = __expf(lg);
     const int64_t orow = (int64_t)t * p.out_stride + (int64_t)h * DV;
@@ -289,15 +341,49 @@ __global__ void __launch_bounds__(kThreads) recurrent_kernel(SeqLaunch p) {
   // sequence, takes kPre = 1: registers for more would cost occupancy.)
   Tok pre[kPre];
 #pragma unroll
-  for (int i = 0; i < kPre; ++i)
+  for (int i = 0; i < kPre; ++i) {
+    if constexpr (kPre > 1) pre[i] = Tok{};   // (tokens past the end join the scalars' pass below)
     if (t0 + i < t1) load_tok(t0 + i, pre[i]);
+  }
+  if constexpr (kPre > 1) {
+    // The staged tokens' scalars in one pass: the lane group of row r takes token r
+    // (its lanes hold every token's columns), then each token's values go to all lanes.
+    static_assert(L::kRowsPerStep == kPre, "one lane group per staged token");
+    typename Raw4<InT>::type kr[V], qr[V];
+    float a = pre[0].a, b = pre[0].b;
 #pragma unroll
-  for (int i = 0; i < kPre; ++i)
-    if (t0 + i < t1) step(t0 + i, pre[i]);
+    for (int f = 0; f < V; ++f) {
+      kr[f] = pre[0].k[f];
+      qr[f] = pre[0].q[f];
+    }
+#pragma unroll
+    for (int i = 1; i < kPre; ++i)
+      if (rsub == i) {
+#pragma unroll
+        for (int f = 0; f < V; ++f) {
+          kr[f] = pre[i].k[f];
+          qr[f] = pre[i].q[f];
+        }
+        a = pre[i].a;
+        b = pre[i].b;
+      }
+    const TokS mine = scalars(kr, qr, a, b);
+    auto bcast = [&](float v, int i) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), L::kLanesPerRow * i));
+    };
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      if (t0 + i < t1) {
+        const TokS sc = {bcast(mine.rk, i), bcast(mine.rq, i), bcast(mine.kq, i), bcast(mine.lg, i), bcast(mine.bt, i)};
+        step(t0 + i, pre[i], std::true_type{}, sc);
+      }
+  } else {
+    if (t0 < t1) step(t0, pre[0], std::false_type{}, TokS{});
+  }
   for (int t = t0 + kPre; t < t1; ++t) {
     Tok in;
     load_tok(t, in);
-    step(t, in);
+    step(t, in, std::false_type{}, TokS{});
   }
   if (p.keep_pool) return;
 #pragma unroll
