@@ -88,6 +88,14 @@ def _mat_rows(t: torch.Tensor, name: str, T: int, H: int) -> int:
     return t.stride(0) if T > 1 else H
 
 
+def _same_rows(n: int, what: str, **ts):
+    """Every given tensor has n rows (tokens): the library sees plain pointers and
+    cannot check how long a buffer is."""
+    for name, t in ts.items():
+        if t is not None and (t.dim() == 0 or t.shape[0] != n):
+            raise ValueError(f"{name} must have {n} rows ({what}), got shape {tuple(t.shape)}")
+
+
 def _i32(t: torch.Tensor, name: str, n: int) -> torch.Tensor:
     if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
         raise ValueError(f"{name} must be a contiguous int32 vector of length {n}")
@@ -179,6 +187,7 @@ def _extend_args(q, k, v, log_g, beta, cu_seqlens, slot, pool, *, has_init=None,
     T, H_qk, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
     N = cu_seqlens.shape[0] - 1
+    _same_rows(T, "the tokens of q", k=k, v=v, out=out, z=z)
     dev = _on_gpu(q, k, v, log_g, beta, cu_seqlens, slot, pool, has_init, out, D, z)
     if gate is not None and gate.dev != dev:
         raise ValueError("gate inputs live on another device")
@@ -376,6 +385,7 @@ def decode(q, k, v, log_g, beta, slot, pool, *, scale=None, out=None, out_dtype=
     lib = _lib.load()
     B, H_qk, d_k = q.shape
     H_v, d_v = v.shape[1], v.shape[2]
+    _same_rows(B, "one token per sequence of q", k=k, v=v, out=out)
     dev = _on_gpu(q, k, v, log_g, beta, slot, pool, out)
     if gate is not None and gate.dev != dev:
         raise ValueError("gate inputs live on another device")

@@ -378,6 +378,27 @@ def test_gated_calls_validation():
     assert lib.gdn_decode_gated(ct.byref(d), ct.byref(gs), None) == _lib.GDN_E_UNSUPPORTED   # decode is GDN only
 
 
+def test_binding_checks_token_counts():
+    """k, v, out and z must have q's token count (the library cannot see buffer
+    lengths): a shorter one is refused before anything runs."""
+    T, N = 6, 2
+    q = torch.zeros(T, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(T, 4, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 3, 6], dtype=torch.int32)
+    slot = torch.arange(N, dtype=torch.int32)
+    pool = torch.zeros(N, 4, 128, 128)
+    lg = torch.zeros(T, 4)
+    for kw, name in ((dict(k=q[:5]), "k"), (dict(v=v[:4]), "v"), (dict(out=torch.zeros(T - 1, 4, 128)), "out")):
+        a = dict(k=q, v=v, out=None)
+        a.update(kw)
+        with pytest.raises(ValueError, match=f"{name} must have {T} rows"):
+            gdn.extend(q, a["k"], a["v"], lg, lg, cu, slot, pool, out=a["out"])
+    with pytest.raises(ValueError, match=f"z must have {T} rows"):
+        gdn.extend(q, q, v, lg, lg, cu, slot, pool, mode="ssd", z=v[:2])
+    with pytest.raises(ValueError, match="v must have 6 rows"):
+        gdn.decode(q, q, v[:3], lg, lg, torch.arange(T, dtype=torch.int32), pool)
+
+
 def test_binding_rejects_cpu_tensors():
     q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
