@@ -229,6 +229,32 @@ def test_short_extend_token_recurrent(gdn_lib, name, lens, hint, out_dtype):
     assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", 1e-3, 1e-2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_short_extend_head_dim_64(gdn_lib, dtype):
+    """Short extends (hint 8) at d_k = d_v = 64, the tiny workload's head size: the
+    token-recurrent kernel's short-extend layout with one float4 per lane of a 16-lane
+    row, against the oracle (the fp32 inputs to the fp32 bar)."""
+    gdn = gdn_lib
+    _announce(f"short extend d=64 {dtype}")
+    lens = (8, 3, 1, 6, 0, 5)
+    case = synth.edge_case("short-d64", lens, has_init=(1, 0, 1, 1, 1, 0), seed=61, H_qk=2, H_v=4,
+                           d_k=64, d_v=64, dtype=dtype, num_slots=len(lens) + 2)
+    d = upload(case)
+    q, k, v = gdn.split_mixed_qkv(d["mixed"], case.H_qk, case.H_v, case.d_k, case.d_v)
+    lg, bt = gdn.gate(d["a"], d["b"], d["A_log"], d["dt_bias"])
+    assert gdn.extend_kernel(q, k, v, lg, bt, d["cu"], d["slot"], d["pool"], has_init=d["has_init"],
+                             scale=case.scale, max_seqlen=8)[0] == "recurrent"
+    out = run_extend(gdn, case, d, max_seqlen=8)
+    torch.cuda.synchronize()
+    ref, written, fin = oracle.gdn_extend(case.q, case.k, case.v, case.a, case.b, case.A_log,
+                                          case.dt_bias, case.cu_seqlens, case.slot, case.has_init,
+                                          case.pool, case.scale)
+    bar = (2e-3, 1e-2) if dtype == "bf16" else (1e-3, 1e-3)
+    assert_close(out.float().cpu().numpy(), ref, "out", *bar)
+    newpool = oracle.apply_final_states(case.pool, fin)
+    assert_close(d["pool"].cpu().numpy()[case.slot], newpool[case.slot], "states", *bar)
+
+
 def test_skipped_sequences_and_sentinels(gdn_lib):
     gdn = gdn_lib
     _announce("skipped sequences")
