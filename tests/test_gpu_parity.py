@@ -594,19 +594,23 @@ def _ckpt_args(case, relative):
     return tok, np.array(CKPT_SLOT, np.int32)
 
 
-@pytest.mark.parametrize("path", ["chunked-bf16out", "chunked-f32out", "recurrent"])
+@pytest.mark.parametrize("path", ["chunked-bf16out", "chunked-f32out", "recurrent", "recurrent-short"])
 def test_extend_checkpoints(gdn_lib, path):
     """Checkpoint states against the oracle's; outputs, final states and untouched
-    checkpoint rows unchanged by the capture."""
+    checkpoint rows unchanged by the capture.  recurrent-short: the token-recurrent
+    kernel's short-extend layout (host hint 8; the longer sequences continue past the
+    four staged tokens)."""
     gdn = gdn_lib
     _announce(f"extend checkpoints {path}")
-    dtype = "f32" if path == "recurrent" else "bf16"
+    rec = path.startswith("recurrent")
+    hint = 8 if path == "recurrent-short" else 0
+    dtype = "f32" if rec else "bf16"
     case = synth.edge_case("ckpt", CKPT_LENS, has_init=CKPT_INIT, seed=31, num_slots=11, dtype=dtype)
     odt = torch.float32 if path == "chunked-f32out" else None
-    relative = path == "recurrent"
+    relative = rec
     tok, cks = _ckpt_args(case, relative)
     d = upload(case)
-    base = run_extend(gdn, case, d, out_dtype=odt)
+    base = run_extend(gdn, case, d, out_dtype=odt, max_seqlen=hint)
     pool_base = d["pool"].clone()
     d2 = upload(case)
     states = torch.full((8, case.H_v, case.d_v, case.d_k), SENTINEL, dtype=torch.float32, device="cuda")
@@ -615,7 +619,7 @@ def test_extend_checkpoints(gdn_lib, path):
     ti = lambda x: torch.from_numpy(x).to("cuda")
     out = gdn.extend(q, k, v, lg, bt, d2["cu"], d2["slot"], d2["pool"], has_init=d2["has_init"],
                      scale=case.scale, out_dtype=odt, ckpt_token=ti(tok), ckpt_slot=ti(cks),
-                     ckpt_states=states, ckpt_relative=relative)
+                     ckpt_states=states, ckpt_relative=relative, max_seqlen=hint)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int32 if out.dtype == torch.float32 else torch.int16),
                        base.view(torch.int32 if base.dtype == torch.float32 else torch.int16)), "outputs changed"
