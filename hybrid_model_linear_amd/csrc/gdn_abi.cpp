@@ -187,7 +187,7 @@ int64_t gdn_extend_workspace_size(const gdn_extend_args* a, const gdn_gate_args*
   probe.workspace = reinterpret_cast<void*>(uintptr_t(256));
   probe.workspace_bytes = INT64_MAX;
   if (plan_extend(&probe, gate, p, w) != GDN_KERNEL_SSD_CHUNKED) return 0;
-  return gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, p.ssd_segs);
+  return gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, (p.ssd_segs - 1) * p.ssd_sub);
 }
 int gdn_extend_noalloc(const gdn_extend_args* a, const gdn_gate_args* gate, void* stream) {
   if (!a) return GDN_E_NULL;
@@ -201,7 +201,7 @@ int gdn_extend_noalloc(const gdn_extend_args* a, const gdn_gate_args* gate, void
   const int k = plan_extend(&b, gate, p, why);
   if (k <= 0) return -k;
   if (k == GDN_KERNEL_SSD_CHUNKED &&
-      gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 1) > GDN_NOALLOC_SCRATCH_BYTES)
+      gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 0) > GDN_NOALLOC_SCRATCH_BYTES)
     return GDN_E_SCRATCH;
   void* ws = nullptr;
   const int st = scratch_address(&ws);
@@ -234,15 +234,18 @@ int device_cus() {
   return n;
 }
 
-// Segments per sequence for the chunk-128 delta-off kernel: the count (1..16) that
-// minimises the estimated makespan in chunk steps -- ceil(N U s / CUs) rounds (U the
-// workgroups per sequence and segment, one per pair of heads) of
-// ceil(chunks / s) chunk steps for the full pass, plus for s > 1 the state-only pass
-// over all but the last segment (about a third of a full step per chunk) -- among
-// those whose workspace fits in `budget` bytes.  Unknown lengths (max_seqlen 0): one.
+// Segments per sequence for the chunk-128 delta-off kernel, and the pieces the
+// state-only pass cuts each of the first segs - 1 into: the pair (s in 1..16, k in 1..4)
+// that minimises the estimated makespan in chunk steps -- ceil(N U s / CUs) rounds (U
+// the workgroups per sequence and segment, one per pair of heads) of ceil(chunks / s)
+// chunk steps for the full pass, plus for s > 1 the state-only pass, ceil(N U (s - 1) k
+// / CUs) rounds of ceil(chunks / (s k)) steps (about a third of a full step per chunk;
+// smaller pieces fill more CUs) -- among those whose workspace fits in `budget` bytes.
+// Unknown lengths (max_seqlen 0): one segment.
 void ssd_plan(gdn::SeqLaunch& p, int max_seqlen, int64_t budget) {
   p.ssd_segs = 1;
   p.ssd_seg_chunks = 1 << 30;
+  p.ssd_sub = 1;
   if (max_seqlen <= 0) return;
   const int nch = (max_seqlen + 127) / 128;
   const double units = (double)p.N * gdn::ssd_units_per_seq(p), cus = (double)device_cus();
@@ -250,15 +253,20 @@ void ssd_plan(gdn::SeqLaunch& p, int max_seqlen, int64_t budget) {
   for (int s = 1; s <= 16 && s <= nch; ++s) {
     const int sc = (nch + s - 1) / s;
     const int se = (nch + sc - 1) / sc;           // segments that hold chunks
-    if ((int64_t)p.N * se > 65535 || gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, se) > budget) break;
-    // (a segment's workgroup also folds the states of the segments before it: about a
-    // quarter of a chunk step per pair of them)
-    double cost = std::ceil(units * se / cus) * (sc + 0.125 * (se - 1));
-    if (se > 1) cost += std::ceil(units * (se - 1) / cus) * sc * 0.35;
-    if (cost < best * 0.98) {                     // (ties go to fewer segments)
-      best = cost;
-      p.ssd_segs = se;
-      p.ssd_seg_chunks = se > 1 ? sc : 1 << 30;
+    if ((int64_t)p.N * se > 65535 || gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, se - 1) > budget) break;
+    for (int k = 1; k <= (se > 1 ? 4 : 1) && k <= sc; ++k) {
+      const int states = (se - 1) * k;
+      if ((int64_t)p.N * states > 65535 || gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, states) > budget) break;
+      // (a segment's workgroup also folds the states before it: about a quarter of a
+      // chunk step per pair of them)
+      double cost = std::ceil(units * se / cus) * (sc + 0.125 * states);
+      if (se > 1) cost += std::ceil(units * states / cus) * ((sc + k - 1) / k) * 0.35;
+      if (cost < best * 0.98) {                   // (ties go to fewer segments and pieces)
+        best = cost;
+        p.ssd_segs = se;
+        p.ssd_seg_chunks = se > 1 ? sc : 1 << 30;
+        p.ssd_sub = k;
+      }
     }
   }
 }
@@ -356,7 +364,7 @@ int plan_extend(const gdn_extend_args* a, const gdn_gate_args* gate, gdn::SeqLau
   const int common = (a->max_seqlen > 0 && a->max_seqlen <= 8 ? GDN_WHY_SHORT : 0) | (spec ? GDN_WHY_VERIFY : 0);
   if (ssd && a->chunk != 64) {                    // the chunk-128 delta-off kernel
     const int w = gdn::ssd_obstacles(p) | common;
-    const bool ws = a->workspace && a->workspace_bytes >= gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 1);
+    const bool ws = a->workspace && a->workspace_bytes >= gdn::ssd_workspace_bytes(p.T, p.N, p.H_qk, p.H_v, 0);
     if (a->chunk == 128) {
       if (w) return -GDN_E_UNSUPPORTED;
       if (!a->workspace) return -GDN_E_NULL;

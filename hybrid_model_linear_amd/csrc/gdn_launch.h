@@ -88,9 +88,10 @@ struct SeqLaunch {
   int lpt;                    // chunked kernel: longest sequences first (small N)
   // Chunk-128 delta-off kernel: fp16 copies of B (k) and C (q), [T, H_qk, d_k], and the
   // chunks' raw C B^T tiles, in the caller's workspace; each sequence cut into ssd_segs
-  // segments of ssd_seg_chunks chunks (the last takes the rest) with the states segR
-  // [N, segs - 1, H_v, d_v, d_k] and log decays segL [N, segs - 1, H_v] of all but the
-  // last segment.
+  // segments of ssd_seg_chunks chunks (the last takes the rest).  The state-only pass
+  // cuts each of the first segs - 1 segments into ssd_sub pieces and writes their
+  // states segR [N, (segs - 1) ssd_sub, H_v, d_v, d_k] and log decays
+  // segL [N, (segs - 1) ssd_sub, H_v], in token order.
   const u16* ssd_Bh;
   const u16* ssd_Ch;
   const u16* ssd_CB;          // raw C B^T tiles per chunk slot and group (fp16)
@@ -98,6 +99,7 @@ struct SeqLaunch {
   float* segL;
   int ssd_segs;
   int ssd_seg_chunks;
+  int ssd_sub;
 };
 
 // Short causal conv1d (bf16, width K) over packed sequences with a conv-state pool.
@@ -135,7 +137,7 @@ int chunked_obstacles(const SeqLaunch& p);
 bool ssd_chunked_shape(const SeqLaunch& p);
 int ssd_units_per_seq(const SeqLaunch& p);
 int ssd_obstacles(const SeqLaunch& p);
-int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int segs);
+int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int states);
 void ssd_bind_workspace(SeqLaunch& p, void* ws);
 hipError_t launch_ssd(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_conv(const ConvLaunch& p, hipStream_t stream);          // varlen: outputs, then states

@@ -176,15 +176,26 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
   const int hA = j * hpg + 2 * pq;
   const bool two = 2 * pq + 1 < hpg;               // (an odd group's last pair has one head)
   const int hB = two ? hA + 1 : hA;
-  const int gsegs = kFull ? p.ssd_segs : p.ssd_segs - 1;
-  const int nseq = blockIdx.y / gsegs, seg = blockIdx.y % gsegs;
+  // full pass: segment seg of sequence nseq; state-only pass: piece sub of segment seg
+  // (segments 0 .. segs - 2, each cut into ssd_sub pieces of about equal length)
+  const int nsub = kFull ? 1 : p.ssd_sub;
+  const int gsegs = kFull ? p.ssd_segs : (p.ssd_segs - 1) * nsub;
+  const int nseq = blockIdx.y / gsegs, gi = blockIdx.y % gsegs;
+  const int seg = gi / nsub, sub = gi % nsub;
   const int sl = p.slot[nseq];
   if (sl < 0) return;                              // uniform over the block
   const int tbeg = p.cu_seqlens[nseq], tend = p.cu_seqlens[nseq + 1];
   const int nch = (tend - tbeg + CS - 1) / CS;
   const bool last_seg = seg == p.ssd_segs - 1;
-  const int c0 = min(seg * p.ssd_seg_chunks, nch);
-  const int c1 = last_seg ? nch : min(c0 + p.ssd_seg_chunks, nch);
+  int c0, c1;
+  if constexpr (kFull) {
+    c0 = min(seg * p.ssd_seg_chunks, nch);
+    c1 = last_seg ? nch : min(c0 + p.ssd_seg_chunks, nch);
+  } else {
+    const int sb = seg * p.ssd_seg_chunks;
+    c0 = min(sb + sub * p.ssd_seg_chunks / nsub, nch);
+    c1 = min(sb + (sub + 1) * p.ssd_seg_chunks / nsub, nch);
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -225,16 +236,19 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
     for (int tk = 0; tk < 8; ++tk)
       *reinterpret_cast<float4*>(dst + tile_off(tk)) = make_float4(src[tk][0], src[tk][1], src[tk][2], src[tk][3]);
   };
-  const int64_t segbase = ((int64_t)nseq * (p.ssd_segs - 1)) * p.H_v;   // (n, s' = 0, h = 0) in segR / segL
+  // (n, piece 0, h = 0) in segR / segL: the pieces of the first segs - 1 segments in token order
+  const int64_t segbase = ((int64_t)nseq * (p.ssd_segs - 1) * p.ssd_sub) * p.H_v;
 #pragma unroll
   for (int tk = 0; tk < 8; ++tk) Sacc[tk] = f32x4{};
   if constexpr (kFull) {
     const bool init = p.has_init ? (p.has_init[nseq] != 0) : true;
     if (init) load_state(p.pool + ((int64_t)sl * p.H_v + h) * hstride, Sacc);
-    // entry state of the segment: S <- e^{Lambda_s'} S + R_s' over the segments before
-    // it, two segments' loads in flight at a time (the staging registers are free here)
+    // entry state of the segment: S <- e^{Lambda_s'} S + R_s' over the state-only pass's
+    // pieces before it, in order, two pieces' loads in flight at a time (the staging
+    // registers are free here)
+    const int nfold = seg * p.ssd_sub;
     int s2 = 0;
-    for (; s2 + 1 < seg; s2 += 2) {
+    for (; s2 + 1 < nfold; s2 += 2) {
       const int64_t row = segbase + (int64_t)s2 * p.H_v + h;
       const float e0 = __expf(p.segL[row]), e1 = __expf(p.segL[row + p.H_v]);
       f32x4 R0[8], R1[8];
@@ -243,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
 #pragma unroll
       for (int tk = 0; tk < 8; ++tk) Sacc[tk] = (Sacc[tk] * e0 + R0[tk]) * e1 + R1[tk];
     }
-    if (s2 < seg) {
+    if (s2 < nfold) {
       const int64_t row = segbase + (int64_t)s2 * p.H_v + h;
       const float e = __expf(p.segL[row]);
       f32x4 R[8];
@@ -708,7 +722,7 @@ __global__ void __launch_bounds__(kThreads, 1) ssd_kernel(SeqLaunch p) {
       if (!p.keep_pool) store_state(p.pool + ((int64_t)sl * p.H_v + h) * hstride, Sacc);
     }
   } else {
-    const int64_t row = segbase + (int64_t)seg * p.H_v + h;
+    const int64_t row = segbase + (int64_t)(seg * nsub + sub) * p.H_v + h;
     store_state(p.segR + row * hstride, Sacc);
     if (pt == 0 && lane == 0) p.segL[row] = lam;
   }
@@ -789,7 +803,7 @@ hipError_t launch_ssd_typed(const SeqLaunch& p, hipStream_t stream) {
   }
   const unsigned gx = (unsigned)ssd_units_per_seq(p);
   if (p.ssd_segs > 1) {
-    hipLaunchKernelGGL((ssd_kernel<OutT, kGate, false, false>), dim3(gx, p.N * (p.ssd_segs - 1)),
+    hipLaunchKernelGGL((ssd_kernel<OutT, kGate, false, false>), dim3(gx, p.N * (p.ssd_segs - 1) * p.ssd_sub),
                        dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -807,15 +821,15 @@ hipError_t launch_ssd_ck(const SeqLaunch& p, hipStream_t stream) {
 
 }  // namespace
 
-// Workspace of a chunk-128 delta-off call with `segs` segments per sequence: the fp16
-// copies of B and C, the raw C B^T tiles of every chunk slot, then the segment states
-// and log decays (segs - 1 per sequence).
-int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int segs) {
+// Workspace of a chunk-128 delta-off call with `states` state-only pieces per sequence
+// ((segments - 1) x pieces per segment; 0 for one segment): the fp16 copies of B and C,
+// the raw C B^T tiles of every chunk slot, then the pieces' states and log decays.
+int64_t ssd_workspace_bytes(int64_t T, int N, int H_qk, int H_v, int states) {
   auto up = [](int64_t b) { return (b + 255) & ~int64_t(255); };
   const int64_t bc = up(T * H_qk * NS * 2);
   const int64_t cb = up((T / CS + N) * H_qk * kCBTiles * kCBTileElems * 2);
-  const int64_t r = up((int64_t)N * (segs - 1) * H_v * PH * NS * 4);
-  const int64_t l = up((int64_t)N * (segs - 1) * H_v * 4);
+  const int64_t r = up((int64_t)N * states * H_v * PH * NS * 4);
+  const int64_t l = up((int64_t)N * states * H_v * 4);
   return 2 * bc + cb + r + l;
 }
 
@@ -828,7 +842,7 @@ void ssd_bind_workspace(SeqLaunch& p, void* ws) {
   p.ssd_Ch = reinterpret_cast<const u16*>(base + bc);
   p.ssd_CB = reinterpret_cast<const u16*>(base + 2 * bc);
   p.segR = reinterpret_cast<float*>(base + 2 * bc + cb);
-  p.segL = reinterpret_cast<float*>(base + 2 * bc + cb + up((int64_t)p.N * (p.ssd_segs - 1) * p.H_v * PH * NS * 4));
+  p.segL = reinterpret_cast<float*>(base + 2 * bc + cb + up((int64_t)p.N * (p.ssd_segs - 1) * p.ssd_sub * p.H_v * PH * NS * 4));
 }
 
 bool ssd_chunked_shape(const SeqLaunch& p) { return p.ssd && p.d_k == NS && p.d_v == PH; }

@@ -215,8 +215,8 @@ typedef struct gdn_extend_args {
 
 /* Workspace bytes the chunk-128 delta-off kernel wants for a gdn_extend (gate NULL) or
  * gdn_extend_gated call with these arguments (fp16 B and C copies, the C B^T tiles of
- * every chunk, and the states of the segments the library would run: it grows with T
- * and with N x H_v x segments), or
+ * every chunk, and the states of the pieces of the segments the library would run: it
+ * grows with T and with N x H_v x pieces), or
  * 0 when the call would run another kernel or is invalid.  Host-side, launches nothing;
  * args->workspace / workspace_bytes are ignored.  The workspace must be 256-byte
  * aligned (else GDN_E_SHAPE) and is overwritten by the call (its contents need not be

@@ -248,6 +248,20 @@ def test_ssd_workspace_grows_with_segments_and_unknown_length_needs_one():
     assert lib.gdn_extend_workspace_size(ct.byref(a), None) > one
 
 
+def test_ssd_plan_cuts_the_state_pass_finer_than_the_segments():
+    """The Mamba2-shaped call on 256 CUs (the count the host assumes without a device):
+    three segments per sequence for the full pass (2 x 40 head pairs x 3 = 240
+    workgroups), and the state-only pass cuts each of the first two into three pieces
+    (480 workgroups of ~7 chunks instead of 160 of 22): six pieces' fp32 states
+    [80, 64, 128] and log decays per sequence on top of the one-segment workspace."""
+    lib = gdn.load()
+    one = lib.gdn_extend_workspace_size(ct.byref(_ssd(max_seqlen=0)), None)
+    up = lambda b: (b + 255) & ~255
+    pieces = 2 * 6
+    assert lib.gdn_extend_workspace_size(ct.byref(_ssd()), None) == \
+        one + up(pieces * 80 * 64 * 128 * 4) + up(pieces * 80 * 4)
+
+
 def test_extend_noalloc_host_checks_come_before_any_device_call():
     """gdn_extend_noalloc validates everything on the host before it touches a device:
     the workspace fields are its own (a caller's workspace is refused), invalid
