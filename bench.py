@@ -67,6 +67,10 @@ SQ_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES",
 SQ_FILE = os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_sq_counters.txt")
 CONFIGS_PROF_CMD = "python bench.py --steps 20 --no-cpu-baseline --configs-only"
 CONFIGS_STATS_FILE = os.path.join(PROFILES, "gdn_ragged_verify_ssd128_kernel_stats.txt")
+SSD_PMC_CMD = "python bench.py --steps 5 --no-cpu-baseline --configs-only --ssd-only --calibrate-copy-mib 1024"
+SSD_COUNTERS_FILE = os.path.join(PROFILES, "gdn_ssd_chunk128_2x8192x80_counters.txt")
+SSD_KERNELS = (("prep", "ssd_prep_kernel"), ("state_pass", "ssd_kernel<unsigned short, true, false"),
+               ("full_pass", "ssd_kernel<unsigned short, true, true"))
 
 
 def parse():
@@ -86,6 +90,11 @@ def parse():
                     help="also run one device copy of this size (for counter scaling)")
     ap.add_argument("--configs-only", action="store_true",
                     help="time only the ragged, verify and delta-off workloads")
+    ap.add_argument("--ssd-only", action="store_true",
+                    help="with --configs-only: only the delta-off (chunk 128) workload")
+    ap.add_argument("--summarize-ssd-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "PASS1_DIR", "PASS2_DIR"),
+                    help="summarize counter runs of SSD_PMC_CMD (FETCH_SIZE, WRITE_SIZE, the two SQ passes) "
+                         "into profiles/ and exit")
     ap.add_argument("--summarize-prof", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 outputs of this script into profiles/ and exit")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
@@ -128,6 +137,83 @@ def summarize_configs_prof(kt_dir):
     lines = ["# rocprofv3 kernel-trace statistics of the ragged, verify and delta-off workloads",
              "# summarized by: python bench.py --summarize-configs-prof <kt_dir>"] + _stats_lines(kt_dir, CONFIGS_PROF_CMD)
     with open(CONFIGS_STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _per_kernel(d, counter):
+    """{kernel name: [value per dispatch]} of one counter in a rocprofv3 counter run."""
+    vals = {}
+    for r in _csv_rows(d, "*counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def _copy_scales(fetch, write):
+    """FETCH_SIZE / WRITE_SIZE scale factors from the 1 GiB copy (torch.mul reads and
+    writes 1 GiB): the largest MulFunctor dispatch of each run."""
+    cf = max(max(v) for k, v in fetch.items() if "MulFunctor" in k)
+    cw = max(max(v) for k, v in write.items() if "MulFunctor" in k)
+    return cf, cw, 1024 * 1024.0 / cf, 1024 * 1024.0 / cw
+
+
+def summarize_ssd_counters(fetch_dir, write_dir, dir1, dir2):
+    """profiles/ summary of four counter runs of SSD_PMC_CMD: copy-scaled HBM traffic per
+    dispatch of the delta-off kernels (prep, state-only pass, full pass) against the
+    call's algorithmic bytes, and the two SQ counter passes with derived ratios."""
+    fetch, write = _per_kernel(fetch_dir, "FETCH_SIZE"), _per_kernel(write_dir, "WRITE_SIZE")
+    cf, cw, f_scale, w_scale = _copy_scales(fetch, write)
+    sq = {}
+    for d in (dir1, dir2):
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            for kind, needle in SSD_KERNELS:
+                if needle in r["Kernel_Name"]:
+                    sq.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    lines = ["# delta-off (SSD) call at chunk 128, x [2, 8192, 80, 64]: rocprofv3 counters per dispatch",
+             f"# traffic (repository root): export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {SSD_PMC_CMD}",
+             f"#   (and the same with --pmc WRITE_SIZE); KiB scaled by the copy calibration"]
+    for i, counters in enumerate(SQ_PASSES):
+        lines.append(f"# SQ pass {i + 1}: export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(counters)} "
+                     f"--output-format csv -d <dir{i + 1}> -o bench -- {SSD_PMC_CMD}")
+    lines += ["# summarized by: python bench.py --summarize-ssd-counters <fetch_dir> <write_dir> <dir1> <dir2>",
+              f"# kernel source: ssd.hip sha256 {source_sha('ssd')}",
+              f"copy_fetch_kib {cf:.1f}", f"copy_write_kib {cw:.1f}",
+              f"fetch_scale {f_scale:.4f}", f"write_scale {w_scale:.4f}"]
+    total = 0
+    for kind, needle in SSD_KERNELS:
+        fv = [v for k, v in fetch.items() if needle in k]
+        wv = [v for k, v in write.items() if needle in k]
+        if not fv or not wv:
+            raise SystemExit(f"kernel {needle!r} not found")
+        fk, wk = sum(fv[0]) / len(fv[0]), sum(wv[0]) / len(wv[0])
+        b = int(round((fk * f_scale + wk * w_scale) * 1024))
+        total += b
+        lines += [f"{kind}_dispatches {len(fv[0])}", f"{kind}_fetch_kib {fk:.1f}", f"{kind}_write_kib {wk:.1f}",
+                  f"{kind}_traffic_bytes {b}"]
+    alg = 2 * 8192 * SSD_BYTES_PER_TOKEN + 2 * SSD_H * SSD_P * SSD_N * 4
+    lines += [f"call_traffic_bytes {total}", f"call_algorithmic_bytes {alg}",
+              f"call_traffic_over_algorithmic {total / alg:.3f}",
+              f"{'kernel':<11} {'counter':<32} {'dispatches':>10} {'avg':>12}"]
+    for (kind, ctr), v in sorted(sq.items()):
+        lines.append(f"{kind:<11} {ctr:<32} {len(v):10d} {sum(v) / len(v):12.4e}")
+    for kind, _ in SSD_KERNELS:
+        a = {ctr: sum(v) / len(v) for (k, ctr), v in sq.items() if k == kind}
+        if not a:
+            continue
+        lines.append(f"# derived ({kind}):")
+        if a.get("SQ_BUSY_CU_CYCLES"):
+            lines.append(f"#   MFMA busy cycles / (busy CU cycles x 4 SIMDs): "
+                         f"{a.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (4 * a['SQ_BUSY_CU_CYCLES']):.3f}")
+        if a.get("SQ_ACTIVE_INST_LDS"):
+            lines.append(f"#   LDS bank-conflict cycles / LDS-active cycles: "
+                         f"{a.get('SQ_LDS_BANK_CONFLICT', 0) / a['SQ_ACTIVE_INST_LDS']:.2f}")
+        if a.get("SQ_WAVE_CYCLES"):
+            lines.append(f"#   wait cycles / wave cycles: {a.get('SQ_WAIT_ANY', 0) / a['SQ_WAVE_CYCLES']:.2f}")
+        if a.get("SQ_INSTS_MFMA"):
+            lines.append(f"#   VALU instructions per MFMA instruction: {a.get('SQ_INSTS_VALU', 0) / a['SQ_INSTS_MFMA']:.1f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(SSD_COUNTERS_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -183,26 +269,14 @@ def summarize_prof(kt_dir, fetch_dir, write_dir):
     with open(os.path.join(PROFILES, "gdn_step_prefill_8x4096_decode_256_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    def per_kernel(d, counter):
-        vals = {}
-        for r in _csv_rows(d, "*counter_collection.csv"):
-            if r["Counter_Name"] != counter:
-                continue
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    fetch, write = _per_kernel(fetch_dir, "FETCH_SIZE"), _per_kernel(write_dir, "WRITE_SIZE")
 
     def pick(vals, needle):
         for k, v in vals.items():
             if needle in k:
                 return sum(v) / len(v), len(v)
         raise SystemExit(f"kernel {needle!r} not found")
-    copy_kib = 1024 * 1024.0                       # 1 GiB read and written by the copy
-
-    def pick_copy(vals):                           # the largest MulFunctor dispatch
-        return max(max(v) for k, v in vals.items() if "MulFunctor" in k)
-    cf, cw = pick_copy(fetch), pick_copy(write)
-    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    cf, cw, f_scale, w_scale = _copy_scales(fetch, write)
     out = ["# HBM traffic per dispatch from rocprofv3 counters (KiB), scaled by the copy calibration",
            f"# command (fetch, repository root): export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
            f"# command (write, repository root): export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {PMC_CMD}",
@@ -468,6 +542,9 @@ def main():
     if args.summarize_configs_prof:
         summarize_configs_prof(args.summarize_configs_prof)
         return
+    if args.summarize_ssd_counters:
+        summarize_ssd_counters(*args.summarize_ssd_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer needs no collective; heads and "
               f"sequences shard independently); --gpus {args.gpus} is not supported",
@@ -486,7 +563,13 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     if args.configs_only:
-        print(json.dumps({"configs": bench_configs(torch, gdn, synth, args.steps)}), flush=True)
+        if args.calibrate_copy_mib:   # (counter scaling, as in the step's profile)
+            src = torch.ones((args.calibrate_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
+            torch.mul(src, 1.0, out=torch.empty_like(src))
+            torch.cuda.synchronize()
+            del src
+        only = ("ssd_chunk128",) if args.ssd_only else None
+        print(json.dumps({"configs": bench_configs(torch, gdn, synth, args.steps, only=only)}), flush=True)
         return
     # ---------------- inputs (resident in HBM before timing)
     ext = synth.device_config2_prefill()

@@ -98,3 +98,40 @@ def test_cpu_baseline_runs_the_oracle_over_workers(tmp_path, monkeypatch):
     assert "4 (sequence, 16-head) units" in res["sample"]
     assert 1 <= bench.cpu_workers() <= 16
 
+
+
+def test_ssd_counter_summary(tmp_path, monkeypatch):
+    """The delta-off counter summary: copy-scaled traffic per kernel, their sum against
+    the call's algorithmic bytes, and the SQ ratios of each kernel."""
+    bench = load_bench(tmp_path, monkeypatch)
+    monkeypatch.setattr(bench, "SSD_COUNTERS_FILE", str(tmp_path / "profiles" / "ssd.txt"))
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    copy = "vectorized_elementwise_kernel<MulFunctor<float>>"
+    names = {"prep": "gdn::ssd_prep_kernel(gdn::SeqLaunch)",
+             "state": "void gdn::ssd_kernel<unsigned short, true, false, false>(gdn::SeqLaunch)",
+             "full": "void gdn::ssd_kernel<unsigned short, true, true, false>(gdn::SeqLaunch)"}
+    fk = {"prep": 10.0, "state": 20.0, "full": 30.0}
+    wk = {"prep": 1.0, "state": 2.0, "full": 3.0}
+    write_csv(str(tmp_path / "f" / "a_counter_collection.csv"), fields,
+              [{"Kernel_Name": copy, "Counter_Name": "FETCH_SIZE", "Counter_Value": 524288.0}] +
+              [{"Kernel_Name": names[k], "Counter_Name": "FETCH_SIZE", "Counter_Value": v} for k, v in fk.items()])
+    write_csv(str(tmp_path / "w" / "a_counter_collection.csv"), fields,
+              [{"Kernel_Name": copy, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1048576.0}] +
+              [{"Kernel_Name": names[k], "Counter_Name": "WRITE_SIZE", "Counter_Value": v} for k, v in wk.items()])
+    sq1 = [{"Kernel_Name": names["full"], "Counter_Name": c, "Counter_Value": v}
+           for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 40.0), ("SQ_BUSY_CU_CYCLES", 100.0),
+                        ("SQ_INSTS_MFMA", 10.0), ("SQ_INSTS_VALU", 35.0))]
+    sq2 = [{"Kernel_Name": names["full"], "Counter_Name": "SQ_WAIT_ANY", "Counter_Value": 5.0}]
+    write_csv(str(tmp_path / "s1" / "a_counter_collection.csv"), fields, sq1)
+    write_csv(str(tmp_path / "s2" / "a_counter_collection.csv"), fields, sq2)
+    bench.summarize_ssd_counters(*(str(tmp_path / d) for d in ("f", "w", "s1", "s2")))
+    kv = {}
+    for line in open(bench.SSD_COUNTERS_FILE).read().splitlines():
+        if line and not line.startswith("#") and len(line.split()) == 2:
+            kv[line.split()[0]] = line.split()[1]
+    assert int(kv["full_pass_traffic_bytes"]) == (30 * 2 + 3) * 1024
+    assert int(kv["call_traffic_bytes"]) == ((10 + 20 + 30) * 2 + 1 + 2 + 3) * 1024
+    assert int(kv["call_algorithmic_bytes"]) == 2 * 8192 * bench.SSD_BYTES_PER_TOKEN + 2 * 80 * 64 * 128 * 4
+    text = open(bench.SSD_COUNTERS_FILE).read()
+    assert "MFMA busy cycles / (busy CU cycles x 4 SIMDs): 0.100" in text
+    assert "VALU instructions per MFMA instruction: 3.5" in text
