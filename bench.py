@@ -432,6 +432,37 @@ def _rate(us, nbytes, flop):
             "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def measured_peaks(torch, gdn, reps=10):
+    """The box's achievable peaks (library probes, clocks already settled): a streaming
+    copy of 1 GiB (2 GiB of HBM traffic per call) and dependent chains of bf16 MFMAs
+    over 8 workgroups of four waves per CU."""
+    dev = "cuda"
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    us_copy = _time_calls(torch, lambda: gdn.probe_copy(src, dst), reps, warm=3, settle_ms=0.0)
+    us_inplace = _time_calls(torch, lambda: gdn.probe_copy(src, src), reps, warm=3, settle_ms=0.0)
+    del src, dst
+    blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flop = [0]
+
+    def mfma():
+        flop[0] = gdn.probe_mfma(out, blocks, iters)
+    us_mfma = _time_calls(torch, mfma, reps, warm=3, settle_ms=0.0)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("MFMA probe produced non-finite sums")
+    copy, inplace = 2 * nbytes / (us_copy * 1e-6) / 1e9, 2 * nbytes / (us_inplace * 1e-6) / 1e9
+    return {"copy_GB_s": round(copy, 1), "inplace_GB_s": round(inplace, 1),
+            "hbm_GB_s": round(max(copy, inplace), 1),
+            "mfma_bf16_TFLOP_s": round(flop[0] / (us_mfma * 1e-6) / 1e12, 1),
+            "copy": "gdn_probe_copy, 1 GiB read and 1 GiB written: into another buffer (copy) and "
+                    "back into itself (in place, the decode's state pattern); hbm_GB_s the larger",
+            "mfma": f"gdn_probe_mfma, {blocks} workgroups x 4 waves x 4 chains x {iters} "
+                    "32x32x16 bf16 MFMAs"}
+
+
 def _time_calls(torch, fn, steps, warm=10, settle_ms=100.0):
     """Average microseconds per call of fn over `steps` back-to-back calls, from HIP events
     recorded on torch's current stream (the stream the calls launch on), after at least
@@ -657,6 +688,10 @@ def main():
                       "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
     for n in ("extend", "decode"):
         kernels[n]["traffic_bytes"] = measured_traffic(n)
+    peaks = measured_peaks(torch, gdn)
+    for n in names:   # against the box's measured peaks as well as the published ones
+        kernels[n]["hbm_frac_measured"] = round(kernels[n]["GB_s"] / peaks["hbm_GB_s"], 4)
+        kernels[n]["mfma_frac_measured"] = round(kernels[n]["TFLOP_s"] / peaks["mfma_bf16_TFLOP_s"], 4)
     dom = max(("extend", "decode"), key=lambda n: per[n])
     kd = kernels[dom]
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -667,7 +702,8 @@ def main():
                 "unit": "GB/s" if ai < ridge else "TFLOP/s",
                 "frac": kd["hbm_frac"] if ai < ridge else kd["mfma_frac"],
                 "traffic": kd["traffic_bytes"], "arith_intensity": round(ai, 1),
-                "mfma_frac": kd["mfma_frac"], "avg_launch_us": kd["avg_us"]}
+                "mfma_frac": kd["mfma_frac"], "avg_launch_us": kd["avg_us"],
+                "frac_of_measured_peak": kd["hbm_frac_measured"] if ai < ridge else kd["mfma_frac_measured"]}
     tokens = T_e + T_d
     result = {
         "metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
@@ -683,6 +719,7 @@ def main():
         "phases": {"extend_tokens_per_s": round(T_e / (per["extend"] * 1e-3), 1),
                    "decode_tokens_per_s": round(T_d / (per["decode"] * 1e-3), 1)},
         "kernels": kernels,
+        "measured_peaks": peaks,
     }
     result["conv1d"] = bench_conv(torch, gdn, T_e, ext.N, T_d, args.steps)
     if not args.no_configs:

@@ -31,7 +31,7 @@ from ._lib import GDN_BF16, GDN_F32, GDN_MODE_GDN, GDN_MODE_SSD, GDNError
 
 __all__ = ["load", "gate", "ssd_gate", "extend", "extend_noalloc", "extend_kernel",
            "extend_workspace_size", "decode", "conv1d", "conv1d_update", "validate_slots", "forward_gdn",
-           "ssd_combined_fwd", "GDNError", "split_mixed_qkv"]
+           "ssd_combined_fwd", "GDNError", "split_mixed_qkv", "probe_copy", "probe_mfma"]
 
 
 def load():
@@ -427,6 +427,29 @@ def validate_slots(slot: torch.Tensor, num_slots: int) -> int:
     _lib.check("gdn_validate_slots", lib.gdn_validate_slots(_ptr(slot), slot.shape[0], num_slots,
                                                             _ptr(flag), _stream(dev)))
     return int(flag.item())
+
+
+# ------------------------------------------------------------------ measurement helpers
+def probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """gdn_probe_copy: stream src's bytes into dst (same size, contiguous device
+    tensors; dst may be src itself: in place) on the current stream."""
+    lib = _lib.load()
+    dev = _on_gpu(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must be contiguous tensors of the same size in bytes")
+    _lib.check("gdn_probe_copy", lib.gdn_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(dev)))
+
+
+def probe_mfma(out: torch.Tensor, blocks: int, iters: int) -> int:
+    """gdn_probe_mfma on the current stream: out is a float32 device tensor of blocks x 256
+    elements.  Returns the flop the launch performs."""
+    lib = _lib.load()
+    dev = _on_gpu(out)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() < blocks * 256:
+        raise ValueError(f"out must be a contiguous float32 tensor of at least {blocks * 256} elements")
+    _lib.check("gdn_probe_mfma", lib.gdn_probe_mfma(_ptr(out), blocks, iters, _stream(dev)))
+    return blocks * 4 * 4 * iters * 32 * 32 * 16 * 2
 
 
 # ------------------------------------------------------------------ short causal conv

@@ -10,12 +10,12 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_DTYPE, GDN_E_UNSUPPORTED, GDN_E_INDEX, GDN_E_HIP, GDN_E_SCRATCH = range(8)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MODE_GDN, GDN_MODE_SSD = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTED = ["gdn_gate", "gdn_extend", "gdn_decode", "gdn_extend_gated", "gdn_decode_gated",
             "gdn_conv1d", "gdn_conv1d_update", "gdn_validate_slots", "gdn_status_str",
             "gdn_last_hip_error", "gdn_abi_version", "gdn_extend_workspace_size", "gdn_extend_kernel",
-            "gdn_extend_noalloc"]
+            "gdn_extend_noalloc", "gdn_probe_copy", "gdn_probe_mfma"]
 
 # gdn_extend_kernel results and reason bits (include/gdn.h)
 GDN_KERNEL_RECURRENT, GDN_KERNEL_CHUNKED, GDN_KERNEL_SSD_CHUNKED = 1, 2, 3
@@ -104,6 +104,10 @@ def load(path: str | None = None) -> C.CDLL:
     lib.gdn_extend_kernel.restype = C.c_int
     lib.gdn_extend_noalloc.argtypes = [C.POINTER(ExtendArgs), C.POINTER(GateArgs), C.c_void_p]
     lib.gdn_extend_noalloc.restype = C.c_int
+    lib.gdn_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+    lib.gdn_probe_copy.restype = C.c_int
+    lib.gdn_probe_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
+    lib.gdn_probe_mfma.restype = C.c_int
     lib.gdn_status_str.argtypes = [C.c_int]
     lib.gdn_status_str.restype = C.c_char_p
     lib.gdn_last_hip_error.argtypes = []

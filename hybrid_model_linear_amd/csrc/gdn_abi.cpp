@@ -516,6 +516,17 @@ extern "C" {
 int gdn_conv1d(const gdn_conv_args* a, void* stream) { return conv_impl(a, false, stream); }
 int gdn_conv1d_update(const gdn_conv_args* a, void* stream) { return conv_impl(a, true, stream); }
 
+int gdn_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst) return GDN_E_NULL;
+  if (bytes <= 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return GDN_E_SHAPE;
+  return hip_status(gdn::launch_copy_probe(src, dst, bytes, (hipStream_t)stream));
+}
+int gdn_probe_mfma(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (!out) return GDN_E_NULL;
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 20)) return GDN_E_SHAPE;
+  return hip_status(gdn::launch_mfma_probe(out, blocks, iters, (hipStream_t)stream));
+}
 int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
                        void* stream) {
   if (!flag) return GDN_E_NULL;

@@ -143,4 +143,8 @@ hipError_t launch_ssd(const SeqLaunch& p, hipStream_t stream);
 hipError_t launch_conv(const ConvLaunch& p, hipStream_t stream);          // varlen: outputs, then states
 hipError_t launch_conv_update(const ConvLaunch& p, hipStream_t stream);   // one token per row
 
+// measurement helpers (probe.hip)
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
+
 }  // namespace gdn

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -402,6 +402,21 @@ int gdn_conv1d_update(const gdn_conv_args* args, void* stream);
  * and may repeat.  Asynchronous like the others; O(n^2) comparisons. */
 int gdn_validate_slots(const int32_t* slot, int32_t n, int64_t num_slots, int32_t* flag,
                        void* stream);
+
+/* Measurement helpers, not part of the layer: they give the achievable peaks of the
+ * running GPU that the layer's kernels are reported against, beside the published ones.
+ *
+ * gdn_probe_copy: copies `bytes` bytes from src to dst (device pointers, 16-byte
+ * aligned, bytes a positive multiple of 16; dst either equal to src -- in place, every
+ * element read and rewritten -- or not overlapping it) with a streaming kernel; the
+ * caller times it.  HBM traffic: 2 x bytes.
+ * gdn_probe_mfma: `blocks` workgroups of four waves (1 <= blocks <= 65536), each wave
+ * four chains of `iters` (1 <= iters <= 1 << 20) dependent 32x32x16 bf16 MFMAs with
+ * fp32 accumulation: blocks x 4 x 4 x iters x 32768 flop.  out (device, blocks x 256
+ * floats, caller-owned) receives one finite sum per thread.
+ * Both are asynchronous on `stream`; GDN_E_NULL / GDN_E_SHAPE on bad arguments. */
+int gdn_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+int gdn_probe_mfma(float* out, int32_t blocks, int32_t iters, void* stream);
 
 const char* gdn_status_str(int status);
 int gdn_last_hip_error(void);

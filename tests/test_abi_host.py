@@ -598,3 +598,18 @@ def test_ssd_combined_rejects_unsupported_arguments():
         gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, out=x)
     with pytest.raises(NotImplementedError):
         gdn.ssd_combined_fwd(x, x[..., 0], None, x, x, update_seq_chunk_cumsum=True)
+
+
+def test_probe_argument_checks():
+    """The measurement probes refuse bad arguments before any launch."""
+    lib = gdn.load()
+    p = ct.c_void_p(0x100000)
+    assert lib.gdn_probe_copy(None, p, 1024, None) == _lib.GDN_E_NULL
+    assert lib.gdn_probe_copy(p, p, 1000, None) == _lib.GDN_E_SHAPE          # not a multiple of 16
+    assert lib.gdn_probe_copy(p, ct.c_void_p(0x100008), 1024, None) == _lib.GDN_E_SHAPE   # misaligned
+    assert lib.gdn_probe_copy(p, p, 0, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_probe_mfma(None, 1, 1, None) == _lib.GDN_E_NULL
+    assert lib.gdn_probe_mfma(p, 0, 1, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_probe_mfma(p, 1, 0, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_probe_mfma(p, 65537, 1, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_probe_mfma(p, 1, (1 << 20) + 1, None) == _lib.GDN_E_SHAPE
