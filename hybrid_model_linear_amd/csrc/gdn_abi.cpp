@@ -518,8 +518,9 @@ int gdn_conv1d_update(const gdn_conv_args* a, void* stream) { return conv_impl(a
 
 int gdn_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (!src || !dst) return GDN_E_NULL;
-  if (bytes <= 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
-    return GDN_E_SHAPE;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  if (bytes <= 0 || bytes % 16 != 0 || (s | d) % 16 != 0) return GDN_E_SHAPE;
+  if (s != d && (s < d ? d - s : s - d) < (uint64_t)bytes) return GDN_E_SHAPE;   // partial overlap
   return hip_status(gdn::launch_copy_probe(src, dst, bytes, (hipStream_t)stream));
 }
 int gdn_probe_mfma(float* out, int32_t blocks, int32_t iters, void* stream) {

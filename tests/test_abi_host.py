@@ -608,6 +608,7 @@ def test_probe_argument_checks():
     assert lib.gdn_probe_copy(p, p, 1000, None) == _lib.GDN_E_SHAPE          # not a multiple of 16
     assert lib.gdn_probe_copy(p, ct.c_void_p(0x100008), 1024, None) == _lib.GDN_E_SHAPE   # misaligned
     assert lib.gdn_probe_copy(p, p, 0, None) == _lib.GDN_E_SHAPE
+    assert lib.gdn_probe_copy(p, ct.c_void_p(0x100000 + 512), 1024, None) == _lib.GDN_E_SHAPE   # overlap
     assert lib.gdn_probe_mfma(None, 1, 1, None) == _lib.GDN_E_NULL
     assert lib.gdn_probe_mfma(p, 0, 1, None) == _lib.GDN_E_SHAPE
     assert lib.gdn_probe_mfma(p, 1, 0, None) == _lib.GDN_E_SHAPE
