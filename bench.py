@@ -15,6 +15,8 @@ Prints ONE JSON line.  `roofline` covers the kernel with the largest share of th
 step (per-launch time from HIP events recorded on the launch stream, which is
 torch's current stream); its `traffic` comes from the committed hardware-counter
 summary under profiles/ when that summary was taken on the same kernel source.
+`measured_peaks` holds the box's own copy bandwidth and bf16 MFMA rate (the library's
+probes), and every kernel entry its fraction of them beside the published peaks.
 `cpu_baseline` times the float64 CPU oracle on the whole prefill workload over the
 host's cores (one single-threaded worker process per unit; the one-thread rate beside
 it).
